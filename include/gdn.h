@@ -1,0 +1,149 @@
+/*
+ * gdn.h -- C ABI of the gfx950 (MI355X) gated delta rule library (libgdn.so).
+ *
+ * The operation (jianyuh.github.io reading notes on Qwen3.8-Next, section 2.1 "Gated
+ * DeltaNet", the four-line recurrence and its boxed transition-matrix form): for every
+ * sequence n and head h, with a state S in R^{d_k x d_v} (rows over the key dimension),
+ * scalar gates alpha_t in (0,1] (decay) and beta_t in [0,1] (write strength),
+ *
+ *     S_t = alpha_t S_{t-1} + beta_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T
+ *         = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     y_t = S_t^T q_t                       (read from the updated state)
+ *
+ * The library takes q, k, v and the gates as given: it does not normalise q or k, apply
+ * a feature map or a query scale, or derive alpha from log-space parameters.
+ *
+ * Layouts (all row-major, no padding):
+ *   q, k      [rows, H, d_k]       rows = total tokens of the packed batch (prefill)
+ *   v, y      [rows, H, d_v]                or the batch size (decode)
+ *   alpha,beta[rows, H]            fp32
+ *   state     [N, H, d_k, d_v]     fp32, element (i, j) at i * d_v + j
+ * q, k, v and y share one dtype (gdn_dtype); the state is always fp32.
+ *
+ * Ownership and threading: every pointer is a device pointer owned by the caller.  The
+ * library never allocates device memory, frees, or synchronises; all work is enqueued on
+ * the caller's stream (a hipStream_t passed as void*, NULL = the null stream) and the call
+ * returns before it completes.  Device faults surface at the caller's next synchronisation.
+ * The library keeps no global state and is safe to call from several threads.
+ *
+ * Errors: every precondition that can be checked on the host is checked before anything is
+ * enqueued; a violation returns a status code and enqueues nothing.  Values inside device
+ * buffers (cu_seqlens contents, gate ranges, NaNs) are preconditions that are not checked.
+ *
+ * Supported shapes: d_k, d_v in {64, 128}; any H >= 1; any lengths (including 0).
+ * Alignment: q, k, v and y to four elements (8 bytes for bf16, 16 for fp32); states and
+ * the workspace to 16 bytes; alpha, beta and cu_seqlens to 4 bytes.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1,     /* null pointer, bad size, misalignment, bad aliasing */
+    GDN_ERR_UNSUPPORTED = 2,          /* head dimension or dtype not built */
+    GDN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < gdn_prefill_workspace_bytes() */
+    GDN_ERR_HIP = 4                   /* the HIP runtime refused a launch */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_F32 = 0,   /* IEEE binary32 */
+    GDN_DTYPE_BF16 = 1   /* bfloat16; y is rounded to nearest even */
+} gdn_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *gdn_status_str(int32_t status);
+
+/* Library version string, e.g. "gdn-gfx950 0.1". */
+const char *gdn_version(void);
+
+/*
+ * Bytes of device workspace gdn_prefill needs for this problem (a pure function of the
+ * arguments; 0 on invalid arguments).  The workspace holds the chunk/segment table and,
+ * for long sequences, the per-segment transition matrices and start states of the
+ * segment-parallel scan.
+ */
+size_t gdn_prefill_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H,
+                                   int32_t d_k, int32_t d_v, int32_t dtype);
+
+/*
+ * Chunked prefill over a packed batch of sequences (the recurrence above, evaluated 64
+ * tokens at a time with the exact WY/UT chunk form and an fp32 state).
+ *
+ *   q, k, v        [total_T, H, d]  dtype           (read only)
+ *   alpha, beta    [total_T, H]     fp32            (read only)
+ *   initial_state  [num_seqs, H, d_k, d_v] fp32, or NULL for zeros   (read only)
+ *   cu_seqlens     device int32 [num_seqs + 1]: 0 = cu[0] <= cu[1] <= ... = total_T,
+ *                  or NULL: num_seqs sequences of total_T / num_seqs tokens each
+ *                  (total_T must then be a multiple of num_seqs)
+ *   y              [total_T, H, d_v] dtype          (written; every element)
+ *   final_state    [num_seqs, H, d_k, d_v] fp32 or NULL (not written).  It may be exactly
+ *                  initial_state (in-place resume); any other overlap between an output and
+ *                  an input, or between the two outputs, is rejected when it can be seen from
+ *                  the pointers and sizes.
+ *   workspace      device buffer of at least gdn_prefill_workspace_bytes(...) bytes (may be
+ *                  NULL when that size is 0); its contents need no initialisation.
+ * A zero-length sequence writes no y and returns its initial state.
+ */
+gdn_status gdn_prefill(const void *q, const void *k, const void *v,
+                       const float *alpha, const float *beta,
+                       const float *initial_state, const int32_t *cu_seqlens,
+                       int32_t num_seqs, int64_t total_T, int32_t H,
+                       int32_t d_k, int32_t d_v, int32_t dtype,
+                       void *y, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Tuning override of gdn_prefill (same semantics and results up to rounding order):
+ * dv_tile in {0 = automatic, 16, 32, 64, 128} columns of the state per workgroup (must divide
+ * d_v; fp32 allows at most 64, or 32 when d_k = 128), segment_chunks = 0 (automatic), -1 (never split a sequence) or the number of
+ * 64-token chunks per segment of the segment-parallel scan.  The workspace must be sized
+ * with gdn_prefill_workspace_bytes_ex for the same options.
+ */
+size_t gdn_prefill_workspace_bytes_ex(int32_t num_seqs, int64_t total_T, int32_t H,
+                                      int32_t d_k, int32_t d_v, int32_t dtype,
+                                      int32_t dv_tile, int32_t segment_chunks);
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_T, int32_t H,
+                          int32_t d_k, int32_t d_v, int32_t dtype,
+                          void *y, float *final_state,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          int32_t dv_tile, int32_t segment_chunks);
+
+/*
+ * The launch plan gdn_prefill would use for this problem: state columns per workgroup and
+ * chunks per segment (-1 = sequences are not split).  For reporting.
+ */
+gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                            int32_t d_v, int32_t dtype, int32_t *dv_tile,
+                            int32_t *segment_chunks);
+
+/*
+ * One decode step for a batch of B sequences (one token each), state updated in place:
+ *
+ *   q, k   [B, H, d_k] dtype;  v [B, H, d_v] dtype;  alpha, beta [B, H] fp32  (read only)
+ *   state  [B, H, d_k, d_v] fp32, read and then overwritten with S_t
+ *   y      [B, H, d_v] dtype, written with S_t^T q_t
+ *
+ * Each head's state is read once and written once.  state must not overlap any other
+ * argument.
+ */
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta,
+                           float *state, void *y,
+                           int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

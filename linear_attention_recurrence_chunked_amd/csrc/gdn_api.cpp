@@ -1,0 +1,213 @@
+// gdn_api.cpp -- the C ABI of libgdn (declared in include/gdn.h).
+//
+// Host-side argument validation and launch.  Nothing here allocates device memory,
+// synchronises or keeps state between calls; every check that can be made from the host
+// happens before the first HIP call, so invalid arguments never reach the runtime.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// [a, a + na) and [b, b + nb) overlap (both non-empty)
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t esize(int32_t dtype) { return dtype == GDN_DTYPE_BF16 ? 2 : 4; }
+
+gdn_status check_common(int64_t rows, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype)
+{
+    if (rows < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_str(int32_t status)
+{
+    switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    default: return "GDN_ERR_UNKNOWN";
+    }
+}
+
+const char *gdn_version(void) { return "gdn-gfx950 0.1"; }
+
+static bool plan_for(int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k, int32_t d_v,
+                     int32_t dtype, int32_t dv_tile, int32_t seg, gdn::PrefillPlan *plan)
+{
+    if (num_seqs <= 0 || check_common(total_T, H, d_k, d_v, dtype) != GDN_OK) return false;
+    return gdn::make_plan(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile, seg, plan);
+}
+
+size_t gdn_prefill_workspace_bytes_ex(int32_t num_seqs, int64_t total_T, int32_t H,
+                                      int32_t d_k, int32_t d_v, int32_t dtype,
+                                      int32_t dv_tile, int32_t segment_chunks)
+{
+    gdn::PrefillPlan plan;
+    if (!plan_for(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile, segment_chunks, &plan))
+        return 0;
+    return plan.ws_table + plan.ws_seg;
+}
+
+size_t gdn_prefill_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                                   int32_t d_v, int32_t dtype)
+{
+    return gdn_prefill_workspace_bytes_ex(num_seqs, total_T, H, d_k, d_v, dtype, 0, 0);
+}
+
+gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                            int32_t d_v, int32_t dtype, int32_t *dv_tile,
+                            int32_t *segment_chunks)
+{
+    if (!dv_tile || !segment_chunks) return GDN_ERR_INVALID_ARGUMENT;
+    gdn_status st = check_common(total_T, H, d_k, d_v, dtype);
+    if (st != GDN_OK) return st;
+    if (num_seqs <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    gdn::PrefillPlan plan;
+    if (!gdn::make_plan(num_seqs, total_T, H, d_k, d_v, dtype, 0, 0, &plan))
+        return GDN_ERR_UNSUPPORTED;
+    *dv_tile = plan.dv_tile;
+    *segment_chunks = plan.seg_chunks;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, const float *initial_state,
+                          const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_T,
+                          int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void *y,
+                          float *final_state, void *workspace, size_t workspace_bytes,
+                          void *stream, int32_t dv_tile, int32_t segment_chunks)
+{
+    gdn_status st = check_common(total_T, H, d_k, d_v, dtype);
+    if (st != GDN_OK) return st;
+    if (num_seqs <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (!cu_seqlens && total_T % num_seqs != 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (total_T > 0 && (!q || !k || !v || !alpha || !beta || !y))
+        return GDN_ERR_INVALID_ARGUMENT;
+    // q, k, v, y: four elements; states and workspace: 16 bytes; gates, cu_seqlens: 4 bytes
+    const uintptr_t quad = 4 * esize(dtype);
+    const void *quads[] = {q, k, v, y};
+    for (const void *p : quads)
+        if (p && !aligned(p, quad)) return GDN_ERR_INVALID_ARGUMENT;
+    const void *vec[] = {initial_state, final_state, workspace};
+    for (const void *p : vec)
+        if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARGUMENT;
+    const void *words[] = {alpha, beta, cu_seqlens};
+    for (const void *p : words)
+        if (p && !aligned(p, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    if (dv_tile < 0 || segment_chunks < -1) return GDN_ERR_INVALID_ARGUMENT;
+
+    // In-place resume (final_state == initial_state) never splits sequences: a later
+    // segment would overwrite the state that the first segment of its sequence still reads.
+    const bool in_place = final_state && final_state == initial_state;
+    if (in_place && segment_chunks > 0) return GDN_ERR_INVALID_ARGUMENT;
+    gdn::PrefillPlan plan;
+    if (!gdn::make_plan(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile,
+                        in_place ? -1 : segment_chunks, &plan))
+        return dv_tile != 0 ? GDN_ERR_UNSUPPORTED : GDN_ERR_INVALID_ARGUMENT;
+    const size_t need = plan.ws_table + plan.ws_seg;
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+
+    // aliasing: outputs may not overlap inputs (final_state == initial_state is allowed)
+    const size_t e = esize(dtype);
+    const size_t rows = (size_t)total_T;
+    const size_t n_qk = rows * H * d_k * e, n_v = rows * H * d_v * e, n_g = rows * H * 4;
+    const size_t n_s = (size_t)num_seqs * H * d_k * d_v * 4;
+    const size_t n_cu = cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0;
+    struct Span { const void *p; size_t n; };
+    const Span inputs[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_g}, {beta, n_g},
+                           {cu_seqlens, n_cu}};
+    const Span outs[] = {{y, n_v}, {final_state, final_state ? n_s : 0}, {workspace, need}};
+    for (const Span &o : outs) {
+        for (const Span &in : inputs)
+            if (overlap(o.p, o.n, in.p, in.n)) return GDN_ERR_INVALID_ARGUMENT;
+        if (o.p != final_state && overlap(o.p, o.n, initial_state, initial_state ? n_s : 0))
+            return GDN_ERR_INVALID_ARGUMENT;
+    }
+    if (final_state && initial_state && final_state != initial_state &&
+        overlap(final_state, n_s, initial_state, n_s))
+        return GDN_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return GDN_ERR_INVALID_ARGUMENT;
+
+    gdn::PrefillProblem p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.s0 = initial_state;
+    p.cu = cu_seqlens;
+    p.num_seqs = num_seqs;
+    p.total_T = total_T;
+    p.H = H;
+    p.dk = d_k;
+    p.dv = d_v;
+    p.dtype = dtype;
+    p.y = y;
+    p.s_final = final_state;
+    hipError_t err = gdn::launch_prefill(p, plan, workspace, (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *alpha,
+                       const float *beta, const float *initial_state,
+                       const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_T,
+                       int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void *y,
+                       float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream)
+{
+    return gdn_prefill_ex(q, k, v, alpha, beta, initial_state, cu_seqlens, num_seqs, total_T,
+                          H, d_k, d_v, dtype, y, final_state, workspace, workspace_bytes,
+                          stream, 0, 0);
+}
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *beta, float *state, void *y, int32_t B, int32_t H,
+                           int32_t d_k, int32_t d_v, int32_t dtype, void *stream)
+{
+    gdn_status st = check_common(B, H, d_k, d_v, dtype);
+    if (st != GDN_OK) return st;
+    if (B == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !y) return GDN_ERR_INVALID_ARGUMENT;
+    const uintptr_t quad = 4 * esize(dtype);
+    if (!aligned(q, quad) || !aligned(k, quad) || !aligned(v, quad) || !aligned(y, quad) ||
+        !aligned(state, 16) || !aligned(alpha, 4) || !aligned(beta, 4))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const size_t e = esize(dtype);
+    const size_t n_s = (size_t)B * H * d_k * d_v * 4;
+    const size_t n_qk = (size_t)B * H * d_k * e, n_v = (size_t)B * H * d_v * e;
+    const size_t n_g = (size_t)B * H * 4;
+    struct Span { const void *p; size_t n; };
+    const Span others[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_g}, {beta, n_g}, {y, n_v}};
+    for (const Span &o : others)
+        if (overlap(state, n_s, o.p, o.n)) return GDN_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(y, n_v, others[i].p, others[i].n)) return GDN_ERR_INVALID_ARGUMENT;
+    hipError_t err = gdn::launch_decode(q, k, v, alpha, beta, state, y, B, H, d_k, d_v, dtype,
+                                        (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// gdn_device.hpp -- device-side helpers shared by the gfx950 kernels of libgdn.
+//
+// bf16 is carried as raw uint16_t bit patterns in memory and as __bf16 vectors only where
+// an MFMA consumes it.  Conversions are written from the bf16 definition (the upper 16
+// bits of an IEEE binary32 word), rounding to nearest even on the way down.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Element loads/stores for the two storage types.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float *p) { return *p; }
+    static __device__ __forceinline__ void store(float *p, float x) { *p = x; }
+};
+
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t *p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ void store(uint16_t *p, float x) {
+        *p = (uint16_t)f32_to_bf16(x);
+    }
+};
+
+// Four consecutive elements as floats.
+__device__ __forceinline__ f32x4 load4(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ f32x4 load4(const uint16_t *p) {
+    u32x2 w = *(const u32x2 *)p;
+    f32x4 r;
+    r[0] = __uint_as_float(w[0] << 16);
+    r[1] = __uint_as_float(w[0] & 0xffff0000u);
+    r[2] = __uint_as_float(w[1] << 16);
+    r[3] = __uint_as_float(w[1] & 0xffff0000u);
+    return r;
+}
+__device__ __forceinline__ void store4(float *p, f32x4 x) { *(f32x4 *)p = x; }
+__device__ __forceinline__ void store4(uint16_t *p, f32x4 x) {
+    u32x2 w;
+    w[0] = pack_bf16x2(x[0], x[1]);
+    w[1] = pack_bf16x2(x[2], x[3]);
+    *(u32x2 *)p = w;
+}
+
+__device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
+
+}  // namespace gdn

@@ -1,0 +1,45 @@
+// gdn_internal.hpp -- host-side declarations shared by the libgdn translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+constexpr int kChunk = 64;    // tokens per chunk of the chunked prefill
+
+// Problem description handed from the C ABI to the prefill launchers.
+struct PrefillProblem {
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    const float *s0;            // [N, H, dk, dv] or null
+    const int32_t *cu;          // [N+1] device or null (equal lengths)
+    int num_seqs;
+    long long total_T;
+    int H, dk, dv, dtype;
+    void *y;
+    float *s_final;             // or null
+};
+
+// Launch plan: columns of the state per workgroup and chunks per segment (-1: no split).
+struct PrefillPlan {
+    int dv_tile;
+    int seg_chunks;
+    long long max_segments;     // upper bound on table entries (segments over all sequences)
+    size_t ws_table, ws_seg;    // workspace bytes for the table and per-segment matrices
+};
+
+bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype,
+               int dv_tile_req, int seg_chunks_req, PrefillPlan *plan);
+
+hipError_t launch_prefill(const PrefillProblem &p, const PrefillPlan &plan, void *workspace,
+                          hipStream_t stream);
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *alpha,
+                         const float *beta, float *state, void *y, int B, int H, int dk,
+                         int dv, int dtype, hipStream_t stream);
+
+}  // namespace gdn

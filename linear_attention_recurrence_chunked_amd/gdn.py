@@ -1,0 +1,166 @@
+"""Python binding of libgdn (the gfx950 gated delta rule library).
+
+Argument marshalling only: every function passes device pointers, sizes and the current HIP
+stream to the C ABI of the same name (include/gdn.h) and raises ``GdnError`` on a non-OK
+status.  All computation happens in the library's HIP kernels; there is no fallback path, and
+a missing library is an error.
+
+Tensors are torch tensors on the GPU (torch is used for device memory and streams only).
+q, k, v and y are float32 or bfloat16; gates and states are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARGUMENT = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_WORKSPACE_TOO_SMALL = 3
+GDN_ERR_HIP = 4
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s" % (fn, status_str(status)))
+        self.status = status
+
+
+def load(path: Optional[str] = None):
+    """Load libgdn.so (built by ``linear_attention_recurrence_chunked_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m linear_attention_recurrence_chunked_amd.build" % p)
+    lib = ctypes.CDLL(p)
+    c = ctypes
+    vp, i32, i64, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_size_t
+    lib.gdn_status_str.restype = c.c_char_p
+    lib.gdn_status_str.argtypes = [i32]
+    lib.gdn_version.restype = c.c_char_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_prefill_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.gdn_prefill_workspace_bytes_ex.restype = sz
+    lib.gdn_prefill_workspace_bytes_ex.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
+    lib.gdn_prefill_plan.restype = i32
+    lib.gdn_prefill_plan.argtypes = [i32, i64, i32, i32, i32, i32,
+                                     c.POINTER(i32), c.POINTER(i32)]
+    pre = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.gdn_prefill.restype = i32
+    lib.gdn_prefill.argtypes = pre
+    lib.gdn_prefill_ex.restype = i32
+    lib.gdn_prefill_ex.argtypes = pre + [i32, i32]
+    lib.gdn_decode_step.restype = i32
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().gdn_status_str(int(status)).decode()
+
+
+gdn_status_str = status_str
+
+
+def gdn_version() -> str:
+    return load().gdn_version().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GDN_DTYPE_F32
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != GDN_OK:
+        raise GdnError(fn, status)
+
+
+def gdn_prefill_workspace_bytes(num_seqs: int, total_T: int, H: int, d_k: int, d_v: int,
+                                dtype: int, dv_tile: int = 0, segment_chunks: int = 0) -> int:
+    return int(load().gdn_prefill_workspace_bytes_ex(num_seqs, total_T, H, d_k, d_v, dtype,
+                                                     dv_tile, segment_chunks))
+
+
+def gdn_prefill_plan(num_seqs: int, total_T: int, H: int, d_k: int, d_v: int,
+                     dtype: int) -> Tuple[int, int]:
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check("gdn_prefill_plan", load().gdn_prefill_plan(num_seqs, total_T, H, d_k, d_v, dtype,
+                                                       ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, num_seqs=None,
+                y=None, final_state=None, workspace=None, stream=None, dv_tile: int = 0,
+                segment_chunks: int = 0, want_final_state: bool = True):
+    """Chunked prefill.  q, k: [T, H, d_k]; v: [T, H, d_v]; alpha, beta: [T, H] fp32;
+    initial_state: [N, H, d_k, d_v] fp32 or None; cu_seqlens: int32 [N+1] on the device or
+    None (N equal sequences, ``num_seqs`` required).  Returns (y, final_state)."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        n = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != n:
+            raise ValueError("num_seqs does not match cu_seqlens")
+        num_seqs = n
+    elif num_seqs is None:
+        num_seqs = 1
+    if y is None:
+        y = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = gdn_prefill_workspace_bytes(num_seqs, T, H, dk, dv, dt, dv_tile, segment_chunks)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gdn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(initial_state), _ptr(cu_seqlens), num_seqs, T, H, dk, dv,
+                               dt, _ptr(y), _ptr(final_state), _ptr(workspace), wbytes,
+                               _stream(stream), dv_tile, segment_chunks)
+    _check("gdn_prefill", st)
+    return y, final_state
+
+
+def gdn_decode_step(q, k, v, alpha, beta, state, y=None, stream=None):
+    """One decode step: q, k [B, H, d_k]; v [B, H, d_v]; alpha, beta [B, H] fp32;
+    state [B, H, d_k, d_v] fp32 updated in place.  Returns y [B, H, d_v]."""
+    import torch
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    st = load().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(state), _ptr(y), B, H, dk, dv, _dtype_code(q),
+                                _stream(stream))
+    _check("gdn_decode_step", st)
+    return y

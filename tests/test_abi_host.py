@@ -1,0 +1,145 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every declared symbol,
+and rejects every invalid argument before anything reaches the HIP runtime.
+
+The pointers below are fake but aligned device addresses; every call here fails validation,
+so nothing is ever launched or dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_chunked_amd import gdn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "gdn.h")
+G = 1 << 32   # spacing between fake buffers (no two overlap)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built; run __graft_entry__.build()")
+    return gdn.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "gdn_prefill" in names and "gdn_decode_step" in names
+    for n in names:
+        assert hasattr(lib, n), "symbol %s missing from libgdn.so" % n
+
+
+def test_status_strings_and_version(lib):
+    assert gdn.status_str(0) == "GDN_OK"
+    assert gdn.status_str(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
+    assert gdn.status_str(99) == "GDN_ERR_UNKNOWN"
+    assert gdn.gdn_version().startswith("gdn-gfx950")
+
+
+def test_plans_for_the_workloads(lib):
+    # 64 chains (B=4, H=16): split the state columns, never the sequences
+    t, s = gdn.gdn_prefill_plan(4, 4 * 4096, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert t in (32, 64) and s == -1
+    # 16 chains of 1M tokens: segment-parallel scan
+    t, s = gdn.gdn_prefill_plan(1, 1 << 20, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert s > 0
+    assert gdn.gdn_prefill_workspace_bytes(1, 1 << 20, 16, 128, 128, 1) > 0
+    # 512 chains: enough work without splitting
+    t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert s == -1
+    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == 0
+    # fp32 tiles stay within the LDS budget
+    t, s = gdn.gdn_prefill_plan(1, 256, 2, 64, 64, gdn.GDN_DTYPE_F32)
+    assert t in (16, 32, 64)
+
+
+def test_workspace_query_rejects_bad_shapes(lib):
+    assert gdn.gdn_prefill_workspace_bytes(0, 10, 1, 128, 128, 1) == 0
+    assert gdn.gdn_prefill_workspace_bytes(1, 10, 1, 96, 128, 1) == 0
+    assert gdn.gdn_prefill_workspace_bytes(1, 10, 1, 128, 128, 7) == 0
+    # explicit segmentation needs table + per-segment matrices
+    w = gdn.gdn_prefill_workspace_bytes(2, 1000, 3, 64, 128, 1, 32, 2)
+    assert w >= 3 * 8 * (64 * 128 + 64 * 64) * 4
+
+
+def prefill(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, s0=None, cu=None,
+             n=2, T=256, H=2, dk=128, dv=128, dt=1, y=6 * G, sf=7 * G, ws=None, wsb=0,
+             stream=None, tile=0, seg=-1)
+    a.update(kw)
+    return lib.gdn_prefill_ex(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["cu"],
+                              a["n"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["y"],
+                              a["sf"], a["ws"], a["wsb"], a["stream"], a["tile"], a["seg"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(alpha=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(y=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(n=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(H=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(T=255), gdn.GDN_ERR_INVALID_ARGUMENT),          # not a multiple of n without cu
+    (dict(dk=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dv=256), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dt=5), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(tile=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dt=0, tile=128), gdn.GDN_ERR_UNSUPPORTED),      # fp32 tile over the LDS budget
+    (dict(seg=-2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(k=2 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),    # misaligned (bf16 quad = 8 B)
+    (dict(dt=0, k=2 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),   # fp32 quad = 16 B
+    (dict(alpha=4 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(sf=7 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(y=1 * G + 4096), gdn.GDN_ERR_INVALID_ARGUMENT), # y overlaps q
+    (dict(sf=5 * G), gdn.GDN_ERR_INVALID_ARGUMENT),       # final state overlaps beta
+    (dict(s0=8 * G, y=8 * G), gdn.GDN_ERR_INVALID_ARGUMENT),   # y overlaps initial state
+    (dict(s0=8 * G, sf=8 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # partial overlap
+    (dict(s0=8 * G, sf=8 * G, seg=2), gdn.GDN_ERR_INVALID_ARGUMENT),  # in place + split
+    (dict(seg=2), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),       # needs a workspace
+    (dict(seg=2, ws=9 * G, wsb=64), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def decode(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, state=6 * G, y=7 * G,
+             B=4, H=2, dk=128, dv=128, dt=1, stream=None)
+    a.update(kw)
+    return lib.gdn_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["state"],
+                               a["y"], a["B"], a["H"], a["dk"], a["dv"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(v=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(H=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dt=2), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=1 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(state=6 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(y=6 * G + 1024), gdn.GDN_ERR_INVALID_ARGUMENT),   # y inside the state
+    (dict(state=1 * G), gdn.GDN_ERR_INVALID_ARGUMENT),      # state over q
+    (dict(y=3 * G), gdn.GDN_ERR_INVALID_ARGUMENT),          # y over v
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    # B = 0 returns before any HIP call
+    assert decode(lib, B=0) == gdn.GDN_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.load(str(tmp_path / "missing.so"))
