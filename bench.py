@@ -1,0 +1,254 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  ``value`` is prefill throughput (tokens/s) on the B=4, H=16,
+T=4096, d=128 bf16 workload with inputs resident in HBM; the decode step on B=128, H=16,
+d=128 (1024 successive steps) is reported in the ``decode`` object.  Timing uses HIP events
+on the stream the library launches on.  The fp64 oracle is timed on the host cores as a
+baseline (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (MFMA %) + decode steps/s at B=128 (HBM GB/s %)"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+CHUNK = 64
+
+
+def prefill_flops_per_token_head(d: int, C: int = CHUNK) -> int:
+    # dense-tile count of the chunked form: K K^T, Q K^T, the solve-side products T.K, T.V,
+    # P.U (five C-sized products) and W.S, Q.S, K^T.U (three d-sized products)
+    return 2 * d * (5 * C + 3 * d)
+
+
+def prefill_bytes(T: int, H: int, d: int, nseq: int) -> int:
+    # q, k, v, y (bf16), alpha, beta (fp32), final state (fp32)
+    return T * H * (4 * d * 2 + 2 * 4) + nseq * H * d * d * 4
+
+
+def decode_bytes_per_head_step(d: int) -> int:
+    # state read + write (fp32), q, k, v (bf16), alpha, beta (fp32), y (bf16)
+    return 2 * d * d * 4 + 3 * d * 2 + 2 * 4 + d * 2
+
+
+def sha_of(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, source: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_sha") != sha_of(source):
+        return None
+    return ent
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrence_chunked_amd import gdn
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    gdn.load()
+
+    # ------------------------------------------------------------------ prefill
+    w = wl.PREFILL
+    t0 = time.time()
+    inp = wl.workload_inputs(w)
+    print("[bench] prefill inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
+          flush=True)
+    q = wl.to_torch(inp["q"], dev, "bf16")
+    k = wl.to_torch(inp["k"], dev, "bf16")
+    v = wl.to_torch(inp["v"], dev, "bf16")
+    alpha = torch.from_numpy(inp["alpha"]).to(dev)
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    T, H, d = q.shape
+    nseq = w.B
+    y = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    sf = torch.empty((nseq, H, d, d), dtype=torch.float32, device=dev)
+    tile, seg = gdn.gdn_prefill_plan(nseq, T, H, d, d, gdn.GDN_DTYPE_BF16)
+    need = gdn.gdn_prefill_workspace_bytes(nseq, T, H, d, d, gdn.GDN_DTYPE_BF16)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def run_prefill():
+        gdn.gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
+                        num_seqs=nseq, y=y, final_state=sf, workspace=ws if need else None)
+
+    for _ in range(args.warmup):
+        run_prefill()
+    torch.cuda.synchronize()
+
+    # cold-cache timing: 512 MiB written between launches, outside the events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for e0, e1 in evs:
+        if not args.no_flush:
+            flush.fill_(1)
+        e0.record(stream)
+        run_prefill()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    times_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    pre_ms = float(np.mean(times_ms))
+    pre_med = float(np.median(times_ms))
+
+    # warm back-to-back timing
+    ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ew0.record(stream)
+    for _ in range(args.steps):
+        run_prefill()
+    ew1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = ew0.elapsed_time(ew1) / args.steps
+
+    tok_s = T / (pre_ms * 1e-3)
+    flops = prefill_flops_per_token_head(d) * T * H
+    achieved_tflops = flops / (pre_ms * 1e-3) / 1e12
+    pbytes = prefill_bytes(T, H, d, nseq)
+    kernel_src = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc",
+                              "gdn_prefill.hip")
+    tr = load_traffic("prefill_bf16_B4_H16_T4096_d128", kernel_src)
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": None if tr is None else tr["bytes_per_launch"],
+        "kernel": "prefill_kernel<128,%d,bf16,scan>" % tile,
+        "flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": pbytes,
+        "hbm_frac_of_algorithmic_bytes": round(pbytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+    # ------------------------------------------------------------------ decode
+    wd = wl.DECODE
+    nsteps = args.decode_steps
+    t0 = time.time()
+    dd = wl.decode_inputs(wd, steps=nsteps)
+    print("[bench] decode inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
+          flush=True)
+    dq = wl.to_torch(dd["q"], dev, "bf16")
+    dk_ = wl.to_torch(dd["k"], dev, "bf16")
+    dv_ = wl.to_torch(dd["v"], dev, "bf16")
+    da = torch.from_numpy(dd["alpha"]).to(dev)
+    db = torch.from_numpy(dd["beta"]).to(dev)
+    s0 = torch.from_numpy(dd["s0"]).to(dev)
+    B, Hd, dh = wd.B, wd.H, wd.dk
+    dy = torch.empty((nsteps, B, Hd, dh), dtype=torch.bfloat16, device=dev)
+    state = s0.clone()
+
+    def run_decode(states):
+        for s in range(nsteps):
+            gdn.gdn_decode_step(dq[s], dk_[s], dv_[s], da[s], db[s], states[s % len(states)],
+                                y=dy[s])
+
+    run_decode([state])          # warm-up pass over all steps
+    state.copy_(s0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run_decode([state])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1e3 / nsteps
+    # cache-defeating variant: four independent state sets (512 MiB) in rotation
+    states4 = [s0.clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    run_decode(states4)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    dec4_us = e2.elapsed_time(e3) * 1e3 / nsteps
+    dbytes = decode_bytes_per_head_step(dh) * B * Hd
+    gbs = dbytes / (dec_us * 1e-6) / 1e9
+    gbs4 = dbytes / (dec4_us * 1e-6) / 1e9
+    dsrc = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc",
+                        "gdn_decode.hip")
+    dtr = load_traffic("decode_bf16_B128_H16_d128", dsrc)
+    decode = {
+        "workload": wd.name, "steps": nsteps, "steps_per_s": round(1e6 / dec_us, 1),
+        "us_per_step": round(dec_us, 2), "tokens_per_s": round(B * 1e6 / dec_us, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if dtr is None else dtr["bytes_per_launch"],
+                     "algorithmic_bytes_per_launch": dbytes},
+        "rotating_4_states": {"us_per_step": round(dec4_us, 2),
+                              "steps_per_s": round(1e6 / dec4_us, 1),
+                              "achieved_GBs": round(gbs4, 1),
+                              "frac": round(gbs4 / PEAK_HBM_GBS, 4)},
+    }
+
+    # ------------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        threads = max(1, min(16, os.cpu_count() or 1))
+        units = nseq * H
+        use = min(threads, units)
+        c0 = time.perf_counter()
+        oracle.prefill(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None,
+                       threads=use, want_y=True, want_state=True)
+        csec = time.perf_counter() - c0
+        cpu = {"value": round(T / csec, 1), "unit": "tokens/s", "cores": use, "kind": "oracle",
+               "sample": "the whole prefill workload (B=4, H=16, T=4096, d=128), fp64 C "
+                         "oracle, %d threads, %.1f s" % (use, csec)}
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": H, "T": w.T, "d_k": d, "d_v": d,
+                   "chunk": CHUNK, "dv_tile": tile, "segment_chunks": seg,
+                   "parallelism": "single GPU"},
+        "prefill": {"ms_median": round(pre_med, 4), "ms_warm_back_to_back": round(warm_ms, 4),
+                    "tokens_per_s_warm": round(T / (warm_ms * 1e-3), 1),
+                    "wall_s_timed_loop_incl_flush": round(wall, 4)},
+        "roofline": roofline,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

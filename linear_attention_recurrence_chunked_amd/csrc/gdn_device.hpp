@@ -1,8 +1,9 @@
 // gdn_device.hpp -- device-side helpers shared by the gfx950 kernels of libgdn.
 //
 // bf16 is carried as raw uint16_t bit patterns in memory and as __bf16 vectors only where
-// an MFMA consumes it.  Conversions are written from the bf16 definition (the upper 16
-// bits of an IEEE binary32 word), rounding to nearest even on the way down.
+// an MFMA consumes it.  Widening uses the bf16 definition (the upper 16 bits of an IEEE
+// binary32 word); narrowing goes through the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32, round to nearest even).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,6 +12,8 @@
 namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -20,18 +23,6 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
-}
-
-// Round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
 // Element loads/stores for the two storage types.
@@ -45,7 +36,7 @@ template <> struct Elem<float> {
 template <> struct Elem<uint16_t> {
     static __device__ __forceinline__ float load(const uint16_t *p) { return bf16_to_f32(*p); }
     static __device__ __forceinline__ void store(uint16_t *p, float x) {
-        *p = (uint16_t)f32_to_bf16(x);
+        *(__bf16 *)p = (__bf16)x;
     }
 };
 
@@ -62,10 +53,7 @@ __device__ __forceinline__ f32x4 load4(const uint16_t *p) {
 }
 __device__ __forceinline__ void store4(float *p, f32x4 x) { *(f32x4 *)p = x; }
 __device__ __forceinline__ void store4(uint16_t *p, f32x4 x) {
-    u32x2 w;
-    w[0] = pack_bf16x2(x[0], x[1]);
-    w[1] = pack_bf16x2(x[2], x[3]);
-    *(u32x2 *)p = w;
+    *(bf16x4 *)p = __builtin_convertvector(x, bf16x4);
 }
 
 __device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, kWave); }

@@ -35,7 +35,7 @@
 namespace gdn {
 
 constexpr int kThreads = 256;
-constexpr float kLogAlphaFloor = -87.0f;   // log alpha clamp: keeps alpha = 0 finite
+constexpr float kLog2AlphaFloor = -126.0f;   // log2 alpha clamp: keeps alpha = 0 finite
 
 // ---------------------------------------------------------------------------------------
 // MFMA wrappers.  A "K-block" is 32 values of the contraction index.  Each lane holds 8 of
@@ -46,6 +46,17 @@ constexpr float kLogAlphaFloor = -87.0f;   // log alpha clamp: keeps alpha = 0 f
 // hardware sums them in.  The accumulator layout of every 16x16 MFMA is: lane holds column
 // (lane % 16), rows 4 (lane / 16) + 0..3.
 // ---------------------------------------------------------------------------------------
+// Drain after a chain of v_mfma_f32_16x16x4_f32 whose result is read by anything but the
+// next MFMA's accumulator input.  On gfx950 the wait states the compiler inserts before such
+// a read were measured too few for this instruction (stale accumulator values; results
+// correct once 32 wait states separate the chain from the read).
+__device__ __forceinline__ void mfma_f32_drain()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <typename OP> struct Mma;
 
 template <> struct Mma<uint16_t> {
@@ -57,19 +68,13 @@ template <> struct Mma<uint16_t> {
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ void put4(uint16_t *p, f32x4 x) {
-        u32x2 w;
-        w[0] = pack_bf16x2(x[0], x[1]);
-        w[1] = pack_bf16x2(x[2], x[3]);
-        *(u32x2 *)p = w;
+        *(bf16x4 *)p = __builtin_convertvector(x, bf16x4);
     }
     static __device__ __forceinline__ f32x4 get4(const uint16_t *p) { return load4(p); }
     static __device__ __forceinline__ frag from_f32(f32x4 lo, f32x4 hi) {
-        u32x4 w;
-        w[0] = pack_bf16x2(lo[0], lo[1]);
-        w[1] = pack_bf16x2(lo[2], lo[3]);
-        w[2] = pack_bf16x2(hi[0], hi[1]);
-        w[3] = pack_bf16x2(hi[2], hi[3]);
-        return __builtin_bit_cast(frag, w);
+        const bf16x4 l = __builtin_convertvector(lo, bf16x4);
+        const bf16x4 h = __builtin_convertvector(hi, bf16x4);
+        return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
     }
 };
 
@@ -90,6 +95,7 @@ template <> struct Mma<float> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+        mfma_f32_drain();
     }
     static __device__ __forceinline__ void put4(float *p, f32x4 x) { *(f32x4 *)p = x; }
     static __device__ __forceinline__ f32x4 get4(const float *p) { return *(const f32x4 *)p; }
@@ -108,6 +114,7 @@ template <> struct Quad<uint16_t> {
     static __device__ __forceinline__ Quad load(const uint16_t *p) { Quad q; q.w = *(const u32x2 *)p; return q; }
     static __device__ __forceinline__ Quad zero() { Quad q; q.w[0] = 0; q.w[1] = 0; return q; }
     __device__ __forceinline__ void store(uint16_t *p) const { *(u32x2 *)p = w; }
+    __device__ __forceinline__ void mask(unsigned m) { w[0] &= m; w[1] &= m; }
     // column j of a 4x4 block given as four row quads
     static __device__ __forceinline__ Quad column(const Quad *r, int j) {
         Quad o;
@@ -127,6 +134,9 @@ template <> struct Quad<float> {
     static __device__ __forceinline__ Quad load(const float *p) { Quad q; q.w = *(const f32x4 *)p; return q; }
     static __device__ __forceinline__ Quad zero() { Quad q; q.w = f32x4{0.f, 0.f, 0.f, 0.f}; return q; }
     __device__ __forceinline__ void store(float *p) const { *(f32x4 *)p = w; }
+    __device__ __forceinline__ void mask(unsigned m) {
+        w = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, w) & m);
+    }
     static __device__ __forceinline__ Quad column(const Quad *r, int j) {
         Quad o;
         o.w[0] = r[0].w[j];
@@ -138,36 +148,43 @@ template <> struct Quad<float> {
 };
 
 // ---------------------------------------------------------------------------------------
-// LDS carve-up.  Rows are padded by 16 bytes so that the 16-lane groups of a fragment load
-// fall on different banks.  Region R1 is time-shared by (i) the row-major Q and K tiles,
-// (ii) the fp32 solve buffers and (iii) the transposed R / U / scaled-U tiles.
+// LDS layout.  Operand tiles are stored unpadded with the 16-byte granules of each row
+// XOR-swizzled by s(row) = (row ^ row >> 3) & 7, so that a fragment load (eight consecutive
+// elements of 16 consecutive rows), a quad store from the accumulator layout (four
+// consecutive elements of 16 rows) and the transposing quad stores of the input tiles all
+// spread over distinct banks.  Regions are reused by liveness within a chunk:
+//   U1: K and Q, row major (phases a-b)   |  R^T, U^T, scaled U^T (phases c-f)
+//   U2: V^T (phases a-b)                  |  the four diagonal blocks of X (phases c-d)
 // ---------------------------------------------------------------------------------------
+template <typename OP, int W>
+__device__ __forceinline__ int swz(int row, int col)
+{
+    constexpr int E = (int)sizeof(OP);
+    const int b = col * E;
+    const int s = (row ^ (row >> 3)) & 7;
+    return row * (W * E) + (((b >> 4) ^ s) << 4) + (b & 15);
+}
+
 template <int DK, int DVT, typename OP>
 struct Lds {
     static constexpr int E = sizeof(OP);
-    static constexpr int LDK = DK + 16 / E;      // row length of [*, DK] tiles
-    static constexpr int LDT = kChunk + 16 / E;  // row length of [*, 64 tokens] tiles
-    static constexpr int LDA = kChunk + 4;       // fp32 solve rows
-    static constexpr int al(int x) { return (x + 15) & ~15; }
+    static constexpr int al(int x) { return (x + 255) & ~255; }
     static constexpr int mx(int a, int b) { return a > b ? a : b; }
-    static constexpr int szQK = 2 * kChunk * LDK * E;
-    static constexpr int szSolve = 2 * kChunk * LDA * 4 + 3 * 16 * 16 * 4;
-    static constexpr int szRU = 3 * DVT * LDT * E;
-    static constexpr int R1 = al(mx(szQK, mx(szSolve, szRU)));
-    static constexpr int oQ = 0;
-    static constexpr int oK = kChunk * LDK * E;
-    static constexpr int oA = 0;
-    static constexpr int oX = kChunk * LDA * 4;
-    static constexpr int oY = 2 * kChunk * LDA * 4;
-    static constexpr int oRt = 0;
-    static constexpr int oUt = DVT * LDT * E;
-    static constexpr int oUs = 2 * DVT * LDT * E;
-    static constexpr int oKt = R1;
-    static constexpr int oVt = al(oKt + DK * LDT * E);
-    static constexpr int oP = al(oVt + DVT * LDT * E);
-    static constexpr int oT = al(oP + kChunk * LDT * E);
-    static constexpr int oSt = al(oT + kChunk * LDT * E);
-    static constexpr int oG = al(oSt + DVT * LDK * E);
+    static constexpr int szRow = kChunk * DK * E;     // [64][DK]
+    static constexpr int szTr = DVT * kChunk * E;     // [DVT][64]
+    static constexpr int LDA = kChunk + 4;            // padded fp32 rows of the solve
+    static constexpr int LDX = 20;                    // padded rows of a diagonal X block
+    static constexpr int oK = 0, oQ = szRow;
+    static constexpr int oRt = 0, oUt = szTr, oUs = 2 * szTr;
+    static constexpr int U1 = al(mx(2 * szRow, 3 * szTr));
+    static constexpr int oVt = U1, oX = U1;
+    static constexpr int U2 = al(mx(szTr, 4 * 16 * LDX * 4));
+    static constexpr int oKt = U1 + U2;
+    static constexpr int oA = al(oKt + DK * kChunk * E);
+    static constexpr int oP = al(oA + kChunk * LDA * 4);
+    static constexpr int oT = al(oP + kChunk * kChunk * E);
+    static constexpr int oSt = al(oT + kChunk * kChunk * E);
+    static constexpr int oG = al(oSt + DVT * DK * E);
     static constexpr int oB = oG + kChunk * 4;
     static constexpr int total = oB + kChunk * 4;
 };
@@ -231,7 +248,38 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs &a, int n, long lon
 // The chunked scan.  MODE == kModeScan: start from S0 (or a segment start state), write y
 // and (for the last segment) the final state.  MODE == kModeAug: phase A of the segment
 // scan; no y; columns col0 >= d_v belong to the transition part (V = 0, start = identity).
+//
+// Per chunk, six barriers separate the phases:
+//   a  prefetched K, Q, V, gates -> LDS (K, Q row major; K, V transposed); log2 prefix of
+//      alpha; issue the global loads of the next chunk
+//   b  Gram tiles K K^T, K Q^T -> decay-masked A (fp32) and P; K S and S^T Q^T; R
+//   c  R -> LDS; diagonal 16 x 16 blocks of X = (I + A)^{-1} by forward substitution
+//   d  off-diagonal blocks of X on fp32 MFMA; T' = X diag(beta)
+//   e  U = T' R
+//   f  Y^T = S^T Q^T diag(gamma) + U^T P^T -> y; S = gamma_C S + K^T diag(gamma_C/gamma) U
 // ---------------------------------------------------------------------------------------
+// DPP move within a wave; lanes without a source (or outside row_mask) read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f32(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf,
+                                                      false));
+}
+
+template <typename OP, int W>
+__device__ __forceinline__ typename Mma<OP>::frag ldfrag(const unsigned char *base, int row,
+                                                        int k0)
+{
+    if constexpr (sizeof(OP) == 2) {
+        return *(const bf16x8 *)(base + swz<OP, W>(row, k0));
+    } else {
+        typename Mma<OP>::frag f;
+        f.lo = *(const f32x4 *)(base + swz<OP, W>(row, k0));
+        f.hi = *(const f32x4 *)(base + swz<OP, W>(row, k0 + 4));
+        return f;
+    }
+}
+
 template <int DK, int DVT, typename OP, int MODE>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
 {
@@ -243,26 +291,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     constexpr int MBS = DK / 64;          // 16-row blocks of S owned by each wave
     constexpr int DQ = DK / 4;            // quads per key row
     constexpr int VQ = DVT / 4;           // quads per value-tile row
-    constexpr int KBLK = (16 * DQ + kThreads - 1) / kThreads;   // 4x4 blocks per thread (q, k)
-    constexpr int VBLK = (16 * VQ + kThreads - 1) / kThreads;   // 4x4 blocks per thread (v)
-    constexpr bool kWantY = (MODE == kModeScan);
+    constexpr int KBLK = (16 * DQ + kThreads - 1) / kThreads;   // 4x4 blocks per thread
+    constexpr int VBLK = (16 * VQ + kThreads - 1) / kThreads;
+    constexpr bool kY = (MODE == kModeScan);
 
     __shared__ __align__(16) unsigned char smem[L::total];
-    OP *sQ = (OP *)(smem + L::oQ);
-    OP *sK = (OP *)(smem + L::oK);
-    float *sA = (float *)(smem + L::oA);
-    float *sX = (float *)(smem + L::oX);
-    float *sY = (float *)(smem + L::oY);
-    OP *sRt = (OP *)(smem + L::oRt);
-    OP *sUt = (OP *)(smem + L::oUt);
-    OP *sUs = (OP *)(smem + L::oUs);
-    OP *sKt = (OP *)(smem + L::oKt);
-    OP *sVt = (OP *)(smem + L::oVt);
-    OP *sP = (OP *)(smem + L::oP);
-    OP *sT = (OP *)(smem + L::oT);
-    OP *sSt = (OP *)(smem + L::oSt);
-    float *sG = (float *)(smem + L::oG);
-    float *sBeta = (float *)(smem + L::oB);
+    unsigned char *const bK = smem + L::oK;
+    unsigned char *const bQ = smem + L::oQ;
+    unsigned char *const bRt = smem + L::oRt;
+    unsigned char *const bUt = smem + L::oUt;
+    unsigned char *const bUs = smem + L::oUs;
+    unsigned char *const bVt = smem + L::oVt;
+    float *const sX = (float *)(smem + L::oX);
+    unsigned char *const bKt = smem + L::oKt;
+    float *const sA = (float *)(smem + L::oA);
+    unsigned char *const bP = smem + L::oP;
+    unsigned char *const bT = smem + L::oT;
+    unsigned char *const bSt = smem + L::oSt;
+    float *const sG = (float *)(smem + L::oG);
+    float *const sBeta = (float *)(smem + L::oB);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -312,7 +359,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     f32x4 S[MBS][NB];
     {
         const float *src = nullptr;
-        long long ld = DV;
         if (MODE == kModeScan) {
             if (job.seg == 0) {
                 if (a.s0) src = a.s0 + ((long long)job.n * H + job.h) * DK * DV + job.col0;
@@ -332,15 +378,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
                     const int col = nb * 16 + ln;
                     float x = 0.f;
                     if (mpart) x = (row == job.col0 - DV + col) ? 1.f : 0.f;
-                    else if (src) x = src[(long long)row * ld + col];
+                    else if (src) x = src[(long long)row * DV + col];
                     S[mb][nb][i] = x;
                 }
     }
 
-    // ---- global -> register prefetch of one chunk ----
+    // ---- global -> register prefetch of one chunk.  Rows past the end of the sequence are
+    //      clamped to its last row (no load is predicated); they are zeroed when the
+    //      registers are stored to LDS in the next iteration, so nothing here waits for the
+    //      loads to return.
     Q4 pk[KBLK][4], pq[KBLK][4], pv[VBLK][4];
-    float pa = 1.f;   // threads 0..63: alpha of token (tid); threads 64..127: beta of token
+    float pa = 1.f;   // threads 0..63: alpha of token (tid); threads 64..127: beta
     auto prefetch = [&](long long t0, int nvalid) {
+        const OP *ck = gk + (t0 * H + job.h) * (long long)DK;
+        const OP *cq = gq + (t0 * H + job.h) * (long long)DK;
 #pragma unroll
         for (int j = 0; j < KBLK; ++j) {
             const int b = tid + kThreads * j;
@@ -348,79 +399,84 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 4 * tq + i;
-                if (b < 16 * DQ && t < nvalid) {
-                    const long long off = ((t0 + t) * H + job.h) * (long long)DK + 4 * dq;
-                    pk[j][i] = Q4::load(gk + off);
-                    if (kWantY) pq[j][i] = Q4::load(gq + off);
-                } else {
-                    pk[j][i] = Q4::zero();
-                    if (kWantY) pq[j][i] = Q4::zero();
-                }
+                const int tc = t < nvalid ? t : nvalid - 1;
+                const int off = tc * H * DK + 4 * dq;
+                pk[j][i] = Q4::load(ck + off);
+                if (kY) pq[j][i] = Q4::load(cq + off);
             }
         }
+        // V tile (every thread loads; threads past the 16 x VQ blocks re-read a valid block
+        // and never store it).  The transition columns of phase A have V = 0 (uniform per
+        // workgroup).
+        if (!mpart) {
+            const OP *cv = gv + (t0 * H + job.h) * (long long)DV + job.col0;
 #pragma unroll
-        for (int j = 0; j < VBLK; ++j) {
-            const int b = tid + kThreads * j;
-            const int dq = b % VQ, tq = b / VQ;
+            for (int j = 0; j < VBLK; ++j) {
+                const int b = (tid + kThreads * j) % (16 * VQ);
+                const int dq = b % VQ, tq = b / VQ;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * tq + i;
-                if (!mpart && b < 16 * VQ && t < nvalid) {
-                    const long long off =
-                        ((t0 + t) * H + job.h) * (long long)DV + job.col0 + 4 * dq;
-                    pv[j][i] = Q4::load(gv + off);
-                } else {
-                    pv[j][i] = Q4::zero();
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 4 * tq + i;
+                    const int tc = t < nvalid ? t : nvalid - 1;
+                    pv[j][i] = Q4::load(cv + tc * H * DV + 4 * dq);
                 }
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < VBLK; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[j][i] = Q4::zero();
         }
-        if (tid < 64) {
-            pa = (tid < nvalid) ? a.alpha[(t0 + tid) * H + job.h] : 1.f;
-        } else if (tid < 128) {
-            const int t = tid - 64;
-            pa = (t < nvalid) ? a.beta[(t0 + t) * H + job.h] : 0.f;
+        // gates: lanes of wave 0 read alpha, every other lane beta, of token (lane)
+        {
+            const int t = lane;
+            const int tc = t < nvalid ? t : nvalid - 1;
+            const float *g = (tid < 64) ? a.alpha : a.beta;
+            pa = g[(t0 + tc) * H + job.h];
         }
     };
 
-    // S -> LDS (transposed bf16/fp32 copy used as the B operand of [K; Q] S)
+    // S -> LDS (transposed copy, the operand of K S and S^T Q^T)
     auto store_state_lds = [&]() {
 #pragma unroll
         for (int mb = 0; mb < MBS; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int row = (wave * MBS + mb) * 16 + 4 * lg;
-                M::put4(sSt + (nb * 16 + ln) * L::LDK + row, S[mb][nb]);
-            }
+            for (int nb = 0; nb < NB; ++nb)
+                M::put4((OP *)(bSt + swz<OP, DK>(nb * 16 + ln, (wave * MBS + mb) * 16 + 4 * lg)),
+                        S[mb][nb]);
     };
     store_state_lds();
 
     const int nchunks = (job.len + kChunk - 1) / kChunk;
     if (nchunks > 0) prefetch(job.tok0, job.len < kChunk ? job.len : kChunk);
 
-    // Gram tile pairs (t-block, i-block) with i-block <= t-block, spread over the waves
-    constexpr int kPairs = 10;
+    constexpr int kPairs = 10;           // Gram tile pairs (t-block, i-block), i-block <= t-block
     constexpr int kPairsPerWave = 3;
+    const int trow = wave * 16 + 4 * lg;   // first token row of this lane in the acc layout
 
     for (int c = 0; c < nchunks; ++c) {
         const long long t0 = job.tok0 + (long long)c * kChunk;
         const int nvalid = (job.len - c * kChunk) < kChunk ? (job.len - c * kChunk) : kChunk;
         __syncthreads();   // the previous chunk is done with every LDS buffer
 
-        // ---- registers -> LDS: Q, K row major; K, V transposed; g; beta ----
+        // ---- a: registers -> LDS (rows past the end of the sequence become zeros) ----
 #pragma unroll
         for (int j = 0; j < KBLK; ++j) {
             const int b = tid + kThreads * j;
-            if (b < 16 * DQ) {
-                const int dq = b % DQ, tq = b / DQ;
+            const int dq = b % DQ, tq = b / DQ;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pk[j][i].store(sK + (4 * tq + i) * L::LDK + 4 * dq);
-                    if (kWantY) pq[j][i].store(sQ + (4 * tq + i) * L::LDK + 4 * dq);
+            for (int i = 0; i < 4; ++i) {
+                const unsigned keep = (4 * tq + i < nvalid) ? 0xffffffffu : 0u;
+                pk[j][i].mask(keep);
+                pk[j][i].store((OP *)(bK + swz<OP, DK>(4 * tq + i, 4 * dq)));
+                if (kY) {
+                    pq[j][i].mask(keep);
+                    pq[j][i].store((OP *)(bQ + swz<OP, DK>(4 * tq + i, 4 * dq)));
                 }
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    Q4::column(pk[j], jj).store(sKt + (4 * dq + jj) * L::LDT + 4 * tq);
             }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                Q4::column(pk[j], jj).store((OP *)(bKt + swz<OP, kChunk>(4 * dq + jj, 4 * tq)));
         }
 #pragma unroll
         for (int j = 0; j < VBLK; ++j) {
@@ -428,21 +484,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             if (b < 16 * VQ) {
                 const int dq = b % VQ, tq = b / VQ;
 #pragma unroll
+                for (int i = 0; i < 4; ++i) pv[j][i].mask((4 * tq + i < nvalid) ? 0xffffffffu : 0u);
+#pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    Q4::column(pv[j], jj).store(sVt + (4 * dq + jj) * L::LDT + 4 * tq);
+                    Q4::column(pv[j], jj).store((OP *)(bVt + swz<OP, kChunk>(4 * dq + jj, 4 * tq)));
             }
         }
         if (wave == 0) {
-            // inclusive prefix sum of log alpha over the chunk (lane = token)
-            float x = fmaxf(logf(pa), kLogAlphaFloor);
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
+            // inclusive prefix sum of log2 alpha over the chunk (lane = token): Hillis-Steele
+            // within each 16-lane row by DPP row shifts, then across rows by row broadcasts
+            float x = lane < nvalid ? fmaxf(__builtin_amdgcn_logf(pa), kLog2AlphaFloor) : 0.f;
+            x += dpp_f32<0x111, 0xf>(x);   // row_shr:1
+            x += dpp_f32<0x112, 0xf>(x);   // row_shr:2
+            x += dpp_f32<0x114, 0xf>(x);   // row_shr:4
+            x += dpp_f32<0x118, 0xf>(x);   // row_shr:8
+            x += dpp_f32<0x142, 0xa>(x);   // row_bcast:15 -> rows 1, 3
+            x += dpp_f32<0x143, 0xc>(x);   // row_bcast:31 -> rows 2, 3
             sG[lane] = x;
         } else if (wave == 1) {
-            sBeta[lane] = pa;
+            sBeta[lane] = lane < nvalid ? pa : 0.f;
         }
         if (c + 1 < nchunks) {
             const int nv = (job.len - (c + 1) * kChunk) < kChunk ? (job.len - (c + 1) * kChunk)
@@ -451,162 +511,179 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
         }
         __syncthreads();
 
-        // ---- a1/a4: Gram tiles (K K^T and K Q^T, lower pairs), and [K; Q] S ----
-        f32x4 accG[kPairsPerWave], accP[kPairsPerWave];
+        // ---- b: Gram tiles -> A, P (masked by the decay).  Pair p = (t-block, i-block):
+        //      0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3);
+        //      wave w takes pairs w, w + 4 and (waves 0, 1) w + 8.  A diagonal tile also
+        //      gets its strictly lower part mirrored into its upper half (column access
+        //      for the substitution of phase c).
+        auto gram_pair = [&](int p) {
+            const int tb = p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3));
+            const int ib = p - tb * (tb + 1) / 2;
+            const int t = tb * 16 + ln;
+            const float gt = sG[t];
+            const float bt_ = sBeta[t];
+            const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+            f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pi = 0; pi < kPairsPerWave; ++pi) {
-            const int p = wave + 4 * pi;
-            accG[pi] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accP[pi] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (p < kPairs) {
-                // pair p -> (tb, ib): 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) ...
-                const int tb = p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3));
-                const int ib = p - tb * (tb + 1) / 2;
-#pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) {
-                    const auto ai = M::load(sK + (ib * 16 + ln) * L::LDK + kb * 32 + 8 * lg);
-                    const auto bt = M::load(sK + (tb * 16 + ln) * L::LDK + kb * 32 + 8 * lg);
-                    M::mma(accG[pi], ai, bt);
-                    if (kWantY) {
-                        const auto bq = M::load(sQ + (tb * 16 + ln) * L::LDK + kb * 32 + 8 * lg);
-                        M::mma(accP[pi], ai, bq);
-                    }
+            for (int kb = 0; kb < KBD; ++kb) {
+                const auto ai = ldfrag<OP, DK>(bK, ib * 16 + ln, kb * 32 + 8 * lg);
+                const auto bt = ldfrag<OP, DK>(bK, tb * 16 + ln, kb * 32 + 8 * lg);
+                M::mma(accG, ai, bt);
+                if (kY) {
+                    const auto bq = ldfrag<OP, DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg);
+                    M::mma(accP, ai, bq);
                 }
             }
-        }
-        f32x4 accKS[NB], accQS[NB];
+            // accG[r] = k_i . k_t and accP[r] = k_i . q_t for i = ib*16 + 4lg + r
+            f32x4 av, pv4;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            accKS[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accQS[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) {
-            const auto ak = M::load(sK + (wave * 16 + ln) * L::LDK + kb * 32 + 8 * lg);
-            typename M::frag aq;
-            if (kWantY) aq = M::load(sQ + (wave * 16 + ln) * L::LDK + kb * 32 + 8 * lg);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const auto bs = M::load(sSt + (nb * 16 + ln) * L::LDK + kb * 32 + 8 * lg);
-                M::mma(accKS[nb], ak, bs);
-                if (kWantY) M::mma(accQS[nb], aq, bs);
+            for (int r = 0; r < 4; ++r) {
+                const int i = ib * 16 + 4 * lg + r;
+                const float dec = (i <= t) ? __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+                av[r] = (i < t) ? bt_ * accG[r] * dec : 0.f;
+                pv4[r] = accP[r] * dec;
             }
-        }
-        __syncthreads();   // Q and K row-major tiles are dead; R1 becomes the solve area
-
-        // ---- decay masks: A (fp32, strictly lower, rows scaled by beta) and P ----
-#pragma unroll
-        for (int pi = 0; pi < kPairsPerWave; ++pi) {
-            const int p = wave + 4 * pi;
-            if (p < kPairs) {
-                const int tb = p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3));
-                const int ib = p - tb * (tb + 1) / 2;
-                const int t = tb * 16 + ln;
-                const float gt = sG[t];
-                const float bt = sBeta[t];
-                f32x4 av, pv4;
+            *(f32x4 *)(sA + t * L::LDA + ib * 16 + 4 * lg) = av;
+            if (tb == ib) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = ib * 16 + 4 * lg + r;
-                    const float dec = (i <= t) ? expf(gt - sG[i]) : 0.f;
-                    av[r] = (i < t) ? bt * accG[pi][r] * dec : 0.f;
-                    pv4[r] = accP[pi][r] * dec;
+                    if (i < t) sA[i * L::LDA + t] = av[r];
                 }
-                *(f32x4 *)(sA + t * L::LDA + ib * 16 + 4 * lg) = av;
-                if (kWantY) M::put4(sP + t * L::LDT + ib * 16 + 4 * lg, pv4);
             }
+            if (kY) M::put4((OP *)(bP + swz<OP, kChunk>(t, ib * 16 + 4 * lg)), pv4);
+        };
+        gram_pair(wave);
+        gram_pair(wave + 4);
+        if (wave < 2) gram_pair(wave + 8);
+        // P blocks (0,1) and (2,3) lie inside the diagonal 32-wide K-blocks of U^T P^T
+        if (kY && (wave == 0 || wave == 2)) {
+            M::put4((OP *)(bP + swz<OP, kChunk>(wave * 16 + ln, wave * 16 + 16 + 4 * lg)),
+                    f32x4{0.f, 0.f, 0.f, 0.f});
         }
-        // upper tiles (i-block > t-block) are zero
-#pragma unroll
-        for (int ui = 0; ui < 2; ++ui) {
-            const int u = wave + 4 * ui;
-            if (u < 6) {
-                // 0:(0,1) 1:(0,2) 2:(0,3) 3:(1,2) 4:(1,3) 5:(2,3)
-                const int tb = u < 3 ? 0 : (u < 5 ? 1 : 2);
-                const int ib = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-                const int t = tb * 16 + ln;
-                *(f32x4 *)(sA + t * L::LDA + ib * 16 + 4 * lg) = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (kWantY) M::put4(sP + t * L::LDT + ib * 16 + 4 * lg, f32x4{0.f, 0.f, 0.f, 0.f});
-            }
-        }
-        __syncthreads();
-
-        // ---- a2: X = (I + A)^{-1}, blocked by 16 ----
-        {
-            // diagonal blocks: wave w inverts block w by forward substitution, one column
-            // per lane (the four 16-lane groups compute the same columns; group 0 stores)
-            const int d0 = wave * 16;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-                for (int cc = 0; cc < r; ++cc) acc -= sA[(d0 + r) * L::LDA + d0 + cc] * x[cc];
-                x[r] = acc;
-            }
-            if (lg == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sX[(d0 + r) * L::LDA + d0 + ln] = x[r];
-            }
-        }
-        __syncthreads();
-        // off-diagonal blocks by distance: X_ij = -X_ii * sum_{m in blocks j..i-1} A_im X_mj
-        {
-            const int r = tid >> 4, cc = tid & 15;
-#pragma unroll
-            for (int dist = 1; dist <= 3; ++dist) {
-                const int npairs = 4 - dist;
-                // Y_ij[r][cc] = sum_m A[16i + r][m] X[m][16j + cc]
-                for (int pj = 0; pj < npairs; ++pj) {
-                    const int j = pj, i = pj + dist;
-                    float acc = 0.f;
-                    for (int m = 16 * j; m < 16 * i; ++m)
-                        acc += sA[(16 * i + r) * L::LDA + m] * sX[m * L::LDA + 16 * j + cc];
-                    sY[(pj * 16 + r) * 16 + cc] = acc;
-                }
-                __syncthreads();
-                for (int pj = 0; pj < npairs; ++pj) {
-                    const int j = pj, i = pj + dist;
-                    float acc = 0.f;
-#pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        acc += sX[(16 * i + r) * L::LDA + 16 * i + m] * sY[(pj * 16 + m) * 16 + cc];
-                    sX[(16 * i + r) * L::LDA + 16 * j + cc] = -acc;
-                }
-                __syncthreads();
-            }
-        }
-        // T' = X diag(beta) (unit diagonal of X -> beta_t), lower triangle only
-        {
-            const int t = tid >> 2;
-            const int i0 = (tid & 3) * 16;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                f32x4 tv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = i0 + 4 * q4 + e;
-                    tv[e] = (i < t) ? sX[t * L::LDA + i] * sBeta[i] : (i == t ? sBeta[t] : 0.f);
-                }
-                M::put4(sT + t * L::LDT + i0 + 4 * q4, tv);
-            }
-        }
-        __syncthreads();   // solve buffers are dead; R1 becomes the R / U area
-
-        // ---- R = V - diag(gamma) K S   (wave w: token rows 16w .. 16w + 15) ----
-        const int trow = wave * 16 + 4 * lg;
-        f32x4 gam;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gam[r] = expf(sG[trow + r]);
+        // ---- b: K S (rows 16w..) and S^T Q^T (tokens 16w..) ----
+        f32x4 accKS[NB], accYt[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int col = nb * 16 + ln;
-            const f32x4 vv = M::get4(sVt + col * L::LDT + trow);
-            M::put4(sRt + col * L::LDT + trow, vv - gam * accKS[nb]);
+            accKS[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accYt[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            const auto ak = ldfrag<OP, DK>(bK, wave * 16 + ln, kb * 32 + 8 * lg);
+            typename M::frag bq;
+            if (kY) bq = ldfrag<OP, DK>(bQ, wave * 16 + ln, kb * 32 + 8 * lg);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const auto bs = ldfrag<OP, DK>(bSt, nb * 16 + ln, kb * 32 + 8 * lg);
+                M::mma(accKS[nb], ak, bs);
+                if (kY) M::mma(accYt[nb], bs, bq);
+            }
+        }
+        // ---- b: R = V - diag(gamma) K S   (wave w: token rows 16w .. 16w + 15) ----
+        f32x4 gam;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gam[r] = __builtin_amdgcn_exp2f(sG[trow + r]);
+        f32x4 R[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const f32x4 vv = M::get4((const OP *)(bVt + swz<OP, kChunk>(nb * 16 + ln, trow)));
+            R[nb] = vv - gam * accKS[nb];
+        }
+        __syncthreads();   // K, Q row-major tiles and V^T are dead
+
+        // ---- c: R -> LDS; diagonal blocks of X = (I + A)^{-1} ----
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            M::put4((OP *)(bRt + swz<OP, kChunk>(nb * 16 + ln, trow)), R[nb]);
+        // wave w inverts diagonal block w by forward substitution, one column per lane (the
+        // four 16-lane groups compute the same columns).  Each lane then keeps rows
+        // 4 lg .. 4 lg + 3 of its column: the accumulator layout of that block.
+        f32x4 xcol[4];
+        {
+            const int d0 = wave * 16;
+            // right-looking: once x[c] is final, subtract its column from the rows below;
+            // row c of the block's upper half holds A[r][c] for r > c (mirrored in phase b)
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
+#pragma unroll
+            for (int c = 0; c < 15; ++c) {
+                const float *col = sA + (d0 + c) * L::LDA + d0;
+#pragma unroll
+                for (int q4 = (c + 1) / 4; q4 < 4; ++q4) {
+                    const f32x4 a4 = *(const f32x4 *)(col + 4 * q4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q4 + e > c) x[4 * q4 + e] -= a4[e] * x[c];
+                }
+            }
+            f32x4 mine;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mine[i] = lg == 0 ? x[i] : (lg == 1 ? x[4 + i] : (lg == 2 ? x[8 + i] : x[12 + i]));
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xcol[m] = (m == wave) ? mine : f32x4{0.f, 0.f, 0.f, 0.f};
+            // row-major copy of the block (an MFMA A operand for the other block columns)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sX[(d0 + 4 * lg + i) * L::LDX + ln] = mine[i];
+            const float bcol = sBeta[d0 + ln];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                Elem<OP>::store((OP *)(bT + swz<OP, kChunk>(d0 + 4 * lg + i, d0 + ln)),
+                                mine[i] * bcol);
+            // zero the blocks of T' that the K-blocks of U = T' R read above the diagonal
+            if (wave == 0 || wave == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Elem<OP>::store((OP *)(bT + swz<OP, kChunk>(d0 + 4 * lg + i, d0 + 16 + ln)),
+                                    0.f);
+            }
         }
         __syncthreads();
 
-        // ---- U = T' R (lower triangular: K-blocks up to the diagonal) ----
+        // ---- d: wave j walks down block column j: X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj.
+        //      Every product runs on v_mfma_f32_16x16x4_f32; the column's blocks stay in the
+        //      accumulator layout, which is the B-operand layout of the next product
+        //      (contraction index 4 lg + s in step s).
+        {
+            const int j = wave;
+            const float bcol = sBeta[16 * j + ln];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) {
+                if (i > j) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < 3; ++m) {
+                        if (m >= j && m < i) {
+                            const f32x4 a4 = *(const f32x4 *)(sA + (16 * i + ln) * L::LDA +
+                                                              16 * m + 4 * lg);
+                            const f32x4 b4 = xcol[m];
+#pragma unroll
+                            for (int st = 0; st < 4; ++st)
+                                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[st], b4[st], acc,
+                                                                           0, 0, 0);
+                        }
+                    }
+                    mfma_f32_drain();
+                    const f32x4 xi = *(const f32x4 *)(sX + (16 * i + ln) * L::LDX + 4 * lg);
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st)
+                        z = __builtin_amdgcn_mfma_f32_16x16x4f32(xi[st], acc[st], z, 0, 0, 0);
+                    mfma_f32_drain();
+                    xcol[i] = -z;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Elem<OP>::store((OP *)(bT + swz<OP, kChunk>(16 * i + 4 * lg + r,
+                                                                    16 * j + ln)),
+                                        -z[r] * bcol);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- e: U = T' R (lower triangular: K-blocks up to the diagonal) ----
         const float gC = sG[kChunk - 1];
         f32x4 accU[NB];
 #pragma unroll
@@ -614,56 +691,51 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (kb <= (wave >> 1)) {
-                const auto at = M::load(sT + (wave * 16 + ln) * L::LDT + kb * 32 + 8 * lg);
+                const auto at = ldfrag<OP, kChunk>(bT, wave * 16 + ln, kb * 32 + 8 * lg);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const auto br = M::load(sRt + (nb * 16 + ln) * L::LDT + kb * 32 + 8 * lg);
+                    const auto br = ldfrag<OP, kChunk>(bRt, nb * 16 + ln, kb * 32 + 8 * lg);
                     M::mma(accU[nb], at, br);
                 }
             }
         }
         f32x4 tail;   // gamma_C / gamma_t
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tail[r] = expf(gC - sG[trow + r]);
+        for (int r = 0; r < 4; ++r) tail[r] = __builtin_amdgcn_exp2f(gC - sG[trow + r]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int col = nb * 16 + ln;
-            if (kWantY) M::put4(sUt + col * L::LDT + trow, accU[nb]);
-            M::put4(sUs + col * L::LDT + trow, accU[nb] * tail);
+            if (kY) M::put4((OP *)(bUt + swz<OP, kChunk>(nb * 16 + ln, trow)), accU[nb]);
+            M::put4((OP *)(bUs + swz<OP, kChunk>(nb * 16 + ln, trow)), accU[nb] * tail);
         }
         __syncthreads();
 
-        // ---- Y = diag(gamma) Q S + P U ----
-        if (kWantY) {
-            f32x4 accY[NB];
+        // ---- f: Y^T = S^T Q^T diag(gamma) + U^T P^T (tokens 16w .. 16w + 15) ----
+        if (kY) {
+            const float gtok = __builtin_amdgcn_exp2f(sG[wave * 16 + ln]);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) accY[nb] = gam * accQS[nb];
+            for (int nb = 0; nb < NB; ++nb) accYt[nb] *= gtok;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb <= (wave >> 1)) {
-                    const auto ap = M::load(sP + (wave * 16 + ln) * L::LDT + kb * 32 + 8 * lg);
+                    const auto bp = ldfrag<OP, kChunk>(bP, wave * 16 + ln, kb * 32 + 8 * lg);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        const auto bu = M::load(sUt + (nb * 16 + ln) * L::LDT + kb * 32 + 8 * lg);
-                        M::mma(accY[nb], ap, bu);
+                        const auto au = ldfrag<OP, kChunk>(bUt, nb * 16 + ln, kb * 32 + 8 * lg);
+                        M::mma(accYt[nb], au, bp);
                     }
                 }
             }
-            OP *gy = (OP *)a.y;
+            // lane (token 16w + ln) holds columns 4 lg .. 4 lg + 3 of each 16-column block
+            const int t = wave * 16 + ln;
+            if (t < nvalid) {
+                OP *gy = (OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + job.col0 + 4 * lg;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = trow + r;
-                    if (t < nvalid)
-                        Elem<OP>::store(gy + ((t0 + t) * H + job.h) * (long long)DV + job.col0 +
-                                            nb * 16 + ln,
-                                        accY[nb][r]);
-                }
+                for (int nb = 0; nb < NB; ++nb) store4(gy + nb * 16, accYt[nb]);
+            }
         }
 
-        // ---- S = gamma_C S + (diag(gamma_C / gamma) K)^T U ----
-        const float gamC = expf(gC);
+        // ---- f: S = gamma_C S + (diag(gamma_C / gamma) K)^T U ----
+        const float gamC = __builtin_amdgcn_exp2f(gC);
 #pragma unroll
         for (int mb = 0; mb < MBS; ++mb) {
             const int drow = (wave * MBS + mb) * 16;
@@ -671,10 +743,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             for (int nb = 0; nb < NB; ++nb) S[mb][nb] *= gamC;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const auto ak = M::load(sKt + (drow + ln) * L::LDT + kb * 32 + 8 * lg);
+                const auto ak = ldfrag<OP, kChunk>(bKt, drow + ln, kb * 32 + 8 * lg);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const auto bu = M::load(sUs + (nb * 16 + ln) * L::LDT + kb * 32 + 8 * lg);
+                    const auto bu = ldfrag<OP, kChunk>(bUs, nb * 16 + ln, kb * 32 + 8 * lg);
                     M::mma(S[mb][nb], ak, bu);
                 }
             }
@@ -904,13 +976,30 @@ static hipError_t dispatch_dk_dvt(const PrefillArgs &args, const PrefillPlan &pl
     return hipErrorInvalidValue;
 }
 
-// Tiles each dtype supports (LDS budget): bf16 16..128, fp32 16..64.
+// Column tiles whose kernel fits the 160 KiB of LDS of a gfx950 CU.
+template <typename OP, int DK>
+static constexpr bool fits(int t)
+{
+    return t == 16    ? Lds<DK, 16, OP>::total <= 160 * 1024
+           : t == 32  ? Lds<DK, 32, OP>::total <= 160 * 1024
+           : t == 64  ? Lds<DK, 64, OP>::total <= 160 * 1024
+           : t == 128 ? Lds<DK, 128, OP>::total <= 160 * 1024
+                      : false;
+}
+
 static bool tile_ok(int dtype, int dk, int dv, int t)
 {
     if (t != 16 && t != 32 && t != 64 && t != 128) return false;
     if (dv % t != 0) return false;
-    if (dtype == kDtypeF32 && (t > 64 || (dk == 128 && t > 32))) return false;
-    return true;
+    if (dtype == kDtypeF32) return dk == 128 ? fits<float, 128>(t) : fits<float, 64>(t);
+    return dk == 128 ? fits<uint16_t, 128>(t) : fits<uint16_t, 64>(t);
+}
+
+static int largest_tile(int dtype, int dk, int dv)
+{
+    for (int t = 128; t >= 16; t >>= 1)
+        if (tile_ok(dtype, dk, dv, t)) return t;
+    return 0;
 }
 
 bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype,
@@ -921,9 +1010,8 @@ bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype
     int tile = dv_tile_req;
     const long long chains = (long long)num_seqs * H;
     if (tile == 0) {
-        tile = (dtype == kDtypeF32) ? (dk == 128 ? 32 : 64) : dv;
+        tile = largest_tile(dtype, dk, dv);
         while (tile > 32 && chains * (dv / tile) < 512) tile >>= 1;
-        if (!tile_ok(dtype, dk, dv, tile)) tile = 32;
     }
     if (!tile_ok(dtype, dk, dv, tile)) return false;
     // Segments: split sequences when the chains alone cannot fill the chip and the average

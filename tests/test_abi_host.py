@@ -93,6 +93,7 @@ def prefill(lib, **kw):
     (dict(dt=5), gdn.GDN_ERR_UNSUPPORTED),
     (dict(tile=48), gdn.GDN_ERR_UNSUPPORTED),
     (dict(dt=0, tile=128), gdn.GDN_ERR_UNSUPPORTED),      # fp32 tile over the LDS budget
+    (dict(dt=0, tile=32), gdn.GDN_ERR_UNSUPPORTED),       # fp32, d_k = 128: 16 columns only
     (dict(seg=-2), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(k=2 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),    # misaligned (bf16 quad = 8 B)
     (dict(dt=0, k=2 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),   # fp32 quad = 16 B

@@ -39,8 +39,7 @@ def test_tiny_fp32_workload(dev, oracle_lib, tile):
 def test_ragged_lengths(dev, oracle_lib, dtype, d):
     lengths = [1, 63, 64, 65, 0, 127, 200]
     inp = _inp(lengths, H=3, d=d, dtype=dtype, seed=11)
-    tile = 32 if dtype == "f32" else 0
-    check_prefill(inp, dev, oracle_lib, dv_tile=tile, label="ragged")
+    check_prefill(inp, dev, oracle_lib, label="ragged")
 
 
 @pytest.mark.parametrize("tile", [16, 32, 64, 128])
@@ -78,7 +77,7 @@ def test_strong_decay_fp32(dev, oracle_lib):
 def test_segmented_scan(dev, oracle_lib, seg, dtype):
     lengths = [500, 64, 0, 129, 1000, 65]
     inp = _inp(lengths, H=2, dtype=dtype, seed=16 + seg, alpha=(3.0, 1.0))
-    tile = 32 if dtype == "f32" else 64
+    tile = 16 if dtype == "f32" else 64
     check_prefill(inp, dev, oracle_lib, dv_tile=tile, segment_chunks=seg, label="segmented")
 
 
