@@ -62,6 +62,28 @@ def load_traffic(kernel_key: str, source: str):
     return ent
 
 
+def profile_run(torch, gdn, wl, dev):
+    """Three prefill launches, three decode steps and a 1 GiB copy, nothing timed."""
+    inp = wl.workload_inputs(wl.PREFILL)
+    q, k, v = (wl.to_torch(inp[n], dev, "bf16") for n in ("q", "k", "v"))
+    a = torch.from_numpy(inp["alpha"]).to(dev)
+    b = torch.from_numpy(inp["beta"]).to(dev)
+    for _ in range(3):
+        gdn.gdn_prefill(q, k, v, a, b, num_seqs=wl.PREFILL.B)
+    d = wl.decode_inputs(wl.DECODE, steps=3)
+    state = torch.from_numpy(d["s0"]).to(dev)
+    for s in range(3):
+        gdn.gdn_decode_step(wl.to_torch(d["q"][s], dev, "bf16"), wl.to_torch(d["k"][s], dev, "bf16"),
+                            wl.to_torch(d["v"][s], dev, "bf16"), torch.from_numpy(d["alpha"][s]).to(dev),
+                            torch.from_numpy(d["beta"][s]).to(dev), state)
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile run done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,6 +92,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3 counter passes: 3 prefill launches, 3 decode "
+                         "steps and a plain 1 GiB device copy (the counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -85,6 +110,9 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     gdn.load()
+    if args.profile:
+        profile_run(torch, gdn, wl, dev)
+        return
 
     # ------------------------------------------------------------------ prefill
     w = wl.PREFILL
