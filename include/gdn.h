@@ -31,8 +31,9 @@
  * buffers (cu_seqlens contents, gate ranges, NaNs) are preconditions that are not checked.
  *
  * Supported shapes: d_k, d_v in {64, 128}; any H >= 1; any lengths (including 0).
- * Alignment: q, k, v and y to four elements (8 bytes for bf16, 16 for fp32); states and
- * the workspace to 16 bytes; alpha, beta and cu_seqlens to 4 bytes.
+ * Alignment: q, k, v, y, the states and the workspace to 16 bytes (the kernels move these
+ * in 16-byte units); alpha, beta and cu_seqlens to 4 bytes.  Rows of one token are
+ * contiguous, so slicing whole tokens off an aligned tensor keeps the alignment.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -65,9 +66,11 @@ const char *gdn_version(void);
 
 /*
  * Bytes of device workspace gdn_prefill needs for this problem (a pure function of the
- * arguments; 0 on invalid arguments).  The workspace holds the chunk/segment table and,
- * for long sequences, the per-segment transition matrices and start states of the
- * segment-parallel scan.
+ * arguments; 0 on invalid arguments).  The workspace holds, for bf16 inputs, one 16640-byte
+ * record per (64-token chunk, head) (the chunk's inverted triangular system, its decay-masked
+ * Q K^T block and its log-decay prefix, (total_T / 64 + num_seqs) * H records in all) and,
+ * for long sequences, the segment table, per-segment transition matrices and start states
+ * of the segment-parallel scan.  fp32 inputs without segments need none.
  */
 size_t gdn_prefill_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H,
                                    int32_t d_k, int32_t d_v, int32_t dtype);

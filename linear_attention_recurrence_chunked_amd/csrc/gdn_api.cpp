@@ -65,7 +65,7 @@ size_t gdn_prefill_workspace_bytes_ex(int32_t num_seqs, int64_t total_T, int32_t
     gdn::PrefillPlan plan;
     if (!plan_for(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile, segment_chunks, &plan))
         return 0;
-    return plan.ws_table + plan.ws_seg;
+    return plan.ws_table + plan.ws_seg + plan.ws_prep;
 }
 
 size_t gdn_prefill_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
@@ -103,11 +103,10 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     if (!cu_seqlens && total_T % num_seqs != 0) return GDN_ERR_INVALID_ARGUMENT;
     if (total_T > 0 && (!q || !k || !v || !alpha || !beta || !y))
         return GDN_ERR_INVALID_ARGUMENT;
-    // q, k, v, y: four elements; states and workspace: 16 bytes; gates, cu_seqlens: 4 bytes
-    const uintptr_t quad = 4 * esize(dtype);
+    // q, k, v, y, states, workspace: 16 bytes; gates, cu_seqlens: 4 bytes
     const void *quads[] = {q, k, v, y};
     for (const void *p : quads)
-        if (p && !aligned(p, quad)) return GDN_ERR_INVALID_ARGUMENT;
+        if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARGUMENT;
     const void *vec[] = {initial_state, final_state, workspace};
     for (const void *p : vec)
         if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARGUMENT;
@@ -124,7 +123,7 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     if (!gdn::make_plan(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile,
                         in_place ? -1 : segment_chunks, &plan))
         return dv_tile != 0 ? GDN_ERR_UNSUPPORTED : GDN_ERR_INVALID_ARGUMENT;
-    const size_t need = plan.ws_table + plan.ws_seg;
+    const size_t need = plan.ws_table + plan.ws_seg + plan.ws_prep;
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE_TOO_SMALL;
 
     // aliasing: outputs may not overlap inputs (final_state == initial_state is allowed)
@@ -191,8 +190,7 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     if (st != GDN_OK) return st;
     if (B == 0) return GDN_OK;
     if (!q || !k || !v || !alpha || !beta || !state || !y) return GDN_ERR_INVALID_ARGUMENT;
-    const uintptr_t quad = 4 * esize(dtype);
-    if (!aligned(q, quad) || !aligned(k, quad) || !aligned(v, quad) || !aligned(y, quad) ||
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(y, 16) ||
         !aligned(state, 16) || !aligned(alpha, 4) || !aligned(beta, 4))
         return GDN_ERR_INVALID_ARGUMENT;
     const size_t e = esize(dtype);

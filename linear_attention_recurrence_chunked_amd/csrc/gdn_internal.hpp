@@ -10,6 +10,9 @@ namespace gdn {
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 constexpr int kChunk = 64;    // tokens per chunk of the chunked prefill
+// Workspace record per (chunk slot, head) of the two-launch bf16 prefill: T' and P
+// ([64][64] bf16 each) and the 64 log2 decay prefixes (fp32).
+constexpr int kPrepRecordBytes = 2 * kChunk * kChunk * 2 + kChunk * 4;
 
 // Problem description handed from the C ABI to the prefill launchers.
 struct PrefillProblem {
@@ -29,7 +32,10 @@ struct PrefillPlan {
     int dv_tile;
     int seg_chunks;
     long long max_segments;     // upper bound on table entries (segments over all sequences)
+    int two_launch;             // 1: chunk-parallel records, then the state scan (bf16)
+    long long nslots;           // chunk slots of the records
     size_t ws_table, ws_seg;    // workspace bytes for the table and per-segment matrices
+    size_t ws_prep;             // workspace bytes for the chunk records
 };
 
 bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype,

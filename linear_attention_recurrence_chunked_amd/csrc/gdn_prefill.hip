@@ -677,8 +677,8 @@ template <int DK, int DVT, typename OP, int MODE>
 static hipError_t launch_scan(const PrefillArgs &args, long long units, int ntiles,
                               hipStream_t stream)
 {
-    if constexpr (sizeof(OP) == 2 && (DVT == 32 || DVT == 64)) {
-        if (!args.four_wave) return launch_scan_ws<DK, DVT, MODE>(args, units, ntiles, stream);
+    if constexpr (sizeof(OP) == 2 && DVT <= 64) {
+        if (args.prep) return launch_scan_split<DK, DVT, MODE>(args, units, ntiles, stream);
     }
     const long long groups = cdiv(units * args.H, 8) * 8 * ntiles;
     if (groups <= 0) return hipSuccess;
@@ -695,6 +695,13 @@ static hipError_t run_prefill(const PrefillArgs &args, const PrefillPlan &plan,
                               long long max_entries, hipStream_t stream)
 {
     const int dv = args.dv;
+    if constexpr (sizeof(OP) == 2) {
+        if (args.prep) {
+            // records of every chunk (read by phase A and by the final scan)
+            hipError_t err = launch_chunk_prep<DK>(args, plan.nslots, stream);
+            if (err != hipSuccess) return err;
+        }
+    }
     if (plan.seg_chunks < 0) {
         return launch_scan<DK, DVT, OP, kModeScan>(args, args.num_seqs, dv / DVT, stream);
     }
@@ -781,9 +788,15 @@ bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype
     const long long chains = (long long)num_seqs * H;
     if (tile == 0) {
         tile = largest_tile(dtype, dk, dv);
+        if (dtype == kDtypeBF16 && tile > 64) tile = 64;   // the two-launch path
         while (tile > 32 && chains * (dv / tile) < 512) tile >>= 1;
     }
     if (!tile_ok(dtype, dk, dv, tile)) return false;
+    plan->two_launch = (dtype == kDtypeBF16 && tile <= 64) ? 1 : 0;
+    plan->nslots = total_T / kChunk + num_seqs;
+    plan->ws_prep = plan->two_launch
+                        ? (size_t)plan->nslots * H * kPrepRecordBytes
+                        : 0;
     // Segments: split sequences when the chains alone cannot fill the chip and the average
     // sequence is long enough to pay for the extra phases.
     int seg = seg_chunks_req;
@@ -842,6 +855,7 @@ hipError_t launch_prefill(const PrefillProblem &p, const PrefillPlan &plan, void
         a.segB = seg;
         a.segM = seg + (size_t)plan.max_segments * p.H * p.dk * p.dv;
     }
+    if (plan.two_launch) a.prep = (unsigned char *)workspace + plan.ws_table + plan.ws_seg;
     if (p.dtype == kDtypeBF16)
         return dispatch_dk_dvt<uint16_t>(a, plan, p.dk, plan.max_segments, stream);
     return dispatch_dk_dvt<float>(a, plan, p.dk, plan.max_segments, stream);

@@ -124,20 +124,29 @@ template <> struct Quad<float> {
 
 // ---------------------------------------------------------------------------------------
 // LDS layout.  Operand tiles are stored unpadded with the 16-byte granules of each row
-// XOR-swizzled by s(row) = (row ^ row >> 3) & 7, so that a fragment load (eight consecutive
+// XOR-swizzled by a key of the row (swz_key), so that a fragment load (eight consecutive
 // elements of 16 consecutive rows), a quad store from the accumulator layout (four
 // consecutive elements of 16 rows) and the transposing quad stores of the input tiles all
 // spread over distinct banks.  Regions are reused by liveness within a chunk:
 //   U1: K and Q, row major (phases a-b)   |  R^T, U^T, scaled U^T (phases c-f)
 //   U2: V^T (phases a-b)                  |  the four diagonal blocks of X (phases c-d)
 // ---------------------------------------------------------------------------------------
+// Swizzle key of a row: rows of 16 or more granules (256 bytes) take a 4-bit key, so that the
+// 16 rows of a fragment load land on 16 different granule positions; narrower rows a 3-bit
+// key (odd and even rows already fall in different halves of a 256-byte bank window).
+template <typename OP, int W>
+__device__ __forceinline__ int swz_key(int row)
+{
+    if constexpr (W * (int)sizeof(OP) >= 256) return (row ^ (row >> 4)) & 15;
+    else return (row ^ (row >> 3)) & 7;
+}
+
 template <typename OP, int W>
 __device__ __forceinline__ int swz(int row, int col)
 {
     constexpr int E = (int)sizeof(OP);
     const int b = col * E;
-    const int s = (row ^ (row >> 3)) & 7;
-    return row * (W * E) + (((b >> 4) ^ s) << 4) + (b & 15);
+    return row * (W * E) + (((b >> 4) ^ swz_key<OP, W>(row)) << 4) + (b & 15);
 }
 
 template <int DK, int DVT, typename OP>
@@ -205,7 +214,7 @@ struct PrefillArgs {
     float *segM;               // [entries, H, DK, DK]  segment transition matrices
     int ntiles;                // column tiles per (unit, head)
     long long units;           // sequences or table capacity
-    int four_wave;             // 1: use the 4-wave kernel even where the specialised one exists
+    void *prep;                // chunk records of the two-launch path, or null
 };
 
 __device__ __forceinline__ void seq_bounds(const PrefillArgs &a, int n, long long &t0, int &len) {
@@ -243,10 +252,12 @@ __device__ __forceinline__ typename Mma<OP>::frag ldfrag(const unsigned char *ba
 }
 
 
-// Warp-specialised bf16 scan (gdn_prefill_ws.hip); instantiated for d_k in {64, 128} and
-// 32 or 64 state columns per workgroup.
+// Two-launch bf16 path (gdn_prefill_split.hip): chunk records, then the state scan with
+// 16, 32 or 64 state columns per workgroup; d_k in {64, 128}.
+template <int DK>
+hipError_t launch_chunk_prep(const PrefillArgs &args, long long nslots, hipStream_t stream);
 template <int DK, int DVT, int MODE>
-hipError_t launch_scan_ws(const PrefillArgs &args, long long units, int ntiles,
-                          hipStream_t stream);
+hipError_t launch_scan_split(const PrefillArgs &args, long long units, int ntiles,
+                             hipStream_t stream);
 
 }  // namespace gdn

@@ -55,7 +55,11 @@ def test_plans_for_the_workloads(lib):
     # 512 chains: enough work without splitting
     t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
     assert s == -1
-    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == 0
+    # bf16: one 16640-byte record (T', P, g) per chunk slot and head
+    slots = 270336 // 64 + 32
+    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == slots * 16 * 16640
+    # fp32 without segments needs no workspace
+    assert gdn.gdn_prefill_workspace_bytes(1, 256, 2, 64, 64, 0) == 0
     # fp32 tiles stay within the LDS budget
     t, s = gdn.gdn_prefill_plan(1, 256, 2, 64, 64, gdn.GDN_DTYPE_F32)
     assert t in (16, 32, 64)
@@ -72,7 +76,7 @@ def test_workspace_query_rejects_bad_shapes(lib):
 
 def prefill(lib, **kw):
     a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, s0=None, cu=None,
-             n=2, T=256, H=2, dk=128, dv=128, dt=1, y=6 * G, sf=7 * G, ws=None, wsb=0,
+             n=2, T=256, H=2, dk=128, dv=128, dt=1, y=6 * G, sf=7 * G, ws=9 * G, wsb=G,
              stream=None, tile=0, seg=-1)
     a.update(kw)
     return lib.gdn_prefill_ex(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["cu"],
@@ -95,8 +99,11 @@ def prefill(lib, **kw):
     (dict(dt=0, tile=128), gdn.GDN_ERR_UNSUPPORTED),      # fp32 tile over the LDS budget
     (dict(dt=0, tile=32), gdn.GDN_ERR_UNSUPPORTED),       # fp32, d_k = 128: 16 columns only
     (dict(seg=-2), gdn.GDN_ERR_INVALID_ARGUMENT),
-    (dict(k=2 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),    # misaligned (bf16 quad = 8 B)
-    (dict(dt=0, k=2 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),   # fp32 quad = 16 B
+    (dict(k=2 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),    # misaligned (16 B required)
+    (dict(k=2 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),    # bf16: eight elements too
+    (dict(dt=0, k=2 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(v=3 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(y=6 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(alpha=4 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(sf=7 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(y=1 * G + 4096), gdn.GDN_ERR_INVALID_ARGUMENT), # y overlaps q
@@ -104,7 +111,9 @@ def prefill(lib, **kw):
     (dict(s0=8 * G, y=8 * G), gdn.GDN_ERR_INVALID_ARGUMENT),   # y overlaps initial state
     (dict(s0=8 * G, sf=8 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # partial overlap
     (dict(s0=8 * G, sf=8 * G, seg=2), gdn.GDN_ERR_INVALID_ARGUMENT),  # in place + split
-    (dict(seg=2), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),       # needs a workspace
+    (dict(ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # bf16 chunk records
+    (dict(wsb=6 * 2 * 16640 - 1), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+    (dict(seg=2, ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # segments too
     (dict(seg=2, ws=9 * G, wsb=64), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_prefill_rejects(lib, kw, code):
@@ -127,6 +136,7 @@ def decode(lib, **kw):
     (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
     (dict(dt=2), gdn.GDN_ERR_UNSUPPORTED),
     (dict(q=1 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(q=1 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(state=6 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(y=6 * G + 1024), gdn.GDN_ERR_INVALID_ARGUMENT),   # y inside the state
     (dict(state=1 * G), gdn.GDN_ERR_INVALID_ARGUMENT),      # state over q
