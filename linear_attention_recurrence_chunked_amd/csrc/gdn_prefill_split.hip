@@ -360,45 +360,61 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
 }
 
 // =========================================================================================
-// Launch 2: the state scan.  Waves 0-1 load, waves 2 .. 2 + DVT/16 - 1 scan.
+// Launch 2: the state scan.  Waves 0-1 copy, the others scan (16 or 32 columns each).
 // =========================================================================================
-// Loader waves per workgroup: enough in-flight loads per CU to cover the memory latency.
-template <int DVT> constexpr int loaders_for() { return 2; }
+constexpr int kLoaders = 2;
 
-// Both stages of an array sit next to each other, so that the stage of a chunk is an
-// immediate offset of the LDS instructions (the chunk loop is unrolled by two).
+// One pipeline stage: K rows (internal token order, swizzled), Q rows (swizzled), the record
+// (T', P, g) and the V tile (rows = tokens, plain).  Three stages when they fit in LDS, so
+// that the copies of a chunk have two chunk-steps to arrive; two otherwise.
 template <int DK, int DVT>
 struct LdsSplit {
+    static constexpr int al(int x) { return (x + 255) & ~255; }
     static constexpr int szRow = kChunk * DK * 2;       // [64][DK] bf16
-    static constexpr int szV = DVT * kChunk * 2;        // [DVT][64] bf16
-    static constexpr int sK = 0;                        // K rows (d_k permuted)
-    static constexpr int sQ = 2 * szRow;                // Q rows (d_k permuted)
-    static constexpr int sKt = 4 * szRow;               // K^T [DK][64] (tokens permuted)
-    static constexpr int sRec = 6 * szRow;              // T', P, g (the record)
-    static constexpr int sV = sRec + 2 * kPrepRecordBytes;   // V^T tile [DVT][64]
-    static constexpr int total = sV + 2 * szV;
-    static constexpr int stK = szRow, stKt = szRow, stRec = kPrepRecordBytes, stV = szV;
+    static constexpr int szV = kChunk * DVT * 2;        // [64][DVT] bf16
+    static constexpr int sK = 0;
+    static constexpr int sQ = szRow;
+    static constexpr int sRec = 2 * szRow;
+    static constexpr int sV = sRec + kPrepRecordBytes;
+    static constexpr int stage = al(sV + szV);
+    static constexpr int nst = 3 * stage <= 160 * 1024 ? 3 : 2;
+    static constexpr int total = nst * stage;
 };
 
+// Four bf16 values by the gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each
+// group of 16 lanes, lane j receives element (j % 4) of the 8-byte rows addressed by lanes
+// j / 4, j / 4 + 4, j / 4 + 8 and j / 4 + 12, in that order.
+__device__ __forceinline__ bf16x4 ldtr(const unsigned char *p)
+{
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Column groups (16 state columns each) per scan wave.  One group per wave is the faster
+// shape (the chunk update is a latency-bound chain, so more waves beat longer ones); the
+// 64-column tile takes two groups per wave so that the workgroup stays at four waves (one
+// per SIMD, with the full register file each).
+template <int DVT> constexpr int groups_per_wave() { return DVT >= 64 ? 2 : 1; }
+template <int DVT> constexpr int scan_waves() { return DVT / (16 * groups_per_wave<DVT>()); }
+
 template <int DK, int DVT, int MODE>
-__global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_split_kernel(PrefillArgs a)
+__global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_split_kernel(PrefillArgs a)
 {
     using L = LdsSplit<DK, DVT>;
+    constexpr int NG = groups_per_wave<DVT>();
     using OP = uint16_t;
     using M = Mma<OP>;
-    using Q4 = Quad<OP>;
+    constexpr int NST = L::nst;
     constexpr int MBK = DK / 16;           // 16-row blocks of the state
     constexpr int KBD = DK / 32;           // K-blocks over the key dimension
-    constexpr int kLoaders = loaders_for<DVT>();
     constexpr int KG = DK / 8;             // 16-byte granules per key row
-    constexpr int VG = DVT / 8;            // 16-byte granules per value-tile row
-    constexpr int KB8 = (16 * KG) / 64;    // 4-row x 8-column blocks of K per lane of wave 1
-    constexpr int NVB = 16 * VG;           // 4-row x 8-column blocks of the V tile
-    constexpr int VB8 = (NVB + 63) / 64;   // ... per lane of wave 1
-    constexpr int QI = (kChunk * KG) / 64; // 1 KiB copies of Q rows (wave 0)
-    constexpr int RI = kRecG / 1024;       // 1 KiB copies of T' and P (wave 0)
+    constexpr int CK = L::szRow / 1024;    // 1 KiB copies per K (or Q) tile
+    constexpr int CV = L::szV / 1024 > 0 ? L::szV / 1024 : 1;   // ... per V tile
+    constexpr int CR = kRecG / 1024;       // ... per T' + P
     constexpr bool kY = (MODE == kModeScan);
-    static_assert(kLoaders == 2 && (16 * KG) % 64 == 0, "loader split");
+    static_assert(CK % kLoaders == 0 && CR % kLoaders == 0, "copy split");
 
     __shared__ __align__(16) unsigned char smem[L::total];
 
@@ -454,225 +470,125 @@ __global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_spl
 
     // ================================================================ loader waves
     if (loader) {
-        // Wave 0 copies Q rows and the record of a chunk global -> LDS with the direct-to-LDS
-        // loads (16 bytes per lane; lane l lands at the wave's LDS pointer + 16 l).  It makes
-        // no other LDS access, so nothing waits on these copies before the chunk's barrier:
-        // the copies of chunk c+1 are issued at the start of iteration c, into the stage that
-        // iteration c-1 finished reading.  Wave 1 moves K and the V tile through registers
-        // (4-row x 8-column blocks, loaded one chunk ahead), because they are also stored
-        // transposed.  Global addresses are a per-chunk base plus 32-bit byte offsets.
+        // Every operand tile is a set of whole token rows, so both loader waves only issue
+        // direct-to-LDS copies (16 bytes per lane; lane l lands at the wave's LDS pointer +
+        // 16 l) and never touch LDS otherwise.  Copy j of a tile fills its bytes
+        // [1024 j, 1024 j + 1024); the lane's source row and column follow from the
+        // destination through the swizzle and, for K, the internal token order.  Rows past
+        // the end of the job repeat its last row: they meet zero rows and columns of T'.
         typedef __attribute__((address_space(3))) void lds_void;
         const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;  // bytes
-        auto bytes = [](const void *p, unsigned off) {
-            return (const void *)((const unsigned char *)p + off);
-        };
-        auto row_base = [&](const void *t, long long t0, int D) {
-            return (const unsigned char *)t + ((t0 * H + job.h) * (long long)D) * 2;
-        };
-        const std::integral_constant<int, 0> st0{};
-        const std::integral_constant<int, 1> st1{};
-        if (wave == 0) {
-            auto copy = [&](auto stc, int c) {
-                constexpr int ST = decltype(stc)::value;
-                const long long t0 = job.tok0 + (long long)c * kChunk;
-                const int last = nvalid_of(c) - 1;
-                if (kY) {
-                    const unsigned char *cq = row_base(a.q, t0, DK);
+        // per-lane (row, byte column) of this wave's copies
+        int kr[CK / kLoaders], kc[CK / kLoaders], qr[CK / kLoaders], qc[CK / kLoaders];
 #pragma unroll
-                    for (int j = 0; j < QI; ++j) {
-                        // physical granule P of the swizzled tile <- logical granule pg ^ s(r)
-                        const int P = 64 * j + lane;
-                        const int r = P / KG, pg = P % KG;
-                        const int rc = r < last ? r : last;
-                        const unsigned off = (unsigned)rc * rsK + 16 * (pg ^ swz_key<OP, DK>(r));
-                        __builtin_amdgcn_global_load_lds(
-                            (const void *)(cq + off),
-                            (lds_void *)(smem + L::sQ + ST * L::stK + 1024 * j), 16, 0, 0);
-                    }
-                }
-                const unsigned char *rec = (const unsigned char *)a.prep +
-                                           ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
-#pragma unroll
-                for (int j = 0; j < RI; ++j)
-                    __builtin_amdgcn_global_load_lds(
-                        (const void *)(rec + 16 * (64 * j + lane)),
-                        (lds_void *)(smem + L::sRec + ST * L::stRec + 1024 * j), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(rec + kRecG + 4 * lane),
-                    (lds_void *)(smem + L::sRec + ST * L::stRec + kRecG), 4, 0, 0);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            };
-            if (nchunks > 0) {
-                copy(st0, 0);
-                __syncthreads();
-            }
-            for (int c = 0; c < nchunks; c += 2) {
-                if (c + 1 < nchunks) copy(st1, c + 1);
-                __syncthreads();
-                if (c + 1 < nchunks) {
-                    if (c + 2 < nchunks) copy(st0, c + 2);
-                    __syncthreads();
-                }
-            }
-            return;
+        for (int j = 0; j < CK / kLoaders; ++j) {
+            const int P = 64 * (wave + kLoaders * j) + lane;     // granule of the tile
+            const int r = P / KG, pg = P % KG;
+            const int lgq = pg ^ swz_key<OP, DK>(r);              // logical granule
+            kr[j] = split_orig(r);
+            kc[j] = 16 * lgq;
+            qr[j] = r;
+            qc[j] = 16 * lgq;
         }
-        const int ltid = lane;              // wave 1
-        unsigned gK[KB8][4], gV[VB8][4];
+        int vr[CV], vc[CV];
 #pragma unroll
-        for (int j = 0; j < KB8; ++j) {
-            const int b = ltid + 64 * j;
-            const int dg = b / 16, tq = b % 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gK[j][i] = (unsigned)(4 * tq + i) * rsK + 16 * dg;
+        for (int j = 0; j < CV; ++j) {
+            const int byte = 1024 * j + 16 * lane;
+            vr[j] = byte / (DVT * 2);
+            vc[j] = byte % (DVT * 2);
         }
-#pragma unroll
-        for (int j = 0; j < VB8; ++j) {
-            const int b = (ltid + 64 * j) % NVB;
-            const int dg = b / 16, tq = b % 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gV[j][i] = (unsigned)(4 * tq + i) * rsV + 16 * dg;
-        }
-        // Block b = lane + 64 j covers token rows 4 tq .. 4 tq + 3 (tq = b % 16, the fastest,
-        // so that the transposed quad stores of 16 lanes fill whole rows of K^T and V^T) and
-        // columns 8 dg .. 8 dg + 7 (dg = b / 16).
-        // LDS byte offsets of this lane's stores (within a stage)
-        unsigned lKr[KB8][4], lKt[KB8][8], lVt[VB8][8];
-#pragma unroll
-        for (int j = 0; j < KB8; ++j) {
-            const int b = ltid + 64 * j;
-            const int dg = b / 16, tq = b % 16;
-            const int pr = split_pos(4 * tq);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lKr[j][i] = (unsigned)(L::sK + swz<OP, DK>(pr + i, 8 * dg));
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                lKt[j][e] = (unsigned)(L::sKt + swz<OP, kChunk>(split_pos(8 * dg + e), 4 * tq));
-        }
-#pragma unroll
-        for (int j = 0; j < VB8; ++j) {
-            const int b = (ltid + 64 * j) % NVB;
-            const int dg = b / 16, tq = b % 16;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                lVt[j][e] = (unsigned)(L::sV + swz<OP, kChunk>(8 * dg + e, 4 * tq));
-        }
-        u32x4 pk[KB8][4], pv[VB8][4];
-        auto vblock = [&](int j) { return ltid + 64 * j < NVB; };
-        // register loads of K and V of chunk c
-        auto load = [&](int c) {
+        const int vcol0 = mpart ? 0 : job.col0;   // the M part copies (unused) V columns
+        auto copy = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            unsigned char *stg = smem + ST * L::stage;
             const long long t0 = job.tok0 + (long long)c * kChunk;
             const int last = nvalid_of(c) - 1;
-            const unsigned char *ck = row_base(a.k, t0, DK);
-            const unsigned char *cv = row_base(a.v, t0, DV) + job.col0 * 2;
-            if (last == kChunk - 1) {
+            const unsigned char *ck = (const unsigned char *)a.k + (t0 * H + job.h) * (long long)DK * 2;
+            const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + job.h) * (long long)DK * 2;
+            const unsigned char *cv = (const unsigned char *)a.v +
+                                      ((t0 * H + job.h) * (long long)DV + vcol0) * 2;
+            const unsigned char *rec = (const unsigned char *)a.prep +
+                                       ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
 #pragma unroll
-                for (int j = 0; j < KB8; ++j)
+            for (int j = 0; j < CK / kLoaders; ++j) {
+                const int jj = wave + kLoaders * j;
+                const int r = kr[j] < last ? kr[j] : last;
+                __builtin_amdgcn_global_load_lds((const void *)(ck + (unsigned)r * rsK + kc[j]),
+                                                 (lds_void *)(stg + L::sK + 1024 * jj), 16, 0, 0);
+            }
+            if (kY) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) pk[j][i] = *(const u32x4 *)bytes(ck, gK[j][i]);
-                if (!mpart) {
-#pragma unroll
-                    for (int j = 0; j < VB8; ++j)
-                        if (vblock(j)) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                pv[j][i] = *(const u32x4 *)bytes(cv, gV[j][i]);
-                        }
+                for (int j = 0; j < CK / kLoaders; ++j) {
+                    const int jj = wave + kLoaders * j;
+                    const int r = qr[j] < last ? qr[j] : last;
+                    __builtin_amdgcn_global_load_lds((const void *)(cq + (unsigned)r * rsK + qc[j]),
+                                                     (lds_void *)(stg + L::sQ + 1024 * jj), 16, 0,
+                                                     0);
                 }
-            } else {
-                // the job's last chunk: rows past its end read its last row instead
+            }
 #pragma unroll
-                for (int j = 0; j < KB8; ++j) {
-                    const int b = ltid + 64 * j;
-                    const int dg = b / 16, tq = b % 16;
+            for (int j = 0; j < CR / kLoaders; ++j) {
+                const int jj = wave + kLoaders * j;
+                __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * (64 * jj + lane)),
+                                                 (lds_void *)(stg + L::sRec + 1024 * jj), 16, 0, 0);
+            }
+            // g (both waves write the same 256 bytes) and the V tile (both waves copy it)
+            __builtin_amdgcn_global_load_lds((const void *)(rec + kRecG + 4 * lane),
+                                             (lds_void *)(stg + L::sRec + kRecG), 4, 0, 0);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 4 * tq + i < last ? 4 * tq + i : last;
-                        pk[j][i] = *(const u32x4 *)bytes(ck, (unsigned)t * rsK + 16 * dg);
-                    }
-                }
-                if (!mpart) {
-#pragma unroll
-                    for (int j = 0; j < VB8; ++j)
-                        if (vblock(j)) {
-                            const int b = ltid + 64 * j;
-                            const int dg = b / 16, tq = b % 16;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int t = 4 * tq + i < last ? 4 * tq + i : last;
-                                pv[j][i] = *(const u32x4 *)bytes(cv, (unsigned)t * rsV + 16 * dg);
-                            }
-                        }
+            for (int j = 0; j < CV; ++j) {
+                if (L::szV >= 1024 || 16 * lane < L::szV) {
+                    const int r = vr[j] < last ? vr[j] : last;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)(cv + (unsigned)r * rsV + vc[j]),
+                        (lds_void *)(stg + L::sV + 1024 * j), 16, 0, 0);
                 }
             }
         };
-        // K rows (internal token order), K^T (internal d_k order) and V^T of chunk c
-        auto store = [&](auto stc, int c) {
-            constexpr int ST = decltype(stc)::value;
-            const int nv = nvalid_of(c);
-            const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int j = 0; j < KB8; ++j) {
-                const int tq = (ltid + 64 * j) % 16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (4 * tq + i >= nv) pk[j][i] = z;
-                    *(u32x4 *)(smem + lKr[j][i] + ST * L::stK) = pk[j][i];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int w = e >> 1;
-                    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 col;
-                    col[0] = __builtin_amdgcn_perm(pk[j][1][w], pk[j][0][w], sel);
-                    col[1] = __builtin_amdgcn_perm(pk[j][3][w], pk[j][2][w], sel);
-                    *(u32x2 *)(smem + lKt[j][e] + ST * L::stKt) = col;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < VB8; ++j) {
-                if (!vblock(j)) continue;
-                const int tq = (ltid + 64 * j) % 16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (mpart || 4 * tq + i >= nv) pv[j][i] = z;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int w = e >> 1;
-                    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 col;
-                    col[0] = __builtin_amdgcn_perm(pv[j][1][w], pv[j][0][w], sel);
-                    col[1] = __builtin_amdgcn_perm(pv[j][3][w], pv[j][2][w], sel);
-                    *(u32x2 *)(smem + lVt[j][e] + ST * L::stV) = col;
-                }
-            }
+        constexpr int kCopies = CK / kLoaders * (kY ? 2 : 1) + CR / kLoaders + 1 + CV;
+        // Wait for the copies of the chunk the scan reads next.  With three stages those
+        // were issued one step before the kCopies copies just issued (and copies complete in
+        // order); with two stages they are the copies just issued.
+        auto wait_prev = [&](bool issued_next) {
+            if (NST == 3 && issued_next)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
+        auto step = [&](auto stn, int c) {   // iteration c: issue chunk c + NST - 1
+            const int cn = c + NST - 1;
+            if (cn < nchunks) copy(stn, cn);
+            wait_prev(cn < nchunks);
+            __syncthreads();
+        };
+        const std::integral_constant<int, 0> s0{};
+        const std::integral_constant<int, 1> s1{};
+        const std::integral_constant<int, 2> s2{};
         if (nchunks > 0) {
-            load(0);
-            store(st0, 0);
-            if (nchunks > 1) load(1);
+            copy(s0, 0);
+            if (NST == 3 && nchunks > 1) copy(s1, 1);
+            wait_prev(NST == 3 && nchunks > 1);
             __syncthreads();
         }
-        // iteration c stores chunk c+1 (stage (c+1) & 1) and loads chunk c+2
-        for (int c = 0; c < nchunks; c += 2) {
-            if (c + 1 < nchunks) {
-                store(st1, c + 1);
-                if (c + 2 < nchunks) load(c + 2);
+        if constexpr (NST == 3) {
+            for (int c = 0; c < nchunks; c += 3) {
+                step(s2, c);
+                if (c + 1 < nchunks) step(s0, c + 1);
+                if (c + 2 < nchunks) step(s1, c + 2);
             }
-            __syncthreads();
-            if (c + 1 < nchunks) {
-                if (c + 2 < nchunks) {
-                    store(st0, c + 2);
-                    if (c + 3 < nchunks) load(c + 3);
-                }
-                __syncthreads();
+        } else {
+            for (int c = 0; c < nchunks; c += 2) {
+                step(s1, c);
+                if (c + 1 < nchunks) step(s0, c + 1);
             }
         }
         return;
     }
 
     // ================================================================ scan waves
-    const int c0 = job.col0 + 16 * sw;     // first state column of this wave
-    f32x4 S[MBK];
+    // this wave owns state columns c0 + 16 g + ln, g < NG
+    const int c0 = job.col0 + 16 * NG * sw;
+    f32x4 S[NG][MBK];
     {
         const float *src = nullptr;
         if (MODE == kModeScan) {
@@ -684,28 +600,30 @@ __global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_spl
         } else if (!mpart && job.seg == 0 && a.s0) {
             src = a.s0 + ((long long)job.n * H + job.h) * DK * DV + c0;
         }
-        // register S[m][i] of lane (ln, lg) holds state row split_orig(16 m + 4 lg + i)
+        // register S[g][m][i] of lane (ln, lg) holds state row split_orig(16 m + 4 lg + i)
 #pragma unroll
-        for (int m = 0; m < MBK; ++m)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = split_orig(16 * m + 4 * lg + i);
-                float x = 0.f;
-                if (mpart) x = (row == c0 - DV + ln) ? 1.f : 0.f;
-                else if (src) x = src[(long long)row * DV + ln];
-                S[m][i] = x;
-            }
+            for (int m = 0; m < MBK; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = split_orig(16 * m + 4 * lg + i);
+                    const int col = 16 * g + ln;
+                    float x = 0.f;
+                    if (mpart) x = (row == c0 - DV + col) ? 1.f : 0.f;
+                    else if (src) x = src[(long long)row * DV + col];
+                    S[g][m][i] = x;
+                }
     }
     auto chunk = [&](auto stc, int c) {
         constexpr int ST = decltype(stc)::value;
-        const unsigned char *bKc = smem + L::sK + ST * L::stK;
-        const unsigned char *bQc = smem + L::sQ + ST * L::stK;
-        const unsigned char *bKt = smem + L::sKt + ST * L::stKt;
-        const unsigned char *rec = smem + L::sRec + ST * L::stRec;
-        const unsigned char *bTc = rec + kRecT;
-        const unsigned char *bPc = rec + kRecP;
-        const float *sGc = (const float *)(rec + kRecG);
-        const unsigned char *bVc = smem + L::sV + ST * L::stV;
+        const unsigned char *stg = smem + ST * L::stage;
+        const unsigned char *bKc = stg + L::sK;
+        const unsigned char *bQc = stg + L::sQ;
+        const unsigned char *bTc = stg + L::sRec + kRecT;
+        const unsigned char *bPc = stg + L::sRec + kRecP;
+        const float *sGc = (const float *)(stg + L::sRec + kRecG);
+        const unsigned char *bVc = stg + L::sV;
         const long long t0 = job.tok0 + (long long)c * kChunk;
         const int nv = nvalid_of(c);
         // Fragments are loaded one step ahead of the MFMAs that use them; the scheduling
@@ -721,25 +639,46 @@ __global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_spl
         auto frag64 = [&](const unsigned char *base, int row, int k0) {
             return ldfrag<OP, kChunk>(base, row, k0 + 8 * lg);
         };
+        // K^T fragment for the state update: A[row = state row 16 m + ln (internal)][k =
+        // tokens 32 kt + 8 lg .. + 7] by two transposing reads of the K rows.  Lane ln of the
+        // group addresses token 32 kt + 8 lg + (ln / 4) (+ 4) and the four key columns that
+        // lanes 4 (ln % 4) .. + 3 receive.
+        auto frag_kt = [&](int m, int kt) {
+            const int col = 32 * (m >> 1) + 8 * (ln & 3) + 4 * (m & 1);
+            const int t = 32 * kt + 8 * lg + (ln >> 2);
+            const bf16x4 lo = ldtr(bKc + swz<OP, DK>(split_pos(t), col));
+            const bf16x4 hi = ldtr(bKc + swz<OP, DK>(split_pos(t + 4), col));
+            return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
 
         // ---- K S and S^T Q^T from the chunk-start state ----
-        f32x4 accYt[4], acc_ks[4], vv[4], gam[4];
-        bf16x8 Sb[KBD];
+        f32x4 accYt[NG][4], acc_ks[NG][4], vv[NG][4], gam[4];
+        bf16x8 Sb[NG][KBD];
         ld_kq(0, 0);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            // rows of K S held by this lane: internal 16 tb + 4 lg + i, i.e. tokens o0 + i
+            // rows of K S held by this lane: internal 16 tb + 4 lg + i, i.e. tokens o0 + i;
+            // V[o0 .. o0 + 3][column] by one transposing read of the V rows
             const int o0 = split_orig(tb * 16 + 4 * lg);
-            vv[tb] = load4((const OP *)(bVc + swz<OP, kChunk>(16 * sw + ln, o0)));
             gam[tb] = *(const f32x4 *)(sGc + o0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int col = c0 - job.col0 + 16 * g + 4 * (ln & 3);
+                const bf16x4 v4 = ldtr(bVc + ((o0 + (ln >> 2)) * DVT + col) * 2);
+                vv[g][tb] = mpart ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_convertvector(v4, f32x4);
+            }
         }
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) Sb[kb] = pack8s(S[2 * kb], S[2 * kb + 1]);
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            acc_ks[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accYt[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int kb = 0; kb < KBD; ++kb) Sb[g][kb] = pack8s(S[g][2 * kb], S[g][2 * kb + 1]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                acc_ks[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accYt[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
             if (kb + 1 < KBD) {
@@ -753,51 +692,60 @@ __global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_spl
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                M::mma(acc_ks[tb], fk[kb & 1][tb], Sb[kb]);
-                if (kY) M::mma(accYt[tb], Sb[kb], fq[kb & 1][tb]);
-            }
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    M::mma(acc_ks[g][tb], fk[kb & 1][tb], Sb[g][kb]);
+                    if (kY) M::mma(accYt[g][tb], Sb[g][kb], fq[kb & 1][tb]);
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- R = V - diag(gamma) K S;  U = T' R ----
         bf16x8 fkt[2][MBK];
 #pragma unroll
-        for (int m = 0; m < MBK; ++m) fkt[0][m] = frag64(bKt, m * 16 + ln, 0);
-        f32x4 U[4];
-        {
+        for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+        f32x4 U[NG][4];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
             f32x4 R[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) R[tb] = vv[tb] - exp2x4(gam[tb]) * acc_ks[tb];
+            for (int tb = 0; tb < 4; ++tb) R[tb] = vv[g][tb] - exp2x4(gam[tb]) * acc_ks[g][tb];
             const bf16x8 Rb0 = pack8s(R[0], R[1]);
             const bf16x8 Rb1 = pack8s(R[2], R[3]);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                M::mma(U[mb], ft[mb], Rb0);
+                U[g][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                M::mma(U[g][mb], ft[mb], Rb0);
             }
-            M::mma(U[2], ft[4], Rb1);
-            M::mma(U[3], ft[5], Rb1);
+            M::mma(U[g][2], ft[4], Rb1);
+            M::mma(U[g][3], ft[5], Rb1);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < MBK; ++m) fkt[1][m] = frag64(bKt, m * 16 + ln, 32);
+        for (int m = 0; m < MBK; ++m) fkt[1][m] = frag_kt(m, 1);
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U ----
         const float gC = sGc[kChunk - 1];
         {
-            f32x4 Us[4];
+            bf16x8 Ub0[NG], Ub1[NG];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) Us[mb] = U[mb] * exp2x4(gC - gam[mb]);
-            const bf16x8 Ub0 = pack8s(Us[0], Us[1]);
-            const bf16x8 Ub1 = pack8s(Us[2], Us[3]);
+            for (int g = 0; g < NG; ++g) {
+                f32x4 Us[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) Us[mb] = U[g][mb] * exp2x4(gC - gam[mb]);
+                Ub0[g] = pack8s(Us[0], Us[1]);
+                Ub1[g] = pack8s(Us[2], Us[3]);
+            }
             const float gamC = __builtin_amdgcn_exp2f(gC);
 #pragma unroll
-            for (int m = 0; m < MBK; ++m) {
-                S[m] *= gamC;
-                M::mma(S[m], fkt[0][m], Ub0);
-            }
+            for (int m = 0; m < MBK; ++m)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    S[g][m] *= gamC;
+                    M::mma(S[g][m], fkt[0][m], Ub0[g]);
+                }
             __builtin_amdgcn_sched_barrier(0);
             if (kY) {
 #pragma unroll
@@ -807,34 +755,50 @@ __global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_spl
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < MBK; ++m) M::mma(S[m], fkt[1][m], Ub1);
+            for (int m = 0; m < MBK; ++m)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) M::mma(S[g][m], fkt[1][m], Ub1[g]);
         }
 
         // ---- Y^T = S^T Q^T diag(gamma) + U^T P^T ----
         if (kY) {
-            const bf16x8 Uu0 = pack8s(U[0], U[1]);
-            const bf16x8 Uu1 = pack8s(U[2], U[3]);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                accYt[tb] *= __builtin_amdgcn_exp2f(sGc[tb * 16 + ln]);
-                M::mma(accYt[tb], Uu0, ft[tb]);
-            }
-            M::mma(accYt[2], Uu1, ft[4]);
-            M::mma(accYt[3], Uu1, ft[5]);
+            for (int g = 0; g < NG; ++g) {
+                const bf16x8 Uu0 = pack8s(U[g][0], U[g][1]);
+                const bf16x8 Uu1 = pack8s(U[g][2], U[g][3]);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int t = tb * 16 + ln;
-                if (t < nv)
-                    store4((OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + c0 + 4 * lg,
-                           accYt[tb]);
+                for (int tb = 0; tb < 4; ++tb) {
+                    accYt[g][tb] *= __builtin_amdgcn_exp2f(sGc[tb * 16 + ln]);
+                    M::mma(accYt[g][tb], Uu0, ft[tb]);
+                }
+                M::mma(accYt[g][2], Uu1, ft[4]);
+                M::mma(accYt[g][3], Uu1, ft[5]);
             }
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int t = tb * 16 + ln;
+                    if (t < nv)
+                        store4((OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + c0 + 16 * g +
+                                   4 * lg,
+                               accYt[g][tb]);
+                }
         }
         __syncthreads();
     };
     if (nchunks > 0) __syncthreads();     // the prologue's barrier (chunk 0 staged)
-    for (int c = 0; c < nchunks; c += 2) {
-        chunk(std::integral_constant<int, 0>{}, c);
-        if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1);
+    if constexpr (NST == 3) {
+        for (int c = 0; c < nchunks; c += 3) {
+            chunk(std::integral_constant<int, 0>{}, c);
+            if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1);
+            if (c + 2 < nchunks) chunk(std::integral_constant<int, 2>{}, c + 2);
+        }
+    } else {
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(std::integral_constant<int, 0>{}, c);
+            if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1);
+        }
     }
 
     // ================================================================ state out
@@ -852,10 +816,13 @@ __global__ __launch_bounds__(64 * (DVT / 16 + loaders_for<DVT>())) void scan_spl
         }
         if (dst) {
 #pragma unroll
-            for (int m = 0; m < MBK; ++m)
+            for (int g = 0; g < NG; ++g)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dst[(long long)split_orig(16 * m + 4 * lg + i) * ld + ln] = S[m][i];
+                for (int m = 0; m < MBK; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dst[(long long)split_orig(16 * m + 4 * lg + i) * ld + 16 * g + ln] =
+                            S[g][m][i];
         }
     }
 }
@@ -883,7 +850,7 @@ hipError_t launch_scan_split(const PrefillArgs &args, long long units, int ntile
     a2.units = units;
     a2.ntiles = ntiles;
     hipLaunchKernelGGL((scan_split_kernel<DK, DVT, MODE>), dim3((unsigned)groups),
-                       dim3(64 * (DVT / 16 + loaders_for<DVT>())), 0, stream, a2);
+                       dim3(64 * (scan_waves<DVT>() + kLoaders)), 0, stream, a2);
     return hipGetLastError();
 }
 
