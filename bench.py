@@ -45,7 +45,7 @@ def decode_bytes_per_head_step(d: int) -> int:
 
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc")
 PREFILL_SOURCES = ["gdn_device.hpp", "gdn_prefill_common.hpp", "gdn_prefill.hip",
-                   "gdn_prefill_ws.hip"]
+                   "gdn_prefill_split.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
 
 
@@ -178,10 +178,14 @@ def main():
     torch.cuda.synchronize()
     warm_ms = ew0.elapsed_time(ew1) / args.steps
 
-    if tile in (32, 64) and seg < 0:
-        kernel_name = "prefill_ws_kernel<128,%d,scan>" % tile
+    # bf16 prefill = two launches: chunk records, then the state scan; the roofline covers
+    # the pair (HIP events around the library call); rocprofv3 splits it per kernel
+    if tile <= 64:
+        kernel_name = "chunk_prep_kernel<128> + scan_split_kernel<128,%d,scan>" % tile
     else:
-        kernel_name = "prefill_kernel<128,%d,bf16,scan> (+ segment phases)" % tile
+        kernel_name = "prefill_kernel<128,%d,bf16,scan>" % tile
+    if seg >= 0:
+        kernel_name += " (+ segment phases)"
     tok_s = T / (pre_ms * 1e-3)
     flops = prefill_flops_per_token_head(d) * T * H
     achieved_tflops = flops / (pre_ms * 1e-3) / 1e12
