@@ -66,9 +66,9 @@ const char *gdn_version(void);
 
 /*
  * Bytes of device workspace gdn_prefill needs for this problem (a pure function of the
- * arguments; 0 on invalid arguments).  The workspace holds, for bf16 inputs, one 16640-byte
- * record per (64-token chunk, head) (the chunk's inverted triangular system, its decay-masked
- * Q K^T block and its log-decay prefix, (total_T / 64 + num_seqs) * H records in all) and,
+ * arguments; 0 on invalid arguments).  The workspace holds, for bf16 inputs, one 8448-byte
+ * record per (64-token chunk, head) (the chunk's inverted triangular system and its log-decay
+ * prefix, (total_T / 64 + num_seqs) * H records in all) and,
  * for long sequences, the segment table, per-segment transition matrices and start states
  * of the segment-parallel scan.  fp32 inputs without segments need none.
  */

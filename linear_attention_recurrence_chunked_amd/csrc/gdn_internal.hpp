@@ -10,9 +10,9 @@ namespace gdn {
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 constexpr int kChunk = 64;    // tokens per chunk of the chunked prefill
-// Workspace record per (chunk slot, head) of the two-launch bf16 prefill: T' and P
-// ([64][64] bf16 each) and the 64 log2 decay prefixes (fp32).
-constexpr int kPrepRecordBytes = 2 * kChunk * kChunk * 2 + kChunk * 4;
+// Workspace record per (chunk slot, head) of the two-launch bf16 prefill: T' ([64][64]
+// bf16) and the 64 log2 decay prefixes (fp32).
+constexpr int kPrepRecordBytes = kChunk * kChunk * 2 + kChunk * 4;
 
 // Problem description handed from the C ABI to the prefill launchers.
 struct PrefillProblem {

@@ -9,12 +9,12 @@
 //     g   = within-chunk inclusive prefix of log2 alpha,  gamma = 2^g
 //     A   = diag(beta) strictlower(K K^T (.) Gamma),  Gamma_ti = gamma_t / gamma_i
 //     T'  = (I + A)^{-1} diag(beta)            (blocked inversion, see below)
-//     P   = lower_incl(Q K^T (.) Gamma)
-//   and writes T', P and g to the workspace (16640 bytes per record).
+//   and writes T' and g to the workspace (8448 bytes per record).
 //
 //   scan_split_kernel (one workgroup per (sequence or segment, head, column tile)):
-//     two loader waves stream K, Q, V and the record of chunk c+1 into a second LDS stage
-//     while the scan waves apply chunk c to the state held in MFMA accumulator registers:
+//     two loader waves copy K, Q, V and the record of a chunk into an LDS stage ahead of
+//     use and form P = lower_incl(Q K^T (.) Gamma) there, while the scan waves apply the
+//     current chunk to the state held in MFMA accumulator registers:
 //     R = V - diag(gamma) K S,  U = T' R,  Y^T = S^T Q^T diag(gamma) + U^T P^T,
 //     S = gamma_C S + K^T diag(gamma_C / gamma) U.   One barrier per chunk.
 //
@@ -27,11 +27,10 @@
 namespace gdn {
 
 // Record of one (slot, head): T' [64][64] bf16 (rows in the internal token order defined
-// below) and P [64][64] bf16, both in the XOR-swizzled byte layout of a 64-wide LDS tile (so
-// both launches copy them granule for granule), then g [64] fp32.
+// below) in the XOR-swizzled byte layout of a 64-wide LDS tile (so both launches copy it
+// granule for granule), then g [64] fp32.
 constexpr int kRecT = 0;
-constexpr int kRecP = kChunk * kChunk * 2;
-constexpr int kRecG = 2 * kChunk * kChunk * 2;
+constexpr int kRecG = kChunk * kChunk * 2;
 static_assert(kRecG + kChunk * 4 == kPrepRecordBytes, "record layout");
 constexpr int kRecGranules = kPrepRecordBytes / 16;
 
@@ -121,14 +120,13 @@ struct LdsPrep {
     static constexpr int szRow = kChunk * DK * 2;
     static constexpr int LDA = kChunk + 4;          // padded fp32 rows of A
     static constexpr int LDX = 20;                  // padded rows of a diagonal X block
-    static constexpr int oT = kRecT, oP = kRecP, oG = kRecG;
+    static constexpr int oT = kRecT, oG = kRecG;
     static constexpr int oBeta = kPrepRecordBytes;
-    static constexpr int oK = oBeta + 256;          // K, Q rows (phases 1-2) ...
-    static constexpr int oQ = oK + szRow;
+    static constexpr int oK = oBeta + 256;          // K rows (phases 1-2) ...
     static constexpr int oA = oK;                   // ... then A and the X blocks (phase 3)
     static constexpr int oX = oA + kChunk * LDA * 4;
-    static constexpr int total = oK + (2 * szRow > kChunk * LDA * 4 + 4 * 16 * LDX * 4
-                                           ? 2 * szRow
+    static constexpr int total = oK + (szRow > kChunk * LDA * 4 + 4 * 16 * LDX * 4
+                                           ? szRow
                                            : kChunk * LDA * 4 + 4 * 16 * LDX * 4);
 };
 
@@ -147,8 +145,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
     float *const sA = (float *)(smem + L::oA);
     float *const sX = (float *)(smem + L::oX);
     unsigned char *const bK = smem + L::oK;
-    unsigned char *const bQ = smem + L::oQ;
-    unsigned char *const bP = smem + L::oP;
     unsigned char *const bT = smem + L::oT;
 
     const int tid = threadIdx.x;
@@ -174,11 +170,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
     const long long t0 = st0 + c * kChunk;
     const int nv = (int)((slen - c * kChunk) < kChunk ? (slen - c * kChunk) : kChunk);
 
-    // ---- phase 1: K, Q rows (zero beyond the chunk's last row), g, beta ----
+    // ---- phase 1: K rows (zero beyond the chunk's last row), g, beta ----
     {
         const OP *gk = (const OP *)a.k;
-        const OP *gq = (const OP *)a.q;
-        u32x4 rk[NG], rq[NG];
+        u32x4 rk[NG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
             const int idx = tid + 256 * j;
@@ -186,7 +181,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
             const int tc = row < nv ? row : nv - 1;
             const long long off = ((t0 + tc) * H + h) * (long long)DK + 8 * gc;
             rk[j] = ld16(gk + off);
-            rq[j] = ld16(gq + off);
         }
         float pa = 0.f;
         if (wave < 2) {
@@ -199,7 +193,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
             const int row = idx / GR, gc = idx % GR;
             const u32x4 z = {0u, 0u, 0u, 0u};
             *(u32x4 *)(bK + swz<OP, DK>(row, 8 * gc)) = row < nv ? rk[j] : z;
-            *(u32x4 *)(bQ + swz<OP, DK>(row, 8 * gc)) = row < nv ? rq[j] : z;
         }
         if (wave == 0) {
             float x = lane < nv ? fmaxf(__builtin_amdgcn_logf(pa), kLog2AlphaFloor) : 0.f;
@@ -225,12 +218,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
     const int ib1 = wave == 0 ? 0 : 1;
     const int tbs[3] = {wave, tb0, 3};
     const int ibs[3] = {wave, ib0, ib1};
-    f32x4 accG[3], accP[3];
+    f32x4 accG[3];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-        accG[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accP[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int p = 0; p < 3; ++p) accG[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb) {
 #pragma unroll
@@ -238,33 +228,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
             if (p < np) {
                 const auto ai = ldfrag<OP, DK>(bK, ibs[p] * 16 + ln, kb * 32 + 8 * lg);
                 const auto bt = ldfrag<OP, DK>(bK, tbs[p] * 16 + ln, kb * 32 + 8 * lg);
-                const auto bq = ldfrag<OP, DK>(bQ, tbs[p] * 16 + ln, kb * 32 + 8 * lg);
                 M::mma(accG[p], ai, bt);
-                M::mma(accP[p], ai, bq);
             }
         }
     }
-    // accG[p][r] = k_i . k_t, accP[p][r] = k_i . q_t for i = ib*16 + 4lg + r, t = tb*16 + ln.
-    // Masked values: A^T block (row i, column t) and P (row t, column i).
-    auto masked = [&](int tb, int ib, f32x4 g_, f32x4 p_, f32x4 &av) {
+    // accG[p][r] = k_i . k_t for i = ib*16 + 4lg + r, t = tb*16 + ln.  Masked value: the A^T
+    // block (row i, column t).
+    auto masked = [&](int tb, int ib, f32x4 g_, f32x4 &av) {
         const int t = tb * 16 + ln;
         const float gt = sG[t];
         const float bt_ = sBeta[t];
         const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
-        f32x4 pv4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = ib * 16 + 4 * lg + r;
-            const float dec = (i <= t) ? __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
-            av[r] = (i < t) ? bt_ * g_[r] * dec : 0.f;
-            pv4[r] = p_[r] * dec;
+            av[r] = (i < t) ? bt_ * g_[r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
         }
-        M::put4((OP *)(bP + swz<OP, kChunk>(t, ib * 16 + 4 * lg)), pv4);
     };
     f32x4 nT, a1, a2;
-    masked(wave, wave, accG[0], accP[0], nT);
-    masked(tb0, ib0, accG[1], accP[1], a1);
-    if (np == 3) masked(3, ib1, accG[2], accP[2], a2);
+    masked(wave, wave, accG[0], nT);
+    masked(tb0, ib0, accG[1], a1);
+    if (np == 3) masked(3, ib1, accG[2], a2);
     // N (accumulator layout of the strictly lower diagonal block, row i, column t)
     f32x4 nC;
     {
@@ -278,15 +262,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
             nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
         }
     }
-    // zero blocks above the diagonal of T' and P: wave w clears blocks (w, j), j > w
+    // zero blocks above the diagonal of T': wave w clears blocks (w, j), j > w
 #pragma unroll
     for (int j = 1; j < 4; ++j) {
-        if (j > wave) {
-            M::put4((OP *)(bP + swz<OP, kChunk>(d0 + ln, 16 * j + 4 * lg)),
-                    f32x4{0.f, 0.f, 0.f, 0.f});
+        if (j > wave)
             M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), 16 * j + 4 * lg)),
                     f32x4{0.f, 0.f, 0.f, 0.f});
-        }
     }
     // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0.  C = the
     // accumulator layout of a block, T = of its transpose (which is the row layout of it).
@@ -304,7 +285,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
     f32x4 xC = p2C, xT = p2T;
     mm16s(xC, p2T, n8C);
     mm16s(xT, n8C, p2T);
-    __syncthreads();   // K and Q are dead: their space now holds A and the X blocks
+    __syncthreads();   // K is dead: its space now holds A and the X blocks
 
     // ---- phase 3 (stores): A blocks, X_ww in the row layout, T' diagonal block ----
     *(f32x4 *)(sA + (tb0 * 16 + ln) * L::LDA + ib0 * 16 + 4 * lg) = a1;
@@ -365,8 +346,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
 constexpr int kLoaders = 2;
 
 // One pipeline stage: K rows (internal token order, swizzled), Q rows (swizzled), the record
-// (T', P, g) and the V tile (rows = tokens, plain).  Three stages when they fit in LDS, so
-// that the copies of a chunk have two chunk-steps to arrive; two otherwise.
+// (T', g), P (formed by the loader waves) and the V tile (rows = tokens, plain).  Three stages
+// when they fit in LDS, so that the copies of a chunk have two chunk-steps to arrive; two
+// otherwise.
 template <int DK, int DVT>
 struct LdsSplit {
     static constexpr int al(int x) { return (x + 255) & ~255; }
@@ -375,7 +357,8 @@ struct LdsSplit {
     static constexpr int sK = 0;
     static constexpr int sQ = szRow;
     static constexpr int sRec = 2 * szRow;
-    static constexpr int sV = sRec + kPrepRecordBytes;
+    static constexpr int sP = sRec + kPrepRecordBytes;  // [64][64] bf16, swizzled
+    static constexpr int sV = sP + kChunk * kChunk * 2;
     static constexpr int stage = al(sV + szV);
     static constexpr int nst = 3 * stage <= 160 * 1024 ? 3 : 2;
     static constexpr int total = nst * stage;
@@ -412,9 +395,9 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
     constexpr int KG = DK / 8;             // 16-byte granules per key row
     constexpr int CK = L::szRow / 1024;    // 1 KiB copies per K (or Q) tile
     constexpr int CV = L::szV / 1024 > 0 ? L::szV / 1024 : 1;   // ... per V tile
-    constexpr int CR = kRecG / 1024;       // ... per T' + P
+    constexpr int CR = kRecG / 1024;       // ... per T'
     constexpr bool kY = (MODE == kModeScan);
-    static_assert(CK % kLoaders == 0 && CR % kLoaders == 0, "copy split");
+    static_assert(CK % 2 == 0 && CR % 2 == 0, "copy split");
 
     __shared__ __align__(16) unsigned char smem[L::total];
 
@@ -470,33 +453,21 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 
     // ================================================================ loader waves
     if (loader) {
-        // Every operand tile is a set of whole token rows, so both loader waves only issue
-        // direct-to-LDS copies (16 bytes per lane; lane l lands at the wave's LDS pointer +
-        // 16 l) and never touch LDS otherwise.  Copy j of a tile fills its bytes
-        // [1024 j, 1024 j + 1024); the lane's source row and column follow from the
-        // destination through the swizzle and, for K, the internal token order.  Rows past
-        // the end of the job repeat its last row: they meet zero rows and columns of T'.
+        // Every operand tile is a set of whole token rows, copied global -> LDS by the
+        // direct-to-LDS loads (16 bytes per lane; lane l lands at the wave's LDS pointer +
+        // 16 l).  Copy j of a tile fills its bytes [1024 j, 1024 j + 1024); the lane's source
+        // row and column follow from the destination through the swizzle and, for K, the
+        // internal token order.  Rows past the end of the job repeat its last row: they meet
+        // zero rows and columns of T'.  P = lower_incl(Q K^T (.) Gamma) is formed in LDS from
+        // the copied K, Q and g.
+        //   three stages: wave 0 only copies (chunk c+2 during iteration c, into the stage
+        //     iteration c-1 finished reading; it makes no other LDS access, so nothing waits
+        //     on these copies before the end of the iteration) and wave 1 only forms P of
+        //     chunk c+1, whose copies completed before the barrier that began iteration c;
+        //   two stages: both waves copy chunk c+1, wait for it, and form half of its P.
         typedef __attribute__((address_space(3))) void lds_void;
+        constexpr int CW = NST == 3 ? 1 : 2;                  // copying waves
         const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;  // bytes
-        // per-lane (row, byte column) of this wave's copies
-        int kr[CK / kLoaders], kc[CK / kLoaders], qr[CK / kLoaders], qc[CK / kLoaders];
-#pragma unroll
-        for (int j = 0; j < CK / kLoaders; ++j) {
-            const int P = 64 * (wave + kLoaders * j) + lane;     // granule of the tile
-            const int r = P / KG, pg = P % KG;
-            const int lgq = pg ^ swz_key<OP, DK>(r);              // logical granule
-            kr[j] = split_orig(r);
-            kc[j] = 16 * lgq;
-            qr[j] = r;
-            qc[j] = 16 * lgq;
-        }
-        int vr[CV], vc[CV];
-#pragma unroll
-        for (int j = 0; j < CV; ++j) {
-            const int byte = 1024 * j + 16 * lane;
-            vr[j] = byte / (DVT * 2);
-            vc[j] = byte % (DVT * 2);
-        }
         const int vcol0 = mpart ? 0 : job.col0;   // the M part copies (unused) V columns
         auto copy = [&](auto stc, int c) {
             constexpr int ST = decltype(stc)::value;
@@ -510,73 +481,143 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             const unsigned char *rec = (const unsigned char *)a.prep +
                                        ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
 #pragma unroll
-            for (int j = 0; j < CK / kLoaders; ++j) {
-                const int jj = wave + kLoaders * j;
-                const int r = kr[j] < last ? kr[j] : last;
-                __builtin_amdgcn_global_load_lds((const void *)(ck + (unsigned)r * rsK + kc[j]),
-                                                 (lds_void *)(stg + L::sK + 1024 * jj), 16, 0, 0);
-            }
-            if (kY) {
-#pragma unroll
-                for (int j = 0; j < CK / kLoaders; ++j) {
-                    const int jj = wave + kLoaders * j;
-                    const int r = qr[j] < last ? qr[j] : last;
-                    __builtin_amdgcn_global_load_lds((const void *)(cq + (unsigned)r * rsK + qc[j]),
-                                                     (lds_void *)(stg + L::sQ + 1024 * jj), 16, 0,
-                                                     0);
+            for (int j = 0; j < CK / CW; ++j) {
+                const int jj = wave + CW * j;
+                const int P = 64 * jj + lane;                      // granule of the tile
+                const int r = P / KG, pg = P % KG;
+                const int lgq = pg ^ swz_key<OP, DK>(r);           // logical granule
+                const int rk = split_orig(r) < last ? split_orig(r) : last;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(ck + (unsigned)rk * rsK + 16 * lgq),
+                    (lds_void *)(stg + L::sK + 1024 * jj), 16, 0, 0);
+                if (kY) {
+                    const int rq = r < last ? r : last;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)(cq + (unsigned)rq * rsK + 16 * lgq),
+                        (lds_void *)(stg + L::sQ + 1024 * jj), 16, 0, 0);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < CR / kLoaders; ++j) {
-                const int jj = wave + kLoaders * j;
+            for (int j = 0; j < CR / CW; ++j) {
+                const int jj = wave + CW * j;
                 __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * (64 * jj + lane)),
                                                  (lds_void *)(stg + L::sRec + 1024 * jj), 16, 0, 0);
             }
-            // g (both waves write the same 256 bytes) and the V tile (both waves copy it)
+            // g (with two copying waves both write the same 256 bytes)
             __builtin_amdgcn_global_load_lds((const void *)(rec + kRecG + 4 * lane),
                                              (lds_void *)(stg + L::sRec + kRecG), 4, 0, 0);
 #pragma unroll
-            for (int j = 0; j < CV; ++j) {
-                if (L::szV >= 1024 || 16 * lane < L::szV) {
-                    const int r = vr[j] < last ? vr[j] : last;
+            for (int j = 0; j < (CV + CW - 1) / CW; ++j) {
+                const int jj = wave + CW * j;
+                if (jj < CV) {
+                    const int byte = 1024 * jj + 16 * lane;
+                    const int r0 = byte / (DVT * 2), cb = byte % (DVT * 2);
+                    const int r = r0 < last ? r0 : last;
                     __builtin_amdgcn_global_load_lds(
-                        (const void *)(cv + (unsigned)r * rsV + vc[j]),
-                        (lds_void *)(stg + L::sV + 1024 * j), 16, 0, 0);
+                        (const void *)(cv + (unsigned)r * rsV + cb),
+                        (lds_void *)(stg + L::sV + 1024 * jj), 16, 0, 0);
                 }
             }
         };
-        constexpr int kCopies = CK / kLoaders * (kY ? 2 : 1) + CR / kLoaders + 1 + CV;
-        // Wait for the copies of the chunk the scan reads next.  With three stages those
-        // were issued one step before the kCopies copies just issued (and copies complete in
-        // order); with two stages they are the copies just issued.
-        auto wait_prev = [&](bool issued_next) {
-            if (NST == 3 && issued_next)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        };
-        auto step = [&](auto stn, int c) {   // iteration c: issue chunk c + NST - 1
-            const int cn = c + NST - 1;
-            if (cn < nchunks) copy(stn, cn);
-            wait_prev(cn < nchunks);
-            __syncthreads();
+        // P of the chunk in stage ST from its K and Q rows and g.  Blocks (t-block, i-block):
+        // (0,0) (1,0) (1,1) (2,0) (3,0) (2,1) (2,2) (3,1) (3,2) (3,3), split in halves when
+        // two waves share the work; the blocks (0,1) and (2,3) that the scan reads are zero.
+        // Accumulator [r] = k_i . q_t, i = 16 ib + 4 lg + r, t = 16 tb + ln: row t, columns
+        // i .. i + 3 of P.
+        auto make_p = [&](auto stc, auto nwc, int pw) {
+            constexpr int ST = decltype(stc)::value;
+            constexpr int NB = 10 / decltype(nwc)::value;
+            unsigned char *stg = smem + ST * L::stage;
+            const unsigned char *bK = stg + L::sK;
+            const unsigned char *bQ = stg + L::sQ;
+            const float *sG = (const float *)(stg + L::sRec + kRecG);
+            unsigned char *bP = stg + L::sP;
+            constexpr int kTb[10] = {0, 1, 1, 2, 3, 2, 2, 3, 3, 3};
+            constexpr int kIb[10] = {0, 0, 1, 0, 0, 1, 2, 1, 2, 3};
+            f32x4 acc[NB];
+#pragma unroll
+            for (int p = 0; p < NB; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+                for (int p = 0; p < NB; ++p) {
+                    const int tb = kTb[pw * NB + p], ib = kIb[pw * NB + p];
+                    M::mma(acc[p], ldfrag<OP, DK>(bK, split_pos(ib * 16 + ln), kb * 32 + 8 * lg),
+                           ldfrag<OP, DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg));
+                }
+#pragma unroll
+            for (int p = 0; p < NB; ++p) {
+                const int tb = kTb[pw * NB + p], ib = kIb[pw * NB + p];
+                const int t = tb * 16 + ln;
+                const float gt = sG[t];
+                const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+                f32x4 pv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ib * 16 + 4 * lg + r;
+                    pv[r] = (i <= t) ? acc[p][r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+                }
+                M::put4((OP *)(bP + swz<OP, kChunk>(t, ib * 16 + 4 * lg)), pv);
+            }
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            if (NB == 10 || pw == 0) M::put4((OP *)(bP + swz<OP, kChunk>(ln, 16 + 4 * lg)), z);
+            if (NB == 10 || pw == 1) M::put4((OP *)(bP + swz<OP, kChunk>(32 + ln, 48 + 4 * lg)), z);
         };
         const std::integral_constant<int, 0> s0{};
         const std::integral_constant<int, 1> s1{};
         const std::integral_constant<int, 2> s2{};
-        if (nchunks > 0) {
-            copy(s0, 0);
-            if (NST == 3 && nchunks > 1) copy(s1, 1);
-            wait_prev(NST == 3 && nchunks > 1);
-            __syncthreads();
-        }
         if constexpr (NST == 3) {
-            for (int c = 0; c < nchunks; c += 3) {
-                step(s2, c);
-                if (c + 1 < nchunks) step(s0, c + 1);
-                if (c + 2 < nchunks) step(s1, c + 2);
+            const std::integral_constant<int, 1> one{};
+            if (wave == 0) {
+                if (nchunks > 0) {
+                    copy(s0, 0);
+                    if (nchunks > 1) copy(s1, 1);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    __syncthreads();    // chunks 0 and 1 are in LDS
+                    __syncthreads();    // chunk 0 has its P
+                }
+                auto step = [&](auto stc, int c) {
+                    if (c + 2 < nchunks) copy(stc, c + 2);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    __syncthreads();
+                };
+                for (int c = 0; c < nchunks; c += 3) {
+                    step(s2, c);
+                    if (c + 1 < nchunks) step(s0, c + 1);
+                    if (c + 2 < nchunks) step(s1, c + 2);
+                }
+            } else {
+                if (nchunks > 0) {
+                    __syncthreads();
+                    if (kY) make_p(s0, one, 0);
+                    __syncthreads();
+                }
+                auto step = [&](auto stp, int c) {
+                    if (kY && c + 1 < nchunks) make_p(stp, one, 0);
+                    __syncthreads();
+                };
+                for (int c = 0; c < nchunks; c += 3) {
+                    step(s1, c);
+                    if (c + 1 < nchunks) step(s2, c + 1);
+                    if (c + 2 < nchunks) step(s0, c + 2);
+                }
             }
         } else {
+            const std::integral_constant<int, 2> two{};
+            if (nchunks > 0) {
+                copy(s0, 0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (kY) make_p(s0, two, wave);
+                __syncthreads();
+            }
+            auto step = [&](auto stn, int c) {
+                if (c + 1 < nchunks) {
+                    copy(stn, c + 1);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    if (kY) make_p(stn, two, wave);
+                }
+                __syncthreads();
+            };
             for (int c = 0; c < nchunks; c += 2) {
                 step(s1, c);
                 if (c + 1 < nchunks) step(s0, c + 1);
@@ -621,7 +662,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         const unsigned char *bKc = stg + L::sK;
         const unsigned char *bQc = stg + L::sQ;
         const unsigned char *bTc = stg + L::sRec + kRecT;
-        const unsigned char *bPc = stg + L::sRec + kRecP;
+        const unsigned char *bPc = stg + L::sP;
         const float *sGc = (const float *)(stg + L::sRec + kRecG);
         const unsigned char *bVc = stg + L::sV;
         const long long t0 = job.tok0 + (long long)c * kChunk;
@@ -787,7 +828,10 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         }
         __syncthreads();
     };
-    if (nchunks > 0) __syncthreads();     // the prologue's barrier (chunk 0 staged)
+    if (nchunks > 0) {                    // the prologue's barriers (chunk 0 staged)
+        __syncthreads();
+        if (NST == 3) __syncthreads();
+    }
     if constexpr (NST == 3) {
         for (int c = 0; c < nchunks; c += 3) {
             chunk(std::integral_constant<int, 0>{}, c);

@@ -55,9 +55,9 @@ def test_plans_for_the_workloads(lib):
     # 512 chains: enough work without splitting
     t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
     assert s == -1
-    # bf16: one 16640-byte record (T', P, g) per chunk slot and head
+    # bf16: one 8448-byte record (T', g) per chunk slot and head
     slots = 270336 // 64 + 32
-    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == slots * 16 * 16640
+    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == slots * 16 * 8448
     # fp32 without segments needs no workspace
     assert gdn.gdn_prefill_workspace_bytes(1, 256, 2, 64, 64, 0) == 0
     # fp32 tiles stay within the LDS budget
@@ -112,7 +112,7 @@ def prefill(lib, **kw):
     (dict(s0=8 * G, sf=8 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # partial overlap
     (dict(s0=8 * G, sf=8 * G, seg=2), gdn.GDN_ERR_INVALID_ARGUMENT),  # in place + split
     (dict(ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # bf16 chunk records
-    (dict(wsb=6 * 2 * 16640 - 1), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+    (dict(wsb=6 * 2 * 8448 - 1), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
     (dict(seg=2, ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # segments too
     (dict(seg=2, ws=9 * G, wsb=64), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
 ])
