@@ -346,7 +346,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
 constexpr int kLoaders = 2;
 
 // One pipeline stage: K rows (internal token order, swizzled), Q rows (swizzled), the record
-// (T', g), P (formed by the loader waves) and the V tile (rows = tokens, plain).  Three stages
+// (T', g), P and the decay factors (formed by the loader waves) and the V tile (rows =
+// tokens, plain).  Three stages
 // when they fit in LDS, so that the copies of a chunk have two chunk-steps to arrive; two
 // otherwise.
 template <int DK, int DVT>
@@ -358,7 +359,9 @@ struct LdsSplit {
     static constexpr int sQ = szRow;
     static constexpr int sRec = 2 * szRow;
     static constexpr int sP = sRec + kPrepRecordBytes;  // [64][64] bf16, swizzled
-    static constexpr int sV = sP + kChunk * kChunk * 2;
+    static constexpr int sGam = sP + kChunk * kChunk * 2;   // gamma_t = 2^g_t, fp32
+    static constexpr int sRho = sGam + kChunk * 4;          // gamma_C / gamma_t, fp32
+    static constexpr int sV = sRho + kChunk * 4;
     static constexpr int stage = al(sV + szV);
     static constexpr int nst = 3 * stage <= 160 * 1024 ? 3 : 2;
     static constexpr int total = nst * stage;
@@ -563,6 +566,15 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             if (NB == 10 || pw == 0) M::put4((OP *)(bP + swz<OP, kChunk>(ln, 16 + 4 * lg)), z);
             if (NB == 10 || pw == 1) M::put4((OP *)(bP + swz<OP, kChunk>(32 + ln, 48 + 4 * lg)), z);
         };
+        // gamma_t = 2^g_t and gamma_C / gamma_t of the chunk in stage ST, one token per lane
+        auto make_gamma = [&](auto stc) {
+            constexpr int ST = decltype(stc)::value;
+            unsigned char *stg = smem + ST * L::stage;
+            const float *sG = (const float *)(stg + L::sRec + kRecG);
+            const float gt = sG[lane], gC = sG[kChunk - 1];
+            ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt);
+            ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f(gC - gt);
+        };
         const std::integral_constant<int, 0> s0{};
         const std::integral_constant<int, 1> s1{};
         const std::integral_constant<int, 2> s2{};
@@ -589,11 +601,15 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             } else {
                 if (nchunks > 0) {
                     __syncthreads();
+                    make_gamma(s0);
                     if (kY) make_p(s0, one, 0);
                     __syncthreads();
                 }
                 auto step = [&](auto stp, int c) {
-                    if (kY && c + 1 < nchunks) make_p(stp, one, 0);
+                    if (c + 1 < nchunks) {
+                        make_gamma(stp);
+                        if (kY) make_p(stp, one, 0);
+                    }
                     __syncthreads();
                 };
                 for (int c = 0; c < nchunks; c += 3) {
@@ -607,6 +623,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             if (nchunks > 0) {
                 copy(s0, 0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (wave == 0) make_gamma(s0);
                 if (kY) make_p(s0, two, wave);
                 __syncthreads();
             }
@@ -614,6 +631,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                 if (c + 1 < nchunks) {
                     copy(stn, c + 1);
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    if (wave == 0) make_gamma(stn);
                     if (kY) make_p(stn, two, wave);
                 }
                 __syncthreads();
@@ -656,6 +674,10 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                     S[g][m][i] = x;
                 }
     }
+    // The state is held as S = 2^ls * Shat (ls uniform, in [-32, 0]): the per-chunk decay
+    // gamma_C goes into ls instead of a pass over the registers, and Shat is rescaled only
+    // when ls would fall below -32.
+    float ls = 0.f;
     auto chunk = [&](auto stc, int c) {
         constexpr int ST = decltype(stc)::value;
         const unsigned char *stg = smem + ST * L::stage;
@@ -664,9 +686,12 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         const unsigned char *bTc = stg + L::sRec + kRecT;
         const unsigned char *bPc = stg + L::sP;
         const float *sGc = (const float *)(stg + L::sRec + kRecG);
+        const float *sGam = (const float *)(stg + L::sGam);
+        const float *sRho = (const float *)(stg + L::sRho);
         const unsigned char *bVc = stg + L::sV;
         const long long t0 = job.tok0 + (long long)c * kChunk;
         const int nv = nvalid_of(c);
+        const float sp = __builtin_amdgcn_exp2f(ls);     // S = sp * Shat
         // Fragments are loaded one step ahead of the MFMAs that use them; the scheduling
         // fences keep the compiler from sinking each load next to its use.
         bf16x8 fk[2][4], fq[2][4], ft[6];
@@ -693,7 +718,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         };
 
         // ---- K S and S^T Q^T from the chunk-start state ----
-        f32x4 accYt[NG][4], acc_ks[NG][4], vv[NG][4], gam[4];
+        f32x4 accYt[NG][4], acc_ks[NG][4], vv[NG][4], gam[4], rho[4];
         bf16x8 Sb[NG][KBD];
         ld_kq(0, 0);
 #pragma unroll
@@ -701,7 +726,8 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             // rows of K S held by this lane: internal 16 tb + 4 lg + i, i.e. tokens o0 + i;
             // V[o0 .. o0 + 3][column] by one transposing read of the V rows
             const int o0 = split_orig(tb * 16 + 4 * lg);
-            gam[tb] = *(const f32x4 *)(sGc + o0);
+            gam[tb] = *(const f32x4 *)(sGam + o0) * sp;
+            rho[tb] = *(const f32x4 *)(sRho + o0);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int col = c0 - job.col0 + 16 * g + 4 * (ln & 3);
@@ -751,7 +777,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         for (int g = 0; g < NG; ++g) {
             f32x4 R[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) R[tb] = vv[g][tb] - exp2x4(gam[tb]) * acc_ks[g][tb];
+            for (int tb = 0; tb < 4; ++tb) R[tb] = vv[g][tb] - gam[tb] * acc_ks[g][tb];
             const bf16x8 Rb0 = pack8s(R[0], R[1]);
             const bf16x8 Rb1 = pack8s(R[2], R[3]);
 #pragma unroll
@@ -767,26 +793,33 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         for (int m = 0; m < MBK; ++m) fkt[1][m] = frag_kt(m, 1);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U ----
-        const float gC = sGc[kChunk - 1];
+        // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U / 2^ls ----
         {
+            float ln_ = ls + sGc[kChunk - 1];
+            ln_ = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ln_)));
+            if (ln_ < -32.f) {                     // fold the scale into Shat (rare)
+                const float f = __builtin_amdgcn_exp2f(ln_);
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+#pragma unroll
+                    for (int m = 0; m < MBK; ++m) S[g][m] *= f;
+                ln_ = 0.f;
+            }
+            ls = ln_;
+            const float inv = __builtin_amdgcn_exp2f(-ln_);
             bf16x8 Ub0[NG], Ub1[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 f32x4 Us[4];
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) Us[mb] = U[g][mb] * exp2x4(gC - gam[mb]);
+                for (int mb = 0; mb < 4; ++mb) Us[mb] = U[g][mb] * (rho[mb] * inv);
                 Ub0[g] = pack8s(Us[0], Us[1]);
                 Ub1[g] = pack8s(Us[2], Us[3]);
             }
-            const float gamC = __builtin_amdgcn_exp2f(gC);
 #pragma unroll
             for (int m = 0; m < MBK; ++m)
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    S[g][m] *= gamC;
-                    M::mma(S[g][m], fkt[0][m], Ub0[g]);
-                }
+                for (int g = 0; g < NG; ++g) M::mma(S[g][m], fkt[0][m], Ub0[g]);
             __builtin_amdgcn_sched_barrier(0);
             if (kY) {
 #pragma unroll
@@ -809,7 +842,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                 const bf16x8 Uu1 = pack8s(U[g][2], U[g][3]);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    accYt[g][tb] *= __builtin_amdgcn_exp2f(sGc[tb * 16 + ln]);
+                    accYt[g][tb] *= sGam[tb * 16 + ln] * sp;
                     M::mma(accYt[g][tb], Uu0, ft[tb]);
                 }
                 M::mma(accYt[g][2], Uu1, ft[4]);
@@ -859,6 +892,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             dst = a.segB + ((long long)job.entry * H + job.h) * DK * DV + c0;
         }
         if (dst) {
+            const float sp = __builtin_amdgcn_exp2f(ls);
 #pragma unroll
             for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -866,7 +900,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         dst[(long long)split_orig(16 * m + 4 * lg + i) * ld + 16 * g + ln] =
-                            S[g][m][i];
+                            S[g][m][i] * sp;
         }
     }
 }
