@@ -359,12 +359,13 @@ struct LdsSplit {
     static constexpr int sQ = szRow;
     static constexpr int sRec = 2 * szRow;
     static constexpr int sP = sRec + kPrepRecordBytes;  // [64][64] bf16, swizzled
-    static constexpr int sGam = sP + kChunk * kChunk * 2;   // gamma_t = 2^g_t, fp32
-    static constexpr int sRho = sGam + kChunk * 4;          // gamma_C / gamma_t, fp32
+    static constexpr int sGam = sP + kChunk * kChunk * 2;   // gamma_t 2^ls, fp32
+    static constexpr int sRho = sGam + kChunk * 4;          // gamma_C / gamma_t / 2^ls', fp32
     static constexpr int sV = sRho + kChunk * 4;
     static constexpr int stage = al(sV + szV);
-    static constexpr int nst = 3 * stage <= 160 * 1024 ? 3 : 2;
-    static constexpr int total = nst * stage;
+    static constexpr int nst = 3 * stage + 16 <= 160 * 1024 ? 3 : 2;
+    static constexpr int sFlag = nst * stage;                // two ints (two-stage loaders)
+    static constexpr int total = sFlag + 16;
 };
 
 // Four bf16 values by the gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each
@@ -442,6 +443,10 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
     if (MODE == kModeAug) {
         if (job.seg == job.nseg - 1) return;
         if (mpart && job.seg == 0) return;
+    }
+    if constexpr (NST == 2) {
+        if (tid < 2) ((volatile int *)(smem + L::sFlag))[tid] = -1;
+        __syncthreads();
     }
     const int H = a.H;
     const int DV = a.dv;
@@ -566,14 +571,27 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             if (NB == 10 || pw == 0) M::put4((OP *)(bP + swz<OP, kChunk>(ln, 16 + 4 * lg)), z);
             if (NB == 10 || pw == 1) M::put4((OP *)(bP + swz<OP, kChunk>(32 + ln, 48 + 4 * lg)), z);
         };
-        // gamma_t = 2^g_t and gamma_C / gamma_t of the chunk in stage ST, one token per lane
-        auto make_gamma = [&](auto stc) {
+        // The scan holds its state as S = 2^ls Shat.  ls starts at 0 and after each chunk
+        // becomes ls + g_C, or 0 when that would fall below -32 (the scan then rescales Shat);
+        // both sides follow the same rule on the same g_C, so they agree bit for bit.  The
+        // loader folds 2^ls into the factors it leaves in the stage:
+        //   sGam[t] = gamma_t 2^ls,  sRho[t] = (gamma_C / gamma_t) / 2^ls'
+        // (ls of the chunk, ls' of the next).
+        float lsl = 0.f;
+        auto prepare = [&](auto stc, auto nwc, int pw, bool gam_writer) {
             constexpr int ST = decltype(stc)::value;
             unsigned char *stg = smem + ST * L::stage;
             const float *sG = (const float *)(stg + L::sRec + kRecG);
             const float gt = sG[lane], gC = sG[kChunk - 1];
-            ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt);
-            ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f(gC - gt);
+            const float lsc = lsl;
+            float lsn = lsc + gC;
+            if (lsn < -32.f) lsn = 0.f;
+            if (gam_writer) {
+                ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt + lsc);
+                ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
+            }
+            if (kY) make_p(stc, nwc, pw);
+            lsl = lsn;
         };
         const std::integral_constant<int, 0> s0{};
         const std::integral_constant<int, 1> s1{};
@@ -601,15 +619,11 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             } else {
                 if (nchunks > 0) {
                     __syncthreads();
-                    make_gamma(s0);
-                    if (kY) make_p(s0, one, 0);
+                    prepare(s0, one, 0, true);
                     __syncthreads();
                 }
                 auto step = [&](auto stp, int c) {
-                    if (c + 1 < nchunks) {
-                        make_gamma(stp);
-                        if (kY) make_p(stp, one, 0);
-                    }
+                    if (c + 1 < nchunks) prepare(stp, one, 0, true);
                     __syncthreads();
                 };
                 for (int c = 0; c < nchunks; c += 3) {
@@ -620,19 +634,25 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             }
         } else {
             const std::integral_constant<int, 2> two{};
+            // the two waves copy alternate 1 KiB pieces of every tile, so each waits for the
+            // other's copies (a flag per wave in LDS) before it reads the K and Q rows
+            volatile int *flag = (volatile int *)(smem + L::sFlag);
+            auto both_copied = [&](int c) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (lane == 0) flag[wave] = c;
+                while (flag[1 - wave] < c) __builtin_amdgcn_s_sleep(1);
+            };
             if (nchunks > 0) {
                 copy(s0, 0);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                if (wave == 0) make_gamma(s0);
-                if (kY) make_p(s0, two, wave);
+                both_copied(0);
+                prepare(s0, two, wave, wave == 0);
                 __syncthreads();
             }
             auto step = [&](auto stn, int c) {
                 if (c + 1 < nchunks) {
                     copy(stn, c + 1);
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    if (wave == 0) make_gamma(stn);
-                    if (kY) make_p(stn, two, wave);
+                    both_copied(c + 1);
+                    prepare(stn, two, wave, wave == 0);
                 }
                 __syncthreads();
             };
@@ -691,17 +711,9 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         const unsigned char *bVc = stg + L::sV;
         const long long t0 = job.tok0 + (long long)c * kChunk;
         const int nv = nvalid_of(c);
-        const float sp = __builtin_amdgcn_exp2f(ls);     // S = sp * Shat
         // Fragments are loaded one step ahead of the MFMAs that use them; the scheduling
         // fences keep the compiler from sinking each load next to its use.
         bf16x8 fk[2][4], fq[2][4], ft[6];
-        auto ld_kq = [&](int kb, int buf) {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                fk[buf][tb] = ldfrag<OP, DK>(bKc, tb * 16 + ln, kb * 32 + 8 * lg);
-                if (kY) fq[buf][tb] = ldfrag<OP, DK>(bQc, tb * 16 + ln, kb * 32 + 8 * lg);
-            }
-        };
         auto frag64 = [&](const unsigned char *base, int row, int k0) {
             return ldfrag<OP, kChunk>(base, row, k0 + 8 * lg);
         };
@@ -717,24 +729,11 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
 
-        // ---- K S and S^T Q^T from the chunk-start state ----
-        f32x4 accYt[NG][4], acc_ks[NG][4], vv[NG][4], gam[4], rho[4];
+        // ---- K S from the chunk-start state (the head of the state chain) ----
+        f32x4 accYt[NG][4], acc_ks[NG][4];
         bf16x8 Sb[NG][KBD];
-        ld_kq(0, 0);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            // rows of K S held by this lane: internal 16 tb + 4 lg + i, i.e. tokens o0 + i;
-            // V[o0 .. o0 + 3][column] by one transposing read of the V rows
-            const int o0 = split_orig(tb * 16 + 4 * lg);
-            gam[tb] = *(const f32x4 *)(sGam + o0) * sp;
-            rho[tb] = *(const f32x4 *)(sRho + o0);
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int col = c0 - job.col0 + 16 * g + 4 * (ln & 3);
-                const bf16x4 v4 = ldtr(bVc + ((o0 + (ln >> 2)) * DVT + col) * 2);
-                vv[g][tb] = mpart ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_convertvector(v4, f32x4);
-            }
-        }
+        for (int tb = 0; tb < 4; ++tb) fk[0][tb] = ldfrag<OP, DK>(bKc, tb * 16 + ln, 8 * lg);
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -742,14 +741,13 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                acc_ks[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                accYt[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int tb = 0; tb < 4; ++tb) acc_ks[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
             if (kb + 1 < KBD) {
-                ld_kq(kb + 1, (kb + 1) & 1);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    fk[(kb + 1) & 1][tb] = ldfrag<OP, DK>(bKc, tb * 16 + ln, (kb + 1) * 32 + 8 * lg);
             } else {
                 // T' fragments for U = T' R: rows 0..31 use tokens 0..31 only
 #pragma unroll
@@ -761,23 +759,33 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    M::mma(acc_ks[g][tb], fk[kb & 1][tb], Sb[g][kb]);
-                    if (kY) M::mma(accYt[g][tb], Sb[g][kb], fq[kb & 1][tb]);
-                }
+                for (int g = 0; g < NG; ++g) M::mma(acc_ks[g][tb], fk[kb & 1][tb], Sb[g][kb]);
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- R = V - diag(gamma) K S;  U = T' R ----
-        bf16x8 fkt[2][MBK];
-#pragma unroll
-        for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+        // ---- R = V - diag(gamma 2^ls) K Shat;  U = T' R ----
+        // the rows of K S this lane holds are internal 16 tb + 4 lg + i, i.e. tokens o0 + i
+        f32x4 gam[4], rho[4];
         f32x4 U[NG][4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int o0 = split_orig(tb * 16 + 4 * lg);
+            gam[tb] = *(const f32x4 *)(sGam + o0);
+            rho[tb] = *(const f32x4 *)(sRho + o0);
+        }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             f32x4 R[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) R[tb] = vv[g][tb] - gam[tb] * acc_ks[g][tb];
+            for (int tb = 0; tb < 4; ++tb) {
+                // V[o0 .. o0 + 3][column] by one transposing read of the V rows
+                const int o0 = split_orig(tb * 16 + 4 * lg);
+                const int col = c0 - job.col0 + 16 * g + 4 * (ln & 3);
+                const bf16x4 v4 = ldtr(bVc + ((o0 + (ln >> 2)) * DVT + col) * 2);
+                const f32x4 vv =
+                    mpart ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_convertvector(v4, f32x4);
+                R[tb] = vv - gam[tb] * acc_ks[g][tb];
+            }
             const bf16x8 Rb0 = pack8s(R[0], R[1]);
             const bf16x8 Rb1 = pack8s(R[2], R[3]);
 #pragma unroll
@@ -789,11 +797,40 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             M::mma(U[g][3], ft[5], Rb1);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < MBK; ++m) fkt[1][m] = frag_kt(m, 1);
-        __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U / 2^ls ----
+        // ---- S^T Q^T from the chunk-start state (off the state chain: fills U's latency) ----
+        bf16x8 fkt[2][MBK];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) accYt[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kY) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) fq[0][tb] = ldfrag<OP, DK>(bQc, tb * 16 + ln, 8 * lg);
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) {
+                if (kb + 1 < KBD) {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        fq[(kb + 1) & 1][tb] =
+                            ldfrag<OP, DK>(bQc, tb * 16 + ln, (kb + 1) * 32 + 8 * lg);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) M::mma(accYt[g][tb], Sb[g][kb], fq[kb & 1][tb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+        }
+
+        // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U ----
         {
             float ln_ = ls + sGc[kChunk - 1];
             ln_ = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ln_)));
@@ -806,13 +843,12 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                 ln_ = 0.f;
             }
             ls = ln_;
-            const float inv = __builtin_amdgcn_exp2f(-ln_);
             bf16x8 Ub0[NG], Ub1[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 f32x4 Us[4];
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) Us[mb] = U[g][mb] * (rho[mb] * inv);
+                for (int mb = 0; mb < 4; ++mb) Us[mb] = U[g][mb] * rho[mb];
                 Ub0[g] = pack8s(Us[0], Us[1]);
                 Ub1[g] = pack8s(Us[2], Us[3]);
             }
@@ -821,6 +857,8 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 #pragma unroll
                 for (int g = 0; g < NG; ++g) M::mma(S[g][m], fkt[0][m], Ub0[g]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < MBK; ++m) fkt[1][m] = frag_kt(m, 1);
             if (kY) {
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) ft[tb] = frag64(bPc, tb * 16 + ln, 0);
@@ -834,7 +872,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                 for (int g = 0; g < NG; ++g) M::mma(S[g][m], fkt[1][m], Ub1[g]);
         }
 
-        // ---- Y^T = S^T Q^T diag(gamma) + U^T P^T ----
+        // ---- Y^T = Shat^T Q^T diag(gamma 2^ls) + U^T P^T ----
         if (kY) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
@@ -842,7 +880,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                 const bf16x8 Uu1 = pack8s(U[g][2], U[g][3]);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    accYt[g][tb] *= sGam[tb * 16 + ln] * sp;
+                    accYt[g][tb] *= sGam[tb * 16 + ln];
                     M::mma(accYt[g][tb], Uu0, ft[tb]);
                 }
                 M::mma(accYt[g][2], Uu1, ft[4]);
