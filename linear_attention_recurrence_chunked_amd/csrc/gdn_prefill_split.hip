@@ -532,9 +532,10 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         // two waves share the work; the blocks (0,1) and (2,3) that the scan reads are zero.
         // Accumulator [r] = k_i . q_t, i = 16 ib + 4 lg + r, t = 16 tb + ln: row t, columns
         // i .. i + 3 of P.
-        auto make_p = [&](auto stc, auto nwc, int pw) {
+        auto make_p = [&](auto stc, auto nwc, auto pwc) {
             constexpr int ST = decltype(stc)::value;
             constexpr int NB = 10 / decltype(nwc)::value;
+            constexpr int pw = decltype(pwc)::value;
             unsigned char *stg = smem + ST * L::stage;
             const unsigned char *bK = stg + L::sK;
             const unsigned char *bQ = stg + L::sQ;
@@ -578,7 +579,8 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         //   sGam[t] = gamma_t 2^ls,  sRho[t] = (gamma_C / gamma_t) / 2^ls'
         // (ls of the chunk, ls' of the next).
         float lsl = 0.f;
-        auto prepare = [&](auto stc, auto nwc, int pw, bool gam_writer) {
+        auto prepare = [&](auto stc, auto nwc, auto pwc) {
+            constexpr bool gam_writer = decltype(pwc)::value == 0;
             constexpr int ST = decltype(stc)::value;
             unsigned char *stg = smem + ST * L::stage;
             const float *sG = (const float *)(stg + L::sRec + kRecG);
@@ -590,12 +592,14 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                 ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt + lsc);
                 ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
             }
-            if (kY) make_p(stc, nwc, pw);
+            if (kY) make_p(stc, nwc, pwc);
             lsl = lsn;
         };
         const std::integral_constant<int, 0> s0{};
         const std::integral_constant<int, 1> s1{};
         const std::integral_constant<int, 2> s2{};
+        const std::integral_constant<int, 0> w0{};    // (the wave index as a constant keeps
+        const std::integral_constant<int, 1> w1{};    //  make_p's block tables in registers)
         if constexpr (NST == 3) {
             const std::integral_constant<int, 1> one{};
             if (wave == 0) {
@@ -619,11 +623,11 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             } else {
                 if (nchunks > 0) {
                     __syncthreads();
-                    prepare(s0, one, 0, true);
+                    prepare(s0, one, w0);
                     __syncthreads();
                 }
                 auto step = [&](auto stp, int c) {
-                    if (c + 1 < nchunks) prepare(stp, one, 0, true);
+                    if (c + 1 < nchunks) prepare(stp, one, w0);
                     __syncthreads();
                 };
                 for (int c = 0; c < nchunks; c += 3) {
@@ -645,14 +649,16 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             if (nchunks > 0) {
                 copy(s0, 0);
                 both_copied(0);
-                prepare(s0, two, wave, wave == 0);
+                if (wave == 0) prepare(s0, two, w0);
+                else prepare(s0, two, w1);
                 __syncthreads();
             }
             auto step = [&](auto stn, int c) {
                 if (c + 1 < nchunks) {
                     copy(stn, c + 1);
                     both_copied(c + 1);
-                    prepare(stn, two, wave, wave == 0);
+                    if (wave == 0) prepare(stn, two, w0);
+                    else prepare(stn, two, w1);
                 }
                 __syncthreads();
             };
@@ -800,6 +806,7 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 
         // ---- S^T Q^T from the chunk-start state (off the state chain: fills U's latency) ----
         bf16x8 fkt[2][MBK];
+        float gy[4];
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -815,8 +822,15 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
                         fq[(kb + 1) & 1][tb] =
                             ldfrag<OP, DK>(bQc, tb * 16 + ln, (kb + 1) * 32 + 8 * lg);
                 } else {
+                    // K^T for the first half of the update, P for U^T P^T, gamma_t 2^ls
 #pragma unroll
                     for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) ft[tb] = frag64(bPc, tb * 16 + ln, 0);
+                    ft[4] = frag64(bPc, 32 + ln, 32);
+                    ft[5] = frag64(bPc, 48 + ln, 32);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) gy[tb] = sGam[tb * 16 + ln];
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -828,6 +842,24 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         } else {
 #pragma unroll
             for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+        }
+
+        // ---- U^T P^T (before the update, so that the output's epilogue runs while the
+        //      update's products are in flight) ----
+        f32x4 accPU[NG][4];
+        if (kY) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const bf16x8 Uu0 = pack8s(U[g][0], U[g][1]);
+                const bf16x8 Uu1 = pack8s(U[g][2], U[g][3]);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    accPU[g][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    M::mma(accPU[g][tb], Uu0, ft[tb]);
+                }
+                M::mma(accPU[g][2], Uu1, ft[4]);
+                M::mma(accPU[g][3], Uu1, ft[5]);
+            }
         }
 
         // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U ----
@@ -859,12 +891,6 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < MBK; ++m) fkt[1][m] = frag_kt(m, 1);
-            if (kY) {
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) ft[tb] = frag64(bPc, tb * 16 + ln, 0);
-                ft[4] = frag64(bPc, 32 + ln, 32);
-                ft[5] = frag64(bPc, 48 + ln, 32);
-            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < MBK; ++m)
@@ -875,26 +901,15 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
         // ---- Y^T = Shat^T Q^T diag(gamma 2^ls) + U^T P^T ----
         if (kY) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const bf16x8 Uu0 = pack8s(U[g][0], U[g][1]);
-                const bf16x8 Uu1 = pack8s(U[g][2], U[g][3]);
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    accYt[g][tb] *= sGam[tb * 16 + ln];
-                    M::mma(accYt[g][tb], Uu0, ft[tb]);
-                }
-                M::mma(accYt[g][2], Uu1, ft[4]);
-                M::mma(accYt[g][3], Uu1, ft[5]);
-            }
-#pragma unroll
             for (int g = 0; g < NG; ++g)
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const int t = tb * 16 + ln;
+                    const f32x4 yv = accYt[g][tb] * gy[tb] + accPU[g][tb];
                     if (t < nv)
                         store4((OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + c0 + 16 * g +
                                    4 * lg,
-                               accYt[g][tb]);
+                               yv);
                 }
         }
         __syncthreads();
@@ -944,6 +959,614 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 }
 
 // =========================================================================================
+// Launch 2, pipelined form (bf16, 16 or 32 state columns per workgroup).  The output
+// products leave the state chain: each 16-column group has a chain wave that carries the
+// state and an output wave that forms Y, and the two meet in LDS.  During chunk step c:
+//   wave 0         issues the copies of chunk c+2 (K in the internal token order, Q, T',
+//                  V) and of g of chunk c+3, and waits only for those of the step before,
+//                  so that every copy has two chunk-steps to arrive
+//   wave 1         forms the decay factors of chunk c+1 and P of chunk c
+//   chain waves    R = V - diag(gamma 2^ls) K Shat, U = T' R and the state update of chunk
+//                  c; they leave bf16 U and bf16 Shat (start of chunk c+1) in LDS
+//   output waves   Shat^T Q^T of chunk c, then Y of chunk c-1 = diag(gamma 2^ls) Q Shat
+//                  + P U, stored to y
+// One barrier per chunk step.  P, U and Shat have one LDS buffer each: the output wave
+// raises a flag once it holds its copy in registers, and the writer of the next value
+// waits for that flag.
+// =========================================================================================
+// Swizzle of the K and Q tiles of the pipelined scan.  For 256-byte rows the key rotates the
+// row's low four bits and flips bit 1 on odd 16-row blocks: the 16 consecutive rows of a
+// fragment load, and the rows {16 b + 0..7, 16 b + 16..23} that a fragment of K in the
+// internal token order touches, stay on distinct granules, and the transposing reads of
+// K^T (8 rows x 4 granules per half-wave) meet at most two rows per bank.  128-byte rows
+// keep the key of swz_key.
+template <int DK>
+__device__ __forceinline__ int kq_key(int row)
+{
+    if constexpr (DK * 2 >= 256) {
+        const int x = row & 15;
+        return (((x & 3) << 2) | ((x >> 2) & 3)) ^ (((row >> 4) & 1) << 1);
+    } else {
+        return swz_key<uint16_t, DK>(row);
+    }
+}
+template <int DK>
+__device__ __forceinline__ int swz_kq(int row, int col)
+{
+    const int b = col * 2;
+    return row * (DK * 2) + (((b >> 4) ^ kq_key<DK>(row)) << 4) + (b & 15);
+}
+template <int DK>
+__device__ __forceinline__ bf16x8 ldfrag_kq(const unsigned char *base, int row, int k0)
+{
+    return *(const bf16x8 *)(base + swz_kq<DK>(row, k0));
+}
+
+template <int DK, int DVT>
+struct LdsPipe {
+    static constexpr int al(int x) { return (x + 255) & ~255; }
+    static constexpr int NS = DVT / 16;               // 16-column groups
+    static constexpr int szRow = kChunk * DK * 2;     // [64][DK] bf16
+    static constexpr int szV = kChunk * DVT * 2;      // [64][DVT] bf16
+    static constexpr int szP = kChunk * kChunk * 2;   // [64][64] bf16, swizzled
+    static constexpr int szSb = DK * 16 * 2;          // bf16 Shat of a group, lane-linear
+    static constexpr int szU = kChunk * 16 * 2;       // bf16 U of a group, lane-linear
+    static constexpr int sK = 0;
+    static constexpr int sQ = szRow;
+    static constexpr int sRec = 2 * szRow;                  // T'
+    static constexpr int sGam = sRec + kRecG;               // gamma_t 2^ls, fp32
+    static constexpr int sRho = sGam + kChunk * 4;          // gamma_C / gamma_t / 2^ls', fp32
+    static constexpr int sEp = sRho + kChunk * 4;           // 2^g_t and 2^-g_t, fp32
+    static constexpr int sEm = sEp + kChunk * 4;
+    static constexpr int sV = sEm + kChunk * 4;
+    static constexpr int stage = al(sV + szV);        // three stages: chunk c in stage c % 3
+    static constexpr int sG = 3 * stage;              // g of chunk c in slot c % 4 (fp32)
+    static constexpr int sPb = sG + 4 * kChunk * 4;
+    static constexpr int sSb = sPb + szP;
+    static constexpr int sUb = sSb + NS * szSb;
+    static constexpr int sFlag = sUb + NS * szU;      // [3][NS] ints: Shat, U, P taken
+    static constexpr int total = sFlag + 3 * NS * 4;
+    static_assert(total <= 160 * 1024, "LDS");
+};
+
+template <int DK, int DVT>
+__global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(PrefillArgs a)
+{
+    using L = LdsPipe<DK, DVT>;
+    constexpr int NS = L::NS;
+    using OP = uint16_t;
+    using M = Mma<OP>;
+    constexpr int MBK = DK / 16;           // 16-row blocks of the state
+    constexpr int KBD = DK / 32;           // K-blocks over the key dimension
+    constexpr int KG = DK / 8;             // 16-byte granules per key row
+    constexpr int CK = L::szRow / 1024;    // 1 KiB copies per K or Q tile
+    constexpr int CV = L::szV / 1024;      // ... per V tile
+    constexpr int CR = kRecG / 1024;       // ... per T'
+    constexpr int kCopies = 2 * CK + CR + CV;       // copy instructions per chunk (K, Q, T', V)
+    static_assert(L::szV % 1024 == 0 && kCopies < 64, "copies");
+
+    __shared__ __align__(16) unsigned char smem[L::total];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+
+    // ---- job (as in scan_split_kernel) ----
+    const int xcd = blockIdx.x & 7;
+    const int rest = blockIdx.x >> 3;
+    const int tile = rest % a.ntiles;
+    const long long uh = (long long)(rest / a.ntiles) * 8 + xcd;
+    if (uh >= a.units * a.H) return;
+    Job job;
+    job.h = (int)(uh % a.H);
+    const long long unit = uh / a.H;
+    job.col0 = tile * DVT;
+    if (a.table) {
+        if (unit >= (long long)*a.n_entries) return;
+        const SegEntry e = a.table[unit];
+        job.n = e.n;
+        job.tok0 = e.tok0;
+        job.len = e.len;
+        job.seg = e.seg;
+        job.nseg = e.nseg;
+        job.entry = (int)unit;
+    } else {
+        job.n = (int)unit;
+        seq_bounds(a, job.n, job.tok0, job.len);
+        job.seg = 0;
+        job.nseg = 1;
+        job.entry = -1;
+    }
+    const int H = a.H;
+    const int DV = a.dv;
+    const int nchunks = (job.len + kChunk - 1) / kChunk;
+    const long long srow0 = first_row(a, job.n);
+    const long long slot0 = (srow0 >> 6) + job.n + (job.tok0 - srow0) / kChunk;
+    auto nvalid_of = [&](int c) {
+        const int r = job.len - c * kChunk;
+        return r < kChunk ? r : kChunk;
+    };
+    // (LDS-qualified, so that the flags take LDS instructions and no memory-counter waits)
+    typedef __attribute__((address_space(3))) volatile int lds_flag;
+    lds_flag *flagS = (lds_flag *)(smem + L::sFlag);
+    lds_flag *flagU = flagS + NS;
+    lds_flag *flagP = flagS + 2 * NS;
+    if (tid < 3 * NS) flagS[tid] = -1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // wait until flag[i] >= v (the output waves raise these early in every chunk step)
+    auto wait_flag = [&](lds_flag *f, int v) {
+        while (*f < v) __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");
+    };
+    const std::integral_constant<int, 0> s0{};
+    const std::integral_constant<int, 1> s1{};
+    const std::integral_constant<int, 2> s2{};
+
+    // ================================================================ copy wave
+    if (wave == 0) {
+        typedef __attribute__((address_space(3))) void lds_void;
+        const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
+        // Copy j of a tile fills its bytes [1024 j, 1024 j + 1024); each lane's source row
+        // and column follow from its destination through the swizzle and, for K, the
+        // internal token order.  Rows past the end of the job repeat its last row.  Every
+        // call issues exactly kCopies copies.
+        auto copy = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            unsigned char *stg = smem + ST * L::stage;
+            const long long t0 = job.tok0 + (long long)c * kChunk;
+            const int last = nvalid_of(c) - 1;
+            const unsigned char *ck = (const unsigned char *)a.k + (t0 * H + job.h) * (long long)DK * 2;
+            const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + job.h) * (long long)DK * 2;
+            const unsigned char *cv = (const unsigned char *)a.v +
+                                      ((t0 * H + job.h) * (long long)DV + job.col0) * 2;
+            const unsigned char *rec = (const unsigned char *)a.prep +
+                                       ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
+#pragma unroll
+            for (int j = 0; j < CK; ++j) {
+                const int P = 64 * j + lane;                       // granule of the tile
+                const int r = P / KG, pg = P % KG;
+                const int lgq = pg ^ kq_key<DK>(r);                // logical granule
+                const int rk = split_orig(r) < last ? split_orig(r) : last;
+                const int rq = r < last ? r : last;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(ck + (unsigned)rk * rsK + 16 * lgq),
+                    (lds_void *)(stg + L::sK + 1024 * j), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(cq + (unsigned)rq * rsK + 16 * lgq),
+                    (lds_void *)(stg + L::sQ + 1024 * j), 16, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < CR; ++j)
+                __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * (64 * j + lane)),
+                                                 (lds_void *)(stg + L::sRec + 1024 * j), 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < CV; ++j) {
+                const int byte = 1024 * j + 16 * lane;
+                const int r0 = byte / (DVT * 2), cb = byte % (DVT * 2);
+                const int r = r0 < last ? r0 : last;
+                __builtin_amdgcn_global_load_lds((const void *)(cv + (unsigned)r * rsV + cb),
+                                                 (lds_void *)(stg + L::sV + 1024 * j), 16, 0, 0);
+            }
+        };
+        // g of chunk c (one copy instruction), a step earlier than the rest of its data
+        auto copy_g = [&](int c) {
+            const unsigned char *rec = (const unsigned char *)a.prep +
+                                       ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
+            __builtin_amdgcn_global_load_lds((const void *)(rec + kRecG + 4 * lane),
+                                             (lds_void *)(smem + L::sG + (c & 3) * kChunk * 4),
+                                             4, 0, 0);
+        };
+        // (the barrier without a fence: this wave's copies are ordered by the counts alone)
+        if (nchunks > 0) {
+            copy_g(0);
+            if (nchunks > 1) copy_g(1);
+            if (nchunks > 2) copy_g(2);
+            copy(s0, 0);
+            if (nchunks > 1) {
+                copy(s1, 1);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");   // all but chunk 1
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        // step c: chunk c+2 and g of chunk c+3; then everything issued before this step is in
+        auto step = [&](auto stc, int c) {
+            if (c + 3 < nchunks) {
+                copy(stc, c + 2);
+                copy_g(c + 3);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies + 1) : "memory");
+            } else if (c + 2 < nchunks) {
+                copy(stc, c + 2);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int c = 0; c < nchunks; c += 3) {
+            step(s2, c);
+            if (c + 1 < nchunks) step(s0, c + 1);
+            if (c + 2 < nchunks) step(s1, c + 2);
+        }
+        return;
+    }
+
+    // ================================================================ factor / P wave
+    if (wave == 1) {
+        // The scan holds its state as S = 2^ls Shat: ls starts at 0 and after each chunk
+        // becomes ls + g_C, or 0 when that would fall below -32 (the chain waves then
+        // rescale Shat); both follow the same rule on the same g_C, so they agree bit for
+        // bit.  This wave folds 2^ls into the factors it leaves in the stage:
+        //   sGam[t] = gamma_t 2^ls,  sRho[t] = (gamma_C / gamma_t) / 2^ls'
+        // (ls of the chunk, ls' of the next).
+        float lsl = 0.f;
+        auto factors = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            unsigned char *stg = smem + ST * L::stage;
+            const float *gc = (const float *)(smem + L::sG + (c & 3) * kChunk * 4);
+            const float gt = gc[lane], gC = gc[kChunk - 1];
+            const float lsc = lsl;
+            float lsn = lsc + gC;
+            if (lsn < -32.f) lsn = 0.f;
+            ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt + lsc);
+            ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
+            // Gamma_ti = 2^g_t 2^-g_i (g >= -126: both factors are normal floats)
+            ((float *)(stg + L::sEp))[lane] = __builtin_amdgcn_exp2f(gt);
+            ((float *)(stg + L::sEm))[lane] = __builtin_amdgcn_exp2f(-gt);
+            lsl = lsn;
+        };
+        // P = lower_incl(Q K^T (.) Gamma) of chunk c, blocks (t-block, i-block) (0,0) (1,0)
+        // (1,1) (2,0) (3,0) (2,1) (2,2) (3,1) (3,2) (3,3); the blocks (0,1) and (2,3) that
+        // the output waves read are zero.  Accumulator [r] = k_i . q_t, i = 16 ib + 4 lg + r,
+        // t = 16 tb + ln: row t, columns i .. i + 3 of P.
+        auto make_p = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            const unsigned char *stg = smem + ST * L::stage;
+            const float *sEp = (const float *)(stg + L::sEp);
+            const float *sEm = (const float *)(stg + L::sEm);
+            const unsigned char *bK = stg + L::sK;
+            const unsigned char *bQ = stg + L::sQ;
+            unsigned char *bP = smem + L::sPb;
+            constexpr int kTb[10] = {0, 1, 1, 2, 3, 2, 2, 3, 3, 3};
+            constexpr int kIb[10] = {0, 0, 1, 0, 0, 1, 2, 1, 2, 3};
+            // every fragment in one batch of LDS reads
+            bf16x8 fkb[KBD][4], fqb[KBD][4];
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fkb[kb][i] = ldfrag_kq<DK>(bK, split_pos(i * 16 + ln), kb * 32 + 8 * lg);
+                    fqb[kb][i] = ldfrag_kq<DK>(bQ, i * 16 + ln, kb * 32 + 8 * lg);
+                }
+            float et[4];
+            f32x4 ei[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                et[i] = sEp[i * 16 + ln];
+                ei[i] = *(const f32x4 *)(sEm + i * 16 + 4 * lg);
+            }
+            f32x4 acc[10];
+#pragma unroll
+            for (int p = 0; p < 10; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+                for (int p = 0; p < 10; ++p) M::mma(acc[p], fkb[kb][kIb[p]], fqb[kb][kTb[p]]);
+            f32x4 pv[10];
+#pragma unroll
+            for (int p = 0; p < 10; ++p) {
+                const int tb = kTb[p], ib = kIb[p];
+                const int t = tb * 16 + ln;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ib * 16 + 4 * lg + r;
+                    pv[p][r] = (i <= t) ? acc[p][r] * et[tb] * ei[ib][r] : 0.f;
+                }
+            }
+            // the output waves hold P of chunk c-1 in registers once these flags are up
+            if (c > 0)
+                for (int g = 0; g < NS; ++g) wait_flag(flagP + g, c - 1);
+#pragma unroll
+            for (int p = 0; p < 10; ++p)
+                M::put4((OP *)(bP + swz<OP, kChunk>(kTb[p] * 16 + ln, kIb[p] * 16 + 4 * lg)), pv[p]);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            M::put4((OP *)(bP + swz<OP, kChunk>(ln, 16 + 4 * lg)), z);
+            M::put4((OP *)(bP + swz<OP, kChunk>(32 + ln, 48 + 4 * lg)), z);
+        };
+        if (nchunks > 0) {
+            __syncthreads();
+            factors(s0, 0);
+            __syncthreads();
+        }
+        // step c: decay factors of chunk c+1 (stage STn), P of chunk c (stage STc)
+        auto step = [&](auto stc, auto stn, int c) {
+            if (c + 1 < nchunks) factors(stn, c + 1);
+            make_p(stc, c);
+            __syncthreads();
+        };
+        for (int c = 0; c < nchunks; c += 3) {
+            step(s0, s1, c);
+            if (c + 1 < nchunks) step(s1, s2, c + 1);
+            if (c + 2 < nchunks) step(s2, s0, c + 2);
+        }
+        return;
+    }
+
+    // ================================================================ chain waves
+    if (wave < 2 + NS) {
+        const int sw = wave - 2;
+        // this wave owns state columns c0 + ln
+        const int c0 = job.col0 + 16 * sw;
+        f32x4 S[MBK];
+        {
+            const float *src = nullptr;
+            if (job.seg == 0) {
+                if (a.s0) src = a.s0 + ((long long)job.n * H + job.h) * DK * DV + c0;
+            } else {
+                src = a.segB + ((long long)(job.entry - 1) * H + job.h) * DK * DV + c0;
+            }
+            // register S[m][i] of lane (ln, lg) holds state row split_orig(16 m + 4 lg + i)
+#pragma unroll
+            for (int m = 0; m < MBK; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[m][i] = src ? src[(long long)split_orig(16 * m + 4 * lg + i) * DV + ln] : 0.f;
+        }
+        unsigned char *sb = smem + L::sSb + sw * L::szSb;
+        unsigned char *ub = smem + L::sUb + sw * L::szU;
+        bf16x8 Sb[KBD];
+        // bf16 Shat for the state products of a chunk, also left in LDS (lane-linear) for
+        // the output wave of this group
+        auto pack_state = [&]() {
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) Sb[kb] = pack8s(S[2 * kb], S[2 * kb + 1]);
+        };
+        auto put_state = [&]() {
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) *(bf16x8 *)(sb + (kb * 64 + lane) * 16) = Sb[kb];
+        };
+        float ls = 0.f;
+        pack_state();
+        put_state();
+        auto chunk = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            const unsigned char *stg = smem + ST * L::stage;
+            const unsigned char *bKc = stg + L::sK;
+            const unsigned char *bTc = stg + L::sRec + kRecT;
+            const float *sGc = (const float *)(smem + L::sG + (c & 3) * kChunk * 4);
+            const float *sGam = (const float *)(stg + L::sGam);
+            const float *sRho = (const float *)(stg + L::sRho);
+            const unsigned char *bVc = stg + L::sV;
+            auto frag64 = [&](const unsigned char *base, int row, int k0) {
+                return ldfrag<OP, kChunk>(base, row, k0 + 8 * lg);
+            };
+            // K^T fragment for the state update: A[row = state row 16 m + ln (internal)][k =
+            // tokens 32 kt + 8 lg .. + 7] by two transposing reads of the K rows.
+            auto frag_kt = [&](int m, int kt) {
+                const int col = 32 * (m >> 1) + 8 * (ln & 3) + 4 * (m & 1);
+                const int t = 32 * kt + 8 * lg + (ln >> 2);
+                const bf16x4 lo = ldtr(bKc + swz_kq<DK>(split_pos(t), col));
+                const bf16x4 hi = ldtr(bKc + swz_kq<DK>(split_pos(t + 4), col));
+                return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
+
+            // ---- K S from the chunk-start state (the head of the state chain) ----
+            bf16x8 fk[2][4], ft[6];
+            f32x4 acc_ks[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) fk[0][tb] = ldfrag_kq<DK>(bKc, tb * 16 + ln, 8 * lg);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc_ks[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) {
+                if (kb + 1 < KBD) {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        fk[(kb + 1) & 1][tb] =
+                            ldfrag_kq<DK>(bKc, tb * 16 + ln, (kb + 1) * 32 + 8 * lg);
+                } else {
+                    // T' fragments for U = T' R: rows 0..31 use tokens 0..31 only
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) ft[mb] = frag64(bTc, mb * 16 + ln, 0);
+                    ft[4] = frag64(bTc, 32 + ln, 32);
+                    ft[5] = frag64(bTc, 48 + ln, 32);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) M::mma(acc_ks[tb], fk[kb & 1][tb], Sb[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- R = V - diag(gamma 2^ls) K Shat;  U = T' R ----
+            // the rows of K S this lane holds are internal 16 tb + 4 lg + i: tokens o0 + i
+            f32x4 gam[4], rho[4], U[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int o0 = split_orig(tb * 16 + 4 * lg);
+                gam[tb] = *(const f32x4 *)(sGam + o0);
+                rho[tb] = *(const f32x4 *)(sRho + o0);
+            }
+            {
+                f32x4 R[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    // V[o0 .. o0 + 3][column] by one transposing read of the V rows
+                    const int o0 = split_orig(tb * 16 + 4 * lg);
+                    const int col = 16 * sw + 4 * (ln & 3);
+                    const bf16x4 v4 = ldtr(bVc + ((o0 + (ln >> 2)) * DVT + col) * 2);
+                    R[tb] = __builtin_convertvector(v4, f32x4) - gam[tb] * acc_ks[tb];
+                }
+                const bf16x8 Rb0 = pack8s(R[0], R[1]);
+                const bf16x8 Rb1 = pack8s(R[2], R[3]);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    M::mma(U[mb], ft[mb], Rb0);
+                }
+                M::mma(U[2], ft[4], Rb1);
+                M::mma(U[3], ft[5], Rb1);
+            }
+            bf16x8 fkt[2][MBK];
+#pragma unroll
+            for (int m = 0; m < MBK; ++m) fkt[0][m] = frag_kt(m, 0);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- bf16 U for the output wave (which holds U of chunk c-1 by now) ----
+            {
+                const bf16x8 Uu0 = pack8s(U[0], U[1]);
+                const bf16x8 Uu1 = pack8s(U[2], U[3]);
+                if (c > 0) wait_flag(flagU + sw, c - 1);
+                *(bf16x8 *)(ub + lane * 16) = Uu0;
+                *(bf16x8 *)(ub + 1024 + lane * 16) = Uu1;
+            }
+            // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U ----
+            float ln_ = ls + sGc[kChunk - 1];
+            ln_ = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ln_)));
+            if (ln_ < -32.f) {                     // fold the scale into Shat (rare)
+                const float f = __builtin_amdgcn_exp2f(ln_);
+#pragma unroll
+                for (int m = 0; m < MBK; ++m) S[m] *= f;
+                ln_ = 0.f;
+            }
+            ls = ln_;
+            bf16x8 Ub0, Ub1;
+            {
+                f32x4 Us[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) Us[mb] = U[mb] * rho[mb];
+                Ub0 = pack8s(Us[0], Us[1]);
+                Ub1 = pack8s(Us[2], Us[3]);
+            }
+#pragma unroll
+            for (int m = 0; m < MBK; ++m) M::mma(S[m], fkt[0][m], Ub0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < MBK; ++m) fkt[1][m] = frag_kt(m, 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < MBK; ++m) M::mma(S[m], fkt[1][m], Ub1);
+            pack_state();
+            wait_flag(flagS + sw, c);              // the output wave holds Shat of chunk c
+            put_state();
+            __syncthreads();
+        };
+        if (nchunks > 0) {                // the prologue's barriers (chunk 0 staged)
+            __syncthreads();
+            __syncthreads();
+        }
+        for (int c = 0; c < nchunks; c += 3) {
+            chunk(s0, c);
+            if (c + 1 < nchunks) chunk(s1, c + 1);
+            if (c + 2 < nchunks) chunk(s2, c + 2);
+        }
+        if (job.seg == job.nseg - 1 && a.s_final) {
+            float *dst = a.s_final + ((long long)job.n * H + job.h) * DK * DV + c0;
+            const float sp = __builtin_amdgcn_exp2f(ls);
+#pragma unroll
+            for (int m = 0; m < MBK; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[(long long)split_orig(16 * m + 4 * lg + i) * DV + ln] = S[m][i] * sp;
+        }
+        return;
+    }
+
+    // ================================================================ output waves
+    {
+        const int yw = wave - 2 - NS;
+        const int c0 = job.col0 + 16 * yw;
+        const unsigned char *sb = smem + L::sSb + yw * L::szSb;
+        const unsigned char *ub = smem + L::sUb + yw * L::szU;
+        const unsigned char *bP = smem + L::sPb;
+        f32x4 accYp[4];
+        float gyp[4];
+        // U and P of chunk c into registers, then the flags that free their buffers
+        bf16x8 Uu0, Uu1, fp[6];
+        auto take_up = [&](int c) {
+            Uu0 = *(const bf16x8 *)(ub + lane * 16);
+            Uu1 = *(const bf16x8 *)(ub + 1024 + lane * 16);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) fp[tb] = ldfrag<OP, kChunk>(bP, tb * 16 + ln, 8 * lg);
+            fp[4] = ldfrag<OP, kChunk>(bP, 32 + ln, 32 + 8 * lg);
+            fp[5] = ldfrag<OP, kChunk>(bP, 48 + ln, 32 + 8 * lg);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) {
+                flagU[yw] = c;
+                flagP[yw] = c;
+            }
+        };
+        // Y of chunk c = diag(gamma 2^ls) (Shat^T Q^T)^T (accYp, gyp) + P U
+        auto finish = [&](int c) {
+            f32x4 pu[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                pu[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                M::mma(pu[tb], Uu0, fp[tb]);
+            }
+            M::mma(pu[2], Uu1, fp[4]);
+            M::mma(pu[3], Uu1, fp[5]);
+            const long long t0 = job.tok0 + (long long)c * kChunk;
+            const int nv = nvalid_of(c);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = tb * 16 + ln;
+                const f32x4 yv = accYp[tb] * gyp[tb] + pu[tb];
+                if (t < nv)
+                    store4((OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + c0 + 4 * lg, yv);
+            }
+        };
+        auto step = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            const unsigned char *stg = smem + ST * L::stage;
+            const float *sGam = (const float *)(stg + L::sGam);
+            const unsigned char *bQ = stg + L::sQ;
+            if (c > 0) take_up(c - 1);
+            bf16x8 Sb[KBD];
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) Sb[kb] = *(const bf16x8 *)(sb + (kb * 64 + lane) * 16);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) flagS[yw] = c;
+            f32x4 accQ[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) accQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    M::mma(accQ[tb], Sb[kb], ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg));
+            float gy[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) gy[tb] = sGam[tb * 16 + ln];
+            __builtin_amdgcn_sched_barrier(0);
+            if (c > 0) finish(c - 1);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                accYp[tb] = accQ[tb];
+                gyp[tb] = gy[tb];
+            }
+            __syncthreads();
+        };
+        if (nchunks > 0) {
+            __syncthreads();
+            __syncthreads();
+        }
+        for (int c = 0; c < nchunks; c += 3) {
+            step(s0, c);
+            if (c + 1 < nchunks) step(s1, c + 1);
+            if (c + 2 < nchunks) step(s2, c + 2);
+        }
+        if (nchunks > 0) {
+            take_up(nchunks - 1);
+            finish(nchunks - 1);
+        }
+    }
+}
+
+// =========================================================================================
 // Host side
 // =========================================================================================
 template <int DK>
@@ -965,8 +1588,13 @@ hipError_t launch_scan_split(const PrefillArgs &args, long long units, int ntile
     PrefillArgs a2 = args;
     a2.units = units;
     a2.ntiles = ntiles;
-    hipLaunchKernelGGL((scan_split_kernel<DK, DVT, MODE>), dim3((unsigned)groups),
-                       dim3(64 * (scan_waves<DVT>() + kLoaders)), 0, stream, a2);
+    if constexpr (MODE == kModeScan && DVT <= 32) {
+        hipLaunchKernelGGL((scan_pipe_kernel<DK, DVT>), dim3((unsigned)groups),
+                           dim3(64 * (2 + 2 * (DVT / 16))), 0, stream, a2);
+    } else {
+        hipLaunchKernelGGL((scan_split_kernel<DK, DVT, MODE>), dim3((unsigned)groups),
+                           dim3(64 * (scan_waves<DVT>() + kLoaders)), 0, stream, a2);
+    }
     return hipGetLastError();
 }
 
