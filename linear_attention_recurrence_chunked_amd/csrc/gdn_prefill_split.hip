@@ -152,19 +152,30 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
     const int H = a.H;
-    const long long slot = (long long)blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
+    const long long slot = (long long)(blockIdx.x / (unsigned)H);
+    const int h = (int)(blockIdx.x % (unsigned)H);
     if (slot >= nslots) return;
-    // sequence of the slot: the last n with first_slot(n) <= slot
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (first_slot(a, mid) <= slot) lo = mid; else hi = mid - 1;
+    // sequence of the slot: the last n with first_slot(n) <= slot (32-bit arithmetic and one
+    // wave-wide vote where they suffice: this runs before anything else in the workgroup)
+    long long per = 0;                     // tokens per sequence when all have one length
+    if (!a.cu)
+        per = a.total_T < 0x7fffffffLL ? (long long)((unsigned)a.total_T / (unsigned)a.num_seqs)
+                                       : a.total_T / a.num_seqs;
+    auto row0 = [&](int m) -> long long { return a.cu ? a.cu[m] : per * m; };
+    int n;
+    if (a.cu && a.num_seqs <= 64) {
+        const bool ok = lane < a.num_seqs && (a.cu[lane] >> 6) + lane <= slot;
+        n = __popcll(__builtin_amdgcn_ballot_w64(ok)) - 1;
+    } else {
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((row0(mid) >> 6) + mid <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
     }
-    const int n = lo;
-    long long st0;
-    int slen;
-    seq_bounds(a, n, st0, slen);
+    const long long st0 = row0(n);
+    const int slen = (int)(a.cu ? a.cu[n + 1] - st0 : per);
     const long long c = slot - ((st0 >> 6) + n);
     if (c < 0 || c * kChunk >= slen) return;          // unused slot
     const long long t0 = st0 + c * kChunk;
