@@ -180,7 +180,9 @@ def main():
 
     # bf16 prefill = two launches: chunk records, then the state scan; the roofline covers
     # the pair (HIP events around the library call); rocprofv3 splits it per kernel
-    if tile <= 64:
+    if tile <= 32:
+        kernel_name = "chunk_prep_kernel<128> + scan_pipe_kernel<128,%d>" % tile
+    elif tile <= 64:
         kernel_name = "chunk_prep_kernel<128> + scan_split_kernel<128,%d,scan>" % tile
     else:
         kernel_name = "prefill_kernel<128,%d,bf16,scan>" % tile
