@@ -118,20 +118,21 @@ __device__ __forceinline__ f32x4 mm16sr(f32x4 arow, f32x4 bcol)
 template <int DK>
 struct LdsPrep {
     static constexpr int szRow = kChunk * DK * 2;
-    static constexpr int LDA = kChunk + 4;          // padded fp32 rows of A
+    static constexpr int LDB = 20;                  // padded fp32 rows of an A block
     static constexpr int LDX = 20;                  // padded rows of a diagonal X block
     static constexpr int oT = kRecT, oG = kRecG;
     static constexpr int oBeta = kPrepRecordBytes;
     static constexpr int oK = oBeta + 256;          // K rows (phases 1-2) ...
     static constexpr int oA = oK;                   // ... then A and the X blocks (phase 3)
-    static constexpr int oX = oA + kChunk * LDA * 4;
-    static constexpr int total = oK + (szRow > kChunk * LDA * 4 + 4 * 16 * LDX * 4
+    // the six strictly lower 16 x 16 blocks of A, block (i, m) at index i (i - 1) / 2 + m
+    static constexpr int oX = oA + 6 * 16 * LDB * 4;
+    static constexpr int total = oK + (szRow > 6 * 16 * LDB * 4 + 4 * 16 * LDX * 4
                                            ? szRow
-                                           : kChunk * LDA * 4 + 4 * 16 * LDX * 4);
+                                           : 6 * 16 * LDB * 4 + 4 * 16 * LDX * 4);
 };
 
 template <int DK>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long long nslots)
+__global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long long nslots)
 {
     using L = LdsPrep<DK>;
     using OP = uint16_t;
@@ -299,8 +300,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
     __syncthreads();   // K is dead: its space now holds A and the X blocks
 
     // ---- phase 3 (stores): A blocks, X_ww in the row layout, T' diagonal block ----
-    *(f32x4 *)(sA + (tb0 * 16 + ln) * L::LDA + ib0 * 16 + 4 * lg) = a1;
-    if (np == 3) *(f32x4 *)(sA + (3 * 16 + ln) * L::LDA + ib1 * 16 + 4 * lg) = a2;
+    auto ablk = [&](int i, int m) { return sA + ((i * (i - 1) / 2 + m) * 16 + ln) * L::LDB + 4 * lg; };
+    *(f32x4 *)ablk(tb0, ib0) = a1;
+    if (np == 3) *(f32x4 *)ablk(3, ib1) = a2;
     *(f32x4 *)(sX + (d0 + ln) * L::LDX + 4 * lg) = xT;
     {
         const f32x4 bcol = *(const f32x4 *)(sBeta + d0 + 4 * lg);
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, long lon
         const int j = wave;
         const float bcol = sBeta[16 * j + ln];
         auto arow = [&](int i, int m) {
-            return *(const f32x4 *)(sA + (16 * i + ln) * L::LDA + 16 * m + 4 * lg);
+            return *(const f32x4 *)ablk(i, m);
         };
         auto xrow = [&](int i) { return *(const f32x4 *)(sX + (16 * i + ln) * L::LDX + 4 * lg); };
         auto put_t = [&](int i, f32x4 z) {
