@@ -152,23 +152,31 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
+    // every argument this kernel reads, fetched in one round of scalar loads
     const int H = a.H;
+    const int32_t *const cu = a.cu;
+    const long long totT = a.total_T;
+    const int nseq = a.num_seqs;
+    const OP *const gk = (const OP *)a.k;
+    const float *const galpha = a.alpha, *const gbeta = a.beta;
+    unsigned char *const gprep = (unsigned char *)a.prep;
+    asm volatile("" ::"s"(H), "s"(cu), "s"(totT), "s"(nseq), "s"(gk), "s"(galpha), "s"(gbeta),
+                 "s"(gprep), "s"(nslots));
     const long long slot = (long long)(blockIdx.x / (unsigned)H);
     const int h = (int)(blockIdx.x % (unsigned)H);
     if (slot >= nslots) return;
     // sequence of the slot: the last n with first_slot(n) <= slot (32-bit arithmetic and one
     // wave-wide vote where they suffice: this runs before anything else in the workgroup)
     long long per = 0;                     // tokens per sequence when all have one length
-    if (!a.cu)
-        per = a.total_T < 0x7fffffffLL ? (long long)((unsigned)a.total_T / (unsigned)a.num_seqs)
-                                       : a.total_T / a.num_seqs;
-    auto row0 = [&](int m) -> long long { return a.cu ? a.cu[m] : per * m; };
+    if (!cu)
+        per = totT < 0x7fffffffLL ? (long long)((unsigned)totT / (unsigned)nseq) : totT / nseq;
+    auto row0 = [&](int m) -> long long { return cu ? cu[m] : per * m; };
     int n;
-    if (a.cu && a.num_seqs <= 64) {
-        const bool ok = lane < a.num_seqs && (a.cu[lane] >> 6) + lane <= slot;
+    if (cu && nseq <= 64) {
+        const bool ok = lane < nseq && (cu[lane] >> 6) + lane <= slot;
         n = __popcll(__builtin_amdgcn_ballot_w64(ok)) - 1;
     } else {
-        int lo = 0, hi = a.num_seqs - 1;
+        int lo = 0, hi = nseq - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if ((row0(mid) >> 6) + mid <= slot) lo = mid; else hi = mid - 1;
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
         n = lo;
     }
     const long long st0 = row0(n);
-    const int slen = (int)(a.cu ? a.cu[n + 1] - st0 : per);
+    const int slen = (int)(cu ? cu[n + 1] - st0 : per);
     const long long c = slot - ((st0 >> 6) + n);
     if (c < 0 || c * kChunk >= slen) return;          // unused slot
     const long long t0 = st0 + c * kChunk;
@@ -184,7 +192,6 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
 
     // ---- phase 1: K rows (zero beyond the chunk's last row), g, beta ----
     {
-        const OP *gk = (const OP *)a.k;
         u32x4 rk[NG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
         float pa = 0.f;
         if (wave < 2) {
             const int tc = lane < nv ? lane : nv - 1;
-            pa = (wave == 0 ? a.alpha : a.beta)[(t0 + tc) * H + h];
+            pa = (wave == 0 ? galpha : gbeta)[(t0 + tc) * H + h];
         }
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     __syncthreads();
 
     // ---- phase 5: the record, granule for granule ----
-    u32x4 *dst = (u32x4 *)((unsigned char *)a.prep + (slot * H + h) * (long long)kPrepRecordBytes);
+    u32x4 *dst = (u32x4 *)(gprep + (slot * H + h) * (long long)kPrepRecordBytes);
     for (int i = tid; i < kRecGranules; i += 256) dst[i] = *(const u32x4 *)(smem + 16 * i);
 }
 
