@@ -710,8 +710,14 @@ static hipError_t run_prefill(const PrefillArgs &args, const PrefillPlan &plan,
                        (int32_t *)args.n_entries);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // phase A: [S | M] scans of every segment but the last of each sequence
-    err = launch_scan<DK, DVT, OP, kModeAug>(args, max_entries, (dv + DK) / DVT, stream);
+    // phase A: [S | M] scans of every segment but the last of each sequence (bf16: 64-column
+    // tiles, which halve the per-tile copies of the chunk's K, Q and record for the d_v + d_k
+    // columns of [S | M]; phase C keeps the plan's tile)
+    constexpr int DVTA = (sizeof(OP) == 2 && DVT == 32) ? 64 : DVT;
+    if (dv % DVTA == 0)
+        err = launch_scan<DK, DVTA, OP, kModeAug>(args, max_entries, (dv + DK) / DVTA, stream);
+    else
+        err = launch_scan<DK, DVT, OP, kModeAug>(args, max_entries, (dv + DK) / DVT, stream);
     if (err != hipSuccess) return err;
     // phase B: fold the segment maps
     {
@@ -788,7 +794,8 @@ bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype
     const long long chains = (long long)num_seqs * H;
     if (tile == 0) {
         tile = largest_tile(dtype, dk, dv);
-        if (dtype == kDtypeBF16 && tile > 64) tile = 64;   // the two-launch path
+        // the two-launch path; its pipelined scan takes 16 or 32 columns per workgroup
+        if (dtype == kDtypeBF16 && tile > 32) tile = 32;
         while (tile > 32 && chains * (dv / tile) < 512) tile >>= 1;
     }
     if (!tile_ok(dtype, dk, dv, tile)) return false;
