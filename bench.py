@@ -44,8 +44,8 @@ def decode_bytes_per_head_step(d: int) -> int:
 
 
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc")
-PREFILL_SOURCES = ["gdn_device.hpp", "gdn_prefill_common.hpp", "gdn_prefill.hip",
-                   "gdn_prefill_split.hip"]
+PREFILL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_prefill_common.hpp",
+                   "gdn_prefill.hip", "gdn_prefill_split.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
 
 

@@ -34,13 +34,9 @@ constexpr int kRecG = kChunk * kChunk * 2;
 static_assert(kRecG + kChunk * 4 == kPrepRecordBytes, "record layout");
 constexpr int kRecGranules = kPrepRecordBytes / 16;
 
-// 16 bytes from global memory that is only guaranteed 8-byte aligned.
-__device__ __forceinline__ u32x4 ld16(const uint16_t *p)
-{
-    const u32x2 lo = *(const u32x2 *)p;
-    const u32x2 hi = *(const u32x2 *)(p + 4);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
+// 16 bytes of a key row (the entry points accept only 16-byte aligned q, k and v, and rows
+// of 64 or 128 bf16 keep every 8-element granule aligned).
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *(const u32x4 *)p; }
 
 __device__ __forceinline__ long long first_row(const PrefillArgs &a, int n)
 {
@@ -982,39 +978,59 @@ __global__ __launch_bounds__(64 * (scan_waves<DVT>() + kLoaders)) void scan_spli
 // Launch 2, pipelined form (bf16, 16 or 32 state columns per workgroup).  The output
 // products leave the state chain: each 16-column group has a chain wave that carries the
 // state and an output wave that forms Y, and the two meet in LDS.  During chunk step c:
-//   wave 0         issues the copies of chunk c+2 (K in the internal token order, Q, T',
-//                  V) and of g of chunk c+3, and waits only for those of the step before,
-//                  so that every copy has two chunk-steps to arrive
-//   wave 1         forms the decay factors of chunk c+1 and P of chunk c
+//   copiers A, B   issue the copies of chunk c+2 (A: K in the internal token order and T';
+//                  B: Q, V and g of chunk c+3) and wait only for their own copies of the
+//                  step before, so that every copy has two chunk-steps to arrive
+//   P wave         forms P of chunk c as six operand fragments
 //   chain waves    R = V - diag(gamma 2^ls) K Shat, U = T' R and the state update of chunk
 //                  c; they leave bf16 U and bf16 Shat (start of chunk c+1) in LDS
 //   output waves   Shat^T Q^T of chunk c, then Y of chunk c-1 = diag(gamma 2^ls) Q Shat
-//                  + P U, stored to y
-// One barrier per chunk step.  P, U and Shat have one LDS buffer each: the output wave
-// raises a flag once it holds its copy in registers, and the writer of the next value
-// waits for that flag.
+//                  + P U, stored to y; the first also forms the decay factors of chunk c+1
+// One barrier per chunk step.  P has two LDS buffers, by chunk parity, ordered by the step
+// barriers; U and Shat have one each: the output wave raises a flag once it holds its copy
+// in registers, and the chain wave waits for that flag before it writes the next value.
 // =========================================================================================
-// Swizzle of the K and Q tiles of the pipelined scan.  For 256-byte rows the key rotates the
-// row's low four bits and flips bit 1 on odd 16-row blocks: the 16 consecutive rows of a
-// fragment load, and the rows {16 b + 0..7, 16 b + 16..23} that a fragment of K in the
-// internal token order touches, stay on distinct granules, and the transposing reads of
-// K^T (8 rows x 4 granules per half-wave) meet at most two rows per bank.  128-byte rows
-// keep the key of swz_key.
+// Swizzle of the K and Q tiles of the pipelined scan.  The gfx950 LDS has 64 four-byte banks
+// (256 bytes per cycle).  The bank-conflict counters, read over single-wave probes of many
+// address patterns, fit this model: a 16-byte read (ds_read_b128) serves two groups of eight
+// lanes per cycle, lanes 8a .. 8a+7 with lanes
+// 8(a^3) .. 8(a^3)+7, and it takes an extra cycle unless each group stays within one
+// 128-byte half of the banks on distinct 16-byte slots and the two groups use different
+// halves; the transposing read (ds_read_b64_tr_b16) serves 32 lanes per cycle, eight bytes
+// each.  For 256-byte rows, logical granule g of row r is stored at slot pi(g) ^ (r & 7),
+// pi(g) = (g & 1) << 3 | g >> 1 (the half is the granule's parity):
+//   - a fragment load reads granule g of 16 consecutive rows (lane group ln / 8 = 0 or 1,
+//     lg = granule offset); each group of eight rows meets eight distinct slots of the
+//     half g & 1, and the paired group (granule g ^ 1) the other half: no conflicts;
+//   - a transposing read of K^T meets rows 4a .. 4a+3 of one eight-row block at four
+//     consecutive granules (two per half) and reads the same eight bytes of each, so every
+//     slot serves exactly two of the 32 lanes of a cycle, the least that this shape allows.
+// 128-byte rows keep the XOR key of swz_key.
 template <int DK>
-__device__ __forceinline__ int kq_key(int row)
+__device__ __forceinline__ int kq_slot(int row, int g)
 {
     if constexpr (DK * 2 >= 256) {
-        const int x = row & 15;
-        return (((x & 3) << 2) | ((x >> 2) & 3)) ^ (((row >> 4) & 1) << 1);
+        return (((g & 1) << 3) | ((g >> 1) & 7)) ^ (row & 7);
     } else {
-        return swz_key<uint16_t, DK>(row);
+        return g ^ swz_key<uint16_t, DK>(row);
+    }
+}
+// the logical granule that slot p of row `row` holds (inverse of kq_slot)
+template <int DK>
+__device__ __forceinline__ int kq_logical(int row, int p)
+{
+    if constexpr (DK * 2 >= 256) {
+        const int x = p ^ (row & 7);
+        return ((x & 7) << 1) | (x >> 3);
+    } else {
+        return p ^ swz_key<uint16_t, DK>(row);
     }
 }
 template <int DK>
 __device__ __forceinline__ int swz_kq(int row, int col)
 {
     const int b = col * 2;
-    return row * (DK * 2) + (((b >> 4) ^ kq_key<DK>(row)) << 4) + (b & 15);
+    return row * (DK * 2) + (kq_slot<DK>(row, b >> 4) << 4) + (b & 15);
 }
 template <int DK>
 __device__ __forceinline__ bf16x8 ldfrag_kq(const unsigned char *base, int row, int k0)
@@ -1028,7 +1044,7 @@ struct LdsPipe {
     static constexpr int NS = DVT / 16;               // 16-column groups
     static constexpr int szRow = kChunk * DK * 2;     // [64][DK] bf16
     static constexpr int szV = kChunk * DVT * 2;      // [64][DVT] bf16
-    static constexpr int szP = kChunk * kChunk * 2;   // [64][64] bf16, swizzled
+    static constexpr int szP = 6 * 1024;              // six bf16 operand fragments of P
     static constexpr int szSb = DK * 16 * 2;          // bf16 Shat of a group, lane-linear
     static constexpr int szU = kChunk * 16 * 2;       // bf16 U of a group, lane-linear
     static constexpr int sK = 0;
@@ -1036,21 +1052,19 @@ struct LdsPipe {
     static constexpr int sRec = 2 * szRow;                  // T'
     static constexpr int sGam = sRec + kRecG;               // gamma_t 2^ls, fp32
     static constexpr int sRho = sGam + kChunk * 4;          // gamma_C / gamma_t / 2^ls', fp32
-    static constexpr int sEp = sRho + kChunk * 4;           // 2^g_t and 2^-g_t, fp32
-    static constexpr int sEm = sEp + kChunk * 4;
-    static constexpr int sV = sEm + kChunk * 4;
+    static constexpr int sV = sRho + kChunk * 4;
     static constexpr int stage = al(sV + szV);        // three stages: chunk c in stage c % 3
     static constexpr int sG = 3 * stage;              // g of chunk c in slot c % 4 (fp32)
-    static constexpr int sPb = sG + 4 * kChunk * 4;
-    static constexpr int sSb = sPb + szP;
+    static constexpr int sPb = sG + 4 * kChunk * 4;   // P of chunk c in buffer c & 1
+    static constexpr int sSb = sPb + 2 * szP;
     static constexpr int sUb = sSb + NS * szSb;
-    static constexpr int sFlag = sUb + NS * szU;      // [3][NS] ints: Shat, U, P taken
-    static constexpr int total = sFlag + 3 * NS * 4;
+    static constexpr int sFlag = sUb + NS * szU;      // [2][NS] ints: Shat, U taken
+    static constexpr int total = sFlag + 2 * NS * 4;
     static_assert(total <= 160 * 1024, "LDS");
 };
 
 template <int DK, int DVT>
-__global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(PrefillArgs a)
+__global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(PrefillArgs a)
 {
     using L = LdsPipe<DK, DVT>;
     constexpr int NS = L::NS;
@@ -1062,14 +1076,22 @@ __global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
     constexpr int CK = L::szRow / 1024;    // 1 KiB copies per K or Q tile
     constexpr int CV = L::szV / 1024;      // ... per V tile
     constexpr int CR = kRecG / 1024;       // ... per T'
-    constexpr int kCopies = 2 * CK + CR + CV;       // copy instructions per chunk (K, Q, T', V)
-    static_assert(L::szV % 1024 == 0 && kCopies < 64, "copies");
+    constexpr int kCopiesA = CK + CR;      // copy instructions per chunk: K and T' (copier A)
+    constexpr int kCopiesB = CK + CV;      // ... Q and V (copier B, plus one for g)
+    // two chunks of copies in flight per copier stay below the 63 its counter holds
+    static_assert(L::szV % 1024 == 0 && 2 * kCopiesA < 64 && 2 * (kCopiesB + 1) < 64, "copies");
 
     __shared__ __align__(16) unsigned char smem[L::total];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // role of the wave: 0 copier A, 1 P, 2 .. 1 + NS chains, 2 + NS .. 1 + 2 NS output,
+    // 2 + 2 NS copier B.  Waves w and w + 4 share a SIMD: with two groups the P wave (the
+    // longest step) has a SIMD of its own, each chain wave pairs with a copier and the two
+    // output waves pair (wave -> role: 0 -> 0, 1 -> 4, 2 -> 2, 3 -> 1, 4 -> 3, 5 -> 5,
+    // 6 -> 6).
+    const int role = NS == 2 ? (wave == 1 ? 4 : wave == 3 ? 1 : wave == 4 ? 3 : wave) : wave;
     const int ln = lane & 15;
     const int lg = lane >> 4;
 
@@ -1112,8 +1134,7 @@ __global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
     typedef __attribute__((address_space(3))) volatile int lds_flag;
     lds_flag *flagS = (lds_flag *)(smem + L::sFlag);
     lds_flag *flagU = flagS + NS;
-    lds_flag *flagP = flagS + 2 * NS;
-    if (tid < 3 * NS) flagS[tid] = -1;
+    if (tid < 2 * NS) flagS[tid] = -1;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // wait until flag[i] >= v (the output waves raise these early in every chunk step)
     auto wait_flag = [&](lds_flag *f, int v) {
@@ -1123,44 +1144,83 @@ __global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
     const std::integral_constant<int, 0> s0{};
     const std::integral_constant<int, 1> s1{};
     const std::integral_constant<int, 2> s2{};
+    // Decay factors of chunk c into its stage (formed by the first output wave, a step ahead).
+    // The scan holds its state as S = 2^ls Shat: ls starts at 0 and after each chunk becomes
+    // ls + g_C, or 0 when that would fall below -32 (the chain waves then rescale Shat); both
+    // follow the same rule on the same g_C, so they agree bit for bit.  The factors carry
+    // 2^ls:  sGam[t] = gamma_t 2^ls,  sRho[t] = (gamma_C / gamma_t) / 2^ls'  (ls of the
+    // chunk, ls' of the next).
+    float lsl = 0.f;
+    auto factors = [&](auto stc, int c) {
+        constexpr int ST = decltype(stc)::value;
+        unsigned char *stg = smem + ST * L::stage;
+        const float *gc = (const float *)(smem + L::sG + (c & 3) * kChunk * 4);
+        const float gt = gc[lane], gC = gc[kChunk - 1];
+        const float lsc = lsl;
+        float lsn = lsc + gC;
+        if (lsn < -32.f) lsn = 0.f;
+        ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt + lsc);
+        ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
+        lsl = lsn;
+    };
 
-    // ================================================================ copy wave
-    if (wave == 0) {
+    // ================================================================ copy waves
+    // Two waves issue the copies, so that each stays within the 63 outstanding vector
+    // memory instructions a wave can count: copier A the K tile and T', copier B the Q tile,
+    // V and g.  Copy j of a tile fills its bytes [1024 j, 1024 j + 1024); each lane's source row
+    // and column follow from its destination through the swizzle and, for K, the internal
+    // token order.  Rows past the end of the job repeat its last row.  In step c a copier
+    // issues its copies of chunk c+2 (copier B also g of chunk c+3), then waits only for
+    // those it issued in the step before; the barrier needs no fence, as each copier's
+    // copies are ordered by its counter alone.
+    if (role == 0 || role == 2 + 2 * NS) {
         typedef __attribute__((address_space(3))) void lds_void;
+        const bool is_a = role == 0;
         const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
-        // Copy j of a tile fills its bytes [1024 j, 1024 j + 1024); each lane's source row
-        // and column follow from its destination through the swizzle and, for K, the
-        // internal token order.  Rows past the end of the job repeat its last row.  Every
-        // call issues exactly kCopies copies.
-        auto copy = [&](auto stc, int c) {
+        auto rec_of = [&](int c) {
+            return (const unsigned char *)a.prep +
+                   ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
+        };
+        // copier A: the K tile (rows in the internal token order) and T'
+        auto copy_a = [&](auto stc, int c) {
             constexpr int ST = decltype(stc)::value;
             unsigned char *stg = smem + ST * L::stage;
             const long long t0 = job.tok0 + (long long)c * kChunk;
             const int last = nvalid_of(c) - 1;
             const unsigned char *ck = (const unsigned char *)a.k + (t0 * H + job.h) * (long long)DK * 2;
-            const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + job.h) * (long long)DK * 2;
-            const unsigned char *cv = (const unsigned char *)a.v +
-                                      ((t0 * H + job.h) * (long long)DV + job.col0) * 2;
-            const unsigned char *rec = (const unsigned char *)a.prep +
-                                       ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
+            const unsigned char *rec = rec_of(c);
 #pragma unroll
             for (int j = 0; j < CK; ++j) {
                 const int P = 64 * j + lane;                       // granule of the tile
                 const int r = P / KG, pg = P % KG;
-                const int lgq = pg ^ kq_key<DK>(r);                // logical granule
                 const int rk = split_orig(r) < last ? split_orig(r) : last;
-                const int rq = r < last ? r : last;
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)(ck + (unsigned)rk * rsK + 16 * lgq),
+                    (const void *)(ck + (unsigned)rk * rsK + 16 * kq_logical<DK>(r, pg)),
                     (lds_void *)(stg + L::sK + 1024 * j), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(cq + (unsigned)rq * rsK + 16 * lgq),
-                    (lds_void *)(stg + L::sQ + 1024 * j), 16, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < CR; ++j)
                 __builtin_amdgcn_global_load_lds((const void *)(rec + 16 * (64 * j + lane)),
                                                  (lds_void *)(stg + L::sRec + 1024 * j), 16, 0, 0);
+        };
+        // copier B: the Q tile and the V tile
+        auto copy_b = [&](auto stc, int c) {
+            constexpr int ST = decltype(stc)::value;
+            unsigned char *stg = smem + ST * L::stage;
+            const long long t0 = job.tok0 + (long long)c * kChunk;
+            const int last = nvalid_of(c) - 1;
+            const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + job.h) * (long long)DK * 2;
+            const unsigned char *cv = (const unsigned char *)a.v +
+                                      ((t0 * H + job.h) * (long long)DV + job.col0) * 2;
+#pragma unroll
+            for (int j = 0; j < CK; ++j) {
+                const int P = 64 * j + lane;
+                const int r = P / KG, pg = P % KG;
+                const int rq = r < last ? r : last;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(cq + (unsigned)rq * rsK + 16 * kq_logical<DK>(r, pg)),
+                    (lds_void *)(stg + L::sQ + 1024 * j), 16, 0, 0);
+            }
 #pragma unroll
             for (int j = 0; j < CV; ++j) {
                 const int byte = 1024 * j + 16 * lane;
@@ -1172,153 +1232,160 @@ __global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
         };
         // g of chunk c (one copy instruction), a step earlier than the rest of its data
         auto copy_g = [&](int c) {
-            const unsigned char *rec = (const unsigned char *)a.prep +
-                                       ((slot0 + c) * H + job.h) * (long long)kPrepRecordBytes;
-            __builtin_amdgcn_global_load_lds((const void *)(rec + kRecG + 4 * lane),
+            __builtin_amdgcn_global_load_lds((const void *)(rec_of(c) + kRecG + 4 * lane),
                                              (lds_void *)(smem + L::sG + (c & 3) * kChunk * 4),
                                              4, 0, 0);
         };
-        // (the barrier without a fence: this wave's copies are ordered by the counts alone)
-        if (nchunks > 0) {
-            copy_g(0);
-            if (nchunks > 1) copy_g(1);
-            if (nchunks > 2) copy_g(2);
-            copy(s0, 0);
-            if (nchunks > 1) {
-                copy(s1, 1);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");   // all but chunk 1
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (is_a) {
+            if (nchunks > 0) {
+                copy_a(s0, 0);
+                if (nchunks > 1) {
+                    copy_a(s1, 1);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopiesA) : "memory");   // all but chunk 1
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_s_barrier();
             }
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_s_barrier();
-        }
-        // step c: chunk c+2 and g of chunk c+3; then everything issued before this step is in
-        auto step = [&](auto stc, int c) {
-            if (c + 3 < nchunks) {
-                copy(stc, c + 2);
-                copy_g(c + 3);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies + 1) : "memory");
-            } else if (c + 2 < nchunks) {
-                copy(stc, c + 2);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            auto step = [&](auto stc, int c) {
+                if (c + 2 < nchunks) {
+                    copy_a(stc, c + 2);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopiesA) : "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                __builtin_amdgcn_s_barrier();
+            };
+            for (int c = 0; c < nchunks; c += 3) {
+                step(s2, c);
+                if (c + 1 < nchunks) step(s0, c + 1);
+                if (c + 2 < nchunks) step(s1, c + 2);
             }
-            __builtin_amdgcn_s_barrier();
-        };
-        for (int c = 0; c < nchunks; c += 3) {
-            step(s2, c);
-            if (c + 1 < nchunks) step(s0, c + 1);
-            if (c + 2 < nchunks) step(s1, c + 2);
+        } else {
+            if (nchunks > 0) {
+                copy_g(0);
+                if (nchunks > 1) copy_g(1);
+                if (nchunks > 2) copy_g(2);
+                copy_b(s0, 0);
+                if (nchunks > 1) {
+                    copy_b(s1, 1);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopiesB) : "memory");   // all but chunk 1
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_s_barrier();
+            }
+            auto step = [&](auto stc, int c) {
+                if (c + 3 < nchunks) {
+                    copy_b(stc, c + 2);
+                    copy_g(c + 3);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopiesB + 1) : "memory");
+                } else if (c + 2 < nchunks) {
+                    copy_b(stc, c + 2);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopiesB) : "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                __builtin_amdgcn_s_barrier();
+            };
+            for (int c = 0; c < nchunks; c += 3) {
+                step(s2, c);
+                if (c + 1 < nchunks) step(s0, c + 1);
+                if (c + 2 < nchunks) step(s1, c + 2);
+            }
         }
         return;
     }
 
-    // ================================================================ factor / P wave
-    if (wave == 1) {
-        // The scan holds its state as S = 2^ls Shat: ls starts at 0 and after each chunk
-        // becomes ls + g_C, or 0 when that would fall below -32 (the chain waves then
-        // rescale Shat); both follow the same rule on the same g_C, so they agree bit for
-        // bit.  This wave folds 2^ls into the factors it leaves in the stage:
-        //   sGam[t] = gamma_t 2^ls,  sRho[t] = (gamma_C / gamma_t) / 2^ls'
-        // (ls of the chunk, ls' of the next).
-        float lsl = 0.f;
-        auto factors = [&](auto stc, int c) {
-            constexpr int ST = decltype(stc)::value;
-            unsigned char *stg = smem + ST * L::stage;
-            const float *gc = (const float *)(smem + L::sG + (c & 3) * kChunk * 4);
-            const float gt = gc[lane], gC = gc[kChunk - 1];
-            const float lsc = lsl;
-            float lsn = lsc + gC;
-            if (lsn < -32.f) lsn = 0.f;
-            ((float *)(stg + L::sGam))[lane] = __builtin_amdgcn_exp2f(gt + lsc);
-            ((float *)(stg + L::sRho))[lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
-            // Gamma_ti = 2^g_t 2^-g_i (g >= -126: both factors are normal floats)
-            ((float *)(stg + L::sEp))[lane] = __builtin_amdgcn_exp2f(gt);
-            ((float *)(stg + L::sEm))[lane] = __builtin_amdgcn_exp2f(-gt);
-            lsl = lsn;
-        };
-        // P = lower_incl(Q K^T (.) Gamma) of chunk c, blocks (t-block, i-block) (0,0) (1,0)
-        // (1,1) (2,0) (3,0) (2,1) (2,2) (3,1) (3,2) (3,3); the blocks (0,1) and (2,3) that
-        // the output waves read are zero.  Accumulator [r] = k_i . q_t, i = 16 ib + 4 lg + r,
-        // t = 16 tb + ln: row t, columns i .. i + 3 of P.
+    // ================================================================ P wave
+    if (role == 1) {
+        // P = lower_incl(Q K^T (.) Gamma) of chunk c as the six operand fragments the output
+        // waves read: fragment f < 4 holds rows 16 f .. 16 f + 15 and columns 0 .. 31,
+        // fragments 4 and 5 rows 32 .. 47 and 48 .. 63 and columns 32 .. 63 (the rest of P is
+        // zero); lane (ln, lg) holds row r0 + ln, columns c0 + 8 lg .. c0 + 8 lg + 7.  The K
+        // operand takes the tile's rows as they lie (the internal token order), so the two
+        // accumulator blocks of a 32-column half pack into a fragment directly: accumulator
+        // [r] of block (tb, ib) = k_i . q_t, t = 16 tb + ln, i = original token of internal
+        // row 16 ib + 4 lg + r, which is 32 (ib / 2) + 8 lg + 4 (ib % 2) + r.
+        // Gamma_ti = 2^g_t 2^-g_i (g >= -126: both factors are normal floats).
         auto make_p = [&](auto stc, int c) {
             constexpr int ST = decltype(stc)::value;
             const unsigned char *stg = smem + ST * L::stage;
-            const float *sEp = (const float *)(stg + L::sEp);
-            const float *sEm = (const float *)(stg + L::sEm);
+            const float *gc = (const float *)(smem + L::sG + (c & 3) * kChunk * 4);
             const unsigned char *bK = stg + L::sK;
             const unsigned char *bQ = stg + L::sQ;
-            unsigned char *bP = smem + L::sPb;
-            constexpr int kTb[10] = {0, 1, 1, 2, 3, 2, 2, 3, 3, 3};
-            constexpr int kIb[10] = {0, 0, 1, 0, 0, 1, 2, 1, 2, 3};
-            // every fragment in one batch of LDS reads
+            unsigned char *bP = smem + L::sPb + (c & 1) * L::szP;
+            // blocks (tb, ib) in fragment order: (f, 0), (f, 1) for f < 4, then (2, 2) (2, 3)
+            // (3, 2) (3, 3)
+            constexpr int kTb[12] = {0, 0, 1, 1, 2, 2, 3, 3, 2, 2, 3, 3};
+            constexpr int kIb[12] = {0, 1, 0, 1, 0, 1, 0, 1, 2, 3, 2, 3};
             bf16x8 fkb[KBD][4], fqb[KBD][4];
 #pragma unroll
             for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    fkb[kb][i] = ldfrag_kq<DK>(bK, split_pos(i * 16 + ln), kb * 32 + 8 * lg);
+                    fkb[kb][i] = ldfrag_kq<DK>(bK, i * 16 + ln, kb * 32 + 8 * lg);
                     fqb[kb][i] = ldfrag_kq<DK>(bQ, i * 16 + ln, kb * 32 + 8 * lg);
                 }
+            float gt[4];
+            f32x4 gi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gt[i] = gc[i * 16 + ln];
+                gi[i] = *(const f32x4 *)(gc + 32 * (i >> 1) + 8 * lg + 4 * (i & 1));
+            }
+            f32x4 acc[12];
+#pragma unroll
+            for (int p = 0; p < 12; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+                for (int p = 0; p < 12; ++p) M::mma(acc[p], fkb[kb][kIb[p]], fqb[kb][kTb[p]]);
             float et[4];
             f32x4 ei[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                et[i] = sEp[i * 16 + ln];
-                ei[i] = *(const f32x4 *)(sEm + i * 16 + 4 * lg);
+                et[i] = __builtin_amdgcn_exp2f(gt[i]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ei[i][r] = __builtin_amdgcn_exp2f(-gi[i][r]);
             }
-            f32x4 acc[10];
+            f32x4 pv[12];
 #pragma unroll
-            for (int p = 0; p < 10; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KBD; ++kb)
-#pragma unroll
-                for (int p = 0; p < 10; ++p) M::mma(acc[p], fkb[kb][kIb[p]], fqb[kb][kTb[p]]);
-            f32x4 pv[10];
-#pragma unroll
-            for (int p = 0; p < 10; ++p) {
+            for (int p = 0; p < 12; ++p) {
                 const int tb = kTb[p], ib = kIb[p];
                 const int t = tb * 16 + ln;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = ib * 16 + 4 * lg + r;
+                    const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
                     pv[p][r] = (i <= t) ? acc[p][r] * et[tb] * ei[ib][r] : 0.f;
                 }
             }
-            // the output waves hold P of chunk c-1 in registers once these flags are up
-            if (c > 0)
-                for (int g = 0; g < NS; ++g) wait_flag(flagP + g, c - 1);
 #pragma unroll
-            for (int p = 0; p < 10; ++p)
-                M::put4((OP *)(bP + swz<OP, kChunk>(kTb[p] * 16 + ln, kIb[p] * 16 + 4 * lg)), pv[p]);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            M::put4((OP *)(bP + swz<OP, kChunk>(ln, 16 + 4 * lg)), z);
-            M::put4((OP *)(bP + swz<OP, kChunk>(32 + ln, 48 + 4 * lg)), z);
+            for (int f = 0; f < 6; ++f)
+                *(bf16x8 *)(bP + (f * 64 + lane) * 16) = pack8s(pv[2 * f], pv[2 * f + 1]);
         };
         if (nchunks > 0) {
             __syncthreads();
-            factors(s0, 0);
             __syncthreads();
         }
-        // step c: decay factors of chunk c+1 (stage STn), P of chunk c (stage STc)
-        auto step = [&](auto stc, auto stn, int c) {
-            if (c + 1 < nchunks) factors(stn, c + 1);
+        // step c: P of chunk c (stage STc)
+        auto step = [&](auto stc, int c) {
             make_p(stc, c);
             __syncthreads();
         };
         for (int c = 0; c < nchunks; c += 3) {
-            step(s0, s1, c);
-            if (c + 1 < nchunks) step(s1, s2, c + 1);
-            if (c + 2 < nchunks) step(s2, s0, c + 2);
+            step(s0, c);
+            if (c + 1 < nchunks) step(s1, c + 1);
+            if (c + 2 < nchunks) step(s2, c + 2);
         }
         return;
     }
 
     // ================================================================ chain waves
-    if (wave < 2 + NS) {
-        const int sw = wave - 2;
+    if (role < 2 + NS) {
+        const int sw = role - 2;
         // this wave owns state columns c0 + ln
         const int c0 = job.col0 + 16 * sw;
         f32x4 S[MBK];
@@ -1497,27 +1564,23 @@ __global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
 
     // ================================================================ output waves
     {
-        const int yw = wave - 2 - NS;
+        const int yw = role - 2 - NS;
         const int c0 = job.col0 + 16 * yw;
         const unsigned char *sb = smem + L::sSb + yw * L::szSb;
         const unsigned char *ub = smem + L::sUb + yw * L::szU;
-        const unsigned char *bP = smem + L::sPb;
         f32x4 accYp[4];
         float gyp[4];
-        // U and P of chunk c into registers, then the flags that free their buffers
+        // U and P of chunk c into registers, then the flag that frees the U buffer (P has two
+        // buffers, by chunk parity, ordered by the step barriers)
         bf16x8 Uu0, Uu1, fp[6];
         auto take_up = [&](int c) {
             Uu0 = *(const bf16x8 *)(ub + lane * 16);
             Uu1 = *(const bf16x8 *)(ub + 1024 + lane * 16);
+            const unsigned char *bP = smem + L::sPb + (c & 1) * L::szP;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) fp[tb] = ldfrag<OP, kChunk>(bP, tb * 16 + ln, 8 * lg);
-            fp[4] = ldfrag<OP, kChunk>(bP, 32 + ln, 32 + 8 * lg);
-            fp[5] = ldfrag<OP, kChunk>(bP, 48 + ln, 32 + 8 * lg);
+            for (int f = 0; f < 6; ++f) fp[f] = *(const bf16x8 *)(bP + (f * 64 + lane) * 16);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (lane == 0) {
-                flagU[yw] = c;
-                flagP[yw] = c;
-            }
+            if (lane == 0) flagU[yw] = c;
         };
         // Y of chunk c = diag(gamma 2^ls) (Shat^T Q^T)^T (accYp, gyp) + P U
         auto finish = [&](int c) {
@@ -1568,10 +1631,12 @@ __global__ __launch_bounds__(64 * (2 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
                 accYp[tb] = accQ[tb];
                 gyp[tb] = gy[tb];
             }
+            if (yw == 0 && c + 1 < nchunks) factors(std::integral_constant<int, (ST + 1) % 3>{}, c + 1);
             __syncthreads();
         };
         if (nchunks > 0) {
             __syncthreads();
+            if (yw == 0) factors(s0, 0);
             __syncthreads();
         }
         for (int c = 0; c < nchunks; c += 3) {
@@ -1610,7 +1675,7 @@ hipError_t launch_scan_split(const PrefillArgs &args, long long units, int ntile
     a2.ntiles = ntiles;
     if constexpr (MODE == kModeScan && DVT <= 32) {
         hipLaunchKernelGGL((scan_pipe_kernel<DK, DVT>), dim3((unsigned)groups),
-                           dim3(64 * (2 + 2 * (DVT / 16))), 0, stream, a2);
+                           dim3(64 * (3 + 2 * (DVT / 16))), 0, stream, a2);
     } else {
         hipLaunchKernelGGL((scan_split_kernel<DK, DVT, MODE>), dim3((unsigned)groups),
                            dim3(64 * (scan_waves<DVT>() + kLoaders)), 0, stream, a2);
