@@ -145,6 +145,53 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                            void *stream);
 
+/*
+ * The steps either side of the rule, as the reading notes on Qwen3.8-Next give them
+ * (section 2.1 "Gated DeltaNet": "Feature parameterization", "Gating dynamics" and the output
+ * equation).  Each is one streaming pass; none allocates, synchronises or keeps state.
+ */
+
+/*
+ * Short causal depthwise convolution, SiLU and (head_dim > 0) L2 normalisation per head:
+ *   out[t, c] = SiLU(sum_j weight[c, j] x[t - (width-1) + j, c])  over t's own sequence,
+ *   then, with head_dim > 0, each head's head_dim channels divided by sqrt(sum^2 + 1e-6).
+ * The width - 1 inputs before a sequence's first token come from state_in (or are zero).
+ *   x, out       [total_T, channels] dtype (token-major, e.g. channels = H * d); 16-byte
+ *                aligned; out must not overlap any input
+ *   weight       [channels, width] fp32; weight[c, width-1] weighs the current token
+ *   cu_seqlens   device int32 [num_seqs + 1] (as for gdn_prefill) or NULL (equal lengths)
+ *   state_in     [num_seqs, channels, width - 1] fp32, oldest input first, or NULL (zeros)
+ *   state_out    same shape, or NULL: the width - 1 inputs that end each sequence (reaching
+ *                into state_in for sequences shorter than width - 1).  It may be exactly
+ *                state_in (carried in place); a decode step is a call with num_seqs = B
+ *                sequences of one token each.
+ * channels: a multiple of 64; width in 1..4; head_dim in {0, 64, 128}, dividing channels.
+ */
+gdn_status gdn_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_T, int32_t channels, int32_t width,
+                          int32_t head_dim, int32_t dtype, void *out, const float *state_in,
+                          float *state_out, void *stream);
+
+/*
+ * Gates:  alpha = exp(-exp(A[h]) * softplus(a + b_alpha[h])),  beta = sigmoid(b).
+ *   a, b          [total_T, H] fp32 pre-activations (read only)
+ *   A, b_alpha    [H] fp32 per-head time constant and bias
+ *   alpha, beta   [total_T, H] fp32 (written), the gates gdn_prefill and gdn_decode_step take
+ * Outputs must not overlap the inputs or each other.
+ */
+gdn_status gdn_gates(const float *a, const float *b, const float *A, const float *b_alpha,
+                     int64_t total_T, int32_t H, float *alpha, float *beta, void *stream);
+
+/*
+ * Output gate with a zero-centred RMSNorm, per row of d_v values:
+ *   out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + weight)
+ *   y, z, out  [rows, d_v] dtype (rows = total_T * H); 16-byte aligned; out may be exactly y
+ *   weight     [d_v] fp32, the scale's offset from one (zero = plain RMSNorm)
+ * d_v in {64, 128}; eps >= 0 (the binding's default is 1e-6).
+ */
+gdn_status gdn_output_gate(const void *y, const void *z, const float *weight, int64_t rows,
+                           int32_t d_v, float eps, int32_t dtype, void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -208,4 +208,81 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_T, int32_t channels, int32_t width,
+                          int32_t head_dim, int32_t dtype, void *out, const float *state_in,
+                          float *state_out, void *stream)
+{
+    if (total_T < 0 || num_seqs <= 0 || channels <= 0 || channels % 64 != 0)
+        return GDN_ERR_INVALID_ARGUMENT;
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (width < 1 || width > 4) return GDN_ERR_UNSUPPORTED;
+    if (head_dim != 0 && head_dim != 64 && head_dim != 128) return GDN_ERR_UNSUPPORTED;
+    if (head_dim != 0 && channels % head_dim != 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (!cu_seqlens && total_T % num_seqs != 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (!weight || (total_T > 0 && (!x || !out))) return GDN_ERR_INVALID_ARGUMENT;
+    if ((x && !aligned(x, 16)) || (out && !aligned(out, 16)) || !aligned(weight, 4) ||
+        (state_in && !aligned(state_in, 4)) || (state_out && !aligned(state_out, 4)) ||
+        (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const size_t n_x = (size_t)total_T * channels * esize(dtype);
+    const size_t n_w = (size_t)channels * width * 4;
+    const size_t n_s = (size_t)num_seqs * channels * (width - 1) * 4;
+    const size_t n_cu = cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0;
+    struct Span { const void *p; size_t n; };
+    const Span ins[] = {{x, n_x}, {weight, n_w}, {state_in, n_s}, {cu_seqlens, n_cu}};
+    for (const Span &i : ins) {
+        if (overlap(out, n_x, i.p, i.n)) return GDN_ERR_INVALID_ARGUMENT;
+        // the carried state may be updated in place (state_out == state_in exactly)
+        if (i.p != state_in || state_out != state_in)
+            if (overlap(state_out, n_s, i.p, i.n)) return GDN_ERR_INVALID_ARGUMENT;
+    }
+    if (overlap(state_out, n_s, out, n_x)) return GDN_ERR_INVALID_ARGUMENT;
+    hipError_t err = gdn::launch_short_conv(x, weight, cu_seqlens, num_seqs, total_T, channels,
+                                            width, head_dim, dtype, state_in, state_out, out,
+                                            (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_gates(const float *a, const float *b, const float *A, const float *b_alpha,
+                     int64_t total_T, int32_t H, float *alpha, float *beta, void *stream)
+{
+    if (total_T < 0 || H <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (total_T == 0) return GDN_OK;
+    if (!a || !b || !A || !b_alpha || !alpha || !beta) return GDN_ERR_INVALID_ARGUMENT;
+    const void *all[] = {a, b, A, b_alpha, alpha, beta};
+    for (const void *p : all)
+        if (!aligned(p, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    const size_t n = (size_t)total_T * H * 4, nh = (size_t)H * 4;
+    struct Span { const void *p; size_t n; };
+    const Span ins[] = {{a, n}, {b, n}, {A, nh}, {b_alpha, nh}};
+    for (const Span &i : ins)
+        if (overlap(alpha, n, i.p, i.n) || overlap(beta, n, i.p, i.n))
+            return GDN_ERR_INVALID_ARGUMENT;
+    if (overlap(alpha, n, beta, n)) return GDN_ERR_INVALID_ARGUMENT;
+    hipError_t err = gdn::launch_gates(a, b, A, b_alpha, total_T, H, alpha, beta,
+                                       (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_output_gate(const void *y, const void *z, const float *weight, int64_t rows,
+                           int32_t d_v, float eps, int32_t dtype, void *out, void *stream)
+{
+    if (rows < 0 || !(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (rows == 0) return GDN_OK;
+    if (!y || !z || !weight || !out) return GDN_ERR_INVALID_ARGUMENT;
+    if (!aligned(y, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(weight, 4))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const size_t n = (size_t)rows * d_v * esize(dtype);
+    // out may be y exactly (each row is read whole before it is written)
+    if ((out != y && overlap(out, n, y, n)) || overlap(out, n, z, n) ||
+        overlap(out, n, weight, (size_t)d_v * 4))
+        return GDN_ERR_INVALID_ARGUMENT;
+    hipError_t err = gdn::launch_output_gate(y, z, weight, rows, d_v, eps, dtype, out,
+                                             (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

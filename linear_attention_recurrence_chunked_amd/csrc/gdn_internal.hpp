@@ -48,4 +48,13 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
                          const float *beta, float *state, void *y, int B, int H, int dk,
                          int dv, int dtype, hipStream_t stream);
 
+hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, int nseq,
+                             long long total_T, int C, int W, int head_dim, int dtype,
+                             const float *state_in, float *state_out, void *out,
+                             hipStream_t stream);
+hipError_t launch_gates(const float *a, const float *b, const float *A, const float *b_alpha,
+                        long long total_T, int H, float *alpha, float *beta, hipStream_t stream);
+hipError_t launch_output_gate(const void *y, const void *z, const float *w, long long rows,
+                              int dv, float eps, int dtype, void *out, hipStream_t stream);
+
 }  // namespace gdn

@@ -64,6 +64,12 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill_ex.argtypes = pre + [i32, i32]
     lib.gdn_decode_step.restype = i32
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.gdn_short_conv.restype = i32
+    lib.gdn_short_conv.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.gdn_gates.restype = i32
+    lib.gdn_gates.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp, vp]
+    lib.gdn_output_gate.restype = i32
+    lib.gdn_output_gate.argtypes = [vp, vp, vp, i64, i32, c.c_float, i32, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -164,3 +170,56 @@ def gdn_decode_step(q, k, v, alpha, beta, state, y=None, stream=None):
                                 _stream(stream))
     _check("gdn_decode_step", st)
     return y
+
+
+# ---- the steps either side of the rule ------------------------------------------------------
+
+def gdn_short_conv(x, weight, cu_seqlens=None, num_seqs=None, head_dim: int = 0, out=None,
+                   state_in=None, state_out=None, stream=None):
+    """Causal depthwise convolution + SiLU (+ per-head L2Norm when head_dim > 0).
+    x: [T, C] (or [T, H, d], taken as [T, H*d]) float32/bfloat16; weight: [C, W] fp32;
+    state_in/state_out: [N, C, W-1] fp32 or None.  Returns out (same shape as x)."""
+    import torch
+    T = x.shape[0]
+    C = x.numel() // T if T else int(torch.tensor(x.shape[1:]).prod())
+    W = weight.shape[1]
+    if cu_seqlens is not None:
+        num_seqs = cu_seqlens.shape[0] - 1
+    elif num_seqs is None:
+        num_seqs = 1
+    if out is None:
+        out = torch.empty_like(x)
+    st = load().gdn_short_conv(_ptr(x), _ptr(weight), _ptr(cu_seqlens), num_seqs, T, C, W,
+                               head_dim, _dtype_code(x), _ptr(out), _ptr(state_in),
+                               _ptr(state_out), _stream(stream))
+    _check("gdn_short_conv", st)
+    return out
+
+
+def gdn_gates(a, b, A, b_alpha, alpha=None, beta=None, stream=None):
+    """alpha = exp(-exp(A) softplus(a + b_alpha)), beta = sigmoid(b); a, b [T, H] fp32,
+    A, b_alpha [H] fp32.  Returns (alpha, beta)."""
+    import torch
+    T, H = a.shape
+    if alpha is None:
+        alpha = torch.empty_like(a)
+    if beta is None:
+        beta = torch.empty_like(a)
+    st = load().gdn_gates(_ptr(a), _ptr(b), _ptr(A), _ptr(b_alpha), T, H, _ptr(alpha),
+                          _ptr(beta), _stream(stream))
+    _check("gdn_gates", st)
+    return alpha, beta
+
+
+def gdn_output_gate(y, z, weight, eps: float = 1e-6, out=None, stream=None):
+    """sigmoid(z) * RMSNorm(y) * (1 + weight) over the last axis (d_v in {64, 128});
+    y, z [..., d_v] float32/bfloat16, weight [d_v] fp32.  Returns out (may be y)."""
+    import torch
+    dv = y.shape[-1]
+    rows = y.numel() // dv
+    if out is None:
+        out = torch.empty_like(y)
+    st = load().gdn_output_gate(_ptr(y), _ptr(z), _ptr(weight), rows, dv, float(eps),
+                                _dtype_code(y), _ptr(out), _stream(stream))
+    _check("gdn_output_gate", st)
+    return out

@@ -223,3 +223,42 @@ def to_torch(arr: np.ndarray, device, dtype: str):
     else:
         t = torch.from_numpy(np.ascontiguousarray(arr))
     return t.to(device)
+
+
+def layer_step_inputs(lengths, H: int, d: int, width: int, dtype: str, seed: int,
+                      with_state: bool = True) -> dict:
+    """Seeded random inputs of the steps either side of the rule (random draws only):
+    projections x_q, x_k, x_v [T, H*d] and the output gate's z and y [T, H, d] in ``dtype``;
+    conv weights [H*d, width] ~ N(0, 1/width) and carried conv states [N, H*d, width-1]
+    ~ N(0, 1) in fp32; gate pre-activations a, b [T, H] ~ N(0, 2^2), time constants
+    A [H] ~ U(-2, 1), biases b_alpha [H] ~ N(0, 1) and the norm offset [d] ~ N(0, 0.1^2)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    C = H * d
+    N = len(lengths)
+    rng = np.random.default_rng([seed, 9001])
+    out = {"lengths": lengths, "T": T, "H": H, "d": d, "C": C, "W": width, "N": N,
+           "dtype": dtype,
+           "cu_seqlens": np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)}
+    for n in ("x_q", "x_k", "x_v"):
+        out[n] = _store(rng.standard_normal((T, C)), dtype)
+    for n in ("w_q", "w_k", "w_v"):
+        out[n] = (rng.standard_normal((C, width)) / np.sqrt(width)).astype(np.float32)
+    for n in ("s_q", "s_k", "s_v"):
+        out[n] = (rng.standard_normal((N, C, width - 1)).astype(np.float32)
+                  if with_state and width > 1 else None)
+    out["a"] = (2.0 * rng.standard_normal((T, H))).astype(np.float32)
+    out["b"] = (2.0 * rng.standard_normal((T, H))).astype(np.float32)
+    out["A"] = rng.uniform(-2.0, 1.0, H).astype(np.float32)
+    out["b_alpha"] = rng.standard_normal(H).astype(np.float32)
+    out["z"] = _store(rng.standard_normal((T, H, d)), dtype)
+    out["y"] = _store(rng.standard_normal((T, H, d)), dtype)
+    out["norm_w"] = (0.1 * rng.standard_normal(d)).astype(np.float32)
+    return out
+
+
+def as_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact values a stored array holds, as float64."""
+    if dtype == "bf16" and arr.dtype == np.uint16:
+        return bf16_to_f64(arr)
+    return np.asarray(arr, dtype=np.float64)

@@ -154,3 +154,79 @@ def test_decode_empty_batch_is_a_no_op(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         gdn.load(str(tmp_path / "missing.so"))
+
+
+# ---- the layer steps --------------------------------------------------------------------
+
+def short_conv(lib, **kw):
+    a = dict(x=1 * G, w=2 * G, cu=None, N=2, T=64, C=256, W=4, hd=128, dt=1, out=3 * G,
+             sin=4 * G, sout=5 * G, stream=None)
+    a.update(kw)
+    return lib.gdn_short_conv(a["x"], a["w"], a["cu"], a["N"], a["T"], a["C"], a["W"], a["hd"],
+                              a["dt"], a["out"], a["sin"], a["sout"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=100), gdn.GDN_ERR_INVALID_ARGUMENT),            # not a multiple of 64
+    (dict(W=5), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(W=0), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(hd=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(C=192, hd=128), gdn.GDN_ERR_INVALID_ARGUMENT),    # heads do not tile the channels
+    (dict(T=63), gdn.GDN_ERR_INVALID_ARGUMENT),             # T not a multiple of N
+    (dict(N=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(dt=2), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(x=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(w=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(x=1 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(out=1 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # out overlaps x
+    (dict(sout=2 * G), gdn.GDN_ERR_INVALID_ARGUMENT),       # state over the weights
+    (dict(sout=4 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),   # state partly over state_in
+])
+def test_short_conv_rejects(lib, kw, code):
+    assert short_conv(lib, **kw) == code
+
+
+def gates(lib, **kw):
+    a = dict(a=1 * G, b=2 * G, A=3 * G, ba=4 * G, T=64, H=16, al=5 * G, be=6 * G, stream=None)
+    a.update(kw)
+    return lib.gdn_gates(a["a"], a["b"], a["A"], a["ba"], a["T"], a["H"], a["al"], a["be"],
+                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(A=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(al=1 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(al=1 * G), gdn.GDN_ERR_INVALID_ARGUMENT),         # alpha over a
+    (dict(be=5 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),     # beta over alpha
+])
+def test_gates_reject(lib, kw, code):
+    assert gates(lib, **kw) == code
+
+
+def output_gate(lib, **kw):
+    a = dict(y=1 * G, z=2 * G, w=3 * G, rows=64, dv=128, eps=1e-6, dt=1, out=4 * G, stream=None)
+    a.update(kw)
+    return lib.gdn_output_gate(a["y"], a["z"], a["w"], a["rows"], a["dv"], a["eps"], a["dt"],
+                               a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dv=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dt=3), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(rows=-1), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(eps=-1.0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(eps=float("nan")), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(z=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(y=1 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(out=2 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # out over z
+    (dict(out=1 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # out partly over y
+])
+def test_output_gate_rejects(lib, kw, code):
+    assert output_gate(lib, **kw) == code
+
+
+def test_layer_steps_empty_is_a_no_op(lib):
+    assert gates(lib, T=0) == gdn.GDN_OK
+    assert output_gate(lib, rows=0) == gdn.GDN_OK
