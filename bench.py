@@ -102,6 +102,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-layer-steps", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 counter passes: 3 prefill launches, 3 decode "
                          "steps and an elementwise kernel over 1 GiB (the calibration)")
@@ -143,6 +144,14 @@ def main():
     need = gdn.gdn_prefill_workspace_bytes(nseq, T, H, d, d, gdn.GDN_DTYPE_BF16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_r = torch.ones(128 << 20, dtype=torch.float32, device=dev)     # 512 MiB
+
+    def cache_flush():
+        # write 512 MiB, then read another 512 MiB: the read evicts the dirty lines the write
+        # left in L2 and the MALL, so the timed call starts with cold caches and no pending
+        # write-back of unrelated data
+        flush.fill_(1)
+        flush_r.sum()
 
     def run_prefill():
         gdn.gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
@@ -152,14 +161,14 @@ def main():
         run_prefill()
     torch.cuda.synchronize()
 
-    # cold-cache timing: 512 MiB written between launches, outside the events
+    # cold-cache timing: the caches are flushed between launches, outside the events
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for e0, e1 in evs:
         if not args.no_flush:
-            flush.fill_(1)
+            cache_flush()
         e0.record(stream)
         run_prefill()
         e1.record(stream)
@@ -177,6 +186,19 @@ def main():
     ew1.record(stream)
     torch.cuda.synchronize()
     warm_ms = ew0.elapsed_time(ew1) / args.steps
+
+    # the same calls after a write-only flush, whose dirty lines are written back during the
+    # timed call (for comparison with the flush above)
+    wo = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_prefill()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wo.append(e0.elapsed_time(e1))
+    wo_med = float(np.median(wo))
 
     # bf16 prefill = two launches: chunk records, then the state scan; the roofline covers
     # the pair (HIP events around the library call); rocprofv3 splits it per kernel
@@ -260,6 +282,53 @@ def main():
                               "frac": round(gbs4 / PEAK_HBM_GBS, 4)},
     }
 
+    # ------------------------------------------------------------------ layer steps
+    # the steps either side of the rule at the prefill workload's shape (bf16, H*d = 2048
+    # channels, conv width 4): each is one streaming pass, timed after a cache flush
+    layer = None
+    if not args.no_layer_steps:
+        li = wl.layer_step_inputs([w.T] * nseq, H, d, 4, "bf16", seed=2)
+        C = H * d
+        lx = wl.to_torch(li["x_q"], dev, "bf16")
+        lw = torch.from_numpy(li["w_q"]).to(dev)
+        ls_in = torch.from_numpy(li["s_q"]).to(dev)
+        ls_out = torch.empty_like(ls_in)
+        lo = torch.empty_like(lx)
+        la, lb = (torch.from_numpy(li[n]).to(dev) for n in ("a", "b"))
+        lA, lba = (torch.from_numpy(li[n]).to(dev) for n in ("A", "b_alpha"))
+        lal, lbe = torch.empty_like(la), torch.empty_like(la)
+        ly, lz = wl.to_torch(li["y"], dev, "bf16"), wl.to_torch(li["z"], dev, "bf16")
+        lnw = torch.from_numpy(li["norm_w"]).to(dev)
+        lout = torch.empty_like(ly)
+        e2b = T * C * 2
+        steps_def = {
+            "short_conv_silu_l2norm": (lambda: gdn.gdn_short_conv(
+                lx, lw, num_seqs=nseq, head_dim=d, out=lo, state_in=ls_in, state_out=ls_out),
+                2 * e2b + C * 4 * 4 + 2 * nseq * C * 3 * 4),
+            "gates": (lambda: gdn.gdn_gates(la, lb, lA, lba, alpha=lal, beta=lbe),
+                      4 * T * H * 4 + 2 * H * 4),
+            "output_gate": (lambda: gdn.gdn_output_gate(ly, lz, lnw, out=lout),
+                            3 * e2b + d * 4),
+        }
+        layer = {"workload": "bf16 T=%d (%d x %d) H=%d d=%d conv width 4" % (T, nseq, w.T, H, d)}
+        for name, (fn, nbytes) in steps_def.items():
+            for _ in range(3):
+                fn()
+            times = []
+            for _ in range(10):
+                cache_flush()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3)
+            us = float(np.median(times))
+            gb = nbytes / (us * 1e-6) / 1e9
+            layer[name] = {"us": round(us, 2), "algorithmic_bytes": nbytes,
+                           "achieved_GBs": round(gb, 1), "frac_of_hbm_peak": round(gb / PEAK_HBM_GBS, 4)}
+        del lx, lo, ly, lz, lout
+
     # ------------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -292,10 +361,12 @@ def main():
                    "chunk": CHUNK, "dv_tile": tile, "segment_chunks": seg,
                    "parallelism": "single GPU"},
         "prefill": {"ms_median": round(pre_med, 4), "ms_warm_back_to_back": round(warm_ms, 4),
+                    "ms_median_after_write_only_flush": round(wo_med, 4),
                     "tokens_per_s_warm": round(T / (warm_ms * 1e-3), 1),
                     "wall_s_timed_loop_incl_flush": round(wall, 4)},
         "roofline": roofline,
         "decode": decode,
+        "layer_steps": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

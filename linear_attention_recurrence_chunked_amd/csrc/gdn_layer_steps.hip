@@ -6,36 +6,53 @@
 //   features  q, k = L2Norm(SiLU(ShortConv(.))),  v = SiLU(ShortConv(.))   (per head)
 //   gates     beta = sigmoid(b),  alpha = exp(-exp(A) softplus(a + b_alpha))
 //   output    o = sigmoid(z) (.) RMSNorm(y), the RMSNorm scale stored as an offset from one
-// All three stream their operands once and are HBM-bound, so each kernel is laid out for
-// coalesced rows: one wave owns 128 consecutive channels (two per lane) of a row.
+// All three stream their operands once and are HBM-bound, so each kernel moves 16 bytes per
+// lane per access (eight bf16 or, in two halves, eight fp32 values) along contiguous rows.
 //
 // Short convolution: out[t, c] = sum_j w[c, j] x[t - (W-1) + j, c] over the tokens of t's
 // own sequence, the W-1 inputs before a sequence's first token coming from a carried state
-// [N, C, W-1] (oldest first) or zero.  A wave takes 16 consecutive tokens of its 128 channels
-// and keeps the 16 + W - 1 input rows it needs in registers.
+// [N, C, W-1] (oldest first) or zero.  A wave takes 8 consecutive tokens of 512 channels and
+// keeps the 8 + W - 1 input rows it needs in registers.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
 namespace gdn {
 
 constexpr int kLsThreads = 256;
-constexpr int kConvTokens = 16;            // tokens per wave
+constexpr int kConvTokens = 8;             // tokens per wave
 constexpr float kLsEps = 1e-6f;
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-template <typename T> struct Pair;
-template <> struct Pair<float> {
-    static __device__ __forceinline__ f32x2 load(const float *p) { return *(const f32x2 *)p; }
-    static __device__ __forceinline__ void store(float *p, f32x2 x) { *(f32x2 *)p = x; }
-};
-template <> struct Pair<uint16_t> {
-    static __device__ __forceinline__ f32x2 load(const uint16_t *p) {
-        const uint32_t w = *(const uint32_t *)p;
-        return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+// Eight consecutive elements (16 bytes of bf16, 32 of fp32) as floats, and back.
+template <typename T> struct Oct;
+template <> struct Oct<uint16_t> {
+    typedef u32x4 raw;
+    static __device__ __forceinline__ raw load(const uint16_t *p) { return *(const u32x4 *)p; }
+    static __device__ __forceinline__ float get(const raw &r, int e) {
+        const uint32_t w = r[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     }
-    static __device__ __forceinline__ void store(uint16_t *p, f32x2 x) {
-        *(bf16x2 *)p = __builtin_convertvector(x, bf16x2);
+    static __device__ __forceinline__ raw zero() { return u32x4{0u, 0u, 0u, 0u}; }
+    static __device__ __forceinline__ void store(uint16_t *p, const float *x) {
+        *(bf16x8 *)p = bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                              (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
+    }
+};
+template <> struct Oct<float> {
+    struct raw { f32x4 lo, hi; };
+    static __device__ __forceinline__ raw load(const float *p) {
+        return raw{*(const f32x4 *)p, *(const f32x4 *)(p + 4)};
+    }
+    static __device__ __forceinline__ float get(const raw &r, int e) {
+        return e < 4 ? r.lo[e] : r.hi[e - 4];
+    }
+    static __device__ __forceinline__ raw zero() {
+        return raw{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    }
+    static __device__ __forceinline__ void store(float *p, const float *x) {
+        *(f32x4 *)p = f32x4{x[0], x[1], x[2], x[3]};
+        *(f32x4 *)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
     }
 };
 
@@ -51,47 +68,56 @@ __device__ __forceinline__ int seq_of(const int32_t *cu, int nseq, long long per
     return lo;
 }
 
-// Sum over lanes of one head: 64 lanes (128 channels) or each 32-lane half (64 channels).
-template <int HD>
+// Sum over the LPH lanes of one head (lanes LPH h .. LPH h + LPH - 1).
+template <int LPH>
 __device__ __forceinline__ float head_sum(float x)
 {
-    x += __shfl_xor(x, 1, kWave);
-    x += __shfl_xor(x, 2, kWave);
-    x += __shfl_xor(x, 4, kWave);
-    x += __shfl_xor(x, 8, kWave);
-    x += __shfl_xor(x, 16, kWave);
-    if constexpr (HD == 128) x += __shfl_xor(x, 32, kWave);
+#pragma unroll
+    for (int m = 1; m < LPH; m <<= 1) x += __shfl_xor(x, m, kWave);
     return x;
 }
 
-// HD: 0 (no normalisation), 64 or 128 channels per head.
+// One wave: 8 consecutive tokens of 512 channels, eight per lane; HD = 0 (no normalisation),
+// 64 or 128 channels per head (8 or 16 lanes).
 template <typename T, int W, int HD>
 __global__ __launch_bounds__(kLsThreads) void short_conv_kernel(
     const T *__restrict__ x, const float *__restrict__ wgt, const int32_t *__restrict__ cu,
     int nseq, long long total_T, int C, const float *__restrict__ state_in, T *__restrict__ out)
 {
+    using O = Oct<T>;
     const int lane = threadIdx.x & 63;
-    const int groups = (C + 127) / 128;
+    const int groups = (C + 511) / 512;
     const long long wid = (long long)blockIdx.x * (kLsThreads / 64) + (threadIdx.x >> 6);
     const long long tb = wid / groups;
-    const int c = (int)(wid % groups) * 128 + 2 * lane;           // this lane's two channels
+    const int c = (int)(wid % groups) * 512 + 8 * lane;           // this lane's 8 channels
     const long long t0 = tb * kConvTokens;
     if (t0 >= total_T) return;
     const bool live = c < C;
+    const int cc = live ? c : 0;                                   // in-bounds for every lane
     const long long per = cu ? 0 : total_T / nseq;
-    // weights of the two channels
-    f32x2 w[W];
+    // rows t0 - (W-1) .. t0 + kConvTokens - 1, each loaded from a row clamped into
+    // [0, total_T): rows outside it are never used (the token loop stops at total_T and the
+    // rows before a sequence come from the carried state)
+    constexpr int NR = kConvTokens + W - 1;
+    float xr[NR][8];
+    {
+        typename O::raw r[NR];
 #pragma unroll
-    for (int j = 0; j < W; ++j)
-        w[j] = live ? f32x2{wgt[(long long)c * W + j], wgt[(long long)(c + 1) * W + j]}
-                    : f32x2{0.f, 0.f};
-    // rows t0 - (W-1) .. t0 + 15 (rows outside [0, total_T) are never used)
-    f32x2 r[kConvTokens + W - 1];
+        for (int i = 0; i < NR; ++i) {
+            long long t = t0 - (W - 1) + i;
+            t = t < 0 ? 0 : (t >= total_T ? total_T - 1 : t);
+            r[i] = O::load(x + t * C + cc);
+        }
 #pragma unroll
-    for (int i = 0; i < kConvTokens + W - 1; ++i) {
-        const long long t = t0 - (W - 1) + i;
-        r[i] = (live && t >= 0 && t < total_T) ? Pair<T>::load(x + t * C + c) : f32x2{0.f, 0.f};
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[i][e] = O::get(r[i], e);
     }
+    float w[8][W];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < W; ++j) w[e][j] = wgt[(long long)(cc + e) * W + j];
     int n = seq_of(cu, nseq, per, t0);
     long long s_n = cu ? (long long)cu[n] : per * n;
     long long e_n = cu ? (long long)cu[n + 1] : per * (n + 1);
@@ -104,27 +130,35 @@ __global__ __launch_bounds__(kLsThreads) void short_conv_kernel(
             s_n = e_n;
             e_n = cu ? (long long)cu[n + 1] : per * (n + 1);
         }
-        f32x2 acc = {0.f, 0.f};
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
         for (int j = 0; j < W; ++j) {
             const long long tj = t - (W - 1) + j;
-            f32x2 xv = r[i + j];
-            if (tj < s_n) {                                    // before the sequence: state
-                xv = f32x2{0.f, 0.f};
-                if (state_in && live) {
-                    const long long sidx = (W - 1) + (tj - s_n);   // index into the state row
-                    const float *sp = state_in + ((long long)n * C + c) * (W - 1) + sidx;
-                    xv = f32x2{sp[0], sp[W - 1]};
-                }
+            if (tj >= s_n) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += w[e][j] * xr[i + j][e];
+            } else if (state_in) {                             // before the sequence: state
+                const long long sidx = (W - 1) + (tj - s_n);
+                const float *sp = state_in + ((long long)n * C + cc) * (W - 1) + sidx;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += w[e][j] * sp[e * (W - 1)];
             }
-            acc += w[j] * xv;
         }
-        f32x2 o = acc / (1.f + f32x2{__expf(-acc[0]), __expf(-acc[1])});   // SiLU
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // SiLU: x sigmoid(x) with the hardware reciprocal (about 1 ulp)
+            o[e] = o[e] * __builtin_amdgcn_rcpf(1.f + __expf(-o[e]));
+            ss += o[e] * o[e];
+        }
         if constexpr (HD > 0) {
-            const float ss = head_sum<HD>(o[0] * o[0] + o[1] * o[1]);
-            o *= __builtin_amdgcn_rsqf(ss + kLsEps);
+            const float f = __builtin_amdgcn_rsqf(head_sum<HD / 8>(ss) + kLsEps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= f;
         }
-        if (live) Pair<T>::store(out + t * C + c, o);
+        if (live) O::store(out + t * C + c, o);
     }
 }
 
@@ -168,41 +202,51 @@ __global__ __launch_bounds__(kLsThreads) void gates_kernel(
     beta[i] = sigmoidf_(b[i]);
 }
 
-// out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + w) over each row of DV values; one
-// wave per row, rows strided over the grid.  out may be y.
+// out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + w) over each row of DV values.  Eight
+// values per lane, DV / 8 lanes per row, 64 * 8 / DV rows per wave and step; two steps in
+// flight per iteration.  out may be y (each lane reads its values before it writes them).
 template <typename T, int DV>
 __global__ __launch_bounds__(kLsThreads) void output_gate_kernel(
     const T *y, const T *__restrict__ z, const float *__restrict__ w, long long rows,
     float eps, T *out)
 {
-    constexpr int PER = DV / 64;                                 // 1 or 2 values per lane
+    using O = Oct<T>;
+    constexpr int LPR = DV / 8;                                  // lanes per row
+    constexpr int RPW = 64 / LPR;                                // rows per wave and step
     const int lane = threadIdx.x & 63;
+    const int sub = lane / LPR, col = 8 * (lane % LPR);
     const long long wid = (long long)blockIdx.x * (kLsThreads / 64) + (threadIdx.x >> 6);
     const long long nw = (long long)gridDim.x * (kLsThreads / 64);
-    float ws[PER];
+    float ws[8];
 #pragma unroll
-    for (int p = 0; p < PER; ++p) ws[p] = 1.f + w[PER * lane + p];
-    for (long long row = wid; row < rows; row += nw) {
-        const long long base = row * DV + PER * lane;
-        float yv[PER], zv[PER];
-        if constexpr (PER == 2) {
-            const f32x2 a2 = Pair<T>::load(y + base), b2 = Pair<T>::load(z + base);
-            yv[0] = a2[0]; yv[1] = a2[1]; zv[0] = b2[0]; zv[1] = b2[1];
-        } else {
-            yv[0] = Elem<T>::load(y + base);
-            zv[0] = Elem<T>::load(z + base);
+    for (int e = 0; e < 8; ++e) ws[e] = 1.f + w[col + e];
+    for (long long r0 = 2 * wid * RPW; r0 < rows; r0 += 2 * nw * RPW) {
+        typename O::raw yv[2], zv[2];
+        long long row[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            row[u] = r0 + u * RPW + sub;
+            if (row[u] < rows) {
+                yv[u] = O::load(y + row[u] * DV + col);
+                zv[u] = O::load(z + row[u] * DV + col);
+            } else {
+                yv[u] = O::zero();
+                zv[u] = O::zero();
+            }
         }
-        float ss = 0.f;
 #pragma unroll
-        for (int p = 0; p < PER; ++p) ss += yv[p] * yv[p];
+        for (int u = 0; u < 2; ++u) {
+            float ss = 0.f;
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m, kWave);
-        const float inv = __builtin_amdgcn_rsqf(ss / DV + eps);
-        float o[PER];
+            for (int e = 0; e < 8; ++e) ss += O::get(yv[u], e) * O::get(yv[u], e);
+            ss = head_sum<LPR>(ss);
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.f / DV) + eps);
+            float o[8];
 #pragma unroll
-        for (int p = 0; p < PER; ++p) o[p] = yv[p] * inv * ws[p] * sigmoidf_(zv[p]);
-        if constexpr (PER == 2) Pair<T>::store(out + base, f32x2{o[0], o[1]});
-        else Elem<T>::store(out + base, o[0]);
+            for (int e = 0; e < 8; ++e)
+                o[e] = O::get(yv[u], e) * inv * ws[e] * sigmoidf_(O::get(zv[u], e));
+            if (row[u] < rows) O::store(out + row[u] * DV + col, o);
+        }
     }
 }
 
@@ -212,7 +256,7 @@ static hipError_t launch_conv_w(const void *x, const float *w, const int32_t *cu
                                 long long total_T, int C, int head_dim, const float *sin,
                                 float *sout, void *out, hipStream_t st)
 {
-    const long long waves = (total_T + kConvTokens - 1) / kConvTokens * ((C + 127) / 128);
+    const long long waves = (total_T + kConvTokens - 1) / kConvTokens * ((C + 511) / 512);
     const long long blocks = (waves + 3) / 4;
     if (blocks > 0) {
         if (head_dim == 128)
@@ -279,9 +323,11 @@ hipError_t launch_output_gate(const void *y, const void *z, const float *w, long
                               int dv, float eps, int dtype, void *out, hipStream_t stream)
 {
     if (rows <= 0) return hipSuccess;
-    // a few rows per wave: at most 2^16 workgroups of four waves
-    long long blocks = (rows + 3) / 4;
-    if (blocks > 65536) blocks = 65536;
+    // two steps of 64 * 8 / dv rows per wave and iteration; at most 8192 workgroups of four
+    // waves (32 per CU), each looping over its share
+    const long long per_wave = 2 * (64 * 8 / dv);
+    long long blocks = (rows + 4 * per_wave - 1) / (4 * per_wave);
+    if (blocks > 8192) blocks = 8192;
 #define GDN_OG(T, DV)                                                                       \
     hipLaunchKernelGGL((output_gate_kernel<T, DV>), dim3((unsigned)blocks), dim3(kLsThreads), \
                        0, stream, (const T *)y, (const T *)z, w, rows, eps, (T *)out)
