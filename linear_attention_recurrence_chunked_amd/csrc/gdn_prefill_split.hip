@@ -1144,6 +1144,9 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
     const std::integral_constant<int, 0> s0{};
     const std::integral_constant<int, 1> s1{};
     const std::integral_constant<int, 2> s2{};
+    // The step barrier orders LDS only: no wave reads another wave's global stores (y) during
+    // the scan, so the barrier waits for this wave's LDS operations and not for its stores.
+    auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     // Decay factors of chunk c into its stage (formed by the first output wave, a step ahead).
     // The scan holds its state as S = 2^ls Shat: ls starts at 0 and after each chunk becomes
     // ls + g_C, or 0 when that would fall below -32 (the chain waves then rescale Shat); both
@@ -1367,13 +1370,13 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
                 *(bf16x8 *)(bP + (f * 64 + lane) * 16) = pack8s(pv[2 * f], pv[2 * f + 1]);
         };
         if (nchunks > 0) {
-            __syncthreads();
-            __syncthreads();
+            lds_barrier();
+            lds_barrier();
         }
         // step c: P of chunk c (stage STc)
         auto step = [&](auto stc, int c) {
             make_p(stc, c);
-            __syncthreads();
+            lds_barrier();
         };
         for (int c = 0; c < nchunks; c += 3) {
             step(s0, c);
@@ -1539,11 +1542,11 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
             pack_state();
             wait_flag(flagS + sw, c);              // the output wave holds Shat of chunk c
             put_state();
-            __syncthreads();
+            lds_barrier();
         };
         if (nchunks > 0) {                // the prologue's barriers (chunk 0 staged)
-            __syncthreads();
-            __syncthreads();
+            lds_barrier();
+            lds_barrier();
         }
         for (int c = 0; c < nchunks; c += 3) {
             chunk(s0, c);
@@ -1632,12 +1635,12 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
                 gyp[tb] = gy[tb];
             }
             if (yw == 0 && c + 1 < nchunks) factors(std::integral_constant<int, (ST + 1) % 3>{}, c + 1);
-            __syncthreads();
+            lds_barrier();
         };
         if (nchunks > 0) {
-            __syncthreads();
+            lds_barrier();
             if (yw == 0) factors(s0, 0);
-            __syncthreads();
+            lds_barrier();
         }
         for (int c = 0; c < nchunks; c += 3) {
             step(s0, c);
