@@ -81,29 +81,32 @@ __device__ __forceinline__ f32x4 exp2x4(f32x4 x)
     return r;
 }
 
-// C += A B for 16 x 16 fp32 blocks on v_mfma_f32_16x16x32_bf16 with hi/lo bf16 splitting
-// (relative error about 2^-16).  A arrives in the row layout (lane (ln, lg) holds
-// A[ln][4lg + s]) and B in the accumulator layout (lane holds B[4lg + s][ln]); the 32-wide K
-// of the instruction carries (A_hi | A_lo) x (B_hi | B_hi), then (A_hi | 0) x (B_lo | 0).
-__device__ __forceinline__ void mm16s(f32x4 &c, f32x4 arow, f32x4 bcol)
+// C += A B for 16 x 16 fp32 blocks with hi/lo bf16 splitting (relative error about 2^-16):
+// A_hi B_hi + A_lo B_hi + A_hi B_lo on three v_mfma_f32_16x16x16_bf16.  A arrives in the row
+// layout (lane (ln, lg) holds A[ln][4lg + s]) and B in the accumulator layout (lane holds
+// B[4lg + s][ln]), which are the operand layouts of that instruction.  A value that enters
+// several products is split once (Sp).
+struct Sp {
+    bf16x4 hi, lo;
+};
+__device__ __forceinline__ Sp split4(f32x4 x)
 {
-    const bf16x4 ah = __builtin_convertvector(arow, bf16x4);
-    const bf16x4 al = __builtin_convertvector(arow - __builtin_convertvector(ah, f32x4), bf16x4);
-    const bf16x4 bh = __builtin_convertvector(bcol, bf16x4);
-    const bf16x4 bl = __builtin_convertvector(bcol - __builtin_convertvector(bh, f32x4), bf16x4);
-    const __bf16 z = (__bf16)0.f;
-    const bf16x8 a1 = {ah[0], ah[1], ah[2], ah[3], al[0], al[1], al[2], al[3]};
-    const bf16x8 b1 = {bh[0], bh[1], bh[2], bh[3], bh[0], bh[1], bh[2], bh[3]};
-    const bf16x8 a2 = {ah[0], ah[1], ah[2], ah[3], z, z, z, z};
-    const bf16x8 b2 = {bl[0], bl[1], bl[2], bl[3], z, z, z, z};
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, c, 0, 0, 0);
+    const bf16x4 h = __builtin_convertvector(x, bf16x4);
+    return Sp{h, __builtin_convertvector(x - __builtin_convertvector(h, f32x4), bf16x4)};
 }
-
-__device__ __forceinline__ f32x4 mm16sr(f32x4 arow, f32x4 bcol)
+__device__ __forceinline__ void mm3(f32x4 &c, const Sp &a, const Sp &b)
+{
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s ah = __builtin_bit_cast(v4s, a.hi), al = __builtin_bit_cast(v4s, a.lo);
+    const v4s bh = __builtin_bit_cast(v4s, b.hi), bl = __builtin_bit_cast(v4s, b.lo);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mm3r(const Sp &a, const Sp &b)
 {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    mm16s(c, arow, bcol);
+    mm3(c, a, b);
     return c;
 }
 
@@ -289,17 +292,21 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     f32x4 eye;
 #pragma unroll
     for (int r = 0; r < 4; ++r) eye[r] = (4 * lg + r == ln) ? 1.f : 0.f;
-    const f32x4 n2C = mm16sr(nT, nC), n2T = mm16sr(nC, nT);
-    const f32x4 m1C = mm16sr(nT, n2C), m1T = mm16sr(n2C, nT);
-    const f32x4 n4C = mm16sr(n2T, n2C), n4T = mm16sr(n2C, n2T);
+    const Sp snT = split4(nT), snC = split4(nC);
+    const f32x4 n2C = mm3r(snT, snC), n2T = mm3r(snC, snT);
+    const Sp sn2C = split4(n2C), sn2T = split4(n2T);
+    const f32x4 m1C = mm3r(snT, sn2C), m1T = mm3r(sn2C, snT);
+    const f32x4 n4C = mm3r(sn2T, sn2C), n4T = mm3r(sn2C, sn2T);
     const f32x4 p1C = eye - nC + n2C - m1C, p1T = eye - nT + n2T - m1T;
-    const f32x4 n8C = mm16sr(n4T, n4C);
+    const Sp sn4C = split4(n4C), sp1T = split4(p1T);
+    const f32x4 n8C = mm3r(split4(n4T), sn4C);
     f32x4 p2C = p1C, p2T = p1T;
-    mm16s(p2C, p1T, n4C);
-    mm16s(p2T, n4C, p1T);
+    mm3(p2C, sp1T, sn4C);
+    mm3(p2T, sn4C, sp1T);
+    const Sp sn8C = split4(n8C), sp2T = split4(p2T);
     f32x4 xC = p2C, xT = p2T;
-    mm16s(xC, p2T, n8C);
-    mm16s(xT, n8C, p2T);
+    mm3(xC, sp2T, sn8C);
+    mm3(xT, sn8C, sp2T);
     __syncthreads();   // K is dead: its space now holds A and the X blocks
 
     // ---- phase 3 (stores): A blocks, X_ww in the row layout, T' diagonal block ----
@@ -318,10 +325,10 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     {
         const int j = wave;
         const float bcol = sBeta[16 * j + ln];
-        auto arow = [&](int i, int m) {
-            return *(const f32x4 *)ablk(i, m);
+        auto arow = [&](int i, int m) { return split4(*(const f32x4 *)ablk(i, m)); };
+        auto xrow = [&](int i) {
+            return split4(*(const f32x4 *)(sX + (16 * i + ln) * L::LDX + 4 * lg));
         };
-        auto xrow = [&](int i) { return *(const f32x4 *)(sX + (16 * i + ln) * L::LDX + 4 * lg); };
         auto put_t = [&](int i, f32x4 z) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -329,21 +336,22 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
                                 z[r] * bcol);
         };
         if (j <= 2) {
-            const f32x4 xjj = xC;
-            f32x4 acc1 = mm16sr(arow(j + 1, j), xjj);
+            const Sp xjj = split4(xC);
+            f32x4 acc1 = mm3r(arow(j + 1, j), xjj);
             f32x4 acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
-            if (j + 2 <= 3) acc2 = mm16sr(arow(j + 2, j), xjj);
-            if (j + 3 <= 3) acc3 = mm16sr(arow(j + 3, j), xjj);
-            const f32x4 x1 = -mm16sr(xrow(j + 1), acc1);            // X_{j+1,j}
+            if (j + 2 <= 3) acc2 = mm3r(arow(j + 2, j), xjj);
+            if (j + 3 <= 3) acc3 = mm3r(arow(j + 3, j), xjj);
+            const f32x4 x1 = -mm3r(xrow(j + 1), split4(acc1));      // X_{j+1,j}
             put_t(j + 1, x1);
             if (j + 2 <= 3) {
-                mm16s(acc2, arow(j + 2, j + 1), x1);
-                if (j + 3 <= 3) mm16s(acc3, arow(j + 3, j + 1), x1);
-                const f32x4 x2 = -mm16sr(xrow(j + 2), acc2);        // X_{j+2,j}
+                const Sp sx1 = split4(x1);
+                mm3(acc2, arow(j + 2, j + 1), sx1);
+                if (j + 3 <= 3) mm3(acc3, arow(j + 3, j + 1), sx1);
+                const f32x4 x2 = -mm3r(xrow(j + 2), split4(acc2));  // X_{j+2,j}
                 put_t(j + 2, x2);
                 if (j + 3 <= 3) {
-                    mm16s(acc3, arow(j + 3, j + 2), x2);
-                    const f32x4 x3 = -mm16sr(xrow(j + 3), acc3);    // X_{j+3,j}
+                    mm3(acc3, arow(j + 3, j + 2), split4(x2));
+                    const f32x4 x3 = -mm3r(xrow(j + 3), split4(acc3));  // X_{j+3,j}
                     put_t(j + 3, x3);
                 }
             }
