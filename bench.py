@@ -269,17 +269,20 @@ def main():
     gbs = dbytes / (dec_us * 1e-6) / 1e9
     gbs4 = dbytes / (dec4_us * 1e-6) / 1e9
     dtr = load_traffic("decode_bf16_B128_H16_d128", DECODE_SOURCES)
+    # the roofline takes the rotating measurement: four state sets (512 MiB) exceed the
+    # 256 MB MALL, so each step streams its state from and to HBM, as in a many-layer model
     decode = {
-        "workload": wd.name, "steps": nsteps, "steps_per_s": round(1e6 / dec_us, 1),
-        "us_per_step": round(dec_us, 2), "tokens_per_s": round(B * 1e6 / dec_us, 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "workload": wd.name, "steps": nsteps, "steps_per_s": round(1e6 / dec4_us, 1),
+        "us_per_step": round(dec4_us, 2), "tokens_per_s": round(B * 1e6 / dec4_us, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs4, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs4 / PEAK_HBM_GBS, 4),
                      "traffic": None if dtr is None else dtr["bytes_per_launch"],
-                     "algorithmic_bytes_per_launch": dbytes},
-        "rotating_4_states": {"us_per_step": round(dec4_us, 2),
-                              "steps_per_s": round(1e6 / dec4_us, 1),
-                              "achieved_GBs": round(gbs4, 1),
-                              "frac": round(gbs4 / PEAK_HBM_GBS, 4)},
+                     "algorithmic_bytes_per_launch": dbytes,
+                     "measured_on": "4 state sets in rotation (512 MiB)"},
+        "one_state_set": {"us_per_step": round(dec_us, 2),
+                          "steps_per_s": round(1e6 / dec_us, 1),
+                          "achieved_GBs": round(gbs, 1),
+                          "frac": round(gbs / PEAK_HBM_GBS, 4)},
     }
 
     # ------------------------------------------------------------------ layer steps

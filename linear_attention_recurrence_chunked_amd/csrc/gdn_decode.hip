@@ -9,7 +9,9 @@
 // The step is HBM-bound (about 0.9 flop per byte), so the design is about bytes: each
 // workgroup owns a 64-column slice of one head's state, loads it into registers with
 // 16-byte coalesced loads, reduces S^T k and S^T q over the key dimension with wavefront
-// shuffles and a 1 KiB LDS exchange, and stores the updated slice once.
+// shuffles and a 1 KiB LDS exchange, and stores the updated slice once.  The state is read
+// and written with non-temporal hints: a layer's state is touched once per step, and a
+// model's states together do not stay in the caches between steps.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     f32x4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        s[i] = *(const f32x4 *)(S + (long)(rg + 16 * i) * DV + col);
+        s[i] = __builtin_nontemporal_load((const f32x4 *)(S + (long)(rg + 16 * i) * DV + col));
 
     float kr[RPT], qr[RPT];
 #pragma unroll
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const float bk = b * kr[i];
-        *(f32x4 *)(S + (long)(rg + 16 * i) * DV + col) = a * s[i] + bk * e;
+        __builtin_nontemporal_store(a * s[i] + bk * e, (f32x4 *)(S + (long)(rg + 16 * i) * DV + col));
     }
 }
 
