@@ -1066,8 +1066,8 @@ struct LdsPipe {
     static constexpr int sPb = sG + 4 * kChunk * 4;   // P of chunk c in buffer c & 1
     static constexpr int sSb = sPb + 2 * szP;
     static constexpr int sUb = sSb + NS * szSb;
-    static constexpr int sFlag = sUb + NS * szU;      // [2][NS] ints: Shat, U taken
-    static constexpr int total = sFlag + 2 * NS * 4;
+    static constexpr int sFlag = sUb + NS * szU;      // [2][NS][NS] ints: Shat, U taken
+    static constexpr int total = sFlag + 2 * NS * NS * 4;
     static_assert(total <= 160 * 1024, "LDS");
 };
 
@@ -1140,9 +1140,10 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
     };
     // (LDS-qualified, so that the flags take LDS instructions and no memory-counter waits)
     typedef __attribute__((address_space(3))) volatile int lds_flag;
+    // flag[g * NS + w]: output wave w holds the chain group g's Shat (flagS) or U (flagU)
     lds_flag *flagS = (lds_flag *)(smem + L::sFlag);
-    lds_flag *flagU = flagS + NS;
-    if (tid < 2 * NS) flagS[tid] = -1;
+    lds_flag *flagU = flagS + NS * NS;
+    if (tid < 2 * NS * NS) flagS[tid] = -1;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // wait until flag[i] >= v (the output waves raise these early in every chunk step)
     auto wait_flag = [&](lds_flag *f, int v) {
@@ -1397,8 +1398,10 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
     // ================================================================ chain waves
     if (role < 2 + NS) {
         const int sw = role - 2;
-        // this wave owns state columns c0 + ln
-        const int c0 = job.col0 + 16 * sw;
+        // this wave owns the state columns col0 + kq(sw, ln): its 16 columns interleave with
+        // the other group's in runs of four, so that the output waves hold, per lane, NS runs
+        // of four that are adjacent in the row (one 16-byte store at NS = 2)
+        const int c0 = job.col0 + 4 * NS * (ln >> 2) + 4 * sw + (ln & 3);
         f32x4 S[MBK];
         {
             const float *src = nullptr;
@@ -1412,7 +1415,7 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
             for (int m = 0; m < MBK; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[m][i] = src ? src[(long long)split_orig(16 * m + 4 * lg + i) * DV + ln] : 0.f;
+                    S[m][i] = src ? src[(long long)split_orig(16 * m + 4 * lg + i) * DV] : 0.f;
         }
         unsigned char *sb = smem + L::sSb + sw * L::szSb;
         unsigned char *ub = smem + L::sUb + sw * L::szU;
@@ -1494,7 +1497,8 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
                 for (int tb = 0; tb < 4; ++tb) {
                     // V[o0 .. o0 + 3][column] by one transposing read of the V rows
                     const int o0 = split_orig(tb * 16 + 4 * lg);
-                    const int col = 16 * sw + 4 * (ln & 3);
+                    // (lane j receives column 4 NS (j / 4) + 4 sw + j % 4 of tile rows o0..o0+3)
+                    const int col = 4 * NS * (ln & 3) + 4 * sw;
                     const bf16x4 v4 = ldtr(bVc + ((o0 + (ln >> 2)) * DVT + col) * 2);
                     R[tb] = __builtin_convertvector(v4, f32x4) - gam[tb] * acc_ks[tb];
                 }
@@ -1517,7 +1521,8 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
             {
                 const bf16x8 Uu0 = pack8s(U[0], U[1]);
                 const bf16x8 Uu1 = pack8s(U[2], U[3]);
-                if (c > 0) wait_flag(flagU + sw, c - 1);
+                if (c > 0)
+                    for (int w = 0; w < NS; ++w) wait_flag(flagU + sw * NS + w, c - 1);
                 *(bf16x8 *)(ub + lane * 16) = Uu0;
                 *(bf16x8 *)(ub + 1024 + lane * 16) = Uu1;
             }
@@ -1548,7 +1553,8 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
 #pragma unroll
             for (int m = 0; m < MBK; ++m) M::mma(S[m], fkt[1][m], Ub1);
             pack_state();
-            wait_flag(flagS + sw, c);              // the output wave holds Shat of chunk c
+            // every output wave holds Shat of chunk c
+            for (int w = 0; w < NS; ++w) wait_flag(flagS + sw * NS + w, c);
             put_state();
             lds_barrier();
         };
@@ -1568,49 +1574,63 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
             for (int m = 0; m < MBK; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[(long long)split_orig(16 * m + 4 * lg + i) * DV + ln] = S[m][i] * sp;
+                    dst[(long long)split_orig(16 * m + 4 * lg + i) * DV] = S[m][i] * sp;
         }
         return;
     }
 
     // ================================================================ output waves
+    // Output wave w forms y for tokens 64 w / NS .. 64 (w + 1) / NS - 1 of every chunk and
+    // all DVT columns: per 16-token block and column group g, Shat_g^T Q^T and U_g^T P^T in
+    // the accumulator layout (lane (ln, lg): token ln, the group's columns 4 lg .. 4 lg + 3,
+    // i.e. tile columns 4 NS lg + 4 g .. + 3), so that a lane's NS runs of four are adjacent.
     {
         const int yw = role - 2 - NS;
-        const int c0 = job.col0 + 16 * yw;
-        const unsigned char *sb = smem + L::sSb + yw * L::szSb;
-        const unsigned char *ub = smem + L::sUb + yw * L::szU;
-        f32x4 accYp[4];
-        float gyp[4];
-        // U and P of chunk c into registers, then the flag that frees the U buffer (P has two
-        // buffers, by chunk parity, ordered by the step barriers)
-        bf16x8 Uu0, Uu1, fp[6];
+        constexpr int TPW = 4 / NS;                   // 16-token blocks per output wave
+        const int tbw = TPW * yw;                     // this wave's first block
+        f32x4 accYp[NS][TPW];
+        float gyp[TPW];
+        // U of every group and the P fragments of this wave's token blocks, chunk c
+        bf16x8 Uu0[NS], Uu1[NS], fp[TPW][2];
         auto take_up = [&](int c) {
-            Uu0 = *(const bf16x8 *)(ub + lane * 16);
-            Uu1 = *(const bf16x8 *)(ub + 1024 + lane * 16);
+#pragma unroll
+            for (int g = 0; g < NS; ++g) {
+                const unsigned char *ub = smem + L::sUb + g * L::szU;
+                Uu0[g] = *(const bf16x8 *)(ub + lane * 16);
+                Uu1[g] = *(const bf16x8 *)(ub + 1024 + lane * 16);
+            }
             const unsigned char *bP = smem + L::sPb + (c & 1) * L::szP;
 #pragma unroll
-            for (int f = 0; f < 6; ++f) fp[f] = *(const bf16x8 *)(bP + (f * 64 + lane) * 16);
+            for (int u = 0; u < TPW; ++u) {
+                const int tb = tbw + u;
+                fp[u][0] = *(const bf16x8 *)(bP + (tb * 64 + lane) * 16);
+                if (tb >= 2) fp[u][1] = *(const bf16x8 *)(bP + ((tb + 2) * 64 + lane) * 16);
+            }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (lane == 0) flagU[yw] = c;
+            if (lane == 0)
+                for (int g = 0; g < NS; ++g) flagU[g * NS + yw] = c;
         };
         // Y of chunk c = diag(gamma 2^ls) (Shat^T Q^T)^T (accYp, gyp) + P U
         auto finish = [&](int c) {
-            f32x4 pu[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                pu[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                M::mma(pu[tb], Uu0, fp[tb]);
-            }
-            M::mma(pu[2], Uu1, fp[4]);
-            M::mma(pu[3], Uu1, fp[5]);
             const long long t0 = job.tok0 + (long long)c * kChunk;
             const int nv = nvalid_of(c);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
+            for (int u = 0; u < TPW; ++u) {
+                const int tb = tbw + u;
+                f32x4 yv[NS];
+#pragma unroll
+                for (int g = 0; g < NS; ++g) {
+                    f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+                    M::mma(pu, Uu0[g], fp[u][0]);
+                    if (tb >= 2) M::mma(pu, Uu1[g], fp[u][1]);
+                    yv[g] = accYp[g][u] * gyp[u] + pu;
+                }
                 const int t = tb * 16 + ln;
-                const f32x4 yv = accYp[tb] * gyp[tb] + pu[tb];
-                if (t < nv)
-                    store4((OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + c0 + 4 * lg, yv);
+                OP *dst = (OP *)a.y + ((t0 + t) * H + job.h) * (long long)DV + job.col0 + 4 * NS * lg;
+                if (t < nv) {
+                    if constexpr (NS == 2) *(bf16x8 *)dst = pack8s(yv[0], yv[1]);
+                    else store4(dst, yv[0]);
+                }
             }
         };
         auto step = [&](auto stc, int c) {
@@ -1619,28 +1639,39 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
             const float *sGam = (const float *)(stg + L::sGam);
             const unsigned char *bQ = stg + L::sQ;
             if (c > 0) take_up(c - 1);
-            bf16x8 Sb[KBD];
+            bf16x8 Sb[NS][KBD];
 #pragma unroll
-            for (int kb = 0; kb < KBD; ++kb) Sb[kb] = *(const bf16x8 *)(sb + (kb * 64 + lane) * 16);
+            for (int g = 0; g < NS; ++g) {
+                const unsigned char *sb = smem + L::sSb + g * L::szSb;
+#pragma unroll
+                for (int kb = 0; kb < KBD; ++kb) Sb[g][kb] = *(const bf16x8 *)(sb + (kb * 64 + lane) * 16);
+            }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (lane == 0) flagS[yw] = c;
-            f32x4 accQ[4];
+            if (lane == 0)
+                for (int g = 0; g < NS; ++g) flagS[g * NS + yw] = c;
+            f32x4 accQ[NS][TPW];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) accQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int g = 0; g < NS; ++g)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) accQ[g][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    M::mma(accQ[tb], Sb[kb], ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg));
-            float gy[4];
+                for (int u = 0; u < TPW; ++u) {
+                    const bf16x8 qf = ldfrag_kq<DK>(bQ, (tbw + u) * 16 + ln, kb * 32 + 8 * lg);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) gy[tb] = sGam[tb * 16 + ln];
+                    for (int g = 0; g < NS; ++g) M::mma(accQ[g][u], Sb[g][kb], qf);
+                }
+            float gy[TPW];
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) gy[u] = sGam[(tbw + u) * 16 + ln];
             __builtin_amdgcn_sched_barrier(0);
             if (c > 0) finish(c - 1);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                accYp[tb] = accQ[tb];
-                gyp[tb] = gy[tb];
+            for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+                for (int g = 0; g < NS; ++g) accYp[g][u] = accQ[g][u];
+                gyp[u] = gy[u];
             }
             if (yw == 0 && c + 1 < nchunks) factors(std::integral_constant<int, (ST + 1) % 3>{}, c + 1);
             lds_barrier();
