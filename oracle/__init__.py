@@ -11,6 +11,10 @@ Two implementations of the same definition live here:
 * :func:`chain_numpy` -- the same recurrence in numpy, for tiny cases and as an
   independent cross-check of the C code's indexing.
 
+The derivative of the same recurrence (for training) is :func:`prefill_backward` (C) and
+:func:`chain_backward_numpy` (numpy): reverse mode, token by token, through the four lines
+below.
+
 Both follow the jianyuh.github.io reading notes on Qwen3.8-Next, section 2.1 "Gated
 DeltaNet" (the four-line gated delta recurrence):
 
@@ -59,6 +63,15 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.gdn_oracle_backward.restype = ctypes.c_int
+        lib.gdn_oracle_backward.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -189,3 +202,108 @@ def chain_c(q, k, v, alpha, beta, s0=None):
     s = None if s0 is None else np.asarray(s0, dtype=np.float64)[None, None]
     y, sf = run(q, k, v, a, b, [0], [T], 1, s0=s, threads=1)
     return y[:, 0, :], sf[0, 0]
+
+
+def prefill_backward(q, k, v, alpha, beta, dy, cu_seqlens=None, s0=None, ds_final=None,
+                     heads=None, threads: int = 0):
+    """Reverse-mode derivative of :func:`prefill` for L = <dy, y> + <ds_final, S_T>.
+
+    dy: [rows, H, d_v] (any float dtype, widened to float64); ds_final: [nseq, H, d_k, d_v]
+    or None (zero).  Returns a dict of float64 arrays holding heads ``heads`` (all by
+    default): dq, dk [rows, nh, d_k], dv [rows, nh, d_v], dalpha, dbeta [rows, nh] and
+    ds0 [nseq, nh, d_k, d_v].  See gdn_oracle_backward in gdn_oracle.c.
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k and v must share one dtype")
+    rows, H, dk = q.shape
+    dv = v.shape[2]
+    alpha = np.ascontiguousarray(alpha, dtype=np.float64)
+    beta = np.ascontiguousarray(beta, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    if dy.shape != (rows, H, dv) or alpha.shape != (rows, H) or beta.shape != (rows, H):
+        raise ValueError("shape mismatch")
+    cu = np.array([0, rows], dtype=np.int64) if cu_seqlens is None else \
+        np.asarray(cu_seqlens, dtype=np.int64)
+    row0 = np.ascontiguousarray(cu[:-1])
+    lens = np.ascontiguousarray(np.diff(cu))
+    nseq = int(row0.shape[0])
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        if s0.shape != (nseq, H, dk, dv):
+            raise ValueError("s0 must be [nseq, H, d_k, d_v]")
+    if ds_final is not None:
+        ds_final = np.ascontiguousarray(ds_final, dtype=np.float64)
+        if ds_final.shape != (nseq, H, dk, dv):
+            raise ValueError("ds_final must be [nseq, H, d_k, d_v]")
+    h_lo, h_hi = (0, H) if heads is None else (int(heads[0]), int(heads[1]))
+    nh = h_hi - h_lo
+    out = dict(dq=np.zeros((rows, nh, dk)), dk=np.zeros((rows, nh, dk)),
+               dv=np.zeros((rows, nh, dv)), dalpha=np.zeros((rows, nh)),
+               dbeta=np.zeros((rows, nh)), ds0=np.zeros((nseq, nh, dk, dv)))
+    rc = _load().gdn_oracle_backward(
+        _ptr(q), _ptr(k), _ptr(v), dt, _ptr(alpha), _ptr(beta), _ptr(s0),
+        _ptr(row0), _ptr(lens), 1, nseq, H, dk, dv, h_lo, h_hi, _ptr(dy), _ptr(ds_final),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+        _ptr(out["dbeta"]), _ptr(out["ds0"]), int(threads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_backward failed with code %d" % rc)
+    return out
+
+
+def chain_backward_c(q, k, v, alpha, beta, s0, dy, ds_final):
+    """One chain through the C backward (same signature as :func:`chain_backward_numpy`)."""
+    q = np.asarray(q, dtype=np.float64)[:, None, :]
+    k = np.asarray(k, dtype=np.float64)[:, None, :]
+    v = np.asarray(v, dtype=np.float64)[:, None, :]
+    T = q.shape[0]
+    a = np.asarray(alpha, dtype=np.float64).reshape(T, 1)
+    b = np.asarray(beta, dtype=np.float64).reshape(T, 1)
+    s = None if s0 is None else np.asarray(s0, dtype=np.float64)[None, None]
+    d = None if ds_final is None else np.asarray(ds_final, dtype=np.float64)[None, None]
+    o = prefill_backward(q, k, v, a, b, np.asarray(dy, np.float64)[:, None, :], s0=s,
+                         ds_final=d, threads=1)
+    return dict(dq=o["dq"][:, 0], dk=o["dk"][:, 0], dv=o["dv"][:, 0],
+                dalpha=o["dalpha"][:, 0], dbeta=o["dbeta"][:, 0], ds0=o["ds0"][0, 0])
+
+
+def chain_backward_numpy(q, k, v, alpha, beta, s0, dy, ds_final):
+    """One (sequence, head) chain of the derivative in numpy, fp64, token by token.
+
+    q, k: [T, d_k]; v, dy: [T, d_v]; alpha, beta: [T]; s0, ds_final: [d_k, d_v] or None.
+    Returns dict(dq, dk, dv, dalpha, dbeta, ds0) for L = <dy, y> + <ds_final, S_T>.  The
+    forward states are kept whole (tiny cases only); each line of the recurrence is then
+    taken backwards as in gdn_oracle_backward.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = [np.zeros((dk, dv)) if s0 is None else np.array(s0, dtype=np.float64)]
+    for t in range(T):
+        St = float(alpha[t]) * S[-1]
+        e = v[t] - St.T @ k[t]
+        S.append(St + float(beta[t]) * np.outer(k[t], e))
+    D = np.zeros((dk, dv)) if ds_final is None else np.array(ds_final, dtype=np.float64)
+    out = dict(dq=np.zeros((T, dk)), dk=np.zeros((T, dk)), dv=np.zeros((T, dv)),
+               dalpha=np.zeros(T), dbeta=np.zeros(T))
+    for t in range(T - 1, -1, -1):
+        a, b = float(alpha[t]), float(beta[t])
+        D = D + np.outer(q[t], dy[t])                  # y_t = S_t^T q_t
+        out["dq"][t] = S[t + 1] @ dy[t]
+        St = a * S[t]                                  # S~ = alpha_t S_{t-1}
+        e = v[t] - St.T @ k[t]                         # e = v_t - S~^T k_t
+        de = b * (D.T @ k[t])                          # S_t = S~ + beta_t k_t e^T
+        out["dbeta"][t] = k[t] @ D @ e
+        out["dv"][t] = de
+        out["dk"][t] = b * (D @ e) - St @ de
+        dSt = D - np.outer(k[t], de)
+        out["dalpha"][t] = np.sum(dSt * S[t])
+        D = a * dSt
+    out["ds0"] = D
+    return out
