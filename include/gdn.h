@@ -130,6 +130,41 @@ gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_
                             int32_t *segment_chunks);
 
 /*
+ * Chunked backward (training) of gdn_prefill.
+ *
+ * For the scalar L = sum <dy, y> + sum <d_final_state, S_T> of the prefill with the same
+ * arguments, writes its derivatives with respect to q, k, v, alpha, beta and the initial
+ * state.  The derivative is that of the recurrence of the reading notes (Gated DeltaNet,
+ * section 2.1), taken through the chunked WY / UT form: the forward states at every chunk
+ * start and the state adjoints at every chunk end are kept in the workspace, then each chunk
+ * is differentiated on its own.
+ *
+ *   q, k, v, alpha, beta, initial_state, cu_seqlens, num_seqs, total_T, H, d_k, d_v:
+ *                  as for gdn_prefill (initial_state NULL = zeros)
+ *   dtype          GDN_DTYPE_BF16 only (GDN_ERR_UNSUPPORTED otherwise)
+ *   dy             [total_T, H, d_v] bf16, the adjoint of y
+ *   d_final_state  [N, H, d_k, d_v] fp32, the adjoint of the final state, or NULL (zero)
+ *   dq, dk         [total_T, H, d_k] bf16 (written)
+ *   dv             [total_T, H, d_v] bf16 (written)
+ *   dalpha, dbeta  [total_T, H] fp32 (written); dalpha is zero where alpha < e^-87 (the
+ *                  floor of log alpha)
+ *   d_initial_state [N, H, d_k, d_v] fp32 (written) or NULL
+ *   workspace      gdn_prefill_backward_workspace_bytes(...) bytes, 16-byte aligned
+ * Outputs may overlap neither the inputs nor each other.  Pointers as for gdn_prefill (16-
+ * byte alignment for tensors, 4 for gates and cu_seqlens).  Invalid arguments are rejected
+ * before anything is launched.
+ */
+size_t gdn_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H,
+                                            int32_t d_k, int32_t d_v, int32_t dtype);
+gdn_status gdn_prefill_backward(const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, const float *initial_state,
+                                const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_T,
+                                int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                                const void *dy, const float *d_final_state, void *dq, void *dk,
+                                void *dv, float *dalpha, float *dbeta, float *d_initial_state,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for a batch of B sequences (one token each), state updated in place:
  *
  *   q, k   [B, H, d_k] dtype;  v [B, H, d_v] dtype;  alpha, beta [B, H] fp32  (read only)

@@ -182,6 +182,86 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                           stream, 0, 0);
 }
 
+size_t gdn_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H,
+                                            int32_t d_k, int32_t d_v, int32_t dtype)
+{
+    if (num_seqs <= 0 || check_common(total_T, H, d_k, d_v, dtype) != GDN_OK) return 0;
+    if (dtype != GDN_DTYPE_BF16) return 0;
+    return gdn::backward_workspace_bytes(num_seqs, total_T, H, d_k, d_v);
+}
+
+gdn_status gdn_prefill_backward(const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, const float *initial_state,
+                                const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_T,
+                                int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                                const void *dy, const float *d_final_state, void *dq, void *dk,
+                                void *dv, float *dalpha, float *dbeta, float *d_initial_state,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    gdn_status st = check_common(total_T, H, d_k, d_v, dtype);
+    if (st != GDN_OK) return st;
+    if (dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (num_seqs <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (!cu_seqlens && total_T % num_seqs != 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (total_T > 0 && (!q || !k || !v || !alpha || !beta || !dy || !dq || !dk || !dv ||
+                        !dalpha || !dbeta))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const void *quads[] = {q, k, v, dy, dq, dk, dv, initial_state, d_final_state,
+                           d_initial_state, workspace};
+    for (const void *p : quads)
+        if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARGUMENT;
+    const void *words[] = {alpha, beta, dalpha, dbeta, cu_seqlens};
+    for (const void *p : words)
+        if (p && !aligned(p, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    const size_t need = gdn::backward_workspace_bytes(num_seqs, total_T, H, d_k, d_v);
+    if (workspace_bytes < need || !workspace) return GDN_ERR_WORKSPACE_TOO_SMALL;
+
+    // outputs overlap neither the inputs nor each other
+    const size_t rows = (size_t)total_T;
+    const size_t n_qk = rows * H * d_k * 2, n_v = rows * H * d_v * 2, n_g = rows * H * 4;
+    const size_t n_s = (size_t)num_seqs * H * d_k * d_v * 4;
+    const size_t n_cu = cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0;
+    struct Span { const void *p; size_t n; };
+    const Span inputs[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_g}, {beta, n_g},
+                           {dy, n_v}, {cu_seqlens, n_cu},
+                           {initial_state, initial_state ? n_s : 0},
+                           {d_final_state, d_final_state ? n_s : 0}};
+    const Span outs[] = {{dq, n_qk}, {dk, n_qk}, {dv, n_v}, {dalpha, n_g}, {dbeta, n_g},
+                         {d_initial_state, d_initial_state ? n_s : 0}, {workspace, need}};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Span &in : inputs)
+            if (overlap(outs[i].p, outs[i].n, in.p, in.n)) return GDN_ERR_INVALID_ARGUMENT;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return GDN_ERR_INVALID_ARGUMENT;
+    }
+
+    gdn::BackwardProblem p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.dy = dy;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.s0 = initial_state;
+    p.ds_final = d_final_state;
+    p.cu = cu_seqlens;
+    p.num_seqs = num_seqs;
+    p.total_T = total_T;
+    p.H = H;
+    p.dk = d_k;
+    p.dv = d_v;
+    p.dq = dq;
+    p.dk_out = dk;
+    p.dv_out = dv;
+    p.dalpha = dalpha;
+    p.dbeta = dbeta;
+    p.ds0 = d_initial_state;
+    hipError_t err = gdn::launch_backward(p, workspace, (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
                            const float *beta, float *state, void *y, int32_t B, int32_t H,
                            int32_t d_k, int32_t d_v, int32_t dtype, void *stream)

@@ -44,6 +44,22 @@ bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype
 hipError_t launch_prefill(const PrefillProblem &p, const PrefillPlan &plan, void *workspace,
                           hipStream_t stream);
 
+// Problem description of the chunked backward (bf16 activations).
+struct BackwardProblem {
+    const void *q, *k, *v, *dy;
+    const float *alpha, *beta;
+    const float *s0, *ds_final;  // [N, H, dk, dv] or null (zeros)
+    const int32_t *cu;
+    int num_seqs;
+    long long total_T;
+    int H, dk, dv;
+    void *dq, *dk_out, *dv_out;
+    float *dalpha, *dbeta, *ds0;  // ds0 may be null
+};
+
+size_t backward_workspace_bytes(int num_seqs, long long total_T, int H, int dk, int dv);
+hipError_t launch_backward(const BackwardProblem &p, void *workspace, hipStream_t stream);
+
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *alpha,
                          const float *beta, float *state, void *y, int B, int H, int dk,
                          int dv, int dtype, hipStream_t stream);

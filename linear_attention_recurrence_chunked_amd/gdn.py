@@ -62,6 +62,11 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill.argtypes = pre
     lib.gdn_prefill_ex.restype = i32
     lib.gdn_prefill_ex.argtypes = pre + [i32, i32]
+    lib.gdn_prefill_backward_workspace_bytes.restype = sz
+    lib.gdn_prefill_backward_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.gdn_prefill_backward.restype = i32
+    lib.gdn_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                         i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_decode_step.restype = i32
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.gdn_short_conv.restype = i32
@@ -155,6 +160,52 @@ def gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, num_s
                                _stream(stream), dv_tile, segment_chunks)
     _check("gdn_prefill", st)
     return y, final_state
+
+
+def gdn_prefill_backward_workspace_bytes(num_seqs: int, total_T: int, H: int, d_k: int,
+                                         d_v: int, dtype: int = GDN_DTYPE_BF16) -> int:
+    return int(load().gdn_prefill_backward_workspace_bytes(num_seqs, total_T, H, d_k, d_v,
+                                                           dtype))
+
+
+def gdn_prefill_backward(q, k, v, alpha, beta, dy, initial_state=None, d_final_state=None,
+                         cu_seqlens=None, num_seqs=None, workspace=None, stream=None,
+                         want_d_initial_state: bool = True, out=None):
+    """Backward of :func:`gdn_prefill` for L = <dy, y> + <d_final_state, S_T> (bf16).
+    Returns (dq, dk, dv, dalpha, dbeta, d_initial_state); ``out`` may supply that tuple of
+    preallocated tensors (d_initial_state may be None)."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        n = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != n:
+            raise ValueError("num_seqs does not match cu_seqlens")
+        num_seqs = n
+    elif num_seqs is None:
+        num_seqs = 1
+    if out is None:
+        dev = q.device
+        out = (torch.empty((T, H, dk), dtype=q.dtype, device=dev),
+               torch.empty((T, H, dk), dtype=q.dtype, device=dev),
+               torch.empty((T, H, dv), dtype=q.dtype, device=dev),
+               torch.empty((T, H), dtype=torch.float32, device=dev),
+               torch.empty((T, H), dtype=torch.float32, device=dev),
+               torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+               if want_d_initial_state else None)
+    gq, gk, gv, ga, gb, gs = out
+    need = gdn_prefill_backward_workspace_bytes(num_seqs, T, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = load().gdn_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(cu_seqlens), num_seqs, T, H, dk, dv, dt, _ptr(dy), _ptr(d_final_state),
+        _ptr(gq), _ptr(gk), _ptr(gv), _ptr(ga), _ptr(gb), _ptr(gs), _ptr(workspace), wbytes,
+        _stream(stream))
+    _check("gdn_prefill_backward", st)
+    return gq, gk, gv, ga, gb, gs
 
 
 def gdn_decode_step(q, k, v, alpha, beta, state, y=None, stream=None):

@@ -15,7 +15,9 @@ Recipe (shared by every workload):
 * v ~ N(0, 1), rounded the same way;
 * alpha = sigmoid(N(mu_a, sd_a)) and beta = sigmoid(N(mu_b, sd_b)) in fp64, stored fp32;
 * optional initial state S0 ~ N(0, sd_s0) fp32 per (sequence, head);
-* variable lengths are integers uniform in [lo, hi], both ends included.
+* variable lengths are integers uniform in [lo, hi], both ends included;
+* for the backward: the output adjoint dy ~ N(0, 1) in the storage dtype, and an optional
+  final-state adjoint ~ N(0, sd) fp32 per (sequence, head).
 
 bf16 tensors are handled as ``uint16`` bit patterns on the numpy side and viewed as
 ``torch.bfloat16`` when moved to the GPU.
@@ -30,7 +32,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 BLOCK_ROWS = 65536
-T_Q, T_K, T_V, T_ALPHA, T_BETA, T_S0, T_LENS = range(7)
+T_Q, T_K, T_V, T_ALPHA, T_BETA, T_S0, T_LENS, T_DY, T_DSF = range(9)
 
 
 @dataclass(frozen=True)
@@ -137,10 +139,10 @@ def draw_qk(rows: int, H: int, d: int, dtype: str, seed: int, tid: int) -> np.nd
     return out
 
 
-def draw_v(rows: int, H: int, d: int, dtype: str, seed: int) -> np.ndarray:
+def draw_v(rows: int, H: int, d: int, dtype: str, seed: int, tid: int = T_V) -> np.ndarray:
     out = np.empty((rows, H, d), dtype=np.uint16 if dtype == "bf16" else
                    (np.float32 if dtype == "f32" else np.float64))
-    _fill(out, seed, T_V, lambda rng, n: _store(rng.standard_normal((n, H, d)), dtype))
+    _fill(out, seed, tid, lambda rng, n: _store(rng.standard_normal((n, H, d)), dtype))
     return out
 
 
@@ -183,6 +185,19 @@ def make_inputs(lengths, H: int, dk: int, dv: int, dtype: str, alpha=(3.0, 1.0),
         cu_seqlens=cu.astype(np.int32) if varlen else None,
         lengths=lengths, num_seqs=len(lengths), H=H, dk=dk, dv=dv, dtype=dtype)
     return inp
+
+
+def backward_inputs(inp: dict, ds_sd: Optional[float] = 0.02, seed: int = 0) -> dict:
+    """Adjoints for the backward of the prefill ``inp``: dy [rows, H, dv] in inp's dtype and
+    d_final_state [N, H, dk, dv] fp32 (None when ``ds_sd`` is None)."""
+    rows = int(inp["q"].shape[0])
+    dy = draw_v(rows, inp["H"], inp["dv"], inp["dtype"], seed, T_DY)
+    dsf = None
+    if ds_sd is not None:
+        rng = np.random.default_rng([seed, T_DSF, 0])
+        dsf = (ds_sd * rng.standard_normal((inp["num_seqs"], inp["H"], inp["dk"],
+                                            inp["dv"]))).astype(np.float32)
+    return dict(dy=dy, ds_final=dsf)
 
 
 def workload_inputs(w: Workload) -> dict:

@@ -230,3 +230,51 @@ def test_output_gate_rejects(lib, kw, code):
 def test_layer_steps_empty_is_a_no_op(lib):
     assert gates(lib, T=0) == gdn.GDN_OK
     assert output_gate(lib, rows=0) == gdn.GDN_OK
+
+
+# ---- backward -------------------------------------------------------------------------------
+
+def backward(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, s0=None, cu=None, N=2,
+             T=256, H=2, dk=128, dv=128, dt=1, dy=6 * G, dsf=None, dq=7 * G, dkk=8 * G,
+             dvv=9 * G, da=10 * G, db=11 * G, ds0=12 * G, ws=13 * G, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.gdn_prefill_backward(
+        a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["cu"], a["N"], a["T"],
+        a["H"], a["dk"], a["dv"], a["dt"], a["dy"], a["dsf"], a["dq"], a["dkk"], a["dvv"],
+        a["da"], a["db"], a["ds0"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_backward_workspace_query(lib):
+    # records (T', P, g: 33,024 bytes) plus the kept states and adjoints per chunk slot
+    slots = 4 * 4096 // 64 + 4
+    rec = slots * 16 * (2 * 64 * 64 + 64) * 4
+    st = slots * 16 * 128 * 128 * 4
+    assert gdn.gdn_prefill_backward_workspace_bytes(4, 4 * 4096, 16, 128, 128) == rec + 2 * st
+    assert gdn.gdn_prefill_backward_workspace_bytes(4, 4 * 4096, 16, 128, 128,
+                                                    gdn.GDN_DTYPE_F32) == 0
+    assert gdn.gdn_prefill_backward_workspace_bytes(0, 16, 16, 128, 128) == 0
+    assert gdn.gdn_prefill_backward_workspace_bytes(1, 16, 16, 96, 128) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), gdn.GDN_ERR_UNSUPPORTED),                # bf16 only
+    (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(N=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(T=255), gdn.GDN_ERR_INVALID_ARGUMENT),          # N equal lengths must divide T
+    (dict(dy=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(da=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(dq=7 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),   # 16-byte alignment
+    (dict(dsf=14 * G + 4), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(db=11 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(dq=1 * G), gdn.GDN_ERR_INVALID_ARGUMENT),       # dq over q
+    (dict(dvv=6 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # dv inside dy
+    (dict(ds0=7 * G), gdn.GDN_ERR_INVALID_ARGUMENT),      # dS0 over dq
+    (dict(s0=14 * G, ds0=14 * G), gdn.GDN_ERR_INVALID_ARGUMENT),  # dS0 over S0
+    (dict(ws=12 * G + 1024), gdn.GDN_ERR_INVALID_ARGUMENT),       # workspace over dS0
+    (dict(ws=None), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+    (dict(wsb=1024), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_backward_rejects(lib, kw, code):
+    assert backward(lib, **kw) == code
