@@ -33,6 +33,14 @@ def prefill_flops_per_token_head(d: int, C: int = CHUNK) -> int:
     return 2 * d * (5 * C + 3 * d)
 
 
+def backward_flops_per_token_head(d: int, C: int = CHUNK) -> int:
+    """Dense-tile FLOPs of the chunked backward per token-head, each distinct product once:
+    K K^T and Q K^T (4Cd); the forward state pass K S, T' R, K^T U (4d^2 + 2Cd); the adjoint
+    pass P^T dY, K D, T'^T dU, L^T Z, Q^T dY, K^T Z (6d^2 + 6Cd); dY U^T and E U^T (4Cd);
+    dY S^T, Z S^T, U D^T (6d^2); the four c x c by c x d products of dQ and dK (8Cd)."""
+    return 24 * C * d + 16 * d * d
+
+
 def prefill_bytes(T: int, H: int, d: int, nseq: int) -> int:
     # q, k, v, y (bf16), alpha, beta (fp32), final state (fp32)
     return T * H * (4 * d * 2 + 2 * 4) + nseq * H * d * d * 4
@@ -103,6 +111,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-layer-steps", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 counter passes: 3 prefill launches, 3 decode "
                          "steps and an elementwise kernel over 1 GiB (the calibration)")
@@ -332,6 +341,49 @@ def main():
                            "achieved_GBs": round(gb, 1), "frac_of_hbm_peak": round(gb / PEAK_HBM_GBS, 4)}
         del lx, lo, ly, lz, lout
 
+    # ------------------------------------------------------------------ backward
+    # the chunked backward of the same prefill (dy ~ N(0, 1) bf16, zero final-state
+    # adjoint), timed after a cache flush like the forward
+    backward = None
+    if not args.no_backward:
+        adj = wl.backward_inputs(inp, None, seed=2)
+        bdy = wl.to_torch(adj["dy"], dev, "bf16")
+        bout = (torch.empty((T, H, d), dtype=torch.bfloat16, device=dev),
+                torch.empty((T, H, d), dtype=torch.bfloat16, device=dev),
+                torch.empty((T, H, d), dtype=torch.bfloat16, device=dev),
+                torch.empty((T, H), dtype=torch.float32, device=dev),
+                torch.empty((T, H), dtype=torch.float32, device=dev),
+                torch.empty((nseq, H, d, d), dtype=torch.float32, device=dev))
+        bneed = gdn.gdn_prefill_backward_workspace_bytes(nseq, T, H, d, d)
+        bws = torch.empty(bneed, dtype=torch.uint8, device=dev)
+
+        def run_backward():
+            gdn.gdn_prefill_backward(q, k, v, alpha, beta, bdy, num_seqs=nseq, workspace=bws,
+                                     out=bout)
+
+        for _ in range(3):
+            run_backward()
+        times = []
+        for _ in range(10):
+            cache_flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_backward()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        bms = float(np.median(times))
+        bflops = backward_flops_per_token_head(d) * T * H
+        btf = bflops / (bms * 1e-3) / 1e12
+        backward = {"workload": w.name, "ms_median": round(bms, 4),
+                    "tokens_per_s": round(T / (bms * 1e-3), 1),
+                    "flops_per_launch": bflops, "achieved_TFLOPs": round(btf, 2),
+                    "frac_of_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                    "workspace_bytes": bneed,
+                    "kernels": "bwd_prep_kernel<128> + bwd_states_kernel<128,128> + "
+                               "bwd_dstates_kernel<128,128> + bwd_chunk_kernel<128,128>"}
+        del bws, bout, bdy
+
     # ------------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -370,6 +422,7 @@ def main():
         "roofline": roofline,
         "decode": decode,
         "layer_steps": layer,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -18,21 +18,27 @@
 //   dK = -diag(gamma) Z S^T + diag(gamma_C/gamma) U D^T + (dP (.) Gamma)^T Q
 //        + (dL (.) Gamma) K + (dL (.) Gamma)^T K,        dL = -diag(beta) strictlower(E U^T)
 //   dbeta_t = sum_j E_tj R_tj - sum_i L_ti (E U^T)_ti
-//   dg_t    = sum_i (Q (.) Gq)_ti + (K (.) GkA)_ti - (K (.) GkB)_ti
+//   dg_t    = sum_i (Q (.) Gq)_ti + (K (.) Ga)_ti - (K (.) Gb)_ti
 //             + sum_i (dP (.) P + dL (.) L)_ti - sum_s (dP (.) P + dL (.) L)_st
-//             + [t = last] (gamma_C <S, D> + sum_{s,i} (K (.) GkB)_si)
-//   with Gq = diag(gamma) dY S^T, GkA = -diag(gamma) Z S^T, GkB = diag(gamma_C/gamma) U D^T;
+//             + [t = last] (gamma_C <S, D> + sum_{s,i} (K (.) Gb)_si)
+//   with Gq = diag(gamma) dY S^T, Ga = -diag(gamma) Z S^T, Gb = diag(gamma_C/gamma) U D^T;
 //   dlog alpha_s = sum_{t >= s in the chunk} dg_t,  dalpha = dlog alpha / alpha.
 //
 // Four launches:
-//   bwd_prep_kernel     (chunk slot, head): T' and P (fp32) and g into a record.
+//   bwd_prep_kernel     (chunk slot, head): T' (forward substitution in fp32) and P, bf16,
+//                       and g into a record.
 //   bwd_states_kernel   (sequence, head, 32 state columns): the forward scan, keeping S at
 //                       the start of every chunk.
 //   bwd_dstates_kernel  (sequence, head, 32 state columns): the adjoint scan from the last
 //                       chunk to the first, keeping D at the end of every chunk; dS_0.
 //   bwd_chunk_kernel    (chunk slot, head): everything else, from the kept S and D.
-// Every product runs on 16x16x16 bf16 MFMAs with fp32 operands split into two bf16 halves
-// (hi + lo; three products per step, two when one operand is exactly bf16).
+// Products run on 16x16x32 bf16 MFMAs with fp32 accumulation, operands rounded once to bf16
+// (as in the forward), except where short sequences make the gradient a small difference of
+// large terms: U = T' R, dY U^T and the three products with S and D take their right operand
+// as bf16 hi + lo.  Tiles live in LDS in one orientation; an operand that is the
+// transpose of a stored tile is read with the transposing LDS read.  The two scans keep
+// their fp32 state in MFMA accumulators across chunks and fetch the next chunk's inputs into
+// registers while the current one is computed.
 //
 // Chunk slots are the prefill's: chunk c of sequence n (first row t0_n) has slot
 // floor(t0_n / 64) + n + c, below floor(total_T / 64) + num_seqs.
@@ -44,71 +50,109 @@ namespace {
 
 constexpr int C = kChunk;
 constexpr float kLnAlphaFloor = -87.0f;   // e^-87 is still a normal fp32
-constexpr int LDC = C + 4;                 // padded fp32 rows of a 64 x 64 matrix
-constexpr int kRecFloats = 2 * C * C + C;  // T' [64][64], P [64][64], g [64]
-constexpr int DVT = 32;                    // state columns per workgroup of the scans
-constexpr int LDT = DVT + 4;
-constexpr int DVB = 16;                    // value columns per pass of the chunk kernel
-constexpr int LDB = DVB + 4;
+constexpr int L64 = C + 8;                 // bf16 row stride of a [.][64] LDS tile
+constexpr int DVT = 32;                    // state columns per workgroup of the two scans
+constexpr int LVT = DVT + 8;               // bf16 row stride of a [.][32] LDS tile
+constexpr int DVB = 32;                    // value columns per pass of the chunk kernel
+constexpr int LF = C + 4;                  // fp32 row stride of the prep kernel's solve
+// Record of one (chunk slot, head), in bf16 units: T' [64][64], P [64][64], then the 64
+// within-chunk log-decay prefixes g as fp32.
+constexpr int kRT = 0, kRP = C * C, kRG = 2 * C * C;
+constexpr int kRecHalfs = 2 * C * C + 2 * C;
+constexpr int kThreadsScan = 512;
 
-typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ float bf(const uint16_t *p) { return bf16_to_f32(*p); }
 
-struct Split {
-    v4s hi, lo;
-};
-__device__ __forceinline__ Split split(f32x4 x)
+// Four bf16 values by the transposing LDS read: within each group of 16 lanes, lane j
+// receives element j % 4 of the 8-byte rows addressed by lanes j / 4 + 4 s, s = 0..3.
+__device__ __forceinline__ bf16x4 ldtr(const uint16_t *p)
 {
-    const bf16x4 h = __builtin_convertvector(x, bf16x4);
-    const bf16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4), bf16x4);
-    return Split{__builtin_bit_cast(v4s, h), __builtin_bit_cast(v4s, l)};
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)p);
+    return __builtin_bit_cast(bf16x4, r);
 }
 
-__device__ __forceinline__ float ldsf(const float *p) { return *p; }
-__device__ __forceinline__ float ldsf(const uint16_t *p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ f32x4 lds4(const float *p) { return *(const f32x4 *)p; }
-__device__ __forceinline__ f32x4 lds4(const uint16_t *p) { return load4(p); }
-
-// acc += opA[m0 .. m0+15][0 .. kd) * opB[0 .. kd)[n0 .. n0+15] with
-//   opA(m, k) = TA ? A[k * lda + m] : A[m * lda + k],
-//   opB(k, n) = TB ? B[n * ldb + k] : B[k * ldb + n].
-// Lane (r = lane % 16, q = lane / 16) feeds row m0 + r of opA and column n0 + r of opB with
-// contraction indices k0 + 4q .. k0 + 4q + 3; the accumulator holds rows m0 + 4q + i,
-// column n0 + r.  XA / XB: the operand holds bf16 values exactly (its low half is zero).
-template <bool TA, bool TB, bool XA, bool XB, typename EA, typename EB>
-__device__ __forceinline__ void mm(f32x4 &acc, const EA *A, int lda, const EB *B, int ldb,
-                                   int m0, int n0, int kd)
+// MFMA operand fragments (16x16x32): lane (r = lane % 16, g = lane / 16) supplies the eight
+// contraction indices k0 + 8 g .. k0 + 8 g + 7 of row m0 + r of the operand.
+//   frag_r: the operand is stored row major, [m][ld] with k contiguous (one 16-byte read);
+//   frag_c: the operand is the transpose of a stored [k][ld] tile (two transposing reads).
+__device__ __forceinline__ bf16x8 frag_r(const uint16_t *X, int ld, int m0, int k0)
 {
-    const int lane = threadIdx.x & 63, r = lane & 15, q4 = (lane >> 4) * 4;
-    for (int k0 = 0; k0 < kd; k0 += 16) {
-        f32x4 a, b;
-        if constexpr (!TA) {
-            a = lds4(A + (m0 + r) * lda + k0 + q4);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = ldsf(A + (k0 + q4 + i) * lda + m0 + r);
-        }
-        if constexpr (TB) {
-            b = lds4(B + (n0 + r) * ldb + k0 + q4);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) b[i] = ldsf(B + (k0 + q4 + i) * ldb + n0 + r);
-        }
-        const Split sa = split(a), sb = split(b);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa.hi, sb.hi, acc, 0, 0, 0);
-        if constexpr (!XA) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa.lo, sb.hi, acc, 0, 0, 0);
-        if constexpr (!XB) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa.hi, sb.lo, acc, 0, 0, 0);
+    const int lane = threadIdx.x & 63;
+    return *(const bf16x8 *)(X + (m0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+__device__ __forceinline__ bf16x8 frag_c(const uint16_t *X, int ld, int m0, int k0)
+{
+    const int lane = threadIdx.x & 63, l = lane & 15;
+    const uint16_t *p = X + (k0 + 8 * (lane >> 4) + (l >> 2)) * ld + m0 + 4 * (l & 3);
+    const bf16x4 lo = ldtr(p), hi = ldtr(p + 4 * ld);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// acc += opA[m0 .. m0+15][0 .. kd) opB[0 .. kd)[n0 .. n0+15].
+//   AT = false: A stored [m][k];  AT = true: A stored [k][m] (opA is its transpose).
+//   BT = true:  B stored [n][k];  BT = false: B stored [k][n].
+// The accumulator holds rows m0 + 4 (lane / 16) + i, column n0 + lane % 16.
+template <bool AT, bool BT>
+__device__ __forceinline__ void mm(f32x4 &acc, const uint16_t *A, int lda, const uint16_t *B,
+                                   int ldb, int m0, int n0, int kd)
+{
+    for (int k0 = 0; k0 < kd; k0 += 32) {
+        const bf16x8 a = AT ? frag_c(A, lda, m0, k0) : frag_r(A, lda, m0, k0);
+        const bf16x8 b = BT ? frag_r(B, ldb, n0, k0) : frag_c(B, ldb, n0, k0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
 }
 
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// The same with the B operand held as two bf16 tiles, hi + lo (an fp32 value to about 16
+// significant bits): two products per step.
+template <bool AT, bool BT>
+__device__ __forceinline__ void mm2(f32x4 &acc, const uint16_t *A, int lda, const uint16_t *Bh,
+                                    const uint16_t *Bl, int ldb, int m0, int n0, int kd)
+{
+    for (int k0 = 0; k0 < kd; k0 += 32) {
+        const bf16x8 a = AT ? frag_c(A, lda, m0, k0) : frag_r(A, lda, m0, k0);
+        const bf16x8 bh = BT ? frag_r(Bh, ldb, n0, k0) : frag_c(Bh, ldb, n0, k0);
+        const bf16x8 bl = BT ? frag_r(Bl, ldb, n0, k0) : frag_c(Bl, ldb, n0, k0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+    }
+}
 
-// Sum over the 16 lanes that share lane / 16.
+// An accumulator tile (rows m0 + 4 g + i, column n0 + r) stored transposed into a bf16
+// [n][ld] tile: one 8-byte store per lane.  put_t2 also stores the rounding remainder.
+__device__ __forceinline__ void put_t(uint16_t *D, int ld, int m0, int n0, f32x4 v)
+{
+    const int lane = threadIdx.x & 63;
+    *(bf16x4 *)(D + (n0 + (lane & 15)) * ld + m0 + 4 * (lane >> 4)) =
+        __builtin_convertvector(v, bf16x4);
+}
+__device__ __forceinline__ void put_t2(uint16_t *Dh, uint16_t *Dl, int ld, int m0, int n0,
+                                       f32x4 v)
+{
+    const int lane = threadIdx.x & 63;
+    const int o = (n0 + (lane & 15)) * ld + m0 + 4 * (lane >> 4);
+    const bf16x4 h = __builtin_convertvector(v, bf16x4);
+    *(bf16x4 *)(Dh + o) = h;
+    *(bf16x4 *)(Dl + o) = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bf16x4);
+}
+
+// Sum over the 16 lanes that share lane / 16, and over the whole wave.
 __device__ __forceinline__ float sum16(float x)
 {
     x += __shfl_xor(x, 1, kWave);
     x += __shfl_xor(x, 2, kWave);
     x += __shfl_xor(x, 4, kWave);
     x += __shfl_xor(x, 8, kWave);
+    return x;
+}
+__device__ __forceinline__ float sum64(float x)
+{
+    x = sum16(x);
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
     return x;
 }
 
@@ -122,7 +166,7 @@ struct BwdArgs {
     int H;
     uint16_t *dq, *dk, *dv;
     float *dalpha, *dbeta, *ds0;
-    float *rec;        // [nslots, H, kRecFloats]
+    uint16_t *rec;     // [nslots, H, kRecHalfs]
     float *hs;         // [nslots, H, DK, DV]  state at the start of each chunk
     float *dhs;        // [nslots, H, DK, DV]  adjoint of the state at the end of each chunk
     long long nslots;
@@ -161,89 +205,36 @@ __device__ __forceinline__ bool decode_slot(const BwdArgs &a, long long slot, in
     return true;
 }
 
-// Rows [t0, t0 + nv) of a [rows, H, W] bf16 tensor (head h) into LDS as bf16 [64][ld], rows
-// nv .. 63 zero.  16-byte pieces, all threads.
-template <int W>
-__device__ __forceinline__ void load_rows_bf16(uint16_t *dst, int ld, const uint16_t *src,
-                                               long long t0, int nv, int H, int h)
-{
-    constexpr int P = W / 8;
-    for (int i = threadIdx.x; i < C * P; i += blockDim.x) {
-        const int t = i / P, p = i % P;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (t < nv) x = *(const u32x4 *)(src + ((t0 + t) * H + h) * (long long)W + 8 * p);
-        *(u32x2 *)(dst + t * ld + 8 * p) = u32x2{x[0], x[1]};
-        *(u32x2 *)(dst + t * ld + 8 * p + 4) = u32x2{x[2], x[3]};
-    }
-}
-
-// Columns [col0, col0 + NC) of rows [t0, t0 + nv) of a [rows, H, W] bf16 tensor into LDS as
-// fp32 [64][ld]; rows nv .. 63 zero.
+// Piece i (16 bytes: row i / (NC / 8), columns col0 + 8 (i % (NC / 8)) ..) of the rows
+// [t0, t0 + nv) of a [rows, H, W] bf16 tensor, head h; zero beyond nv.
 template <int W, int NC>
-__device__ __forceinline__ void load_cols_f32(float *dst, int ld, const uint16_t *src,
-                                              long long t0, int nv, int H, int h, int col0)
+__device__ __forceinline__ u32x4 piece(const uint16_t *src, long long t0, int nv, int H, int h,
+                                       int col0, int i)
 {
-    constexpr int P = NC / 4;
-    for (int i = threadIdx.x; i < C * P; i += blockDim.x) {
-        const int t = i / P, p = i % P;
-        f32x4 x = zero4();
-        if (t < nv) x = load4(src + ((t0 + t) * H + h) * (long long)W + col0 + 4 * p);
-        *(f32x4 *)(dst + t * ld + 4 * p) = x;
-    }
+    constexpr int P = NC / 8;
+    const int t = i / P, p = i % P;
+    if (t >= nv) return u32x4{0u, 0u, 0u, 0u};
+    return *(const u32x4 *)(src + ((t0 + t) * H + h) * (long long)W + col0 + 8 * p);
+}
+template <int NC>
+__device__ __forceinline__ void put_piece(uint16_t *dst, int ld, int i, u32x4 x)
+{
+    constexpr int P = NC / 8;
+    *(u32x4 *)(dst + (i / P) * ld + 8 * (i % P)) = x;
 }
 
-// A [64][64] fp32 block of global memory (row stride 64) into LDS [64][LDC].
-__device__ __forceinline__ void load_mat64(float *dst, const float *src)
+// Eight bf16 (one piece) times a scalar, rounded back to bf16.
+__device__ __forceinline__ u32x4 scale_piece(u32x4 x, float s)
 {
-    for (int i = threadIdx.x; i < C * C / 4; i += blockDim.x) {
-        const int t = i / (C / 4), p = i % (C / 4);
-        *(f32x4 *)(dst + t * LDC + 4 * p) = *(const f32x4 *)(src + t * C + 4 * p);
-    }
-}
-
-// Rows x cols fp32 sub-block (cols a multiple of 4) between global (row stride gs) and LDS.
-__device__ __forceinline__ void load_blk(float *dst, int ld, const float *src, long long gs,
-                                         int rows, int cols)
-{
-    const int P = cols / 4;
-    for (int i = threadIdx.x; i < rows * P; i += blockDim.x) {
-        const int r = i / P, p = i % P;
-        *(f32x4 *)(dst + r * ld + 4 * p) = *(const f32x4 *)(src + r * gs + 4 * p);
-    }
-}
-__device__ __forceinline__ void store_blk(float *dst, long long gs, const float *src, int ld,
-                                          int rows, int cols)
-{
-    const int P = cols / 4;
-    for (int i = threadIdx.x; i < rows * P; i += blockDim.x) {
-        const int r = i / P, p = i % P;
-        *(f32x4 *)(dst + r * gs + 4 * p) = *(const f32x4 *)(src + r * ld + 4 * p);
-    }
-}
-
-// g (within-chunk prefix of the floored log alpha; 0 beyond nv), gamma = e^g and
-// rat = e^{g_last - g} into LDS, by the first wave.  g_last is g[63]: tokens beyond nv add 0.
-__device__ __forceinline__ void gate_prefix(float *g, float *gam, float *rat, float *bet,
-                                            const float *alpha, const float *beta,
-                                            long long t0, int nv, int H, int h)
-{
-    if (threadIdx.x >= kWave) return;
-    const int t = threadIdx.x;
-    float la = 0.f, b = 0.f;
-    if (t < nv) {
-        la = fmaxf(__logf(alpha[(t0 + t) * H + h]), kLnAlphaFloor);
-        b = beta[(t0 + t) * H + h];
-    }
+    u32x4 o;
 #pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) {
-        const float o = __shfl_up(la, s, kWave);
-        if (t >= s) la += o;
+    for (int w = 0; w < 4; ++w) {
+        const float lo = __uint_as_float(x[w] << 16) * s;
+        const float hi = __uint_as_float(x[w] & 0xffff0000u) * s;
+        const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+        o[w] = __builtin_bit_cast(uint32_t, b);
     }
-    const float last = __shfl(la, kWave - 1, kWave);
-    g[t] = la;
-    gam[t] = __expf(la);
-    rat[t] = __expf(last - la);
-    if (bet) bet[t] = b;
+    return o;
 }
 
 // Gamma_ti = e^{g_t - g_i} for i <= t, else 0.
@@ -252,20 +243,30 @@ __device__ __forceinline__ float decay(const float *g, int t, int i)
     return i <= t ? __expf(g[t] - g[i]) : 0.f;
 }
 
+// Record pieces (16 bytes of a [64][64] bf16 matrix) and their place in an LDS tile
+// [64][L64].
+__device__ __forceinline__ u32x4 rec_piece(const uint16_t *rec, int off, int i)
+{
+    return *(const u32x4 *)(rec + off + 8 * i);
+}
+__device__ __forceinline__ void put_rec_piece(uint16_t *dst, int i, u32x4 x)
+{
+    *(u32x4 *)(dst + (i >> 3) * L64 + 8 * (i & 7)) = x;
+}
+
 // ======================================================================================
 // bwd_prep_kernel: per (chunk slot, head) T' = (I + diag(beta) L)^{-1} diag(beta) by forward
-// substitution, P = lower_incl(Q K^T (.) Gamma), g.
+// substitution (fp32), P = lower_incl(Q K^T (.) Gamma), g.  Four waves.
 // ======================================================================================
 template <int DK>
 struct PrepLds {
-    static constexpr int LDK = DK + 8;
+    static constexpr int LK = DK + 8;
     static constexpr int oK = 0;
-    static constexpr int oQ = oK + C * LDK * 2;
-    static constexpr int oL = oQ + C * LDK * 2;
-    static constexpr int oG = oL + C * LDC * 4;
-    static constexpr int oGam = oG + C * 4;
-    static constexpr int oRat = oGam + C * 4;
-    static constexpr int oBet = oRat + C * 4;
+    static constexpr int oQ = oK + C * LK * 2;
+    static constexpr int oL = oQ + C * LK * 2;      // [64][LF] fp32
+    static constexpr int oT = oL + C * LF * 4;      // [64][LF] fp32
+    static constexpr int oG = oT + C * LF * 4;
+    static constexpr int oBet = oG + C * 4;
     static constexpr int total = oBet + C * 4;
 };
 
@@ -273,44 +274,61 @@ template <int DK>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 {
     using L = PrepLds<DK>;
+    constexpr int LK = L::LK;
     __shared__ __align__(16) unsigned char smem[L::total];
     uint16_t *sK = (uint16_t *)(smem + L::oK), *sQ = (uint16_t *)(smem + L::oQ);
-    float *sL = (float *)(smem + L::oL);
-    float *g = (float *)(smem + L::oG), *gam = (float *)(smem + L::oGam);
-    float *rat = (float *)(smem + L::oRat), *bet = (float *)(smem + L::oBet);
+    float *sL = (float *)(smem + L::oL), *sT = (float *)(smem + L::oT);
+    float *g = (float *)(smem + L::oG), *bet = (float *)(smem + L::oBet);
     const int H = a.H;
     const long long slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int n, c, nv;
     long long t0;
     if (!decode_slot(a, slot, n, c, t0, nv)) return;
-    float *rec = a.rec + (slot * H + h) * (long long)kRecFloats;
+    uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, q4 = (lane >> 4) * 4;
 
-    load_rows_bf16<DK>(sK, L::LDK, a.k, t0, nv, H, h);
-    load_rows_bf16<DK>(sQ, L::LDK, a.q, t0, nv, H, h);
-    gate_prefix(g, gam, rat, bet, a.alpha, a.beta, t0, nv, H, h);
+    for (int i = tid; i < C * DK / 8; i += 256) {
+        put_piece<DK>(sK, LK, i, piece<DK, DK>(a.k, t0, nv, H, h, 0, i));
+        put_piece<DK>(sQ, LK, i, piece<DK, DK>(a.q, t0, nv, H, h, 0, i));
+    }
+    if (tid < C) {
+        float la = 0.f, b = 0.f;
+        if (tid < nv) {
+            la = fmaxf(__logf(a.alpha[(t0 + tid) * H + h]), kLnAlphaFloor);
+            b = a.beta[(t0 + tid) * H + h];
+        }
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const float o = __shfl_up(la, s, kWave);
+            if (tid >= s) la += o;
+        }
+        g[tid] = la;
+        bet[tid] = b;
+        ((float *)(rec + kRG))[tid] = la;
+    }
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, q4 = (lane >> 4) * 4;
-    // L (to LDS) and P (to the record): 16 tiles each, four per wave
+    // L (fp32, for the solve) and P (bf16, to the record): 16 tiles each, four per wave
     for (int tile = wave; tile < 16; tile += 4) {
         const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
         f32x4 kk = zero4(), qk = zero4();
-        mm<false, true, true, true>(kk, sK, L::LDK, sK, L::LDK, m0, n0, DK);
-        mm<false, true, true, true>(qk, sQ, L::LDK, sK, L::LDK, m0, n0, DK);
+        mm<false, true>(kk, sK, LK, sK, LK, m0, n0, DK);
+        mm<false, true>(qk, sQ, LK, sK, LK, m0, n0, DK);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = m0 + q4 + i, s = n0 + r;
             const float G = decay(g, t, s);
-            sL[t * LDC + s] = s < t ? kk[i] * G : 0.f;
-            rec[C * C + t * C + s] = qk[i] * G;
+            sL[t * LF + s] = s < t ? kk[i] * G : 0.f;
+            rec[kRP + t * C + s] = __builtin_bit_cast(uint16_t, (__bf16)(qk[i] * G));
         }
     }
     __syncthreads();
 
-    // forward substitution, one column per lane group: wave w owns columns 16w .. 16w+15;
-    // lane (j = 16w + r, p = lane / 16) keeps rows i = 4m + p of its column in registers.
+    // forward substitution, T'[t] = beta_t (e_t - sum_{i<t} L[t][i] T'[i]): wave w owns
+    // columns 16w .. 16w+15; lane (j = 16w + r, p = lane / 16) keeps rows 4m + p of its
+    // column in registers.
     const int j = 16 * wave + r, p = lane >> 4;
     float col[16];
 #pragma unroll
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
         for (int m = 0; m < 16; ++m) {
             if (4 * m < t) {
                 const int i = 4 * m + p;
-                if (i < t) s += sL[t * LDC + i] * col[m];
+                if (i < t) s += sL[t * LF + i] * col[m];
             }
         }
         s += __shfl_xor(s, 16, kWave);
@@ -330,264 +348,402 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
         const float val = bet[t] * ((t == j ? 1.f : 0.f) - s);
         if (p == (t & 3)) {
             col[t >> 2] = val;
-            rec[t * C + j] = val;
+            sT[t * LF + j] = val;
         }
     }
-    if (threadIdx.x < C) rec[2 * C * C + threadIdx.x] = g[threadIdx.x];
+    __syncthreads();
+    // T' to the record in 16-byte pieces
+    for (int i = tid; i < C * C / 8; i += 256) {
+        const int t = i >> 3, c8 = 8 * (i & 7);
+        const f32x4 lo = *(const f32x4 *)(sT + t * LF + c8);
+        const f32x4 hi = *(const f32x4 *)(sT + t * LF + c8 + 4);
+        const bf16x4 bl = __builtin_convertvector(lo, bf16x4);
+        const bf16x4 bh = __builtin_convertvector(hi, bf16x4);
+        *(bf16x8 *)(rec + kRT + t * C + c8) =
+            bf16x8{bl[0], bl[1], bl[2], bl[3], bh[0], bh[1], bh[2], bh[3]};
+    }
 }
 
 // ======================================================================================
 // bwd_states_kernel: S at the start of every chunk of (sequence, head), 32 columns.
+// Eight waves; wave w keeps state tiles w, w + 8, ... (16 x 16, row block id / 2, column
+// block id % 2) in fp32 accumulators.  Per chunk:
+//   X = V - diag(gamma) K S;  U = T' X;  S = gamma_C S + K^T diag(gamma_C / gamma) U
 // ======================================================================================
 template <int DK>
-struct ScanLds {
-    static constexpr int LDK = DK + 8;
-    static constexpr int oS = 0;                              // [DK][LDT] fp32
-    static constexpr int oK = oS + DK * LDT * 4;              // [64][LDK] bf16
-    static constexpr int oQ = oK + C * LDK * 2;               // [64][LDK] bf16 (adjoint scan)
-    static constexpr int oT = oQ + C * LDK * 2;               // [64][LDC] fp32
-    static constexpr int oP = oT + C * LDC * 4;               // [64][LDC] fp32 (adjoint scan)
-    static constexpr int oA = oP + C * LDC * 4;               // [64][LDT] fp32 (V or dY)
-    static constexpr int oB = oA + C * LDT * 4;               // [64][LDT] fp32
-    static constexpr int oX = oB + C * LDT * 4;               // [64][LDT] fp32
-    static constexpr int oG = oX + C * LDT * 4;
-    static constexpr int oGam = oG + C * 4;
+struct StLds {
+    static constexpr int LK = DK + 8;
+    static constexpr int oK = 0;                         // [64][LK]   K
+    static constexpr int oT = oK + C * LK * 2;           // [64][L64]  T'
+    static constexpr int oV = oT + C * L64 * 2;          // [64][LVT]  V columns
+    static constexpr int oSt = oV + C * LVT * 2;         // [DVT][LK]  S^T (bf16)
+    static constexpr int oXt = oSt + DVT * LK * 2;       // [DVT][L64] X^T
+    static constexpr int oUt = oXt + DVT * L64 * 2;      // [DVT][L64] (diag(rho) U)^T
+    static constexpr int oGam = oUt + DVT * L64 * 2;
     static constexpr int oRat = oGam + C * 4;
     static constexpr int total = oRat + C * 4;
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs a)
+__global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
 {
-    using L = ScanLds<DK>;
-    constexpr int NT = DV / DVT;
+    using L = StLds<DK>;
+    constexpr int LK = L::LK, NT = DV / DVT;
+    constexpr int KP = C * DK / 8;                     // 16-byte pieces of K
+    constexpr int KPT = (KP + kThreadsScan - 1) / kThreadsScan;
+    constexpr int VP = C * DVT / 8;                    // pieces of the V columns
+    constexpr int SPW = DK / 64;                       // state tiles per wave
     __shared__ __align__(16) unsigned char smem[L::total];
-    float *sS = (float *)(smem + L::oS);
-    uint16_t *sK = (uint16_t *)(smem + L::oK);
-    float *sT = (float *)(smem + L::oT), *sV = (float *)(smem + L::oA);
-    float *sU = (float *)(smem + L::oB), *sX = (float *)(smem + L::oX);
-    float *g = (float *)(smem + L::oG), *gam = (float *)(smem + L::oGam);
-    float *rat = (float *)(smem + L::oRat);
+    uint16_t *sK = (uint16_t *)(smem + L::oK), *sT = (uint16_t *)(smem + L::oT);
+    uint16_t *sV = (uint16_t *)(smem + L::oV), *sSt = (uint16_t *)(smem + L::oSt);
+    uint16_t *sXt = (uint16_t *)(smem + L::oXt), *sUt = (uint16_t *)(smem + L::oUt);
+    float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
     const int H = a.H;
     const int tile = blockIdx.x % NT;
     const int h = (blockIdx.x / NT) % H;
     const int n = blockIdx.x / (NT * H);
     const int col0 = tile * DVT;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
-
-    if (a.s0) load_blk(sS, LDT, a.s0 + ((long long)n * H + h) * DK * DV + col0, DV, DK, DVT);
-    else
-        for (int i = threadIdx.x; i < DK * LDT; i += blockDim.x) sS[i] = 0.f;
     const long long r0 = row0_of(a, n);
     const int len = len_of(a, n);
     const int nch = (len + C - 1) / C;
-    for (int c = 0; c < nch; ++c) {
+
+    f32x4 S[SPW];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int id = wave + 8 * k, mi = id >> 1, nt = id & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[k][i] = a.s0 ? a.s0[(((long long)n * H + h) * DK + 16 * mi + q4 + i) * DV + col0 +
+                                  16 * nt + r]
+                           : 0.f;
+        put_t(sSt, LK, 16 * mi, 16 * nt, S[k]);
+    }
+
+    u32x4 pk[KPT], pt, pv;
+    float pg = 0.f, pgl = 0.f;
+    auto fetch = [&](int c) {
         const long long slot = slot_of(a, n, c);
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
-        const float *rec = a.rec + (slot * H + h) * (long long)kRecFloats;
-        load_rows_bf16<DK>(sK, L::LDK, a.k, t0, nv, H, h);
-        load_cols_f32<DV, DVT>(sV, LDT, a.v, t0, nv, H, h, col0);
-        load_mat64(sT, rec);
-        if (threadIdx.x < C) {
-            const float gt = rec[2 * C * C + threadIdx.x], gl = rec[2 * C * C + C - 1];
-            g[threadIdx.x] = gt;
-            gam[threadIdx.x] = __expf(gt);
-            rat[threadIdx.x] = __expf(gl - gt);
+        const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = tid + kThreadsScan * j;
+            if (i < KP) pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
         }
-        __syncthreads();
-        store_blk(a.hs + ((slot * H + h) * DK) * (long long)DV + col0, DV, sS, LDT, DK, DVT);
-        // X = V - diag(gamma) K S   (4 x 2 tiles)
-        for (int tl = wave; tl < 8; tl += 4) {
-            const int m0 = 16 * (tl >> 1), n0 = 16 * (tl & 1);
+        pt = rec_piece(rec, kRT, tid);
+        if (tid < VP) pv = piece<DV, DVT>(a.v, t0, nv, H, h, col0, tid);
+        if (tid < C) {
+            pg = ((const float *)(rec + kRG))[tid];
+            pgl = ((const float *)(rec + kRG))[C - 1];
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = tid + kThreadsScan * j;
+            if (i < KP) put_piece<DK>(sK, LK, i, pk[j]);
+        }
+        put_rec_piece(sT, tid, pt);
+        if (tid < VP) put_piece<DVT>(sV, LVT, tid, pv);
+        if (tid < C) {
+            gam[tid] = __expf(pg);
+            rat[tid] = __expf(pgl - pg);
+        }
+    };
+
+    if (nch > 0) {
+        fetch(0);
+        commit();
+    }
+    __syncthreads();
+    const int mt = wave >> 1, nt = wave & 1;          // this wave's c x 32 tile
+    for (int c = 0; c < nch; ++c) {
+        const long long slot = slot_of(a, n, c);
+        if (c + 1 < nch) fetch(c + 1);
+        float *hs = a.hs + ((slot * H + h) * DK) * (long long)DV + col0;
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hs[(16 * mi + q4 + i) * DV + 16 * nk + r] = S[k][i];
+        }
+        // X = V - diag(gamma) K S
+        {
             f32x4 acc = zero4();
-            mm<false, false, true, false>(acc, sK, L::LDK, sS, LDT, m0, n0, DK);
+            mm<false, true>(acc, sK, LK, sSt, LK, 16 * mt, 16 * nt, DK);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = m0 + q4 + i;
-                sX[t * LDT + n0 + r] = sV[t * LDT + n0 + r] - gam[t] * acc[i];
+                const int t = 16 * mt + q4 + i;
+                acc[i] = bf(sV + t * LVT + 16 * nt + r) - gam[t] * acc[i];
             }
+            put_t(sXt, L64, 16 * mt, 16 * nt, acc);
         }
         __syncthreads();
         // U = T' X, kept as diag(gamma_C / gamma) U
-        for (int tl = wave; tl < 8; tl += 4) {
-            const int m0 = 16 * (tl >> 1), n0 = 16 * (tl & 1);
+        {
             f32x4 acc = zero4();
-            mm<false, false, false, false>(acc, sT, LDC, sX, LDT, m0, n0, C);
+            mm<false, true>(acc, sT, L64, sXt, L64, 16 * mt, 16 * nt, C);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = m0 + q4 + i;
-                sU[t * LDT + n0 + r] = rat[t] * acc[i];
-            }
+            for (int i = 0; i < 4; ++i) acc[i] *= rat[16 * mt + q4 + i];
+            put_t(sUt, L64, 16 * mt, 16 * nt, acc);
         }
         __syncthreads();
-        // S = gamma_C S + K^T (diag(gamma_C / gamma) U)   (DK/16 x 2 tiles)
+        // S = gamma_C S + K^T (diag(gamma_C / gamma) U)
         const float gC = gam[C - 1];
-        for (int tl = wave; tl < (DK / 16) * 2; tl += 4) {
-            const int m0 = 16 * (tl >> 1), n0 = 16 * (tl & 1);
-            f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gC * sS[(m0 + q4 + i) * LDT + n0 + r];
-            mm<true, false, true, false>(acc, sK, L::LDK, sU, LDT, m0, n0, C);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sS[(m0 + q4 + i) * LDT + n0 + r] = acc[i];
+        for (int k = 0; k < SPW; ++k) {
+            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
+            S[k] *= gC;
+            mm<true, true>(S[k], sK, LK, sUt, L64, 16 * mi, 16 * nk, C);
+            put_t(sSt, LK, 16 * mi, 16 * nk, S[k]);
         }
+        __syncthreads();
+        if (c + 1 < nch) commit();
         __syncthreads();
     }
 }
 
 // ======================================================================================
 // bwd_dstates_kernel: the adjoint D of the state at the end of every chunk, last chunk
-// first; dS_0 after the first chunk.
+// first; dS_0 after the first chunk.  Per chunk:
+//   X = P^T dY + diag(gamma_C / gamma) K D;  Z = T'^T X;
+//   D = gamma_C D + Q^T diag(gamma) dY - K^T diag(gamma) Z
 // ======================================================================================
+template <int DK>
+struct DsLds {
+    static constexpr int LK = DK + 8;
+    static constexpr int oK = 0;                         // [64][LK]   K
+    static constexpr int oQ = oK + C * LK * 2;           // [64][LK]   Q
+    static constexpr int oP = oQ + C * LK * 2;           // [64][L64]  P
+    static constexpr int oT = oP + C * L64 * 2;          // [64][L64]  T'
+    static constexpr int oY = oT + C * L64 * 2;          // [64][LVT]  dY columns
+    static constexpr int oYg = oY + C * LVT * 2;         // [64][LVT]  diag(gamma) dY
+    static constexpr int oDt = oYg + C * LVT * 2;        // [DVT][LK]  D^T (bf16)
+    static constexpr int oXt = oDt + DVT * LK * 2;       // [DVT][L64] X^T
+    static constexpr int oZt = oXt + DVT * L64 * 2;      // [DVT][L64] (-diag(gamma) Z)^T
+    static constexpr int oGam = oZt + DVT * L64 * 2;
+    static constexpr int oRat = oGam + C * 4;
+    static constexpr int total = oRat + C * 4;
+};
+
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_dstates_kernel(BwdArgs a)
+__global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
 {
-    using L = ScanLds<DK>;
-    constexpr int NT = DV / DVT;
+    using L = DsLds<DK>;
+    constexpr int LK = L::LK, NT = DV / DVT;
+    constexpr int KP = C * DK / 8;
+    constexpr int KPT = (KP + kThreadsScan - 1) / kThreadsScan;
+    constexpr int VP = C * DVT / 8;
+    constexpr int SPW = DK / 64;
     __shared__ __align__(16) unsigned char smem[L::total];
-    float *sD = (float *)(smem + L::oS);
     uint16_t *sK = (uint16_t *)(smem + L::oK), *sQ = (uint16_t *)(smem + L::oQ);
-    float *sT = (float *)(smem + L::oT), *sP = (float *)(smem + L::oP);
-    float *sY = (float *)(smem + L::oA), *sZ = (float *)(smem + L::oB);
-    float *sX = (float *)(smem + L::oX);
-    float *g = (float *)(smem + L::oG), *gam = (float *)(smem + L::oGam);
-    float *rat = (float *)(smem + L::oRat);
+    uint16_t *sP = (uint16_t *)(smem + L::oP), *sT = (uint16_t *)(smem + L::oT);
+    uint16_t *sY = (uint16_t *)(smem + L::oY), *sYg = (uint16_t *)(smem + L::oYg);
+    uint16_t *sDt = (uint16_t *)(smem + L::oDt), *sXt = (uint16_t *)(smem + L::oXt);
+    uint16_t *sZt = (uint16_t *)(smem + L::oZt);
+    float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
     const int H = a.H;
     const int tile = blockIdx.x % NT;
     const int h = (blockIdx.x / NT) % H;
     const int n = blockIdx.x / (NT * H);
     const int col0 = tile * DVT;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
-
-    if (a.ds_final)
-        load_blk(sD, LDT, a.ds_final + ((long long)n * H + h) * DK * DV + col0, DV, DK, DVT);
-    else
-        for (int i = threadIdx.x; i < DK * LDT; i += blockDim.x) sD[i] = 0.f;
     const long long r0 = row0_of(a, n);
     const int len = len_of(a, n);
     const int nch = (len + C - 1) / C;
-    for (int c = nch - 1; c >= 0; --c) {
+
+    f32x4 D[SPW];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int id = wave + 8 * k, mi = id >> 1, nt = id & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            D[k][i] = a.ds_final ? a.ds_final[(((long long)n * H + h) * DK + 16 * mi + q4 + i) *
+                                                  DV + col0 + 16 * nt + r]
+                                 : 0.f;
+        put_t(sDt, LK, 16 * mi, 16 * nt, D[k]);
+    }
+
+    u32x4 pk[KPT], pq[KPT], pp, pt, py;
+    float pg = 0.f, pgl = 0.f, pgy = 0.f;
+    auto fetch = [&](int c) {
         const long long slot = slot_of(a, n, c);
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
-        const float *rec = a.rec + (slot * H + h) * (long long)kRecFloats;
-        load_rows_bf16<DK>(sK, L::LDK, a.k, t0, nv, H, h);
-        load_rows_bf16<DK>(sQ, L::LDK, a.q, t0, nv, H, h);
-        load_cols_f32<DV, DVT>(sY, LDT, a.dy, t0, nv, H, h, col0);
-        load_mat64(sT, rec);
-        load_mat64(sP, rec + C * C);
-        if (threadIdx.x < C) {
-            const float gt = rec[2 * C * C + threadIdx.x], gl = rec[2 * C * C + C - 1];
-            g[threadIdx.x] = gt;
-            gam[threadIdx.x] = __expf(gt);
-            rat[threadIdx.x] = __expf(gl - gt);
-        }
-        __syncthreads();
-        store_blk(a.dhs + ((slot * H + h) * DK) * (long long)DV + col0, DV, sD, LDT, DK, DVT);
-        // X = P^T dY + diag(gamma_C / gamma) K D
-        for (int tl = wave; tl < 8; tl += 4) {
-            const int m0 = 16 * (tl >> 1), n0 = 16 * (tl & 1);
-            f32x4 a1 = zero4(), a2 = zero4();
-            mm<true, false, false, true>(a1, sP, LDC, sY, LDT, m0, n0, C);
-            mm<false, false, true, false>(a2, sK, L::LDK, sD, LDT, m0, n0, DK);
+        const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
+        const float *rg = (const float *)(rec + kRG);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = m0 + q4 + i;
-                sX[t * LDT + n0 + r] = a1[i] + rat[t] * a2[i];
+        for (int j = 0; j < KPT; ++j) {
+            const int i = tid + kThreadsScan * j;
+            if (i < KP) {
+                pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
+                pq[j] = piece<DK, DK>(a.q, t0, nv, H, h, 0, i);
             }
+        }
+        pp = rec_piece(rec, kRP, tid);
+        pt = rec_piece(rec, kRT, tid);
+        if (tid < VP) {
+            py = piece<DV, DVT>(a.dy, t0, nv, H, h, col0, tid);
+            pgy = rg[tid / (DVT / 8)];
+        }
+        if (tid < C) {
+            pg = rg[tid];
+            pgl = rg[C - 1];
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = tid + kThreadsScan * j;
+            if (i < KP) {
+                put_piece<DK>(sK, LK, i, pk[j]);
+                put_piece<DK>(sQ, LK, i, pq[j]);
+            }
+        }
+        put_rec_piece(sP, tid, pp);
+        put_rec_piece(sT, tid, pt);
+        if (tid < VP) {
+            put_piece<DVT>(sY, LVT, tid, py);
+            put_piece<DVT>(sYg, LVT, tid, scale_piece(py, __expf(pgy)));
+        }
+        if (tid < C) {
+            gam[tid] = __expf(pg);
+            rat[tid] = __expf(pgl - pg);
+        }
+    };
+
+    if (nch > 0) {
+        fetch(nch - 1);
+        commit();
+    }
+    __syncthreads();
+    const int mt = wave >> 1, nt = wave & 1;
+    for (int c = nch - 1; c >= 0; --c) {
+        const long long slot = slot_of(a, n, c);
+        if (c > 0) fetch(c - 1);
+        float *dh = a.dhs + ((slot * H + h) * DK) * (long long)DV + col0;
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dh[(16 * mi + q4 + i) * DV + 16 * nk + r] = D[k][i];
+        }
+        // X = P^T dY + diag(gamma_C / gamma) K D
+        {
+            f32x4 a1 = zero4(), a2 = zero4();
+            mm<true, false>(a1, sP, L64, sY, LVT, 16 * mt, 16 * nt, C);
+            mm<false, true>(a2, sK, LK, sDt, LK, 16 * mt, 16 * nt, DK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a1[i] += rat[16 * mt + q4 + i] * a2[i];
+            put_t(sXt, L64, 16 * mt, 16 * nt, a1);
         }
         __syncthreads();
         // Z = T'^T X, kept as -diag(gamma) Z
-        for (int tl = wave; tl < 8; tl += 4) {
-            const int m0 = 16 * (tl >> 1), n0 = 16 * (tl & 1);
+        {
             f32x4 acc = zero4();
-            mm<true, false, false, false>(acc, sT, LDC, sX, LDT, m0, n0, C);
+            mm<true, true>(acc, sT, L64, sXt, L64, 16 * mt, 16 * nt, C);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = m0 + q4 + i;
-                sZ[t * LDT + n0 + r] = -gam[t] * acc[i];
-            }
-        }
-        // diag(gamma) dY in place (P^T dY above was the last use of dY itself)
-        for (int i = threadIdx.x; i < C * DVT; i += blockDim.x) {
-            const int t = i / DVT, jj = i % DVT;
-            sY[t * LDT + jj] *= gam[t];
+            for (int i = 0; i < 4; ++i) acc[i] *= -gam[16 * mt + q4 + i];
+            put_t(sZt, L64, 16 * mt, 16 * nt, acc);
         }
         __syncthreads();
         // D = gamma_C D + Q^T (diag(gamma) dY) + K^T (-diag(gamma) Z)
         const float gC = gam[C - 1];
-        for (int tl = wave; tl < (DK / 16) * 2; tl += 4) {
-            const int m0 = 16 * (tl >> 1), n0 = 16 * (tl & 1);
-            f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gC * sD[(m0 + q4 + i) * LDT + n0 + r];
-            mm<true, false, true, false>(acc, sQ, L::LDK, sY, LDT, m0, n0, C);
-            mm<true, false, true, false>(acc, sK, L::LDK, sZ, LDT, m0, n0, C);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sD[(m0 + q4 + i) * LDT + n0 + r] = acc[i];
+        for (int k = 0; k < SPW; ++k) {
+            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
+            D[k] *= gC;
+            mm<true, false>(D[k], sQ, LK, sYg, LVT, 16 * mi, 16 * nk, C);
+            mm<true, true>(D[k], sK, LK, sZt, L64, 16 * mi, 16 * nk, C);
+            put_t(sDt, LK, 16 * mi, 16 * nk, D[k]);
         }
         __syncthreads();
+        if (c > 0) commit();
+        __syncthreads();
     }
-    if (a.ds0) store_blk(a.ds0 + ((long long)n * H + h) * DK * DV + col0, DV, sD, LDT, DK, DVT);
+    if (a.ds0) {
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.ds0[(((long long)n * H + h) * DK + 16 * mi + q4 + i) * DV + col0 + 16 * nk +
+                      r] = D[k][i];
+        }
+    }
 }
 
 // ======================================================================================
 // bwd_chunk_kernel: per (chunk slot, head), eight waves.  Passes over the value columns in
-// blocks of 16 accumulate the products that contract over d_v; the rest follows.
+// blocks of 32 accumulate the products that contract over d_v; the rest follows.
 // ======================================================================================
 template <int DK>
-struct ChunkLds {
-    static constexpr int LDK = DK + 8;
-    static constexpr int oK = 0;
-    static constexpr int oQ = oK + C * LDK * 2;
-    static constexpr int oT = oQ + C * LDK * 2;
-    static constexpr int oP = oT + C * LDC * 4;
-    static constexpr int oL = oP + C * LDC * 4;
-    static constexpr int oBlk = oL + C * LDC * 4;             // per-pass region
-    static constexpr int oS = oBlk;                           // [DK][LDB] state block
-    static constexpr int oD = oS + DK * LDB * 4;              // [DK][LDB] adjoint block
-    static constexpr int oV = oD + DK * LDB * 4;              // [64][LDB] each below
-    static constexpr int oY = oV + C * LDB * 4;
-    static constexpr int oR = oY + C * LDB * 4;
-    static constexpr int oDU = oR + C * LDB * 4;
-    static constexpr int oU = oDU + C * LDB * 4;
-    static constexpr int oZ = oU + C * LDB * 4;
-    static constexpr int oE = oZ + C * LDB * 4;
-    static constexpr int blkEnd = oE + C * LDB * 4;
-    static constexpr int oDP = oBlk;                          // after the passes
-    static constexpr int oDL = oDP + C * LDC * 4;
-    static constexpr int oPart = oDL + C * LDC * 4;          // row-sum partials
-    static_assert(oPart + (20 * C + 40) * 4 <= blkEnd, "dP, dL and partials fit");
-    static constexpr int oG = blkEnd;
+struct CkLds {
+    static constexpr int LK = DK + 8;
+    // kept for the whole chunk
+    static constexpr int oK = 0;                          // [64][LK]   K
+    static constexpr int oT = oK + C * LK * 2;            // [64][L64]  T'
+    static constexpr int oP = oT + C * L64 * 2;           // [64][L64]  P
+    static constexpr int oLt = oP + C * L64 * 2;          // [64][L64]  L^T
+    static constexpr int oG = oLt + C * L64 * 2;          // g, gamma, rho, beta [64] fp32
     static constexpr int oGam = oG + C * 4;
     static constexpr int oRat = oGam + C * 4;
     static constexpr int oBet = oRat + C * 4;
-    static constexpr int oDb = oBet + C * 4;
-    static constexpr int total = oDb + C * 4;
+    static constexpr int oDbp = oBet + C * 4;             // [2][64] dbeta partials
+    static constexpr int oBlk = oDbp + 2 * C * 4;
+    // one pass over 32 value columns
+    // (S, D, R and U also as the remainders of their bf16 rounding: *l)
+    static constexpr int oS = oBlk;                       // [DK][LVT]  S columns
+    static constexpr int oSl = oS + DK * LVT * 2;
+    static constexpr int oD = oSl + DK * LVT * 2;         // [DK][LVT]  D columns
+    static constexpr int oDl = oD + DK * LVT * 2;
+    static constexpr int oV = oDl + DK * LVT * 2;         // [64][LVT]  V columns
+    static constexpr int oY = oV + C * LVT * 2;           // [64][LVT]  dY columns
+    static constexpr int oRt = oY + C * LVT * 2;          // [32][L64]  R^T
+    static constexpr int oRtl = oRt + DVB * L64 * 2;
+    static constexpr int oUt = oRtl + DVB * L64 * 2;      // U^T
+    static constexpr int oUtl = oUt + DVB * L64 * 2;
+    static constexpr int oDUt = oUtl + DVB * L64 * 2;     // dU^T
+    static constexpr int oZt = oDUt + DVB * L64 * 2;      // Z^T
+    static constexpr int oEt = oZt + DVB * L64 * 2;       // E^T
+    static constexpr int blkEnd = oEt + DVB * L64 * 2;
+    // after the passes (the pass region is free)
+    static constexpr int oQ = oBlk;                       // [64][LK]   Q
+    static constexpr int oDPt = oQ + C * LK * 2;          // [64][L64]  (dP (.) Gamma)^T
+    static constexpr int oDLs = oDPt + C * L64 * 2;       // [64][L64]  dLG + dLG^T
+    static constexpr int oPart = oDLs + C * L64 * 2;      // row-sum partials (fp32)
+    static constexpr int partFloats = 20 * C + 40;
+    static_assert(oPart + partFloats * 4 <= blkEnd, "the after-pass data fits the pass region");
+    static constexpr int total = blkEnd;
 };
 
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
 {
-    using L = ChunkLds<DK>;
-    constexpr int LDK = L::LDK;
+    using L = CkLds<DK>;
+    constexpr int LK = L::LK;
     constexpr int KT = DK / 16;                 // 16-column tiles of d_k
+    constexpr int NQ = 4 * KT / 8;              // c x d_k tiles per wave
+    constexpr int KP = C * DK / 8;
     __shared__ __align__(16) unsigned char smem[L::total];
-    uint16_t *sK = (uint16_t *)(smem + L::oK), *sQ = (uint16_t *)(smem + L::oQ);
-    float *sT = (float *)(smem + L::oT), *sP = (float *)(smem + L::oP);
-    float *sL = (float *)(smem + L::oL);
-    float *sS = (float *)(smem + L::oS), *sD = (float *)(smem + L::oD);
-    float *sV = (float *)(smem + L::oV), *sY = (float *)(smem + L::oY);
-    float *sR = (float *)(smem + L::oR), *sDU = (float *)(smem + L::oDU);
-    float *sU = (float *)(smem + L::oU), *sZ = (float *)(smem + L::oZ);
-    float *sE = (float *)(smem + L::oE);
-    float *sDP = (float *)(smem + L::oDP), *sDL = (float *)(smem + L::oDL);
+    uint16_t *sK = (uint16_t *)(smem + L::oK), *sT = (uint16_t *)(smem + L::oT);
+    uint16_t *sP = (uint16_t *)(smem + L::oP), *sLt = (uint16_t *)(smem + L::oLt);
     float *g = (float *)(smem + L::oG), *gam = (float *)(smem + L::oGam);
     float *rat = (float *)(smem + L::oRat), *bet = (float *)(smem + L::oBet);
-    float *db = (float *)(smem + L::oDb);
+    float *dbp = (float *)(smem + L::oDbp);
+    uint16_t *sS = (uint16_t *)(smem + L::oS), *sD = (uint16_t *)(smem + L::oD);
+    uint16_t *sSl = (uint16_t *)(smem + L::oSl), *sDl = (uint16_t *)(smem + L::oDl);
+    uint16_t *sRtl = (uint16_t *)(smem + L::oRtl), *sUtl = (uint16_t *)(smem + L::oUtl);
+    uint16_t *sV = (uint16_t *)(smem + L::oV), *sY = (uint16_t *)(smem + L::oY);
+    uint16_t *sRt = (uint16_t *)(smem + L::oRt), *sUt = (uint16_t *)(smem + L::oUt);
+    uint16_t *sDUt = (uint16_t *)(smem + L::oDUt), *sZt = (uint16_t *)(smem + L::oZt);
+    uint16_t *sEt = (uint16_t *)(smem + L::oEt);
+    uint16_t *sQ = (uint16_t *)(smem + L::oQ), *sDPt = (uint16_t *)(smem + L::oDPt);
+    uint16_t *sDLs = (uint16_t *)(smem + L::oDLs);
 
     const int H = a.H;
     const long long slot = blockIdx.x / H;
@@ -595,156 +751,152 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     int n, c, nv;
     long long t0;
     if (!decode_slot(a, slot, n, c, t0, nv)) return;
-    const float *rec = a.rec + (slot * H + h) * (long long)kRecFloats;
+    const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
     const float *hs = a.hs + (slot * H + h) * (long long)DK * DV;
     const float *dhs = a.dhs + (slot * H + h) * (long long)DK * DV;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
 
-    load_rows_bf16<DK>(sK, LDK, a.k, t0, nv, H, h);
-    load_rows_bf16<DK>(sQ, LDK, a.q, t0, nv, H, h);
-    load_mat64(sT, rec);
-    load_mat64(sP, rec + C * C);
-    if (threadIdx.x < C) {
-        const int t = threadIdx.x;
-        const float gt = rec[2 * C * C + t], gl = rec[2 * C * C + C - 1];
-        g[t] = gt;
-        gam[t] = __expf(gt);
-        rat[t] = __expf(gl - gt);
-        bet[t] = t < nv ? a.beta[(t0 + t) * H + h] : 0.f;
-        db[t] = 0.f;
+    for (int i = tid; i < KP; i += 512)
+        put_piece<DK>(sK, LK, i, piece<DK, DK>(a.k, t0, nv, H, h, 0, i));
+    put_rec_piece(sT, tid, rec_piece(rec, kRT, tid));
+    put_rec_piece(sP, tid, rec_piece(rec, kRP, tid));
+    if (tid < C) {
+        const float gt = ((const float *)(rec + kRG))[tid];
+        const float gl = ((const float *)(rec + kRG))[C - 1];
+        g[tid] = gt;
+        gam[tid] = __expf(gt);
+        rat[tid] = __expf(gl - gt);
+        bet[tid] = tid < nv ? a.beta[(t0 + tid) * H + h] : 0.f;
+        dbp[tid] = 0.f;
+        dbp[C + tid] = 0.f;
     }
     __syncthreads();
-    // L = strictlower(K K^T (.) Gamma): 16 tiles, two per wave
+    // L = strictlower(K K^T (.) Gamma), stored transposed: 16 tiles, two per wave
     for (int tile = wave; tile < 16; tile += 8) {
         const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
         f32x4 kk = zero4();
-        mm<false, true, true, true>(kk, sK, LDK, sK, LDK, m0, n0, DK);
+        mm<false, true>(kk, sK, LK, sK, LK, m0, n0, DK);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = m0 + q4 + i, s = n0 + r;
-            sL[t * LDC + s] = s < t ? kk[i] * decay(g, t, s) : 0.f;
+            kk[i] = s < t ? kk[i] * decay(g, t, s) : 0.f;
         }
+        put_t(sLt, L64, m0, n0, kk);
     }
 
-    // accumulators over the passes (tile ids: c x c tiles w, w + 8; c x d_k tiles w + 8 j)
-    constexpr int NQ = 4 * KT / 8;              // c x d_k tiles per wave
+    // accumulators over the passes (c x c tiles wave, wave + 8; c x d_k tiles wave + 8 j)
     f32x4 accM[2], accEu[2], accGq[NQ], accGa[NQ], accGb[NQ];
 #pragma unroll
     for (int i = 0; i < 2; ++i) accM[i] = accEu[i] = zero4();
 #pragma unroll
     for (int i = 0; i < NQ; ++i) accGq[i] = accGa[i] = accGb[i] = zero4();
     float sd = 0.f;                             // partial <S, D>
+    const int mt = wave >> 1, nt = wave & 1;    // this wave's c x 32 tile of a pass
 
     for (int col0 = 0; col0 < DV; col0 += DVB) {
-        __syncthreads();   // previous pass done (and L written before the first)
-        load_blk(sS, LDB, hs + col0, DV, DK, DVB);
-        load_blk(sD, LDB, dhs + col0, DV, DK, DVB);
-        load_cols_f32<DV, DVB>(sV, LDB, a.v, t0, nv, H, h, col0);
-        load_cols_f32<DV, DVB>(sY, LDB, a.dy, t0, nv, H, h, col0);
-        for (int i = threadIdx.x; i < DK * DVB / 4; i += blockDim.x) {
-            const int rr = i / (DVB / 4), p = i % (DVB / 4);
-            const f32x4 s4 = *(const f32x4 *)(hs + rr * DV + col0 + 4 * p);
-            const f32x4 d4 = *(const f32x4 *)(dhs + rr * DV + col0 + 4 * p);
+        __syncthreads();   // the previous pass is done (and L^T written before the first)
+        for (int i = tid; i < DK * DVB / 4; i += 512) {
+            const int row = i / (DVB / 4), c4 = 4 * (i % (DVB / 4));
+            const f32x4 s4 = *(const f32x4 *)(hs + row * DV + col0 + c4);
+            const f32x4 d4 = *(const f32x4 *)(dhs + row * DV + col0 + c4);
             sd += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
+            const bf16x4 sh = __builtin_convertvector(s4, bf16x4);
+            const bf16x4 dh = __builtin_convertvector(d4, bf16x4);
+            *(bf16x4 *)(sS + row * LVT + c4) = sh;
+            *(bf16x4 *)(sD + row * LVT + c4) = dh;
+            *(bf16x4 *)(sSl + row * LVT + c4) =
+                __builtin_convertvector(s4 - __builtin_convertvector(sh, f32x4), bf16x4);
+            *(bf16x4 *)(sDl + row * LVT + c4) =
+                __builtin_convertvector(d4 - __builtin_convertvector(dh, f32x4), bf16x4);
+        }
+        if (tid < C * DVB / 8) {
+            put_piece<DVB>(sV, LVT, tid, piece<DV, DVB>(a.v, t0, nv, H, h, col0, tid));
+        } else if (tid < 2 * C * DVB / 8) {
+            const int i = tid - C * DVB / 8;
+            put_piece<DVB>(sY, LVT, i, piece<DV, DVB>(a.dy, t0, nv, H, h, col0, i));
         }
         __syncthreads();
-        // phase 1: R = V - diag(gamma) K S (waves 0-3), diag(gamma_C/gamma) K D (waves 4-7)
-        {
-            const int m0 = 16 * (wave & 3);
-            f32x4 acc = zero4();
-            if (wave < 4) {
-                mm<false, false, true, false>(acc, sK, LDK, sS, LDB, m0, 0, DK);
+        // phase 1: R = V - diag(gamma) K S;  diag(gamma_C / gamma) K D (kept in registers)
+        f32x4 R = zero4(), kd = zero4();
+        mm<false, false>(R, sK, LK, sS, LVT, 16 * mt, 16 * nt, DK);
+        mm<false, false>(kd, sK, LK, sD, LVT, 16 * mt, 16 * nt, DK);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = m0 + q4 + i;
-                    sR[t * LDB + r] = sV[t * LDB + r] - gam[t] * acc[i];
-                }
-            } else {
-                mm<false, false, true, false>(acc, sK, LDK, sD, LDB, m0, 0, DK);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = m0 + q4 + i;
-                    sDU[t * LDB + r] = rat[t] * acc[i];
-                }
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * mt + q4 + i;
+            R[i] = bf(sV + t * LVT + 16 * nt + r) - gam[t] * R[i];
+            kd[i] *= rat[t];
         }
+        put_t2(sRt, sRtl, L64, 16 * mt, 16 * nt, R);
         __syncthreads();
-        // phase 2: U = T' R (waves 0-3), dU = P^T dY + that (waves 4-7)
+        // phase 2: U = T' R;  dU = P^T dY + diag(gamma_C / gamma) K D
         {
-            const int m0 = 16 * (wave & 3);
-            if (wave < 4) {
-                f32x4 acc = zero4();
-                mm<false, false, false, false>(acc, sT, LDC, sR, LDB, m0, 0, C);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sU[(m0 + q4 + i) * LDB + r] = acc[i];
-            } else {
-                f32x4 acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = sDU[(m0 + q4 + i) * LDB + r];
-                mm<true, false, false, true>(acc, sP, LDC, sY, LDB, m0, 0, C);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sDU[(m0 + q4 + i) * LDB + r] = acc[i];
-            }
+            f32x4 U = zero4();
+            mm2<false, true>(U, sT, L64, sRt, sRtl, L64, 16 * mt, 16 * nt, C);
+            put_t2(sUt, sUtl, L64, 16 * mt, 16 * nt, U);
         }
+        f32x4 dU = kd;
+        mm<true, false>(dU, sP, L64, sY, LVT, 16 * mt, 16 * nt, C);
+        put_t(sDUt, L64, 16 * mt, 16 * nt, dU);
         __syncthreads();
         // phase 3: Z = T'^T dU (= dV)
-        if (wave < 4) {
-            const int m0 = 16 * wave;
-            f32x4 acc = zero4();
-            mm<true, false, false, false>(acc, sT, LDC, sDU, LDB, m0, 0, C);
+        {
+            f32x4 Z = zero4();
+            mm<true, true>(Z, sT, L64, sDUt, L64, 16 * mt, 16 * nt, C);
+            put_t(sZt, L64, 16 * mt, 16 * nt, Z);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = m0 + q4 + i;
-                sZ[t * LDB + r] = acc[i];
-                if (t < nv) Elem<uint16_t>::store(a.dv + ((t0 + t) * H + h) * (long long)DV + col0 + r, acc[i]);
+                const int t = 16 * mt + q4 + i;
+                if (t < nv)
+                    Elem<uint16_t>::store(a.dv + ((t0 + t) * H + h) * (long long)DV + col0 +
+                                              16 * nt + r, Z[i]);
             }
         }
         __syncthreads();
         // phase 4: E = dU - L^T Z;  dbeta_t += sum_j E_tj R_tj
-        if (wave < 4) {
-            const int m0 = 16 * wave;
-            f32x4 acc = zero4();
-            mm<true, false, false, false>(acc, sL, LDC, sZ, LDB, m0, 0, C);
+        {
+            f32x4 lz = zero4();
+            mm<false, true>(lz, sLt, L64, sZt, L64, 16 * mt, 16 * nt, C);
+            const f32x4 E = dU - lz;
+            put_t(sEt, L64, 16 * mt, 16 * nt, E);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = m0 + q4 + i;
-                const float e = sDU[t * LDB + r] - acc[i];
-                sE[t * LDB + r] = e;
-                const float s = sum16(e * sR[t * LDB + r]);
-                if (r == 0) db[t] += s;     // one lane per row: no other writer
+                const float s = sum16(E[i] * R[i]);
+                if (r == 0) dbp[nt * C + 16 * mt + q4 + i] += s;   // one writer per (nt, t)
             }
         }
         __syncthreads();
-        // phase 5: M += dY U^T, Eu += E U^T (c x c); Gq += dY S^T, Ga += Z S^T, Gb += U D^T
+        // phase 5: M += dY U^T, Eu += E U^T (c x c);  Gq += dY S^T, Ga += Z S^T, Gb += U D^T
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int tile = wave + 8 * i;
             const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
-            mm<false, true, false, false>(accM[i], sY, LDB, sU, LDB, m0, n0, DVB);
-            mm<false, true, false, false>(accEu[i], sE, LDB, sU, LDB, m0, n0, DVB);
+            mm2<false, false>(accM[i], sY, LVT, sUt, sUtl, L64, m0, n0, DVB);
+            mm<true, false>(accEu[i], sEt, L64, sUt, L64, m0, n0, DVB);
         }
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int tile = wave + 8 * i;
             const int m0 = 16 * (tile / KT), n0 = 16 * (tile % KT);
-            mm<false, true, false, false>(accGq[i], sY, LDB, sS, LDB, m0, n0, DVB);
-            mm<false, true, false, false>(accGa[i], sZ, LDB, sS, LDB, m0, n0, DVB);
-            mm<false, true, false, false>(accGb[i], sU, LDB, sD, LDB, m0, n0, DVB);
+            mm2<false, true>(accGq[i], sY, LVT, sS, sSl, LVT, m0, n0, DVB);
+            mm2<true, true>(accGa[i], sZt, L64, sS, sSl, LVT, m0, n0, DVB);
+            mm2<true, true>(accGb[i], sUt, L64, sD, sDl, LVT, m0, n0, DVB);
         }
     }
-    __syncthreads();   // the per-pass region becomes dP and dL
+    __syncthreads();   // the pass region now takes Q, (dP (.) Gamma)^T, dLG + dLG^T, partials
 
-    // Row sums below are written per source tile into the free part of the per-pass region
-    // and added in a fixed order afterwards, so every output is bitwise repeatable.
+    for (int i = tid; i < KP; i += 512)
+        put_piece<DK>(sQ, LK, i, piece<DK, DK>(a.q, t0, nv, H, h, 0, i));
+    // Row sums are written per source tile and added in a fixed order afterwards, so every
+    // output is bitwise repeatable.
     //   pG[kt][t]  row dot of the c x d_k accumulators, column tile kt
     //   pR[ct][t]  row sums of dP (.) P + dL (.) L over column tile ct
     //   pC[rt][s]  column sums of the same over row tile rt
     //   pB[ct][t]  row sums of L (.) Eu over column tile ct
-    //   pX[...]    per-tile sums of K (.) Gb (32) and per-wave partials of <S, D> (8)
+    //   pX[...]    per-tile sums of K (.) Gb (up to 32) and per-wave partials of <S, D> (8)
     float *pG = (float *)(smem + L::oPart);
     float *pR = pG + 8 * C, *pC = pR + 4 * C, *pB = pC + 4 * C, *pX = pB + 4 * C;
-    // scale the c x d_k accumulators by their row factors; their row dots with Q and K
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const int tile = wave + 8 * i;
@@ -756,26 +908,17 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             accGq[i][ii] *= gam[t];
             accGa[i][ii] *= -gam[t];
             accGb[i][ii] *= rat[t];
-            const float qv = ldsf(sQ + t * LDK + col), kv = ldsf(sK + t * LDK + col);
+            const float qv = bf(sQ + t * LK + col), kv = bf(sK + t * LK + col);
             const float xb = kv * accGb[i][ii];
             const float d = sum16(qv * accGq[i][ii] + kv * accGa[i][ii] - xb);
             if (r == 0) pG[(n0 / 16) * C + t] = d;
             xs += xb;
         }
-        xs = sum16(xs);
-        xs += __shfl_xor(xs, 16, kWave);
-        xs += __shfl_xor(xs, 32, kWave);
+        xs = sum64(xs);
         if (lane == 0) pX[tile] = xs;
     }
-    // <S, D> over the chunk
     {
-        float s = sd;
-        s += __shfl_xor(s, 1, kWave);
-        s += __shfl_xor(s, 2, kWave);
-        s += __shfl_xor(s, 4, kWave);
-        s += __shfl_xor(s, 8, kWave);
-        s += __shfl_xor(s, 16, kWave);
-        s += __shfl_xor(s, 32, kWave);
+        const float s = sum64(sd);
         if (lane == 0) pX[32 + wave] = s;
     }
     // dP = lower_incl(M), dL = -diag(beta) strictlower(Eu); their decayed forms to LDS;
@@ -784,17 +927,24 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     for (int i = 0; i < 2; ++i) {
         const int tile = wave + 8 * i;
         const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
+        f32x4 dpg;
         float cs = 0.f;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = m0 + q4 + ii, s = n0 + r;
             const float G = decay(g, t, s);
             const float dP = s <= t ? accM[i][ii] : 0.f;
-            const float lv = sL[t * LDC + s];
+            const float lv = bf(sLt + s * L64 + t);
             const float dL = s < t ? -bet[t] * accEu[i][ii] : 0.f;
-            sDP[t * LDC + s] = dP * G;
-            sDL[t * LDC + s] = dL * G;
-            const float w = dP * sP[t * LDC + s] + dL * lv;
+            dpg[ii] = dP * G;
+            const __bf16 dl = (__bf16)(dL * G);
+            if (s < t) {
+                *(__bf16 *)(sDLs + t * L64 + s) = dl;
+                *(__bf16 *)(sDLs + s * L64 + t) = dl;
+            } else if (s == t) {
+                sDLs[t * L64 + t] = 0;
+            }
+            const float w = dP * bf(sP + t * L64 + s) + dL * lv;
             const float rs = sum16(w);
             const float bsum = sum16(s < t ? lv * accEu[i][ii] : 0.f);
             if (r == 0) {
@@ -803,23 +953,22 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             }
             cs += w;
         }
+        put_t(sDPt, L64, m0, n0, dpg);
         cs += __shfl_xor(cs, 16, kWave);
         cs += __shfl_xor(cs, 32, kWave);
         if (lane < 16) pC[(m0 / 16) * C + n0 + r] = cs;
     }
     __syncthreads();
-    // dQ = Gq + (dP (.) Gamma) K;  dK = Ga + Gb + (dP (.) Gamma)^T Q + (dL (.) Gamma) K
-    //                                     + (dL (.) Gamma)^T K
+    // dQ = Gq + (dP (.) Gamma) K;  dK = Ga + Gb + (dP (.) Gamma)^T Q + (dLG + dLG^T) K
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const int tile = wave + 8 * i;
         const int m0 = 16 * (tile / KT), n0 = 16 * (tile % KT);
         f32x4 aq = accGq[i];
-        mm<false, false, false, true>(aq, sDP, LDC, sK, LDK, m0, n0, C);
+        mm<true, false>(aq, sDPt, L64, sK, LK, m0, n0, C);
         f32x4 ak = accGa[i] + accGb[i];
-        mm<true, false, false, true>(ak, sDP, LDC, sQ, LDK, m0, n0, C);
-        mm<false, false, false, true>(ak, sDL, LDC, sK, LDK, m0, n0, C);
-        mm<true, false, false, true>(ak, sDL, LDC, sK, LDK, m0, n0, C);
+        mm<false, false>(ak, sDPt, L64, sQ, LK, m0, n0, C);
+        mm<false, false>(ak, sDLs, L64, sK, LK, m0, n0, C);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = m0 + q4 + ii;
@@ -830,14 +979,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             }
         }
     }
-    __syncthreads();
     // dlog alpha = reverse prefix of dg (the chunk-end terms land on the last slot)
-    if (threadIdx.x < C) {
-        const int t = threadIdx.x;
+    if (tid < C) {
+        const int t = tid;
         float x = 0.f;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) x += pG[kt * C + t];
-        float bt = db[t];
+        float bt = dbp[t] + dbp[C + t];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             x += pR[ct * C + t] - pC[ct * C + t];
@@ -870,9 +1018,9 @@ hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t stream)
     const long long slots = a.nslots * a.H;
     hipLaunchKernelGGL(bwd_prep_kernel<DK>, dim3((unsigned)slots), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((bwd_states_kernel<DK, DV>), dim3((unsigned)(units * (DV / DVT))),
-                       dim3(256), 0, stream, a);
+                       dim3(kThreadsScan), 0, stream, a);
     hipLaunchKernelGGL((bwd_dstates_kernel<DK, DV>), dim3((unsigned)(units * (DV / DVT))),
-                       dim3(256), 0, stream, a);
+                       dim3(kThreadsScan), 0, stream, a);
     hipLaunchKernelGGL((bwd_chunk_kernel<DK, DV>), dim3((unsigned)slots), dim3(512), 0, stream,
                        a);
     return hipGetLastError();
@@ -885,7 +1033,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t backward_workspace_bytes(int num_seqs, long long total_T, int H, int dk, int dv)
 {
     const long long nslots = total_T / kChunk + num_seqs;
-    const size_t rec = align256((size_t)nslots * H * kRecFloats * 4);
+    const size_t rec = align256((size_t)nslots * H * kRecHalfs * 2);
     const size_t st = align256((size_t)nslots * H * dk * dv * 4);
     return rec + 2 * st;
 }
@@ -912,9 +1060,9 @@ hipError_t launch_backward(const BackwardProblem &p, void *workspace, hipStream_
     a.dbeta = p.dbeta;
     a.ds0 = p.ds0;
     a.nslots = p.total_T / kChunk + p.num_seqs;
-    const size_t rec = align256((size_t)a.nslots * p.H * kRecFloats * 4);
+    const size_t rec = align256((size_t)a.nslots * p.H * kRecHalfs * 2);
     const size_t st = align256((size_t)a.nslots * p.H * p.dk * p.dv * 4);
-    a.rec = (float *)workspace;
+    a.rec = (uint16_t *)workspace;
     a.hs = (float *)((unsigned char *)workspace + rec);
     a.dhs = (float *)((unsigned char *)workspace + rec + st);
     if (p.dk == 128 && p.dv == 128) return launch_bwd_dims<128, 128>(a, stream);

@@ -247,9 +247,9 @@ def backward(lib, **kw):
 
 
 def test_backward_workspace_query(lib):
-    # records (T', P, g: 33,024 bytes) plus the kept states and adjoints per chunk slot
+    # records (T' and P in bf16, g in fp32: 16,640 bytes) plus the kept states and adjoints
     slots = 4 * 4096 // 64 + 4
-    rec = slots * 16 * (2 * 64 * 64 + 64) * 4
+    rec = slots * 16 * (2 * 64 * 64 * 2 + 64 * 4)
     st = slots * 16 * 128 * 128 * 4
     assert gdn.gdn_prefill_backward_workspace_bytes(4, 4 * 4096, 16, 128, 128) == rec + 2 * st
     assert gdn.gdn_prefill_backward_workspace_bytes(4, 4 * 4096, 16, 128, 128,
