@@ -25,8 +25,8 @@
 //   dlog alpha_s = sum_{t >= s in the chunk} dg_t,  dalpha = dlog alpha / alpha.
 //
 // Four launches:
-//   bwd_prep_kernel     (chunk slot, head): T' (forward substitution in fp32) and P, bf16,
-//                       and g into a record.
+//   bwd_prep_kernel     (chunk slot, head): T' (forward substitution in fp32) and P^T,
+//                       bf16, and g into a record.
 //   bwd_states_kernel   (sequence, head, 32 state columns): the forward scan, keeping S at
 //                       the start of every chunk.
 //   bwd_dstates_kernel  (sequence, head, 32 state columns): the adjoint scan from the last
@@ -55,7 +55,7 @@ constexpr int DVT = 32;                    // state columns per workgroup of the
 constexpr int LVT = DVT + 8;               // bf16 row stride of a [.][32] LDS tile
 constexpr int DVB = 32;                    // value columns per pass of the chunk kernel
 constexpr int LF = C + 4;                  // fp32 row stride of the prep kernel's solve
-// Record of one (chunk slot, head), in bf16 units: T' [64][64], P [64][64], then the 64
+// Record of one (chunk slot, head), in bf16 units: T' [64][64], P^T [64][64], then the 64
 // within-chunk log-decay prefixes g as fp32.
 constexpr int kRT = 0, kRP = C * C, kRG = 2 * C * C;
 constexpr int kRecHalfs = 2 * C * C + 2 * C;
@@ -185,6 +185,20 @@ __device__ __forceinline__ long long slot_of(const BwdArgs &a, int n, int c)
     return (row0_of(a, n) >> 6) + n + c;
 }
 
+// (unit = sequence * H + head, column tile) of a scan workgroup.  Workgroups are dealt to the
+// eight XCDs in turn (block b to XCD b % 8); when the grid divides evenly, the NT column
+// tiles of a unit get block indices of one residue mod 8, so the K, Q and record bytes they
+// all read are fetched into one L2.
+template <int NT>
+__device__ __forceinline__ void scan_job(int &unit, int &tile)
+{
+    const int b = blockIdx.x, G = gridDim.x;
+    int idx = b;
+    if (G % (8 * NT) == 0) idx = (b & 7) * (G >> 3) + (b >> 3);
+    unit = idx / NT;
+    tile = idx % NT;
+}
+
 // (sequence, chunk) of a slot, or false for a slot no chunk uses.
 __device__ __forceinline__ bool decode_slot(const BwdArgs &a, long long slot, int &n, int &c,
                                             long long &t0, int &nv)
@@ -265,7 +279,8 @@ struct PrepLds {
     static constexpr int oQ = oK + C * LK * 2;
     static constexpr int oL = oQ + C * LK * 2;      // [64][LF] fp32
     static constexpr int oT = oL + C * LF * 4;      // [64][LF] fp32
-    static constexpr int oG = oT + C * LF * 4;
+    static constexpr int oPb = oT + C * LF * 4;     // [64][L64] bf16 P^T
+    static constexpr int oG = oPb + C * L64 * 2;
     static constexpr int oBet = oG + C * 4;
     static constexpr int total = oBet + C * 4;
 };
@@ -279,6 +294,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     uint16_t *sK = (uint16_t *)(smem + L::oK), *sQ = (uint16_t *)(smem + L::oQ);
     float *sL = (float *)(smem + L::oL), *sT = (float *)(smem + L::oT);
     float *g = (float *)(smem + L::oG), *bet = (float *)(smem + L::oBet);
+    uint16_t *sPb = (uint16_t *)(smem + L::oPb);
     const int H = a.H;
     const long long slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -321,8 +337,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
             const int t = m0 + q4 + i, s = n0 + r;
             const float G = decay(g, t, s);
             sL[t * LF + s] = s < t ? kk[i] * G : 0.f;
-            rec[kRP + t * C + s] = __builtin_bit_cast(uint16_t, (__bf16)(qk[i] * G));
+            qk[i] *= G;
         }
+        put_t(sPb, L64, m0, n0, qk);   // P^T
     }
     __syncthreads();
 
@@ -335,14 +352,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     for (int m = 0; m < 16; ++m) col[m] = 0.f;
 #pragma unroll
     for (int t = 0; t < C; ++t) {
-        float s = 0.f;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};    // four partial sums: a short dependency chain
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             if (4 * m < t) {
                 const int i = 4 * m + p;
-                if (i < t) s += sL[t * LF + i] * col[m];
+                if (i < t) ps[m & 3] += sL[t * LF + i] * col[m];
             }
         }
+        float s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         s += __shfl_xor(s, 16, kWave);
         s += __shfl_xor(s, 32, kWave);
         const float val = bet[t] * ((t == j ? 1.f : 0.f) - s);
@@ -352,7 +370,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
         }
     }
     __syncthreads();
-    // T' to the record in 16-byte pieces
+    // T' and P^T to the record in 16-byte pieces
+    for (int i = tid; i < C * C / 8; i += 256)
+        *(u32x4 *)(rec + kRP + 8 * i) = *(const u32x4 *)(sPb + (i >> 3) * L64 + 8 * (i & 7));
     for (int i = tid; i < C * C / 8; i += 256) {
         const int t = i >> 3, c8 = 8 * (i & 7);
         const f32x4 lo = *(const f32x4 *)(sT + t * LF + c8);
@@ -399,9 +419,10 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     uint16_t *sXt = (uint16_t *)(smem + L::oXt), *sUt = (uint16_t *)(smem + L::oUt);
     float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
     const int H = a.H;
-    const int tile = blockIdx.x % NT;
-    const int h = (blockIdx.x / NT) % H;
-    const int n = blockIdx.x / (NT * H);
+    int unit, tile;
+    scan_job<NT>(unit, tile);
+    const int h = unit % H;
+    const int n = unit / H;
     const int col0 = tile * DVT;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
@@ -421,9 +442,13 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
         put_t(sSt, LK, 16 * mi, 16 * nt, S[k]);
     }
 
-    u32x4 pk[KPT], pt, pv;
-    float pg = 0.f, pgl = 0.f;
-    auto fetch = [&](int c) {
+    // inputs of a later chunk, fetched two chunks ahead into one of two register sets
+    struct Pre {
+        u32x4 pk[KPT], pt, pv;
+        float pg, pgl;
+    };
+    Pre ra, rb;
+    auto fetch = [&](Pre &R, int c) {
         const long long slot = slot_of(a, n, c);
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
@@ -431,38 +456,40 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
-            if (i < KP) pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
+            if (i < KP) R.pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
         }
-        pt = rec_piece(rec, kRT, tid);
-        if (tid < VP) pv = piece<DV, DVT>(a.v, t0, nv, H, h, col0, tid);
+        R.pt = rec_piece(rec, kRT, tid);
+        if (tid < VP) R.pv = piece<DV, DVT>(a.v, t0, nv, H, h, col0, tid);
         if (tid < C) {
-            pg = ((const float *)(rec + kRG))[tid];
-            pgl = ((const float *)(rec + kRG))[C - 1];
+            R.pg = ((const float *)(rec + kRG))[tid];
+            R.pgl = ((const float *)(rec + kRG))[C - 1];
         }
     };
-    auto commit = [&]() {
+    auto commit = [&](const Pre &R) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
-            if (i < KP) put_piece<DK>(sK, LK, i, pk[j]);
+            if (i < KP) put_piece<DK>(sK, LK, i, R.pk[j]);
         }
-        put_rec_piece(sT, tid, pt);
-        if (tid < VP) put_piece<DVT>(sV, LVT, tid, pv);
+        put_rec_piece(sT, tid, R.pt);
+        if (tid < VP) put_piece<DVT>(sV, LVT, tid, R.pv);
         if (tid < C) {
-            gam[tid] = __expf(pg);
-            rat[tid] = __expf(pgl - pg);
+            gam[tid] = __expf(R.pg);
+            rat[tid] = __expf(R.pgl - R.pg);
         }
     };
 
     if (nch > 0) {
-        fetch(0);
-        commit();
+        fetch(ra, 0);
+        commit(ra);
     }
+    if (nch > 1) fetch(ra, 1);
     __syncthreads();
     const int mt = wave >> 1, nt = wave & 1;          // this wave's c x 32 tile
-    for (int c = 0; c < nch; ++c) {
+    // chunk c: LDS holds chunk c, cur holds chunk c + 1, nxt receives chunk c + 2
+    auto step = [&](int c, Pre &cur, Pre &nxt) {
         const long long slot = slot_of(a, n, c);
-        if (c + 1 < nch) fetch(c + 1);
+        if (c + 2 < nch) fetch(nxt, c + 2);
         float *hs = a.hs + ((slot * H + h) * DK) * (long long)DV + col0;
 #pragma unroll
         for (int k = 0; k < SPW; ++k) {
@@ -501,8 +528,12 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
             put_t(sSt, LK, 16 * mi, 16 * nk, S[k]);
         }
         __syncthreads();
-        if (c + 1 < nch) commit();
+        if (c + 1 < nch) commit(cur);
         __syncthreads();
+    };
+    for (int c = 0; c < nch; c += 2) {
+        step(c, ra, rb);
+        if (c + 1 < nch) step(c + 1, rb, ra);
     }
 }
 
@@ -517,7 +548,7 @@ struct DsLds {
     static constexpr int LK = DK + 8;
     static constexpr int oK = 0;                         // [64][LK]   K
     static constexpr int oQ = oK + C * LK * 2;           // [64][LK]   Q
-    static constexpr int oP = oQ + C * LK * 2;           // [64][L64]  P
+    static constexpr int oP = oQ + C * LK * 2;           // [64][L64]  P^T
     static constexpr int oT = oP + C * L64 * 2;          // [64][L64]  T'
     static constexpr int oY = oT + C * L64 * 2;          // [64][LVT]  dY columns
     static constexpr int oYg = oY + C * LVT * 2;         // [64][LVT]  diag(gamma) dY
@@ -546,9 +577,10 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
     uint16_t *sZt = (uint16_t *)(smem + L::oZt);
     float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
     const int H = a.H;
-    const int tile = blockIdx.x % NT;
-    const int h = (blockIdx.x / NT) % H;
-    const int n = blockIdx.x / (NT * H);
+    int unit, tile;
+    scan_job<NT>(unit, tile);
+    const int h = unit % H;
+    const int n = unit / H;
     const int col0 = tile * DVT;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
@@ -568,9 +600,12 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
         put_t(sDt, LK, 16 * mi, 16 * nt, D[k]);
     }
 
-    u32x4 pk[KPT], pq[KPT], pp, pt, py;
-    float pg = 0.f, pgl = 0.f, pgy = 0.f;
-    auto fetch = [&](int c) {
+    struct Pre {
+        u32x4 pk[KPT], pq[KPT], pp, pt, py;
+        float pg, pgl, pgy;
+    };
+    Pre ra, rb;
+    auto fetch = [&](Pre &R, int c) {
         const long long slot = slot_of(a, n, c);
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
@@ -580,51 +615,53 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
             if (i < KP) {
-                pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
-                pq[j] = piece<DK, DK>(a.q, t0, nv, H, h, 0, i);
+                R.pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
+                R.pq[j] = piece<DK, DK>(a.q, t0, nv, H, h, 0, i);
             }
         }
-        pp = rec_piece(rec, kRP, tid);
-        pt = rec_piece(rec, kRT, tid);
+        R.pp = rec_piece(rec, kRP, tid);
+        R.pt = rec_piece(rec, kRT, tid);
         if (tid < VP) {
-            py = piece<DV, DVT>(a.dy, t0, nv, H, h, col0, tid);
-            pgy = rg[tid / (DVT / 8)];
+            R.py = piece<DV, DVT>(a.dy, t0, nv, H, h, col0, tid);
+            R.pgy = rg[tid / (DVT / 8)];
         }
         if (tid < C) {
-            pg = rg[tid];
-            pgl = rg[C - 1];
+            R.pg = rg[tid];
+            R.pgl = rg[C - 1];
         }
     };
-    auto commit = [&]() {
+    auto commit = [&](const Pre &R) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
             if (i < KP) {
-                put_piece<DK>(sK, LK, i, pk[j]);
-                put_piece<DK>(sQ, LK, i, pq[j]);
+                put_piece<DK>(sK, LK, i, R.pk[j]);
+                put_piece<DK>(sQ, LK, i, R.pq[j]);
             }
         }
-        put_rec_piece(sP, tid, pp);
-        put_rec_piece(sT, tid, pt);
+        put_rec_piece(sP, tid, R.pp);
+        put_rec_piece(sT, tid, R.pt);
         if (tid < VP) {
-            put_piece<DVT>(sY, LVT, tid, py);
-            put_piece<DVT>(sYg, LVT, tid, scale_piece(py, __expf(pgy)));
+            put_piece<DVT>(sY, LVT, tid, R.py);
+            put_piece<DVT>(sYg, LVT, tid, scale_piece(R.py, __expf(R.pgy)));
         }
         if (tid < C) {
-            gam[tid] = __expf(pg);
-            rat[tid] = __expf(pgl - pg);
+            gam[tid] = __expf(R.pg);
+            rat[tid] = __expf(R.pgl - R.pg);
         }
     };
 
     if (nch > 0) {
-        fetch(nch - 1);
-        commit();
+        fetch(ra, nch - 1);
+        commit(ra);
     }
+    if (nch > 1) fetch(ra, nch - 2);
     __syncthreads();
     const int mt = wave >> 1, nt = wave & 1;
-    for (int c = nch - 1; c >= 0; --c) {
+    // chunk c: LDS holds chunk c, cur holds chunk c - 1, nxt receives chunk c - 2
+    auto step = [&](int c, Pre &cur, Pre &nxt) {
         const long long slot = slot_of(a, n, c);
-        if (c > 0) fetch(c - 1);
+        if (c >= 2) fetch(nxt, c - 2);
         float *dh = a.dhs + ((slot * H + h) * DK) * (long long)DV + col0;
 #pragma unroll
         for (int k = 0; k < SPW; ++k) {
@@ -635,7 +672,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
         // X = P^T dY + diag(gamma_C / gamma) K D
         {
             f32x4 a1 = zero4(), a2 = zero4();
-            mm<true, false>(a1, sP, L64, sY, LVT, 16 * mt, 16 * nt, C);
+            mm<false, false>(a1, sP, L64, sY, LVT, 16 * mt, 16 * nt, C);
             mm<false, true>(a2, sK, LK, sDt, LK, 16 * mt, 16 * nt, DK);
 #pragma unroll
             for (int i = 0; i < 4; ++i) a1[i] += rat[16 * mt + q4 + i] * a2[i];
@@ -662,8 +699,12 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
             put_t(sDt, LK, 16 * mi, 16 * nk, D[k]);
         }
         __syncthreads();
-        if (c > 0) commit();
+        if (c > 0) commit(cur);
         __syncthreads();
+    };
+    for (int c = nch - 1; c >= 0; c -= 2) {
+        step(c, ra, rb);
+        if (c >= 1) step(c - 1, rb, ra);
     }
     if (a.ds0) {
 #pragma unroll
@@ -687,7 +728,7 @@ struct CkLds {
     // kept for the whole chunk
     static constexpr int oK = 0;                          // [64][LK]   K
     static constexpr int oT = oK + C * LK * 2;            // [64][L64]  T'
-    static constexpr int oP = oT + C * L64 * 2;           // [64][L64]  P
+    static constexpr int oP = oT + C * L64 * 2;           // [64][L64]  P^T
     static constexpr int oLt = oP + C * L64 * 2;          // [64][L64]  L^T
     static constexpr int oG = oLt + C * L64 * 2;          // g, gamma, rho, beta [64] fp32
     static constexpr int oGam = oG + C * 4;
@@ -794,12 +835,28 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     float sd = 0.f;                             // partial <S, D>
     const int mt = wave >> 1, nt = wave & 1;    // this wave's c x 32 tile of a pass
 
-    for (int col0 = 0; col0 < DV; col0 += DVB) {
-        __syncthreads();   // the previous pass is done (and L^T written before the first)
-        for (int i = tid; i < DK * DVB / 4; i += 512) {
+    // the next pass's S and D columns (fp32) and V or dY columns are fetched into registers
+    // while the current pass computes
+    constexpr int SP = DK * DVB / 4 / 512;
+    f32x4 ps[SP], pd[SP];
+    u32x4 pvy;
+    auto fetch = [&](int col0) {
+#pragma unroll
+        for (int j = 0; j < SP; ++j) {
+            const int i = tid + 512 * j;
             const int row = i / (DVB / 4), c4 = 4 * (i % (DVB / 4));
-            const f32x4 s4 = *(const f32x4 *)(hs + row * DV + col0 + c4);
-            const f32x4 d4 = *(const f32x4 *)(dhs + row * DV + col0 + c4);
+            ps[j] = *(const f32x4 *)(hs + row * DV + col0 + c4);
+            pd[j] = *(const f32x4 *)(dhs + row * DV + col0 + c4);
+        }
+        if (tid < C * DVB / 8) pvy = piece<DV, DVB>(a.v, t0, nv, H, h, col0, tid);
+        else pvy = piece<DV, DVB>(a.dy, t0, nv, H, h, col0, tid - C * DVB / 8);
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int j = 0; j < SP; ++j) {
+            const int i = tid + 512 * j;
+            const int row = i / (DVB / 4), c4 = 4 * (i % (DVB / 4));
+            const f32x4 s4 = ps[j], d4 = pd[j];
             sd += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
             const bf16x4 sh = __builtin_convertvector(s4, bf16x4);
             const bf16x4 dh = __builtin_convertvector(d4, bf16x4);
@@ -810,13 +867,17 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             *(bf16x4 *)(sDl + row * LVT + c4) =
                 __builtin_convertvector(d4 - __builtin_convertvector(dh, f32x4), bf16x4);
         }
-        if (tid < C * DVB / 8) {
-            put_piece<DVB>(sV, LVT, tid, piece<DV, DVB>(a.v, t0, nv, H, h, col0, tid));
-        } else if (tid < 2 * C * DVB / 8) {
-            const int i = tid - C * DVB / 8;
-            put_piece<DVB>(sY, LVT, i, piece<DV, DVB>(a.dy, t0, nv, H, h, col0, i));
-        }
+        if (tid < C * DVB / 8) put_piece<DVB>(sV, LVT, tid, pvy);
+        else put_piece<DVB>(sY, LVT, tid - C * DVB / 8, pvy);
+    };
+    static_assert(2 * C * DVB / 8 == 512 && SP >= 1, "one V or dY piece per thread");
+
+    fetch(0);
+    for (int col0 = 0; col0 < DV; col0 += DVB) {
+        __syncthreads();   // the previous pass is done (and L^T written before the first)
+        commit();
         __syncthreads();
+        if (col0 + DVB < DV) fetch(col0 + DVB);
         // phase 1: R = V - diag(gamma) K S;  diag(gamma_C / gamma) K D (kept in registers)
         f32x4 R = zero4(), kd = zero4();
         mm<false, false>(R, sK, LK, sS, LVT, 16 * mt, 16 * nt, DK);
@@ -836,7 +897,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             put_t2(sUt, sUtl, L64, 16 * mt, 16 * nt, U);
         }
         f32x4 dU = kd;
-        mm<true, false>(dU, sP, L64, sY, LVT, 16 * mt, 16 * nt, C);
+        mm<false, false>(dU, sP, L64, sY, LVT, 16 * mt, 16 * nt, C);
         put_t(sDUt, L64, 16 * mt, 16 * nt, dU);
         __syncthreads();
         // phase 3: Z = T'^T dU (= dV)
@@ -944,7 +1005,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             } else if (s == t) {
                 sDLs[t * L64 + t] = 0;
             }
-            const float w = dP * bf(sP + t * L64 + s) + dL * lv;
+            const float w = dP * bf(sP + s * L64 + t) + dL * lv;
             const float rs = sum16(w);
             const float bsum = sum16(s < t ? lv * accEu[i][ii] : 0.f);
             if (r == 0) {
