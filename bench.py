@@ -41,6 +41,13 @@ def backward_flops_per_token_head(d: int, C: int = CHUNK) -> int:
     return 24 * C * d + 16 * d * d
 
 
+def backward_bytes(T: int, H: int, d: int, nseq: int) -> int:
+    """Algorithmic HBM bytes of one backward call (bf16 activations): q, k, v, dy read and dq,
+    dk, dv written (2 bytes each), alpha and beta read and dalpha, dbeta written (fp32), dS0
+    written (fp32)."""
+    return 7 * T * H * d * 2 + 4 * T * H * 4 + nseq * H * d * d * 4
+
+
 def prefill_bytes(T: int, H: int, d: int, nseq: int) -> int:
     # q, k, v, y (bf16), alpha, beta (fp32), final state (fp32)
     return T * H * (4 * d * 2 + 2 * 4) + nseq * H * d * d * 4
@@ -55,6 +62,7 @@ CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc")
 PREFILL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_prefill_common.hpp",
                    "gdn_prefill.hip", "gdn_prefill_split.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
+BACKWARD_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_backward.hip"]
 
 
 def sha_of(names) -> str:
@@ -80,7 +88,8 @@ def load_traffic(kernel_key: str, sources):
 
 
 def profile_run(torch, gdn, wl, dev):
-    """Three prefill launches, three decode steps and a 1 GiB elementwise pass, untimed."""
+    """Three prefill launches, three decode steps, three backward calls and a 1 GiB
+    elementwise pass, untimed."""
     inp = wl.workload_inputs(wl.PREFILL)
     q, k, v = (wl.to_torch(inp[n], dev, "bf16") for n in ("q", "k", "v"))
     a = torch.from_numpy(inp["alpha"]).to(dev)
@@ -93,6 +102,11 @@ def profile_run(torch, gdn, wl, dev):
         gdn.gdn_decode_step(wl.to_torch(d["q"][s], dev, "bf16"), wl.to_torch(d["k"][s], dev, "bf16"),
                             wl.to_torch(d["v"][s], dev, "bf16"), torch.from_numpy(d["alpha"][s]).to(dev),
                             torch.from_numpy(d["beta"][s]).to(dev), state)
+    adj = wl.backward_inputs(inp, None, seed=2)
+    dy = wl.to_torch(adj["dy"], dev, "bf16")
+    for _ in range(3):
+        gdn.gdn_prefill_backward(q, k, v, a, b, dy, num_seqs=wl.PREFILL.B)
+    del dy
     # calibration: an elementwise kernel that reads 1 GiB and writes 1 GiB
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -375,11 +389,15 @@ def main():
         bms = float(np.median(times))
         bflops = backward_flops_per_token_head(d) * T * H
         btf = bflops / (bms * 1e-3) / 1e12
+        btr = load_traffic("backward_bf16_B4_H16_T4096_d128", BACKWARD_SOURCES)
+        bbytes = backward_bytes(T, H, d, nseq)
         backward = {"workload": w.name, "ms_median": round(bms, 4),
                     "tokens_per_s": round(T / (bms * 1e-3), 1),
                     "flops_per_launch": bflops, "achieved_TFLOPs": round(btf, 2),
                     "frac_of_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
                     "workspace_bytes": bneed,
+                    "algorithmic_bytes_per_launch": bbytes,
+                    "traffic": None if btr is None else btr["bytes_per_launch"],
                     "kernels": "bwd_prep_kernel<128> + bwd_states_kernel<128,128> + "
                                "bwd_dstates_kernel<128,128> + bwd_chunk_kernel<128,128>"}
         del bws, bout, bdy
