@@ -11,6 +11,10 @@ Two implementations of the same definition live here:
 * :func:`chain_numpy` -- the same recurrence in numpy, for tiny cases and as an
   independent cross-check of the C code's indexing.
 
+The channel-wise gated variants (a decay per key channel, erase and write gates per value
+channel; the rule is the special case of uniform gates) are :func:`channel_prefill` (C) and
+:func:`channel_chain_numpy` (numpy).
+
 The derivative of the same recurrence (for training) is :func:`prefill_backward` (C) and
 :func:`chain_backward_numpy` (numpy): reverse mode, token by token, through the four lines
 below.
@@ -72,6 +76,13 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.gdn_oracle_channel_run.restype = ctypes.c_int
+        lib.gdn_oracle_channel_run.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -307,3 +318,80 @@ def chain_backward_numpy(q, k, v, alpha, beta, s0, dy, ds_final):
         D = a * dSt
     out["ds0"] = D
     return out
+
+
+def channel_prefill(q, k, v, a, b, w, cu_seqlens=None, s0=None, heads=None, threads: int = 0,
+                    want_y=True, want_state=True, seq_row0=None, seq_len=None, row_step=1):
+    """Channel-wise gated variants (see gdn_oracle_channel_run in gdn_oracle.c).
+
+    q, k: [rows, H, d_k]; v: [rows, H, d_v] (one dtype); a: [rows, H, d_k] decay per key
+    channel; b, w: [rows, H, d_v] erase and write gates per value channel; s0:
+    [nseq, H, d_k, d_v] or None.  Rows follow cu_seqlens (packed) unless seq_row0/seq_len/
+    row_step give them explicitly.  Returns (y [rows, nh, d_v], s_final [nseq, nh, d_k, d_v])."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k and v must share one dtype")
+    rows, H, dk = q.shape
+    dv = v.shape[2]
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    if a.shape != (rows, H, dk) or b.shape != (rows, H, dv) or w.shape != (rows, H, dv):
+        raise ValueError("gate shapes")
+    if seq_row0 is None:
+        cu = np.array([0, rows], dtype=np.int64) if cu_seqlens is None else \
+            np.asarray(cu_seqlens, dtype=np.int64)
+        seq_row0, seq_len = cu[:-1], np.diff(cu)
+    seq_row0 = np.ascontiguousarray(seq_row0, dtype=np.int64)
+    seq_len = np.ascontiguousarray(seq_len, dtype=np.int64)
+    nseq = int(seq_row0.shape[0])
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        if s0.shape != (nseq, H, dk, dv):
+            raise ValueError("s0 must be [nseq, H, d_k, d_v]")
+    h_lo, h_hi = (0, H) if heads is None else (int(heads[0]), int(heads[1]))
+    nh = h_hi - h_lo
+    y = np.zeros((rows, nh, dv)) if want_y else None
+    sf = np.zeros((nseq, nh, dk, dv)) if want_state else None
+    rc = _load().gdn_oracle_channel_run(
+        _ptr(q), _ptr(k), _ptr(v), dt, _ptr(a), _ptr(b), _ptr(w), _ptr(s0), _ptr(seq_row0),
+        _ptr(seq_len), int(row_step), nseq, H, dk, dv, h_lo, h_hi, _ptr(y), _ptr(sf),
+        int(threads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_channel_run failed with code %d" % rc)
+    return y, sf
+
+
+def channel_chain_c(q, k, v, a, b, w, s0=None):
+    """One chain through the C version (same signature as :func:`channel_chain_numpy`)."""
+    T = np.asarray(q).shape[0]
+    y, sf = channel_prefill(np.asarray(q, np.float64)[:, None], np.asarray(k, np.float64)[:, None],
+                            np.asarray(v, np.float64)[:, None], np.asarray(a)[:, None],
+                            np.asarray(b)[:, None], np.asarray(w)[:, None],
+                            s0=None if s0 is None else np.asarray(s0, np.float64)[None, None],
+                            threads=1)
+    return y[:, 0], sf[0, 0]
+
+
+def channel_chain_numpy(q, k, v, a, b, w, s0=None):
+    """One (sequence, head) chain of the channel-wise gated form in numpy, fp64.
+
+    q, k, a: [T, d_k]; v, b, w: [T, d_v]; s0: [d_k, d_v] or None.  Returns (y, S_T):
+    decay each key channel, retrieve with the key, write the gated value minus the gated
+    retrieval along the key, read with the query."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if s0 is None else np.array(s0, dtype=np.float64)
+    y = np.zeros((T, dv))
+    for t in range(T):
+        St = np.asarray(a[t], np.float64)[:, None] * S          # S~ = Diag(a_t) S
+        e = np.asarray(w[t]) * v[t] - np.asarray(b[t]) * (St.T @ k[t])
+        S = St + np.outer(k[t], e)                             # S = S~ + k_t e^T
+        y[t] = S.T @ q[t]                                      # y_t = S_t^T q_t
+    return y, S

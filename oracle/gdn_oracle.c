@@ -384,3 +384,104 @@ int gdn_oracle_backward(const void *q, const void *k, const void *v, int dtype,
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * Channel-wise gated variants of the rule (TEST INFRASTRUCTURE ONLY).
+ *
+ * The pages say of Kimi Delta Attention only that every feature channel gets its own gate,
+ * and of Gated DeltaNet-2 only that erase and write get separate channel-wise gates.  The
+ * reading taken (one form covering both, and the rule itself as a special case): per token,
+ *
+ *     S~  = Diag(a_t) S                          a_t in (0, 1]^{d_k}: decay per key channel
+ *     r   = S~^T k_t                             what the key retrieves
+ *     e   = (w_t .* v_t) - (b_t .* r)            b_t, w_t in [0, 1]^{d_v}: erase and write
+ *     S   = S~ + k_t e^T                         gates per value channel
+ *     y_t = S^T q_t
+ *
+ * a_t = alpha_t 1, b_t = w_t = beta_t 1 is the gated delta rule (gdn_oracle_run);
+ * b_t = w_t = beta_t 1 with a free a_t is the channel-decay variant.  Addressing as in
+ * gdn_oracle_run; a is [rows, H, d_k], b and w are [rows, H, d_v] (all heads).
+ */
+int gdn_oracle_channel_run(const void *q, const void *k, const void *v, int dtype,
+                           const double *a, const double *b, const double *w,
+                           const double *s0, const int64_t *seq_row0, const int64_t *seq_len,
+                           int64_t row_step, int nseq, int H, int dk, int dv, int head_lo,
+                           int head_hi, double *y, double *s_final, int nthreads)
+{
+    if (!q || !k || !v || !a || !b || !w || !seq_row0 || !seq_len) return -1;
+    if (nseq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (head_lo < 0 || head_hi > H || head_lo >= head_hi) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
+    const int nh = head_hi - head_lo;
+    const int64_t units = (int64_t)nseq * nh;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)dk * dv);
+        double *kv = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *vv = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !kv || !qv || !vv || !e) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < units; ++u) {
+                const int n = (int)(u / nh);
+                const int h = head_lo + (int)(u % nh);
+                const int hy = h - head_lo;
+                if (s0) memcpy(S, s0 + ((int64_t)n * H + h) * dk * dv, sizeof(double) * (size_t)dk * dv);
+                else memset(S, 0, sizeof(double) * (size_t)dk * dv);
+                for (int64_t s = 0; s < seq_len[n]; ++s) {
+                    const int64_t row = seq_row0[n] + s * row_step;
+                    const int64_t qk_base = (row * H + h) * (int64_t)dk;
+                    const int64_t v_base = (row * H + h) * (int64_t)dv;
+                    for (int i = 0; i < dk; ++i) {
+                        kv[i] = load_elem(k, qk_base + i, dtype);
+                        qv[i] = load_elem(q, qk_base + i, dtype);
+                    }
+                    for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, v_base + j, dtype);
+                    /* S~ = Diag(a_t) S */
+                    for (int i = 0; i < dk; ++i) {
+                        const double ai = a[qk_base + i];
+                        for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] *= ai;
+                    }
+                    /* e = w .* v - b .* (S~^T k) */
+                    for (int j = 0; j < dv; ++j) {
+                        double r = 0.0;
+                        for (int i = 0; i < dk; ++i) r += S[(int64_t)i * dv + j] * kv[i];
+                        e[j] = w[v_base + j] * vv[j] - b[v_base + j] * r;
+                    }
+                    /* S = S~ + k e^T */
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] += kv[i] * e[j];
+                    /* y_t = S^T q_t */
+                    if (y) {
+                        double *yo = y + (row * nh + hy) * (int64_t)dv;
+                        for (int j = 0; j < dv; ++j) {
+                            double acc = 0.0;
+                            for (int i = 0; i < dk; ++i) acc += S[(int64_t)i * dv + j] * qv[i];
+                            yo[j] = acc;
+                        }
+                    }
+                }
+                if (s_final)
+                    memcpy(s_final + ((int64_t)n * nh + hy) * dk * dv, S, sizeof(double) * (size_t)dk * dv);
+            }
+        }
+        free(S);
+        free(kv);
+        free(qv);
+        free(vv);
+        free(e);
+    }
+    return failed ? -2 : 0;
+}
