@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 METRIC = "GDN prefill tokens/s (MFMA %) + decode steps/s at B=128 (HBM GB/s %)"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3    # MI355X fp32 vector (256 CUs x 2.4 GHz x 256 FLOP/clock)
 CHUNK = 64
 
 
@@ -126,6 +127,7 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-layer-steps", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-channel", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 counter passes: 3 prefill launches, 3 decode "
                          "steps and an elementwise kernel over 1 GiB (the calibration)")
@@ -402,6 +404,76 @@ def main():
                                "bwd_dstates_kernel<128,128> + bwd_chunk_kernel<128,128>"}
         del bws, bout, bdy
 
+    # ------------------------------------------------------------------ channel-wise gates
+    # the channel-gated variant (decay per key channel, erase and write gates per value
+    # channel), token by token in fp32: at the prefill workload's shape, and as decode steps
+    # (one token for each of 128 sequences) over four state sets in rotation
+    chan = None
+    if not args.no_channel:
+        cg = wl.channel_gates(inp, seed=2)
+        ca, cb, cw = (torch.from_numpy(cg[n]).to(dev) for n in ("decay", "erase", "write"))
+        del cg
+        cy = torch.empty_like(y)
+        cs = torch.empty_like(sf)
+
+        def run_chan():
+            gdn.gdn_channel_gated(q, k, v, ca, cb, cw, num_seqs=nseq, y=cy, final_state=cs)
+
+        for _ in range(2):
+            run_chan()
+        times = []
+        for _ in range(5):
+            cache_flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_chan()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        cms = float(np.median(times))
+        cflops = 7 * d * d * T * H          # decay, retrieval, write and read-out per token-head
+        ctf = cflops / (cms * 1e-3) / 1e12
+        del ca, cb, cw, cy, cs
+        ns = 64
+        dg = wl.channel_gates({"q": np.empty((ns * B, 1, 1)), "H": Hd, "dk": dh, "dv": dh},
+                              seed=3)
+        dga, dgb, dgw = (torch.from_numpy(dg[n]).to(dev).view(ns, B, Hd, dh)
+                         for n in ("decay", "erase", "write"))
+        del dg
+        cstates = [s0.clone() for _ in range(4)]
+        cyd = torch.empty((B, Hd, dh), dtype=torch.bfloat16, device=dev)
+
+        def run_chan_decode():
+            for s in range(ns):
+                st = cstates[s % 4]
+                gdn.gdn_channel_gated(dq[s], dk_[s], dv_[s], dga[s], dgb[s], dgw[s],
+                                      initial_state=st, num_seqs=B, y=cyd, final_state=st)
+
+        run_chan_decode()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_chan_decode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cd_us = e0.elapsed_time(e1) * 1e3 / ns
+        cdbytes = (2 * dh * dh * 4 + 4 * dh * 2 + 3 * dh * 4) * B * Hd
+        cgbs = cdbytes / (cd_us * 1e-6) / 1e9
+        chan = {"kernel": "channel_gated_kernel<128, bf16>",
+                "prefill": {"workload": w.name, "ms_median": round(cms, 4),
+                            "tokens_per_s": round(T / (cms * 1e-3), 1),
+                            "flops_per_launch": cflops,
+                            "roofline": {"bound": "alu", "achieved": round(ctf, 2),
+                                         "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(ctf / PEAK_FP32_VALU_TFLOPS, 4)}},
+                "decode": {"workload": "B=%d H=%d d=%d, %d steps over 4 state sets" % (B, Hd, dh, ns),
+                           "us_per_step": round(cd_us, 2),
+                           "algorithmic_bytes_per_launch": cdbytes,
+                           "roofline": {"bound": "hbm", "achieved": round(cgbs, 1),
+                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": round(cgbs / PEAK_HBM_GBS, 4)}}}
+        del dga, dgb, dgw, cstates
+
     # ------------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -441,6 +513,7 @@ def main():
         "decode": decode,
         "layer_steps": layer,
         "backward": backward,
+        "channel_gated": chan,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

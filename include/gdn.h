@@ -130,6 +130,33 @@ gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_
                             int32_t *segment_chunks);
 
 /*
+ * Channel-wise gated variants of the rule (the reading notes' successors of Gated DeltaNet:
+ * Kimi Delta Attention, a gate per feature channel, and Gated DeltaNet-2, separate
+ * channel-wise erase and write gates; the notes give no equations, the form below is the
+ * library's reading).  Per sequence and head, for every token in order:
+ *
+ *     S~ = Diag(a_t) S,   e = (w_t .* v_t) - (b_t .* (S~^T k_t)),   S = S~ + k_t e^T,
+ *     y_t = S^T q_t
+ *
+ *   q, k           [total_T, H, d_k] dtype; v, y [total_T, H, d_v] dtype (16-byte aligned)
+ *   decay          a: [total_T, H, d_k] fp32 in (0, 1] (16-byte aligned)
+ *   erase, write   b, w: [total_T, H, d_v] fp32 in [0, 1]
+ *   initial_state  [N, H, d_k, d_v] fp32 or NULL (zeros); final_state the same shape or NULL,
+ *                  and may be exactly initial_state (a decode step: one token per sequence,
+ *                  state carried in place)
+ *   cu_seqlens     as for gdn_prefill
+ * Uniform gates (a_t = alpha_t, b_t = w_t = beta_t) give gdn_prefill's rule; b_t = w_t =
+ * beta_t with a free a_t is the channel-decay form.  Computed token by token in fp32 with
+ * the state in registers (no chunked form yet).  d_k, d_v in {64, 128}.
+ */
+gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const float *decay,
+                             const float *erase, const float *write,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                             int32_t d_v, int32_t dtype, void *y, float *final_state,
+                             void *stream);
+
+/*
  * Chunked backward (training) of gdn_prefill.
  *
  * For the scalar L = sum <dy, y> + sum <d_final_state, S_T> of the prefill with the same

@@ -262,6 +262,68 @@ gdn_status gdn_prefill_backward(const void *q, const void *k, const void *v, con
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const float *decay,
+                             const float *erase, const float *write,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                             int32_t d_v, int32_t dtype, void *y, float *final_state,
+                             void *stream)
+{
+    gdn_status st = check_common(total_T, H, d_k, d_v, dtype);
+    if (st != GDN_OK) return st;
+    if (num_seqs <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (!cu_seqlens && total_T % num_seqs != 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (total_T > 0 && (!q || !k || !v || !decay || !erase || !write || !y))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const void *quads[] = {q, k, v, y, decay, initial_state, final_state};
+    for (const void *p : quads)
+        if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARGUMENT;
+    const void *words[] = {erase, write, cu_seqlens};
+    for (const void *p : words)
+        if (p && !aligned(p, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    const size_t e = esize(dtype);
+    const size_t rows = (size_t)total_T;
+    const size_t n_qk = rows * H * d_k * e, n_v = rows * H * d_v * e;
+    const size_t n_a = rows * H * d_k * 4, n_g = rows * H * d_v * 4;
+    const size_t n_s = (size_t)num_seqs * H * d_k * d_v * 4;
+    const size_t n_cu = cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0;
+    struct Span { const void *p; size_t n; };
+    const Span inputs[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {decay, n_a}, {erase, n_g},
+                           {write, n_g}, {cu_seqlens, n_cu}};
+    const Span outs[] = {{y, n_v}, {final_state, final_state ? n_s : 0}};
+    for (const Span &o : outs) {
+        for (const Span &in : inputs)
+            if (overlap(o.p, o.n, in.p, in.n)) return GDN_ERR_INVALID_ARGUMENT;
+        if (o.p != final_state && overlap(o.p, o.n, initial_state, initial_state ? n_s : 0))
+            return GDN_ERR_INVALID_ARGUMENT;
+    }
+    if (overlap(y, n_v, final_state, final_state ? n_s : 0)) return GDN_ERR_INVALID_ARGUMENT;
+    // the state may be carried in place (final_state == initial_state exactly)
+    if (final_state && initial_state && final_state != initial_state &&
+        overlap(final_state, n_s, initial_state, n_s))
+        return GDN_ERR_INVALID_ARGUMENT;
+
+    gdn::ChannelProblem c;
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.a = decay;
+    c.b = erase;
+    c.w = write;
+    c.s0 = initial_state;
+    c.cu = cu_seqlens;
+    c.num_seqs = num_seqs;
+    c.total_T = total_T;
+    c.H = H;
+    c.dk = d_k;
+    c.dv = d_v;
+    c.dtype = dtype;
+    c.y = y;
+    c.s_final = final_state;
+    hipError_t err = gdn::launch_channel_gated(c, (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
                            const float *beta, float *state, void *y, int32_t B, int32_t H,
                            int32_t d_k, int32_t d_v, int32_t dtype, void *stream)

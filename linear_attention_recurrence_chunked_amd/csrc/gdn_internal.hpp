@@ -60,6 +60,21 @@ struct BackwardProblem {
 size_t backward_workspace_bytes(int num_seqs, long long total_T, int H, int dk, int dv);
 hipError_t launch_backward(const BackwardProblem &p, void *workspace, hipStream_t stream);
 
+// Channel-wise gated variants: decay per key channel, erase and write gates per value
+// channel (token by token).
+struct ChannelProblem {
+    const void *q, *k, *v;
+    const float *a, *b, *w;     // [T, H, dk], [T, H, dv], [T, H, dv]
+    const float *s0;            // [N, H, dk, dv] or null
+    const int32_t *cu;
+    int num_seqs;
+    long long total_T;
+    int H, dk, dv, dtype;
+    void *y;
+    float *s_final;             // or null; may equal s0
+};
+hipError_t launch_channel_gated(const ChannelProblem &c, hipStream_t stream);
+
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *alpha,
                          const float *beta, float *state, void *y, int B, int H, int dk,
                          int dv, int dtype, hipStream_t stream);

@@ -67,6 +67,9 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill_backward.restype = i32
     lib.gdn_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                          i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_channel_gated.restype = i32
+    lib.gdn_channel_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                      i32, vp, vp, vp]
     lib.gdn_decode_step.restype = i32
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.gdn_short_conv.restype = i32
@@ -206,6 +209,31 @@ def gdn_prefill_backward(q, k, v, alpha, beta, dy, initial_state=None, d_final_s
         _stream(stream))
     _check("gdn_prefill_backward", st)
     return gq, gk, gv, ga, gb, gs
+
+
+def gdn_channel_gated(q, k, v, decay, erase, write, initial_state=None, cu_seqlens=None,
+                      num_seqs=None, y=None, final_state=None, want_final_state=True,
+                      stream=None):
+    """Channel-wise gated variants: decay [T, H, d_k], erase and write [T, H, d_v] fp32
+    gates; otherwise as :func:`gdn_prefill`.  final_state may be initial_state (in place).
+    Returns (y, final_state)."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        num_seqs = cu_seqlens.shape[0] - 1
+    elif num_seqs is None:
+        num_seqs = 1
+    if y is None:
+        y = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    st = load().gdn_channel_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(erase),
+                                  _ptr(write), _ptr(initial_state), _ptr(cu_seqlens), num_seqs,
+                                  T, H, dk, dv, _dtype_code(q), _ptr(y), _ptr(final_state),
+                                  _stream(stream))
+    _check("gdn_channel_gated", st)
+    return y, final_state
 
 
 def gdn_decode_step(q, k, v, alpha, beta, state, y=None, stream=None):

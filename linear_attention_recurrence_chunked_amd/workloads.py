@@ -17,7 +17,9 @@ Recipe (shared by every workload):
 * optional initial state S0 ~ N(0, sd_s0) fp32 per (sequence, head);
 * variable lengths are integers uniform in [lo, hi], both ends included;
 * for the backward: the output adjoint dy ~ N(0, 1) in the storage dtype, and an optional
-  final-state adjoint ~ N(0, sd) fp32 per (sequence, head).
+  final-state adjoint ~ N(0, sd) fp32 per (sequence, head);
+* for the channel-wise gated variants: a decay per key channel sigmoid(N(mu_a, sd_a)) and
+  erase and write gates per value channel sigmoid(N(mu_b, sd_b)), fp32.
 
 bf16 tensors are handled as ``uint16`` bit patterns on the numpy side and viewed as
 ``torch.bfloat16`` when moved to the GPU.
@@ -32,7 +34,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 BLOCK_ROWS = 65536
-T_Q, T_K, T_V, T_ALPHA, T_BETA, T_S0, T_LENS, T_DY, T_DSF = range(9)
+T_Q, T_K, T_V, T_ALPHA, T_BETA, T_S0, T_LENS, T_DY, T_DSF, T_CA, T_CB, T_CW = range(12)
 
 
 @dataclass(frozen=True)
@@ -198,6 +200,19 @@ def backward_inputs(inp: dict, ds_sd: Optional[float] = 0.02, seed: int = 0) -> 
         dsf = (ds_sd * rng.standard_normal((inp["num_seqs"], inp["H"], inp["dk"],
                                             inp["dv"]))).astype(np.float32)
     return dict(dy=dy, ds_final=dsf)
+
+
+def channel_gates(inp: dict, a=(3.0, 1.0), b=(0.0, 1.0), seed: int = 0) -> dict:
+    """Channel-wise gates for the prefill ``inp``: decay [rows, H, dk], erase and write
+    [rows, H, dv], fp32."""
+    rows, H, dk, dv = int(inp["q"].shape[0]), inp["H"], inp["dk"], inp["dv"]
+
+    def draw(tid, d, mu, sd):
+        out = np.empty((rows, H, d), dtype=np.float32)
+        _fill(out, seed, tid, lambda rng, n: _sigmoid(mu + sd * rng.standard_normal((n, H, d))).astype(np.float32))
+        return out
+
+    return dict(decay=draw(T_CA, dk, *a), erase=draw(T_CB, dv, *b), write=draw(T_CW, dv, *b))
 
 
 def workload_inputs(w: Workload) -> dict:

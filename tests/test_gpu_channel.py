@@ -1,0 +1,128 @@
+"""GPU parity of gdn_channel_gated (channel-wise decay, erase and write gates) against the
+fp64 oracle of the variants: per-(sequence, head) max relative error of y and the final
+state, 1e-4 for fp32 inputs and 2e-2 for bf16."""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, cu_of, say, slice_rel_err, state_rel_err, torch_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _inp(lengths, H=2, d=(128, 128), dtype="bf16", s0=0.02, seed=0, varlen=True):
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    return wl.make_inputs(lengths, H, d[0], d[1], dtype, s0_sd=s0, seed=seed, varlen=varlen)
+
+
+def run_gpu(inp, gates, dev, want_state=True, state_in_place=False):
+    from linear_attention_recurrence_chunked_amd import gdn
+    t = torch_inputs(inp, dev)
+    g = {n: torch.from_numpy(gates[n]).to(dev) for n in ("decay", "erase", "write")}
+    fs = t["s0"] if state_in_place else None
+    y, sf = gdn.gdn_channel_gated(t["q"], t["k"], t["v"], g["decay"], g["erase"], g["write"],
+                                  initial_state=t["s0"], cu_seqlens=t["cu"],
+                                  num_seqs=inp["num_seqs"], final_state=fs,
+                                  want_final_state=want_state)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), None if sf is None else sf.cpu().numpy()
+
+
+def check(inp, gates, dev, oracle, label, heads=None):
+    say("[gpu] channel %s lengths=%s H=%d dk=%d dv=%d %s" % (
+        label, list(inp["lengths"][:8]), inp["H"], inp["dk"], inp["dv"], inp["dtype"]))
+    gy, gs = run_gpu(inp, gates, dev)
+    ry, rs = oracle.channel_prefill(inp["q"], inp["k"], inp["v"], gates["decay"],
+                                    gates["erase"], gates["write"], cu_seqlens=cu_of(inp),
+                                    s0=inp["s0"], heads=heads, threads=16)
+    h0, h1 = (0, inp["H"]) if heads is None else heads
+    ey = slice_rel_err(gy[:, h0:h1], ry, cu_of(inp))
+    es = state_rel_err(gs[:, h0:h1], rs)
+    say("    err y %.3e  state %.3e" % (ey, es))
+    tol = TOL[inp["dtype"]]
+    assert np.all(np.isfinite(gy)) and np.all(np.isfinite(gs))
+    assert ey <= tol and es <= tol, (ey, es)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_channel_ragged(dev, oracle_lib, dtype, d):
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = _inp([1, 63, 0, 130, 7], H=3, d=d, dtype=dtype, seed=31)
+    check(inp, wl.channel_gates(inp, seed=31), dev, oracle_lib, "ragged")
+
+
+def test_channel_strong_decay_and_gate_edges(dev, oracle_lib):
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = _inp([300, 41], H=2, seed=32)
+    g = wl.channel_gates(inp, a=(1.0, 2.0), b=(0.0, 2.0), seed=32)
+    g["decay"][::3] = 1.0
+    g["erase"][::5] = 0.0
+    g["write"][1::7] = 1.0
+    g["erase"][2::7] = 1.0
+    check(inp, g, dev, oracle_lib, "strong-decay-edges")
+
+
+def test_channel_without_states(dev, oracle_lib):
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = _inp([96] * 3, H=2, s0=None, seed=33, varlen=False)
+    check(inp, wl.channel_gates(inp, seed=33), dev, oracle_lib, "no-state")
+
+
+def test_uniform_gates_match_the_chunked_rule(dev):
+    """a = alpha, b = w = beta reproduce gdn_prefill (chunked, bf16 MFMA) within its bound."""
+    from linear_attention_recurrence_chunked_amd import gdn
+    inp = _inp([200, 64, 333], H=2, seed=34)
+    H, dk, dv = inp["H"], inp["dk"], inp["dv"]
+    gates = dict(decay=np.repeat(inp["alpha"][:, :, None], dk, 2),
+                 erase=np.repeat(inp["beta"][:, :, None], dv, 2),
+                 write=np.repeat(inp["beta"][:, :, None], dv, 2))
+    gy, gs = run_gpu(inp, gates, dev)
+    t = torch_inputs(inp, dev)
+    y, sf = gdn.gdn_prefill(t["q"], t["k"], t["v"], t["alpha"], t["beta"],
+                            initial_state=t["s0"], cu_seqlens=t["cu"])
+    ey = slice_rel_err(gy, y.float().cpu().numpy().astype(np.float64), cu_of(inp))
+    es = state_rel_err(gs, sf.cpu().numpy())
+    say("    channel vs chunked rule: y %.3e state %.3e" % (ey, es))
+    assert ey <= 2e-2 and es <= 2e-2
+
+
+def test_decode_steps_in_place_equal_one_call(dev):
+    """T one-token calls carrying the state in place give bitwise the y and state of one call
+    over the T tokens."""
+    from linear_attention_recurrence_chunked_amd import gdn
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    B, T, H = 3, 9, 2
+    inp = _inp([T] * B, H=H, seed=35, varlen=False)
+    g = wl.channel_gates(inp, seed=35)
+    gy, gs = run_gpu(inp, g, dev)
+    t = torch_inputs(inp, dev)
+    gt = {n: torch.from_numpy(g[n]).to(dev) for n in ("decay", "erase", "write")}
+    state = t["s0"].clone()
+    ys = torch.empty_like(t["v"])
+    for s in range(T):
+        idx = torch.arange(B, device=dev) * T + s
+        y, _ = gdn.gdn_channel_gated(t["q"][idx].contiguous(), t["k"][idx].contiguous(),
+                                     t["v"][idx].contiguous(), gt["decay"][idx].contiguous(),
+                                     gt["erase"][idx].contiguous(), gt["write"][idx].contiguous(),
+                                     initial_state=state, num_seqs=B, final_state=state)
+        ys[idx] = y
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ys.float().cpu().numpy(), gy)
+    np.testing.assert_array_equal(state.cpu().numpy(), gs)
+
+
+def test_channel_full_prefill_shape_sampled_heads(dev, oracle_lib):
+    """4 x 4096 tokens, 16 heads of 128, bf16: two heads against the oracle."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = wl.workload_inputs(wl.PREFILL)
+    g = wl.channel_gates(inp, seed=36)
+    for h in (0, 13):
+        check(inp, g, dev, oracle_lib, "full-size head %d" % h, heads=(h, h + 1))
