@@ -11,22 +11,30 @@
 // write gates per value channel).  Uniform gates a_t = alpha_t, b_t = w_t = beta_t give the
 // gated delta rule.
 //
-// channel_gated_kernel: one wave per (sequence, head, 8 value columns), four waves per
-// workgroup.  Lane (g = lane / 8, j = lane % 8) keeps rows g R .. g R + R - 1 (R = d_k / 8) of
-// column j of the fp32 state in registers for the whole sequence; per token it decays its
-// rows, forms its part of S~^T k and of S^T q and the wave adds the eight parts with three
-// shuffles.  There are no barriers: every wave runs its own chain.  The next token's inputs
-// are loaded while the current one is computed.  A decode step is a call with one token per
-// sequence and the state carried in place.
+// Both kernels keep each (sequence, head) state column in fp32 registers across the whole
+// sequence, split over lanes by rows; per token a lane decays its rows and forms its parts of
+// S~^T k and S^T q, and the lanes of a column add their parts.
+//
+// channel_gated_kernel (sequences of 16 or more tokens on average): eight waves per
+// (sequence, head, 32 value columns); lane (j = lane / 16, g = lane % 16) holds rows
+// g d_k/16 .. of column 4 w + j, so a column's sums stay inside one 16-lane row and take four
+// DPP rotations.  The workgroup stages blocks of 32 tokens (k, q and decay rows, v and the
+// gates of its columns) in LDS, fetching the next block into registers while the current one
+// is processed: global latency is paid once per block, with one barrier per block.
+//
+// channel_step_kernel (short sequences, e.g. a decode step: one token per sequence, state
+// carried in place): four waves per (sequence, head, 32 columns), lane (g = lane / 8, j =
+// lane % 8) holds rows g d_k/8 .. of column 8 w + j, inputs loaded straight from memory one
+// token ahead, no LDS and no barriers.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
 namespace gdn {
 namespace {
 
-constexpr int kGroups = 8;      // row groups per wave
-constexpr int kCols = 8;        // value columns per wave
-constexpr int kWgCols = 4 * kCols;
+constexpr int kGroups = 8;      // row groups per wave of the step kernel
+constexpr int kCols = 8;        // value columns per wave of the step kernel
+constexpr int kWgCols = 32;     // value columns per workgroup (both kernels)
 
 struct ChanArgs {
     const void *q, *k, *v;
@@ -39,6 +47,16 @@ struct ChanArgs {
     void *y;
     float *s_final;
 };
+
+// Sum over a 16-lane row, every lane receiving the total (four DPP rotations).
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+    return x;
+}
 
 // R consecutive elements as floats (R a multiple of 8; 16-byte aligned).
 template <int R>
@@ -83,7 +101,7 @@ struct Tok {
 };
 
 template <int DK, typename T>
-__global__ __launch_bounds__(256) void channel_gated_kernel(ChanArgs p)
+__global__ __launch_bounds__(256) void channel_step_kernel(ChanArgs p)
 {
     constexpr int R = DK / kGroups;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -158,6 +176,202 @@ __global__ __launch_bounds__(256) void channel_gated_kernel(ChanArgs p)
     }
 }
 
+constexpr int TB = 32;          // tokens per staged block
+
+template <int DK>
+struct ChanLds {
+    static constexpr int oK = 0;                          // [TB][DK] fp32 k
+    static constexpr int oQ = oK + TB * DK * 4;           // [TB][DK] fp32 q
+    static constexpr int oA = oQ + TB * DK * 4;           // [TB][DK] fp32 decay
+    static constexpr int oV = oA + TB * DK * 4;           // [TB][32] fp32 v
+    static constexpr int oB = oV + TB * kWgCols * 4;      // [TB][32] fp32 erase gate
+    static constexpr int oW = oB + TB * kWgCols * 4;      // [TB][32] fp32 write gate
+    static constexpr int buf = oW + TB * kWgCols * 4;
+    static constexpr int total = 2 * buf;
+};
+
+// 16-byte pieces of a staged block held in registers: k and q rows (dtype), decay rows,
+// then the workgroup's 32 columns of v and of the two gates.
+template <int DK, typename T>
+struct Stage {
+    static constexpr int E = (int)sizeof(T);
+    static constexpr int KP = TB * DK * E / 16;           // pieces of k (and of q)
+    static constexpr int AP = TB * DK / 4;                // pieces of the decay rows
+    static constexpr int VP = TB * kWgCols * E / 16;      // pieces of v
+    static constexpr int GP = TB * kWgCols / 4;           // pieces of each gate
+    static constexpr int N = 2 * KP + AP + VP + 2 * GP;
+    static constexpr int PER = (N + 511) / 512;
+    u32x4 x[PER];
+};
+
+template <int DK, typename T>
+__global__ __launch_bounds__(512) void channel_gated_kernel(ChanArgs p)
+{
+    constexpr int R = DK / 16;
+    using L = ChanLds<DK>;
+    using S = Stage<DK, T>;
+    constexpr int EP = 16 / S::E;                         // elements per piece (dtype)
+    __shared__ __align__(16) unsigned char smem[L::total];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane & 15, j = lane >> 4;
+    const int H = p.H, dv = p.dv;
+    const int tiles = dv / kWgCols;
+    const int tile = blockIdx.x % tiles;
+    const int h = (blockIdx.x / tiles) % H;
+    const int n = blockIdx.x / (tiles * H);
+    const int col0 = tile * kWgCols;
+    const int cl = wave * 4 + j;                          // this lane's column in the tile
+    long long t0;
+    int len;
+    if (p.cu) {
+        t0 = p.cu[n];
+        len = (int)(p.cu[n + 1] - p.cu[n]);
+    } else {
+        const long long per = p.total_T / p.num_seqs;
+        t0 = per * n;
+        len = (int)per;
+    }
+    const T *gq = (const T *)p.q, *gk = (const T *)p.k, *gv = (const T *)p.v;
+    T *gy = (T *)p.y;
+
+    float s[R];
+    const long long sbase = (((long long)n * H + h) * DK + g * R) * dv + col0 + cl;
+#pragma unroll
+    for (int i = 0; i < R; ++i) s[i] = p.s0 ? p.s0[sbase + (long long)i * dv] : 0.f;
+
+    // piece id -> (kind, token, offset); tokens past the sequence read as zero
+    S st;
+    auto fetch = [&](int blk) {
+#pragma unroll
+        for (int u = 0; u < S::PER; ++u) {
+            int i = tid + 512 * u;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (i < 2 * S::KP) {
+                const T *src = i < S::KP ? gk : gq;
+                const int ii = i % S::KP, per = DK / EP, t = ii / per, c = ii % per;
+                if (blk * TB + t < len)
+                    x = *(const u32x4 *)(src + ((t0 + blk * TB + t) * H + h) * DK + c * EP);
+            } else if ((i -= 2 * S::KP) < S::AP) {
+                const int per = DK / 4, t = i / per, c = i % per;
+                if (blk * TB + t < len)
+                    x = *(const u32x4 *)(p.a + ((t0 + blk * TB + t) * H + h) * DK + c * 4);
+            } else if ((i -= S::AP) < S::VP) {
+                const int per = kWgCols / EP, t = i / per, c = i % per;
+                if (blk * TB + t < len)
+                    x = *(const u32x4 *)(gv + ((t0 + blk * TB + t) * H + h) * (long long)dv +
+                                         col0 + c * EP);
+            } else if ((i -= S::VP) < 2 * S::GP) {
+                const float *src = i < S::GP ? p.b : p.w;
+                const int ii = i % S::GP, per = kWgCols / 4, t = ii / per, c = ii % per;
+                if (blk * TB + t < len)
+                    x = *(const u32x4 *)(src + ((t0 + blk * TB + t) * H + h) * (long long)dv +
+                                         col0 + c * 4);
+            }
+            st.x[u] = x;
+        }
+    };
+    // write a piece as fp32 into LDS: dtype pieces widen to two 16-byte stores for bf16
+    auto put = [&](float *dst, u32x4 x) {
+        if constexpr (S::E == 2) {
+            f32x4 lo, hi;
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                lo[2 * w] = __uint_as_float(x[w] << 16);
+                lo[2 * w + 1] = __uint_as_float(x[w] & 0xffff0000u);
+                hi[2 * w] = __uint_as_float(x[2 + w] << 16);
+                hi[2 * w + 1] = __uint_as_float(x[2 + w] & 0xffff0000u);
+            }
+            *(f32x4 *)dst = lo;
+            *(f32x4 *)(dst + 4) = hi;
+        } else {
+            *(u32x4 *)dst = x;
+        }
+    };
+    auto commit = [&](int buf) {
+        unsigned char *base = smem + buf * L::buf;
+#pragma unroll
+        for (int u = 0; u < S::PER; ++u) {
+            int i = tid + 512 * u;
+            const u32x4 x = st.x[u];
+            if (i < 2 * S::KP) {
+                float *dst = (float *)(base + (i < S::KP ? L::oK : L::oQ));
+                const int ii = i % S::KP, per = DK / EP, t = ii / per, c = ii % per;
+                put(dst + t * DK + c * EP, x);
+            } else if ((i -= 2 * S::KP) < S::AP) {
+                const int per = DK / 4, t = i / per, c = i % per;
+                *(u32x4 *)((float *)(base + L::oA) + t * DK + c * 4) = x;
+            } else if ((i -= S::AP) < S::VP) {
+                const int per = kWgCols / EP, t = i / per, c = i % per;
+                put((float *)(base + L::oV) + t * kWgCols + c * EP, x);
+            } else if ((i -= S::VP) < 2 * S::GP) {
+                float *dst = (float *)(base + (i < S::GP ? L::oB : L::oW));
+                const int ii = i % S::GP, per = kWgCols / 4, t = ii / per, c = ii % per;
+                *(u32x4 *)(dst + t * kWgCols + c * 4) = x;
+            }
+        }
+    };
+
+    const int nblk = (len + TB - 1) / TB;
+    if (nblk > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 1 < nblk) fetch(blk + 1);
+        const unsigned char *base = smem + (blk & 1) * L::buf;
+        const float *sk = (const float *)(base + L::oK), *sq = (const float *)(base + L::oQ);
+        const float *sa = (const float *)(base + L::oA), *sv = (const float *)(base + L::oV);
+        const float *sb = (const float *)(base + L::oB), *sw = (const float *)(base + L::oW);
+        const int nt = len - blk * TB < TB ? len - blk * TB : TB;
+#pragma unroll 2
+        for (int t = 0; t < nt; ++t) {
+            float kr[R], qr[R], ar[R];
+#pragma unroll
+            for (int i = 0; i < R; i += 4) {
+                const f32x4 k4 = *(const f32x4 *)(sk + t * DK + g * R + i);
+                const f32x4 q4 = *(const f32x4 *)(sq + t * DK + g * R + i);
+                const f32x4 a4 = *(const f32x4 *)(sa + t * DK + g * R + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kr[i + e] = k4[e];
+                    qr[i + e] = q4[e];
+                    ar[i + e] = a4[e];
+                }
+            }
+            const float vv = sv[t * kWgCols + cl], bb = sb[t * kWgCols + cl];
+            const float ww = sw[t * kWgCols + cl];
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; i += 2) {
+                s[i] *= ar[i];
+                s[i + 1] *= ar[i + 1];
+                r0 += s[i] * kr[i];
+                r1 += s[i + 1] * kr[i + 1];
+            }
+            const float r = row_sum16(r0 + r1);
+            const float e = ww * vv - bb * r;
+            float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; i += 2) {
+                s[i] += kr[i] * e;
+                s[i + 1] += kr[i + 1] * e;
+                y0 += s[i] * qr[i];
+                y1 += s[i + 1] * qr[i + 1];
+            }
+            const float yo = row_sum16(y0 + y1);
+            if (g == 0)
+                Elem<T>::store(gy + ((t0 + blk * TB + t) * H + h) * (long long)dv + col0 + cl, yo);
+        }
+        if (blk + 1 < nblk) commit((blk + 1) & 1);
+        __syncthreads();
+    }
+    if (p.s_final) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) p.s_final[sbase + (long long)i * dv] = s[i];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_channel_gated(const ChannelProblem &c, hipStream_t stream)
@@ -179,12 +393,24 @@ hipError_t launch_channel_gated(const ChannelProblem &c, hipStream_t stream)
     p.s_final = c.s_final;
     const unsigned grid = (unsigned)((long long)c.num_seqs * c.H * (c.dv / kWgCols));
     const bool bf = c.dtype == kDtypeBF16;
-    if (c.dk == 128) {
-        if (bf) hipLaunchKernelGGL((channel_gated_kernel<128, uint16_t>), dim3(grid), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((channel_gated_kernel<128, float>), dim3(grid), dim3(256), 0, stream, p);
+    // staging pays off from about one block of tokens per sequence on
+    const bool staged = c.total_T >= 16LL * c.num_seqs;
+    if (staged) {
+        if (c.dk == 128) {
+            if (bf) hipLaunchKernelGGL((channel_gated_kernel<128, uint16_t>), dim3(grid), dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((channel_gated_kernel<128, float>), dim3(grid), dim3(512), 0, stream, p);
+        } else {
+            if (bf) hipLaunchKernelGGL((channel_gated_kernel<64, uint16_t>), dim3(grid), dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((channel_gated_kernel<64, float>), dim3(grid), dim3(512), 0, stream, p);
+        }
     } else {
-        if (bf) hipLaunchKernelGGL((channel_gated_kernel<64, uint16_t>), dim3(grid), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((channel_gated_kernel<64, float>), dim3(grid), dim3(256), 0, stream, p);
+        if (c.dk == 128) {
+            if (bf) hipLaunchKernelGGL((channel_step_kernel<128, uint16_t>), dim3(grid), dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((channel_step_kernel<128, float>), dim3(grid), dim3(256), 0, stream, p);
+        } else {
+            if (bf) hipLaunchKernelGGL((channel_step_kernel<64, uint16_t>), dim3(grid), dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((channel_step_kernel<64, float>), dim3(grid), dim3(256), 0, stream, p);
+        }
     }
     return hipGetLastError();
 }

@@ -126,3 +126,29 @@ def test_channel_full_prefill_shape_sampled_heads(dev, oracle_lib):
     g = wl.channel_gates(inp, seed=36)
     for h in (0, 13):
         check(inp, g, dev, oracle_lib, "full-size head %d" % h, heads=(h, h + 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_channel_short_sequences(dev, oracle_lib, dtype):
+    """Sequences of a few tokens (the one-token-ahead kernel) against the oracle."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = _inp([1, 3, 7, 2, 0, 5, 1, 1], H=2, dtype=dtype, seed=37)
+    check(inp, wl.channel_gates(inp, seed=37), dev, oracle_lib, "short")
+
+
+def test_staged_and_step_kernels_agree(dev):
+    """The same four 40-token sequences through the staged kernel and, padded with empty
+    sequences so that the average length falls below one block, through the step kernel."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = _inp([40] * 4, H=2, d=(128, 64), dtype="f32", seed=38)
+    g = wl.channel_gates(inp, seed=38)
+    ya, sa = run_gpu(inp, g, dev)
+    pad = dict(inp)
+    pad["lengths"] = np.array([40] * 4 + [0] * 12)
+    pad["num_seqs"] = 16
+    pad["cu_seqlens"] = np.concatenate([[0], np.cumsum(pad["lengths"])]).astype(np.int32)
+    pad["s0"] = np.concatenate([inp["s0"], np.zeros((12,) + inp["s0"].shape[1:], np.float32)])
+    yb, sb = run_gpu(pad, g, dev)
+    np.testing.assert_allclose(ya, yb, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(sa, sb[:4], rtol=1e-5, atol=1e-6)
+    np.testing.assert_array_equal(sb[4:], 0.0)
