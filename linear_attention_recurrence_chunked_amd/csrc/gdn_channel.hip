@@ -22,10 +22,12 @@
 // gates of its columns) in LDS, fetching the next block into registers while the current one
 // is processed: global latency is paid once per block, with one barrier per block.
 //
-// channel_step_kernel (short sequences, e.g. a decode step: one token per sequence, state
-// carried in place): four waves per (sequence, head, 32 columns), lane (g = lane / 8, j =
-// lane % 8) holds rows g d_k/8 .. of column 8 w + j, inputs loaded straight from memory one
-// token ahead, no LDS and no barriers.
+// channel_step_kernel (short sequences): four waves per (sequence, head, 32 columns), lane
+// (g = lane / 8, j = lane % 8) holds rows g d_k/8 .. of column 8 w + j, inputs loaded
+// straight from memory one token ahead, no LDS and no barriers.
+//
+// channel_decode_kernel (one token per sequence, the state carried in place): one streaming
+// pass over the state (below).
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -372,6 +374,94 @@ __global__ __launch_bounds__(512) void channel_gated_kernel(ChanArgs p)
     }
 }
 
+// channel_decode_kernel: every sequence has exactly one token (a decode step).  One pass over
+// the state: with the decay folded into the key and the query,
+//     r = S^T (a .* k),  s = S^T (a .* q),  e = w .* v - b .* r,
+//     y = s + (k . q) e,  S <- Diag(a) S + k e^T,
+// each workgroup streams a 64-column slice of one head's state once in and once out with
+// 16-byte non-temporal accesses (lane: 4 columns, 16 row groups), reducing over the key
+// dimension with shuffles and a small LDS exchange.
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__(256) void channel_decode_kernel(ChanArgs p)
+{
+    constexpr int NCT = DV / 64;
+    constexpr int RPT = DK / 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid & 15, rg = tid >> 4;
+    const int slice = blockIdx.x % NCT;
+    const long long bh = blockIdx.x / NCT;
+    const int col = slice * 64 + cg * 4;
+    const T *gq = (const T *)p.q, *gk = (const T *)p.k, *gv = (const T *)p.v;
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = p.s0 ? __builtin_nontemporal_load(
+                          (const f32x4 *)(p.s0 + (bh * DK + rg + 16 * i) * DV + col))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    float kr[RPT], ka[RPT], qa[RPT], ar[RPT];
+    float pkq = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const long long o = bh * DK + rg + 16 * i;
+        kr[i] = Elem<T>::load(gk + o);
+        const float qv = Elem<T>::load(gq + o);
+        ar[i] = p.a[o];
+        ka[i] = ar[i] * kr[i];
+        qa[i] = ar[i] * qv;
+        pkq += kr[i] * qv;
+    }
+    f32x4 pr = {0.f, 0.f, 0.f, 0.f}, ps = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        pr += s[i] * ka[i];
+        ps += s[i] * qa[i];
+    }
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pr[c] += __shfl_xor(pr[c], m, kWave);
+            ps[c] += __shfl_xor(ps[c], m, kWave);
+        }
+        pkq += __shfl_xor(pkq, m, kWave);
+    }
+    __shared__ f32x4 red_r[4][16], red_s[4][16];
+    __shared__ float red_kq[4];
+    if (lane < 16) {
+        red_r[wave][lane] = pr;
+        red_s[wave][lane] = ps;
+    }
+    if (lane == 0) red_kq[wave] = pkq;
+    __syncthreads();
+    const f32x4 r = red_r[0][cg] + red_r[1][cg] + red_r[2][cg] + red_r[3][cg];
+    const f32x4 sq = red_s[0][cg] + red_s[1][cg] + red_s[2][cg] + red_s[3][cg];
+    const float kq = red_kq[0] + red_kq[1] + red_kq[2] + red_kq[3];
+    const long long vo = bh * DV + col;
+    const f32x4 e = *(const f32x4 *)(p.w + vo) * load4(gv + vo) - *(const f32x4 *)(p.b + vo) * r;
+    if (rg == 0) store4((T *)p.y + vo, sq + kq * e);
+    if (p.s_final) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            __builtin_nontemporal_store(ar[i] * s[i] + kr[i] * e,
+                                        (f32x4 *)(p.s_final + (bh * DK + rg + 16 * i) * DV + col));
+    }
+}
+
+template <typename T>
+hipError_t launch_decode_kernel(const ChanArgs &p, int dk, int dv, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)((long long)p.num_seqs * p.H * (dv / 64));
+    if (dk == 128 && dv == 128)
+        hipLaunchKernelGGL((channel_decode_kernel<128, 128, T>), dim3(grid), dim3(256), 0, stream, p);
+    else if (dk == 128)
+        hipLaunchKernelGGL((channel_decode_kernel<128, 64, T>), dim3(grid), dim3(256), 0, stream, p);
+    else if (dv == 128)
+        hipLaunchKernelGGL((channel_decode_kernel<64, 128, T>), dim3(grid), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((channel_decode_kernel<64, 64, T>), dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_channel_gated(const ChannelProblem &c, hipStream_t stream)
@@ -391,8 +481,11 @@ hipError_t launch_channel_gated(const ChannelProblem &c, hipStream_t stream)
     p.dv = c.dv;
     p.y = c.y;
     p.s_final = c.s_final;
-    const unsigned grid = (unsigned)((long long)c.num_seqs * c.H * (c.dv / kWgCols));
     const bool bf = c.dtype == kDtypeBF16;
+    if (!c.cu && c.total_T == c.num_seqs)     // one token per sequence: a decode step
+        return bf ? launch_decode_kernel<uint16_t>(p, c.dk, c.dv, stream)
+                  : launch_decode_kernel<float>(p, c.dk, c.dv, stream);
+    const unsigned grid = (unsigned)((long long)c.num_seqs * c.H * (c.dv / kWgCols));
     // staging pays off from about one block of tokens per sequence on
     const bool staged = c.total_T >= 16LL * c.num_seqs;
     if (staged) {

@@ -94,29 +94,40 @@ def test_uniform_gates_match_the_chunked_rule(dev):
     assert ey <= 2e-2 and es <= 2e-2
 
 
-def test_decode_steps_in_place_equal_one_call(dev):
-    """T one-token calls carrying the state in place give bitwise the y and state of one call
-    over the T tokens."""
+def test_decode_steps_in_place(dev, oracle_lib):
+    """T one-token calls (the decode kernel) carrying the state in place agree with one call
+    over the T tokens and with the oracle."""
     from linear_attention_recurrence_chunked_amd import gdn
     from linear_attention_recurrence_chunked_amd import workloads as wl
-    B, T, H = 3, 9, 2
-    inp = _inp([T] * B, H=H, seed=35, varlen=False)
-    g = wl.channel_gates(inp, seed=35)
-    gy, gs = run_gpu(inp, g, dev)
-    t = torch_inputs(inp, dev)
-    gt = {n: torch.from_numpy(g[n]).to(dev) for n in ("decay", "erase", "write")}
-    state = t["s0"].clone()
-    ys = torch.empty_like(t["v"])
-    for s in range(T):
-        idx = torch.arange(B, device=dev) * T + s
-        y, _ = gdn.gdn_channel_gated(t["q"][idx].contiguous(), t["k"][idx].contiguous(),
-                                     t["v"][idx].contiguous(), gt["decay"][idx].contiguous(),
-                                     gt["erase"][idx].contiguous(), gt["write"][idx].contiguous(),
-                                     initial_state=state, num_seqs=B, final_state=state)
-        ys[idx] = y
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(ys.float().cpu().numpy(), gy)
-    np.testing.assert_array_equal(state.cpu().numpy(), gs)
+    for dtype, d in (("bf16", (128, 128)), ("f32", (64, 128)), ("bf16", (128, 64))):
+        B, T, H = 3, 9, 2
+        inp = _inp([T] * B, H=H, d=d, dtype=dtype, seed=35, varlen=False)
+        g = wl.channel_gates(inp, seed=35)
+        gy, gs = run_gpu(inp, g, dev)
+        t = torch_inputs(inp, dev)
+        gt = {n: torch.from_numpy(g[n]).to(dev) for n in ("decay", "erase", "write")}
+        state = t["s0"].clone()
+        ys = torch.empty_like(t["v"])
+        for s in range(T):
+            idx = torch.arange(B, device=dev) * T + s
+            y, _ = gdn.gdn_channel_gated(t["q"][idx].contiguous(), t["k"][idx].contiguous(),
+                                         t["v"][idx].contiguous(), gt["decay"][idx].contiguous(),
+                                         gt["erase"][idx].contiguous(),
+                                         gt["write"][idx].contiguous(), initial_state=state,
+                                         num_seqs=B, final_state=state)
+            ys[idx] = y
+        torch.cuda.synchronize()
+        dy = ys.float().cpu().numpy()
+        ds = state.cpu().numpy()
+        tol = 1e-5 if dtype == "f32" else 2e-2
+        assert slice_rel_err(dy, gy, cu_of(inp)) <= tol
+        assert state_rel_err(ds, gs) <= 1e-5
+        ry, rs = oracle_lib.channel_prefill(inp["q"], inp["k"], inp["v"], g["decay"],
+                                            g["erase"], g["write"], cu_seqlens=cu_of(inp),
+                                            s0=inp["s0"])
+        ey, es = slice_rel_err(dy, ry, cu_of(inp)), state_rel_err(ds, rs)
+        say("    decode %s d=%s: err y %.3e state %.3e" % (dtype, d, ey, es))
+        assert ey <= TOL[dtype] and es <= TOL[dtype]
 
 
 def test_channel_full_prefill_shape_sampled_heads(dev, oracle_lib):
