@@ -63,6 +63,7 @@ CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc")
 PREFILL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_prefill_common.hpp",
                    "gdn_prefill.hip", "gdn_prefill_split.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
+CHANNEL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_channel.hip"]
 BACKWARD_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_backward.hip"]
 
 
@@ -89,8 +90,9 @@ def load_traffic(kernel_key: str, sources):
 
 
 def profile_run(torch, gdn, wl, dev):
-    """Three prefill launches, three decode steps, three backward calls and a 1 GiB
-    elementwise pass, untimed."""
+    """Three prefill launches, three decode steps, three backward calls, three channel-gated
+    prefills and decode steps and a 1 GiB elementwise pass, untimed."""
+    import numpy as np
     inp = wl.workload_inputs(wl.PREFILL)
     q, k, v = (wl.to_torch(inp[n], dev, "bf16") for n in ("q", "k", "v"))
     a = torch.from_numpy(inp["alpha"]).to(dev)
@@ -108,6 +110,19 @@ def profile_run(torch, gdn, wl, dev):
     for _ in range(3):
         gdn.gdn_prefill_backward(q, k, v, a, b, dy, num_seqs=wl.PREFILL.B)
     del dy
+    # the channel-gated variant at the prefill shape, and three of its decode steps
+    cg = wl.channel_gates(inp, seed=2)
+    ca, cb, cw = (torch.from_numpy(cg[n]).to(dev) for n in ("decay", "erase", "write"))
+    for _ in range(3):
+        gdn.gdn_channel_gated(q, k, v, ca, cb, cw, num_seqs=wl.PREFILL.B)
+    del ca, cb, cw, cg
+    B, H, dh = wl.DECODE.B, wl.DECODE.H, wl.DECODE.dk
+    dg = wl.channel_gates({"q": np.empty((B, 1, 1)), "H": H, "dk": dh, "dv": dh}, seed=3)
+    dga, dgb, dgw = (torch.from_numpy(dg[n]).to(dev) for n in ("decay", "erase", "write"))
+    for s in range(3):
+        gdn.gdn_channel_gated(wl.to_torch(d["q"][s], dev, "bf16"), wl.to_torch(d["k"][s], dev, "bf16"),
+                              wl.to_torch(d["v"][s], dev, "bf16"), dga, dgb, dgw,
+                              initial_state=state, num_seqs=B, final_state=state)
     # calibration: an elementwise kernel that reads 1 GiB and writes 1 GiB
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -459,19 +474,23 @@ def main():
         cd_us = e0.elapsed_time(e1) * 1e3 / ns
         cdbytes = (2 * dh * dh * 4 + 4 * dh * 2 + 3 * dh * 4) * B * Hd
         cgbs = cdbytes / (cd_us * 1e-6) / 1e9
+        ctr_p = load_traffic("channel_prefill_bf16_B4_H16_T4096_d128", CHANNEL_SOURCES)
+        ctr_d = load_traffic("channel_decode_bf16_B128_H16_d128", CHANNEL_SOURCES)
         chan = {"kernel": "channel_gated_kernel<128, bf16>",
                 "prefill": {"workload": w.name, "ms_median": round(cms, 4),
                             "tokens_per_s": round(T / (cms * 1e-3), 1),
                             "flops_per_launch": cflops,
                             "roofline": {"bound": "alu", "achieved": round(ctf, 2),
                                          "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                                         "frac": round(ctf / PEAK_FP32_VALU_TFLOPS, 4)}},
+                                         "frac": round(ctf / PEAK_FP32_VALU_TFLOPS, 4),
+                                         "traffic": None if ctr_p is None else ctr_p["bytes_per_launch"]}},
                 "decode": {"workload": "B=%d H=%d d=%d, %d steps over 4 state sets" % (B, Hd, dh, ns),
                            "us_per_step": round(cd_us, 2),
                            "algorithmic_bytes_per_launch": cdbytes,
                            "roofline": {"bound": "hbm", "achieved": round(cgbs, 1),
                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                        "frac": round(cgbs / PEAK_HBM_GBS, 4)}}}
+                                        "frac": round(cgbs / PEAK_HBM_GBS, 4),
+                                        "traffic": None if ctr_d is None else ctr_d["bytes_per_launch"]}}}
         del dga, dgb, dgw, cstates
 
     # ------------------------------------------------------------------ CPU baseline

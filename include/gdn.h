@@ -147,7 +147,8 @@ gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_
  *   cu_seqlens     as for gdn_prefill
  * Uniform gates (a_t = alpha_t, b_t = w_t = beta_t) give gdn_prefill's rule; b_t = w_t =
  * beta_t with a free a_t is the channel-decay form.  Computed token by token in fp32 with
- * the state in registers (no chunked form yet).  d_k, d_v in {64, 128}.
+ * the state in registers (no chunked form); with one token per sequence and no cu_seqlens
+ * (a decode step) in one streaming pass over the state.  d_k, d_v in {64, 128}.
  */
 gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const float *decay,
                              const float *erase, const float *write,
