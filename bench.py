@@ -64,6 +64,7 @@ PREFILL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_prefill_common.hpp
                    "gdn_prefill.hip", "gdn_prefill_split.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
 CHANNEL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_channel.hip"]
+QSA_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_qsa.hip"]
 BACKWARD_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_backward.hip"]
 
 
@@ -143,6 +144,7 @@ def main():
     ap.add_argument("--no-layer-steps", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-channel", action="store_true")
+    ap.add_argument("--no-qsa", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 counter passes: 3 prefill launches, 3 decode "
                          "steps and an elementwise kernel over 1 GiB (the calibration)")
@@ -493,6 +495,50 @@ def main():
                                         "traffic": None if ctr_d is None else ctr_d["bytes_per_launch"]}}}
         del dga, dgb, dgw, cstates
 
+    # ------------------------------------------------------------------ sparse-attention indexer
+    # one sequence of 65,536 tokens (the largest supported), 4 query heads and a key head of
+    # 128, budget 512 blocks: normalise/rotate, block scores, top-K and expansion
+    qsa_obj = None
+    if not args.no_qsa:
+        nq = 65536
+        qi = wl.qsa_inputs(nq, "bf16", seed=2)
+        iq = wl.to_torch(qi["q"], dev, "bf16")
+        ik = wl.to_torch(qi["k"], dev, "bf16")
+        del qi
+        qws = torch.empty(gdn.gdn_qsa_workspace_bytes(nq), dtype=torch.uint8, device=dev)
+
+        def run_qsa():
+            return gdn.gdn_qsa_index(iq, ik, block_budget=512, want_blocks=False, workspace=qws)
+
+        for _ in range(2):
+            run_qsa()
+        times = []
+        for _ in range(5):
+            cache_flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_qsa()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        qms = float(np.median(times))
+        nbq = nq // 4
+        pairs = sum(min((i + 1) // 4, nbq) for i in range(nq))       # causal (query, block)
+        qflops = pairs * 4 * 128 * 2
+        # HBM bytes the method cannot avoid: inputs read, token lists written; the scores
+        # the kernels exchange (written once, read once) are the implementation's choice
+        qbytes = nq * 5 * 128 * 2 + nq * (4 * 512 + 3) * 4
+        qsa_obj = {"workload": "one sequence of %d tokens, 4 query heads, d=128, blocks of 4, "
+                               "budget 512 blocks" % nq,
+                   "ms_median": round(qms, 4), "queries_per_s": round(nq / (qms * 1e-3), 1),
+                   "score_flops": qflops,
+                   "score_TFLOPs": round(qflops / (qms * 1e-3) / 1e12, 2),
+                   "frac_of_bf16_peak": round(qflops / (qms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "score_bytes_written_and_read": 2 * pairs * 4,
+                   "algorithmic_bytes": qbytes,
+                   "kernels": "qsa_prep_kernel + qsa_score_kernel + qsa_topk_kernel"}
+        del iq, ik, qws
+
     # ------------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -533,6 +579,7 @@ def main():
         "layer_steps": layer,
         "backward": backward,
         "channel_gated": chan,
+        "qsa_indexer": qsa_obj,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

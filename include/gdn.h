@@ -158,6 +158,32 @@ gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const 
                              void *stream);
 
 /*
+ * The compressed block indexer of the reading notes' sparse attention (QSA, "The compressed
+ * lightweight indexer"), for one sequence of n tokens: 4 query heads and one shared key head
+ * of 128 dimensions (the projections are done by the caller), key blocks of 4 tokens.
+ *   q_i^h = PRoPE(RMSNorm(q_i^h), i),  kb_b = PRoPE(RMSNorm(mean of keys 4b .. 4b+3), 4b)
+ *   I_ib  = sum_h ReLU(<q_i^h, kb_b>) over the blocks complete before i (4b + 3 <= i)
+ *   the block_budget highest-scoring blocks (ties to the lower index; all complete blocks
+ *   when there are fewer), expanded to their tokens and joined with the tail of the current
+ *   block, {floor((i+1)/4) 4 .. i}.
+ * Readings of what the notes leave open: RMSNorm(x) = x / sqrt(mean(x^2) + 1e-6) without a
+ * scale; PRoPE rotates dims (m, m + 32), m < 32, by pos * 10000^(-2m/64) and passes dims
+ * 64..127.
+ *   q          [n, 4, 128] dtype (16-byte aligned);  k  [n, 128] dtype (16-byte aligned)
+ *   blocks     [n, block_budget] int32 or NULL: selected blocks, ascending, -1 padded
+ *   tokens     [n, 4 block_budget + 3] int32 or NULL: the selected tokens, ascending (the
+ *              blocks' tokens, then the tail), -1 padded.  At least one output is required.
+ *   workspace  gdn_qsa_workspace_bytes(n) bytes (holds the n x n/4 fp32 scores)
+ * n <= 65536 (GDN_ERR_UNSUPPORTED beyond); the notes' budget is block_budget = 512 (2048
+ * tokens).  The scores use bf16 products of the normalised, rotated vectors with fp32
+ * accumulation.
+ */
+size_t gdn_qsa_workspace_bytes(int64_t n);
+gdn_status gdn_qsa_index(const void *q, const void *k, int64_t n, int32_t dtype,
+                         int32_t block_budget, int32_t *blocks, int32_t *tokens,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Chunked backward (training) of gdn_prefill.
  *
  * For the scalar L = sum <dy, y> + sum <d_final_state, S_T> of the prefill with the same

@@ -324,6 +324,52 @@ gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const 
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_qsa_workspace_bytes(int64_t n)
+{
+    if (n <= 0 || n > gdn::qsa_max_tokens()) return 0;
+    return gdn::qsa_workspace_bytes(n);
+}
+
+gdn_status gdn_qsa_index(const void *q, const void *k, int64_t n, int32_t dtype,
+                         int32_t block_budget, int32_t *blocks, int32_t *tokens,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (n <= 0 || block_budget <= 0) return GDN_ERR_INVALID_ARGUMENT;
+    if (n > gdn::qsa_max_tokens()) return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !workspace || (!blocks && !tokens)) return GDN_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(workspace, 16) ||
+        (blocks && !aligned(blocks, 4)) || (tokens && !aligned(tokens, 4)))
+        return GDN_ERR_INVALID_ARGUMENT;
+    const size_t need = gdn::qsa_workspace_bytes(n);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    const size_t e = esize(dtype);
+    const size_t n_q = (size_t)n * 4 * 128 * e, n_k = (size_t)n * 128 * e;
+    const size_t n_b = (size_t)n * block_budget * 4;
+    const size_t n_t = (size_t)n * ((size_t)block_budget * 4 + 3) * 4;
+    struct Span { const void *p; size_t n; };
+    const Span ins[] = {{q, n_q}, {k, n_k}};
+    const Span outs[] = {{blocks, blocks ? n_b : 0}, {tokens, tokens ? n_t : 0},
+                         {workspace, need}};
+    for (int i = 0; i < 3; ++i) {
+        for (const Span &in : ins)
+            if (overlap(outs[i].p, outs[i].n, in.p, in.n)) return GDN_ERR_INVALID_ARGUMENT;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return GDN_ERR_INVALID_ARGUMENT;
+    }
+    gdn::QsaProblem p;
+    p.q = q;
+    p.k = k;
+    p.n = n;
+    p.dtype = dtype;
+    p.block_budget = block_budget;
+    p.blocks = blocks;
+    p.tokens = tokens;
+    hipError_t err = gdn::launch_qsa(p, workspace, (hipStream_t)stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
                            const float *beta, float *state, void *y, int32_t B, int32_t H,
                            int32_t d_k, int32_t d_v, int32_t dtype, void *stream)

@@ -75,6 +75,17 @@ struct ChannelProblem {
 };
 hipError_t launch_channel_gated(const ChannelProblem &c, hipStream_t stream);
 
+// Sparse-attention block indexer (4 query heads, one 128-dim key head, blocks of 4 tokens).
+struct QsaProblem {
+    const void *q, *k;          // [n, 4, 128], [n, 128] dtype
+    long long n;
+    int dtype, block_budget;
+    int32_t *blocks, *tokens;   // [n, budget], [n, 4 budget + 3] or null
+};
+size_t qsa_workspace_bytes(long long n);
+long long qsa_max_tokens();
+hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream);
+
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *alpha,
                          const float *beta, float *state, void *y, int B, int H, int dk,
                          int dv, int dtype, hipStream_t stream);

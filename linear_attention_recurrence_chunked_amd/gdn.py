@@ -70,6 +70,10 @@ def load(path: Optional[str] = None):
     lib.gdn_channel_gated.restype = i32
     lib.gdn_channel_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                       i32, vp, vp, vp]
+    lib.gdn_qsa_workspace_bytes.restype = sz
+    lib.gdn_qsa_workspace_bytes.argtypes = [i64]
+    lib.gdn_qsa_index.restype = i32
+    lib.gdn_qsa_index.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
     lib.gdn_decode_step.restype = i32
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.gdn_short_conv.restype = i32
@@ -234,6 +238,32 @@ def gdn_channel_gated(q, k, v, decay, erase, write, initial_state=None, cu_seqle
                                   _stream(stream))
     _check("gdn_channel_gated", st)
     return y, final_state
+
+
+def gdn_qsa_workspace_bytes(n: int) -> int:
+    return int(load().gdn_qsa_workspace_bytes(n))
+
+
+def gdn_qsa_index(q, k, block_budget: int = 512, want_blocks: bool = True,
+                  want_tokens: bool = True, workspace=None, stream=None):
+    """Sparse-attention block indexer for one sequence: q [n, 4, 128], k [n, 128]
+    (bf16 or fp32).  Returns (blocks [n, budget] int32 or None, tokens [n, 4 budget + 3]
+    int32 or None), both ascending and -1 padded."""
+    import torch
+    n = q.shape[0]
+    blocks = torch.empty((n, block_budget), dtype=torch.int32, device=q.device) \
+        if want_blocks else None
+    tokens = torch.empty((n, 4 * block_budget + 3), dtype=torch.int32, device=q.device) \
+        if want_tokens else None
+    if workspace is None:
+        workspace = torch.empty(max(gdn_qsa_workspace_bytes(n), 16), dtype=torch.uint8,
+                                device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = load().gdn_qsa_index(_ptr(q), _ptr(k), n, _dtype_code(q), block_budget,
+                              _ptr(blocks), _ptr(tokens), _ptr(workspace), wbytes,
+                              _stream(stream))
+    _check("gdn_qsa_index", st)
+    return blocks, tokens
 
 
 def gdn_decode_step(q, k, v, alpha, beta, state, y=None, stream=None):

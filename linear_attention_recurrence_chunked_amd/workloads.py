@@ -19,7 +19,9 @@ Recipe (shared by every workload):
 * for the backward: the output adjoint dy ~ N(0, 1) in the storage dtype, and an optional
   final-state adjoint ~ N(0, sd) fp32 per (sequence, head);
 * for the channel-wise gated variants: a decay per key channel sigmoid(N(mu_a, sd_a)) and
-  erase and write gates per value channel sigmoid(N(mu_b, sd_b)), fp32.
+  erase and write gates per value channel sigmoid(N(mu_b, sd_b)), fp32;
+* for the sparse-attention indexer: projected queries [n, 4, 128] and keys [n, 128], N(0, 1)
+  in the storage dtype.
 
 bf16 tensors are handled as ``uint16`` bit patterns on the numpy side and viewed as
 ``torch.bfloat16`` when moved to the GPU.
@@ -34,7 +36,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 BLOCK_ROWS = 65536
-T_Q, T_K, T_V, T_ALPHA, T_BETA, T_S0, T_LENS, T_DY, T_DSF, T_CA, T_CB, T_CW = range(12)
+T_Q, T_K, T_V, T_ALPHA, T_BETA, T_S0, T_LENS, T_DY, T_DSF, T_CA, T_CB, T_CW, T_IQ, T_IK = range(14)
 
 
 @dataclass(frozen=True)
@@ -213,6 +215,15 @@ def channel_gates(inp: dict, a=(3.0, 1.0), b=(0.0, 1.0), seed: int = 0) -> dict:
         return out
 
     return dict(decay=draw(T_CA, dk, *a), erase=draw(T_CB, dv, *b), write=draw(T_CW, dv, *b))
+
+
+def qsa_inputs(n: int, dtype: str = "bf16", seed: int = 0) -> dict:
+    """Indexer inputs for one sequence of n tokens: q [n, 4, 128], k [n, 128]."""
+    q = np.empty((n, 4, 128), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    k = np.empty((n, 128), dtype=q.dtype)
+    _fill(q, seed, T_IQ, lambda rng, m: _store(rng.standard_normal((m, 4, 128)), dtype))
+    _fill(k, seed, T_IK, lambda rng, m: _store(rng.standard_normal((m, 128)), dtype))
+    return dict(q=q, k=k, n=n, dtype=dtype)
 
 
 def workload_inputs(w: Workload) -> dict:

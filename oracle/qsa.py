@@ -69,6 +69,8 @@ def prepare(q, k, r=R):
     n = q.shape[0]
     nb = n // r
     qr = rope(rmsnorm(q), np.arange(n)[:, None] * np.ones(q.shape[1]))
+    if nb == 0:                      # no complete block: nothing to pool
+        return qr, np.zeros((0, k.shape[1]))
     pooled = k[:nb * r].reshape(nb, r, -1).mean(axis=1)
     kb = rope(rmsnorm(pooled), np.arange(nb) * r)
     return qr, kb

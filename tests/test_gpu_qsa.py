@@ -1,0 +1,106 @@
+"""GPU parity of gdn_qsa_index (the sparse-attention block indexer) against the fp64 oracle.
+
+The selection is integer output decided by floating-point scores.  The kernel scores with
+bf16 products of the normalised, rotated vectors, the oracle in fp64, so near the selection
+threshold the two may order blocks differently.  The checks: everything that is unique is
+exact (the count, order, range and padding of the blocks, their expansion to tokens and the
+tail); the selection is a valid top-K under the oracle's scores within the kernel's rounding
+bound E_ib = 2^-8 sum_h |q_i^h| . |kb_b| (both operands rounded to bf16, each by at most
+2^-9 relative); and where all scores are exactly equal (zero keys) the tie-break is exact.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def run(inp, dev, kb):
+    from linear_attention_recurrence_chunked_amd import gdn
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    q = wl.to_torch(inp["q"], dev, inp["dtype"])
+    k = wl.to_torch(inp["k"], dev, inp["dtype"])
+    b, t = gdn.gdn_qsa_index(q, k, block_budget=kb)
+    torch.cuda.synchronize()
+    return b.cpu().numpy().astype(np.int64), t.cpu().numpy().astype(np.int64)
+
+
+def check_rows(inp, blocks, tokens, kb, rows, label):
+    from oracle import qsa
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    n = inp["n"]
+    q = wl.as_f64(inp["q"], inp["dtype"])
+    k = wl.as_f64(inp["k"], inp["dtype"])
+    qr, kbk = qsa.prepare(q, k)
+    nb = n // 4
+    W = 4 * kb + 3
+    exact = 0
+    worst_margin = np.inf
+    for i in rows:
+        nvalid = min((i + 1) // 4, nb)
+        sel = blocks[i][blocks[i] >= 0]
+        nsel = min(kb, nvalid)
+        assert len(sel) == nsel, (label, i, len(sel), nsel)
+        assert np.all(blocks[i][nsel:] == -1)
+        assert np.all(np.diff(sel) > 0) and (nsel == 0 or sel[-1] < nvalid)
+        toks = (sel[:, None] * 4 + np.arange(4)[None, :]).reshape(-1)
+        want = np.concatenate([toks, np.arange(((i + 1) // 4) * 4, i + 1)])
+        assert np.array_equal(tokens[i][:len(want)], want), (label, i)
+        assert np.all(tokens[i][len(want):W] == -1)
+        if nvalid > kb:
+            d = np.einsum("hd,bd->hb", qr[i], kbk[:nvalid])
+            I = np.maximum(d, 0).sum(axis=0)
+            E = 2.0 ** -8 * np.einsum("hd,bd->b", np.abs(qr[i]), np.abs(kbk[:nvalid]))
+            rest = np.setdiff1d(np.arange(nvalid), sel)
+            margin = (I[sel] + E[sel]).min() - (I[rest] - E[rest]).max()
+            worst_margin = min(worst_margin, margin)
+            assert margin >= 0, (label, i, margin)
+            order = np.lexsort((np.arange(nvalid), -I))
+            exact += np.array_equal(np.sort(order[:kb]), sel)
+        else:
+            exact += 1
+    say("    %s: %d rows, %d equal to the oracle's selection, worst margin %.3g" % (
+        label, len(rows), exact, worst_margin))
+
+
+@pytest.mark.parametrize("n,kb,dtype", [(1000, 16, "bf16"), (1027, 64, "f32"), (3, 4, "bf16"),
+                                        (258, 1000, "bf16"), (513, 1, "bf16")])
+def test_qsa_against_oracle(dev, n, kb, dtype):
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = wl.qsa_inputs(n, dtype, seed=n)
+    say("[gpu] qsa n=%d budget=%d %s" % (n, kb, dtype))
+    blocks, tokens = run(inp, dev, kb)
+    check_rows(inp, blocks, tokens, kb, range(n), "n=%d" % n)
+
+
+def test_qsa_zero_keys_take_the_lowest_blocks(dev):
+    """Zero keys make every score exactly 0 on both sides: the budget goes to blocks 0.."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = wl.qsa_inputs(400, "bf16", seed=7)
+    inp["k"][:] = 0
+    blocks, tokens = run(inp, dev, 8)
+    for i in range(400):
+        nvalid = (i + 1) // 4
+        want = np.arange(min(8, nvalid))
+        assert np.array_equal(blocks[i][:len(want)], want), i
+
+
+def test_qsa_full_budget_at_the_largest_size(dev):
+    """n = 65536 tokens (16,384 blocks), the notes' budget of 512 blocks: sampled rows."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    n = 65536
+    inp = wl.qsa_inputs(n, "bf16", seed=11)
+    say("[gpu] qsa n=%d budget=512" % n)
+    blocks, tokens = run(inp, dev, 512)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 3, 2047, 2048, 2051, n - 1] + list(rng.integers(0, n, 40))))
+    check_rows(inp, blocks, tokens, 512, rows, "n=65536 sampled")
