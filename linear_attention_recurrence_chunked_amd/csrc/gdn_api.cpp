@@ -336,7 +336,7 @@ gdn_status gdn_qsa_index(const void *q, const void *k, int64_t n, int32_t dtype,
 {
     if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
     if (n <= 0 || block_budget <= 0) return GDN_ERR_INVALID_ARGUMENT;
-    if (n > gdn::qsa_max_tokens()) return GDN_ERR_UNSUPPORTED;
+    if (n > gdn::qsa_max_tokens() || block_budget > (1 << 24)) return GDN_ERR_UNSUPPORTED;
     if (!q || !k || !workspace || (!blocks && !tokens)) return GDN_ERR_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(workspace, 16) ||
         (blocks && !aligned(blocks, 4)) || (tokens && !aligned(tokens, 4)))

@@ -278,3 +278,43 @@ def test_backward_workspace_query(lib):
 ])
 def test_backward_rejects(lib, kw, code):
     assert backward(lib, **kw) == code
+
+
+def qsa(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, n=4096, dt=gdn.GDN_DTYPE_BF16, kb=512, blocks=3 * G,
+             tokens=4 * G, ws=5 * G, wsb=1 << 31, stream=None)
+    a.update(kw)
+    return lib.gdn_qsa_index(a["q"], a["k"], a["n"], a["dt"], a["kb"], a["blocks"],
+                             a["tokens"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_qsa_workspace_query():
+    # bf16 normalised queries [n, 4, 128], block keys [n/4, 128], fp32 scores [n, n/4],
+    # each region rounded up to 256 bytes
+    al = lambda x: (x + 255) // 256 * 256
+    n = 4096
+    assert gdn.gdn_qsa_workspace_bytes(n) == al(n * 4 * 128 * 2) + al(n // 4 * 128 * 2) + \
+        al(n * (n // 4) * 4)
+    assert gdn.gdn_qsa_workspace_bytes(3) == al(3 * 4 * 128 * 2) + al(128 * 2) + al(3 * 4)
+    assert gdn.gdn_qsa_workspace_bytes(0) == 0
+    assert gdn.gdn_qsa_workspace_bytes(65537) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(n=65537), gdn.GDN_ERR_UNSUPPORTED),             # beyond 16,384 blocks
+    (dict(kb=(1 << 24) + 1), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(n=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(kb=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(blocks=None, tokens=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(k=2 * G + 8), gdn.GDN_ERR_INVALID_ARGUMENT),     # 16-byte alignment
+    (dict(tokens=4 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(blocks=1 * G + 4096), gdn.GDN_ERR_INVALID_ARGUMENT),   # blocks over q
+    (dict(tokens=3 * G + 1024), gdn.GDN_ERR_INVALID_ARGUMENT),   # tokens over blocks
+    (dict(ws=4 * G + 4096), gdn.GDN_ERR_INVALID_ARGUMENT),       # workspace over tokens
+    (dict(wsb=1 << 20), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_qsa_rejects(lib, kw, code):
+    assert qsa(lib, **kw) == code
