@@ -15,17 +15,21 @@
 //   qsa_prep_kernel   one wave per query row (token, head) or per key block: normalise,
 //                     rotate (angles and their sines in fp64: positions reach 10^5 radians),
 //                     store bf16.
-//   qsa_score_kernel  16 queries x 64 blocks per workgroup on 16x16x32 bf16 MFMAs: the four
-//                     heads of a query are four consecutive accumulator rows, i.e. the four
-//                     values one lane holds, so the ReLU head-sum needs no exchange; tiles
-//                     entirely after their queries' causal limit are skipped.
-//   qsa_topk_kernel   one workgroup per query: the row's scores in LDS, a radix select of
-//                     the K_B-th largest in three passes of 11, 11 and 10 bits (scores are
-//                     sums of ReLUs, so their bit patterns order like the values; 11-bit
-//                     first digits keep scores of one magnitude from crowding a few bins;
-//                     the digit holding the rank is found over a scan of the histogram),
-//                     ties at the threshold taken in index order, then the ascending block
-//                     list and the expanded token list.
+//   qsa_score_kernel  16 queries per workgroup against all their visible blocks on 16x16x32
+//                     bf16 MFMAs, the queries' fragments held in registers and the block
+//                     keys streamed from L2 one 16-block tile ahead: the four heads of a
+//                     query are four consecutive accumulator rows, i.e. the four values one
+//                     lane holds, so the ReLU head-sum needs no exchange.
+//   qsa_topk_kernel   one workgroup per query: the row's scores in LDS (16-byte loads, eight
+//                     in flight); a 2,048-bin histogram of a digit linear in the score up to
+//                     the row maximum (scores of one magnitude spread over many bins) and a
+//                     scan over it find the bin holding the K_B-th largest score; the scores in
+//                     that bin (a few dozen, typically) are ranked pairwise to find it exactly,
+//                     or, in a crowded bin, by a radix select on 11, 11 and 10 bits of their
+//                     patterns (scores are sums of ReLUs, so their bit patterns order like the
+//                     values).  Ties at the threshold are taken in index order; each wave
+//                     places its range's selected blocks, ascending, by a packed prefix sum of
+//                     (greater, equal) counts, with their tokens, then the tail and padding.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -36,7 +40,6 @@ constexpr int kQH = 4;          // query heads
 constexpr int kQD = 128;        // head dimension
 constexpr int kQR = 4;          // tokens per key block
 constexpr float kQEps = 1e-6f;
-constexpr int kLQ = kQD + 8;    // bf16 LDS row stride
 
 struct QsaArgs {
     const void *q, *k;
@@ -44,7 +47,8 @@ struct QsaArgs {
     int kb;                     // block budget
     uint16_t *qr;               // [n, 4, 128] bf16
     uint16_t *kbk;              // [nb, 128] bf16
-    float *scores;              // [n, nb]
+    float *scores;              // [n, ld]
+    long long ld;               // score row stride: nb rounded up to 4 (16-byte rows)
     int32_t *blocks;            // [n, kb] or null
     int32_t *tokens;            // [n, kb * 4 + 3] or null
 };
@@ -100,52 +104,70 @@ __global__ __launch_bounds__(256) void qsa_prep_kernel(QsaArgs a)
     }
 }
 
-// 16 queries (64 rows of qr) x 64 blocks; wave w takes blocks 16 w .. 16 w + 15.
+// 16 queries (64 rows of qr, token-major, head-minor) against every block visible to the
+// last of them, in tiles of 16 blocks; wave w takes tiles w, w + 4, ...  The queries'
+// MFMA fragments stay in registers for the whole row; the block keys (at most 4 MB, resident
+// in L2) stream in one tile ahead.  Query tiles run last-first: the longest rows start first.
 __global__ __launch_bounds__(256) void qsa_score_kernel(QsaArgs a)
 {
-    __shared__ __align__(16) uint16_t sA[64 * kLQ];
-    __shared__ __align__(16) uint16_t sB[64 * kLQ];
     const long long nb = a.n / kQR;
-    const long long btiles = (nb + 63) / 64;
-    const long long qt = blockIdx.x / btiles, bt = blockIdx.x % btiles;
-    const long long i0 = qt * 16, b0 = bt * 64;
-    // the tile's earliest block must be complete before its last query
-    if (b0 * kQR + kQR - 1 > i0 + 15) return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int p = tid; p < 64 * kQD / 8; p += 256) {
-        const int r = p / (kQD / 8), c = 8 * (p % (kQD / 8));
-        u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-        if (i0 * kQH + r < a.n * kQH) xa = *(const u32x4 *)(a.qr + (i0 * kQH + r) * kQD + c);
-        if (b0 + r < nb) xb = *(const u32x4 *)(a.kbk + (b0 + r) * kQD + c);
-        *(u32x4 *)(sA + r * kLQ + c) = xa;
-        *(u32x4 *)(sB + r * kLQ + c) = xb;
-    }
-    __syncthreads();
-    const int r = lane & 15, g = lane >> 4;
-    f32x4 acc[4];
+    const long long qtiles = (a.n + 15) / 16;
+    const long long i0 = (qtiles - 1 - (long long)blockIdx.x) * 16;
+    const long long ilast = i0 + 15 < a.n - 1 ? i0 + 15 : a.n - 1;
+    const long long nvis = (ilast + 1) / kQR < nb ? (ilast + 1) / kQR : nb;
+    const int ntiles = (int)((nvis + 15) / 16);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    if (wave >= ntiles) return;               // no barriers below
+    // A fragments: tile t holds rows 16 t .. 16 t + 15 (tokens i0 + 4 t .. i0 + 4 t + 3)
+    bf16x8 fa[4][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) {
+        const long long qrow = i0 * kQH + 16 * t + r;
 #pragma unroll
-    for (int k0 = 0; k0 < kQD; k0 += 32) {
-        const bf16x8 fb = *(const bf16x8 *)(sB + (16 * wave + r) * kLQ + k0 + 8 * g);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bf16x8 fa = *(const bf16x8 *)(sA + (16 * t + r) * kLQ + k0 + 8 * g);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[t], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow < a.n * kQH) x = *(const u32x4 *)(a.qr + qrow * kQD + 32 * kk + 8 * g);
+            fa[t][kk] = __builtin_bit_cast(bf16x8, x);
         }
     }
-    // tile t, lane (r, g): rows 16 t + 4 g + h (query 4 t + g, head h), block column r
-    const long long b = b0 + 16 * wave + r;
-    if (b < nb) {
+    u32x4 fb[4], fn[4];
+    auto load_b = [&](int tile, u32x4 (&f)[4]) {
+        const long long b = (long long)tile * 16 + r;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const long long i = i0 + 4 * t + g;
-            if (i < a.n) {
-                const float sc = fmaxf(acc[t][0], 0.f) + fmaxf(acc[t][1], 0.f) +
-                                 fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f);
-                a.scores[i * nb + b] = sc;
+        for (int kk = 0; kk < 4; ++kk) {
+            f[kk] = u32x4{0u, 0u, 0u, 0u};
+            if (b < nb) f[kk] = *(const u32x4 *)(a.kbk + b * kQD + 32 * kk + 8 * g);
+        }
+    };
+    load_b(wave, fb);
+#pragma unroll 1
+    for (int tile = wave; tile < ntiles; tile += 4) {
+        if (tile + 4 < ntiles) load_b(tile + 4, fn);
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 b8 = __builtin_bit_cast(bf16x8, fb[kk]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t][kk], b8, acc[t], 0, 0, 0);
+        }
+        // tile t, lane (r, g): rows 16 t + 4 g + h (token i0 + 4 t + g, head h), block r
+        const long long b = (long long)tile * 16 + r;
+        if (b < nb) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const long long i = i0 + 4 * t + g;
+                if (i < a.n) {
+                    const float sc = fmaxf(acc[t][0], 0.f) + fmaxf(acc[t][1], 0.f) +
+                                     fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f);
+                    a.scores[i * a.ld + b] = sc;
+                }
             }
         }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) fb[kk] = fn[kk];
     }
 }
 
@@ -169,49 +191,101 @@ __device__ __forceinline__ int block_excl_scan(int x, int *tmp)
 
 constexpr int kMaxRow = 16384;  // blocks per row held in LDS (n <= 65536)
 
+// First radix digit: the score scaled linearly onto 2,048 bins by the row maximum.  Monotone
+// in the score (one rounded multiply, then a floor), so ordering by (digit, bit pattern)
+// orders like the scores, and scores of one magnitude spread over many bins.
+__device__ __forceinline__ uint32_t lin_digit(uint32_t x, float s)
+{
+    const float v = __uint_as_float(x) * s;
+    return v < 2047.f ? (uint32_t)v : 2047u;
+}
+
+// inclusive prefix sum over the wave's lanes
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(v, m, kWave);
+        if (lane >= m) v += o;
+    }
+    return v;
+}
+
+constexpr int kCand = 256;      // a threshold bin this small is resolved by pairwise ranks
+
+// One workgroup per query, longest rows first.
 __global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
 {
-    __shared__ uint32_t row[kMaxRow];
+    __shared__ __align__(16) uint32_t row[kMaxRow];
     __shared__ int hist[2048];
+    __shared__ uint32_t cx[kCand];
+    __shared__ int cb[kCand];
     __shared__ int tmp[8];
-    __shared__ uint32_t sh_prefix, sh_need;
-    const long long i = blockIdx.x;
+    __shared__ int wgt[4], weq[4];
+    __shared__ float wmax[4];
+    __shared__ uint32_t sh_prefix, sh_need, sh_c1;
+    __shared__ int sh_cnt, sh_fill;
+    const long long i = a.n - 1 - (long long)blockIdx.x;
     const long long nb = a.n / kQR;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nvalid = (int)((i + 1) / kQR < nb ? (i + 1) / kQR : nb);
     const int KB = a.kb;
-    const int chunk = (nvalid + 255) / 256;
-    const int lo = tid * chunk, hi = lo + chunk < nvalid ? lo + chunk : nvalid;
+    const bool all = nvalid <= KB;            // uniform over the workgroup
+    const int n4 = (nvalid + 3) >> 2;
+    const u32x4 *row4 = (const u32x4 *)row;
 
-    uint32_t tau = 0;         // the K_B-th largest bit pattern (only when nvalid > KB)
-    int need_eq = 0;          // elements equal to tau to take, in index order
-    const bool all = nvalid <= KB;
+    uint32_t tau = 0;         // the bit pattern of the K_B-th largest score (when !all)
+    int need_eq = 0;          // how many scores equal to tau are taken, in index order
     if (!all) {
-        for (int b = tid; b < nvalid; b += 256) row[b] = __float_as_uint(a.scores[i * nb + b]);
+        // the row's visible scores into LDS: 16-byte loads, eight in flight per thread
+        const u32x4 *src = (const u32x4 *)(a.scores + i * a.ld);
+        float mx = 0.f;
+#pragma unroll 1
+        for (int c0 = 0; c0 < n4; c0 += 8 * 256) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * 256 + tid;
+                v[u] = u32x4{0u, 0u, 0u, 0u};
+                if (c < n4) v[u] = src[c];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * 256 + tid;
+                if (c < n4) {
+                    *(u32x4 *)(row + 4 * c) = v[u];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * c + e < nvalid) mx = fmaxf(mx, __uint_as_float(v[u][e]));
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+        if (lane == 0) wmax[wave] = mx;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hist[8 * tid + j] = 0;
         if (tid == 0) {
             sh_prefix = 0;
             sh_need = (uint32_t)KB;
+            sh_fill = 0;
         }
         __syncthreads();
-        // three passes (bits 31..21, 20..10, 9..0): 11-bit first digits spread scores of one
-        // magnitude over many bins; find the digit holding the remaining rank
-#pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-            const int bits = pass == 2 ? 10 : 11;
-            const uint32_t dmask = (1u << bits) - 1;
-            const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (shift + bits));
+        mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        const float s = mx > 0.f ? fminf(2047.f / mx, 1e30f) : 0.f;
+        // first digit: linear in the score
+#pragma unroll 2
+        for (int c = tid; c < n4; c += 256) {
+            const u32x4 x = row4[c];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hist[8 * tid + j] = 0;
-            __syncthreads();
-            const uint32_t pre = sh_prefix;
-            for (int b = tid; b < nvalid; b += 256) {
-                const uint32_t x = row[b];
-                if ((x & mask) == pre) atomicAdd(&hist[(x >> shift) & dmask], 1);
-            }
-            __syncthreads();
-            // thread t looks at digits 2047 - 8t - j (descending); gt = how many matching
-            // values have a larger digit; the digit where the remaining rank falls is unique
+            for (int e = 0; e < 4; ++e)
+                if (4 * c + e < nvalid) atomicAdd(&hist[lin_digit(x[e], s)], 1);
+        }
+        __syncthreads();
+        // thread t looks at digits 2047 - 8t - j (descending); gt = how many values have a
+        // larger digit; the digit where the rank falls is unique
+        {
             int c[8], tot = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -223,79 +297,195 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if ((uint32_t)gt < need && (uint32_t)(gt + c[j]) >= need) {
-                    sh_prefix = pre | ((uint32_t)(2047 - 8 * tid - j) << shift);
+                    sh_c1 = (uint32_t)(2047 - 8 * tid - j);
                     sh_need = need - (uint32_t)gt;
+                    sh_cnt = c[j];
                 }
                 gt += c[j];
             }
             __syncthreads();
         }
-        tau = sh_prefix;
-        need_eq = (int)sh_need;      // how many of the elements equal to tau are taken
-    }
-    // selection flags in index order: chunk per thread, prefix counts of equals and of takes
-    int eq = 0;
-    if (!all)
-        for (int b = lo; b < hi; ++b) eq += row[b] == tau;
-    const int eq_before = all ? 0 : block_excl_scan(eq, tmp);
-    int take = 0;
-    {
-        int e = eq_before;
-        for (int b = lo; b < hi; ++b) {
-            bool t = all;
-            if (!all) {
-                const uint32_t x = row[b];
-                t = x > tau || (x == tau && e < need_eq);
-                e += x == tau;
-            }
-            take += t;
-        }
-    }
-    const int pos0 = block_excl_scan(take, tmp);
-    const int W = KB * kQR + kQR - 1;
-    const int nsel = all ? nvalid : KB;
-    // write the selected blocks and their tokens in ascending order
-    {
-        int e = eq_before, pos = pos0;
-        for (int b = lo; b < hi; ++b) {
-            bool t = all;
-            if (!all) {
-                const uint32_t x = row[b];
-                t = x > tau || (x == tau && e < need_eq);
-                e += x == tau;
-            }
-            if (t) {
-                if (a.blocks) a.blocks[i * KB + pos] = b;
-                if (a.tokens) {
-                    int32_t *tk = a.tokens + i * W + kQR * pos;
+        const uint32_t c1 = sh_c1, need = sh_need;
+        const int cnt = sh_cnt;
+        if (cnt <= kCand) {
+            // gather the bin's scores; the one whose rank among them holds `need` (the first
+            // in index order among equals) is the threshold
+#pragma unroll 2
+            for (int c = tid; c < n4; c += 256) {
+                const u32x4 x = row4[c];
 #pragma unroll
-                    for (int u = 0; u < kQR; ++u) tk[u] = kQR * b + u;
+                for (int e = 0; e < 4; ++e)
+                    if (4 * c + e < nvalid && lin_digit(x[e], s) == c1) {
+                        const int slot = atomicAdd(&sh_fill, 1);
+                        cx[slot] = x[e];
+                        cb[slot] = 4 * c + e;
+                    }
+            }
+            __syncthreads();
+            if (tid < cnt) {
+                const uint32_t xj = cx[tid];
+                const int bj = cb[tid];
+                int above = 0, same = 0, same_first = 1;
+                for (int k = 0; k < cnt; ++k) {
+                    const uint32_t xk = cx[k];
+                    above += xk > xj;
+                    same += xk == xj;
+                    if (xk == xj && cb[k] < bj) same_first = 0;
                 }
-                ++pos;
+                if (same_first && (uint32_t)above < need && need <= (uint32_t)(above + same)) {
+                    sh_prefix = xj;
+                    sh_need = need - (uint32_t)above;
+                }
+            }
+            __syncthreads();
+        } else {
+            // a crowded bin (many equal scores): bits 31..21, 20..10, 9..0 of its scores
+#pragma unroll 1
+            for (int pass = 0; pass < 3; ++pass) {
+                const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+                const int bits = pass == 2 ? 10 : 11;
+                const uint32_t dmask = (1u << bits) - 1;
+                const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (shift + bits));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) hist[8 * tid + j] = 0;
+                __syncthreads();
+                const uint32_t pre = sh_prefix;
+                for (int b = tid; b < nvalid; b += 256) {
+                    const uint32_t x = row[b];
+                    if (lin_digit(x, s) == c1 && (x & mask) == pre)
+                        atomicAdd(&hist[(x >> shift) & dmask], 1);
+                }
+                __syncthreads();
+                int c[8], tot = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    c[j] = hist[2047 - 8 * tid - j];
+                    tot += c[j];
+                }
+                const uint32_t nd = sh_need;
+                int gt = block_excl_scan(tot, tmp);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if ((uint32_t)gt < nd && (uint32_t)(gt + c[j]) >= nd) {
+                        sh_prefix = pre | ((uint32_t)(2047 - 8 * tid - j) << shift);
+                        sh_need = nd - (uint32_t)gt;
+                    }
+                    gt += c[j];
+                }
+                __syncthreads();
             }
         }
+        tau = sh_prefix;
+        need_eq = (int)sh_need;
+    }
+
+    // selection in index order: wave w takes a contiguous range of the row (a multiple of
+    // 256 blocks), lane l the four blocks 4 l .. 4 l + 3 of each 256-block step; a packed
+    // prefix sum over the lanes of (greater, equal) counts places every taken block
+    const int per = ((nvalid + 1023) / 1024) * 256;
+    const int lo = wave * per, hi = lo + per < nvalid ? lo + per : nvalid;
+    if (!all) {
+        int g = 0, q = 0;
+        for (int b0 = lo; b0 < hi; b0 += 256) {
+            const int b = b0 + 4 * lane;
+            if (b < hi) {
+                const u32x4 x = *(const u32x4 *)(row + b);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (b + e < hi) {
+                        g += x[e] > tau;
+                        q += x[e] == tau;
+                    }
+            }
+        }
+        const int tot = __shfl(wave_incl_scan((g << 16) | q), kWave - 1, kWave);
+        if (lane == 0) {
+            wgt[wave] = tot >> 16;
+            weq[wave] = tot & 0xffff;
+        }
+    }
+    __syncthreads();
+    int pos = lo, e = 0;
+    if (!all) {
+        pos = 0;
+        for (int w = 0; w < wave; ++w) {
+            const int left = need_eq - e;
+            pos += wgt[w] + (left <= 0 ? 0 : left < weq[w] ? left : weq[w]);
+            e += weq[w];
+        }
+    }
+    const int W = KB * kQR + kQR - 1;
+    int32_t *blk = a.blocks ? a.blocks + i * KB : nullptr;
+    int32_t *tok = a.tokens ? a.tokens + i * W : nullptr;
+    for (int b0 = lo; b0 < hi; b0 += 256) {
+        const int b = b0 + 4 * lane;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        int g = 0, q = 0;
+        if (b < hi) {
+            if (all) {
+                g = hi - b < 4 ? hi - b : 4;
+            } else {
+                x = *(const u32x4 *)(row + b);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (b + u < hi) {
+                        g += x[u] > tau;
+                        q += x[u] == tau;
+                    }
+            }
+        }
+        const int packed = (g << 16) | q;
+        const int incl = wave_incl_scan(packed);
+        const int tot = __shfl(incl, kWave - 1, kWave);
+        const int excl = incl - packed;
+        const int left = need_eq - e > 0 ? need_eq - e : 0;
+        int p = pos + (excl >> 16) + ((excl & 0xffff) < left ? (excl & 0xffff) : left);
+        int ee = e + (excl & 0xffff);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (b + u < hi) {
+                bool t = all;
+                if (!all) {
+                    t = x[u] > tau || (x[u] == tau && ee < need_eq);
+                    ee += x[u] == tau;
+                }
+                if (t) {
+                    if (blk) blk[p] = b + u;
+                    if (tok) {
+#pragma unroll
+                        for (int v = 0; v < kQR; ++v) tok[kQR * p + v] = kQR * (b + u) + v;
+                    }
+                    ++p;
+                }
+            }
+        }
+        pos += (tot >> 16) + ((tot & 0xffff) < left ? (tot & 0xffff) : left);
+        e += tot & 0xffff;
     }
     // padding, and the tail of the incomplete block after the selected tokens
-    if (a.blocks)
-        for (int p = nsel + tid; p < KB; p += 256) a.blocks[i * KB + p] = -1;
-    if (a.tokens) {
+    const int nsel = all ? nvalid : KB;
+    if (blk)
+        for (int p = nsel + tid; p < KB; p += 256) blk[p] = -1;
+    if (tok) {
         const long long tail0 = ((i + 1) / kQR) * kQR;
         const int ntail = (int)(i + 1 - tail0);
         for (int p = kQR * nsel + tid; p < W; p += 256) {
             const int u = p - kQR * nsel;
-            a.tokens[i * W + p] = u < ntail ? (int32_t)(tail0 + u) : -1;
+            tok[p] = u < ntail ? (int32_t)(tail0 + u) : -1;
         }
     }
 }
 
 }  // namespace
 
+static long long score_ld(long long nb) { return ((nb > 0 ? nb : 1) + 3) & ~3LL; }
+
 size_t qsa_workspace_bytes(long long n)
 {
     const long long nb = n / kQR;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return al((size_t)n * kQH * kQD * 2) + al((size_t)(nb > 0 ? nb : 1) * kQD * 2) +
-           al((size_t)n * (nb > 0 ? nb : 1) * 4);
+           al((size_t)n * score_ld(nb) * 4);
 }
 
 long long qsa_max_tokens() { return (long long)kMaxRow * kQR; }
@@ -314,6 +504,7 @@ hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
     a.kbk = (uint16_t *)(ws + al((size_t)p.n * kQH * kQD * 2));
     a.scores = (float *)(ws + al((size_t)p.n * kQH * kQD * 2) +
                          al((size_t)(nb > 0 ? nb : 1) * kQD * 2));
+    a.ld = score_ld(nb);
     a.blocks = p.blocks;
     a.tokens = p.tokens;
     const long long waves = p.n * kQH + nb;
@@ -323,8 +514,8 @@ hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
     else
         hipLaunchKernelGGL(qsa_prep_kernel<float>, dim3(prep_blocks), dim3(256), 0, stream, a);
     if (nb > 0) {
-        const long long grid = ((p.n + 15) / 16) * ((nb + 63) / 64);
-        hipLaunchKernelGGL(qsa_score_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(qsa_score_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0,
+                           stream, a);
     }
     hipLaunchKernelGGL(qsa_topk_kernel, dim3((unsigned)p.n), dim3(256), 0, stream, a);
     return hipGetLastError();

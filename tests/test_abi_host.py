@@ -289,13 +289,15 @@ def qsa(lib, **kw):
 
 
 def test_qsa_workspace_query():
-    # bf16 normalised queries [n, 4, 128], block keys [n/4, 128], fp32 scores [n, n/4],
-    # each region rounded up to 256 bytes
+    # bf16 normalised queries [n, 4, 128], block keys [n/4, 128], fp32 scores [n, ld] with
+    # ld = n/4 rounded up to 4; each region rounded up to 256 bytes
     al = lambda x: (x + 255) // 256 * 256
     n = 4096
     assert gdn.gdn_qsa_workspace_bytes(n) == al(n * 4 * 128 * 2) + al(n // 4 * 128 * 2) + \
         al(n * (n // 4) * 4)
-    assert gdn.gdn_qsa_workspace_bytes(3) == al(3 * 4 * 128 * 2) + al(128 * 2) + al(3 * 4)
+    assert gdn.gdn_qsa_workspace_bytes(1030) == al(1030 * 4 * 128 * 2) + al(257 * 128 * 2) + \
+        al(1030 * 260 * 4)
+    assert gdn.gdn_qsa_workspace_bytes(3) == al(3 * 4 * 128 * 2) + al(128 * 2) + al(3 * 4 * 4)
     assert gdn.gdn_qsa_workspace_bytes(0) == 0
     assert gdn.gdn_qsa_workspace_bytes(65537) == 0
 

@@ -83,15 +83,45 @@ def test_qsa_against_oracle(dev, n, kb, dtype):
 
 
 def test_qsa_zero_keys_take_the_lowest_blocks(dev):
-    """Zero keys make every score exactly 0 on both sides: the budget goes to blocks 0.."""
+    """Zero keys make every score exactly 0 on both sides: the budget goes to blocks 0..
+    (rows of up to 500 blocks: one crowded threshold bin of equal scores)."""
     from linear_attention_recurrence_chunked_amd import workloads as wl
-    inp = wl.qsa_inputs(400, "bf16", seed=7)
+    inp = wl.qsa_inputs(2000, "bf16", seed=7)
     inp["k"][:] = 0
     blocks, tokens = run(inp, dev, 8)
-    for i in range(400):
+    for i in range(2000):
         nvalid = (i + 1) // 4
         want = np.arange(min(8, nvalid))
         assert np.array_equal(blocks[i][:len(want)], want), i
+
+
+def test_qsa_tie_classes_break_ties_by_index(dev):
+    """Keys zero in the rotated half and equal to one of three vectors within each block give
+    identical block keys, so each query sees three exactly tied score levels (two of them
+    closer than the bf16 rounding bound, so their order may differ from the oracle's).  Every
+    row must be a valid top-K, and within each class of identical keys the selected blocks
+    must be the class's lowest indices (ties to the lower index), through both the small
+    and the crowded threshold-bin paths."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    n = 3000
+    inp = wl.qsa_inputs(n, "bf16", seed=9)
+    rng = np.random.default_rng(9)
+    cls = rng.integers(0, 3, n // 4 + 1)
+    vecs = wl.qsa_inputs(3, "bf16", seed=10)["k"]          # three bf16 rows
+    k = np.zeros_like(inp["k"])
+    for t in range(n):
+        k[t, 64:] = vecs[cls[t // 4], 64:]
+    inp["k"] = k
+    say("[gpu] qsa tie classes n=%d budget=64" % n)
+    blocks, tokens = run(inp, dev, 64)
+    check_rows(inp, blocks, tokens, 64, range(n), "tie classes")
+    for i in range(n):
+        nvalid = min((i + 1) // 4, n // 4)
+        sel = set(blocks[i][blocks[i] >= 0].tolist())
+        for c in range(3):
+            members = [b for b in range(nvalid) if cls[b] == c]
+            m = sum(b in sel for b in members)
+            assert all(b in sel for b in members[:m]), (i, c)
 
 
 def test_qsa_full_budget_at_the_largest_size(dev):
