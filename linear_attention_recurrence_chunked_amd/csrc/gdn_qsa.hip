@@ -160,8 +160,9 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(QsaArgs a)
             for (int t = 0; t < 4; ++t) {
                 const long long i = i0 + 4 * t + g;
                 if (i < a.n) {
+                    // + 0: a sum of four -0 becomes +0 (bit patterns must order like values)
                     const float sc = fmaxf(acc[t][0], 0.f) + fmaxf(acc[t][1], 0.f) +
-                                     fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f);
+                                     fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f) + 0.f;
                     a.scores[i * a.ld + b] = sc;
                 }
             }
@@ -171,7 +172,10 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(QsaArgs a)
     }
 }
 
-// Exclusive prefix sum of one value per thread over the workgroup (256 threads).
+constexpr int kTK = 1024;       // threads of a top-k workgroup
+constexpr int kTW = kTK / kWave;
+
+// Exclusive prefix sum of one value per thread over a workgroup of kTK threads.
 __device__ __forceinline__ int block_excl_scan(int x, int *tmp)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -184,48 +188,48 @@ __device__ __forceinline__ int block_excl_scan(int x, int *tmp)
     if (lane == 63) tmp[wave] = v;
     __syncthreads();
     int off = 0;
-    for (int w = 0; w < wave; ++w) off += tmp[w];
+    for (int w = 0; w < wave; ++w) off += tmp[w];   // wave-uniform
     __syncthreads();
     return off + v - x;
 }
 
 constexpr int kMaxRow = 16384;  // blocks per row held in LDS (n <= 65536)
 
-// First radix digit: the score scaled linearly onto 2,048 bins by the row maximum.  Monotone
-// in the score (one rounded multiply, then a floor), so ordering by (digit, bit pattern)
-// orders like the scores, and scores of one magnitude spread over many bins.
-__device__ __forceinline__ uint32_t lin_digit(uint32_t x, float s)
+// First radix digit of a score x >= lo: (x - lo) scaled linearly onto 2,048 bins.  Monotone
+// in x (a rounded subtraction and multiply, then a floor), so ordering by (digit, bit
+// pattern) orders like the scores, and scores of one magnitude spread over many bins.
+__device__ __forceinline__ uint32_t lin_digit(uint32_t x, float lo, float s)
 {
-    const float v = __uint_as_float(x) * s;
+    const float v = (__uint_as_float(x) - lo) * s;
     return v < 2047.f ? (uint32_t)v : 2047u;
 }
 
-// inclusive prefix sum over the wave's lanes
-__device__ __forceinline__ int wave_incl_scan(int v)
+// number of lanes below this one whose bit is set in m
+__device__ __forceinline__ int lanes_below(uint64_t m)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const int o = __shfl_up(v, m, kWave);
-        if (lane >= m) v += o;
-    }
-    return v;
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 constexpr int kCand = 256;      // a threshold bin this small is resolved by pairwise ranks
 
 // One workgroup per query, longest rows first.
-__global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
+//
+// The K_B-th largest score tau is at least the smallest of the maxima of any K_B disjoint
+// groups of the row (those maxima are K_B scores at least that large), so scores below that
+// bound take no part in the search.  A block is taken when its score is above tau, or equal to
+// it and not after b_last, the index of the last equal score that still fits the budget.
+__global__ __launch_bounds__(kTK) void qsa_topk_kernel(QsaArgs a)
 {
     __shared__ __align__(16) uint32_t row[kMaxRow];
     __shared__ int hist[2048];
     __shared__ uint32_t cx[kCand];
     __shared__ int cb[kCand];
-    __shared__ int tmp[8];
-    __shared__ int wgt[4], weq[4];
-    __shared__ float wmax[4];
+    __shared__ int tmp[kTW];
+    __shared__ int wcount[kTW];
+    __shared__ float wmax[kTW], wmin[kTW];
     __shared__ uint32_t sh_prefix, sh_need, sh_c1;
-    __shared__ int sh_cnt, sh_fill;
+    __shared__ int sh_cnt, sh_fill, sh_blast;
     const long long i = a.n - 1 - (long long)blockIdx.x;
     const long long nb = a.n / kQR;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -236,68 +240,91 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
     const u32x4 *row4 = (const u32x4 *)row;
 
     uint32_t tau = 0;         // the bit pattern of the K_B-th largest score (when !all)
-    int need_eq = 0;          // how many scores equal to tau are taken, in index order
+    int b_last = -1;          // the last taken block among those scoring exactly tau
     if (!all) {
-        // the row's visible scores into LDS: 16-byte loads, eight in flight per thread
+        // the row's visible scores into LDS: 16-byte loads, all of a thread's in flight
         const u32x4 *src = (const u32x4 *)(a.scores + i * a.ld);
-        float mx = 0.f;
-#pragma unroll 1
-        for (int c0 = 0; c0 < n4; c0 += 8 * 256) {
-            u32x4 v[8];
+        {
+            u32x4 v[kMaxRow / 4 / kTK];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * 256 + tid;
+            for (int u = 0; u < kMaxRow / 4 / kTK; ++u) {
+                const int c = u * kTK + tid;
                 v[u] = u32x4{0u, 0u, 0u, 0u};
                 if (c < n4) v[u] = src[c];
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * 256 + tid;
-                if (c < n4) {
-                    *(u32x4 *)(row + 4 * c) = v[u];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * c + e < nvalid) mx = fmaxf(mx, __uint_as_float(v[u][e]));
-                }
+            for (int u = 0; u < kMaxRow / 4 / kTK; ++u) {
+                const int c = u * kTK + tid;
+                if (c < n4) *(u32x4 *)(row + 4 * c) = v[u];
             }
         }
-#pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
-        if (lane == 0) wmax[wave] = mx;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hist[8 * tid + j] = 0;
+        hist[2 * tid] = 0;
+        hist[2 * tid + 1] = 0;
         if (tid == 0) {
             sh_prefix = 0;
             sh_need = (uint32_t)KB;
             sh_fill = 0;
         }
         __syncthreads();
-        mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        const float s = mx > 0.f ? fminf(2047.f / mx, 1e30f) : 0.f;
-        // first digit: linear in the score
+        // group g = the blocks b = g (mod K_B), halved between threads 2g' and 2g' + 1 of a
+        // pair: the row maximum and the smallest group maximum
+        float mx = 0.f, mn = 3.0e38f;
+        for (int g0 = 0; g0 < KB; g0 += kTK / 2) {
+            const int g = g0 + (tid >> 1);
+            float m = 0.f;
+            if (g < KB)
+                for (int b = g + (tid & 1) * KB; b < nvalid; b += 2 * KB)
+                    m = fmaxf(m, __uint_as_float(row[b]));
+            m = fmaxf(m, __shfl_xor(m, 1, kWave));
+            if (g < KB) {
+                mx = fmaxf(mx, m);
+                mn = fminf(mn, m);
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+            mn = fminf(mn, __shfl_xor(mn, m, kWave));
+        }
+        if (lane == 0) {
+            wmax[wave] = mx;
+            wmin[wave] = mn;
+        }
+        __syncthreads();
+        float lo = wmin[0];
+        mx = wmax[0];
+#pragma unroll
+        for (int w = 1; w < kTW; ++w) {
+            mx = fmaxf(mx, wmax[w]);
+            lo = fminf(lo, wmin[w]);
+        }
+        const uint32_t lo_bits = __float_as_uint(lo);
+        const float s = mx > lo ? fminf(2047.f / (mx - lo), 1e30f) : 0.f;
+        // first digit over the scores >= lo
 #pragma unroll 2
-        for (int c = tid; c < n4; c += 256) {
+        for (int c = tid; c < n4; c += kTK) {
             const u32x4 x = row4[c];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (4 * c + e < nvalid) atomicAdd(&hist[lin_digit(x[e], s)], 1);
+                if (4 * c + e < nvalid && x[e] >= lo_bits)
+                    atomicAdd(&hist[lin_digit(x[e], lo, s)], 1);
         }
         __syncthreads();
-        // thread t looks at digits 2047 - 8t - j (descending); gt = how many values have a
+        // thread t looks at digits 2047 - 2t - j (descending); gt = how many values have a
         // larger digit; the digit where the rank falls is unique
         {
-            int c[8], tot = 0;
+            int c[2], tot = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                c[j] = hist[2047 - 8 * tid - j];
+            for (int j = 0; j < 2; ++j) {
+                c[j] = hist[2047 - 2 * tid - j];
                 tot += c[j];
             }
             const uint32_t need = sh_need;
             int gt = block_excl_scan(tot, tmp);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 if ((uint32_t)gt < need && (uint32_t)(gt + c[j]) >= need) {
-                    sh_c1 = (uint32_t)(2047 - 8 * tid - j);
+                    sh_c1 = (uint32_t)(2047 - 2 * tid - j);
                     sh_need = need - (uint32_t)gt;
                     sh_cnt = c[j];
                 }
@@ -309,13 +336,13 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
         const int cnt = sh_cnt;
         if (cnt <= kCand) {
             // gather the bin's scores; the one whose rank among them holds `need` (the first
-            // in index order among equals) is the threshold
+            // in index order among equals) is tau; then the need_eq-th equal in index order
 #pragma unroll 2
-            for (int c = tid; c < n4; c += 256) {
+            for (int c = tid; c < n4; c += kTK) {
                 const u32x4 x = row4[c];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (4 * c + e < nvalid && lin_digit(x[e], s) == c1) {
+                    if (4 * c + e < nvalid && x[e] >= lo_bits && lin_digit(x[e], lo, s) == c1) {
                         const int slot = atomicAdd(&sh_fill, 1);
                         cx[slot] = x[e];
                         cb[slot] = 4 * c + e;
@@ -338,6 +365,15 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
                 }
             }
             __syncthreads();
+            tau = sh_prefix;
+            const int need_eq = (int)sh_need;
+            if (tid < cnt && cx[tid] == tau) {
+                const int bj = cb[tid];
+                int before = 0;
+                for (int k = 0; k < cnt; ++k) before += cx[k] == tau && cb[k] < bj;
+                if (before == need_eq - 1) sh_blast = bj;
+            }
+            __syncthreads();
         } else {
             // a crowded bin (many equal scores): bits 31..21, 20..10, 9..0 of its scores
 #pragma unroll 1
@@ -346,130 +382,113 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(QsaArgs a)
                 const int bits = pass == 2 ? 10 : 11;
                 const uint32_t dmask = (1u << bits) - 1;
                 const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (shift + bits));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) hist[8 * tid + j] = 0;
+                hist[2 * tid] = 0;
+                hist[2 * tid + 1] = 0;
                 __syncthreads();
                 const uint32_t pre = sh_prefix;
-                for (int b = tid; b < nvalid; b += 256) {
+                for (int b = tid; b < nvalid; b += kTK) {
                     const uint32_t x = row[b];
-                    if (lin_digit(x, s) == c1 && (x & mask) == pre)
+                    if (x >= lo_bits && lin_digit(x, lo, s) == c1 && (x & mask) == pre)
                         atomicAdd(&hist[(x >> shift) & dmask], 1);
                 }
                 __syncthreads();
-                int c[8], tot = 0;
+                int c[2], tot = 0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    c[j] = hist[2047 - 8 * tid - j];
+                for (int j = 0; j < 2; ++j) {
+                    c[j] = hist[2047 - 2 * tid - j];
                     tot += c[j];
                 }
                 const uint32_t nd = sh_need;
                 int gt = block_excl_scan(tot, tmp);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < 2; ++j) {
                     if ((uint32_t)gt < nd && (uint32_t)(gt + c[j]) >= nd) {
-                        sh_prefix = pre | ((uint32_t)(2047 - 8 * tid - j) << shift);
+                        sh_prefix = pre | ((uint32_t)(2047 - 2 * tid - j) << shift);
                         sh_need = nd - (uint32_t)gt;
                     }
                     gt += c[j];
                 }
                 __syncthreads();
             }
+            tau = sh_prefix;
+            const int need_eq = (int)sh_need;
+            // the need_eq-th score equal to tau in index order: contiguous ranges per thread
+            const int chunk = (nvalid + kTK - 1) / kTK;
+            const int b0 = tid * chunk, b1 = b0 + chunk < nvalid ? b0 + chunk : nvalid;
+            int eq = 0;
+            for (int b = b0; b < b1; ++b) eq += row[b] == tau;
+            int before = block_excl_scan(eq, tmp);
+            if (before < need_eq && before + eq >= need_eq)
+                for (int b = b0; b < b1; ++b)
+                    if (row[b] == tau && ++before == need_eq) sh_blast = b;
+            __syncthreads();
         }
-        tau = sh_prefix;
-        need_eq = (int)sh_need;
+        b_last = sh_blast;
     }
 
     // selection in index order: wave w takes a contiguous range of the row (a multiple of
-    // 256 blocks), lane l the four blocks 4 l .. 4 l + 3 of each 256-block step; a packed
-    // prefix sum over the lanes of (greater, equal) counts places every taken block
-    const int per = ((nvalid + 1023) / 1024) * 256;
-    const int lo = wave * per, hi = lo + per < nvalid ? lo + per : nvalid;
+    // 256 blocks), lane l the four blocks 4 l .. 4 l + 3 of each 256-block step; ballots of
+    // the four slots place every taken block
+    const int per = ((nvalid + kTW * 256 - 1) / (kTW * 256)) * 256;
+    const int lo_b = wave * per, hi_b = lo_b + per < nvalid ? lo_b + per : nvalid;
+    auto taken = [&](uint32_t x, int b) { return x > tau || (x == tau && b <= b_last); };
     if (!all) {
-        int g = 0, q = 0;
-        for (int b0 = lo; b0 < hi; b0 += 256) {
+        int count = 0;
+#pragma unroll 2
+        for (int b0 = lo_b; b0 < hi_b; b0 += 256) {
             const int b = b0 + 4 * lane;
-            if (b < hi) {
-                const u32x4 x = *(const u32x4 *)(row + b);
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (b < hi_b) x = *(const u32x4 *)(row + b);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (b + e < hi) {
-                        g += x[e] > tau;
-                        q += x[e] == tau;
-                    }
-            }
+            for (int u = 0; u < 4; ++u)
+                count += __popcll(__builtin_amdgcn_ballot_w64(b + u < hi_b && taken(x[u], b + u)));
         }
-        const int tot = __shfl(wave_incl_scan((g << 16) | q), kWave - 1, kWave);
-        if (lane == 0) {
-            wgt[wave] = tot >> 16;
-            weq[wave] = tot & 0xffff;
-        }
+        if (lane == 0) wcount[wave] = count;
     }
     __syncthreads();
-    int pos = lo, e = 0;
+    int pos = lo_b;
     if (!all) {
         pos = 0;
-        for (int w = 0; w < wave; ++w) {
-            const int left = need_eq - e;
-            pos += wgt[w] + (left <= 0 ? 0 : left < weq[w] ? left : weq[w]);
-            e += weq[w];
-        }
+        for (int w = 0; w < wave; ++w) pos += wcount[w];
     }
     const int W = KB * kQR + kQR - 1;
     int32_t *blk = a.blocks ? a.blocks + i * KB : nullptr;
     int32_t *tok = a.tokens ? a.tokens + i * W : nullptr;
-    for (int b0 = lo; b0 < hi; b0 += 256) {
+#pragma unroll 2
+    for (int b0 = lo_b; b0 < hi_b; b0 += 256) {
         const int b = b0 + 4 * lane;
         u32x4 x = {0u, 0u, 0u, 0u};
-        int g = 0, q = 0;
-        if (b < hi) {
-            if (all) {
-                g = hi - b < 4 ? hi - b : 4;
-            } else {
-                x = *(const u32x4 *)(row + b);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (b + u < hi) {
-                        g += x[u] > tau;
-                        q += x[u] == tau;
-                    }
-            }
-        }
-        const int packed = (g << 16) | q;
-        const int incl = wave_incl_scan(packed);
-        const int tot = __shfl(incl, kWave - 1, kWave);
-        const int excl = incl - packed;
-        const int left = need_eq - e > 0 ? need_eq - e : 0;
-        int p = pos + (excl >> 16) + ((excl & 0xffff) < left ? (excl & 0xffff) : left);
-        int ee = e + (excl & 0xffff);
+        if (!all && b < hi_b) x = *(const u32x4 *)(row + b);
+        bool t[4];
+        uint64_t m[4];
+        int p = pos;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (b + u < hi) {
-                bool t = all;
-                if (!all) {
-                    t = x[u] > tau || (x[u] == tau && ee < need_eq);
-                    ee += x[u] == tau;
-                }
-                if (t) {
-                    if (blk) blk[p] = b + u;
-                    if (tok) {
-#pragma unroll
-                        for (int v = 0; v < kQR; ++v) tok[kQR * p + v] = kQR * (b + u) + v;
-                    }
-                    ++p;
-                }
-            }
+            t[u] = b + u < hi_b && (all || taken(x[u], b + u));
+            m[u] = __builtin_amdgcn_ballot_w64(t[u]);
+            p += lanes_below(m[u]);
         }
-        pos += (tot >> 16) + ((tot & 0xffff) < left ? (tot & 0xffff) : left);
-        e += tot & 0xffff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (t[u]) {
+                if (blk) blk[p] = b + u;
+                if (tok) {
+#pragma unroll
+                    for (int v = 0; v < kQR; ++v) tok[kQR * p + v] = kQR * (b + u) + v;
+                }
+                ++p;
+            }
+            pos += __popcll(m[u]);
+        }
     }
     // padding, and the tail of the incomplete block after the selected tokens
     const int nsel = all ? nvalid : KB;
     if (blk)
-        for (int p = nsel + tid; p < KB; p += 256) blk[p] = -1;
+        for (int p = nsel + tid; p < KB; p += kTK) blk[p] = -1;
     if (tok) {
         const long long tail0 = ((i + 1) / kQR) * kQR;
         const int ntail = (int)(i + 1 - tail0);
-        for (int p = kQR * nsel + tid; p < W; p += 256) {
+        for (int p = kQR * nsel + tid; p < W; p += kTK) {
             const int u = p - kQR * nsel;
             tok[p] = u < ntail ? (int32_t)(tail0 + u) : -1;
         }
@@ -517,7 +536,7 @@ hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
         hipLaunchKernelGGL(qsa_score_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0,
                            stream, a);
     }
-    hipLaunchKernelGGL(qsa_topk_kernel, dim3((unsigned)p.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(qsa_topk_kernel, dim3((unsigned)p.n), dim3(kTK), 0, stream, a);
     return hipGetLastError();
 }
 
