@@ -117,6 +117,9 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(QsaArgs a)
     const long long nvis = (ilast + 1) / kQR < nb ? (ilast + 1) / kQR : nb;
     const int ntiles = (int)((nvis + 15) / 16);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    // per wave: its 16 x 16 score tile, rows 16-byte aligned, to turn four 4-byte stores per
+    // lane into one 16-byte store
+    __shared__ __align__(16) float sT[4][16 * 20];
     if (wave >= ntiles) return;               // no barriers below
     // A fragments: tile t holds rows 16 t .. 16 t + 15 (tokens i0 + 4 t .. i0 + 4 t + 3)
     bf16x8 fa[4][4];
@@ -153,20 +156,22 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(QsaArgs a)
             for (int t = 0; t < 4; ++t)
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t][kk], b8, acc[t], 0, 0, 0);
         }
-        // tile t, lane (r, g): rows 16 t + 4 g + h (token i0 + 4 t + g, head h), block r
-        const long long b = (long long)tile * 16 + r;
-        if (b < nb) {
+        // tile t, lane (r, g): rows 16 t + 4 g + h (token i0 + 4 t + g, head h), block r.
+        // + 0: a sum of four -0 becomes +0 (bit patterns must order like values)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const long long i = i0 + 4 * t + g;
-                if (i < a.n) {
-                    // + 0: a sum of four -0 becomes +0 (bit patterns must order like values)
-                    const float sc = fmaxf(acc[t][0], 0.f) + fmaxf(acc[t][1], 0.f) +
-                                     fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f) + 0.f;
-                    a.scores[i * a.ld + b] = sc;
-                }
-            }
+        for (int t = 0; t < 4; ++t)
+            sT[wave][(4 * t + g) * 20 + r] = fmaxf(acc[t][0], 0.f) + fmaxf(acc[t][1], 0.f) +
+                                             fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f) + 0.f;
+        __builtin_amdgcn_wave_barrier();
+        {
+            // lane l: token i0 + l / 4, blocks 16 tile + 4 (l % 4) .. + 3 (a row's padding
+            // to a multiple of 4 blocks absorbs the last group's overhang)
+            const f32x4 v = *(const f32x4 *)&sT[wave][(lane >> 2) * 20 + 4 * (lane & 3)];
+            const long long i = i0 + (lane >> 2);
+            const long long b = (long long)tile * 16 + 4 * (lane & 3);
+            if (i < a.n && b < nb) __builtin_nontemporal_store(v, (f32x4 *)(a.scores + i * a.ld + b));
         }
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) fb[kk] = fn[kk];
     }
