@@ -92,7 +92,7 @@ def load_traffic(kernel_key: str, sources):
 
 def profile_run(torch, gdn, wl, dev):
     """Three prefill launches, three decode steps, three backward calls, three channel-gated
-    prefills and decode steps and a 1 GiB elementwise pass, untimed."""
+    prefills and decode steps, three indexer calls and a 1 GiB elementwise pass, untimed."""
     import numpy as np
     inp = wl.workload_inputs(wl.PREFILL)
     q, k, v = (wl.to_torch(inp[n], dev, "bf16") for n in ("q", "k", "v"))
@@ -124,6 +124,14 @@ def profile_run(torch, gdn, wl, dev):
         gdn.gdn_channel_gated(wl.to_torch(d["q"][s], dev, "bf16"), wl.to_torch(d["k"][s], dev, "bf16"),
                               wl.to_torch(d["v"][s], dev, "bf16"), dga, dgb, dgw,
                               initial_state=state, num_seqs=B, final_state=state)
+    del dga, dgb, dgw
+    # the sparse-attention indexer over one sequence of 65,536 tokens, budget 512 blocks
+    qi = wl.qsa_inputs(65536, "bf16", seed=2)
+    iq, ik = wl.to_torch(qi["q"], dev, "bf16"), wl.to_torch(qi["k"], dev, "bf16")
+    for _ in range(3):
+        gdn.gdn_qsa_index(iq, ik, block_budget=512, want_blocks=False)
+    del iq, ik, qi
+    torch.cuda.synchronize()
     # calibration: an elementwise kernel that reads 1 GiB and writes 1 GiB
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -528,6 +536,7 @@ def main():
         # HBM bytes the method cannot avoid: inputs read, token lists written; the scores
         # the kernels exchange (written once, read once) are the implementation's choice
         qbytes = nq * 5 * 128 * 2 + nq * (4 * 512 + 3) * 4
+        ctr_q = load_traffic("qsa_bf16_n65536_kb512", QSA_SOURCES)
         qsa_obj = {"workload": "one sequence of %d tokens, 4 query heads, d=128, blocks of 4, "
                                "budget 512 blocks" % nq,
                    "ms_median": round(qms, 4), "queries_per_s": round(nq / (qms * 1e-3), 1),
@@ -536,6 +545,7 @@ def main():
                    "frac_of_bf16_peak": round(qflops / (qms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                    "score_bytes_written_and_read": 2 * pairs * 4,
                    "algorithmic_bytes": qbytes,
+                   "traffic": None if ctr_q is None else ctr_q["bytes_per_launch"],
                    "kernels": "qsa_prep_kernel + qsa_score_kernel + qsa_topk_kernel"}
         del iq, ik, qws
 
