@@ -11,15 +11,16 @@
 //
 // Short convolution: out[t, c] = sum_j w[c, j] x[t - (W-1) + j, c] over the tokens of t's
 // own sequence, the W-1 inputs before a sequence's first token coming from a carried state
-// [N, C, W-1] (oldest first) or zero.  A wave takes 8 consecutive tokens of 512 channels and
-// keeps the 8 + W - 1 input rows it needs in registers.
+// [N, C, W-1] (oldest first) or zero.  A wave takes 32 consecutive tokens of 512 channels in
+// steps, keeping the step's input rows and the W - 1 before them in registers and loading the
+// next step's rows while it computes.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
 namespace gdn {
 
 constexpr int kLsThreads = 256;
-constexpr int kConvTokens = 8;             // tokens per wave
+constexpr int kConvTokens = 32;            // tokens per wave
 constexpr float kLsEps = 1e-6f;
 
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
@@ -77,100 +78,15 @@ __device__ __forceinline__ float head_sum(float x)
     return x;
 }
 
-// One wave: 8 consecutive tokens of 512 channels, eight per lane; HD = 0 (no normalisation),
-// 64 or 128 channels per head (8 or 16 lanes).
-template <typename T, int W, int HD>
-__global__ __launch_bounds__(kLsThreads) void short_conv_kernel(
-    const T *__restrict__ x, const float *__restrict__ wgt, const int32_t *__restrict__ cu,
-    int nseq, long long total_T, int C, const float *__restrict__ state_in, T *__restrict__ out)
-{
-    using O = Oct<T>;
-    const int lane = threadIdx.x & 63;
-    const int groups = (C + 511) / 512;
-    const long long wid = (long long)blockIdx.x * (kLsThreads / 64) + (threadIdx.x >> 6);
-    const long long tb = wid / groups;
-    const int c = (int)(wid % groups) * 512 + 8 * lane;           // this lane's 8 channels
-    const long long t0 = tb * kConvTokens;
-    if (t0 >= total_T) return;
-    const bool live = c < C;
-    const int cc = live ? c : 0;                                   // in-bounds for every lane
-    const long long per = cu ? 0 : total_T / nseq;
-    // rows t0 - (W-1) .. t0 + kConvTokens - 1, each loaded from a row clamped into
-    // [0, total_T): rows outside it are never used (the token loop stops at total_T and the
-    // rows before a sequence come from the carried state)
-    constexpr int NR = kConvTokens + W - 1;
-    float xr[NR][8];
-    {
-        typename O::raw r[NR];
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            long long t = t0 - (W - 1) + i;
-            t = t < 0 ? 0 : (t >= total_T ? total_T - 1 : t);
-            r[i] = O::load(x + t * C + cc);
-        }
-#pragma unroll
-        for (int i = 0; i < NR; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xr[i][e] = O::get(r[i], e);
-    }
-    float w[8][W];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int j = 0; j < W; ++j) w[e][j] = wgt[(long long)(cc + e) * W + j];
-    int n = seq_of(cu, nseq, per, t0);
-    long long s_n = cu ? (long long)cu[n] : per * n;
-    long long e_n = cu ? (long long)cu[n + 1] : per * (n + 1);
-#pragma unroll
-    for (int i = 0; i < kConvTokens; ++i) {
-        const long long t = t0 + i;
-        if (t >= total_T) break;
-        while (t >= e_n) {                                    // next sequence (skip empty ones)
-            ++n;
-            s_n = e_n;
-            e_n = cu ? (long long)cu[n + 1] : per * (n + 1);
-        }
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const long long tj = t - (W - 1) + j;
-            if (tj >= s_n) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] += w[e][j] * xr[i + j][e];
-            } else if (state_in) {                             // before the sequence: state
-                const long long sidx = (W - 1) + (tj - s_n);
-                const float *sp = state_in + ((long long)n * C + cc) * (W - 1) + sidx;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] += w[e][j] * sp[e * (W - 1)];
-            }
-        }
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // SiLU: x sigmoid(x) with the hardware reciprocal (about 1 ulp)
-            o[e] = o[e] * __builtin_amdgcn_rcpf(1.f + __expf(-o[e]));
-            ss += o[e] * o[e];
-        }
-        if constexpr (HD > 0) {
-            const float f = __builtin_amdgcn_rsqf(head_sum<HD / 8>(ss) + kLsEps);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= f;
-        }
-        if (live) O::store(out + t * C + c, o);
-    }
-}
-
+// The outgoing convolution state of one (sequence n, channel c), idx = n C + c:
 // state_out[n][c][j] = ext(L_n - (W-1) + j), ext(i) = x[s_n + i][c] for i >= 0, else the
-// incoming state state_in[n][c][(W-1) + i] (or zero).  One thread per (sequence, channel);
-// it reads its own incoming state before writing, so state_out may be state_in.
+// incoming state state_in[n][c][(W-1) + i] (or zero).  It reads its own incoming state before
+// writing, so state_out may be state_in when nothing else reads the incoming state meanwhile.
 template <typename T, int W>
-__global__ __launch_bounds__(kLsThreads) void conv_state_kernel(
-    const T *__restrict__ x, const int32_t *__restrict__ cu, int nseq, long long total_T,
-    int C, const float *state_in, float *state_out)
+__device__ __forceinline__ void conv_state_item(long long idx, const T *x, const int32_t *cu,
+                                                int nseq, long long total_T, int C,
+                                                const float *state_in, float *state_out)
 {
-    const long long idx = (long long)blockIdx.x * kLsThreads + threadIdx.x;
     if (idx >= (long long)nseq * C) return;
     const int n = (int)(idx / C), c = (int)(idx % C);
     const long long per = cu ? 0 : total_T / nseq;
@@ -185,6 +101,204 @@ __global__ __launch_bounds__(kLsThreads) void conv_state_kernel(
     }
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) state_out[idx * (W - 1) + j] = v[j];
+}
+
+// Sum over the LPH (8 or 16) lanes of one head with DPP moves inside a row of 16 lanes: swap
+// neighbours, swap pairs, mirror each half-row (lane i <-> 7 - i), then, for 16, the row
+// (i <-> 15 - i); every lane ends with the head's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int LPH>
+__device__ __forceinline__ float head_sum_dpp(float x)
+{
+    x += dpp_mov<0xb1>(x);                                // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4e>(x);                                // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);                               // row_half_mirror
+    if constexpr (LPH == 16) x += dpp_mov<0x140>(x);      // row_mirror
+    return x;
+}
+
+// One wave: kConvTokens consecutive tokens of 512 channels, eight per lane, in steps of S
+// tokens (four); the next step's rows load while the current step computes,
+// and the last W-1 rows of a step carry over as the window of the next.  HD = 0 (no
+// normalisation), 64 or 128 channels per head (8 or 16 lanes).  Workgroups from conv_blocks
+// on write the outgoing state instead (state_out distinct from state_in, else null).
+template <typename T, int W, int HD>
+__global__ __launch_bounds__(kLsThreads) void short_conv_kernel(
+    const T *__restrict__ x, const float *__restrict__ wgt, const int32_t *__restrict__ cu,
+    int nseq, long long total_T, int C, const float *__restrict__ state_in, T *__restrict__ out,
+    long long conv_blocks, float *__restrict__ state_out)
+{
+    if ((long long)blockIdx.x >= conv_blocks) {
+        conv_state_item<T, W>(((long long)blockIdx.x - conv_blocks) * kLsThreads + threadIdx.x,
+                              x, cu, nseq, total_T, C, state_in, state_out);
+        return;
+    }
+    using O = Oct<T>;
+    constexpr int S = 4;                                           // tokens per step
+    constexpr int NW = W > 1 ? W - 1 : 1;                          // window rows kept
+    const int lane = threadIdx.x & 63;
+    const int groups = (C + 511) / 512;
+    const long long wid = (long long)blockIdx.x * (kLsThreads / 64) + (threadIdx.x >> 6);
+    const long long tb = wid / groups;
+    const int c = (int)(wid % groups) * 512 + 8 * lane;           // this lane's 8 channels
+    const long long t0 = tb * kConvTokens;
+    if (t0 >= total_T) return;
+    const bool live = c < C;
+    const int cc = live ? c : 0;                                   // in-bounds for every lane
+    const long long per = cu ? 0 : total_T / nseq;
+    // every row is loaded from a row clamped into [0, total_T): rows outside it are never
+    // used (the token loop stops at total_T and the rows before a sequence come from the
+    // carried state)
+    auto row_at = [&](long long t) {
+        t = t < 0 ? 0 : (t >= total_T ? total_T - 1 : t);
+        return O::load(x + t * C + cc);
+    };
+    int n = seq_of(cu, nseq, per, t0);
+    long long s_n = cu ? (long long)cu[n] : per * n;
+    long long e_n = cu ? (long long)cu[n + 1] : per * (n + 1);
+    const int n0 = n;                                              // t0's sequence
+    // window: inputs t0 - (W-1) .. t0 - 1 of t0's sequence, from x or, before the sequence's
+    // first token, from the incoming state (loaded here, beside the rows, not per token)
+    float win[NW][8];
+    {
+        typename O::raw r[NW];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) r[i] = row_at(t0 - (W - 1) + i);
+        // all W-1 state slots of the lane's channels in one batch of loads (a branch per
+        // element would wait for each load in turn)
+        float sv[NW][8];
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[k][e] = 0.f;
+        const long long lag = t0 - s_n;                        // 0 .. W-2 when slots are used
+        if (state_in && lag < W - 1) {
+            const float *sb = state_in + ((long long)n * C + cc) * (W - 1);
+#pragma unroll
+            for (int k = 0; k < W - 1; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sv[k][e] = sb[e * (W - 1) + k];
+        }
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            // row t0 - (W-1) + i lies before the sequence when i + lag < W - 1; it is then
+            // state slot i + lag
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = O::get(r[i], e);
+#pragma unroll
+                for (int k = 0; k < W - 1; ++k)
+                    if (i + lag == k) v = sv[k][e];
+                win[i][e] = v;
+            }
+        }
+    }
+    typename O::raw cur[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) cur[i] = row_at(t0 + i);
+    float w[8][W];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < W; ++j) w[e][j] = wgt[(long long)(cc + e) * W + j];
+#pragma unroll 1
+    for (int st = 0; st < kConvTokens / S; ++st) {
+        const long long ts = t0 + (long long)st * S;
+        if (ts >= total_T) break;
+        typename O::raw nxt[S];
+        if (st + 1 < kConvTokens / S) {
+#pragma unroll
+            for (int i = 0; i < S; ++i) nxt[i] = row_at(ts + S + i);
+        }
+        // rows ts - (W-1) .. ts + S - 1
+        float xr[W - 1 + S][8];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[i][e] = win[i][e];
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[W - 1 + i][e] = O::get(cur[i], e);
+        // the sequence of each token (tokens past total_T keep the last one; never stored)
+        long long sn[S];
+        int nn[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const long long t = ts + i;
+            while (t < total_T && t >= e_n) {                 // next sequence (skip empty ones)
+                ++n;
+                s_n = e_n;
+                e_n = cu ? (long long)cu[n + 1] : per * (n + 1);
+            }
+            sn[i] = s_n;
+            nn[i] = n;
+        }
+        // every token's convolution and SiLU, then the head sums side by side
+        float o[S][8], ss[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const long long t = ts + i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                const long long tj = t - (W - 1) + j;
+                // rows of t0's sequence are all in xr (the window holds its state part); a
+                // sequence starting later in the range reads its incoming state here
+                if (tj >= sn[i] || nn[i] == n0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[i][e] += w[e][j] * xr[i + j][e];
+                } else if (state_in) {                         // before the sequence: state
+                    const long long sidx = (W - 1) + (tj - sn[i]);
+                    const float *sp = state_in + ((long long)nn[i] * C + cc) * (W - 1) + sidx;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[i][e] += w[e][j] * sp[e * (W - 1)];
+                }
+            }
+            ss[i] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // SiLU: x sigmoid(x) with the hardware reciprocal (about 1 ulp)
+                o[i][e] = o[i][e] * __builtin_amdgcn_rcpf(1.f + __expf(-o[i][e]));
+                ss[i] += o[i][e] * o[i][e];
+            }
+        }
+        if constexpr (HD > 0) {
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const float f = __builtin_amdgcn_rsqf(head_sum_dpp<HD / 8>(ss[i]) + kLsEps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[i][e] *= f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if (live && ts + i < total_T) O::store(out + (ts + i) * C + c, o[i]);
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[i][e] = xr[S + i][e];
+#pragma unroll
+        for (int i = 0; i < S; ++i) cur[i] = nxt[i];
+    }
+}
+
+// state_out[n][c][j] = ext(L_n - (W-1) + j), ext(i) = x[s_n + i][c] for i >= 0, else the
+// incoming state state_in[n][c][(W-1) + i] (or zero); its own launch, after the convolution,
+// when state_out is state_in.
+template <typename T, int W>
+__global__ __launch_bounds__(kLsThreads) void conv_state_kernel(
+    const T *__restrict__ x, const int32_t *__restrict__ cu, int nseq, long long total_T,
+    int C, const float *state_in, float *state_out)
+{
+    conv_state_item<T, W>((long long)blockIdx.x * kLsThreads + threadIdx.x, x, cu, nseq,
+                          total_T, C, state_in, state_out);
 }
 
 // alpha = exp(-exp(A_h) softplus(a + b_alpha_h)), beta = sigmoid(b); one element per thread
@@ -258,27 +372,31 @@ static hipError_t launch_conv_w(const void *x, const float *w, const int32_t *cu
 {
     const long long waves = (total_T + kConvTokens - 1) / kConvTokens * ((C + 511) / 512);
     const long long blocks = (waves + 3) / 4;
-    if (blocks > 0) {
+    // a distinct outgoing state is written by extra workgroups of the same launch; in place,
+    // it waits for the convolution (which reads the incoming state) in a launch of its own
+    const bool fused = sout && W > 1 && sout != sin;
+    const long long sblocks = ((long long)nseq * C + kLsThreads - 1) / kLsThreads;
+    const long long grid = blocks + (fused ? sblocks : 0);
+    if (grid > 0) {
+        float *fs = fused ? sout : nullptr;
         if (head_dim == 128)
-            hipLaunchKernelGGL((short_conv_kernel<T, W, 128>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((short_conv_kernel<T, W, 128>), dim3((unsigned)grid),
                                dim3(kLsThreads), 0, st, (const T *)x, w, cu, nseq, total_T, C,
-                               sin, (T *)out);
+                               sin, (T *)out, blocks, fs);
         else if (head_dim == 64)
-            hipLaunchKernelGGL((short_conv_kernel<T, W, 64>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((short_conv_kernel<T, W, 64>), dim3((unsigned)grid),
                                dim3(kLsThreads), 0, st, (const T *)x, w, cu, nseq, total_T, C,
-                               sin, (T *)out);
+                               sin, (T *)out, blocks, fs);
         else
-            hipLaunchKernelGGL((short_conv_kernel<T, W, 0>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((short_conv_kernel<T, W, 0>), dim3((unsigned)grid),
                                dim3(kLsThreads), 0, st, (const T *)x, w, cu, nseq, total_T, C,
-                               sin, (T *)out);
+                               sin, (T *)out, blocks, fs);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (sout && W > 1) {
-        const long long n = (long long)nseq * C;
-        hipLaunchKernelGGL((conv_state_kernel<T, W>), dim3((unsigned)((n + kLsThreads - 1) / kLsThreads)),
-                           dim3(kLsThreads), 0, st, (const T *)x, cu, nseq, total_T, C, sin,
-                           sout);
+    if (sout && W > 1 && !fused) {
+        hipLaunchKernelGGL((conv_state_kernel<T, W>), dim3((unsigned)sblocks), dim3(kLsThreads),
+                           0, st, (const T *)x, cu, nseq, total_T, C, sin, sout);
         return hipGetLastError();
     }
     return hipSuccess;
