@@ -174,7 +174,7 @@ gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const 
  *   tokens     [n, 4 block_budget + 3] int32 or NULL: the selected tokens, ascending (the
  *              blocks' tokens, then the tail), -1 padded.  At least one output is required.
  *   workspace  gdn_qsa_workspace_bytes(n) bytes (holds the n x n/4 fp32 scores)
- * n <= 65536 and block_budget <= 2^24 (GDN_ERR_UNSUPPORTED beyond); n <= 0, block_budget
+ * n <= 131072 and block_budget <= 2^24 (GDN_ERR_UNSUPPORTED beyond); n <= 0, block_budget
  * <= 0, a null q, k or workspace, no output, misalignment or an output overlapping an input
  * or another output: GDN_ERR_INVALID_ARGUMENT; a short workspace: GDN_ERR_WORKSPACE_TOO_SMALL.
  * The notes' budget is block_budget = 512 (2048

@@ -198,7 +198,10 @@ __device__ __forceinline__ int block_excl_scan(int x, int *tmp)
     return off + v - x;
 }
 
-constexpr int kMaxRow = 16384;  // blocks per row held in LDS (n <= 65536)
+// blocks per row held in LDS: 16,384 (64 KiB, two workgroups per CU) up to 65,536 tokens,
+// 32,768 (128 KiB, one per CU) up to 131,072
+constexpr int kMaxRowSmall = 16384;
+constexpr int kMaxRow = 32768;
 
 // First radix digit of a score x >= lo: (x - lo) scaled linearly onto 2,048 bins.  Monotone
 // in x (a rounded subtraction and multiply, then a floor), so ordering by (digit, bit
@@ -224,9 +227,10 @@ constexpr int kCand = 256;      // a threshold bin this small is resolved by pai
 // groups of the row (those maxima are K_B scores at least that large), so scores below that
 // bound take no part in the search.  A block is taken when its score is above tau, or equal to
 // it and not after b_last, the index of the last equal score that still fits the budget.
+template <int MAXROW>
 __global__ __launch_bounds__(kTK) void qsa_topk_kernel(QsaArgs a)
 {
-    __shared__ __align__(16) uint32_t row[kMaxRow];
+    __shared__ __align__(16) uint32_t row[MAXROW];
     __shared__ int hist[2048];
     __shared__ uint32_t cx[kCand];
     __shared__ int cb[kCand];
@@ -250,15 +254,15 @@ __global__ __launch_bounds__(kTK) void qsa_topk_kernel(QsaArgs a)
         // the row's visible scores into LDS: 16-byte loads, all of a thread's in flight
         const u32x4 *src = (const u32x4 *)(a.scores + i * a.ld);
         {
-            u32x4 v[kMaxRow / 4 / kTK];
+            u32x4 v[MAXROW / 4 / kTK];
 #pragma unroll
-            for (int u = 0; u < kMaxRow / 4 / kTK; ++u) {
+            for (int u = 0; u < MAXROW / 4 / kTK; ++u) {
                 const int c = u * kTK + tid;
                 v[u] = u32x4{0u, 0u, 0u, 0u};
                 if (c < n4) v[u] = src[c];
             }
 #pragma unroll
-            for (int u = 0; u < kMaxRow / 4 / kTK; ++u) {
+            for (int u = 0; u < MAXROW / 4 / kTK; ++u) {
                 const int c = u * kTK + tid;
                 if (c < n4) *(u32x4 *)(row + 4 * c) = v[u];
             }
@@ -541,7 +545,12 @@ hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
         hipLaunchKernelGGL(qsa_score_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0,
                            stream, a);
     }
-    hipLaunchKernelGGL(qsa_topk_kernel, dim3((unsigned)p.n), dim3(kTK), 0, stream, a);
+    if (nb <= kMaxRowSmall)
+        hipLaunchKernelGGL(qsa_topk_kernel<kMaxRowSmall>, dim3((unsigned)p.n), dim3(kTK), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(qsa_topk_kernel<kMaxRow>, dim3((unsigned)p.n), dim3(kTK), 0, stream,
+                           a);
     return hipGetLastError();
 }
 

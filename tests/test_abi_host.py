@@ -299,12 +299,15 @@ def test_qsa_workspace_query():
         al(1030 * 260 * 4)
     assert gdn.gdn_qsa_workspace_bytes(3) == al(3 * 4 * 128 * 2) + al(128 * 2) + al(3 * 4 * 4)
     assert gdn.gdn_qsa_workspace_bytes(0) == 0
-    assert gdn.gdn_qsa_workspace_bytes(65537) == 0
+    assert gdn.gdn_qsa_workspace_bytes(65537) == al(65537 * 4 * 128 * 2) + al(16384 * 128 * 2) + \
+        al(65537 * 16384 * 4)
+    assert gdn.gdn_qsa_workspace_bytes(131072) > 0
+    assert gdn.gdn_qsa_workspace_bytes(131073) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dt=7), gdn.GDN_ERR_UNSUPPORTED),
-    (dict(n=65537), gdn.GDN_ERR_UNSUPPORTED),             # beyond 16,384 blocks
+    (dict(n=131073), gdn.GDN_ERR_UNSUPPORTED),            # beyond 32,768 blocks
     (dict(kb=(1 << 24) + 1), gdn.GDN_ERR_UNSUPPORTED),
     (dict(n=0), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(kb=0), gdn.GDN_ERR_INVALID_ARGUMENT),

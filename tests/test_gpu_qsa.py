@@ -134,3 +134,16 @@ def test_qsa_full_budget_at_the_largest_size(dev):
     rng = np.random.default_rng(0)
     rows = sorted(set([0, 3, 2047, 2048, 2051, n - 1] + list(rng.integers(0, n, 40))))
     check_rows(inp, blocks, tokens, 512, rows, "n=65536 sampled")
+
+
+def test_qsa_longest_sequence(dev):
+    """n = 131,072 tokens (32,768 blocks: the top-k's larger LDS row), budget 512: sampled
+    rows, the last one included."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    n = 131072
+    inp = wl.qsa_inputs(n, "bf16", seed=13)
+    say("[gpu] qsa n=%d budget=512" % n)
+    blocks, tokens = run(inp, dev, 512)
+    rng = np.random.default_rng(1)
+    rows = sorted(set([2047, 2048, 65535, 65536, 65539, n - 1] + list(rng.integers(0, n, 24))))
+    check_rows(inp, blocks, tokens, 512, rows, "n=131072 sampled")
