@@ -122,6 +122,25 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v,
                           int32_t dv_tile, int32_t segment_chunks);
 
 /*
+ * gdn_prefill with the gates given as their pre-activations (reading notes, section 2.1
+ * "Gating dynamics"): alpha_t = exp(-exp(A_h) softplus(a_t + b_alpha_h)) and
+ * beta_t = sigmoid(b_t), formed inside the chunk-record kernel, which takes log2 alpha
+ * directly as -exp(A_h) softplus(a_t + b_alpha_h) / ln 2 (no exp and log round trip) and is
+ * the only kernel of the bf16 plans that reads the gates.
+ *   a, b     [total_T, H] fp32 (4-byte aligned), in place of alpha and beta
+ *   A, b_alpha [H] fp32 (4-byte aligned)
+ * Every other argument, the workspace (gdn_prefill_workspace_bytes) and the error behaviour
+ * are those of gdn_prefill.  bf16 only (GDN_ERR_UNSUPPORTED for fp32); a null A or b_alpha
+ * with total_T > 0, or A / b_alpha overlapping an output: GDN_ERR_INVALID_ARGUMENT.
+ */
+gdn_status gdn_prefill_gated(const void *q, const void *k, const void *v, const float *a,
+                             const float *b, const float *A, const float *b_alpha,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                             int32_t d_v, int32_t dtype, void *y, float *final_state,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The launch plan gdn_prefill would use for this problem: state columns per workgroup and
  * chunks per segment (-1 = sequences are not split).  For reporting.
  */

@@ -90,15 +90,26 @@ gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_
     return GDN_OK;
 }
 
-gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *alpha,
-                          const float *beta, const float *initial_state,
-                          const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_T,
-                          int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void *y,
-                          float *final_state, void *workspace, size_t workspace_bytes,
-                          void *stream, int32_t dv_tile, int32_t segment_chunks)
+// gdn_prefill_ex and gdn_prefill_gated: with gate_A non-null (gated), alpha and beta are the
+// gate pre-activations a and b, and gate_A, gate_b_alpha [H] complete them.
+static gdn_status prefill_impl(const void *q, const void *k, const void *v, const float *alpha,
+                               const float *beta, const float *gate_A,
+                               const float *gate_b_alpha, bool gated,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                               int32_t d_v, int32_t dtype, void *y, float *final_state,
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               int32_t dv_tile, int32_t segment_chunks)
 {
     gdn_status st = check_common(total_T, H, d_k, d_v, dtype);
     if (st != GDN_OK) return st;
+    if (gated) {
+        if (dtype != GDN_DTYPE_BF16 || dv_tile != 0 || segment_chunks != 0)
+            return GDN_ERR_UNSUPPORTED;
+        if (total_T > 0 && (!gate_A || !gate_b_alpha)) return GDN_ERR_INVALID_ARGUMENT;
+        if ((gate_A && !aligned(gate_A, 4)) || (gate_b_alpha && !aligned(gate_b_alpha, 4)))
+            return GDN_ERR_INVALID_ARGUMENT;
+    }
     if (num_seqs <= 0) return GDN_ERR_INVALID_ARGUMENT;
     if (!cu_seqlens && total_T % num_seqs != 0) return GDN_ERR_INVALID_ARGUMENT;
     if (total_T > 0 && (!q || !k || !v || !alpha || !beta || !y))
@@ -133,8 +144,9 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     const size_t n_s = (size_t)num_seqs * H * d_k * d_v * 4;
     const size_t n_cu = cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0;
     struct Span { const void *p; size_t n; };
+    const size_t n_h = gated ? (size_t)H * 4 : 0;
     const Span inputs[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_g}, {beta, n_g},
-                           {cu_seqlens, n_cu}};
+                           {cu_seqlens, n_cu}, {gate_A, n_h}, {gate_b_alpha, n_h}};
     const Span outs[] = {{y, n_v}, {final_state, final_state ? n_s : 0}, {workspace, need}};
     for (const Span &o : outs) {
         for (const Span &in : inputs)
@@ -166,8 +178,38 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     p.dtype = dtype;
     p.y = y;
     p.s_final = final_state;
+    if (gated) {
+        if (!plan.two_launch) return GDN_ERR_UNSUPPORTED;
+        p.gated = true;
+        p.gate_A = gate_A;
+        p.gate_b_alpha = gate_b_alpha;
+    }
     hipError_t err = gdn::launch_prefill(p, plan, workspace, (hipStream_t)stream);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, const float *initial_state,
+                          const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_T,
+                          int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void *y,
+                          float *final_state, void *workspace, size_t workspace_bytes,
+                          void *stream, int32_t dv_tile, int32_t segment_chunks)
+{
+    return prefill_impl(q, k, v, alpha, beta, nullptr, nullptr, false, initial_state,
+                        cu_seqlens, num_seqs, total_T, H, d_k, d_v, dtype, y, final_state,
+                        workspace, workspace_bytes, stream, dv_tile, segment_chunks);
+}
+
+gdn_status gdn_prefill_gated(const void *q, const void *k, const void *v, const float *a,
+                             const float *b, const float *A, const float *b_alpha,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                             int32_t d_v, int32_t dtype, void *y, float *final_state,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    return prefill_impl(q, k, v, a, b, A, b_alpha, true, initial_state, cu_seqlens, num_seqs,
+                        total_T, H, d_k, d_v, dtype, y, final_state, workspace,
+                        workspace_bytes, stream, 0, 0);
 }
 
 gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *alpha,

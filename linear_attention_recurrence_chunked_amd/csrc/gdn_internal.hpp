@@ -25,6 +25,10 @@ struct PrefillProblem {
     int H, dk, dv, dtype;
     void *y;
     float *s_final;             // or null
+    // gate pre-activations instead of alpha and beta (bf16 two-launch plans only): alpha and
+    // beta then hold a and b [T, H]; gate_A and gate_b_alpha are [H]
+    bool gated = false;
+    const float *gate_A = nullptr, *gate_b_alpha = nullptr;
 };
 
 // Launch plan: columns of the state per workgroup and chunks per segment (-1: no split).

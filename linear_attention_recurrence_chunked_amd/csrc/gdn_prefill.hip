@@ -863,6 +863,11 @@ hipError_t launch_prefill(const PrefillProblem &p, const PrefillPlan &plan, void
         a.segM = seg + (size_t)plan.max_segments * p.H * p.dk * p.dv;
     }
     if (plan.two_launch) a.prep = (unsigned char *)workspace + plan.ws_table + plan.ws_seg;
+    if (p.gated) {
+        if (!plan.two_launch) return hipErrorInvalidValue;   // only the record kernel reads gates
+        a.gate_A = p.gate_A;
+        a.gate_b_alpha = p.gate_b_alpha;
+    }
     if (p.dtype == kDtypeBF16)
         return dispatch_dk_dvt<uint16_t>(a, plan, p.dk, plan.max_segments, stream);
     return dispatch_dk_dvt<float>(a, plan, p.dk, plan.max_segments, stream);

@@ -215,6 +215,8 @@ struct PrefillArgs {
     int ntiles;                // column tiles per (unit, head)
     long long units;           // sequences or table capacity
     void *prep;                // chunk records of the two-launch path, or null
+    const float *gate_A;       // non-null: alpha, beta hold the gate pre-activations a, b and
+    const float *gate_b_alpha; // the record kernel forms log2 alpha and beta from them
 };
 
 __device__ __forceinline__ void seq_bounds(const PrefillArgs &a, int n, long long &t0, int &len) {

@@ -200,10 +200,23 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
             const long long off = ((t0 + tc) * H + h) * (long long)DK + 8 * gc;
             rk[j] = ld16(gk + off);
         }
+        // alpha and beta, or, from gate pre-activations (reading notes, "Gating dynamics"),
+        // log2 alpha = -e^A softplus(a + b_alpha) / ln 2 with no exp/log round trip and
+        // beta = sigmoid(b)
+        const float *const gA = a.gate_A;
         float pa = 0.f;
         if (wave < 2) {
             const int tc = lane < nv ? lane : nv - 1;
             pa = (wave == 0 ? galpha : gbeta)[(t0 + tc) * H + h];
+            if (gA) {
+                if (wave == 0) {
+                    const float u = pa + a.gate_b_alpha[h];
+                    const float sp = u > 20.f ? u : log1pf(__expf(u));          // softplus
+                    pa = -__expf(gA[h]) * sp * 1.44269504088896341f;
+                } else {
+                    pa = __builtin_amdgcn_rcpf(1.f + __expf(-pa));
+                }
+            }
         }
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
@@ -213,7 +226,8 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
             *(u32x4 *)(bK + swz<OP, DK>(row, 8 * gc)) = row < nv ? rk[j] : z;
         }
         if (wave == 0) {
-            float x = lane < nv ? fmaxf(__builtin_amdgcn_logf(pa), kLog2AlphaFloor) : 0.f;
+            float x = lane < nv ? fmaxf(gA ? pa : __builtin_amdgcn_logf(pa), kLog2AlphaFloor)
+                                : 0.f;
             x += dpp_f32<0x111, 0xf>(x);
             x += dpp_f32<0x112, 0xf>(x);
             x += dpp_f32<0x114, 0xf>(x);
@@ -1355,23 +1369,47 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
             for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
                 for (int p = 0; p < 12; ++p) M::mma(acc[p], fkb[kb][kIb[p]], fqb[kb][kTb[p]]);
-            float et[4];
-            f32x4 ei[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                et[i] = __builtin_amdgcn_exp2f(gt[i]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ei[i][r] = __builtin_amdgcn_exp2f(-gi[i][r]);
-            }
+            // Gamma_ti = 2^(g_t - g_i).  g is non-increasing inside a chunk, so when the
+            // chunk's total decay g_C stays above -60 both 2^g_t and 2^-g_i are normal and
+            // their product (formed before it meets the accumulator) costs 8 exponentials;
+            // below, 2^g_t would underflow and 2^-g_i overflow (0 * inf), so every element
+            // takes its own 2^(g_t - g_i).  The branch is uniform over the wave.
+            // g_C from the register lane 63 already holds (gi[3][3] there is g[63])
+            const float gC = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gi[3][3]), 63));
+            const bool factored = gC >= -60.f;
             f32x4 pv[12];
+            if (factored) {
+                float et[4];
+                f32x4 ei[4];
 #pragma unroll
-            for (int p = 0; p < 12; ++p) {
-                const int tb = kTb[p], ib = kIb[p];
-                const int t = tb * 16 + ln;
+                for (int i = 0; i < 4; ++i) {
+                    et[i] = __builtin_amdgcn_exp2f(gt[i]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
-                    pv[p][r] = (i <= t) ? acc[p][r] * et[tb] * ei[ib][r] : 0.f;
+                    for (int r = 0; r < 4; ++r) ei[i][r] = __builtin_amdgcn_exp2f(-gi[i][r]);
+                }
+#pragma unroll
+                for (int p = 0; p < 12; ++p) {
+                    const int tb = kTb[p], ib = kIb[p];
+                    const int t = tb * 16 + ln;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
+                        pv[p][r] = (i <= t) ? acc[p][r] * (et[tb] * ei[ib][r]) : 0.f;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 12; ++p) {
+                    const int tb = kTb[p], ib = kIb[p];
+                    const int t = tb * 16 + ln;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
+                        pv[p][r] = (i <= t)
+                                       ? acc[p][r] * __builtin_amdgcn_exp2f(gt[tb] - gi[ib][r])
+                                       : 0.f;
+                    }
                 }
             }
 #pragma unroll

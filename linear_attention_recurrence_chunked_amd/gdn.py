@@ -62,6 +62,9 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill.argtypes = pre
     lib.gdn_prefill_ex.restype = i32
     lib.gdn_prefill_ex.argtypes = pre + [i32, i32]
+    lib.gdn_prefill_gated.restype = i32
+    lib.gdn_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                      i32, i32, vp, vp, vp, sz, vp]
     lib.gdn_prefill_backward_workspace_bytes.restype = sz
     lib.gdn_prefill_backward_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.gdn_prefill_backward.restype = i32
@@ -166,6 +169,39 @@ def gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, num_s
                                dt, _ptr(y), _ptr(final_state), _ptr(workspace), wbytes,
                                _stream(stream), dv_tile, segment_chunks)
     _check("gdn_prefill", st)
+    return y, final_state
+
+
+def gdn_prefill_gated(q, k, v, a, b, A, b_alpha, initial_state=None, cu_seqlens=None,
+                      num_seqs=None, y=None, final_state=None, workspace=None, stream=None,
+                      want_final_state: bool = True):
+    """Chunked prefill with the gates as pre-activations: a, b [T, H] fp32 and A, b_alpha [H]
+    fp32 (alpha = exp(-exp(A) softplus(a + b_alpha)), beta = sigmoid(b)); bf16 q, k, v.
+    Returns (y, final_state)."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        n = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != n:
+            raise ValueError("num_seqs does not match cu_seqlens")
+        num_seqs = n
+    elif num_seqs is None:
+        num_seqs = 1
+    if y is None:
+        y = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = gdn_prefill_workspace_bytes(num_seqs, T, H, dk, dv, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gdn_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A),
+                                  _ptr(b_alpha), _ptr(initial_state), _ptr(cu_seqlens),
+                                  num_seqs, T, H, dk, dv, dt, _ptr(y), _ptr(final_state),
+                                  _ptr(workspace), wbytes, _stream(stream))
+    _check("gdn_prefill_gated", st)
     return y, final_state
 
 

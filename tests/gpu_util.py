@@ -56,7 +56,9 @@ def slice_rel_err(got_y, ref_y, cu, heads=None):
             ref = ref_y[r0:r1, h]
             den = float(np.max(np.abs(ref)))
             err = float(np.max(np.abs(got_y[r0:r1, h] - ref)))
-            worst = max(worst, err / den if den > 0 else err)
+            e = err / den if den > 0 else err
+            if e != e or (worst == worst and e > worst):   # a NaN stays (max() would drop it)
+                worst = e
     return worst
 
 
@@ -68,7 +70,9 @@ def state_rel_err(got_s, ref_s):
             ref = ref_s[n, h]
             den = float(np.max(np.abs(ref)))
             err = float(np.max(np.abs(got_s[n, h] - ref)))
-            worst = max(worst, err / den if den > 0 else err)
+            e = err / den if den > 0 else err
+            if e != e or (worst == worst and e > worst):   # a NaN stays (max() would drop it)
+                worst = e
     return worst
 
 

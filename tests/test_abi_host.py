@@ -323,3 +323,28 @@ def test_qsa_workspace_query():
 ])
 def test_qsa_rejects(lib, kw, code):
     assert qsa(lib, **kw) == code
+
+
+def prefill_gated(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, v=3 * G, ga=4 * G, gb=5 * G, A=10 * G, bal=11 * G, s0=None,
+             cu=None, n=2, T=256, H=2, dk=128, dv=128, dt=1, y=6 * G, sf=7 * G, ws=9 * G,
+             wsb=G, stream=None)
+    a.update(kw)
+    return lib.gdn_prefill_gated(a["q"], a["k"], a["v"], a["ga"], a["gb"], a["A"], a["bal"],
+                                 a["s0"], a["cu"], a["n"], a["T"], a["H"], a["dk"], a["dv"],
+                                 a["dt"], a["y"], a["sf"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), gdn.GDN_ERR_UNSUPPORTED),                # bf16 only
+    (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(A=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(bal=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(ga=None), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(A=10 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),   # 4-byte alignment
+    (dict(A=6 * G + 64), gdn.GDN_ERR_INVALID_ARGUMENT),   # A inside y
+    (dict(bal=7 * G), gdn.GDN_ERR_INVALID_ARGUMENT),      # b_alpha under the final state
+    (dict(wsb=16), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_prefill_gated_rejects(lib, kw, code):
+    assert prefill_gated(lib, **kw) == code
