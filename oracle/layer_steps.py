@@ -16,7 +16,7 @@ before you write", the paragraph on the actual parameterization):
 * output: sigmoid(z_t) (.) RMSNorm(y_t), with a zero-centred RMSNorm, before the output
   projection.
 
-Readings where the pages are silent (listed in the design doc as well):
+Readings where the pages are silent:
 
 * the convolution width is not given: any width W >= 1 is accepted here; tests use W = 4;
   out[t, c] = sum_j w[c, j] x[t - (W-1) + j, c] (w[c, W-1] weighs the current token), with

@@ -18,7 +18,7 @@ dimensions;
 5. the top K_B = ceil(K / r) = 512 blocks (token budget K = 2048) per query, expanded to their
    tokens and joined with the tail of the current incomplete block, {floor((i+1)/r) r .. i}.
 
-Readings where the pages are silent (listed in the design doc as well):
+Readings where the pages are silent:
 
 * RMSNorm(x) = x / sqrt(mean(x^2) + 1e-6), no learnable scale;
 * the rotated dimensions are the first 64; they are rotated in pairs (m, m + 32),
