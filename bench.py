@@ -24,7 +24,10 @@ if ROOT not in sys.path:
 METRIC = "GDN prefill tokens/s (MFMA %) + decode steps/s at B=128 (HBM GB/s %)"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-PEAK_FP32_VALU_TFLOPS = 157.3    # MI355X fp32 vector (256 CUs x 2.4 GHz x 256 FLOP/clock)
+# fp32 vector peak without packed instructions (every HIP file is built with packed fp32 off):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP per FMA x 2.4 GHz = 78.6 TFLOP/s (the packed rate,
+# 157.3 TFLOP/s, is out of reach of this build)
+PEAK_FP32_VALU_TFLOPS = 78.6
 CHUNK = 64
 
 
@@ -153,6 +156,10 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-channel", action="store_true")
     ap.add_argument("--no-qsa", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 2^20-token single-sequence prefill")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the 32-sequence packed prefill")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3 counter passes: 3 prefill launches, 3 decode "
                          "steps and an elementwise kernel over 1 GiB (the calibration)")
@@ -274,6 +281,68 @@ def main():
         "algorithmic_bytes_per_launch": pbytes,
         "hbm_frac_of_algorithmic_bytes": round(pbytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
+
+    # ------------------------------------------------------------------ other prefill shapes
+    # the 2^20-token single sequence and the 32 packed sequences, each in the library's own
+    # plan, timed call by call after a cache flush
+    def time_workload(wobj, reps):
+        t0 = time.time()
+        wi = wl.workload_inputs(wobj)
+        print("[bench] %s inputs generated in %.1fs" % (wobj.name, time.time() - t0),
+              file=sys.stderr, flush=True)
+        tq = wl.to_torch(wi["q"], dev, "bf16")
+        tk = wl.to_torch(wi["k"], dev, "bf16")
+        tv = wl.to_torch(wi["v"], dev, "bf16")
+        ta = torch.from_numpy(wi["alpha"]).to(dev)
+        tb = torch.from_numpy(wi["beta"]).to(dev)
+        ts0 = None if wi["s0"] is None else torch.from_numpy(wi["s0"]).to(dev)
+        tcu = None if wi["cu_seqlens"] is None else torch.from_numpy(wi["cu_seqlens"]).to(dev)
+        n_s = wi["num_seqs"]
+        TT, HH, dd_ = tq.shape
+        del wi
+        ty = torch.empty((TT, HH, dd_), dtype=torch.bfloat16, device=dev)
+        tsf = torch.empty((n_s, HH, dd_, dd_), dtype=torch.float32, device=dev)
+        ptile, pseg = gdn.gdn_prefill_plan(n_s, TT, HH, dd_, dd_, gdn.GDN_DTYPE_BF16)
+        wneed = gdn.gdn_prefill_workspace_bytes(n_s, TT, HH, dd_, dd_, gdn.GDN_DTYPE_BF16)
+        tws = torch.empty(max(wneed, 16), dtype=torch.uint8, device=dev)
+
+        def call():
+            gdn.gdn_prefill(tq, tk, tv, ta, tb, initial_state=ts0, cu_seqlens=tcu,
+                            num_seqs=n_s, y=ty, final_state=tsf,
+                            workspace=tws if wneed else None)
+
+        call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            cache_flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        fl = prefill_flops_per_token_head(dd_) * TT * HH
+        tf = fl / (ms * 1e-3) / 1e12
+        nb = prefill_bytes(TT, HH, dd_, n_s) + (0 if ts0 is None else n_s * HH * dd_ * dd_ * 4)
+        trk = load_traffic(wobj.name, PREFILL_SOURCES)
+        res = {"workload": wobj.name, "tokens": TT, "sequences": n_s,
+               "dv_tile": ptile, "segment_chunks": pseg, "ms_median": round(ms, 4),
+               "ms_all": [round(x, 4) for x in times],
+               "tokens_per_s": round(TT / (ms * 1e-3), 1),
+               "flops_per_launch": fl,
+               "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                            "traffic": None if trk is None else trk["bytes_per_launch"]},
+               "algorithmic_bytes_per_launch": nb,
+               "hbm_frac_of_algorithmic_bytes": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del tq, tk, tv, ta, tb, ts0, tcu, ty, tsf, tws
+        torch.cuda.empty_cache()
+        return res
+
+    long_obj = None if args.no_long else time_workload(wl.LONG, 5)
+    varlen_obj = None if args.no_varlen else time_workload(wl.VARLEN, 10)
 
     # ------------------------------------------------------------------ decode
     wd = wl.DECODE
@@ -554,9 +623,25 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
-        threads = max(1, min(16, os.cpu_count() or 1))
+        nproc = os.cpu_count() or 1
+        try:
+            avail = len(os.sched_getaffinity(0))
+        except AttributeError:
+            avail = nproc
+        omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
         units = nseq * H
-        use = min(threads, units)
+        # one thread per independent (sequence, head) chain, within the cores this process
+        # may use (and OMP_NUM_THREADS where the host sets a share)
+        use = max(1, min(avail, units, omp if omp > 0 else avail))
+        model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         # whole passes over the workload until at least 10 s of host time (at most 40 passes)
         reps = 0
         c0 = time.perf_counter()
@@ -570,7 +655,9 @@ def main():
         cpu = {"value": round(reps * T / csec, 1), "unit": "tokens/s", "cores": use,
                "kind": "oracle",
                "sample": "%d whole passes over the prefill workload (B=4, H=16, T=4096, d=128), "
-                         "fp64 C oracle, %d threads, %.1f s" % (reps, use, csec)}
+                         "fp64 C oracle, %d threads, %.1f s" % (reps, use, csec),
+               "nproc": nproc, "cpus_available": avail, "cpu_model": model,
+               "independent_units": units}
 
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -585,6 +672,8 @@ def main():
                     "tokens_per_s_warm": round(T / (warm_ms * 1e-3), 1),
                     "wall_s_timed_loop_incl_flush": round(wall, 4)},
         "roofline": roofline,
+        "long_prefill": long_obj,
+        "varlen_prefill": varlen_obj,
         "decode": decode,
         "layer_steps": layer,
         "backward": backward,

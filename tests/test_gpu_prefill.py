@@ -87,6 +87,18 @@ def test_segmented_slow_decay(dev, oracle_lib):
     check_prefill(inp, dev, oracle_lib, dv_tile=128, segment_chunks=2, label="seg-slow-decay")
 
 
+@pytest.mark.parametrize("seg", [1, 2, 3])
+@pytest.mark.parametrize("tile", [16, 32])
+def test_segmented_pipelined_scan_slow_decay(dev, oracle_lib, tile, seg):
+    """The pipelined scan (16- and 32-column tiles) in segmented mode: every segment but a
+    sequence's first starts from the state phases A and B composed, and with alpha close to
+    1 (sigmoid(N(8, 0.5))) that state is far from negligible at every segment boundary."""
+    lengths = [700, 1, 64, 0, 129, 450, 65]
+    inp = _inp(lengths, H=2, seed=40 + 3 * tile + seg, alpha=(8.0, 0.5))
+    check_prefill(inp, dev, oracle_lib, dv_tile=tile, segment_chunks=seg,
+                  label="segmented-pipe")
+
+
 def test_many_sequences_segment_table(dev, oracle_lib):
     """More sequences than one table-building pass (1024) with segments and empties."""
     rng = np.random.default_rng(21)
