@@ -141,6 +141,31 @@ gdn_status gdn_prefill_gated(const void *q, const void *k, const void *v, const 
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same operation, arguments and
+ * results, with no workspace argument.  Its workspace is a fixed array of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from the library's
+ * load until the process ends; the call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *   Limit: problems whose gdn_prefill_workspace_bytes(...) exceeds
+ *   GDN_NOALLOC_SCRATCH_BYTES (= gdn_noalloc_scratch_bytes()) are rejected with
+ *   GDN_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *   Concurrency: every call on one GPU shares that GPU's array.  Calls enqueued on one
+ *   stream are ordered and safe; calls that may run at the same time on one GPU (several
+ *   streams or threads) race on the array and give undefined results.
+ *   Errors: those of gdn_prefill; GDN_ERR_HIP also when the array's device address cannot be
+ *   obtained on the current device.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t gdn_noalloc_scratch_bytes(void);
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_T, int32_t H,
+                               int32_t d_k, int32_t d_v, int32_t dtype,
+                               void *y, float *final_state, void *stream);
+
+/*
  * The launch plan gdn_prefill would use for this problem: state columns per workgroup and
  * chunks per segment (-1 = sequences are not split).  For reporting.
  */

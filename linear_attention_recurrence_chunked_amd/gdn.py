@@ -65,6 +65,11 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill_gated.restype = i32
     lib.gdn_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                       i32, i32, vp, vp, vp, sz, vp]
+    lib.gdn_noalloc_scratch_bytes.restype = sz
+    lib.gdn_noalloc_scratch_bytes.argtypes = []
+    lib.gdn_prefill_noalloc.restype = i32
+    lib.gdn_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                        i32, vp, vp, vp]
     lib.gdn_prefill_backward_workspace_bytes.restype = sz
     lib.gdn_prefill_backward_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.gdn_prefill_backward.restype = i32
@@ -169,6 +174,32 @@ def gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, num_s
                                dt, _ptr(y), _ptr(final_state), _ptr(workspace), wbytes,
                                _stream(stream), dv_tile, segment_chunks)
     _check("gdn_prefill", st)
+    return y, final_state
+
+
+def gdn_noalloc_scratch_bytes() -> int:
+    return int(load().gdn_noalloc_scratch_bytes())
+
+
+def gdn_prefill_noalloc(q, k, v, alpha, beta, y, final_state=None, initial_state=None,
+                        cu_seqlens=None, num_seqs=None, stream=None):
+    """gdn_prefill with the library's fixed per-GPU workspace: nothing is allocated, so y
+    [T, H, d_v] and final_state [N, H, d_k, d_v] fp32 (or None) come from the caller.
+    Returns (y, final_state)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        n = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != n:
+            raise ValueError("num_seqs does not match cu_seqlens")
+        num_seqs = n
+    elif num_seqs is None:
+        num_seqs = 1
+    st = load().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(initial_state), _ptr(cu_seqlens), num_seqs, T, H, dk,
+                                    dv, dt, _ptr(y), _ptr(final_state), _stream(stream))
+    _check("gdn_prefill_noalloc", st)
     return y, final_state
 
 

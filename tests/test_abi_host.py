@@ -120,6 +120,37 @@ def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
 
 
+def prefill_noalloc(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, s0=None, cu=None,
+             n=2, T=256, H=2, dk=128, dv=128, dt=1, y=6 * G, sf=7 * G, stream=None)
+    a.update(kw)
+    return lib.gdn_prefill_noalloc(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"],
+                                   a["cu"], a["n"], a["T"], a["H"], a["dk"], a["dv"], a["dt"],
+                                   a["y"], a["sf"], a["stream"])
+
+
+def test_noalloc_scratch_size(lib):
+    assert gdn.gdn_noalloc_scratch_bytes() == 64 << 20
+
+
+# rejected before any HIP call (the size check is a function of the arguments alone)
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(H=0), gdn.GDN_ERR_INVALID_ARGUMENT),
+    (dict(dk=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dt=5), gdn.GDN_ERR_UNSUPPORTED),
+    # a workspace larger than the fixed array: 2^24 tokens of 16 bf16 heads
+    (dict(n=1, T=1 << 24, H=16), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_prefill_noalloc_rejects(lib, kw, code):
+    need = gdn.gdn_prefill_workspace_bytes(kw.get("n", 2), kw.get("T", 256), kw.get("H", 2),
+                                           kw.get("dk", 128), 128, kw.get("dt", 1))
+    if code == gdn.GDN_ERR_WORKSPACE_TOO_SMALL:
+        assert need > gdn.gdn_noalloc_scratch_bytes()
+    assert prefill_noalloc(lib, **kw) == code
+
+
 def decode(lib, **kw):
     a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, state=6 * G, y=7 * G,
              B=4, H=2, dk=128, dv=128, dt=1, stream=None)
