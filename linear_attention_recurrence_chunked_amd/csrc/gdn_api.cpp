@@ -65,7 +65,7 @@ size_t gdn_prefill_workspace_bytes_ex(int32_t num_seqs, int64_t total_T, int32_t
     gdn::PrefillPlan plan;
     if (!plan_for(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile, segment_chunks, &plan))
         return 0;
-    return plan.ws_table + plan.ws_seg + plan.ws_prep;
+    return plan.ws_table + plan.ws_seg + plan.ws_prep + plan.ws_wide;
 }
 
 size_t gdn_prefill_workspace_bytes(int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
@@ -134,7 +134,7 @@ static gdn_status prefill_impl(const void *q, const void *k, const void *v, cons
     if (!gdn::make_plan(num_seqs, total_T, H, d_k, d_v, dtype, dv_tile,
                         in_place ? -1 : segment_chunks, &plan))
         return dv_tile != 0 ? GDN_ERR_UNSUPPORTED : GDN_ERR_INVALID_ARGUMENT;
-    const size_t need = plan.ws_table + plan.ws_seg + plan.ws_prep;
+    const size_t need = plan.ws_table + plan.ws_seg + plan.ws_prep + plan.ws_wide;
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE_TOO_SMALL;
 
     // aliasing: outputs may not overlap inputs (final_state == initial_state is allowed)
@@ -179,7 +179,7 @@ static gdn_status prefill_impl(const void *q, const void *k, const void *v, cons
     p.y = y;
     p.s_final = final_state;
     if (gated) {
-        if (!plan.two_launch) return GDN_ERR_UNSUPPORTED;
+        if (!plan.two_launch && !plan.wide) return GDN_ERR_UNSUPPORTED;
         p.gated = true;
         p.gate_A = gate_A;
         p.gate_b_alpha = gate_b_alpha;

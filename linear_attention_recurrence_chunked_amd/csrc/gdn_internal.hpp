@@ -40,6 +40,8 @@ struct PrefillPlan {
     long long nslots;           // chunk slots of the records
     size_t ws_table, ws_seg;    // workspace bytes for the table and per-segment matrices
     size_t ws_prep;             // workspace bytes for the chunk records
+    int wide = 0;               // 1: one-launch scan with the whole 128 x 128 state per workgroup
+    size_t ws_wide = 0;         // its job counter, publication flags and segment end states
 };
 
 bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype,

@@ -552,11 +552,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
 // exclusive prefix sum over sequences for the entry offsets, then one entry per segment.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void segment_table_kernel(PrefillArgs a, int seg_tokens,
-                                                             SegEntry *table, int32_t *count)
+                                                             SegEntry *table, int32_t *count,
+                                                             int32_t *zero, long long nzero)
 {
     __shared__ int32_t s_scan[1024];
     __shared__ int32_t s_base;
     const int tid = threadIdx.x;
+    // words the next launch expects to start at zero (the wide scan's job counter and flags)
+    for (long long i = tid; i < nzero; i += 1024) zero[i] = 0;
     if (tid == 0) s_base = 0;
     __syncthreads();
     for (int n0 = 0; n0 < a.num_seqs; n0 += 1024) {
@@ -707,7 +710,7 @@ static hipError_t run_prefill(const PrefillArgs &args, const PrefillPlan &plan,
     }
     hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, args,
                        plan.seg_chunks * kChunk, (SegEntry *)args.table,
-                       (int32_t *)args.n_entries);
+                       (int32_t *)args.n_entries, (int32_t *)nullptr, 0ll);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // phase A: [S | M] scans of every segment but the last of each sequence (bf16: 64-column
@@ -785,9 +788,58 @@ static int largest_tile(int dtype, int dk, int dv)
     return 0;
 }
 
+// The one-launch bf16 scan (gdn_prefill_wide.hip) for d_k = d_v = 128: one workgroup per
+// (segment, head) with the whole state.  Sequences are split into segments until the jobs
+// number about four per CU (at least 16 chunks each), unless the chains alone are that many.
+static bool make_wide_plan(int num_seqs, long long total_T, int H, int seg_chunks_req,
+                           PrefillPlan *plan)
+{
+    const long long chains = (long long)num_seqs * H;
+    const long long total_chunks = cdiv(total_T, kChunk) + num_seqs;
+    int seg = seg_chunks_req;
+    if (seg == 0) {
+        constexpr long long kJobs = 1024;
+        if (chains >= kJobs) {
+            seg = -1;
+        } else {
+            long long s = cdiv(total_chunks * H, kJobs);
+            if (s < 16) s = 16;
+            if (s > (1 << 24)) s = 1 << 24;
+            seg = (int)s;
+            // equal lengths: no split when one segment holds a whole sequence
+            if (total_T % num_seqs == 0 && cdiv(total_T / num_seqs, kChunk) <= seg) seg = -1;
+        }
+    }
+    if (seg == 0 || seg < -1) return false;
+    plan->wide = 1;
+    plan->dv_tile = 128;
+    plan->two_launch = 0;
+    plan->seg_chunks = seg;
+    plan->nslots = 0;
+    plan->ws_prep = 0;
+    plan->ws_seg = 0;
+    if (seg < 0) {
+        plan->max_segments = num_seqs;
+        plan->ws_table = 0;
+        plan->ws_wide = 0;
+    } else {
+        const long long max_entries = num_seqs + cdiv(total_T, (long long)seg * kChunk);
+        plan->max_segments = max_entries;
+        plan->ws_table = (size_t)(cdiv((long long)max_entries * sizeof(SegEntry) + 16, 256) * 256);
+        // job counter and error word (256 bytes), flags [entries, H], end states
+        const size_t flags = (size_t)cdiv(max_entries * H * 4, 256) * 256;
+        plan->ws_wide = 256 + flags + (size_t)max_entries * H * 128 * 128 * 4;
+    }
+    return true;
+}
+
 bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype,
                int dv_tile_req, int seg_chunks_req, PrefillPlan *plan)
 {
+    plan->wide = 0;
+    plan->ws_wide = 0;
+    if (dtype == kDtypeBF16 && dk == 128 && dv == 128 && (dv_tile_req == 0 || dv_tile_req == 128))
+        return make_wide_plan(num_seqs, total_T, H, seg_chunks_req, plan);
     // Column tile: the chains (sequence, head) are independent; split the state columns
     // until there are enough workgroups to cover the 256 CUs, within the LDS budget.
     int tile = dv_tile_req;
@@ -864,9 +916,36 @@ hipError_t launch_prefill(const PrefillProblem &p, const PrefillPlan &plan, void
     }
     if (plan.two_launch) a.prep = (unsigned char *)workspace + plan.ws_table + plan.ws_seg;
     if (p.gated) {
-        if (!plan.two_launch) return hipErrorInvalidValue;   // only the record kernel reads gates
+        // only the record kernel and the wide scan read the gates
+        if (!plan.two_launch && !plan.wide) return hipErrorInvalidValue;
         a.gate_A = p.gate_A;
         a.gate_b_alpha = p.gate_b_alpha;
+    }
+    if (plan.wide) {
+        WideArgs w{};
+        w.a = a;
+        long long jobs = (long long)p.num_seqs * p.H;
+        if (plan.seg_chunks >= 0) {
+            unsigned char *ws = (unsigned char *)workspace;
+            unsigned char *ctl = ws + plan.ws_table;
+            w.counter = (int32_t *)ctl;
+            w.error = (int32_t *)(ctl + 4);
+            w.flags = (int32_t *)(ctl + 256);
+            const size_t flags = (size_t)cdiv(plan.max_segments * p.H * 4, 256) * 256;
+            w.seg_state = (float *)(ctl + 256 + flags);
+            w.wmax = plan.seg_chunks;
+            w.a.segB = nullptr;
+            w.a.segM = nullptr;
+            // the table, and zeros for the counter, the error word and the flags
+            hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, a,
+                               plan.seg_chunks * kChunk, (SegEntry *)a.table,
+                               (int32_t *)a.n_entries, (int32_t *)ctl,
+                               (long long)(256 + flags) / 4);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            jobs = plan.max_segments * p.H;
+        }
+        return launch_wide_scan(w, jobs, stream);
     }
     if (p.dtype == kDtypeBF16)
         return dispatch_dk_dvt<uint16_t>(a, plan, p.dk, plan.max_segments, stream);

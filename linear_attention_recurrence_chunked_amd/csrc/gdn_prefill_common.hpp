@@ -219,6 +219,17 @@ struct PrefillArgs {
     const float *gate_b_alpha; // the record kernel forms log2 alpha and beta from them
 };
 
+// Arguments of the one-launch bf16 scan (gdn_prefill_wide.hip).
+struct WideArgs {
+    PrefillArgs a;
+    int32_t *counter;      // job counter (segmented plans; zeroed before the launch) or null
+    int32_t *flags;        // [entries, H]: column waves that published the end state
+    float *seg_state;      // [entries, H, DK, DV] end states of segments
+    int32_t *error;        // set when a wait gives up (never expected)
+    int wmax;              // longest warm-up window, chunks
+};
+hipError_t launch_wide_scan(const WideArgs &w, long long jobs, hipStream_t stream);
+
 __device__ __forceinline__ void seq_bounds(const PrefillArgs &a, int n, long long &t0, int &len) {
     if (a.cu) {
         const long long b0 = a.cu[n], b1 = a.cu[n + 1];

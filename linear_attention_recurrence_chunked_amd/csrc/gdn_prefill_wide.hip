@@ -1,0 +1,811 @@
+// gdn_prefill_wide.hip -- bf16 prefill for d_k = d_v = 128 in one launch: one workgroup per
+// (segment of a sequence, head) carries the whole 128 x 128 fp32 state and forms every
+// chunk-local quantity itself, so nothing but the inputs, y and the states crosses HBM.
+//
+// The chunk algebra is the WY / UT form of the reading notes' transition-matrix recurrence
+// (Gated DeltaNet, section 2.1), with g the in-chunk inclusive prefix of log2 alpha,
+// gamma = 2^g, Gamma_ti = gamma_t / gamma_i, A = diag(beta) strictlower(K K^T (.) Gamma),
+// T' = (I + A)^{-1} diag(beta), P = lower_incl(Q K^T (.) Gamma):
+//
+//     R = V - diag(gamma) K S,   U = T' R,   Y = diag(gamma) Q S + P U,
+//     S <- gamma_C S + (diag(gamma_C / gamma) K)^T U.
+//
+// Twelve waves.  Waves 0-7 ("column waves") own 16 state columns each and run, for chunk j:
+// K S, R, U = T' R, the state update, Shat^T Q^T of chunk j and Y of chunk j-1 (P of chunk
+// j-1 arrives a step later).  Waves 8-11 ("prep waves") issue the direct-to-LDS copies of
+// the chunks ahead and, for chunk j+1, form g, the Gram blocks, T' (blocked inversion, one
+// 16 x 16 block row per wave) and the decay factors, and P of chunk j.  One workgroup barrier
+// per chunk step; the prep waves meet once more inside a step through an LDS counter.
+//
+// Segments (long sequences, few chains).  A segment that does not start its sequence needs
+// the state at its first token.  Its workgroup first scans, from a zero state and without
+// writing y, the W chunks before it, where W is the least number of whole chunks over which
+// the transition norm provably falls below 2^-48: per token
+// ||alpha (I - beta k k^T)||_2 = alpha max(1, |1 - beta ||k||^2|), so the product of these
+// over the window bounds how much of the true start state the warm-up omits (relative to the
+// state at the window's start).  W is chosen from alpha alone and then verified with the
+// keys; when no window within one segment reaches the bound (decay too slow), or the
+// verification fails, the workgroup instead waits for the previous segment's workgroup to
+// publish its exact end state (workgroups take their jobs in increasing order from an atomic
+// counter, so the one waited for has already started and never waits on a later one).
+#include <type_traits>
+
+#include "gdn_prefill_ops.hpp"
+
+namespace gdn {
+
+constexpr int kWideCol = 8;                 // column waves, 16 state columns each
+constexpr int kWidePrep = 4;                // prep waves
+constexpr int kWideWaves = kWideCol + kWidePrep;
+constexpr float kWarmBound = -48.f;         // log2 transition-norm bound a warm-up must reach
+constexpr float kWarmAlpha = -50.f;         // the window choice on log2 alpha alone
+
+template <int DK, int DV>
+struct LdsWide {
+    static constexpr int szK = kChunk * DK * 2;        // [64][DK] bf16 (K and Q tiles)
+    static constexpr int szV = kChunk * DV * 2;        // [64][DV] bf16
+    static constexpr int szT = kChunk * kChunk * 2;    // T' as a 64-wide swizzled tile
+    static constexpr int szP = 6 * 1024;               // P as six operand fragments
+    static constexpr int szF = 2 * kChunk * 4 + 16;    // gamma 2^ls, rho, g_C
+    static constexpr int szPG = 2 * kChunk * 4;        // a prep wave's g and beta of a chunk
+    static constexpr int LDB = 20;                     // padded fp32 rows of an A block
+    static constexpr int LDX = 20;                     // padded rows of a diagonal X block
+    static constexpr int sK = 0;                       // chunk j in stage j % 3
+    static constexpr int sQ = sK + 3 * szK;            // chunk j in stage j % 2
+    static constexpr int sV = sQ + 2 * szK;            // chunk j in stage j % 2
+    static constexpr int sT = sV + 2 * szV;            // chunk j in buffer j % 2
+    static constexpr int sP = sT + 2 * szT;            // chunk j in buffer j % 2
+    static constexpr int sAB = sP + 2 * szP;           // raw gates [alpha 64][beta 64], j % 2
+    static constexpr int sF = sAB + 2 * 512;           // factors of chunk j in buffer j % 2
+    static constexpr int sPG = sF + 2 * szF;           // [prep wave][j % 2] g, beta
+    static constexpr int sA = sPG + kWidePrep * 2 * szPG;   // six strictly lower A blocks
+    static constexpr int sX = sA + 6 * 16 * LDB * 4;        // four diagonal X blocks
+    static constexpr int sMisc = sX + 4 * 16 * LDX * 4;
+    static constexpr int total = sMisc + 256;
+    static_assert(total <= 160 * 1024, "LDS");
+};
+
+// misc words (int or float)
+enum {
+    kMiscPbar = 0,       // prep-wave barrier counter
+    kMiscJob = 1,        // job id
+    kMiscLamWin = 2,     // running log2 bound over the warm-up chunks (float)
+    kMiscLamPart = 4,    // [2][4] per-wave key terms of a chunk's bound (float)
+    kMiscSums = 16,      // [12] window search: log2 alpha sums of chunks (float)
+};
+
+// log2 alpha of one (token, head), clamped like the scan's decay prefix, from alpha or from
+// the gate pre-activation a (log2 alpha = -e^A softplus(a + b_alpha) / ln 2)
+__device__ __forceinline__ float wide_log2_alpha(const PrefillArgs &a, float x, int h)
+{
+    if (a.gate_A) {
+        const float u = x + a.gate_b_alpha[h];
+        const float sp = u > 20.f ? u : log1pf(__expf(u));
+        return fmaxf(-__expf(a.gate_A[h]) * sp * 1.44269504088896341f, kLog2AlphaFloor);
+    }
+    return fmaxf(__builtin_amdgcn_logf(x), kLog2AlphaFloor);
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += wave_xor(x, m);
+    return x;
+}
+
+// V tile byte address: 256-byte rows, granule g of row r at slot g ^ 4 (r % 4), so the four
+// rows a transposing read meets land on distinct slots.
+template <int DV>
+__device__ __forceinline__ int vswz(int row, int col)
+{
+    const int b = col * 2;
+    return row * (DV * 2) + ((((b >> 4) ^ ((row & 3) << 2))) << 4) + (b & 15);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
+{
+    using L = LdsWide<DK, DV>;
+    using OP = uint16_t;
+    using M = Mma<OP>;
+    constexpr int MBK = DK / 16;           // 16-row blocks of the state
+    constexpr int KBD = DK / 32;           // K-blocks over the key dimension
+    constexpr int KG = DK / 8;             // 16-byte granules per key row
+    constexpr int CK = L::szK / 1024;      // 1 KiB copies per K or Q tile
+    constexpr int CV = L::szV / 1024;      // ... per V tile
+    static_assert(DV == 128 && DK == 128, "the wide scan is built for 128 x 128 states");
+    static_assert(CK % kWidePrep == 0 && CV % kWidePrep == 0, "copy split");
+
+    __shared__ __align__(16) unsigned char smem[L::total];
+    const PrefillArgs &a = w.a;
+    const int tid = threadIdx.x;
+    int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int ln = lane & 15, lg = lane >> 4;
+    // Called at the top of every chunk step: the lane index becomes opaque to the optimizer,
+    // so the LDS addresses derived from it are formed inside the step instead of being hoisted
+    // out of the loop (where they would outnumber the registers and spill).
+    auto refresh_lane = [&]() {
+        asm volatile("" : "+v"(lane));
+        ln = lane & 15;
+        lg = lane >> 4;
+    };
+    int *const misc = (int *)(smem + L::sMisc);
+    float *const miscf = (float *)(smem + L::sMisc);
+    typedef __attribute__((address_space(3))) int lint;
+    lint *const misc_l = (lint *)(smem + L::sMisc);
+
+    // ---- job ----
+    typedef __attribute__((address_space(1))) int32_t gint;
+    if (tid == 0)
+        misc[kMiscJob] = w.counter ? __hip_atomic_fetch_add((gint *)w.counter, 1, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                   : (int)blockIdx.x;
+    if (tid == 1) misc[kMiscPbar] = 0;
+    if (tid == 2) miscf[kMiscLamWin] = 0.f;
+    __syncthreads();
+    const int job = misc[kMiscJob];
+    const int H = a.H;
+    const long long njobs = (long long)(a.table ? *a.n_entries : a.num_seqs) * H;
+    if (job >= njobs) return;
+    const int e = job / H, h = job % H;
+    int n, seg, nseg, len;
+    long long tok0;
+    if (a.table) {
+        const SegEntry en = a.table[e];
+        n = en.n;
+        tok0 = en.tok0;
+        len = en.len;
+        seg = en.seg;
+        nseg = en.nseg;
+    } else {
+        n = e;
+        seq_bounds(a, n, tok0, len);
+        seg = 0;
+        nseg = 1;
+    }
+    long long srow0;
+    int slen;
+    seq_bounds(a, n, srow0, slen);
+    const int c0 = (int)((tok0 - srow0) / kChunk);      // first own chunk in the sequence
+    const int nown = (len + kChunk - 1) / kChunk;
+
+    // ---- warm-up window (segments after a sequence's first) ----
+    // mode 0: start from S0 (or zero) at c0; 1: warm up from zero over [b, c0), verify;
+    // 2: warm up from S0 over [0, c0) (exact); 3: wait for the previous segment's end state
+    int b = c0, mode = 0;
+    if (seg > 0) {
+        const int R = c0 < w.wmax ? c0 : w.wmax;
+        float cum = 0.f;
+        int found = -1;
+        float *const sums = miscf + kMiscSums;
+        for (int r0 = 0; r0 < R && found < 0; r0 += kWideWaves) {
+            const int i = r0 + wave;
+            float s = 0.f;
+            if (i < R) {
+                const long long t = srow0 + (long long)(c0 - 1 - i) * kChunk + lane;
+                s = wave_sum(wide_log2_alpha(a, a.alpha[t * H + h], h));
+            }
+            if (lane == 0) sums[wave] = s;
+            __syncthreads();
+            for (int q = 0; q < kWideWaves && r0 + q < R; ++q) {
+                cum += sums[q];
+                if (cum <= kWarmAlpha) {
+                    found = r0 + q;
+                    break;
+                }
+            }
+            __syncthreads();
+        }
+        if (found >= 0) {
+            b = c0 - 1 - found;
+            mode = b == 0 ? 2 : 1;
+        } else if (R == c0) {
+            b = 0;
+            mode = 2;
+        } else {
+            mode = 3;
+        }
+    }
+    const int nwarm = c0 - b;
+    const int nch = nwarm + nown;
+    auto nvalid = [&](int j) {          // valid tokens of processed chunk j
+        const int r = slen - (b + j) * kChunk;
+        return r < kChunk ? r : kChunk;
+    };
+    auto row0_of = [&](int j) { return srow0 + (long long)(b + j) * kChunk; };
+    auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    // ================================================================ prep waves
+    if (wave >= kWideCol) {
+        const int pw = wave - kWideCol;
+        typedef __attribute__((address_space(3))) void lds_void;
+        const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
+        auto copy_chunk_kq = [&](int j, bool with_k, bool with_q) {
+            const long long t0 = row0_of(j);
+            const int last = nvalid(j) - 1;
+            const unsigned char *ck = (const unsigned char *)a.k + (t0 * H + h) * (long long)DK * 2;
+            const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + h) * (long long)DK * 2;
+            unsigned char *dk = smem + L::sK + (j % 3) * L::szK;
+            unsigned char *dq = smem + L::sQ + (j & 1) * L::szK;
+#pragma unroll
+            for (int q = 0; q < CK / kWidePrep; ++q) {
+                const int jj = pw * (CK / kWidePrep) + q;
+                const int P = 64 * jj + lane;
+                const int r = P / KG, pg = P % KG;
+                const int lgq = kq_logical<DK>(r, pg);
+                if (with_k) {
+                    const int rk = split_orig(r) < last ? split_orig(r) : last;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)(ck + (unsigned)rk * rsK + 16 * lgq),
+                        (lds_void *)(dk + 1024 * jj), 16, 0, 0);
+                }
+                if (with_q) {
+                    const int rq = r < last ? r : last;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)(cq + (unsigned)rq * rsK + 16 * lgq),
+                        (lds_void *)(dq + 1024 * jj), 16, 0, 0);
+                }
+            }
+        };
+        auto copy_chunk_v = [&](int j) {
+            const long long t0 = row0_of(j);
+            const int last = nvalid(j) - 1;
+            const unsigned char *cv = (const unsigned char *)a.v + (t0 * H + h) * (long long)DV * 2;
+            unsigned char *dv = smem + L::sV + (j & 1) * L::szV;
+#pragma unroll
+            for (int q = 0; q < CV / kWidePrep; ++q) {
+                const int jj = pw * (CV / kWidePrep) + q;
+                const int byte = 1024 * jj + 16 * lane;
+                const int r = byte / (DV * 2), p = (byte % (DV * 2)) >> 4;
+                const int g = p ^ ((r & 3) << 2);
+                const int rv = r < last ? r : last;
+                __builtin_amdgcn_global_load_lds((const void *)(cv + (unsigned)rv * rsV + 16 * g),
+                                                 (lds_void *)(dv + 1024 * jj), 16, 0, 0);
+            }
+        };
+        auto copy_chunk_gates = [&](int j) {
+            if (pw < 2) {
+                const long long t0 = row0_of(j);
+                const int last = nvalid(j) - 1;
+                const int tc = lane < last ? lane : last;
+                const float *src = (pw == 0 ? a.alpha : a.beta) + (t0 + tc) * H + h;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)src, (lds_void *)(smem + L::sAB + (j & 1) * 512 + pw * 256), 4,
+                    0, 0);
+            }
+        };
+        // g and beta of chunk j in this wave's own slot (no other wave reads it)
+        auto gates = [&](int j) {
+            const float *ab = (const float *)(smem + L::sAB + (j & 1) * 512);
+            float *pg = (float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            const int nv = nvalid(j);
+            float x = 0.f, bt = 0.f;
+            if (lane < nv) {
+                x = wide_log2_alpha(a, ab[lane], h);
+                const float rb = ab[64 + lane];
+                bt = a.gate_A ? __builtin_amdgcn_rcpf(1.f + __expf(-rb)) : rb;
+            }
+            x += dpp_f32<0x111, 0xf>(x);
+            x += dpp_f32<0x112, 0xf>(x);
+            x += dpp_f32<0x114, 0xf>(x);
+            x += dpp_f32<0x118, 0xf>(x);
+            x += dpp_f32<0x142, 0xa>(x);
+            x += dpp_f32<0x143, 0xc>(x);
+            pg[lane] = x;
+            pg[64 + lane] = bt;
+        };
+        int pbar_target = 0;
+        auto prep_barrier = [&]() {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_fetch_add(misc_l + kMiscPbar, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            pbar_target += kWidePrep;
+            while (__hip_atomic_load(misc_l + kMiscPbar, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP) < pbar_target)
+                __builtin_amdgcn_s_sleep(1);
+            asm volatile("" ::: "memory");
+        };
+        // T' of chunk j (and its key terms of the transition bound).  Wave pw owns block row
+        // and column pw of the 4 x 4 grid of 16 x 16 blocks.
+        auto make_t = [&](int j) {
+            const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
+            unsigned char *bT = smem + L::sT + (j & 1) * L::szT;
+            const float *sG = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            const float *sBeta = sG + 64;
+            float *sA = (float *)(smem + L::sA);
+            float *sX = (float *)(smem + L::sX);
+            const int d0 = pw * 16;
+            const int np = pw < 2 ? 3 : 2;
+            const int tb0 = pw == 0 ? 1 : (pw == 1 ? 2 : (pw == 2 ? 2 : 3));
+            const int ib0 = pw == 0 ? 0 : (pw == 1 ? 0 : (pw == 2 ? 1 : 2));
+            const int ib1 = pw == 0 ? 0 : 1;
+            const int tbs[3] = {pw, tb0, 3};
+            const int ibs[3] = {pw, ib0, ib1};
+            f32x4 accG[3];
+#pragma unroll
+            for (int p = 0; p < 3; ++p) accG[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) {
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    if (p < np) {
+                        const auto ai = ldfrag_kq<DK>(bK, split_pos(ibs[p] * 16 + ln), kb * 32 + 8 * lg);
+                        const auto bt = ldfrag_kq<DK>(bK, split_pos(tbs[p] * 16 + ln), kb * 32 + 8 * lg);
+                        M::mma(accG[p], ai, bt);
+                    }
+                }
+            }
+            // accG[p][r] = k_i . k_t, i = ib 16 + 4 lg + r, t = tb 16 + ln
+            // key terms of the bound: max(0, log2 |1 - beta_t ||k_t||^2|) over this block row
+            {
+                float term = 0.f;
+                if (lg == (ln >> 2)) {
+                    const float kk = accG[0][ln & 3];
+                    const float bt = sBeta[d0 + ln];
+                    term = fmaxf(__builtin_amdgcn_logf(fabsf(1.f - bt * kk)), 0.f);
+                }
+                term = wave_sum(term);
+                if (lane == 0) miscf[kMiscLamPart + (j & 1) * 4 + pw] = term;
+            }
+            auto masked = [&](int tb, int ib, f32x4 g_, f32x4 &av) {
+                const int t = tb * 16 + ln;
+                const float gt = sG[t];
+                const float bt_ = sBeta[t];
+                const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ib * 16 + 4 * lg + r;
+                    av[r] = (i < t) ? bt_ * g_[r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+                }
+            };
+            f32x4 nT, a1, a2;
+            masked(pw, pw, accG[0], nT);
+            masked(tb0, ib0, accG[1], a1);
+            if (np == 3) masked(3, ib1, accG[2], a2);
+            f32x4 nC;
+            {
+                const int t = d0 + ln;
+                const float gt = sG[t];
+                const f32x4 gi = *(const f32x4 *)(sG + d0 + 4 * lg);
+                const f32x4 bi = *(const f32x4 *)(sBeta + d0 + 4 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = d0 + 4 * lg + r;
+                    nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
+                }
+            }
+            // blocks above the diagonal of T' are zero
+#pragma unroll
+            for (int jb = 1; jb < 4; ++jb) {
+                if (jb > pw)
+                    M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), 16 * jb + 4 * lg)),
+                            f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+            // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0
+            f32x4 eye;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) eye[r] = (4 * lg + r == ln) ? 1.f : 0.f;
+            const Sp snT = split4(nT), snC = split4(nC);
+            const f32x4 n2C = mm3r(snT, snC), n2T = mm3r(snC, snT);
+            const Sp sn2C = split4(n2C), sn2T = split4(n2T);
+            const f32x4 m1C = mm3r(snT, sn2C), m1T = mm3r(sn2C, snT);
+            const f32x4 n4C = mm3r(sn2T, sn2C), n4T = mm3r(sn2C, sn2T);
+            const f32x4 p1C = eye - nC + n2C - m1C, p1T = eye - nT + n2T - m1T;
+            const Sp sn4C = split4(n4C), sp1T = split4(p1T);
+            const f32x4 n8C = mm3r(split4(n4T), sn4C);
+            f32x4 p2C = p1C, p2T = p1T;
+            mm3(p2C, sp1T, sn4C);
+            mm3(p2T, sn4C, sp1T);
+            const Sp sn8C = split4(n8C), sp2T = split4(p2T);
+            f32x4 xC = p2C, xT = p2T;
+            mm3(xC, sp2T, sn8C);
+            mm3(xT, sn8C, sp2T);
+            auto ablk = [&](int i, int m) {
+                return sA + ((i * (i - 1) / 2 + m) * 16 + ln) * L::LDB + 4 * lg;
+            };
+            *(f32x4 *)ablk(tb0, ib0) = a1;
+            if (np == 3) *(f32x4 *)ablk(3, ib1) = a2;
+            *(f32x4 *)(sX + (d0 + ln) * L::LDX + 4 * lg) = xT;
+            {
+                const f32x4 bcol = *(const f32x4 *)(sBeta + d0 + 4 * lg);
+                M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), d0 + 4 * lg)), xT * bcol);
+            }
+            prep_barrier();
+            // off-diagonal blocks of X down block column pw:
+            // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj, stored as T'_ij = X_ij diag(beta_j)
+            {
+                const int jc = pw;
+                const float bcol = sBeta[16 * jc + ln];
+                auto arow = [&](int i, int m) { return split4(*(const f32x4 *)ablk(i, m)); };
+                auto xrow = [&](int i) {
+                    return split4(*(const f32x4 *)(sX + (16 * i + ln) * L::LDX + 4 * lg));
+                };
+                auto put_t = [&](int i, f32x4 z) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Elem<OP>::store((OP *)(bT + swz<OP, kChunk>(split_pos(16 * i + 4 * lg + r), 16 * jc + ln)),
+                                        z[r] * bcol);
+                };
+                if (jc <= 2) {
+                    const Sp xjj = split4(xC);
+                    f32x4 acc1 = mm3r(arow(jc + 1, jc), xjj);
+                    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
+                    if (jc + 2 <= 3) acc2 = mm3r(arow(jc + 2, jc), xjj);
+                    if (jc + 3 <= 3) acc3 = mm3r(arow(jc + 3, jc), xjj);
+                    const f32x4 x1 = -mm3r(xrow(jc + 1), split4(acc1));
+                    put_t(jc + 1, x1);
+                    if (jc + 2 <= 3) {
+                        const Sp sx1 = split4(x1);
+                        mm3(acc2, arow(jc + 2, jc + 1), sx1);
+                        if (jc + 3 <= 3) mm3(acc3, arow(jc + 3, jc + 1), sx1);
+                        const f32x4 x2 = -mm3r(xrow(jc + 2), split4(acc2));
+                        put_t(jc + 2, x2);
+                        if (jc + 3 <= 3) {
+                            mm3(acc3, arow(jc + 3, jc + 2), split4(x2));
+                            const f32x4 x3 = -mm3r(xrow(jc + 3), split4(acc3));
+                            put_t(jc + 3, x3);
+                        }
+                    }
+                }
+            }
+            // the bound of a warm-up chunk joins the window's sum (fixed order of terms)
+            if (pw == 0 && j < nwarm && lane == 0) {
+                const float *part = miscf + kMiscLamPart + (j & 1) * 4;
+                const float lam = sG[kChunk - 1] + part[0] + part[1] + part[2] + part[3];
+                miscf[kMiscLamWin] += lam;
+            }
+        };
+        // P = lower_incl(Q K^T (.) Gamma) of chunk j as the six operand fragments the column
+        // waves read (fragment f < 4: rows 16 f .. 16 f + 15, columns 0 .. 31; fragments 4, 5:
+        // rows 32 .. 47 and 48 .. 63, columns 32 .. 63).  The K operand takes the tile's rows as
+        // they lie (internal token order), so the two accumulator blocks of a 32-column half
+        // pack into a fragment directly: accumulator [r] of block (tb, ib) = k_i . q_t,
+        // t = 16 tb + ln, i = 32 (ib / 2) + 8 lg + 4 (ib % 2) + r.
+        auto make_p = [&](int j) {
+            const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
+            const unsigned char *bQ = smem + L::sQ + (j & 1) * L::szK;
+            const float *gc = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            unsigned char *bP = smem + L::sP + (j & 1) * L::szP;
+            constexpr int kTb[12] = {0, 0, 1, 1, 2, 2, 3, 3, 2, 2, 3, 3};
+            constexpr int kIb[12] = {0, 1, 0, 1, 0, 1, 0, 1, 2, 3, 2, 3};
+            // g is non-increasing inside a chunk: while the chunk's total decay stays above
+            // -60, 2^g_t and 2^-g_i are both normal and Gamma_ti is their product; below,
+            // every element takes its own 2^(g_t - g_i) (0 * inf otherwise)
+            const float gC = gc[kChunk - 1];
+            const bool factored = gC >= -60.f;
+            // fragments of this wave: 0 and 1 for waves 0 and 1, {2, 4} and {3, 5} for 2, 3
+            const int nf = pw < 2 ? 1 : 2;
+#pragma unroll
+            for (int fi = 0; fi < 2; ++fi) {
+                if (fi >= nf) break;
+                const int f = fi == 0 ? pw : pw + 2;
+                const int p0 = 2 * f;
+                const int tb = kTb[p0];
+                f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kb = 0; kb < KBD; ++kb) {
+                    const bf16x8 fq = ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int ib = kIb[p0 + u];
+                        M::mma(acc[u], ldfrag_kq<DK>(bK, ib * 16 + ln, kb * 32 + 8 * lg), fq);
+                    }
+                }
+                const int t = tb * 16 + ln;
+                const float gt = gc[t];
+                const float et = __builtin_amdgcn_exp2f(gt);
+                f32x4 pv[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int ib = kIb[p0 + u];
+                    const f32x4 gi = *(const f32x4 *)(gc + 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
+                        const float dec = factored ? et * __builtin_amdgcn_exp2f(-gi[r])
+                                                   : __builtin_amdgcn_exp2f(gt - gi[r]);
+                        pv[u][r] = (i <= t) ? acc[u][r] * dec : 0.f;
+                    }
+                }
+                *(bf16x8 *)(bP + (f * 64 + lane) * 16) = pack8s(pv[0], pv[1]);
+            }
+        };
+        // Decay factors of chunk j (wave 3): the scan holds S = 2^ls Shat; ls starts at 0 and
+        // after each chunk becomes ls + g_C, or 0 when that would fall below -32 (the column
+        // waves then rescale Shat by the same rule on the same g_C).
+        //   F[t] = gamma_t 2^ls,  F[64 + t] = (gamma_C / gamma_t) / 2^ls',  F[128] = g_C
+        float lsl = 0.f;
+        auto factors = [&](int j) {
+            const float *gc = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            float *F = (float *)(smem + L::sF + (j & 1) * L::szF);
+            const float gt = gc[lane], gC = gc[kChunk - 1];
+            const float lsc = lsl;
+            float lsn = lsc + gC;
+            if (lsn < -32.f) lsn = 0.f;
+            F[lane] = __builtin_amdgcn_exp2f(gt + lsc);
+            F[64 + lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
+            if (lane == 0) F[128] = gC;
+            lsl = lsn;
+        };
+
+        if (nch > 0) {
+            copy_chunk_kq(0, true, true);
+            copy_chunk_v(0);
+            copy_chunk_gates(0);
+            if (nch > 1) {
+                copy_chunk_kq(1, true, false);
+                copy_chunk_gates(1);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();                                  // #0: chunk 0 (and K, gates of 1) staged
+        if (nch > 0) {
+            gates(0);
+            make_t(0);
+            if (pw == 3) factors(0);
+        }
+        lds_barrier();                                  // #1: T'(0), factors(0)
+        for (int j = 0; j < nch; ++j) {
+            refresh_lane();
+            if (j + 2 < nch) {
+                copy_chunk_kq(j + 2, true, false);
+                copy_chunk_gates(j + 2);
+            }
+            if (j + 1 < nch) {
+                copy_chunk_kq(j + 1, false, true);
+                copy_chunk_v(j + 1);
+            }
+            if (j + 1 < nch) {
+                gates(j + 1);
+                make_t(j + 1);
+                if (pw == 3) factors(j + 1);
+            }
+            if (j >= nwarm) make_p(j);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ================================================================ column waves
+    const int cw = wave;
+    const int tile = cw >> 1, sw = cw & 1;
+    // this lane's state column: the two waves of a 32-column tile interleave in runs of four,
+    // so a lane of the output layout holds 4 columns that sit next to the other wave's 4
+    const int col = 32 * tile + 8 * (ln >> 2) + 4 * sw + (ln & 3);
+    const long long stride_s = (long long)DK * DV;
+    f32x4 S[MBK];
+    auto load_state = [&](const float *src, float scale) {
+#pragma unroll
+        for (int m = 0; m < MBK; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[m][i] = src ? src[(long long)split_orig(16 * m + 4 * lg + i) * DV + col] * scale
+                              : 0.f;
+    };
+    // the previous segment's published end state (exact chain)
+    auto wait_previous = [&]() -> const float * {
+        const int pj = (e - 1) * H + h;
+        gint *flag = (gint *)(w.flags + pj);
+        long long spins = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < kWideCol) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > (1ll << 26)) {          // a bounded wait: never expected to end here
+                if (lane == 0)
+                    __hip_atomic_fetch_or((gint *)w.error, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                return nullptr;
+            }
+        }
+        return w.seg_state + (long long)pj * stride_s;
+    };
+    if (mode == 0 || mode == 2)
+        load_state(a.s0 ? a.s0 + ((long long)n * H + h) * stride_s : nullptr, 1.f);
+    else if (mode == 1)
+        load_state(nullptr, 1.f);
+    else
+        load_state(wait_previous(), 1.f);
+
+    bf16x8 Sb[KBD];
+    auto pack_state = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) Sb[kb] = pack8s(S[2 * kb], S[2 * kb + 1]);
+    };
+    pack_state();
+    float ls = 0.f;
+    // carried from chunk j to step j + 1: gamma 2^ls (Shat^T Q^T) and bf16 U
+    f32x4 yq[4];
+    bf16x8 Uu0 = {}, Uu1 = {};
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) yq[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Y of chunk jp = carried gamma 2^ls (Shat^T Q^T) + U^T P^T, P from buffer jp % 2
+    auto finish = [&](int jp) {
+        const unsigned char *bP = smem + L::sP + (jp & 1) * L::szP;
+        const long long t0 = row0_of(jp);
+        const int nv = nvalid(jp);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+            M::mma(pu, Uu0, *(const bf16x8 *)(bP + (tb * 64 + lane) * 16));
+            if (tb >= 2) M::mma(pu, Uu1, *(const bf16x8 *)(bP + ((tb + 2) * 64 + lane) * 16));
+            const f32x4 yv = yq[tb] + pu;
+            const int t = tb * 16 + ln;
+            if (t < nv)
+                store4((OP *)a.y + ((t0 + t) * H + h) * (long long)DV + 32 * tile + 8 * lg + 4 * sw,
+                       yv);
+        }
+    };
+
+    lds_barrier();            // #0
+    lds_barrier();            // #1
+    for (int j = 0; j < nch; ++j) {
+        refresh_lane();
+        if (mode == 1 && j == nwarm) {
+            // the warm-up reached the bound, or the exact chain takes over
+            const float lw = __builtin_bit_cast(
+                float, __hip_atomic_load(misc_l + kMiscLamWin, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (!(lw <= kWarmBound)) {
+                load_state(wait_previous(), __builtin_amdgcn_exp2f(-ls));
+                pack_state();
+            }
+        }
+        const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
+        const unsigned char *bQ = smem + L::sQ + (j & 1) * L::szK;
+        const unsigned char *bV = smem + L::sV + (j & 1) * L::szV;
+        const unsigned char *bT = smem + L::sT + (j & 1) * L::szT;
+        const float *F = (const float *)(smem + L::sF + (j & 1) * L::szF);
+        const bool normal = j >= nwarm;
+
+        // ---- K Shat (the head of the state chain) ----
+        f32x4 acc_ks[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc_ks[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            bf16x8 fk[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) fk[tb] = ldfrag_kq<DK>(bK, tb * 16 + ln, kb * 32 + 8 * lg);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) M::mma(acc_ks[tb], fk[tb], Sb[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 ft[6];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) ft[mb] = ldfrag<OP, kChunk>(bT, mb * 16 + ln, 8 * lg);
+        ft[4] = ldfrag<OP, kChunk>(bT, 32 + ln, 32 + 8 * lg);
+        ft[5] = ldfrag<OP, kChunk>(bT, 48 + ln, 32 + 8 * lg);
+
+        // ---- R = V - diag(gamma 2^ls) K Shat;  U = T' R ----
+        f32x4 U[4];
+        {
+            f32x4 R[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                // V[o0 .. o0 + 3][column] by one transposing read: lane j receives column
+                // 32 tile + 8 (j / 4) + 4 sw + j % 4 of rows o0 .. o0 + 3
+                const int o0 = split_orig(tb * 16 + 4 * lg);
+                const f32x4 gam = *(const f32x4 *)(F + o0);
+                const bf16x4 v4 = ldtr(bV + vswz<DV>(o0 + (ln >> 2), 32 * tile + 8 * (ln & 3) + 4 * sw));
+                R[tb] = __builtin_convertvector(v4, f32x4) - gam * acc_ks[tb];
+            }
+            const bf16x8 Rb0 = pack8s(R[0], R[1]);
+            const bf16x8 Rb1 = pack8s(R[2], R[3]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                M::mma(U[mb], ft[mb], Rb0);
+            }
+            M::mma(U[2], ft[4], Rb1);
+            M::mma(U[3], ft[5], Rb1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- Y of chunk j - 1 (its P arrived with this step), then chunk j's carries ----
+        if (j >= 1 && j - 1 >= nwarm) finish(j - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (normal) {
+            // gamma 2^ls (Shat^T Q^T), off the state chain
+            f32x4 accQ[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) accQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    M::mma(accQ[tb], Sb[kb], ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) yq[tb] = accQ[tb] * F[tb * 16 + ln];
+            Uu0 = pack8s(U[0], U[1]);
+            Uu1 = pack8s(U[2], U[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U ----
+        auto frag_kt = [&](int m, int kt) {
+            const int c = 32 * (m >> 1) + 8 * (ln & 3) + 4 * (m & 1);
+            const int t = 32 * kt + 8 * lg + (ln >> 2);
+            const bf16x4 lo = ldtr(bK + swz_kq<DK>(split_pos(t), c));
+            const bf16x4 hi = ldtr(bK + swz_kq<DK>(split_pos(t + 4), c));
+            return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        {
+            float ln_ = ls + F[128];
+            ln_ = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ln_)));
+            if (ln_ < -32.f) {                     // fold the scale into Shat (rare)
+                const float f = __builtin_amdgcn_exp2f(ln_);
+#pragma unroll
+                for (int m = 0; m < MBK; ++m) S[m] *= f;
+                ln_ = 0.f;
+            }
+            ls = ln_;
+            bf16x8 Ub[2];
+            {
+                f32x4 Us[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    const f32x4 rho = *(const f32x4 *)(F + 64 + split_orig(mb * 16 + 4 * lg));
+                    Us[mb] = U[mb] * rho;
+                }
+                Ub[0] = pack8s(Us[0], Us[1]);
+                Ub[1] = pack8s(Us[2], Us[3]);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    bf16x8 fkt[MBK / 2];
+#pragma unroll
+                    for (int q = 0; q < MBK / 2; ++q) fkt[q] = frag_kt(half * (MBK / 2) + q, kt);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int q = 0; q < MBK / 2; ++q)
+                        M::mma(S[half * (MBK / 2) + q], fkt[q], Ub[kt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        pack_state();
+        lds_barrier();
+    }
+    if (nch > 0 && nch - 1 >= nwarm) finish(nch - 1);
+
+    // ---- state out: the final state of the sequence, or the segment's end state for the
+    // next segment's workgroup ----
+    const float sp = __builtin_amdgcn_exp2f(ls);
+    float *dst = nullptr;
+    const bool publish = a.table && seg < nseg - 1;
+    if (publish) dst = w.seg_state + (long long)job * stride_s;
+    else if (a.s_final) dst = a.s_final + ((long long)n * H + h) * stride_s;
+    if (dst) {
+#pragma unroll
+        for (int m = 0; m < MBK; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[(long long)split_orig(16 * m + 4 * lg + i) * DV + col] = S[m][i] * sp;
+    }
+    if (publish) {
+        // every lane's stores are ordered before its wave's release of the flag
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0)
+            __hip_atomic_fetch_add((gint *)(w.flags + job), 1, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// =========================================================================================
+// Host side
+// =========================================================================================
+hipError_t launch_wide_scan(const WideArgs &w, long long jobs, hipStream_t stream)
+{
+    if (jobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL((wide_scan_kernel<128, 128>), dim3((unsigned)jobs),
+                       dim3(64 * kWideWaves), 0, stream, w);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

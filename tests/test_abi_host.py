@@ -45,19 +45,35 @@ def test_status_strings_and_version(lib):
 
 
 def test_plans_for_the_workloads(lib):
-    # 64 chains (B=4, H=16): split the state columns, never the sequences
+    # bf16, d_k = d_v = 128: the one-launch scan with the whole state per workgroup; 64 chains
+    # (B=4, H=16) are split into segments of 16 chunks (256 jobs)
     t, s = gdn.gdn_prefill_plan(4, 4 * 4096, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert t in (32, 64) and s == -1
-    # 16 chains of 1M tokens: segment-parallel scan
+    assert t == 128 and s == 16
+    # 16 chains of 1M tokens: about 1024 segments
     t, s = gdn.gdn_prefill_plan(1, 1 << 20, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert s > 0
-    assert gdn.gdn_prefill_workspace_bytes(1, 1 << 20, 16, 128, 128, 1) > 0
-    # 512 chains: enough work without splitting
+    assert t == 128 and 200 <= s <= 300
+    # 512 packed chains: segments of about 60 chunks balance the unequal lengths
     t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert t == 128 and 32 <= s <= 128
+    # its workspace: the segment table, a control block, flags and one fp32 end state per
+    # (segment, head)
+    entries = 32 + -(-270336 // (s * 64))
+    w = gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1)
+    assert entries * 16 * 128 * 128 * 4 < w < entries * 16 * 128 * 128 * 4 + (64 << 10)
+    # 1024 chains or more: no segments, no workspace
+    t, s = gdn.gdn_prefill_plan(64, 64 * 256, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert t == 128 and s == -1
+    assert gdn.gdn_prefill_workspace_bytes(64, 64 * 256, 16, 128, 128, 1) == 0
+    # equal lengths that fit one segment are not split
+    t, s = gdn.gdn_prefill_plan(2, 2 * 512, 4, 128, 128, gdn.GDN_DTYPE_BF16)
     assert s == -1
-    # bf16: one 8448-byte record (T', g) per chunk slot and head
+    # bf16 with 32-column tiles (the two-launch path): one 8448-byte record (T', g) per chunk
+    # slot and head
     slots = 270336 // 64 + 32
-    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == slots * 16 * 8448
+    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1, 32, -1) == slots * 16 * 8448
+    # other head sizes keep the column-split plans
+    t, s = gdn.gdn_prefill_plan(4, 4 * 4096, 16, 64, 128, gdn.GDN_DTYPE_BF16)
+    assert t in (16, 32, 64)
     # fp32 without segments needs no workspace
     assert gdn.gdn_prefill_workspace_bytes(1, 256, 2, 64, 64, 0) == 0
     # fp32 tiles stay within the LDS budget
@@ -111,8 +127,8 @@ def prefill(lib, **kw):
     (dict(s0=8 * G, y=8 * G), gdn.GDN_ERR_INVALID_ARGUMENT),   # y overlaps initial state
     (dict(s0=8 * G, sf=8 * G + 256), gdn.GDN_ERR_INVALID_ARGUMENT),  # partial overlap
     (dict(s0=8 * G, sf=8 * G, seg=2), gdn.GDN_ERR_INVALID_ARGUMENT),  # in place + split
-    (dict(ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # bf16 chunk records
-    (dict(wsb=6 * 2 * 8448 - 1), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+    (dict(tile=32, ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # bf16 chunk records
+    (dict(tile=32, wsb=6 * 2 * 8448 - 1), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
     (dict(seg=2, ws=None, wsb=0), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),   # segments too
     (dict(seg=2, ws=9 * G, wsb=64), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
 ])
@@ -375,7 +391,8 @@ def prefill_gated(lib, **kw):
     (dict(A=10 * G + 2), gdn.GDN_ERR_INVALID_ARGUMENT),   # 4-byte alignment
     (dict(A=6 * G + 64), gdn.GDN_ERR_INVALID_ARGUMENT),   # A inside y
     (dict(bal=7 * G), gdn.GDN_ERR_INVALID_ARGUMENT),      # b_alpha under the final state
-    (dict(wsb=16), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+    # sequences long enough to be split into segments need a workspace
+    (dict(T=2 * 8192, wsb=16), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_prefill_gated_rejects(lib, kw, code):
     assert prefill_gated(lib, **kw) == code

@@ -99,6 +99,51 @@ def test_segmented_pipelined_scan_slow_decay(dev, oracle_lib, tile, seg):
                   label="segmented-pipe")
 
 
+# ---- the one-launch scan (bf16, d = 128, the whole state per workgroup) -------------------
+# Segments after a sequence's first start from a warm-up over the chunks before them when the
+# transition norm over those chunks provably falls below 2^-48, and otherwise wait for the
+# previous segment's exact end state; these cases force each of the four starts.
+
+@pytest.mark.parametrize("seg", [2, 4])
+def test_wide_segments_warm_up(dev, oracle_lib, seg):
+    """Strong decay (sigmoid(N(1, 2))): every later segment starts from a verified warm-up."""
+    inp = _inp([3000, 1100, 64, 65, 0, 700], H=2, seed=50 + seg, alpha=(1.0, 2.0),
+               beta=(0.0, 1.5))
+    check_prefill(inp, dev, oracle_lib, dv_tile=128, segment_chunks=seg, label="wide-warm")
+
+
+def test_wide_segments_chained(dev, oracle_lib):
+    """Slow decay (sigmoid(N(8, 0.5))): no window within a segment reaches the bound, so
+    every segment takes its predecessor's published end state (and the second segment of a
+    sequence warms up from the sequence start instead)."""
+    inp = _inp([2500, 900, 130], H=3, seed=56, alpha=(8.0, 0.5))
+    check_prefill(inp, dev, oracle_lib, dv_tile=128, segment_chunks=3, label="wide-chain")
+
+
+def test_wide_segments_mixed(dev, oracle_lib):
+    """sigmoid(N(3, 1)) with segments of 8 chunks: windows of about 7-8 chunks, so some
+    segments warm up and others wait for their predecessor."""
+    inp = _inp([5000, 2000], H=4, seed=57, alpha=(3.0, 1.0))
+    check_prefill(inp, dev, oracle_lib, dv_tile=128, segment_chunks=8, label="wide-mixed")
+
+
+def test_wide_segments_unnormalised_keys(dev, oracle_lib):
+    """Keys of norm 1.5: |1 - beta ||k||^2| exceeds 1 for large beta, so the key terms of the
+    bound count and some warm-ups fail verification and fall back to the exact chain."""
+    from linear_attention_recurrence_chunked_amd import workloads as wl
+    inp = _inp([2600, 800], H=2, seed=58, alpha=(1.0, 2.0), beta=(0.0, 1.5))
+    inp["k"] = wl.bf16_bits(wl.bf16_to_f64(inp["k"]) * 1.5)
+    check_prefill(inp, dev, oracle_lib, dv_tile=128, segment_chunks=2, label="wide-keys")
+
+
+def test_wide_unsegmented_many_chains(dev, oracle_lib):
+    """1024 chains and more: no segments, one workgroup per (sequence, head)."""
+    rng = np.random.default_rng(59)
+    lengths = rng.integers(0, 300, size=130)
+    inp = _inp(lengths, H=8, seed=59)
+    check_prefill(inp, dev, oracle_lib, label="wide-unsegmented")
+
+
 def test_many_sequences_segment_table(dev, oracle_lib):
     """More sequences than one table-building pass (1024) with segments and empties."""
     rng = np.random.default_rng(21)
