@@ -64,7 +64,8 @@ def decode_bytes_per_head_step(d: int) -> int:
 
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc")
 PREFILL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_prefill_common.hpp",
-                   "gdn_prefill.hip", "gdn_prefill_split.hip"]
+                   "gdn_prefill_ops.hpp", "gdn_prefill.hip", "gdn_prefill_split.hip",
+                   "gdn_prefill_wide.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
 CHANNEL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_channel.hip"]
 QSA_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_qsa.hip"]
@@ -259,13 +260,17 @@ def main():
 
     # bf16 prefill = two launches: chunk records, then the state scan; the roofline covers
     # the pair (HIP events around the library call); rocprofv3 splits it per kernel
-    if tile <= 32:
+    if tile == 128 and d == 128:
+        kernel_name = "wide_scan_kernel<128,128>"
+        if seg >= 0:
+            kernel_name = "segment_table_kernel + " + kernel_name
+    elif tile <= 32:
         kernel_name = "chunk_prep_kernel<128> + scan_pipe_kernel<128,%d>" % tile
     elif tile <= 64:
         kernel_name = "chunk_prep_kernel<128> + scan_split_kernel<128,%d,scan>" % tile
     else:
         kernel_name = "prefill_kernel<128,%d,bf16,scan>" % tile
-    if seg >= 0:
+    if seg >= 0 and tile != 128:
         kernel_name += " (+ segment phases)"
     tok_s = T / (pre_ms * 1e-3)
     flops = prefill_flops_per_token_head(d) * T * H

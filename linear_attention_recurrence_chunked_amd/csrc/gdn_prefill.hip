@@ -789,8 +789,16 @@ static int largest_tile(int dtype, int dk, int dv)
 }
 
 // The one-launch bf16 scan (gdn_prefill_wide.hip) for d_k = d_v = 128: one workgroup per
-// (segment, head) with the whole state.  Sequences are split into segments until the jobs
-// number about four per CU (at least 16 chunks each), unless the chains alone are that many.
+// (segment, head) with the whole state.  By default it serves the sequences that the
+// column-split scan could only spread over the CUs with the segment phases (few chains of
+// many chunks); they are split into one segment per CU's worth of work.
+static bool use_wide_by_default(int num_seqs, long long total_T, int H)
+{
+    const long long chains = (long long)num_seqs * H;
+    const long long avg_chunks = cdiv(total_T, (long long)num_seqs * kChunk);
+    return chains * 4 < 256 && avg_chunks >= 64;
+}
+
 static bool make_wide_plan(int num_seqs, long long total_T, int H, int seg_chunks_req,
                            PrefillPlan *plan)
 {
@@ -798,7 +806,7 @@ static bool make_wide_plan(int num_seqs, long long total_T, int H, int seg_chunk
     const long long total_chunks = cdiv(total_T, kChunk) + num_seqs;
     int seg = seg_chunks_req;
     if (seg == 0) {
-        constexpr long long kJobs = 1024;
+        constexpr long long kJobs = 256;
         if (chains >= kJobs) {
             seg = -1;
         } else {
@@ -838,7 +846,8 @@ bool make_plan(int num_seqs, long long total_T, int H, int dk, int dv, int dtype
 {
     plan->wide = 0;
     plan->ws_wide = 0;
-    if (dtype == kDtypeBF16 && dk == 128 && dv == 128 && (dv_tile_req == 0 || dv_tile_req == 128))
+    if (dtype == kDtypeBF16 && dk == 128 && dv == 128 &&
+        (dv_tile_req == 128 || (dv_tile_req == 0 && use_wide_by_default(num_seqs, total_T, H))))
         return make_wide_plan(num_seqs, total_T, H, seg_chunks_req, plan);
     // Column tile: the chains (sequence, head) are independent; split the state columns
     // until there are enough workgroups to cover the 256 CUs, within the LDS budget.

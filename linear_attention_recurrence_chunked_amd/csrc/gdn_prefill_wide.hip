@@ -46,16 +46,18 @@ struct LdsWide {
     static constexpr int szV = kChunk * DV * 2;        // [64][DV] bf16
     static constexpr int szT = kChunk * kChunk * 2;    // T' as a 64-wide swizzled tile
     static constexpr int szP = 6 * 1024;               // P as six operand fragments
-    static constexpr int szF = 2 * kChunk * 4 + 16;    // gamma 2^ls, rho, g_C
+    static constexpr int szF = 3 * kChunk * 4 + 16;    // gamma 2^ls, rho, g_C, g
     static constexpr int szPG = 2 * kChunk * 4;        // a prep wave's g and beta of a chunk
-    static constexpr int LDB = 20;                     // padded fp32 rows of an A block
-    static constexpr int LDX = 20;                     // padded rows of a diagonal X block
+    static constexpr int szY = kChunk * DV * 2;        // y of a chunk, bf16 rows (staging)
+    static constexpr int LDB = 16;                     // fp32 rows of an A block
+    static constexpr int LDX = 16;                     // rows of a diagonal X block
     static constexpr int sK = 0;                       // chunk j in stage j % 3
     static constexpr int sQ = sK + 3 * szK;            // chunk j in stage j % 2
     static constexpr int sV = sQ + 2 * szK;            // chunk j in stage j % 2
-    static constexpr int sT = sV + 2 * szV;            // chunk j in buffer j % 2
-    static constexpr int sP = sT + 2 * szT;            // chunk j in buffer j % 2
-    static constexpr int sAB = sP + 2 * szP;           // raw gates [alpha 64][beta 64], j % 2
+    static constexpr int sT = sV + 2 * szV;            // T' of the chunk being scanned, then of the next
+    static constexpr int sP = sT + szT;                // P of the chunk whose y is formed next
+    static constexpr int sY = sP + szP;                // y rows on their way to memory
+    static constexpr int sAB = sY + szY;               // raw gates [alpha 64][beta 64], j % 2
     static constexpr int sF = sAB + 2 * 512;           // factors of chunk j in buffer j % 2
     static constexpr int sPG = sF + 2 * szF;           // [prep wave][j % 2] g, beta
     static constexpr int sA = sPG + kWidePrep * 2 * szPG;   // six strictly lower A blocks
@@ -72,16 +74,26 @@ enum {
     kMiscLamWin = 2,     // running log2 bound over the warm-up chunks (float)
     kMiscLamPart = 4,    // [2][4] per-wave key terms of a chunk's bound (float)
     kMiscSums = 16,      // [12] window search: log2 alpha sums of chunks (float)
+    kMiscCntT = 28,      // column waves that read the T' of their chunk (one count per step)
+    kMiscCntP = 29,      // column waves that read the P of the previous chunk (one per step)
+    kMiscCntY = 30,      // column waves that staged their y pieces
 };
 
-// log2 alpha of one (token, head), clamped like the scan's decay prefix, from alpha or from
-// the gate pre-activation a (log2 alpha = -e^A softplus(a + b_alpha) / ln 2)
-__device__ __forceinline__ float wide_log2_alpha(const PrefillArgs &a, float x, int h)
+// The gate parameters of one head: alpha itself, or its pre-activation a with
+// log2 alpha = -e^A softplus(a + b_alpha) / ln 2 (read once per workgroup).
+struct GateHead {
+    bool pre;        // gates given as pre-activations
+    float scale;     // -e^A / ln 2
+    float b_alpha;
+};
+
+// log2 alpha of one (token, head), clamped like the scan's decay prefix
+__device__ __forceinline__ float wide_log2_alpha(const GateHead &g, float x)
 {
-    if (a.gate_A) {
-        const float u = x + a.gate_b_alpha[h];
+    if (g.pre) {
+        const float u = x + g.b_alpha;
         const float sp = u > 20.f ? u : log1pf(__expf(u));
-        return fmaxf(-__expf(a.gate_A[h]) * sp * 1.44269504088896341f, kLog2AlphaFloor);
+        return fmaxf(g.scale * sp, kLog2AlphaFloor);
     }
     return fmaxf(__builtin_amdgcn_logf(x), kLog2AlphaFloor);
 }
@@ -100,6 +112,26 @@ __device__ __forceinline__ int vswz(int row, int col)
 {
     const int b = col * 2;
     return row * (DV * 2) + ((((b >> 4) ^ ((row & 3) << 2))) << 4) + (b & 15);
+}
+
+// Direct-to-LDS copies (lane l's 16 or 4 bytes land at lds + 16 l or lds + 4 l), written in
+// inline asm so that the compiler does not treat the wave's later LDS reads as waiting on
+// them: the prep waves read other stages while these copies fly, and wait for them
+// (s_waitcnt vmcnt(0)) only before the step barrier that hands them to their readers.  The
+// instruction has no register output; M0 carries the LDS address.
+__device__ __forceinline__ unsigned lds_addr(const void *p)
+{
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void copy16_async(const void *g, unsigned lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_async(const void *g, unsigned lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
 }
 
 template <int DK, int DV>
@@ -143,6 +175,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                                    : (int)blockIdx.x;
     if (tid == 1) misc[kMiscPbar] = 0;
     if (tid == 2) miscf[kMiscLamWin] = 0.f;
+    if (tid >= 3 && tid < 6) misc[kMiscCntT + tid - 3] = 0;
     __syncthreads();
     const int job = misc[kMiscJob];
     const int H = a.H;
@@ -167,6 +200,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     long long srow0;
     int slen;
     seq_bounds(a, n, srow0, slen);
+    GateHead gh;
+    gh.pre = a.gate_A != nullptr;
+    gh.scale = gh.pre ? -__expf(a.gate_A[h]) * 1.44269504088896341f : 0.f;
+    gh.b_alpha = gh.pre ? a.gate_b_alpha[h] : 0.f;
     const int c0 = (int)((tok0 - srow0) / kChunk);      // first own chunk in the sequence
     const int nown = (len + kChunk - 1) / kChunk;
 
@@ -184,7 +221,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             float s = 0.f;
             if (i < R) {
                 const long long t = srow0 + (long long)(c0 - 1 - i) * kChunk + lane;
-                s = wave_sum(wide_log2_alpha(a, a.alpha[t * H + h], h));
+                s = wave_sum(wide_log2_alpha(gh, a.alpha[t * H + h]));
             }
             if (lane == 0) sums[wave] = s;
             __syncthreads();
@@ -215,11 +252,27 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     };
     auto row0_of = [&](int j) { return srow0 + (long long)(b + j) * kChunk; };
     auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // LDS counters between waves of the workgroup: a wave adds one after its LDS operations
+    // complete; a waiting wave spins until the count reaches its target (bounded: a count that
+    // never arrives ends the wait, so no logic error can hang the device)
+    auto lds_count = [&](int which) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0)
+            __hip_atomic_fetch_add(misc_l + which, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto lds_wait = [&](int which, int target) {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(misc_l + which, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
+                target)
+                break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    };
 
     // ================================================================ prep waves
     if (wave >= kWideCol) {
         const int pw = wave - kWideCol;
-        typedef __attribute__((address_space(3))) void lds_void;
         const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
         auto copy_chunk_kq = [&](int j, bool with_k, bool with_q) {
             const long long t0 = row0_of(j);
@@ -236,15 +289,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 const int lgq = kq_logical<DK>(r, pg);
                 if (with_k) {
                     const int rk = split_orig(r) < last ? split_orig(r) : last;
-                    __builtin_amdgcn_global_load_lds(
-                        (const void *)(ck + (unsigned)rk * rsK + 16 * lgq),
-                        (lds_void *)(dk + 1024 * jj), 16, 0, 0);
+                    copy16_async(ck + (unsigned)rk * rsK + 16 * lgq, lds_addr(dk + 1024 * jj));
                 }
                 if (with_q) {
                     const int rq = r < last ? r : last;
-                    __builtin_amdgcn_global_load_lds(
-                        (const void *)(cq + (unsigned)rq * rsK + 16 * lgq),
-                        (lds_void *)(dq + 1024 * jj), 16, 0, 0);
+                    copy16_async(cq + (unsigned)rq * rsK + 16 * lgq, lds_addr(dq + 1024 * jj));
                 }
             }
         };
@@ -260,8 +309,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 const int r = byte / (DV * 2), p = (byte % (DV * 2)) >> 4;
                 const int g = p ^ ((r & 3) << 2);
                 const int rv = r < last ? r : last;
-                __builtin_amdgcn_global_load_lds((const void *)(cv + (unsigned)rv * rsV + 16 * g),
-                                                 (lds_void *)(dv + 1024 * jj), 16, 0, 0);
+                copy16_async(cv + (unsigned)rv * rsV + 16 * g, lds_addr(dv + 1024 * jj));
             }
         };
         auto copy_chunk_gates = [&](int j) {
@@ -270,9 +318,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 const int last = nvalid(j) - 1;
                 const int tc = lane < last ? lane : last;
                 const float *src = (pw == 0 ? a.alpha : a.beta) + (t0 + tc) * H + h;
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)src, (lds_void *)(smem + L::sAB + (j & 1) * 512 + pw * 256), 4,
-                    0, 0);
+                copy4_async(src, lds_addr(smem + L::sAB + (j & 1) * 512 + pw * 256));
             }
         };
         // g and beta of chunk j in this wave's own slot (no other wave reads it)
@@ -282,9 +328,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             const int nv = nvalid(j);
             float x = 0.f, bt = 0.f;
             if (lane < nv) {
-                x = wide_log2_alpha(a, ab[lane], h);
+                x = wide_log2_alpha(gh, ab[lane]);
                 const float rb = ab[64 + lane];
-                bt = a.gate_A ? __builtin_amdgcn_rcpf(1.f + __expf(-rb)) : rb;
+                bt = gh.pre ? __builtin_amdgcn_rcpf(1.f + __expf(-rb)) : rb;
             }
             x += dpp_f32<0x111, 0xf>(x);
             x += dpp_f32<0x112, 0xf>(x);
@@ -297,21 +343,15 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         };
         int pbar_target = 0;
         auto prep_barrier = [&]() {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (lane == 0)
-                __hip_atomic_fetch_add(misc_l + kMiscPbar, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            lds_count(kMiscPbar);
             pbar_target += kWidePrep;
-            while (__hip_atomic_load(misc_l + kMiscPbar, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP) < pbar_target)
-                __builtin_amdgcn_s_sleep(1);
-            asm volatile("" ::: "memory");
+            lds_wait(kMiscPbar, pbar_target);
         };
         // T' of chunk j (and its key terms of the transition bound).  Wave pw owns block row
         // and column pw of the 4 x 4 grid of 16 x 16 blocks.
         auto make_t = [&](int j) {
             const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
-            unsigned char *bT = smem + L::sT + (j & 1) * L::szT;
+            unsigned char *bT = smem + L::sT;
             const float *sG = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
             const float *sBeta = sG + 64;
             float *sA = (float *)(smem + L::sA);
@@ -339,7 +379,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             }
             // accG[p][r] = k_i . k_t, i = ib 16 + 4 lg + r, t = tb 16 + ln
             // key terms of the bound: max(0, log2 |1 - beta_t ||k_t||^2|) over this block row
-            {
+            // (warm-up chunks only)
+            if (j < nwarm) {
                 float term = 0.f;
                 if (lg == (ln >> 2)) {
                     const float kk = accG[0][ln & 3];
@@ -376,13 +417,6 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                     nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
                 }
             }
-            // blocks above the diagonal of T' are zero
-#pragma unroll
-            for (int jb = 1; jb < 4; ++jb) {
-                if (jb > pw)
-                    M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), 16 * jb + 4 * lg)),
-                            f32x4{0.f, 0.f, 0.f, 0.f});
-            }
             // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0
             f32x4 eye;
 #pragma unroll
@@ -408,46 +442,56 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             *(f32x4 *)ablk(tb0, ib0) = a1;
             if (np == 3) *(f32x4 *)ablk(3, ib1) = a2;
             *(f32x4 *)(sX + (d0 + ln) * L::LDX + 4 * lg) = xT;
+            // the tile still holds the T' the column waves read in this step until every one of
+            // them has loaded it (chunk j's is written during step j - 1)
+            lds_wait(kMiscCntT, kWideCol * j);
+            // the blocks above the diagonal that the column waves read, (0, 1) and (2, 3), are zero
+            if (pw == 0 || pw == 2)
+                M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), d0 + 16 + 4 * lg)),
+                        f32x4{0.f, 0.f, 0.f, 0.f});
             {
                 const f32x4 bcol = *(const f32x4 *)(sBeta + d0 + 4 * lg);
                 M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), d0 + 4 * lg)), xT * bcol);
             }
             prep_barrier();
-            // off-diagonal blocks of X down block column pw:
-            // X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj, stored as T'_ij = X_ij diag(beta_j)
+            // The tile holds T' within each 32-token half, T'_AA = X_A diag(beta_A) and
+            // T'_BB = X_B diag(beta_B), and -W with W = X_B A_BA in place of T'_BA (the column
+            // waves form U_B = T'_BB R_B - W U_A).  Blocks of 16: X_10 = -X_11 A_10 X_00 and
+            // X_32 = -X_33 A_32 X_22 (waves 0 and 2), and W_2m = X_22 A_2m,
+            // W_3m = X_33 (A_3m - A_32 W_2m) for m = 0 (wave 1) and m = 1 (wave 3), right to
+            // left so that every product is in the accumulator layout.
             {
-                const int jc = pw;
-                const float bcol = sBeta[16 * jc + ln];
                 auto arow = [&](int i, int m) { return split4(*(const f32x4 *)ablk(i, m)); };
+                // block (i, m) of A in the accumulator layout (lane holds A_im[4 lg + r][ln])
+                auto acol = [&](int i, int m) {
+                    const float *b = sA + (i * (i - 1) / 2 + m) * 16 * L::LDB;
+                    f32x4 v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = b[(4 * lg + r) * L::LDB + ln];
+                    return v;
+                };
                 auto xrow = [&](int i) {
                     return split4(*(const f32x4 *)(sX + (16 * i + ln) * L::LDX + 4 * lg));
                 };
-                auto put_t = [&](int i, f32x4 z) {
+                // store a block given in the accumulator layout at block (i, jc) of the tile
+                auto put_blk = [&](int i, int jc, f32x4 z, float scale) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         Elem<OP>::store((OP *)(bT + swz<OP, kChunk>(split_pos(16 * i + 4 * lg + r), 16 * jc + ln)),
-                                        z[r] * bcol);
+                                        z[r] * scale);
                 };
-                if (jc <= 2) {
-                    const Sp xjj = split4(xC);
-                    f32x4 acc1 = mm3r(arow(jc + 1, jc), xjj);
-                    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
-                    if (jc + 2 <= 3) acc2 = mm3r(arow(jc + 2, jc), xjj);
-                    if (jc + 3 <= 3) acc3 = mm3r(arow(jc + 3, jc), xjj);
-                    const f32x4 x1 = -mm3r(xrow(jc + 1), split4(acc1));
-                    put_t(jc + 1, x1);
-                    if (jc + 2 <= 3) {
-                        const Sp sx1 = split4(x1);
-                        mm3(acc2, arow(jc + 2, jc + 1), sx1);
-                        if (jc + 3 <= 3) mm3(acc3, arow(jc + 3, jc + 1), sx1);
-                        const f32x4 x2 = -mm3r(xrow(jc + 2), split4(acc2));
-                        put_t(jc + 2, x2);
-                        if (jc + 3 <= 3) {
-                            mm3(acc3, arow(jc + 3, jc + 2), split4(x2));
-                            const f32x4 x3 = -mm3r(xrow(jc + 3), split4(acc3));
-                            put_t(jc + 3, x3);
-                        }
-                    }
+                if (pw == 0 || pw == 2) {
+                    // X_{pw+1, pw} = -X_{pw+1, pw+1} A_{pw+1, pw} X_{pw, pw}, times diag(beta_pw)
+                    const f32x4 acc = mm3r(arow(pw + 1, pw), split4(xC));
+                    const f32x4 x1 = -mm3r(xrow(pw + 1), split4(acc));
+                    put_blk(pw + 1, pw, x1, sBeta[16 * pw + ln]);
+                } else {
+                    const int m = pw == 1 ? 0 : 1;
+                    const f32x4 w2 = mm3r(xrow(2), split4(acol(2, m)));
+                    const f32x4 u = acol(3, m) - mm3r(arow(3, 2), split4(w2));
+                    const f32x4 w3 = mm3r(xrow(3), split4(u));
+                    put_blk(2, m, -w2, 1.f);
+                    put_blk(3, m, -w3, 1.f);
                 }
             }
             // the bound of a warm-up chunk joins the window's sum (fixed order of terms)
@@ -457,65 +501,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 miscf[kMiscLamWin] += lam;
             }
         };
-        // P = lower_incl(Q K^T (.) Gamma) of chunk j as the six operand fragments the column
-        // waves read (fragment f < 4: rows 16 f .. 16 f + 15, columns 0 .. 31; fragments 4, 5:
-        // rows 32 .. 47 and 48 .. 63, columns 32 .. 63).  The K operand takes the tile's rows as
-        // they lie (internal token order), so the two accumulator blocks of a 32-column half
-        // pack into a fragment directly: accumulator [r] of block (tb, ib) = k_i . q_t,
-        // t = 16 tb + ln, i = 32 (ib / 2) + 8 lg + 4 (ib % 2) + r.
-        auto make_p = [&](int j) {
-            const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
-            const unsigned char *bQ = smem + L::sQ + (j & 1) * L::szK;
-            const float *gc = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
-            unsigned char *bP = smem + L::sP + (j & 1) * L::szP;
-            constexpr int kTb[12] = {0, 0, 1, 1, 2, 2, 3, 3, 2, 2, 3, 3};
-            constexpr int kIb[12] = {0, 1, 0, 1, 0, 1, 0, 1, 2, 3, 2, 3};
-            // g is non-increasing inside a chunk: while the chunk's total decay stays above
-            // -60, 2^g_t and 2^-g_i are both normal and Gamma_ti is their product; below,
-            // every element takes its own 2^(g_t - g_i) (0 * inf otherwise)
-            const float gC = gc[kChunk - 1];
-            const bool factored = gC >= -60.f;
-            // fragments of this wave: 0 and 1 for waves 0 and 1, {2, 4} and {3, 5} for 2, 3
-            const int nf = pw < 2 ? 1 : 2;
-#pragma unroll
-            for (int fi = 0; fi < 2; ++fi) {
-                if (fi >= nf) break;
-                const int f = fi == 0 ? pw : pw + 2;
-                const int p0 = 2 * f;
-                const int tb = kTb[p0];
-                f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) {
-                    const bf16x8 fq = ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg);
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int ib = kIb[p0 + u];
-                        M::mma(acc[u], ldfrag_kq<DK>(bK, ib * 16 + ln, kb * 32 + 8 * lg), fq);
-                    }
-                }
-                const int t = tb * 16 + ln;
-                const float gt = gc[t];
-                const float et = __builtin_amdgcn_exp2f(gt);
-                f32x4 pv[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int ib = kIb[p0 + u];
-                    const f32x4 gi = *(const f32x4 *)(gc + 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
-                        const float dec = factored ? et * __builtin_amdgcn_exp2f(-gi[r])
-                                                   : __builtin_amdgcn_exp2f(gt - gi[r]);
-                        pv[u][r] = (i <= t) ? acc[u][r] * dec : 0.f;
-                    }
-                }
-                *(bf16x8 *)(bP + (f * 64 + lane) * 16) = pack8s(pv[0], pv[1]);
-            }
-        };
         // Decay factors of chunk j (wave 3): the scan holds S = 2^ls Shat; ls starts at 0 and
         // after each chunk becomes ls + g_C, or 0 when that would fall below -32 (the column
         // waves then rescale Shat by the same rule on the same g_C).
-        //   F[t] = gamma_t 2^ls,  F[64 + t] = (gamma_C / gamma_t) / 2^ls',  F[128] = g_C
+        //   F[t] = gamma_t 2^ls,  F[64 + t] = (gamma_C / gamma_t) / 2^ls',  F[128] = g_C,
+        //   F[132 + t] = g_t
         float lsl = 0.f;
         auto factors = [&](int j) {
             const float *gc = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
@@ -527,6 +517,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             F[lane] = __builtin_amdgcn_exp2f(gt + lsc);
             F[64 + lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
             if (lane == 0) F[128] = gC;
+            F[132 + lane] = gt;
             lsl = lsn;
         };
 
@@ -547,6 +538,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             if (pw == 3) factors(0);
         }
         lds_barrier();                                  // #1: T'(0), factors(0)
+        // the prep waves' work is one long dependent chain per step that every step waits for:
+        // the SIMDs issue their instructions first
+        __builtin_amdgcn_s_setprio(3);
         for (int j = 0; j < nch; ++j) {
             refresh_lane();
             if (j + 2 < nch) {
@@ -562,7 +556,6 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 make_t(j + 1);
                 if (pw == 3) factors(j + 1);
             }
-            if (j >= nwarm) make_p(j);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
@@ -622,20 +615,101 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     for (int tb = 0; tb < 4; ++tb) yq[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Y of chunk jp = carried gamma 2^ls (Shat^T Q^T) + U^T P^T, P from buffer jp % 2
+    // Y of chunk jp = carried gamma 2^ls (Shat^T Q^T) + U^T P^T.  Each wave holds 4 columns of
+    // each of 64 tokens; the pieces meet in LDS (16-byte granules of a row XOR-swizzled by the
+    // row) and leave as whole rows, wave w storing rows 8 w .. 8 w + 7 in two 1 KiB pieces.
+    int ytarget = 0;
     auto finish = [&](int jp) {
-        const unsigned char *bP = smem + L::sP + (jp & 1) * L::szP;
+        const unsigned char *bP = smem + L::sP;
+        unsigned char *bY = smem + L::sY;
         const long long t0 = row0_of(jp);
         const int nv = nvalid(jp);
+        bf16x8 fp[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) fp[f] = *(const bf16x8 *)(bP + (f * 64 + lane) * 16);
+        f32x4 pu[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            f32x4 pu = {0.f, 0.f, 0.f, 0.f};
-            M::mma(pu, Uu0, *(const bf16x8 *)(bP + (tb * 64 + lane) * 16));
-            if (tb >= 2) M::mma(pu, Uu1, *(const bf16x8 *)(bP + ((tb + 2) * 64 + lane) * 16));
-            const f32x4 yv = yq[tb] + pu;
+            pu[tb] = yq[tb];
+            M::mma(pu[tb], Uu0, fp[tb]);
+        }
+        M::mma(pu[2], Uu1, fp[4]);
+        M::mma(pu[3], Uu1, fp[5]);
+        lds_count(kMiscCntP);              // P may now be overwritten by this step's
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
             const int t = tb * 16 + ln;
+            const int b = 2 * (32 * tile + 8 * lg + 4 * sw);
+            *(bf16x4 *)(bY + t * (DV * 2) + ((((b >> 4) ^ (t & 15))) << 4) + (b & 15)) =
+                __builtin_convertvector(pu[tb], bf16x4);
+        }
+        lds_count(kMiscCntY);
+        ytarget += kWideCol;
+        lds_wait(kMiscCntY, ytarget);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = 8 * cw + 4 * i + (lane >> 4);
+            const int g = lane & 15;
+            const u32x4 v = *(const u32x4 *)(bY + t * (DV * 2) + ((g ^ (t & 15)) << 4));
             if (t < nv)
-                store4((OP *)a.y + ((t0 + t) * H + h) * (long long)DV + 32 * tile + 8 * lg + 4 * sw,
-                       yv);
+                *(u32x4 *)((OP *)a.y + ((t0 + t) * H + h) * (long long)DV + 8 * g) = v;
+        }
+    };
+
+    // P = lower_incl(Q K^T (.) Gamma) of chunk j as the six operand fragments read a step
+    // later (fragment f < 4: rows 16 f .. 16 f + 15, columns 0 .. 31; fragments 4, 5: rows
+    // 32 .. 47 and 48 .. 63, columns 32 .. 63), one 16 x 16 block in each 8-byte half of a
+    // lane's 16 bytes.  Column waves 0-3 form fragment cw, waves 4-7 one block of fragments 4
+    // and 5.  The K operand takes the tile's rows as they lie (internal token order):
+    // accumulator [r] of block (tb, ib) = k_i . q_t, t = 16 tb + ln,
+    // i = 32 (ib / 2) + 8 lg + 4 (ib % 2) + r.
+    auto make_p = [&](int j, const unsigned char *bK, const unsigned char *bQ, const float *F) {
+        const float *gc = F + 132;
+        unsigned char *bP = smem + L::sP;
+        constexpr int kTb[12] = {0, 0, 1, 1, 2, 2, 3, 3, 2, 2, 3, 3};
+        constexpr int kIb[12] = {0, 1, 0, 1, 0, 1, 0, 1, 2, 3, 2, 3};
+        // g is non-increasing inside a chunk: while the chunk's total decay stays above -60,
+        // 2^g_t and 2^-g_i are both normal and Gamma_ti is their product; below, every element
+        // takes its own 2^(g_t - g_i) (0 * inf otherwise)
+        const float gC = F[128];
+        const bool factored = gC >= -60.f;
+        const int nb = cw < 4 ? 2 : 1;               // blocks of this wave
+        const int p0 = cw < 4 ? 2 * cw : 8 + (cw - 4);
+        const int tb = kTb[p0];
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            const bf16x8 fq = ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (u < nb)
+                    M::mma(acc[u], ldfrag_kq<DK>(bK, kIb[p0 + u] * 16 + ln, kb * 32 + 8 * lg), fq);
+            }
+        }
+        const int t = tb * 16 + ln;
+        const float gt = gc[t];
+        const float et = __builtin_amdgcn_exp2f(gt);
+        f32x4 pv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ib = kIb[p0 + u];
+            const f32x4 gi = *(const f32x4 *)(gc + 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
+                const float dec = factored ? et * __builtin_amdgcn_exp2f(-gi[r])
+                                           : __builtin_amdgcn_exp2f(gt - gi[r]);
+                pv[u][r] = (i <= t) ? acc[u][r] * dec : 0.f;
+            }
+        }
+        // every column wave has read the previous chunk's P (one count per step)
+        lds_wait(kMiscCntP, kWideCol * (j + 1));
+        if (cw < 4) {
+            *(bf16x8 *)(bP + (cw * 64 + lane) * 16) = pack8s(pv[0], pv[1]);
+        } else {
+            const int f = 4 + ((cw - 4) >> 1), half = (cw - 4) & 1;
+            *(bf16x4 *)(bP + (f * 64 + lane) * 16 + 8 * half) =
+                __builtin_convertvector(pv[0], bf16x4);
         }
     };
 
@@ -656,29 +730,56 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
         const unsigned char *bQ = smem + L::sQ + (j & 1) * L::szK;
         const unsigned char *bV = smem + L::sV + (j & 1) * L::szV;
-        const unsigned char *bT = smem + L::sT + (j & 1) * L::szT;
+        const unsigned char *bT = smem + L::sT;
         const float *F = (const float *)(smem + L::sF + (j & 1) * L::szF);
         const bool normal = j >= nwarm;
 
-        // ---- K Shat (the head of the state chain) ----
-        f32x4 acc_ks[4];
+        // ---- Y of chunk j - 1 first (its P arrived with this step): the carries die early ----
+        if (j >= 1 && j - 1 >= nwarm) finish(j - 1);
+        else lds_count(kMiscCntP);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- K Shat (the head of the state chain) and, beside it, Shat^T Q^T: both read the
+        // chunk-start state's operands ----
+        f32x4 acc_ks[4], accQ[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc_ks[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < 4; ++tb) {
+            acc_ks[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
-            bf16x8 fk[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) fk[tb] = ldfrag_kq<DK>(bK, tb * 16 + ln, kb * 32 + 8 * lg);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int h2 = 0; h2 < 2; ++h2) {          // two token blocks at a time
+                bf16x8 fk[2], fq[2];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) M::mma(acc_ks[tb], fk[tb], Sb[kb]);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < 2; ++u)
+                    fk[u] = ldfrag_kq<DK>(bK, (2 * h2 + u) * 16 + ln, kb * 32 + 8 * lg);
+                if (normal) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        fq[u] = ldfrag_kq<DK>(bQ, (2 * h2 + u) * 16 + ln, kb * 32 + 8 * lg);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) M::mma(acc_ks[2 * h2 + u], fk[u], Sb[kb]);
+                if (normal) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) M::mma(accQ[2 * h2 + u], Sb[kb], fq[u]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (normal) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) yq[tb] = accQ[tb] * F[tb * 16 + ln];
         }
         bf16x8 ft[6];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) ft[mb] = ldfrag<OP, kChunk>(bT, mb * 16 + ln, 8 * lg);
         ft[4] = ldfrag<OP, kChunk>(bT, 32 + ln, 32 + 8 * lg);
         ft[5] = ldfrag<OP, kChunk>(bT, 48 + ln, 32 + 8 * lg);
+        lds_count(kMiscCntT);              // the prep waves may now write the next chunk's T'
 
         // ---- R = V - diag(gamma 2^ls) K Shat;  U = T' R ----
         f32x4 U[4];
@@ -695,34 +796,26 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             }
             const bf16x8 Rb0 = pack8s(R[0], R[1]);
             const bf16x8 Rb1 = pack8s(R[2], R[3]);
+            // U_A = T'_AA R_A;  U_B = T'_BB R_B - W U_A (the tile holds -W in T'_BA's place)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                M::mma(U[mb], ft[mb], Rb0);
-            }
+            for (int mb = 0; mb < 4; ++mb) U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            M::mma(U[0], ft[0], Rb0);
+            M::mma(U[1], ft[1], Rb0);
             M::mma(U[2], ft[4], Rb1);
             M::mma(U[3], ft[5], Rb1);
+            const bf16x8 Ua = pack8s(U[0], U[1]);
+            M::mma(U[2], ft[2], Ua);
+            M::mma(U[3], ft[3], Ua);
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- Y of chunk j - 1 (its P arrived with this step), then chunk j's carries ----
-        if (j >= 1 && j - 1 >= nwarm) finish(j - 1);
-        __builtin_amdgcn_sched_barrier(0);
+        // ---- chunk j's other carry: bf16 U ----
         if (normal) {
-            // gamma 2^ls (Shat^T Q^T), off the state chain
-            f32x4 accQ[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) accQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KBD; ++kb)
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    M::mma(accQ[tb], Sb[kb], ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg));
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) yq[tb] = accQ[tb] * F[tb * 16 + ln];
             Uu0 = pack8s(U[0], U[1]);
             Uu1 = pack8s(U[2], U[3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (normal) make_p(j, bK, bQ, F);
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U ----

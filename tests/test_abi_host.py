@@ -45,35 +45,26 @@ def test_status_strings_and_version(lib):
 
 
 def test_plans_for_the_workloads(lib):
-    # bf16, d_k = d_v = 128: the one-launch scan with the whole state per workgroup; 64 chains
-    # (B=4, H=16) are split into segments of 16 chunks (256 jobs)
+    # 64 chains (B=4, H=16): split the state columns, never the sequences
     t, s = gdn.gdn_prefill_plan(4, 4 * 4096, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert t == 128 and s == 16
-    # 16 chains of 1M tokens: about 1024 segments
+    assert t in (32, 64) and s == -1
+    # 16 chains of 1M tokens: the one-launch scan with the whole state per workgroup, one
+    # segment of about 1,024 chunks per job (256 jobs)
     t, s = gdn.gdn_prefill_plan(1, 1 << 20, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert t == 128 and 200 <= s <= 300
-    # 512 packed chains: segments of about 60 chunks balance the unequal lengths
-    t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert t == 128 and 32 <= s <= 128
+    assert t == 128 and 1000 <= s <= 1100
     # its workspace: the segment table, a control block, flags and one fp32 end state per
     # (segment, head)
-    entries = 32 + -(-270336 // (s * 64))
-    w = gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1)
+    entries = 1 + -(-(1 << 20) // (s * 64))
+    w = gdn.gdn_prefill_workspace_bytes(1, 1 << 20, 16, 128, 128, 1)
     assert entries * 16 * 128 * 128 * 4 < w < entries * 16 * 128 * 128 * 4 + (64 << 10)
-    # 1024 chains or more: no segments, no workspace
-    t, s = gdn.gdn_prefill_plan(64, 64 * 256, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert t == 128 and s == -1
-    assert gdn.gdn_prefill_workspace_bytes(64, 64 * 256, 16, 128, 128, 1) == 0
-    # equal lengths that fit one segment are not split
-    t, s = gdn.gdn_prefill_plan(2, 2 * 512, 4, 128, 128, gdn.GDN_DTYPE_BF16)
+    # 512 chains: enough work without splitting
+    t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
     assert s == -1
-    # bf16 with 32-column tiles (the two-launch path): one 8448-byte record (T', g) per chunk
-    # slot and head
+    # bf16 column-split plans: one 8448-byte record (T', g) per chunk slot and head
     slots = 270336 // 64 + 32
-    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1, 32, -1) == slots * 16 * 8448
-    # other head sizes keep the column-split plans
-    t, s = gdn.gdn_prefill_plan(4, 4 * 4096, 16, 64, 128, gdn.GDN_DTYPE_BF16)
-    assert t in (16, 32, 64)
+    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == slots * 16 * 8448
+    # the one-launch scan on request: segments of 16 chunks for 64 chains by default
+    assert gdn.gdn_prefill_workspace_bytes(4, 4 * 4096, 16, 128, 128, 1, 128, 0) > 0
     # fp32 without segments needs no workspace
     assert gdn.gdn_prefill_workspace_bytes(1, 256, 2, 64, 64, 0) == 0
     # fp32 tiles stay within the LDS budget
@@ -156,8 +147,9 @@ def test_noalloc_scratch_size(lib):
     (dict(H=0), gdn.GDN_ERR_INVALID_ARGUMENT),
     (dict(dk=96), gdn.GDN_ERR_UNSUPPORTED),
     (dict(dt=5), gdn.GDN_ERR_UNSUPPORTED),
-    # a workspace larger than the fixed array: 2^24 tokens of 16 bf16 heads
-    (dict(n=1, T=1 << 24, H=16), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
+    # a workspace larger than the fixed array: 64 sequences of 65,536 tokens, 16 bf16 heads
+    # (chunk records for 2^22 tokens)
+    (dict(n=64, T=1 << 22, H=16), gdn.GDN_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_prefill_noalloc_rejects(lib, kw, code):
     need = gdn.gdn_prefill_workspace_bytes(kw.get("n", 2), kw.get("T", 256), kw.get("H", 2),
