@@ -62,10 +62,20 @@ __device__ __forceinline__ f32x4 exp2x4(f32x4 x)
 struct Sp {
     bf16x4 hi, lo;
 };
+// Pairs go through one two-lane conversion each, and the rounded high parts come back to
+// fp32 by shifting the bf16 bits into place (exact), so a split takes twelve instructions.
 __device__ __forceinline__ Sp split4(f32x4 x)
 {
-    const bf16x4 h = __builtin_convertvector(x, bf16x4);
-    return Sp{h, __builtin_convertvector(x - __builtin_convertvector(h, f32x4), bf16x4)};
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2));
+    const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2));
+    const f32x4 hf = {__builtin_bit_cast(float, h01 << 16), __builtin_bit_cast(float, h01 & 0xffff0000u),
+                      __builtin_bit_cast(float, h23 << 16), __builtin_bit_cast(float, h23 & 0xffff0000u)};
+    const f32x4 r = x - hf;
+    const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[0], r[1]}, bf16x2));
+    const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[2], r[3]}, bf16x2));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return Sp{__builtin_bit_cast(bf16x4, u32x2{h01, h23}), __builtin_bit_cast(bf16x4, u32x2{l01, l23})};
 }
 __device__ __forceinline__ void mm3(f32x4 &c, const Sp &a, const Sp &b)
 {

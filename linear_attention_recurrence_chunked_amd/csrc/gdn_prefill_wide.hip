@@ -46,8 +46,8 @@ struct LdsWide {
     static constexpr int szV = kChunk * DV * 2;        // [64][DV] bf16
     static constexpr int szT = kChunk * kChunk * 2;    // T' as a 64-wide swizzled tile
     static constexpr int szP = 6 * 1024;               // P as six operand fragments
-    static constexpr int szF = 3 * kChunk * 4 + 16;    // gamma 2^ls, rho, g_C, g
-    static constexpr int szPG = 2 * kChunk * 4;        // a prep wave's g and beta of a chunk
+    static constexpr int szF = 5 * kChunk * 4 + 16;    // gamma 2^ls, rho, g_C, g, 2^g, 2^-g
+    static constexpr int szPG = 4 * kChunk * 4;        // a prep wave's g, beta, 2^g, 2^-g
     static constexpr int szY = kChunk * DV * 2;        // y of a chunk, bf16 rows (staging)
     static constexpr int LDB = 16;                     // fp32 rows of an A block
     static constexpr int LDX = 16;                     // rows of a diagonal X block
@@ -59,8 +59,8 @@ struct LdsWide {
     static constexpr int sY = sP + szP;                // y rows on their way to memory
     static constexpr int sAB = sY + szY;               // raw gates [alpha 64][beta 64], j % 2
     static constexpr int sF = sAB + 2 * 512;           // factors of chunk j in buffer j % 2
-    static constexpr int sPG = sF + 2 * szF;           // [prep wave][j % 2] g, beta
-    static constexpr int sA = sPG + kWidePrep * 2 * szPG;   // six strictly lower A blocks
+    static constexpr int sPG = sF + 2 * szF;           // [prep wave] g, beta, 2^g, 2^-g
+    static constexpr int sA = sPG + kWidePrep * szPG;  // six strictly lower A blocks
     static constexpr int sX = sA + 6 * 16 * LDB * 4;        // four diagonal X blocks
     static constexpr int sMisc = sX + 4 * 16 * LDX * 4;
     static constexpr int total = sMisc + 256;
@@ -114,25 +114,45 @@ __device__ __forceinline__ int vswz(int row, int col)
     return row * (DV * 2) + ((((b >> 4) ^ ((row & 3) << 2))) << 4) + (b & 15);
 }
 
-// Direct-to-LDS copies (lane l's 16 or 4 bytes land at lds + 16 l or lds + 4 l), written in
-// inline asm so that the compiler does not treat the wave's later LDS reads as waiting on
-// them: the prep waves read other stages while these copies fly, and wait for them
-// (s_waitcnt vmcnt(0)) only before the step barrier that hands them to their readers.  The
-// instruction has no register output; M0 carries the LDS address.
+// Direct-to-LDS copies (lane l's 16 or 4 bytes land at lds + 16 l or lds + 4 l) from a
+// wave-uniform base address plus a 32-bit per-lane byte offset, written in inline asm so
+// that the compiler does not treat the wave's later LDS reads as waiting on them: the prep
+// waves read other stages while these copies fly, and wait for them (s_waitcnt vmcnt(0))
+// only before the step barrier that hands them to their readers.  The instruction has no
+// register output; M0 carries the LDS address.
 __device__ __forceinline__ unsigned lds_addr(const void *p)
 {
     return (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p;
 }
-__device__ __forceinline__ void copy16_async(const void *g, unsigned lds)
+__device__ __forceinline__ void copy16_async(const void *base, unsigned off, unsigned lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                 "s"(lds)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void copy4_async(const void *g, unsigned lds)
+__device__ __forceinline__ void copy4_async(const void *base, unsigned off, unsigned lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+                 "s"(lds)
                  : "memory", "m0");
 }
+// A wave-uniform value as such (its lanes are known to agree).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long long uni64(long long x)
+{
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)x);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ T *uptr(T *p)
+{
+    return (T *)uni64((long long)(size_t)p);
+}
+// Keeps a register value opaque to the optimizer from this point (no code).
+__device__ __forceinline__ void opaque(unsigned &x) { asm volatile("" : "+v"(x)); }
+// Granule permutation of the 256-byte K and Q rows (the slot before the row's XOR key).
+__device__ __forceinline__ int kq_pi(int g) { return ((g & 1) << 3) | ((g >> 1) & 7); }
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
@@ -177,7 +197,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     if (tid == 2) miscf[kMiscLamWin] = 0.f;
     if (tid >= 3 && tid < 6) misc[kMiscCntT + tid - 3] = 0;
     __syncthreads();
-    const int job = misc[kMiscJob];
+    const int job = uni(misc[kMiscJob]);
     const int H = a.H;
     const long long njobs = (long long)(a.table ? *a.n_entries : a.num_seqs) * H;
     if (job >= njobs) return;
@@ -186,11 +206,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     long long tok0;
     if (a.table) {
         const SegEntry en = a.table[e];
-        n = en.n;
-        tok0 = en.tok0;
-        len = en.len;
-        seg = en.seg;
-        nseg = en.nseg;
+        n = uni(en.n);
+        tok0 = uni64(en.tok0);
+        len = uni(en.len);
+        seg = uni(en.seg);
+        nseg = uni(en.nseg);
     } else {
         n = e;
         seq_bounds(a, n, tok0, len);
@@ -200,6 +220,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     long long srow0;
     int slen;
     seq_bounds(a, n, srow0, slen);
+    srow0 = uni64(srow0);
+    slen = uni(slen);
     GateHead gh;
     gh.pre = a.gate_A != nullptr;
     gh.scale = gh.pre ? -__expf(a.gate_A[h]) * 1.44269504088896341f : 0.f;
@@ -244,6 +266,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             mode = 3;
         }
     }
+    b = uni(b);
+    mode = uni(mode);
     const int nwarm = c0 - b;
     const int nch = nwarm + nown;
     auto nvalid = [&](int j) {          // valid tokens of processed chunk j
@@ -257,8 +281,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     // never arrives ends the wait, so no logic error can hang the device)
     auto lds_count = [&](int which) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (lane == 0)
-            __hip_atomic_fetch_add(misc_l + which, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0)      // one lane's LDS add (written out: no cross-lane bookkeeping needed)
+            asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(misc + which)), "v"(1) : "memory");
     };
     auto lds_wait = [&](int which, int target) {
         for (int spin = 0; spin < (1 << 22); ++spin) {
@@ -274,6 +298,28 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     if (wave >= kWideCol) {
         const int pw = wave - kWideCol;
         const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
+        static_assert(CK / kWidePrep == 4 && CV / kWidePrep == 4 && KG == 16, "copy layout");
+        // Gram fragment rows: see make_t
+        unsigned o_g;
+        {
+            const int ln0 = lane & 15, lg0 = lane >> 4;
+            const int rr = 16 * ((ln0 >> 2) & 1) + 4 * (ln0 >> 3) + (ln0 & 3);
+            o_g = rr * 256 + ((kq_pi(lg0) ^ (rr & 7)) << 4);
+        }
+        // Copy q of this wave fills 1 KiB piece jj = 4 pw + q of a tile: lane (ln, lg) writes
+        // slot ln of tile row r = 16 pw + 4 q + lg.  In a K or Q tile that slot holds logical
+        // granule kq_logical(r, ln), which depends on r only through r % 8 = 4 (q % 2) + lg;
+        // the K tile's row r holds token split_orig(r) = 32 (pw / 2) + 4 (pw % 2) + 8 q + lg,
+        // the Q tile's token r.  In a V tile the slot holds granule ln ^ 4 lg.  So a full
+        // chunk's copies take one of three per-lane byte offsets plus a uniform row offset.
+        unsigned okq0, okq1, ovv, oab;
+        {
+            const int ln0 = lane & 15, lg0 = lane >> 4;
+            okq0 = lg0 * rsK + 16 * kq_logical<DK>(lg0, ln0);
+            okq1 = lg0 * rsK + 16 * kq_logical<DK>(4 + lg0, ln0);
+            ovv = lg0 * rsV + 16 * (ln0 ^ (lg0 << 2));
+            oab = (unsigned)lane * (unsigned)H * 4u;
+        }
         auto copy_chunk_kq = [&](int j, bool with_k, bool with_q) {
             const long long t0 = row0_of(j);
             const int last = nvalid(j) - 1;
@@ -281,19 +327,31 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + h) * (long long)DK * 2;
             unsigned char *dk = smem + L::sK + (j % 3) * L::szK;
             unsigned char *dq = smem + L::sQ + (j & 1) * L::szK;
+            if (last == kChunk - 1) {
 #pragma unroll
-            for (int q = 0; q < CK / kWidePrep; ++q) {
-                const int jj = pw * (CK / kWidePrep) + q;
-                const int P = 64 * jj + lane;
-                const int r = P / KG, pg = P % KG;
-                const int lgq = kq_logical<DK>(r, pg);
-                if (with_k) {
-                    const int rk = split_orig(r) < last ? split_orig(r) : last;
-                    copy16_async(ck + (unsigned)rk * rsK + 16 * lgq, lds_addr(dk + 1024 * jj));
+                for (int q = 0; q < 4; ++q) {
+                    const int jj = pw * 4 + q;
+                    const unsigned o = (q & 1) ? okq1 : okq0;
+                    if (with_k)
+                        copy16_async(ck + (32 * (pw >> 1) + 4 * (pw & 1) + 8 * q) * rsK, o,
+                                     lds_addr(dk + 1024 * jj));
+                    if (with_q)
+                        copy16_async(cq + (16 * pw + 4 * q) * rsK, o, lds_addr(dq + 1024 * jj));
                 }
-                if (with_q) {
-                    const int rq = r < last ? r : last;
-                    copy16_async(cq + (unsigned)rq * rsK + 16 * lgq, lds_addr(dq + 1024 * jj));
+            } else {            // a sequence's last, partial chunk: rows past its end repeat the last
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int jj = pw * 4 + q;
+                    const int r = 16 * pw + 4 * q + (lane >> 4);
+                    const unsigned o = 16 * kq_logical<DK>(r, lane & 15);
+                    if (with_k) {
+                        const int rk = split_orig(r) < last ? split_orig(r) : last;
+                        copy16_async(ck, (unsigned)rk * rsK + o, lds_addr(dk + 1024 * jj));
+                    }
+                    if (with_q) {
+                        const int rq = r < last ? r : last;
+                        copy16_async(cq, (unsigned)rq * rsK + o, lds_addr(dq + 1024 * jj));
+                    }
                 }
             }
         };
@@ -302,29 +360,38 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             const int last = nvalid(j) - 1;
             const unsigned char *cv = (const unsigned char *)a.v + (t0 * H + h) * (long long)DV * 2;
             unsigned char *dv = smem + L::sV + (j & 1) * L::szV;
+            if (last == kChunk - 1) {
 #pragma unroll
-            for (int q = 0; q < CV / kWidePrep; ++q) {
-                const int jj = pw * (CV / kWidePrep) + q;
-                const int byte = 1024 * jj + 16 * lane;
-                const int r = byte / (DV * 2), p = (byte % (DV * 2)) >> 4;
-                const int g = p ^ ((r & 3) << 2);
-                const int rv = r < last ? r : last;
-                copy16_async(cv + (unsigned)rv * rsV + 16 * g, lds_addr(dv + 1024 * jj));
+                for (int q = 0; q < 4; ++q) {
+                    const int jj = pw * 4 + q;
+                    copy16_async(cv + 4 * jj * rsV, ovv, lds_addr(dv + 1024 * jj));
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int jj = pw * 4 + q;
+                    const int r = 4 * jj + (lane >> 4);
+                    const int rv = r < last ? r : last;
+                    copy16_async(cv, (unsigned)rv * rsV + (ovv - (lane >> 4) * rsV),
+                                 lds_addr(dv + 1024 * jj));
+                }
             }
         };
         auto copy_chunk_gates = [&](int j) {
             if (pw < 2) {
                 const long long t0 = row0_of(j);
                 const int last = nvalid(j) - 1;
-                const int tc = lane < last ? lane : last;
-                const float *src = (pw == 0 ? a.alpha : a.beta) + (t0 + tc) * H + h;
-                copy4_async(src, lds_addr(smem + L::sAB + (j & 1) * 512 + pw * 256));
+                const float *src = (pw == 0 ? a.alpha : a.beta) + t0 * H + h;
+                const unsigned o = last == kChunk - 1 ? oab
+                                                      : (unsigned)(lane < last ? lane : last) * (unsigned)H * 4u;
+                copy4_async(src, o, lds_addr(smem + L::sAB + (j & 1) * 512 + pw * 256));
             }
         };
-        // g and beta of chunk j in this wave's own slot (no other wave reads it)
+        // g, beta, 2^g and 2^-g of chunk j in this wave's own slot (no other wave reads it;
+        // it is written and read within one step)
         auto gates = [&](int j) {
             const float *ab = (const float *)(smem + L::sAB + (j & 1) * 512);
-            float *pg = (float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            float *pg = (float *)(smem + L::sPG + pw * L::szPG);
             const int nv = nvalid(j);
             float x = 0.f, bt = 0.f;
             if (lane < nv) {
@@ -340,6 +407,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             x += dpp_f32<0x143, 0xc>(x);
             pg[lane] = x;
             pg[64 + lane] = bt;
+            pg[128 + lane] = __builtin_amdgcn_exp2f(x);
+            pg[192 + lane] = __builtin_amdgcn_exp2f(-x);
         };
         int pbar_target = 0;
         auto prep_barrier = [&]() {
@@ -352,8 +421,14 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         auto make_t = [&](int j) {
             const unsigned char *bK = smem + L::sK + (j % 3) * L::szK;
             unsigned char *bT = smem + L::sT;
-            const float *sG = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            const float *sG = (const float *)(smem + L::sPG + pw * L::szPG);
             const float *sBeta = sG + 64;
+            const float *sE = sG + 128;        // 2^g
+            const float *sIE = sG + 192;       // 2^-g
+            // g is non-increasing inside a chunk: while the chunk's total decay stays above -60,
+            // 2^g_t and 2^-g_i are both normal and Gamma_ti is their product; below, every
+            // element takes its own 2^(g_t - g_i)
+            const bool factored = __builtin_amdgcn_readfirstlane((int)(sG[kChunk - 1] >= -60.f));
             float *sA = (float *)(smem + L::sA);
             float *sX = (float *)(smem + L::sX);
             const int d0 = pw * 16;
@@ -366,13 +441,17 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             f32x4 accG[3];
 #pragma unroll
             for (int p = 0; p < 3; ++p) accG[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // fragment of tokens 16 ib + ln (tile rows split_pos(16 ib + ln) =
+            // 32 (ib / 2) + 8 (ib % 2) + [16 (ln / 4 % 2) + 4 (ln / 8) + ln % 4]), granule 4 kb + lg
+            auto rowoff = [](int ib) { return (32 * (ib >> 1) + 8 * (ib & 1)) * 256; };
 #pragma unroll
             for (int kb = 0; kb < KBD; ++kb) {
+                const unsigned o = o_g ^ (32 * kb);
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
                     if (p < np) {
-                        const auto ai = ldfrag_kq<DK>(bK, split_pos(ibs[p] * 16 + ln), kb * 32 + 8 * lg);
-                        const auto bt = ldfrag_kq<DK>(bK, split_pos(tbs[p] * 16 + ln), kb * 32 + 8 * lg);
+                        const auto ai = *(const bf16x8 *)(bK + rowoff(ibs[p]) + o);
+                        const auto bt = *(const bf16x8 *)(bK + rowoff(tbs[p]) + o);
                         M::mma(accG[p], ai, bt);
                     }
                 }
@@ -392,13 +471,23 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             }
             auto masked = [&](int tb, int ib, f32x4 g_, f32x4 &av) {
                 const int t = tb * 16 + ln;
-                const float gt = sG[t];
                 const float bt_ = sBeta[t];
-                const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+                if (factored) {
+                    const float c = bt_ * sE[t];
+                    const f32x4 ie = *(const f32x4 *)(sIE + ib * 16 + 4 * lg);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ib * 16 + 4 * lg + r;
-                    av[r] = (i < t) ? bt_ * g_[r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = ib * 16 + 4 * lg + r;
+                        av[r] = (i < t) ? (c * ie[r]) * g_[r] : 0.f;
+                    }
+                } else {
+                    const float gt = sG[t];
+                    const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = ib * 16 + 4 * lg + r;
+                        av[r] = (i < t) ? bt_ * g_[r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+                    }
                 }
             };
             f32x4 nT, a1, a2;
@@ -408,13 +497,23 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             f32x4 nC;
             {
                 const int t = d0 + ln;
-                const float gt = sG[t];
-                const f32x4 gi = *(const f32x4 *)(sG + d0 + 4 * lg);
                 const f32x4 bi = *(const f32x4 *)(sBeta + d0 + 4 * lg);
+                if (factored) {
+                    const float iet = sIE[t];
+                    const f32x4 ei = *(const f32x4 *)(sE + d0 + 4 * lg);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = d0 + 4 * lg + r;
-                    nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = d0 + 4 * lg + r;
+                        nC[r] = (t < i) ? (bi[r] * (ei[r] * iet)) * accG[0][r] : 0.f;
+                    }
+                } else {
+                    const float gt = sG[t];
+                    const f32x4 gi = *(const f32x4 *)(sG + d0 + 4 * lg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = d0 + 4 * lg + r;
+                        nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
+                    }
                 }
             }
             // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since N^16 = 0
@@ -505,10 +604,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         // after each chunk becomes ls + g_C, or 0 when that would fall below -32 (the column
         // waves then rescale Shat by the same rule on the same g_C).
         //   F[t] = gamma_t 2^ls,  F[64 + t] = (gamma_C / gamma_t) / 2^ls',  F[128] = g_C,
-        //   F[132 + t] = g_t
+        //   F[132 + t] = g_t,  F[196 + t] = 2^g_t,  F[260 + t] = 2^-g_t
         float lsl = 0.f;
         auto factors = [&](int j) {
-            const float *gc = (const float *)(smem + L::sPG + (pw * 2 + (j & 1)) * L::szPG);
+            const float *gc = (const float *)(smem + L::sPG + pw * L::szPG);
             float *F = (float *)(smem + L::sF + (j & 1) * L::szF);
             const float gt = gc[lane], gC = gc[kChunk - 1];
             const float lsc = lsl;
@@ -518,6 +617,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             F[64 + lane] = __builtin_amdgcn_exp2f((gC - gt) - lsn);
             if (lane == 0) F[128] = gC;
             F[132 + lane] = gt;
+            F[196 + lane] = gc[128 + lane];
+            F[260 + lane] = gc[192 + lane];
             lsl = lsn;
         };
 
@@ -543,6 +644,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         __builtin_amdgcn_s_setprio(3);
         for (int j = 0; j < nch; ++j) {
             refresh_lane();
+            opaque(o_g);
             if (j + 2 < nch) {
                 copy_chunk_kq(j + 2, true, false);
                 copy_chunk_gates(j + 2);
@@ -569,6 +671,27 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     // so a lane of the output layout holds 4 columns that sit next to the other wave's 4
     const int col = 32 * tile + 8 * (ln >> 2) + 4 * sw + (ln & 3);
     const long long stride_s = (long long)DK * DV;
+    // Byte offsets of this lane's per-step LDS and global accesses.  Every access adds to one
+    // of them a uniform stage base and a constant, after at most an XOR with a constant on
+    // bits 5-6 (where the swizzles depend on the contraction block); they are made opaque at
+    // each step so that the optimizer forms these few operations there rather than keeping
+    // every combination live across the loop.
+    //   o_kq: K or Q fragment (row 16 tb + ln, granule 4 kb + lg): + 4096 tb, ^ 32 kb
+    //   o_kt: transposing K^T read (rows 32 kt + 4 lg + ln / 4 (+ 16), granule
+    //         4 (m / 2) + ln % 4, byte 8 (m % 2)): + 8192 kt + 4096 hi + 8 (m % 2), ^ 32 (m / 2)
+    //   o_tt: T' fragment (row 16 mb + ln, granule lg): + 2048 mb, ^ 32 mb
+    //   o_v:  transposing V read (rows 32 (tb / 2) + 8 lg + 4 (tb % 2) + ln / 4, this lane's
+    //         four columns): + 8192 (tb / 2) + 1024 (tb % 2)
+    //   o_ys / o_yr: y staging write (row 16 tb + ln) / row read (row 8 cw + 4 i + lg)
+    //   o_yg: y in memory, token 8 cw + 4 i + lg of the chunk, granule ln
+    unsigned o_kq = ln * 256 + ((kq_pi(lg) ^ (ln & 7)) << 4);
+    unsigned o_kt = (4 * lg + (ln >> 2)) * 256 + ((kq_pi(ln & 3) ^ (4 * (lg & 1) + (ln >> 2))) << 4);
+    unsigned o_tt = ln * 128 + ((lg ^ (ln & 7) ^ (ln >> 3)) << 4);
+    unsigned o_v = (8 * lg + (ln >> 2)) * 256 + (((4 * tile + (ln & 3)) ^ ((ln >> 2) << 2)) << 4) + 8 * sw;
+    unsigned o_ys = ln * 256 + (((4 * tile + lg) ^ ln) << 4) + 8 * sw;
+    unsigned o_yr = (8 * cw + lg) * 256 + ((ln ^ (8 * (cw & 1) + lg)) << 4);
+    unsigned o_yg = (unsigned)lg * (unsigned)(H * DV * 2) + 16 * ln;
+    unsigned o_lane = lane;
     f32x4 S[MBK];
     auto load_state = [&](const float *src, float scale) {
 #pragma unroll
@@ -620,13 +743,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     // row) and leave as whole rows, wave w storing rows 8 w .. 8 w + 7 in two 1 KiB pieces.
     int ytarget = 0;
     auto finish = [&](int jp) {
-        const unsigned char *bP = smem + L::sP;
+        const unsigned char *bP = smem + L::sP + 16 * o_lane;
         unsigned char *bY = smem + L::sY;
         const long long t0 = row0_of(jp);
         const int nv = nvalid(jp);
         bf16x8 fp[6];
 #pragma unroll
-        for (int f = 0; f < 6; ++f) fp[f] = *(const bf16x8 *)(bP + (f * 64 + lane) * 16);
+        for (int f = 0; f < 6; ++f) fp[f] = *(const bf16x8 *)(bP + f * 1024);
         f32x4 pu[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -637,22 +760,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         M::mma(pu[3], Uu1, fp[5]);
         lds_count(kMiscCntP);              // P may now be overwritten by this step's
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int t = tb * 16 + ln;
-            const int b = 2 * (32 * tile + 8 * lg + 4 * sw);
-            *(bf16x4 *)(bY + t * (DV * 2) + ((((b >> 4) ^ (t & 15))) << 4) + (b & 15)) =
-                __builtin_convertvector(pu[tb], bf16x4);
-        }
+        for (int tb = 0; tb < 4; ++tb)
+            *(bf16x4 *)(bY + o_ys + 4096 * tb) = __builtin_convertvector(pu[tb], bf16x4);
         lds_count(kMiscCntY);
         ytarget += kWideCol;
         lds_wait(kMiscCntY, ytarget);
+        unsigned char *const yb = (unsigned char *)a.y + ((t0 + 8 * cw) * H + h) * (long long)(DV * 2);
+        const unsigned lgv = o_lane >> 4;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int t = 8 * cw + 4 * i + (lane >> 4);
-            const int g = lane & 15;
-            const u32x4 v = *(const u32x4 *)(bY + t * (DV * 2) + ((g ^ (t & 15)) << 4));
-            if (t < nv)
-                *(u32x4 *)((OP *)a.y + ((t0 + t) * H + h) * (long long)DV + 8 * g) = v;
+            const u32x4 v = *(const u32x4 *)(bY + ((i ? (o_yr ^ 64) : o_yr) + 1024 * i));
+            if ((int)lgv < nv - 8 * cw - 4 * i)
+                *(u32x4 *)(yb + (unsigned)(4 * i * H * DV * 2) + o_yg) = v;
         }
     };
 
@@ -665,58 +784,75 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     // i = 32 (ib / 2) + 8 lg + 4 (ib % 2) + r.
     auto make_p = [&](int j, const unsigned char *bK, const unsigned char *bQ, const float *F) {
         const float *gc = F + 132;
-        unsigned char *bP = smem + L::sP;
+        unsigned char *bP = smem + L::sP + 16 * o_lane;
         constexpr int kTb[12] = {0, 0, 1, 1, 2, 2, 3, 3, 2, 2, 3, 3};
         constexpr int kIb[12] = {0, 1, 0, 1, 0, 1, 0, 1, 2, 3, 2, 3};
         // g is non-increasing inside a chunk: while the chunk's total decay stays above -60,
         // 2^g_t and 2^-g_i are both normal and Gamma_ti is their product; below, every element
         // takes its own 2^(g_t - g_i) (0 * inf otherwise)
-        const float gC = F[128];
-        const bool factored = gC >= -60.f;
+        const bool factored = __builtin_amdgcn_readfirstlane((int)(F[128] >= -60.f));
         const int nb = cw < 4 ? 2 : 1;               // blocks of this wave
         const int p0 = cw < 4 ? 2 * cw : 8 + (cw - 4);
         const int tb = kTb[p0];
         f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb) {
-            const bf16x8 fq = ldfrag_kq<DK>(bQ, tb * 16 + ln, kb * 32 + 8 * lg);
+            const unsigned o = o_kq ^ (32 * kb);
+            const bf16x8 fq = *(const bf16x8 *)(bQ + 4096 * tb + o);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 if (u < nb)
-                    M::mma(acc[u], ldfrag_kq<DK>(bK, kIb[p0 + u] * 16 + ln, kb * 32 + 8 * lg), fq);
+                    M::mma(acc[u], *(const bf16x8 *)(bK + 4096 * kIb[p0 + u] + o), fq);
             }
         }
         const int t = tb * 16 + ln;
-        const float gt = gc[t];
-        const float et = __builtin_amdgcn_exp2f(gt);
         f32x4 pv[2];
+        if (factored) {
+            const float et = F[196 + t];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ib = kIb[p0 + u];
-            const f32x4 gi = *(const f32x4 *)(gc + 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1));
+            for (int u = 0; u < 2; ++u) {
+                const int ib = kIb[p0 + u];
+                const f32x4 ie = *(const f32x4 *)(F + 260 + 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
-                const float dec = factored ? et * __builtin_amdgcn_exp2f(-gi[r])
-                                           : __builtin_amdgcn_exp2f(gt - gi[r]);
-                pv[u][r] = (i <= t) ? acc[u][r] * dec : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
+                    pv[u][r] = (i <= t) ? acc[u][r] * (et * ie[r]) : 0.f;
+                }
+            }
+        } else {
+            const float gt = gc[t];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int ib = kIb[p0 + u];
+                const f32x4 gi = *(const f32x4 *)(gc + 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 32 * (ib >> 1) + 8 * lg + 4 * (ib & 1) + r;
+                    pv[u][r] = (i <= t) ? acc[u][r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+                }
             }
         }
         // every column wave has read the previous chunk's P (one count per step)
         lds_wait(kMiscCntP, kWideCol * (j + 1));
         if (cw < 4) {
-            *(bf16x8 *)(bP + (cw * 64 + lane) * 16) = pack8s(pv[0], pv[1]);
+            *(bf16x8 *)(bP + cw * 1024) = pack8s(pv[0], pv[1]);
         } else {
             const int f = 4 + ((cw - 4) >> 1), half = (cw - 4) & 1;
-            *(bf16x4 *)(bP + (f * 64 + lane) * 16 + 8 * half) =
-                __builtin_convertvector(pv[0], bf16x4);
+            *(bf16x4 *)(bP + f * 1024 + 8 * half) = __builtin_convertvector(pv[0], bf16x4);
         }
     };
 
     lds_barrier();            // #0
     lds_barrier();            // #1
     for (int j = 0; j < nch; ++j) {
-        refresh_lane();
+        opaque(o_kq);
+        opaque(o_kt);
+        opaque(o_tt);
+        opaque(o_v);
+        opaque(o_ys);
+        opaque(o_yr);
+        opaque(o_yg);
+        opaque(o_lane);
         if (mode == 1 && j == nwarm) {
             // the warm-up reached the bound, or the exact chain takes over
             const float lw = __builtin_bit_cast(
@@ -752,13 +888,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {          // two token blocks at a time
                 bf16x8 fk[2], fq[2];
+                const unsigned o = o_kq ^ (32 * kb);
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    fk[u] = ldfrag_kq<DK>(bK, (2 * h2 + u) * 16 + ln, kb * 32 + 8 * lg);
+                for (int u = 0; u < 2; ++u) fk[u] = *(const bf16x8 *)(bK + 4096 * (2 * h2 + u) + o);
                 if (normal) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        fq[u] = ldfrag_kq<DK>(bQ, (2 * h2 + u) * 16 + ln, kb * 32 + 8 * lg);
+                    for (int u = 0; u < 2; ++u) fq[u] = *(const bf16x8 *)(bQ + 4096 * (2 * h2 + u) + o);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -771,27 +906,32 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             }
         }
         if (normal) {
+            const float *Fl = F + (o_lane & 15);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) yq[tb] = accQ[tb] * F[tb * 16 + ln];
+            for (int tb = 0; tb < 4; ++tb) yq[tb] = accQ[tb] * Fl[tb * 16];
         }
+        // T' fragments: rows 16 mb + ln at granule lg (mb < 4), and rows 32 + ln, 48 + ln at
+        // granule 4 + lg, which take the slots of granule lg in rows ln and 16 + ln
         bf16x8 ft[6];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) ft[mb] = ldfrag<OP, kChunk>(bT, mb * 16 + ln, 8 * lg);
-        ft[4] = ldfrag<OP, kChunk>(bT, 32 + ln, 32 + 8 * lg);
-        ft[5] = ldfrag<OP, kChunk>(bT, 48 + ln, 32 + 8 * lg);
+        for (int mb = 0; mb < 4; ++mb) ft[mb] = *(const bf16x8 *)(bT + 2048 * mb + (o_tt ^ (32 * mb)));
+        ft[4] = *(const bf16x8 *)(bT + 4096 + o_tt);
+        ft[5] = *(const bf16x8 *)(bT + 6144 + (o_tt ^ 32));
         lds_count(kMiscCntT);              // the prep waves may now write the next chunk's T'
 
         // ---- R = V - diag(gamma 2^ls) K Shat;  U = T' R ----
         f32x4 U[4];
         {
             f32x4 R[4];
+            const float *Fq = F + 8 * (o_lane >> 4);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                // V[o0 .. o0 + 3][column] by one transposing read: lane j receives column
+                // V[o0 .. o0 + 3][column], o0 = split_orig(16 tb + 4 lg) = 32 (tb / 2) + 8 lg +
+                // 4 (tb % 2), by one transposing read: lane j receives column
                 // 32 tile + 8 (j / 4) + 4 sw + j % 4 of rows o0 .. o0 + 3
-                const int o0 = split_orig(tb * 16 + 4 * lg);
-                const f32x4 gam = *(const f32x4 *)(F + o0);
-                const bf16x4 v4 = ldtr(bV + vswz<DV>(o0 + (ln >> 2), 32 * tile + 8 * (ln & 3) + 4 * sw));
+                const int c0 = 32 * (tb >> 1) + 4 * (tb & 1);
+                const f32x4 gam = *(const f32x4 *)(Fq + c0);
+                const bf16x4 v4 = ldtr(bV + 256 * c0 + o_v);
                 R[tb] = __builtin_convertvector(v4, f32x4) - gam * acc_ks[tb];
             }
             const bf16x8 Rb0 = pack8s(R[0], R[1]);
@@ -819,11 +959,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U, as Shat += K^T diag(rho) U ----
+        // K^T fragment: columns 32 (m / 2) + 8 (ln % 4) + 4 (m % 2) .. + 3 of the tokens
+        // 32 kt + 8 lg + ln / 4 (+ 4), which sit at tile rows 32 kt + 4 lg + ln / 4 (+ 16)
         auto frag_kt = [&](int m, int kt) {
-            const int c = 32 * (m >> 1) + 8 * (ln & 3) + 4 * (m & 1);
-            const int t = 32 * kt + 8 * lg + (ln >> 2);
-            const bf16x4 lo = ldtr(bK + swz_kq<DK>(split_pos(t), c));
-            const bf16x4 hi = ldtr(bK + swz_kq<DK>(split_pos(t + 4), c));
+            const unsigned char *p = bK + 8192 * kt + 8 * (m & 1) + (o_kt ^ (32 * (m >> 1)));
+            const bf16x4 lo = ldtr(p);
+            const bf16x4 hi = ldtr(p + 4096);
             return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
         {
@@ -841,7 +982,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 f32x4 Us[4];
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
-                    const f32x4 rho = *(const f32x4 *)(F + 64 + split_orig(mb * 16 + 4 * lg));
+                    const f32x4 rho = *(const f32x4 *)(F + 64 + 8 * (o_lane >> 4) + 32 * (mb >> 1) + 4 * (mb & 1));
                     Us[mb] = U[mb] * rho;
                 }
                 Ub[0] = pack8s(Us[0], Us[1]);
