@@ -796,7 +796,12 @@ static bool use_wide_by_default(int num_seqs, long long total_T, int H)
 {
     const long long chains = (long long)num_seqs * H;
     const long long avg_chunks = cdiv(total_T, (long long)num_seqs * kChunk);
-    return chains * 4 < 256 && avg_chunks >= 64;
+    // few long chains: segments of them fill the chip
+    if (chains * 4 < 256 && avg_chunks >= 64) return true;
+    // plenty of work: once every CU has 128 or more chunk steps to run, the one-launch scan
+    // (no chunk records through HBM) beats the two-launch path
+    const long long total_chunks = cdiv(total_T, kChunk) + num_seqs;
+    return total_chunks * H >= 128LL * 256 && avg_chunks >= 32;
 }
 
 static bool make_wide_plan(int num_seqs, long long total_T, int H, int seg_chunks_req,
@@ -808,7 +813,11 @@ static bool make_wide_plan(int num_seqs, long long total_T, int H, int seg_chunk
     if (seg == 0) {
         constexpr long long kJobs = 256;
         if (chains >= kJobs) {
-            seg = -1;
+            // about two jobs per CU, so that unequal lengths even out
+            long long s = cdiv(total_chunks * H, 2 * kJobs);
+            if (s < 64) s = 64;
+            if (s > (1 << 24)) s = 1 << 24;
+            seg = (int)s;
         } else {
             long long s = cdiv(total_chunks * H, kJobs);
             if (s < 16) s = 16;

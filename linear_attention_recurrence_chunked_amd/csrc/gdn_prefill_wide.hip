@@ -883,28 +883,42 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             acc_ks[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
             accQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // eight groups (contraction block kb, token blocks 2 h2 and 2 h2 + 1), software-pipelined:
+        // the fragments of group g + 1 are requested before the products of group g issue
+        auto ks_qs = [&](auto with_q) {
+            constexpr bool WQ = decltype(with_q)::value;
+            auto ld = [&](int g, bf16x8 *fk, bf16x8 *fq) {
+                const unsigned o = o_kq ^ (32 * (g >> 1));
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {          // two token blocks at a time
-                bf16x8 fk[2], fq[2];
-                const unsigned o = o_kq ^ (32 * kb);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) fk[u] = *(const bf16x8 *)(bK + 4096 * (2 * h2 + u) + o);
-                if (normal) {
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) fq[u] = *(const bf16x8 *)(bQ + 4096 * (2 * h2 + u) + o);
+                for (int u = 0; u < 2; ++u) {
+                    fk[u] = *(const bf16x8 *)(bK + 4096 * (2 * (g & 1) + u) + o);
+                    if constexpr (WQ) fq[u] = *(const bf16x8 *)(bQ + 4096 * (2 * (g & 1) + u) + o);
                 }
+            };
+            auto mm = [&](int g, const bf16x8 *fk, const bf16x8 *fq) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) M::mma(acc_ks[2 * (g & 1) + u], fk[u], Sb[g >> 1]);
+                if constexpr (WQ) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) M::mma(accQ[2 * (g & 1) + u], Sb[g >> 1], fq[u]);
+                }
+            };
+            bf16x8 fkA[2], fqA[2], fkB[2], fqB[2];
+            ld(0, fkA, fqA);
+#pragma unroll
+            for (int g = 0; g < 2 * KBD; g += 2) {
+                ld(g + 1, fkB, fqB);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) M::mma(acc_ks[2 * h2 + u], fk[u], Sb[kb]);
-                if (normal) {
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) M::mma(accQ[2 * h2 + u], Sb[kb], fq[u]);
-                }
+                mm(g, fkA, fqA);
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + 2 < 2 * KBD) ld(g + 2, fkA, fqA);
+                __builtin_amdgcn_sched_barrier(0);
+                mm(g + 1, fkB, fqB);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+        if (normal) ks_qs(std::true_type{});
+        else ks_qs(std::false_type{});
         if (normal) {
             const float *Fl = F + (o_lane & 15);
 #pragma unroll
@@ -988,19 +1002,27 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 Ub[0] = pack8s(Us[0], Us[1]);
                 Ub[1] = pack8s(Us[2], Us[3]);
             }
+            // four groups (kt, half) of four K^T fragments, software-pipelined like K Shat
+            auto ldt = [&](int g, bf16x8 *f) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+                for (int q = 0; q < MBK / 2; ++q) f[q] = frag_kt((g & 1) * (MBK / 2) + q, g >> 1);
+            };
+            auto mmt = [&](int g, const bf16x8 *f) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    bf16x8 fkt[MBK / 2];
+                for (int q = 0; q < MBK / 2; ++q) M::mma(S[(g & 1) * (MBK / 2) + q], f[q], Ub[g >> 1]);
+            };
+            bf16x8 ftA[MBK / 2], ftB[MBK / 2];
+            ldt(0, ftA);
 #pragma unroll
-                    for (int q = 0; q < MBK / 2; ++q) fkt[q] = frag_kt(half * (MBK / 2) + q, kt);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int q = 0; q < MBK / 2; ++q)
-                        M::mma(S[half * (MBK / 2) + q], fkt[q], Ub[kt]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int g = 0; g < 4; g += 2) {
+                ldt(g + 1, ftB);
+                __builtin_amdgcn_sched_barrier(0);
+                mmt(g, ftA);
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + 2 < 4) ldt(g + 2, ftA);
+                __builtin_amdgcn_sched_barrier(0);
+                mmt(g + 1, ftB);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         pack_state();

@@ -57,12 +57,16 @@ def test_plans_for_the_workloads(lib):
     entries = 1 + -(-(1 << 20) // (s * 64))
     w = gdn.gdn_prefill_workspace_bytes(1, 1 << 20, 16, 128, 128, 1)
     assert entries * 16 * 128 * 128 * 4 < w < entries * 16 * 128 * 128 * 4 + (64 << 10)
-    # 512 chains: enough work without splitting
+    # 512 chains of mixed lengths, 266 chunk steps per CU: the one-launch scan in segments of
+    # about 133 chunks (two jobs per CU)
     t, s = gdn.gdn_prefill_plan(32, 270336, 16, 128, 128, gdn.GDN_DTYPE_BF16)
-    assert s == -1
+    assert t == 128 and 125 <= s <= 140
+    # 64 chains of 256 chunks (64 chunk steps per CU): the two-launch column-split scan
+    t, s = gdn.gdn_prefill_plan(4, 4 * 16384, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert t in (32, 64) and s == -1
     # bf16 column-split plans: one 8448-byte record (T', g) per chunk slot and head
     slots = 270336 // 64 + 32
-    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1) == slots * 16 * 8448
+    assert gdn.gdn_prefill_workspace_bytes(32, 270336, 16, 128, 128, 1, 32, -1) == slots * 16 * 8448
     # the one-launch scan on request: segments of 16 chunks for 64 chains by default
     assert gdn.gdn_prefill_workspace_bytes(4, 4 * 4096, 16, 128, 128, 1, 128, 0) > 0
     # fp32 without segments needs no workspace
