@@ -141,6 +141,33 @@ gdn_status gdn_prefill_gated(const void *q, const void *k, const void *v, const 
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill followed by the output gate of the layer (reading notes, section 2.1, the output
+ * equation; gdn_output_gate below): per (token, head) row of d_v values,
+ *   out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + weight),  y = the rule's output.
+ *   z       [total_T, H, d_v] dtype, 16-byte aligned, read only
+ *   weight  [d_v] fp32, 4-byte aligned (zero = plain RMSNorm)
+ *   eps     finite, >= 0
+ *   out     [total_T, H, d_v] dtype, in place of y (y itself is not kept)
+ *   dv_tile, segment_chunks: as for gdn_prefill_ex (0, 0 = automatic)
+ * The bf16 one-launch plans (d_k = d_v = 128 with dv_tile 128, the plan gdn_prefill_plan
+ * reports for long or plentiful work) apply the gate as each row of y leaves the scan, so y
+ * never reaches memory; every other plan runs the prefill into out and then the output-gate
+ * kernel over out in place.  Workspace: gdn_prefill_workspace_bytes_ex for the same options.
+ * Errors: those of gdn_prefill_ex; GDN_ERR_INVALID_ARGUMENT also for a null z or weight with
+ * total_T > 0, misalignment, a negative or non-finite eps, or z or weight overlapping an
+ * output.
+ */
+gdn_status gdn_prefill_output_gated(const void *q, const void *k, const void *v,
+                                    const float *alpha, const float *beta,
+                                    const float *initial_state, const int32_t *cu_seqlens,
+                                    int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                                    int32_t d_v, int32_t dtype, const void *z,
+                                    const float *weight, float eps, void *out,
+                                    float *final_state, void *workspace,
+                                    size_t workspace_bytes, void *stream, int32_t dv_tile,
+                                    int32_t segment_chunks);
+
+/*
  * gdn_prefill for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same operation, arguments and
  * results, with no workspace argument.  Its workspace is a fixed array of

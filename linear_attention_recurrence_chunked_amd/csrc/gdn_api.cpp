@@ -90,8 +90,16 @@ gdn_status gdn_prefill_plan(int32_t num_seqs, int64_t total_T, int32_t H, int32_
     return GDN_OK;
 }
 
-// gdn_prefill_ex and gdn_prefill_gated: with gate_A non-null (gated), alpha and beta are the
-// gate pre-activations a and b, and gate_A, gate_b_alpha [H] complete them.
+// The output gate that gdn_prefill_output_gated applies to y.
+struct OutGate {
+    const void *z;
+    const float *w;
+    float eps;
+};
+
+// gdn_prefill_ex, gdn_prefill_gated and gdn_prefill_output_gated: with gate_A non-null
+// (gated), alpha and beta are the gate pre-activations a and b, and gate_A, gate_b_alpha [H]
+// complete them; with og non-null, y receives the output gate's result.
 static gdn_status prefill_impl(const void *q, const void *k, const void *v, const float *alpha,
                                const float *beta, const float *gate_A,
                                const float *gate_b_alpha, bool gated,
@@ -99,10 +107,17 @@ static gdn_status prefill_impl(const void *q, const void *k, const void *v, cons
                                int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
                                int32_t d_v, int32_t dtype, void *y, float *final_state,
                                void *workspace, size_t workspace_bytes, void *stream,
-                               int32_t dv_tile, int32_t segment_chunks)
+                               int32_t dv_tile, int32_t segment_chunks,
+                               const OutGate *og = nullptr)
 {
     gdn_status st = check_common(total_T, H, d_k, d_v, dtype);
     if (st != GDN_OK) return st;
+    if (og) {
+        if (!(og->eps >= 0.f) || !(og->eps <= 3.4e38f)) return GDN_ERR_INVALID_ARGUMENT;
+        if (total_T > 0 && (!og->z || !og->w)) return GDN_ERR_INVALID_ARGUMENT;
+        if ((og->z && !aligned(og->z, 16)) || (og->w && !aligned(og->w, 4)))
+            return GDN_ERR_INVALID_ARGUMENT;
+    }
     if (gated) {
         if (dtype != GDN_DTYPE_BF16 || dv_tile != 0 || segment_chunks != 0)
             return GDN_ERR_UNSUPPORTED;
@@ -146,7 +161,9 @@ static gdn_status prefill_impl(const void *q, const void *k, const void *v, cons
     struct Span { const void *p; size_t n; };
     const size_t n_h = gated ? (size_t)H * 4 : 0;
     const Span inputs[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_g}, {beta, n_g},
-                           {cu_seqlens, n_cu}, {gate_A, n_h}, {gate_b_alpha, n_h}};
+                           {cu_seqlens, n_cu}, {gate_A, n_h}, {gate_b_alpha, n_h},
+                           {og ? og->z : nullptr, og ? n_v : 0},
+                           {og ? og->w : nullptr, og ? (size_t)d_v * 4 : 0}};
     const Span outs[] = {{y, n_v}, {final_state, final_state ? n_s : 0}, {workspace, need}};
     for (const Span &o : outs) {
         for (const Span &in : inputs)
@@ -184,8 +201,34 @@ static gdn_status prefill_impl(const void *q, const void *k, const void *v, cons
         p.gate_A = gate_A;
         p.gate_b_alpha = gate_b_alpha;
     }
+    // the one-launch scan gates each row of y as it leaves; other plans gate y in place after
+    const bool fused_gate = og && plan.wide;
+    if (fused_gate) {
+        p.og_z = og->z;
+        p.og_w = og->w;
+        p.og_eps = og->eps;
+    }
     hipError_t err = gdn::launch_prefill(p, plan, workspace, (hipStream_t)stream);
+    if (err == hipSuccess && og && !fused_gate && total_T > 0)
+        err = gdn::launch_output_gate(y, og->z, og->w, total_T * H, d_v, og->eps, dtype, y,
+                                      (hipStream_t)stream);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_prefill_output_gated(const void *q, const void *k, const void *v,
+                                    const float *alpha, const float *beta,
+                                    const float *initial_state, const int32_t *cu_seqlens,
+                                    int32_t num_seqs, int64_t total_T, int32_t H, int32_t d_k,
+                                    int32_t d_v, int32_t dtype, const void *z,
+                                    const float *weight, float eps, void *out,
+                                    float *final_state, void *workspace,
+                                    size_t workspace_bytes, void *stream, int32_t dv_tile,
+                                    int32_t segment_chunks)
+{
+    const OutGate og{z, weight, eps};
+    return prefill_impl(q, k, v, alpha, beta, nullptr, nullptr, false, initial_state,
+                        cu_seqlens, num_seqs, total_T, H, d_k, d_v, dtype, out, final_state,
+                        workspace, workspace_bytes, stream, dv_tile, segment_chunks, &og);
 }
 
 gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *alpha,

@@ -29,6 +29,10 @@ struct PrefillProblem {
     // beta then hold a and b [T, H]; gate_A and gate_b_alpha are [H]
     bool gated = false;
     const float *gate_A = nullptr, *gate_b_alpha = nullptr;
+    // output gate on y (one-launch bf16 plans only): z [T, H, dv], weight [dv], eps
+    const void *og_z = nullptr;
+    const float *og_w = nullptr;
+    float og_eps = 0.f;
 };
 
 // Launch plan: columns of the state per workgroup and chunks per segment (-1: no split).

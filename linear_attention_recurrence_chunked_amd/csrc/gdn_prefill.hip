@@ -924,6 +924,9 @@ hipError_t launch_prefill(const PrefillProblem &p, const PrefillPlan &plan, void
     a.dv = p.dv;
     a.y = p.y;
     a.s_final = p.s_final;
+    a.og_z = p.og_z;
+    a.og_w = p.og_w;
+    a.og_eps = p.og_eps;
     if (plan.seg_chunks >= 0) {
         unsigned char *ws = (unsigned char *)workspace;
         a.table = (const SegEntry *)ws;

@@ -217,6 +217,11 @@ struct PrefillArgs {
     void *prep;                // chunk records of the two-launch path, or null
     const float *gate_A;       // non-null: alpha, beta hold the gate pre-activations a, b and
     const float *gate_b_alpha; // the record kernel forms log2 alpha and beta from them
+    // output gate applied as y leaves the one-launch scan (null og_z: plain y):
+    // y <- sigmoid(z) y / sqrt(mean(y^2) + og_eps) (1 + og_w), per row of d_v values
+    const void *og_z;
+    const float *og_w;
+    float og_eps;
 };
 
 // Arguments of the one-launch bf16 scan (gdn_prefill_wide.hip).

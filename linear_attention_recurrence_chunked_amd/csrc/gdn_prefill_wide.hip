@@ -136,6 +136,39 @@ __device__ __forceinline__ void copy4_async(const void *base, unsigned off, unsi
                  "s"(lds)
                  : "memory", "m0");
 }
+// Output gate of eight elements of a 128-value row of y whose pieces are held by 16
+// consecutive lanes (one DPP row): sigmoid(z) y / sqrt(mean(y^2) + eps) (1 + w), bf16 in and
+// out, fp32 inside.  The row's sum of squares reaches every lane of the row identically.
+__device__ __forceinline__ u32x4 out_gate8(u32x4 y, u32x4 z, const float *w, float eps)
+{
+    float yf[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t u = y[e >> 1];
+        yf[e] = __builtin_bit_cast(float, (e & 1) ? (u & 0xffff0000u) : (u << 16));
+        ss += yf[e] * yf[e];
+    }
+    ss += dpp_f32<0xb1, 0xf>(ss);          // quad_perm [1, 0, 3, 2]
+    ss += dpp_f32<0x4e, 0xf>(ss);          // quad_perm [2, 3, 0, 1]
+    ss += dpp_f32<0x141, 0xf>(ss);         // row_half_mirror
+    ss += dpp_f32<0x140, 0xf>(ss);         // row_mirror
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.f / 128.f) + eps);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        float o[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint32_t u = z[(e + d) >> 1];
+            const float zf = __builtin_bit_cast(float, d ? (u & 0xffff0000u) : (u << 16));
+            o[d] = yf[e + d] * inv * (1.f + w[e + d]) * __builtin_amdgcn_rcpf(1.f + __expf(-zf));
+        }
+        const bf16x2 h = bf16x2{(__bf16)o[0], (__bf16)o[1]};
+        r[e >> 1] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+}
+
 // A wave-uniform value as such (its lanes are known to agree).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ long long uni64(long long x)
@@ -410,6 +443,38 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             pg[128 + lane] = __builtin_amdgcn_exp2f(x);
             pg[192 + lane] = __builtin_amdgcn_exp2f(-x);
         };
+        // y of chunk jp, which the column waves stage in LDS as whole rows: this wave stores
+        // rows 16 pw .. 16 pw + 15 (four passes of four rows, 16 lanes per row), through the
+        // output gate when one is given
+        int ycount = 0;
+        int ypending = -1;
+        auto store_y = [&](int jp) {
+            ycount += kWideCol;
+            lds_wait(kMiscCntY, ycount);
+            const long long yrow = ((row0_of(jp) + 16 * pw) * H + h) * (long long)(DV * 2);
+            const int nv = nvalid(jp);
+            const unsigned char *bY = smem + L::sY;
+            const int lgy = lane >> 4, g = lane & 15;
+            float w[8];
+            if (a.og_z) {
+                const float *wp = a.og_w + 8 * g;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = wp[e];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 16 * pw + 4 * q + lgy;
+                const u32x4 v = *(const u32x4 *)(bY + t * (DV * 2) + ((g ^ (t & 15)) << 4));
+                const unsigned off = (unsigned)((4 * q + lgy) * H * DV * 2 + 16 * g);
+                if (t < nv) {                       // whole rows (16 lanes) agree
+                    u32x4 o = v;
+                    if (a.og_z)
+                        o = out_gate8(v, *(const u32x4 *)((const unsigned char *)a.og_z + yrow + off),
+                                      w, a.og_eps);
+                    *(u32x4 *)((unsigned char *)a.y + yrow + off) = o;
+                }
+            }
+        };
         int pbar_target = 0;
         auto prep_barrier = [&]() {
             lds_count(kMiscPbar);
@@ -541,6 +606,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             *(f32x4 *)ablk(tb0, ib0) = a1;
             if (np == 3) *(f32x4 *)ablk(3, ib1) = a2;
             *(f32x4 *)(sX + (d0 + ln) * L::LDX + 4 * lg) = xT;
+            // the rows of y staged in this step leave while the column waves reach their T' read
+            if (ypending >= 0) {
+                store_y(ypending);
+                ypending = -1;
+            }
             // the tile still holds the T' the column waves read in this step until every one of
             // them has loaded it (chunk j's is written during step j - 1)
             lds_wait(kMiscCntT, kWideCol * j);
@@ -653,14 +723,22 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 copy_chunk_kq(j + 1, false, true);
                 copy_chunk_v(j + 1);
             }
+            // the column waves stage the y of chunk j - 1 in this step
+            if (j >= 1 && j - 1 >= nwarm) ypending = j - 1;
             if (j + 1 < nch) {
                 gates(j + 1);
                 make_t(j + 1);
                 if (pw == 3) factors(j + 1);
             }
+            if (ypending >= 0) {
+                store_y(ypending);
+                ypending = -1;
+            }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
+        // the last chunk's y, staged by the column waves after their loop
+        if (nch > 0 && nch - 1 >= nwarm) store_y(nch - 1);
         return;
     }
 
@@ -682,15 +760,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     //   o_tt: T' fragment (row 16 mb + ln, granule lg): + 2048 mb, ^ 32 mb
     //   o_v:  transposing V read (rows 32 (tb / 2) + 8 lg + 4 (tb % 2) + ln / 4, this lane's
     //         four columns): + 8192 (tb / 2) + 1024 (tb % 2)
-    //   o_ys / o_yr: y staging write (row 16 tb + ln) / row read (row 8 cw + 4 i + lg)
-    //   o_yg: y in memory, token 8 cw + 4 i + lg of the chunk, granule ln
+    //   o_ys: y staging write (row 16 tb + ln)
     unsigned o_kq = ln * 256 + ((kq_pi(lg) ^ (ln & 7)) << 4);
     unsigned o_kt = (4 * lg + (ln >> 2)) * 256 + ((kq_pi(ln & 3) ^ (4 * (lg & 1) + (ln >> 2))) << 4);
     unsigned o_tt = ln * 128 + ((lg ^ (ln & 7) ^ (ln >> 3)) << 4);
     unsigned o_v = (8 * lg + (ln >> 2)) * 256 + (((4 * tile + (ln & 3)) ^ ((ln >> 2) << 2)) << 4) + 8 * sw;
     unsigned o_ys = ln * 256 + (((4 * tile + lg) ^ ln) << 4) + 8 * sw;
-    unsigned o_yr = (8 * cw + lg) * 256 + ((ln ^ (8 * (cw & 1) + lg)) << 4);
-    unsigned o_yg = (unsigned)lg * (unsigned)(H * DV * 2) + 16 * ln;
     unsigned o_lane = lane;
     f32x4 S[MBK];
     auto load_state = [&](const float *src, float scale) {
@@ -737,16 +812,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) yq[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Y of chunk jp = carried gamma 2^ls (Shat^T Q^T) + U^T P^T, P from buffer jp % 2
     // Y of chunk jp = carried gamma 2^ls (Shat^T Q^T) + U^T P^T.  Each wave holds 4 columns of
     // each of 64 tokens; the pieces meet in LDS (16-byte granules of a row XOR-swizzled by the
-    // row) and leave as whole rows, wave w storing rows 8 w .. 8 w + 7 in two 1 KiB pieces.
-    int ytarget = 0;
+    // row), from where the prep waves store them as whole rows.
     auto finish = [&](int jp) {
+        (void)jp;
         const unsigned char *bP = smem + L::sP + 16 * o_lane;
         unsigned char *bY = smem + L::sY;
-        const long long t0 = row0_of(jp);
-        const int nv = nvalid(jp);
         bf16x8 fp[6];
 #pragma unroll
         for (int f = 0; f < 6; ++f) fp[f] = *(const bf16x8 *)(bP + f * 1024);
@@ -762,17 +834,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
             *(bf16x4 *)(bY + o_ys + 4096 * tb) = __builtin_convertvector(pu[tb], bf16x4);
-        lds_count(kMiscCntY);
-        ytarget += kWideCol;
-        lds_wait(kMiscCntY, ytarget);
-        unsigned char *const yb = (unsigned char *)a.y + ((t0 + 8 * cw) * H + h) * (long long)(DV * 2);
-        const unsigned lgv = o_lane >> 4;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const u32x4 v = *(const u32x4 *)(bY + ((i ? (o_yr ^ 64) : o_yr) + 1024 * i));
-            if ((int)lgv < nv - 8 * cw - 4 * i)
-                *(u32x4 *)(yb + (unsigned)(4 * i * H * DV * 2) + o_yg) = v;
-        }
+        lds_count(kMiscCntY);              // the prep waves store the staged rows
     };
 
     // P = lower_incl(Q K^T (.) Gamma) of chunk j as the six operand fragments read a step
@@ -850,8 +912,6 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         opaque(o_tt);
         opaque(o_v);
         opaque(o_ys);
-        opaque(o_yr);
-        opaque(o_yg);
         opaque(o_lane);
         if (mode == 1 && j == nwarm) {
             // the warm-up reached the bound, or the exact chain takes over

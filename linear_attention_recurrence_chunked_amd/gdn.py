@@ -62,6 +62,10 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill.argtypes = pre
     lib.gdn_prefill_ex.restype = i32
     lib.gdn_prefill_ex.argtypes = pre + [i32, i32]
+    lib.gdn_prefill_output_gated.restype = i32
+    lib.gdn_prefill_output_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                             i32, vp, vp, c.c_float, vp, vp, vp, sz, vp, i32,
+                                             i32]
     lib.gdn_prefill_gated.restype = i32
     lib.gdn_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                       i32, i32, vp, vp, vp, sz, vp]
@@ -175,6 +179,41 @@ def gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, num_s
                                _stream(stream), dv_tile, segment_chunks)
     _check("gdn_prefill", st)
     return y, final_state
+
+
+def gdn_prefill_output_gated(q, k, v, alpha, beta, z, weight, eps: float = 1e-6,
+                             initial_state=None, cu_seqlens=None, num_seqs=None, out=None,
+                             final_state=None, workspace=None, stream=None, dv_tile: int = 0,
+                             segment_chunks: int = 0, want_final_state: bool = True):
+    """Chunked prefill followed by the output gate: out = sigmoid(z) * RMSNorm(y) * (1 +
+    weight) per (token, head) row, with z [T, H, d_v] in q's dtype and weight [d_v] fp32.
+    Other arguments as gdn_prefill.  Returns (out, final_state)."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        n = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != n:
+            raise ValueError("num_seqs does not match cu_seqlens")
+        num_seqs = n
+    elif num_seqs is None:
+        num_seqs = 1
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((num_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = gdn_prefill_workspace_bytes(num_seqs, T, H, dk, dv, dt, dv_tile, segment_chunks)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gdn_prefill_output_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                         _ptr(initial_state), _ptr(cu_seqlens), num_seqs, T, H,
+                                         dk, dv, dt, _ptr(z), _ptr(weight), float(eps), _ptr(out),
+                                         _ptr(final_state), _ptr(workspace), wbytes,
+                                         _stream(stream), dv_tile, segment_chunks)
+    _check("gdn_prefill_output_gated", st)
+    return out, final_state
 
 
 def gdn_noalloc_scratch_bytes() -> int:

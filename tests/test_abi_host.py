@@ -140,6 +140,35 @@ def prefill_noalloc(lib, **kw):
                                    a["y"], a["sf"], a["stream"])
 
 
+def prefill_og(lib, **kw):
+    a = dict(q=1 * G, k=2 * G, v=3 * G, alpha=4 * G, beta=5 * G, s0=None, cu=None, n=2, T=256,
+             H=2, dk=128, dv=128, dt=1, z=8 * G, w=10 * G, eps=1e-6, out=6 * G, sf=7 * G,
+             ws=9 * G, wsb=G, stream=None, tile=0, seg=-1)
+    a.update(kw)
+    return lib.gdn_prefill_output_gated(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"],
+                                        a["cu"], a["n"], a["T"], a["H"], a["dk"], a["dv"],
+                                        a["dt"], a["z"], a["w"], a["eps"], a["out"], a["sf"],
+                                        a["ws"], a["wsb"], a["stream"], a["tile"], a["seg"])
+
+
+# rejected on the host before anything is enqueued
+@pytest.mark.parametrize("kw", [
+    dict(z=None), dict(w=None),                          # missing gate inputs
+    dict(z=8 * G + 8), dict(w=10 * G + 2),               # misaligned
+    dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(z=6 * G),                                       # z is the output
+    dict(w=6 * G + 256),                                 # weight inside the output
+    dict(n=0), dict(H=0),
+])
+def test_prefill_output_gated_rejects(lib, kw):
+    assert prefill_og(lib, **kw) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_output_gated_unsupported(lib):
+    assert prefill_og(lib, dk=96) == gdn.GDN_ERR_UNSUPPORTED
+    assert prefill_og(lib, dt=4) == gdn.GDN_ERR_UNSUPPORTED
+
+
 def test_noalloc_scratch_size(lib):
     assert gdn.gdn_noalloc_scratch_bytes() == 64 << 20
 
