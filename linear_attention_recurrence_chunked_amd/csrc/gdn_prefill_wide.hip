@@ -330,8 +330,6 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
     // ================================================================ prep waves
     if (wave >= kWideCol) {
         const int pw = wave - kWideCol;
-        const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
-        static_assert(CK / kWidePrep == 4 && CV / kWidePrep == 4 && KG == 16, "copy layout");
         // Gram fragment rows: see make_t
         unsigned o_g;
         {
@@ -339,77 +337,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             const int rr = 16 * ((ln0 >> 2) & 1) + 4 * (ln0 >> 3) + (ln0 & 3);
             o_g = rr * 256 + ((kq_pi(lg0) ^ (rr & 7)) << 4);
         }
-        // Copy q of this wave fills 1 KiB piece jj = 4 pw + q of a tile: lane (ln, lg) writes
-        // slot ln of tile row r = 16 pw + 4 q + lg.  In a K or Q tile that slot holds logical
-        // granule kq_logical(r, ln), which depends on r only through r % 8 = 4 (q % 2) + lg;
-        // the K tile's row r holds token split_orig(r) = 32 (pw / 2) + 4 (pw % 2) + 8 q + lg,
-        // the Q tile's token r.  In a V tile the slot holds granule ln ^ 4 lg.  So a full
-        // chunk's copies take one of three per-lane byte offsets plus a uniform row offset.
-        unsigned okq0, okq1, ovv, oab;
-        {
-            const int ln0 = lane & 15, lg0 = lane >> 4;
-            okq0 = lg0 * rsK + 16 * kq_logical<DK>(lg0, ln0);
-            okq1 = lg0 * rsK + 16 * kq_logical<DK>(4 + lg0, ln0);
-            ovv = lg0 * rsV + 16 * (ln0 ^ (lg0 << 2));
-            oab = (unsigned)lane * (unsigned)H * 4u;
-        }
-        auto copy_chunk_kq = [&](int j, bool with_k, bool with_q) {
-            const long long t0 = row0_of(j);
-            const int last = nvalid(j) - 1;
-            const unsigned char *ck = (const unsigned char *)a.k + (t0 * H + h) * (long long)DK * 2;
-            const unsigned char *cq = (const unsigned char *)a.q + (t0 * H + h) * (long long)DK * 2;
-            unsigned char *dk = smem + L::sK + (j % 3) * L::szK;
-            unsigned char *dq = smem + L::sQ + (j & 1) * L::szK;
-            if (last == kChunk - 1) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int jj = pw * 4 + q;
-                    const unsigned o = (q & 1) ? okq1 : okq0;
-                    if (with_k)
-                        copy16_async(ck + (32 * (pw >> 1) + 4 * (pw & 1) + 8 * q) * rsK, o,
-                                     lds_addr(dk + 1024 * jj));
-                    if (with_q)
-                        copy16_async(cq + (16 * pw + 4 * q) * rsK, o, lds_addr(dq + 1024 * jj));
-                }
-            } else {            // a sequence's last, partial chunk: rows past its end repeat the last
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int jj = pw * 4 + q;
-                    const int r = 16 * pw + 4 * q + (lane >> 4);
-                    const unsigned o = 16 * kq_logical<DK>(r, lane & 15);
-                    if (with_k) {
-                        const int rk = split_orig(r) < last ? split_orig(r) : last;
-                        copy16_async(ck, (unsigned)rk * rsK + o, lds_addr(dk + 1024 * jj));
-                    }
-                    if (with_q) {
-                        const int rq = r < last ? r : last;
-                        copy16_async(cq, (unsigned)rq * rsK + o, lds_addr(dq + 1024 * jj));
-                    }
-                }
-            }
-        };
-        auto copy_chunk_v = [&](int j) {
-            const long long t0 = row0_of(j);
-            const int last = nvalid(j) - 1;
-            const unsigned char *cv = (const unsigned char *)a.v + (t0 * H + h) * (long long)DV * 2;
-            unsigned char *dv = smem + L::sV + (j & 1) * L::szV;
-            if (last == kChunk - 1) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int jj = pw * 4 + q;
-                    copy16_async(cv + 4 * jj * rsV, ovv, lds_addr(dv + 1024 * jj));
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int jj = pw * 4 + q;
-                    const int r = 4 * jj + (lane >> 4);
-                    const int rv = r < last ? r : last;
-                    copy16_async(cv, (unsigned)rv * rsV + (ovv - (lane >> 4) * rsV),
-                                 lds_addr(dv + 1024 * jj));
-                }
-            }
-        };
+        const unsigned oab = (unsigned)lane * (unsigned)H * 4u;
         auto copy_chunk_gates = [&](int j) {
             if (pw < 2) {
                 const long long t0 = row0_of(j);
@@ -693,13 +621,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         };
 
         if (nch > 0) {
-            copy_chunk_kq(0, true, true);
-            copy_chunk_v(0);
             copy_chunk_gates(0);
-            if (nch > 1) {
-                copy_chunk_kq(1, true, false);
-                copy_chunk_gates(1);
-            }
+            if (nch > 1) copy_chunk_gates(1);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();                                  // #0: chunk 0 (and K, gates of 1) staged
@@ -715,14 +638,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         for (int j = 0; j < nch; ++j) {
             refresh_lane();
             opaque(o_g);
-            if (j + 2 < nch) {
-                copy_chunk_kq(j + 2, true, false);
-                copy_chunk_gates(j + 2);
-            }
-            if (j + 1 < nch) {
-                copy_chunk_kq(j + 1, false, true);
-                copy_chunk_v(j + 1);
-            }
+            if (j + 2 < nch) copy_chunk_gates(j + 2);
             // the column waves stage the y of chunk j - 1 in this step
             if (j >= 1 && j - 1 >= nwarm) ypending = j - 1;
             if (j + 1 < nch) {
@@ -904,7 +820,59 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         }
     };
 
-    lds_barrier();            // #0
+    // The K, Q and V tiles of the chunks ahead (K two chunks ahead, Q and V one), copied by the
+    // column waves: wave cw fills the 1 KiB pieces jj = 2 cw + q (q = 0, 1) of each tile, lane
+    // (ln, lg) slot ln of tile row r = 8 cw + 4 q + lg.  In a K or Q tile that slot holds logical
+    // granule kq_logical(r, ln), a function of r % 8 = 4 q + lg; the K tile's row r holds token
+    // split_orig(r) = split_orig(8 cw + 4 q) + lg, the Q tile's token r.  In a V tile the slot
+    // holds granule ln ^ 4 lg.  A full chunk's copies thus take a per-lane byte offset and a
+    // uniform row; a sequence's last, partial chunk repeats its last row past the end.
+    const unsigned rsK = (unsigned)(H * DK) * 2, rsV = (unsigned)(H * DV) * 2;   // bytes
+    static_assert(CK == 2 * kWideCol && CV == 2 * kWideCol && KG == 16, "copy layout");
+    auto copy_tiles = [&](int j, bool with_k, bool with_qv) {
+        const long long t0 = row0_of(j);
+        const int last = nvalid(j) - 1;
+        const long long head = (t0 * H + h) * (long long)DK * 2;
+        const unsigned char *ck = (const unsigned char *)a.k + head;
+        const unsigned char *cq = (const unsigned char *)a.q + head;
+        const unsigned char *cv = (const unsigned char *)a.v + (t0 * H + h) * (long long)DV * 2;
+        unsigned char *dk = smem + L::sK + (j % 3) * L::szK;
+        unsigned char *dq = smem + L::sQ + (j & 1) * L::szK;
+        unsigned char *dv = smem + L::sV + (j & 1) * L::szV;
+        const int lnc = (int)(o_lane & 15), lgc = (int)(o_lane >> 4);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int jj = 2 * cw + q;
+            const int r0 = 8 * cw + 4 * q;                 // tile row of lane group 0
+            const unsigned gk = 16 * kq_logical<DK>(4 * q + lgc, lnc);
+            const unsigned gv = 16 * (lnc ^ (lgc << 2));
+            if (last == kChunk - 1) {
+                if (with_k)
+                    copy16_async(ck + split_orig(r0) * rsK, lgc * rsK + gk, lds_addr(dk + 1024 * jj));
+                if (with_qv) {
+                    copy16_async(cq + r0 * rsK, lgc * rsK + gk, lds_addr(dq + 1024 * jj));
+                    copy16_async(cv + r0 * rsV, lgc * rsV + gv, lds_addr(dv + 1024 * jj));
+                }
+            } else {
+                const int r = r0 + lgc;
+                if (with_k) {
+                    const int rk = split_orig(r) < last ? split_orig(r) : last;
+                    copy16_async(ck, (unsigned)rk * rsK + gk, lds_addr(dk + 1024 * jj));
+                }
+                if (with_qv) {
+                    const int rq = r < last ? r : last;
+                    copy16_async(cq, (unsigned)rq * rsK + gk, lds_addr(dq + 1024 * jj));
+                    copy16_async(cv, (unsigned)rq * rsV + gv, lds_addr(dv + 1024 * jj));
+                }
+            }
+        }
+    };
+    if (nch > 0) {
+        copy_tiles(0, true, true);
+        if (nch > 1) copy_tiles(1, true, false);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();            // #0: chunk 0 (and K of chunk 1) staged
     lds_barrier();            // #1
     for (int j = 0; j < nch; ++j) {
         opaque(o_kq);
@@ -913,6 +881,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         opaque(o_v);
         opaque(o_ys);
         opaque(o_lane);
+        if (j + 2 < nch) copy_tiles(j + 2, true, false);
+        if (j + 1 < nch) copy_tiles(j + 1, false, true);
         if (mode == 1 && j == nwarm) {
             // the warm-up reached the bound, or the exact chain takes over
             const float lw = __builtin_bit_cast(
@@ -1086,6 +1056,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             }
         }
         pack_state();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
     }
     if (nch > 0 && nch - 1 >= nwarm) finish(nch - 1);
