@@ -96,7 +96,8 @@ def load_traffic(kernel_key: str, sources):
 
 def profile_run(torch, gdn, wl, dev):
     """Three prefill launches, three decode steps, three backward calls, three channel-gated
-    prefills and decode steps, three indexer calls and a 1 GiB elementwise pass, untimed."""
+    prefills and decode steps, three indexer calls, two prefills of each of the long and the
+    mixed-length workloads and a 1 GiB elementwise pass, untimed."""
     import numpy as np
     inp = wl.workload_inputs(wl.PREFILL)
     q, k, v = (wl.to_torch(inp[n], dev, "bf16") for n in ("q", "k", "v"))
@@ -135,6 +136,21 @@ def profile_run(torch, gdn, wl, dev):
     for _ in range(3):
         gdn.gdn_qsa_index(iq, ik, block_budget=512, want_blocks=False)
     del iq, ik, qi
+    # the 2^20-token sequence and the 32 mixed-length sequences, two prefills each (in that
+    # order: the one-launch scan's dispatches of the long workload come first)
+    for wobj in (wl.LONG, wl.VARLEN):
+        wi = wl.workload_inputs(wobj)
+        tq, tk, tv = (wl.to_torch(wi[n], dev, "bf16") for n in ("q", "k", "v"))
+        ta, tb = (torch.from_numpy(wi[n]).to(dev) for n in ("alpha", "beta"))
+        ts0 = None if wi["s0"] is None else torch.from_numpy(wi["s0"]).to(dev)
+        tcu = None if wi["cu_seqlens"] is None else torch.from_numpy(wi["cu_seqlens"]).to(dev)
+        n_s = wi["num_seqs"]
+        del wi
+        for _ in range(2):
+            gdn.gdn_prefill(tq, tk, tv, ta, tb, initial_state=ts0, cu_seqlens=tcu, num_seqs=n_s)
+        torch.cuda.synchronize()
+        del tq, tk, tv, ta, tb, ts0, tcu
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
     # calibration: an elementwise kernel that reads 1 GiB and writes 1 GiB
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -215,6 +231,49 @@ def main():
         gdn.gdn_prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
                         num_seqs=nseq, y=y, final_state=sf, workspace=ws if need else None)
 
+    def time_output_gated(tq, tk, tv, ta, tb, ts0, tcu, n_s, ty, tsf, reps):
+        """The prefill with the layer's output gate: the fused entry point against the prefill
+        followed by the output-gate kernel, each call timed after a cache flush (z: seeded
+        N(0, 4) bf16, weight: seeded N(0, 0.01))."""
+        TT, HH, dd_ = tq.shape
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234)
+        tz = (2.0 * torch.randn((TT, HH, dd_), generator=g, device=dev)).to(torch.bfloat16)
+        tw = 0.1 * torch.randn((dd_,), generator=g, device=dev)
+        ptile, pseg = gdn.gdn_prefill_plan(n_s, TT, HH, dd_, dd_, gdn.GDN_DTYPE_BF16)
+        wneed = gdn.gdn_prefill_workspace_bytes(n_s, TT, HH, dd_, dd_, gdn.GDN_DTYPE_BF16)
+        tws = torch.empty(max(wneed, 16), dtype=torch.uint8, device=dev)
+
+        def fused():
+            gdn.gdn_prefill_output_gated(tq, tk, tv, ta, tb, tz, tw, 1e-6, initial_state=ts0,
+                                         cu_seqlens=tcu, num_seqs=n_s, out=ty, final_state=tsf,
+                                         workspace=tws if wneed else None)
+
+        def composed():
+            gdn.gdn_prefill(tq, tk, tv, ta, tb, initial_state=ts0, cu_seqlens=tcu,
+                            num_seqs=n_s, y=ty, final_state=tsf,
+                            workspace=tws if wneed else None)
+            gdn.gdn_output_gate(ty, tz, tw, eps=1e-6, out=ty)
+
+        res = {}
+        for name, f in (("ms_fused_call", fused), ("ms_prefill_then_output_gate", composed)):
+            f()
+            torch.cuda.synchronize()
+            ts_ = []
+            for _ in range(reps):
+                cache_flush()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts_.append(e0.elapsed_time(e1))
+            res[name] = round(float(np.median(ts_)), 4)
+        res["gate_applied"] = ("as each row of y leaves the one-launch scan" if ptile == 128
+                               else "by the output-gate kernel after the prefill")
+        del tz, tw, tws
+        return res
+
     for _ in range(args.warmup):
         run_prefill()
     torch.cuda.synchronize()
@@ -287,6 +346,8 @@ def main():
         "hbm_frac_of_algorithmic_bytes": round(pbytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
 
+    og_main = time_output_gated(q, k, v, alpha, beta, None, None, nseq, y, sf, args.steps)
+
     # ------------------------------------------------------------------ other prefill shapes
     # the 2^20-token single sequence and the 32 packed sequences, each in the library's own
     # plan, timed call by call after a cache flush
@@ -342,7 +403,10 @@ def main():
                             "traffic": None if trk is None else trk["bytes_per_launch"]},
                "algorithmic_bytes_per_launch": nb,
                "hbm_frac_of_algorithmic_bytes": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        del tq, tk, tv, ta, tb, ts0, tcu, ty, tsf, tws
+        del tws
+        res["output_gated"] = time_output_gated(tq, tk, tv, ta, tb, ts0, tcu, n_s, ty, tsf,
+                                                reps)
+        del tq, tk, tv, ta, tb, ts0, tcu, ty, tsf
         torch.cuda.empty_cache()
         return res
 

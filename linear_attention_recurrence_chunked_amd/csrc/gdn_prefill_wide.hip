@@ -374,32 +374,47 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         // y of chunk jp, which the column waves stage in LDS as whole rows: this wave stores
         // rows 16 pw .. 16 pw + 15 (four passes of four rows, 16 lanes per row), through the
         // output gate when one is given
+        // With the output gate, this lane's eight weights are read once, and the z pieces of the
+        // rows a step stores are requested at the step's start (their latency then passes
+        // while the step forms T').
         int ycount = 0;
         int ypending = -1;
+        float wg[8];
+        u32x4 zpre[4];
+        if (a.og_z) {
+            const float *wp = a.og_w + 8 * (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wg[e] = wp[e];
+        }
+        auto y_row0 = [&](int jp) { return ((row0_of(jp) + 16 * pw) * H + h) * (long long)(DV * 2); };
+        auto y_off = [&](int q) {
+            return (unsigned)((4 * q + (lane >> 4)) * H * DV * 2 + 16 * (lane & 15));
+        };
+        auto load_z = [&](int jp) {
+            const long long yrow = y_row0(jp);
+            const int nv = nvalid(jp);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                zpre[q] = u32x4{0u, 0u, 0u, 0u};
+                if (16 * pw + 4 * q + (lane >> 4) < nv)
+                    zpre[q] = *(const u32x4 *)((const unsigned char *)a.og_z + yrow + y_off(q));
+            }
+        };
         auto store_y = [&](int jp) {
             ycount += kWideCol;
             lds_wait(kMiscCntY, ycount);
-            const long long yrow = ((row0_of(jp) + 16 * pw) * H + h) * (long long)(DV * 2);
+            const long long yrow = y_row0(jp);
             const int nv = nvalid(jp);
             const unsigned char *bY = smem + L::sY;
             const int lgy = lane >> 4, g = lane & 15;
-            float w[8];
-            if (a.og_z) {
-                const float *wp = a.og_w + 8 * g;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = wp[e];
-            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int t = 16 * pw + 4 * q + lgy;
                 const u32x4 v = *(const u32x4 *)(bY + t * (DV * 2) + ((g ^ (t & 15)) << 4));
-                const unsigned off = (unsigned)((4 * q + lgy) * H * DV * 2 + 16 * g);
                 if (t < nv) {                       // whole rows (16 lanes) agree
                     u32x4 o = v;
-                    if (a.og_z)
-                        o = out_gate8(v, *(const u32x4 *)((const unsigned char *)a.og_z + yrow + off),
-                                      w, a.og_eps);
-                    *(u32x4 *)((unsigned char *)a.y + yrow + off) = o;
+                    if (a.og_z) o = out_gate8(v, zpre[q], wg, a.og_eps);
+                    *(u32x4 *)((unsigned char *)a.y + yrow + y_off(q)) = o;
                 }
             }
         };
@@ -640,7 +655,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             opaque(o_g);
             if (j + 2 < nch) copy_chunk_gates(j + 2);
             // the column waves stage the y of chunk j - 1 in this step
-            if (j >= 1 && j - 1 >= nwarm) ypending = j - 1;
+            if (j >= 1 && j - 1 >= nwarm) {
+                ypending = j - 1;
+                if (a.og_z) load_z(j - 1);
+            }
             if (j + 1 < nch) {
                 gates(j + 1);
                 make_t(j + 1);
@@ -654,7 +672,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             lds_barrier();
         }
         // the last chunk's y, staged by the column waves after their loop
-        if (nch > 0 && nch - 1 >= nwarm) store_y(nch - 1);
+        if (nch > 0 && nch - 1 >= nwarm) {
+            if (a.og_z) load_z(nch - 1);
+            store_y(nch - 1);
+        }
         return;
     }
 
