@@ -739,7 +739,8 @@ def main():
         "prefill": {"ms_median": round(pre_med, 4), "ms_warm_back_to_back": round(warm_ms, 4),
                     "ms_median_after_write_only_flush": round(wo_med, 4),
                     "tokens_per_s_warm": round(T / (warm_ms * 1e-3), 1),
-                    "wall_s_timed_loop_incl_flush": round(wall, 4)},
+                    "wall_s_timed_loop_incl_flush": round(wall, 4),
+                    "output_gated": og_main},
         "roofline": roofline,
         "long_prefill": long_obj,
         "varlen_prefill": varlen_obj,
