@@ -1203,7 +1203,8 @@ __global__ __launch_bounds__(64 * (3 + 2 * (DVT / 16))) void scan_pipe_kernel(Pr
         // accumulator blocks of a 32-column half pack into a fragment directly: accumulator
         // [r] of block (tb, ib) = k_i . q_t, t = 16 tb + ln, i = original token of internal
         // row 16 ib + 4 lg + r, which is 32 (ib / 2) + 8 lg + 4 (ib % 2) + r.
-        // Gamma_ti = 2^g_t 2^-g_i (g >= -126: both factors are normal floats).
+        // Gamma_ti = 2^(g_t - g_i): formed as 2^g_t 2^-g_i while the chunk's total decay g_C
+        // stays at or above -60 (both factors then normal floats), else per element.
         auto make_p = [&](auto stc, int c) {
             constexpr int ST = decltype(stc)::value;
             const unsigned char *stg = smem + ST * L::stage;

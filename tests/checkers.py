@@ -94,11 +94,27 @@ def _mutant(step):
     return run
 
 
-def _undecayed_residual(S, q, k, v, a, b, t):
-    # residual taken against the undecayed state, decay applied afterwards
-    e = v[t] - S.T @ k[t]
-    S = a[t] * S + b[t] * np.outer(k[t], e)
-    return S, S.T @ q[t]
+def _placed_step(residual_against: str, decay_at: str):
+    """One delta-rule step with the decay placed by the arguments.  The rule (Gated DeltaNet,
+    section 2.1; the paper-lens walkthrough's section "Inside GDN: erase before you write")
+    erases against the decayed state and decays before writing: residual_against="decayed",
+    decay_at="before".  The other settings are the plausible misplacements: the residual taken
+    against the state before its decay, and/or the decay applied after the write."""
+    assert residual_against in ("decayed", "undecayed") and decay_at in ("before", "after")
+
+    def step(S, q, k, v, a, b, t):
+        R = a[t] * S if residual_against == "decayed" else S
+        e = v[t] - R.T @ k[t]
+        if decay_at == "before":
+            S = a[t] * S + b[t] * np.outer(k[t], e)
+        else:
+            S = a[t] * (S + b[t] * np.outer(k[t], e))
+        return S, S.T @ q[t]
+    return step
+
+
+# residual against the undecayed state, while the kept part of the state is decayed
+_undecayed_residual = _placed_step("undecayed", "before")
 
 
 def _additive(S, q, k, v, a, b, t):
@@ -114,10 +130,8 @@ def _read_before_write(S, q, k, v, a, b, t):
     return Sd + b[t] * np.outer(k[t], e), y
 
 
-def _decay_after_write(S, q, k, v, a, b, t):
-    e = v[t] - S.T @ k[t]
-    S = a[t] * (S + b[t] * np.outer(k[t], e))
-    return S, S.T @ q[t]
+# the whole update, write included, decayed afterwards
+_decay_after_write = _placed_step("undecayed", "after")
 
 
 def _residual_sign(S, q, k, v, a, b, t):

@@ -131,3 +131,16 @@ def test_bf16_rounding_is_round_to_nearest_even():
     x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 0.0, 1.0 + 2.0 ** -7])
     got = bf16_to_f64(bf16_bits(x))
     np.testing.assert_array_equal(got, [1.0, 1.0 + 2.0 ** -6, -2.5, 0.0, 1.0 + 2.0 ** -7])
+
+
+def test_placed_step_at_the_rule_is_the_oracle(oracle_lib):
+    """The mutants' shared step, at the rule's own placement (residual against the decayed
+    state, decay before the write), reproduces the oracle; so the misplaced settings differ
+    from it by the placement alone."""
+    from checkers import _mutant, _placed_step
+    rng = np.random.default_rng(4)
+    q, k, v, a, b, s0 = pins._rand_chain(rng, 48, 16, 8, a_lo=0.6, a_hi=0.95)
+    y, S = oracle_lib.chain_c(q, k, v, a, b, s0)
+    y2, S2 = _mutant(_placed_step("decayed", "before"))(q, k, v, a, b, s0)
+    assert np.allclose(y2, y, rtol=1e-12, atol=1e-12 * np.max(np.abs(y)))
+    assert np.allclose(S2, S, rtol=1e-12, atol=1e-12 * np.max(np.abs(S)))
