@@ -24,35 +24,49 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=gfx950",
           "-I", os.path.join(os.path.dirname(PKG), "include")]
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the device code is compiled as
+# usual); the library then needs the clang sanitizer runtime preloaded in its process.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
+LIB_SAN = os.path.join(PKG, "libgdn_san.so")
+OUT_DIR_SAN = os.path.join(PKG, "_build_san")
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(OUT_DIR_SAN if sanitize else OUT_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + (SANITIZE if sanitize else []) + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libgdn.so, or with sanitize libgdn_san.so (host code instrumented; for CPU tests
+    of the host side, loaded when GDN_LIB names it)."""
+    lib = LIB_SAN if sanitize else LIB
+    os.makedirs(OUT_DIR_SAN if sanitize else OUT_DIR, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+        objs = list(ex.map(lambda s_: _compile(s_, sanitize), srcs))
+    tmp = lib + ".tmp%d" % os.getpid()
+    san = (["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-shared-libsan"] if sanitize else [])
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950"] + san + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -39,7 +39,7 @@ def load(path: Optional[str] = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("GDN_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build() or "
                            "python -m linear_attention_recurrence_chunked_amd.build" % p)

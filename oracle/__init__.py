@@ -39,28 +39,35 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _LIB = os.path.join(_HERE, "libgdn_oracle.so")
+_LIB_SAN = os.path.join(_HERE, "libgdn_oracle_san.so")     # AddressSanitizer + UBSan build
 _lib = None
 
 F32, BF16, F64 = 0, 1, 2
 
 
-def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (fp64, OpenMP).  Returns the library path."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the C oracle with gcc (fp64, OpenMP).  Returns the library path.  With
+    sanitize, a separate copy instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+    (loaded when GDN_ORACLE_LIB names it, in a process that preloads libasan)."""
+    lib = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        san = (["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                "-fno-omit-frame-pointer", "-g"] if sanitize else [])
+        cmd = (["gcc", "-O1" if sanitize else "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                "-ffp-contract=off"] + san + ["-o", tmp, _SRC, "-lm"])
         subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("GDN_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         lib.gdn_oracle_run.restype = ctypes.c_int
         lib.gdn_oracle_run.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
