@@ -46,7 +46,8 @@ struct LdsPrep {
     static constexpr int LDX = 20;                  // padded rows of a diagonal X block
     static constexpr int oT = kRecT, oG = kRecG;
     static constexpr int oBeta = kPrepRecordBytes;
-    static constexpr int oK = oBeta + 256;          // K rows (phases 1-2) ...
+    static constexpr int oE = oBeta + 256;          // 2^g and 2^-g of the tokens
+    static constexpr int oK = oE + 512;             // K rows (phases 1-2) ...
     static constexpr int oA = oK;                   // ... then A and the X blocks (phase 3)
     // the six strictly lower 16 x 16 blocks of A, block (i, m) at index i (i - 1) / 2 + m
     static constexpr int oX = oA + 6 * 16 * LDB * 4;
@@ -67,6 +68,8 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     __shared__ __align__(16) unsigned char smem[L::total];
     float *const sG = (float *)(smem + L::oG);
     float *const sBeta = (float *)(smem + L::oBeta);
+    float *const sE = (float *)(smem + L::oE);          // 2^g
+    float *const sIE = sE + kChunk;                      // 2^-g
     float *const sA = (float *)(smem + L::oA);
     float *const sX = (float *)(smem + L::oX);
     unsigned char *const bK = smem + L::oK;
@@ -160,6 +163,8 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
             x += dpp_f32<0x142, 0xa>(x);
             x += dpp_f32<0x143, 0xc>(x);
             sG[lane] = x;
+            sE[lane] = __builtin_amdgcn_exp2f(x);
+            sIE[lane] = __builtin_amdgcn_exp2f(-x);
         } else if (wave == 1) {
             sBeta[lane] = lane < nv ? pa : 0.f;
         }
@@ -190,16 +195,28 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
         }
     }
     // accG[p][r] = k_i . k_t for i = ib*16 + 4lg + r, t = tb*16 + ln.  Masked value: the A^T
-    // block (row i, column t).
+    // block (row i, column t).  Gamma_ti = 2^(g_t - g_i): as 2^g_t 2^-g_i while the chunk's
+    // total decay g_C stays at or above -60 (both factors then normal), else per element.
+    const bool factored = __builtin_amdgcn_readfirstlane((int)(sG[kChunk - 1] >= -60.f));
     auto masked = [&](int tb, int ib, f32x4 g_, f32x4 &av) {
         const int t = tb * 16 + ln;
-        const float gt = sG[t];
         const float bt_ = sBeta[t];
-        const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+        if (factored) {
+            const float cf = bt_ * sE[t];
+            const f32x4 ie = *(const f32x4 *)(sIE + ib * 16 + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = ib * 16 + 4 * lg + r;
-            av[r] = (i < t) ? bt_ * g_[r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int i = ib * 16 + 4 * lg + r;
+                av[r] = (i < t) ? (cf * ie[r]) * g_[r] : 0.f;
+            }
+        } else {
+            const float gt = sG[t];
+            const f32x4 gi = *(const f32x4 *)(sG + ib * 16 + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ib * 16 + 4 * lg + r;
+                av[r] = (i < t) ? bt_ * g_[r] * __builtin_amdgcn_exp2f(gt - gi[r]) : 0.f;
+            }
         }
     };
     f32x4 nT, a1, a2;
@@ -210,13 +227,23 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     f32x4 nC;
     {
         const int t = d0 + ln;
-        const float gt = sG[t];
-        const f32x4 gi = *(const f32x4 *)(sG + d0 + 4 * lg);
         const f32x4 bi = *(const f32x4 *)(sBeta + d0 + 4 * lg);
+        if (factored) {
+            const float iet = sIE[t];
+            const f32x4 ei = *(const f32x4 *)(sE + d0 + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = d0 + 4 * lg + r;
-            nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int i = d0 + 4 * lg + r;
+                nC[r] = (t < i) ? (bi[r] * (ei[r] * iet)) * accG[0][r] : 0.f;
+            }
+        } else {
+            const float gt = sG[t];
+            const f32x4 gi = *(const f32x4 *)(sG + d0 + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = d0 + 4 * lg + r;
+                nC[r] = (t < i) ? bi[r] * accG[0][r] * __builtin_amdgcn_exp2f(gi[r] - gt) : 0.f;
+            }
         }
     }
     // zero blocks above the diagonal of T': wave w clears blocks (w, j), j > w
