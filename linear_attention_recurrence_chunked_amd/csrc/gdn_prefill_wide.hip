@@ -549,8 +549,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             *(f32x4 *)ablk(tb0, ib0) = a1;
             if (np == 3) *(f32x4 *)ablk(3, ib1) = a2;
             *(f32x4 *)(sX + (d0 + ln) * L::LDX + 4 * lg) = xT;
-            // the rows of y staged in this step leave while the column waves reach their T' read
-            if (ypending >= 0) {
+            // the rows of y staged in this step leave: waves 2 and 3 (two Gram blocks each) here,
+            // while the column waves reach their T' read; waves 0 and 1 (three blocks, short
+            // work after the barrier below) right after that barrier
+            if (ypending >= 0 && pw >= 2) {
                 store_y(ypending);
                 ypending = -1;
             }
@@ -566,6 +568,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 M::put4((OP *)(bT + swz<OP, kChunk>(split_pos(d0 + ln), d0 + 4 * lg)), xT * bcol);
             }
             prep_barrier();
+            if (ypending >= 0) {
+                store_y(ypending);
+                ypending = -1;
+            }
             // The tile holds T' within each 32-token half, T'_AA = X_A diag(beta_A) and
             // T'_BB = X_B diag(beta_B), and -W with W = X_B A_BA in place of T'_BA (the column
             // waves form U_B = T'_BB R_B - W U_A).  Blocks of 16: X_10 = -X_11 A_10 X_00 and
@@ -613,7 +619,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
                 miscf[kMiscLamWin] += lam;
             }
         };
-        // Decay factors of chunk j (wave 3): the scan holds S = 2^ls Shat; ls starts at 0 and
+        // Decay factors of chunk j (wave 2, whose work after the prep barrier is the shortest):
+        // the scan holds S = 2^ls Shat; ls starts at 0 and
         // after each chunk becomes ls + g_C, or 0 when that would fall below -32 (the column
         // waves then rescale Shat by the same rule on the same g_C).
         //   F[t] = gamma_t 2^ls,  F[64 + t] = (gamma_C / gamma_t) / 2^ls',  F[128] = g_C,
@@ -644,7 +651,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
         if (nch > 0) {
             gates(0);
             make_t(0);
-            if (pw == 3) factors(0);
+            if (pw == 2) factors(0);
         }
         lds_barrier();                                  // #1: T'(0), factors(0)
         // the prep waves' work is one long dependent chain per step that every step waits for:
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void wide_scan_kernel(WideArgs w)
             if (j + 1 < nch) {
                 gates(j + 1);
                 make_t(j + 1);
-                if (pw == 3) factors(j + 1);
+                if (pw == 2) factors(j + 1);
             }
             if (ypending >= 0) {
                 store_y(ypending);
