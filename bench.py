@@ -642,8 +642,9 @@ def main():
         del dga, dgb, dgw, cstates
 
     # ------------------------------------------------------------------ sparse-attention indexer
-    # one sequence of 65,536 tokens (the largest supported), 4 query heads and a key head of
-    # 128, budget 512 blocks: normalise/rotate, block scores, top-K and expansion
+    # one sequence of 65,536 tokens, 4 query heads and a key head of 128, budget 512 blocks:
+    # normalise/rotate, then block scores and their selection in one streaming kernel; and
+    # one sequence of 2^20 tokens (the length the pages time the indexer at)
     qsa_obj = None
     if not args.no_qsa:
         nq = 65536
@@ -668,12 +669,43 @@ def main():
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
         qms = float(np.median(times))
-        nbq = nq // 4
-        pairs = sum(min((i + 1) // 4, nbq) for i in range(nq))       # causal (query, block)
+        del qws
+
+        def causal_pairs(n_):
+            # sum over queries i of min((i + 1) // 4, n_ // 4) visible blocks
+            nb_ = n_ // 4
+            full = 2 * nb_ * (nb_ - 1) + nb_                # queries 0 .. 4 nb_ - 1
+            return full + (n_ - 4 * nb_) * nb_
+
+        pairs = causal_pairs(nq)
         qflops = pairs * 4 * 128 * 2
-        # HBM bytes the method cannot avoid: inputs read, token lists written; the scores
-        # the kernels exchange (written once, read once) are the implementation's choice
+        # HBM bytes the method cannot avoid: inputs read, token lists written
         qbytes = nq * 5 * 128 * 2 + nq * (4 * 512 + 3) * 4
+        # the same at 2^20 tokens: one warm-up and two timed calls
+        nl = 1 << 20
+        t0 = time.time()
+        ql = wl.qsa_inputs(nl, "bf16", seed=3)
+        lq, lk = wl.to_torch(ql["q"], dev, "bf16"), wl.to_torch(ql["k"], dev, "bf16")
+        del ql
+        print("[bench] qsa 2^20 inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
+              flush=True)
+        lws = torch.empty(gdn.gdn_qsa_workspace_bytes(nl), dtype=torch.uint8, device=dev)
+        ltok = torch.empty((nl, 4 * 512 + 3), dtype=torch.int32, device=dev)
+        gdn.gdn_qsa_index(lq, lk, block_budget=512, want_blocks=False, workspace=lws, tokens=ltok)
+        lt = []
+        for _ in range(2):
+            cache_flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gdn.gdn_qsa_index(lq, lk, block_budget=512, want_blocks=False, workspace=lws,
+                              tokens=ltok)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lt.append(e0.elapsed_time(e1))
+        lms = float(np.median(lt))
+        lflops = causal_pairs(nl) * 4 * 128 * 2
+        del lq, lk, lws, ltok
+        torch.cuda.empty_cache()
         ctr_q = load_traffic("qsa_bf16_n65536_kb512", QSA_SOURCES)
         qsa_obj = {"workload": "one sequence of %d tokens, 4 query heads, d=128, blocks of 4, "
                                "budget 512 blocks" % nq,
@@ -681,11 +713,17 @@ def main():
                    "score_flops": qflops,
                    "score_TFLOPs": round(qflops / (qms * 1e-3) / 1e12, 2),
                    "frac_of_bf16_peak": round(qflops / (qms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                   "score_bytes_written_and_read": 2 * pairs * 4,
                    "algorithmic_bytes": qbytes,
                    "traffic": None if ctr_q is None else ctr_q["bytes_per_launch"],
-                   "kernels": "qsa_prep_kernel + qsa_score_kernel + qsa_topk_kernel"}
-        del iq, ik, qws
+                   "workspace_bytes": gdn.gdn_qsa_workspace_bytes(nq),
+                   "kernels": "qsa_prep_kernel + qsa_select_kernel<16>",
+                   "tokens_2p20": {"n": nl, "ms_median": round(lms, 3),
+                                   "ms_all": [round(x, 3) for x in lt],
+                                   "score_flops": lflops,
+                                   "score_TFLOPs": round(lflops / (lms * 1e-3) / 1e12, 2),
+                                   "frac_of_bf16_peak": round(lflops / (lms * 1e-3) / 1e12 /
+                                                              PEAK_BF16_TFLOPS, 4)}}
+        del iq, ik
 
     # ------------------------------------------------------------------ CPU baseline
     cpu = None

@@ -244,13 +244,14 @@ gdn_status gdn_channel_gated(const void *q, const void *k, const void *v, const 
  *   blocks     [n, block_budget] int32 or NULL: selected blocks, ascending, -1 padded
  *   tokens     [n, 4 block_budget + 3] int32 or NULL: the selected tokens, ascending (the
  *              blocks' tokens, then the tail), -1 padded.  At least one output is required.
- *   workspace  gdn_qsa_workspace_bytes(n) bytes (holds the n x n/4 fp32 scores)
- * n <= 131072 and block_budget <= 2^24 (GDN_ERR_UNSUPPORTED beyond); n <= 0, block_budget
+ *   workspace  gdn_qsa_workspace_bytes(n) bytes: the normalised, rotated queries and block
+ *              keys in bf16 (about 1 KiB per token; no score matrix is stored)
+ * n <= 2^20; block_budget <= 2048, or any budget up to 2^24 that is at least n/4 (every row
+ * then takes all its complete blocks): GDN_ERR_UNSUPPORTED beyond.  n <= 0, block_budget
  * <= 0, a null q, k or workspace, no output, misalignment or an output overlapping an input
  * or another output: GDN_ERR_INVALID_ARGUMENT; a short workspace: GDN_ERR_WORKSPACE_TOO_SMALL.
- * The notes' budget is block_budget = 512 (2048
- * tokens).  The scores use bf16 products of the normalised, rotated vectors with fp32
- * accumulation.
+ * The notes' budget is block_budget = 512 (2048 tokens).  The scores use bf16 products of the
+ * normalised, rotated vectors with fp32 accumulation; the selection is exact on those scores.
  */
 size_t gdn_qsa_workspace_bytes(int64_t n);
 gdn_status gdn_qsa_index(const void *q, const void *k, int64_t n, int32_t dtype,

@@ -94,6 +94,7 @@ struct QsaProblem {
 };
 size_t qsa_workspace_bytes(long long n);
 long long qsa_max_tokens();
+bool qsa_budget_supported(long long n, int block_budget);
 hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream);
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *alpha,

@@ -11,25 +11,19 @@
 // PRoPE rotates dims (m, m + 32), m < 32, by pos * 10000^(-2m/64); dims 64..127 pass.
 // RMSNorm(x) = x / sqrt(mean(x^2) + 1e-6), no scale.
 //
-// Three launches:
-//   qsa_prep_kernel   one wave per query row (token, head) or per key block: normalise,
-//                     rotate (angles and their sines in fp64: positions reach 10^5 radians),
-//                     store bf16.
-//   qsa_score_kernel  16 queries per workgroup against all their visible blocks on 16x16x32
-//                     bf16 MFMAs, the queries' fragments held in registers and the block
-//                     keys streamed from L2 one 16-block tile ahead: the four heads of a
-//                     query are four consecutive accumulator rows, i.e. the four values one
-//                     lane holds, so the ReLU head-sum needs no exchange.
-//   qsa_topk_kernel   one workgroup per query: the row's scores in LDS (16-byte loads, eight
-//                     in flight); a 2,048-bin histogram of a digit linear in the score up to
-//                     the row maximum (scores of one magnitude spread over many bins) and a
-//                     scan over it find the bin holding the K_B-th largest score; the scores in
-//                     that bin (a few dozen, typically) are ranked pairwise to find it exactly,
-//                     or, in a crowded bin, by a radix select on 11, 11 and 10 bits of their
-//                     patterns (scores are sums of ReLUs, so their bit patterns order like the
-//                     values).  Ties at the threshold are taken in index order; each wave
-//                     places its range's selected blocks, ascending, by a packed prefix sum of
-//                     (greater, equal) counts, with their tokens, then the tail and padding.
+// Two launches, no score matrix (workspace O(n): the prepared queries and block keys):
+//   qsa_prep_kernel    one wave per query row (token, head) or per key block: normalise,
+//                      rotate (angles and their sines in fp64: positions reach 10^6 radians),
+//                      store bf16.
+//   qsa_select_kernel  QN queries per workgroup against all their visible blocks on 16x16x32
+//                      bf16 MFMAs, the queries' fragments held in registers and the block keys
+//                      streamed from L2 one step ahead: the four heads of a query are four
+//                      consecutive accumulator rows, i.e. the four values one lane holds, so
+//                      the ReLU head-sum needs no exchange.  Each score is compared with its
+//                      query's running threshold as it is formed; the few that pass go to the
+//                      query's candidate list in LDS, in block order, and a list that fills up
+//                      is trimmed to the K_B best (an exact selection over at most a few
+//                      thousand entries), which raises the threshold.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -47,8 +41,6 @@ struct QsaArgs {
     int kb;                     // block budget
     uint16_t *qr;               // [n, 4, 128] bf16
     uint16_t *kbk;              // [nb, 128] bf16
-    float *scores;              // [n, ld]
-    long long ld;               // score row stride: nb rounded up to 4 (16-byte rows)
     int32_t *blocks;            // [n, kb] or null
     int32_t *tokens;            // [n, kb * 4 + 3] or null
 };
@@ -104,114 +96,6 @@ __global__ __launch_bounds__(256) void qsa_prep_kernel(QsaArgs a)
     }
 }
 
-// 16 queries (64 rows of qr, token-major, head-minor) against every block visible to the
-// last of them, in tiles of 16 blocks; wave w takes tiles w, w + 4, ...  The queries'
-// MFMA fragments stay in registers for the whole row; the block keys (at most 4 MB, resident
-// in L2) stream in one tile ahead.  Query tiles run last-first: the longest rows start first.
-__global__ __launch_bounds__(256) void qsa_score_kernel(QsaArgs a)
-{
-    const long long nb = a.n / kQR;
-    const long long qtiles = (a.n + 15) / 16;
-    const long long i0 = (qtiles - 1 - (long long)blockIdx.x) * 16;
-    const long long ilast = i0 + 15 < a.n - 1 ? i0 + 15 : a.n - 1;
-    const long long nvis = (ilast + 1) / kQR < nb ? (ilast + 1) / kQR : nb;
-    const int ntiles = (int)((nvis + 15) / 16);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    // per wave: its 16 x 16 score tile, rows 16-byte aligned, to turn four 4-byte stores per
-    // lane into one 16-byte store
-    __shared__ __align__(16) float sT[4][16 * 20];
-    if (wave >= ntiles) return;               // no barriers below
-    // A fragments: tile t holds rows 16 t .. 16 t + 15 (tokens i0 + 4 t .. i0 + 4 t + 3)
-    bf16x8 fa[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const long long qrow = i0 * kQH + 16 * t + r;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (qrow < a.n * kQH) x = *(const u32x4 *)(a.qr + qrow * kQD + 32 * kk + 8 * g);
-            fa[t][kk] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
-    u32x4 fb[4], fn[4];
-    auto load_b = [&](int tile, u32x4 (&f)[4]) {
-        const long long b = (long long)tile * 16 + r;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            f[kk] = u32x4{0u, 0u, 0u, 0u};
-            if (b < nb) f[kk] = *(const u32x4 *)(a.kbk + b * kQD + 32 * kk + 8 * g);
-        }
-    };
-    load_b(wave, fb);
-#pragma unroll 1
-    for (int tile = wave; tile < ntiles; tile += 4) {
-        if (tile + 4 < ntiles) load_b(tile + 4, fn);
-        f32x4 acc[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 b8 = __builtin_bit_cast(bf16x8, fb[kk]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t][kk], b8, acc[t], 0, 0, 0);
-        }
-        // tile t, lane (r, g): rows 16 t + 4 g + h (token i0 + 4 t + g, head h), block r.
-        // + 0: a sum of four -0 becomes +0 (bit patterns must order like values)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            sT[wave][(4 * t + g) * 20 + r] = fmaxf(acc[t][0], 0.f) + fmaxf(acc[t][1], 0.f) +
-                                             fmaxf(acc[t][2], 0.f) + fmaxf(acc[t][3], 0.f) + 0.f;
-        __builtin_amdgcn_wave_barrier();
-        {
-            // lane l: token i0 + l / 4, blocks 16 tile + 4 (l % 4) .. + 3 (a row's padding
-            // to a multiple of 4 blocks absorbs the last group's overhang)
-            const f32x4 v = *(const f32x4 *)&sT[wave][(lane >> 2) * 20 + 4 * (lane & 3)];
-            const long long i = i0 + (lane >> 2);
-            const long long b = (long long)tile * 16 + 4 * (lane & 3);
-            if (i < a.n && b < nb) __builtin_nontemporal_store(v, (f32x4 *)(a.scores + i * a.ld + b));
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) fb[kk] = fn[kk];
-    }
-}
-
-constexpr int kTK = 1024;       // threads of a top-k workgroup
-constexpr int kTW = kTK / kWave;
-
-// Exclusive prefix sum of one value per thread over a workgroup of kTK threads.
-__device__ __forceinline__ int block_excl_scan(int x, int *tmp)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int v = x;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const int o = __shfl_up(v, m, kWave);
-        if (lane >= m) v += o;
-    }
-    if (lane == 63) tmp[wave] = v;
-    __syncthreads();
-    int off = 0;
-    for (int w = 0; w < wave; ++w) off += tmp[w];   // wave-uniform
-    __syncthreads();
-    return off + v - x;
-}
-
-// blocks per row held in LDS: 16,384 (64 KiB, two workgroups per CU) up to 65,536 tokens,
-// 32,768 (128 KiB, one per CU) up to 131,072
-constexpr int kMaxRowSmall = 16384;
-constexpr int kMaxRow = 32768;
-
-// First radix digit of a score x >= lo: (x - lo) scaled linearly onto 2,048 bins.  Monotone
-// in x (a rounded subtraction and multiply, then a floor), so ordering by (digit, bit
-// pattern) orders like the scores, and scores of one magnitude spread over many bins.
-__device__ __forceinline__ uint32_t lin_digit(uint32_t x, float lo, float s)
-{
-    const float v = (__uint_as_float(x) - lo) * s;
-    return v < 2047.f ? (uint32_t)v : 2047u;
-}
-
 // number of lanes below this one whose bit is set in m
 __device__ __forceinline__ int lanes_below(uint64_t m)
 {
@@ -219,304 +103,588 @@ __device__ __forceinline__ int lanes_below(uint64_t m)
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-constexpr int kCand = 256;      // a threshold bin this small is resolved by pairwise ranks
-
-// One workgroup per query, longest rows first.
-//
-// The K_B-th largest score tau is at least the smallest of the maxima of any K_B disjoint
-// groups of the row (those maxima are K_B scores at least that large), so scores below that
-// bound take no part in the search.  A block is taken when its score is above tau, or equal to
-// it and not after b_last, the index of the last equal score that still fits the budget.
-template <int MAXROW>
-__global__ __launch_bounds__(kTK) void qsa_topk_kernel(QsaArgs a)
+// The 16-lane group g's bits of a ballot (lanes 16 g .. 16 g + 15).
+__device__ __forceinline__ uint32_t group_bits(uint64_t m, int g)
 {
-    __shared__ __align__(16) uint32_t row[MAXROW];
-    __shared__ int hist[2048];
-    __shared__ uint32_t cx[kCand];
-    __shared__ int cb[kCand];
-    __shared__ int tmp[kTW];
-    __shared__ int wcount[kTW];
-    __shared__ float wmax[kTW], wmin[kTW];
-    __shared__ uint32_t sh_prefix, sh_need, sh_c1;
-    __shared__ int sh_cnt, sh_fill, sh_blast;
-    const long long i = a.n - 1 - (long long)blockIdx.x;
-    const long long nb = a.n / kQR;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nvalid = (int)((i + 1) / kQR < nb ? (i + 1) / kQR : nb);
-    const int KB = a.kb;
-    const bool all = nvalid <= KB;            // uniform over the workgroup
-    const int n4 = (nvalid + 3) >> 2;
-    const u32x4 *row4 = (const u32x4 *)row;
+    return (uint32_t)(m >> (16 * g)) & 0xffffu;
+}
 
-    uint32_t tau = 0;         // the bit pattern of the K_B-th largest score (when !all)
-    int b_last = -1;          // the last taken block among those scoring exactly tau
-    if (!all) {
-        // the row's visible scores into LDS: 16-byte loads, all of a thread's in flight
-        const u32x4 *src = (const u32x4 *)(a.scores + i * a.ld);
-        {
-            u32x4 v[MAXROW / 4 / kTK];
+// DPP lane moves within rows of 16 (row_shr:n shifts in zeros; the four butterfly patterns
+// give every lane its row's reduction)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op)
+{
+    x = op(x, dpp_u32<0xb1>(x));            // quad_perm [1, 0, 3, 2]
+    x = op(x, dpp_u32<0x4e>(x));            // quad_perm [2, 3, 0, 1]
+    x = op(x, dpp_u32<0x141>(x));           // row_half_mirror
+    x = op(x, dpp_u32<0x140>(x));           // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+
+// Exclusive prefix sum over the wave's lanes (lane order), and the wave total.
+__device__ __forceinline__ int wave_excl_scan(int x, int &total)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t v = (uint32_t)x;
+    v += dpp_u32<0x111>(v);                 // row_shr:1
+    v += dpp_u32<0x112>(v);                 // row_shr:2
+    v += dpp_u32<0x114>(v);                 // row_shr:4
+    v += dpp_u32<0x118>(v);                 // row_shr:8
+    const int t0 = __builtin_amdgcn_readlane((int)v, 15);
+    const int t1 = __builtin_amdgcn_readlane((int)v, 31);
+    const int t2 = __builtin_amdgcn_readlane((int)v, 47);
+    const int t3 = __builtin_amdgcn_readlane((int)v, 63);
+    const int row = lane >> 4;
+    const int off = row == 0 ? 0 : row == 1 ? t0 : row == 2 ? t0 + t1 : t0 + t1 + t2;
+    total = t0 + t1 + t2 + t3;
+    return off + (int)v - x;
+}
+
+// The k-th largest (1 <= k <= number of flagged keys) of the keys that src flags, and how
+// many keys equal to it are among the k largest (need_eq).  src.load(gi, key, use) gives
+// group gi of the keys, 16 per lane (src.groups() groups).  The key range [lo, hi] starts at
+// the flagged keys' minimum and maximum; each round counts the keys of the range in 256 bins
+// of (key - lo) >> sh and narrows the range to the bin holding the rank still wanted; a bin of
+// at most 64 keys is ranked pairwise, a range of one value ends the search.  scr: 256 ints,
+// cand: 64 words of this wave's LDS.
+template <typename Src>
+__device__ __forceinline__ uint32_t kth_largest(const Src &src, int k, int *scr, uint32_t *cand,
+                                                int &need_eq)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t key[16];
+    bool use[16];
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int gi = 0; gi < src.groups(); ++gi) {
+        src.load(gi, key, use);
 #pragma unroll
-            for (int u = 0; u < MAXROW / 4 / kTK; ++u) {
-                const int c = u * kTK + tid;
-                v[u] = u32x4{0u, 0u, 0u, 0u};
-                if (c < n4) v[u] = src[c];
+        for (int u = 0; u < 16; ++u)
+            if (use[u]) {
+                lo = min(lo, key[u]);
+                hi = max(hi, key[u]);
             }
-#pragma unroll
-            for (int u = 0; u < MAXROW / 4 / kTK; ++u) {
-                const int c = u * kTK + tid;
-                if (c < n4) *(u32x4 *)(row + 4 * c) = v[u];
-            }
-        }
-        hist[2 * tid] = 0;
-        hist[2 * tid + 1] = 0;
-        if (tid == 0) {
-            sh_prefix = 0;
-            sh_need = (uint32_t)KB;
-            sh_fill = 0;
-        }
-        __syncthreads();
-        // group g = the blocks b = g (mod K_B), halved between threads 2g' and 2g' + 1 of a
-        // pair: the row maximum and the smallest group maximum
-        float mx = 0.f, mn = 3.0e38f;
-        for (int g0 = 0; g0 < KB; g0 += kTK / 2) {
-            const int g = g0 + (tid >> 1);
-            float m = 0.f;
-            if (g < KB)
-                for (int b = g + (tid & 1) * KB; b < nvalid; b += 2 * KB)
-                    m = fmaxf(m, __uint_as_float(row[b]));
-            m = fmaxf(m, __shfl_xor(m, 1, kWave));
-            if (g < KB) {
-                mx = fmaxf(mx, m);
-                mn = fminf(mn, m);
-            }
-        }
-#pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) {
-            mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
-            mn = fminf(mn, __shfl_xor(mn, m, kWave));
-        }
-        if (lane == 0) {
-            wmax[wave] = mx;
-            wmin[wave] = mn;
-        }
-        __syncthreads();
-        float lo = wmin[0];
-        mx = wmax[0];
-#pragma unroll
-        for (int w = 1; w < kTW; ++w) {
-            mx = fmaxf(mx, wmax[w]);
-            lo = fminf(lo, wmin[w]);
-        }
-        const uint32_t lo_bits = __float_as_uint(lo);
-        const float s = mx > lo ? fminf(2047.f / (mx - lo), 1e30f) : 0.f;
-        // first digit over the scores >= lo
-#pragma unroll 2
-        for (int c = tid; c < n4; c += kTK) {
-            const u32x4 x = row4[c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * c + e < nvalid && x[e] >= lo_bits)
-                    atomicAdd(&hist[lin_digit(x[e], lo, s)], 1);
-        }
-        __syncthreads();
-        // thread t looks at digits 2047 - 2t - j (descending); gt = how many values have a
-        // larger digit; the digit where the rank falls is unique
-        {
-            int c[2], tot = 0;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                c[j] = hist[2047 - 2 * tid - j];
-                tot += c[j];
-            }
-            const uint32_t need = sh_need;
-            int gt = block_excl_scan(tot, tmp);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if ((uint32_t)gt < need && (uint32_t)(gt + c[j]) >= need) {
-                    sh_c1 = (uint32_t)(2047 - 2 * tid - j);
-                    sh_need = need - (uint32_t)gt;
-                    sh_cnt = c[j];
-                }
-                gt += c[j];
-            }
-            __syncthreads();
-        }
-        const uint32_t c1 = sh_c1, need = sh_need;
-        const int cnt = sh_cnt;
-        if (cnt <= kCand) {
-            // gather the bin's scores; the one whose rank among them holds `need` (the first
-            // in index order among equals) is tau; then the need_eq-th equal in index order
-#pragma unroll 2
-            for (int c = tid; c < n4; c += kTK) {
-                const u32x4 x = row4[c];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * c + e < nvalid && x[e] >= lo_bits && lin_digit(x[e], lo, s) == c1) {
-                        const int slot = atomicAdd(&sh_fill, 1);
-                        cx[slot] = x[e];
-                        cb[slot] = 4 * c + e;
-                    }
-            }
-            __syncthreads();
-            if (tid < cnt) {
-                const uint32_t xj = cx[tid];
-                const int bj = cb[tid];
-                int above = 0, same = 0, same_first = 1;
-                for (int k = 0; k < cnt; ++k) {
-                    const uint32_t xk = cx[k];
-                    above += xk > xj;
-                    same += xk == xj;
-                    if (xk == xj && cb[k] < bj) same_first = 0;
-                }
-                if (same_first && (uint32_t)above < need && need <= (uint32_t)(above + same)) {
-                    sh_prefix = xj;
-                    sh_need = need - (uint32_t)above;
-                }
-            }
-            __syncthreads();
-            tau = sh_prefix;
-            const int need_eq = (int)sh_need;
-            if (tid < cnt && cx[tid] == tau) {
-                const int bj = cb[tid];
-                int before = 0;
-                for (int k = 0; k < cnt; ++k) before += cx[k] == tau && cb[k] < bj;
-                if (before == need_eq - 1) sh_blast = bj;
-            }
-            __syncthreads();
-        } else {
-            // a crowded bin (many equal scores): bits 31..21, 20..10, 9..0 of its scores
+    }
+    lo = wave_reduce_u32(lo, [](uint32_t a, uint32_t b) { return min(a, b); });
+    hi = wave_reduce_u32(hi, [](uint32_t a, uint32_t b) { return max(a, b); });
+    int need = k;
 #pragma unroll 1
-            for (int pass = 0; pass < 3; ++pass) {
-                const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-                const int bits = pass == 2 ? 10 : 11;
-                const uint32_t dmask = (1u << bits) - 1;
-                const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (shift + bits));
-                hist[2 * tid] = 0;
-                hist[2 * tid + 1] = 0;
-                __syncthreads();
-                const uint32_t pre = sh_prefix;
-                for (int b = tid; b < nvalid; b += kTK) {
-                    const uint32_t x = row[b];
-                    if (x >= lo_bits && lin_digit(x, lo, s) == c1 && (x & mask) == pre)
-                        atomicAdd(&hist[(x >> shift) & dmask], 1);
-                }
-                __syncthreads();
-                int c[2], tot = 0;
+    for (int it = 0; it < 8; ++it) {
+        if (lo == hi) break;
+        const uint32_t span = hi - lo;
+        const int sh = max(0, 32 - (int)__builtin_clz(span) - 8);   // span >> sh <= 255
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    c[j] = hist[2047 - 2 * tid - j];
-                    tot += c[j];
-                }
-                const uint32_t nd = sh_need;
-                int gt = block_excl_scan(tot, tmp);
+        for (int v = 0; v < 4; ++v) scr[4 * lane + v] = 0;
+        __builtin_amdgcn_wave_barrier();
+        for (int gi = 0; gi < src.groups(); ++gi) {
+            src.load(gi, key, use);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if ((uint32_t)gt < nd && (uint32_t)(gt + c[j]) >= nd) {
-                        sh_prefix = pre | ((uint32_t)(2047 - 2 * tid - j) << shift);
-                        sh_need = nd - (uint32_t)gt;
-                    }
-                    gt += c[j];
-                }
-                __syncthreads();
-            }
-            tau = sh_prefix;
-            const int need_eq = (int)sh_need;
-            // the need_eq-th score equal to tau in index order: contiguous ranges per thread
-            const int chunk = (nvalid + kTK - 1) / kTK;
-            const int b0 = tid * chunk, b1 = b0 + chunk < nvalid ? b0 + chunk : nvalid;
-            int eq = 0;
-            for (int b = b0; b < b1; ++b) eq += row[b] == tau;
-            int before = block_excl_scan(eq, tmp);
-            if (before < need_eq && before + eq >= need_eq)
-                for (int b = b0; b < b1; ++b)
-                    if (row[b] == tau && ++before == need_eq) sh_blast = b;
-            __syncthreads();
+            for (int u = 0; u < 16; ++u)
+                if (use[u] && key[u] >= lo && key[u] <= hi) atomicAdd(&scr[(key[u] - lo) >> sh], 1);
         }
-        b_last = sh_blast;
+        __builtin_amdgcn_wave_barrier();
+        // lane L holds bins 255 - 4 L - v (descending); excl = keys in higher bins
+        int hv[4], tot = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            hv[v] = scr[255 - 4 * lane - v];
+            tot += hv[v];
+        }
+        int all_;
+        int excl = wave_excl_scan(tot, all_);
+        int fbin = -1, fabove = 0, fcnt = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (excl < need && excl + hv[v] >= need) {
+                fbin = 255 - 4 * lane - v;
+                fabove = excl;
+                fcnt = hv[v];
+            }
+            excl += hv[v];
+        }
+        const uint64_t fm = __builtin_amdgcn_ballot_w64(fbin >= 0);
+        const int fsrc = (int)__builtin_ctzll(fm);
+        const int bin = __builtin_amdgcn_readlane(fbin, fsrc);
+        const int bcnt = __builtin_amdgcn_readlane(fcnt, fsrc);
+        need -= __builtin_amdgcn_readlane(fabove, fsrc);
+        const uint32_t nlo = lo + ((uint32_t)bin << sh);
+        const unsigned long long top = (unsigned long long)nlo + ((1ull << sh) - 1ull);
+        hi = top < (unsigned long long)hi ? (uint32_t)top : hi;
+        lo = nlo;
+        __builtin_amdgcn_wave_barrier();
+        if (bcnt <= 64) {
+            // the bin's keys into cand, then their pairwise ranks
+            int mine = 0;
+            for (int gi = 0; gi < src.groups(); ++gi) {
+                src.load(gi, key, use);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) mine += use[u] && key[u] >= lo && key[u] <= hi;
+            }
+            int tot2;
+            int off = wave_excl_scan(mine, tot2);
+            for (int gi = 0; gi < src.groups(); ++gi) {
+                src.load(gi, key, use);
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (use[u] && key[u] >= lo && key[u] <= hi) cand[off++] = key[u];
+            }
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t xl = lane < bcnt ? cand[lane] : 0u;
+            int gt = 0, eq = 0;
+            for (int j = 0; j < bcnt; ++j) {
+                const uint32_t xj = (uint32_t)__builtin_amdgcn_readlane((int)xl, j);
+                gt += xj > xl;
+                eq += xj == xl;
+            }
+            const bool hit = lane < bcnt && gt < need && need <= gt + eq;
+            const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
+            const int hs = (int)__builtin_ctzll(hm);
+            need_eq = need - __builtin_amdgcn_readlane(gt, hs);
+            const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)xl, hs);
+            __builtin_amdgcn_wave_barrier();
+            return tau;
+        }
     }
+    need_eq = need;
+    return lo;
+}
 
-    // selection in index order: wave w takes a contiguous range of the row (a multiple of
-    // 256 blocks), lane l the four blocks 4 l .. 4 l + 3 of each 256-block step; ballots of
-    // the four slots place every taken block
-    const int per = ((nvalid + kTW * 256 - 1) / (kTW * 256)) * 256;
-    const int lo_b = wave * per, hi_b = lo_b + per < nvalid ? lo_b + per : nvalid;
-    auto taken = [&](uint32_t x, int b) { return x > tau || (x == tau && b <= b_last); };
-    if (!all) {
-        int count = 0;
-#pragma unroll 2
-        for (int b0 = lo_b; b0 < hi_b; b0 += 256) {
-            const int b = b0 + 4 * lane;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (b < hi_b) x = *(const u32x4 *)(row + b);
+// Entry j of a list, 16 per lane per group of 1,024: idx = 1024 gi + 64 u + lane.
+struct ListKeys {          // the score patterns of entries 0 .. c - 1
+    const u32x2 *e;
+    int c;
+    __device__ int groups() const { return (c + 1023) >> 10; }
+    __device__ void load(int gi, uint32_t (&key)[16], bool (&use)[16]) const
+    {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                count += __popcll(__builtin_amdgcn_ballot_w64(b + u < hi_b && taken(x[u], b + u)));
+        for (int u = 0; u < 16; ++u) {
+            const int idx = 1024 * gi + 64 * u + lane;
+            use[u] = idx < c;
+            key[u] = use[u] ? e[idx].x : 0u;
         }
-        if (lane == 0) wcount[wave] = count;
     }
-    __syncthreads();
-    int pos = lo_b;
-    if (!all) {
-        pos = 0;
-        for (int w = 0; w < wave; ++w) pos += wcount[w];
-    }
-    const int W = KB * kQR + kQR - 1;
-    int32_t *blk = a.blocks ? a.blocks + i * KB : nullptr;
-    int32_t *tok = a.tokens ? a.tokens + i * W : nullptr;
-#pragma unroll 2
-    for (int b0 = lo_b; b0 < hi_b; b0 += 256) {
-        const int b = b0 + 4 * lane;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (!all && b < hi_b) x = *(const u32x4 *)(row + b);
-        bool t[4];
-        uint64_t m[4];
-        int p = pos;
+};
+struct TieBlocks {         // the complemented blocks of the entries scoring exactly tau
+    const u32x2 *e;
+    int c;
+    uint32_t tau;
+    __device__ int groups() const { return (c + 1023) >> 10; }
+    __device__ void load(int gi, uint32_t (&key)[16], bool (&use)[16]) const
+    {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            t[u] = b + u < hi_b && (all || taken(x[u], b + u));
-            m[u] = __builtin_amdgcn_ballot_w64(t[u]);
-            p += lanes_below(m[u]);
+        for (int u = 0; u < 16; ++u) {
+            const int idx = 1024 * gi + 64 * u + lane;
+            const u32x2 v = idx < c ? e[idx] : u32x2{0u, 0u};
+            use[u] = idx < c && v.x == tau;
+            key[u] = ~v.y;
         }
+    }
+};
+
+// One wave trims a query's candidate list e[0 .. c) (entries {score bit pattern, block}, in
+// no particular order) to its K best in the order (score descending, block ascending) and
+// returns the bit pattern tau of the K-th best score.  Scores are sums of ReLUs (never -0), so
+// their bit patterns order like the values.  Of the entries scoring exactly tau, the need_eq
+// with the lowest blocks are kept (a second selection, on the complemented block index, when
+// more than need_eq tie).  The kept entries are packed group by group: a group's entries land
+// below the next group's, which is read before anything is written over it.
+__device__ __forceinline__ uint32_t trim_list(u32x2 *e, int c, int K, int *scr, uint32_t *cand)
+{
+    const int lane = threadIdx.x & 63;
+    int need_eq;
+    const uint32_t tau = kth_largest(ListKeys{e, c}, K, scr, cand, need_eq);
+    const int ngroups = (c + 1023) >> 10;
+    int neq = 0;
+    for (int gi = 0; gi < ngroups; ++gi)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t[u]) {
-                if (blk) blk[p] = b + u;
-                if (tok) {
+        for (int u = 0; u < 16; ++u) {
+            const int idx = 1024 * gi + 64 * u + lane;
+            neq += idx < c && e[idx].x == tau;
+        }
+    int tot_eq;
+    wave_excl_scan(neq, tot_eq);
+    uint32_t bmax = 0xffffffffu;          // tau entries kept: block <= bmax
+    if (tot_eq > need_eq) {
+        int dummy;
+        bmax = ~kth_largest(TieBlocks{e, c, tau}, need_eq, scr, cand, dummy);
+    }
+    int out = 0;
+    for (int gi = 0; gi < ngroups; ++gi) {
+        u32x2 v[16];
+        bool keep[16];
+        int mine = 0;
 #pragma unroll
-                    for (int v = 0; v < kQR; ++v) tok[kQR * p + v] = kQR * (b + u) + v;
-                }
-                ++p;
+        for (int u = 0; u < 16; ++u) {
+            const int idx = 1024 * gi + 64 * u + lane;
+            v[u] = idx < c ? e[idx] : u32x2{0u, 0u};
+            keep[u] = idx < c && (v[u].x > tau || (v[u].x == tau && v[u].y <= bmax));
+            mine += keep[u];
+        }
+        int tot;
+        int off = out + wave_excl_scan(mine, tot);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (keep[u]) e[off++] = v[u];
+        __builtin_amdgcn_wave_barrier();
+        out += tot;
+    }
+    return tau;
+}
+
+// The blocks of a query's final list (at most K, R per lane, any order) in ascending order
+// into out[0 .. c): the rank of a block is the number of listed blocks below it, counted on a
+// bitmap of the visible blocks (bm: NW words, 32 NW blocks at a time) with per-word prefix
+// counts (pre: NW words).
+template <int R, int NW>
+__device__ __forceinline__ void sort_blocks(const u32x2 *e, int c, int nvis, uint32_t *out,
+                                            uint32_t *bm, uint32_t *pre)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t blk[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) blk[u] = 64 * u + lane < c ? e[64 * u + lane].y : 0xffffffffu;
+    __builtin_amdgcn_wave_barrier();
+    int base = 0;                               // listed blocks below the current window
+    for (int w0 = 0; w0 < nvis; w0 += 32 * NW) {
+        for (int i = lane; i < NW; i += 64) bm[i] = 0u;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const uint32_t d = blk[u] - (uint32_t)w0;
+            if (d < 32u * NW) atomicOr(&bm[d >> 5], 1u << (d & 31));
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane L owns words NW/64 L .. NW/64 (L + 1) - 1
+        constexpr int PW = NW / 64;
+        int s = 0;
+        uint32_t wv[PW];
+#pragma unroll
+        for (int v = 0; v < PW; ++v) {
+            wv[v] = bm[PW * lane + v];
+            s += __builtin_popcount(wv[v]);
+        }
+        int tot;
+        int run = base + wave_excl_scan(s, tot);
+#pragma unroll
+        for (int v = 0; v < PW; ++v) {
+            pre[PW * lane + v] = (uint32_t)run;
+            run += __builtin_popcount(wv[v]);
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const uint32_t d = blk[u] - (uint32_t)w0;
+            if (d < 32u * NW) {
+                const uint32_t word = bm[d >> 5];
+                out[pre[d >> 5] + __builtin_popcount(word & ((1u << (d & 31)) - 1u))] = blk[u];
             }
-            pos += __popcll(m[u]);
         }
+        __builtin_amdgcn_wave_barrier();
+        base += tot;
     }
-    // padding, and the tail of the incomplete block after the selected tokens
-    const int nsel = all ? nvalid : KB;
-    if (blk)
-        for (int p = nsel + tid; p < KB; p += kTK) blk[p] = -1;
-    if (tok) {
-        const long long tail0 = ((i + 1) / kQR) * kQR;
-        const int ntail = (int)(i + 1 - tail0);
-        for (int p = kQR * nsel + tid; p < W; p += kTK) {
-            const int u = p - kQR * nsel;
-            tok[p] = u < ntail ? (int32_t)(tail0 + u) : -1;
+}
+
+constexpr int kSelWaves = 8;                    // waves of a selection workgroup
+constexpr int kStepBlocks = 256;                // blocks per step: 8 waves x 2 tiles of 16
+constexpr int kSelTiles = kStepBlocks / 16 / kSelWaves;
+constexpr int kSelEntries = 16384;              // candidate entries of a workgroup (128 KiB)
+constexpr int kSelMaxBudget = kSelEntries / 4 / 2;   // 2,048 blocks with 4 queries
+constexpr int kBins = 1024;                     // score histogram: bins of 1/2 over [0, 512)
+
+// Scores are sums over 4 heads of ReLU(<q, kb>) with both vectors of norm at most sqrt(128)
+// (RMS-normalised, then rotated), so they lie in [0, 512] (a little above at most, by the
+// bf16 rounding of the operands): bin = floor(2 score), the last bin open-ended.  Monotone
+// in the score.
+__device__ __forceinline__ int score_bin(float v)
+{
+    return min(kBins - 1, (int)(v * 2.0f));
+}
+
+// Scores and selection without a score matrix.  A workgroup takes QN queries (QN / 4 tiles of
+// 16 MFMA rows: 4 tokens x 4 heads, the queries' fragments held in registers) and streams the
+// blocks visible to its last query twice, in steps of 256: wave w scores blocks 64 w ..
+// 64 w + 63 of each step (the next step's keys in flight meanwhile).
+//   Pass 1 counts each query's scores in a histogram of kBins bins (LDS atomics); the bin
+//   holding the K-th best score, b*, follows from a scan down from the top.
+//   Pass 2 scores again and lists, per query, the blocks whose score falls in b* or above:
+//   the K best and the rest of b*'s bin, in LDS (CAP = 16,384 / QN entries, one LDS atomic
+//   per query and tile reserving their places).  Where a histogram says that a list could
+//   outgrow CAP (a crowded bin), the pass also syncs after every step and trims a list that
+//   could overflow in the next one (more than CAP - 256 entries) to its K best (trim_list);
+//   blocks are then taken only when they also beat the K-th best so far, tau (a block of a
+//   later step that only ties it ranks below the K entries that hold it).
+// Finally every list longer than K is trimmed to its K best, sorted by block and written out.
+// Query tiles run last-first: the longest rows start first.
+template <int QN>
+__global__ __launch_bounds__(64 * kSelWaves) void qsa_select_kernel(QsaArgs a)
+{
+    constexpr int AT = QN / 4;
+    constexpr int CAP = kSelEntries / QN;
+    constexpr int RK = CAP / 128;                // final entries per lane (K <= CAP / 2)
+    static_assert(QN * kBins * 4 <= kSelEntries * 8, "histograms share the lists' LDS");
+    __shared__ __align__(16) u32x2 list[QN * CAP];
+    __shared__ int cnt_s[QN];                    // list lengths (append counters)
+    __shared__ int bmin_s[QN];                   // b*: the lowest bin a block may come from
+    __shared__ float thr_s[QN];
+    __shared__ int crowded_s;
+    __shared__ int scr[kSelWaves][256];
+    __shared__ uint32_t cand[kSelWaves][64];
+    int *hist = (int *)list;                     // pass 1: [QN][kBins]
+    const long long nb = a.n / kQR;
+    const long long qtiles = (a.n + QN - 1) / QN;
+    const long long i0 = (qtiles - 1 - (long long)blockIdx.x) * QN;
+    const long long ilast = i0 + QN - 1 < a.n - 1 ? i0 + QN - 1 : a.n - 1;
+    const int nvis = (int)((ilast + 1) / kQR < nb ? (ilast + 1) / kQR : nb);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int KB = a.kb;
+    const bool all = nvis <= KB;                 // every query takes all its blocks
+    if (!all) {
+        for (int i = threadIdx.x; i < QN * kBins; i += 64 * kSelWaves) hist[i] = 0;
+        if (threadIdx.x < QN) {
+            cnt_s[threadIdx.x] = 0;
+            thr_s[threadIdx.x] = -1.f;
+        }
+        if (threadIdx.x == 0) crowded_s = 0;
+        int nv[AT];
+#pragma unroll
+        for (int t = 0; t < AT; ++t) {
+            const long long i = i0 + 4 * t + g;
+            nv[t] = i < a.n ? (int)((i + 1) / kQR < nb ? (i + 1) / kQR : nb) : 0;
+        }
+        bf16x8 fa[AT][4];
+#pragma unroll
+        for (int t = 0; t < AT; ++t) {
+            const long long qrow = i0 * kQH + 16 * t + r;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (qrow < a.n * kQH) x = *(const u32x4 *)(a.qr + qrow * kQD + 32 * kk + 8 * g);
+                fa[t][kk] = __builtin_bit_cast(bf16x8, x);
+            }
+        }
+        // blocks past the last visible one read that block's key (no lane takes them).  The
+        // keys of a step arrive in one of two register sets while the other feeds the MFMAs:
+        // a load never targets registers that an issued MFMA may still have to read.
+        u32x4 fbA[kSelTiles][4], fbB[kSelTiles][4];
+        auto load_b = [&](int step, u32x4 (&fb)[kSelTiles][4]) {
+#pragma unroll
+            for (int st = 0; st < kSelTiles; ++st) {
+                const int b = min(step * kStepBlocks + (wave * kSelTiles + st) * 16 + r, nvis - 1);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    fb[st][kk] = *(const u32x4 *)(a.kbk + (long long)b * kQD + 32 * kk + 8 * g);
+            }
+        };
+        const int nsteps = (nvis + kStepBlocks - 1) / kStepBlocks;
+        // the step's scores: visit(st, t, blk, v) for lane (r, g) of tile t: query 4 t + g
+        // (heads in acc[st][t][0..3]), block blk.  v is exact up to the sign of a zero.
+        auto scores = [&](int s, u32x4 (&fb)[kSelTiles][4], u32x4 (&fn)[kSelTiles][4],
+                          auto &&visit) {
+            if (s + 1 < nsteps) load_b(s + 1, fn);
+            f32x4 acc[kSelTiles][AT];
+#pragma unroll
+            for (int st = 0; st < kSelTiles; ++st)
+#pragma unroll
+                for (int t = 0; t < AT; ++t) acc[st][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int st = 0; st < kSelTiles; ++st) {
+                    const bf16x8 b8 = __builtin_bit_cast(bf16x8, fb[st][kk]);
+#pragma unroll
+                    for (int t = 0; t < AT; ++t)
+                        acc[st][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t][kk], b8, acc[st][t], 0, 0, 0);
+                }
+#pragma unroll
+            for (int st = 0; st < kSelTiles; ++st) {
+                const int blk = s * kStepBlocks + (wave * kSelTiles + st) * 16 + r;
+#pragma unroll
+                for (int t = 0; t < AT; ++t) {
+                    const f32x4 c4 = acc[st][t];
+                    const float v = __builtin_amdgcn_fmed3f(c4[0], 0.f, 3.0e38f) +
+                                    __builtin_amdgcn_fmed3f(c4[1], 0.f, 3.0e38f) +
+                                    __builtin_amdgcn_fmed3f(c4[2], 0.f, 3.0e38f) +
+                                    __builtin_amdgcn_fmed3f(c4[3], 0.f, 3.0e38f);
+                    visit(st, t, blk, v);
+                }
+            }
+        };
+        // ---- pass 1: histograms
+        load_b(0, fbA);
+        __syncthreads();
+        auto count = [&](int, int t, int blk, float v) {
+            if (blk < nv[t]) atomicAdd(&hist[(4 * t + g) * kBins + score_bin(v)], 1);
+        };
+#pragma unroll 1
+        for (int s = 0; s < nsteps; s += 2) {
+            scores(s, fbA, fbB, count);
+            if (s + 1 < nsteps) scores(s + 1, fbB, fbA, count);
+        }
+        load_b(0, fbA);
+        __syncthreads();
+        // b* per query (its owner wave): lane L holds bins kBins - 1 - 16 L - v, descending
+        for (int q = wave; q < QN; q += kSelWaves) {
+            int hv[16], tot = 0;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                hv[v] = hist[q * kBins + kBins - 1 - 16 * lane - v];
+                tot += hv[v];
+            }
+            int all_;
+            int excl = wave_excl_scan(tot, all_);
+            int fb_ = -1, fabove = 0, fcnt = 0;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if (excl < KB && excl + hv[v] >= KB) {
+                    fb_ = kBins - 1 - 16 * lane - v;
+                    fabove = excl;
+                    fcnt = hv[v];
+                }
+                excl += hv[v];
+            }
+            const uint64_t fm = __builtin_amdgcn_ballot_w64(fb_ >= 0);
+            int bstar = 0, pred = all_;                 // fewer than K blocks: all of them
+            if (fm != 0) {
+                const int fs = (int)__builtin_ctzll(fm);
+                bstar = __builtin_amdgcn_readlane(fb_, fs);
+                pred = __builtin_amdgcn_readlane(fabove, fs) + __builtin_amdgcn_readlane(fcnt, fs);
+            }
+            if (lane == 0) {
+                bmin_s[q] = bstar;
+                if (pred > CAP - kStepBlocks) crowded_s = 1;
+            }
+        }
+        __syncthreads();
+        int bmin[AT];
+        float thr[AT];
+#pragma unroll
+        for (int t = 0; t < AT; ++t) {
+            bmin[t] = bmin_s[4 * t + g];
+            thr[t] = -1.f;
+        }
+        const bool crowded = crowded_s != 0;
+        __syncthreads();                          // the histograms are read: lists may start
+        // ---- pass 2: lists
+        auto collect = [&](int, int t, int blk, float v) {
+            const bool take = blk < nv[t] && score_bin(v) >= bmin[t] && v > thr[t];
+            const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+            if (m == 0) return;                       // the common case: one scalar branch
+            const uint32_t bits = group_bits(m, g);
+            if (bits != 0u) {
+                // the group's lowest taking lane reserves the places
+                const int lead = __builtin_ctz(bits);
+                int base = 0;
+                if (r == lead) base = atomicAdd(&cnt_s[4 * t + g], __builtin_popcount(bits));
+                base = __shfl(base, 16 * g + lead, kWave);
+                // + 0: a zero score's bit pattern is +0 (patterns must order like values)
+                if (take)
+                    list[(4 * t + g) * CAP + base + __builtin_popcount(bits & ((1u << r) - 1u))] =
+                        u32x2{__float_as_uint(v + 0.f), (uint32_t)blk};
+            }
+        };
+        auto sync_trim = [&]() {
+            __syncthreads();
+            // lane q < QN holds list q's length, the same in every wave: no wave appends or
+            // trims before all have read them
+            const int cl = lane < QN ? cnt_s[lane] : 0;
+            const uint64_t over = __builtin_amdgcn_ballot_w64(cl > CAP - kStepBlocks);
+            __syncthreads();
+            if (over != 0) {
+                for (int q = wave; q < QN; q += kSelWaves) {
+                    const int cq = __builtin_amdgcn_readlane(cl, q);
+                    if (cq > CAP - kStepBlocks) {
+                        const uint32_t tau = trim_list(list + q * CAP, cq, KB, scr[wave], cand[wave]);
+                        if (lane == 0) {
+                            thr_s[q] = __uint_as_float(tau);
+                            cnt_s[q] = KB;
+                        }
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int t = 0; t < AT; ++t) thr[t] = thr_s[4 * t + g];
+            }
+        };
+#pragma unroll 1
+        for (int s = 0; s < nsteps; s += 2) {
+            scores(s, fbA, fbB, collect);
+            if (crowded) sync_trim();
+            if (s + 1 < nsteps) {
+                scores(s + 1, fbB, fbA, collect);
+                if (crowded) sync_trim();
+            }
+        }
+        __syncthreads();
+    }
+    // output: query q by wave q % 4; the selected blocks ascending with their tokens, then the
+    // tail of the incomplete block and -1 padding
+    const int W = KB * kQR + kQR - 1;
+    for (int q = wave; q < QN; q += kSelWaves) {
+        const long long i = i0 + q;
+        if (i >= a.n) break;
+        const int nvq = (int)((i + 1) / kQR < nb ? (i + 1) / kQR : nb);
+        int nsel = nvq;
+        uint32_t *sorted = (uint32_t *)(list + q * CAP);        // first CAP / 2 words
+        if (!all) {
+            const int cq = __builtin_amdgcn_readfirstlane(cnt_s[q]);
+            if (cq > KB) trim_list(list + q * CAP, cq, KB, scr[wave], cand[wave]);
+            nsel = cq < KB ? cq : KB;
+            // the bitmap and prefix counts take the second and third quarter words of the
+            // list, the sorted blocks the first (the entries are in registers meanwhile)
+            sort_blocks<RK, CAP / 2>(list + q * CAP, nsel, nvq, sorted, sorted + CAP / 2,
+                                     sorted + CAP);
+        }
+        if (a.blocks) {
+            int32_t *blk = a.blocks + i * KB;
+            for (int p = lane; p < KB; p += kWave)
+                blk[p] = p < nsel ? (all ? p : (int32_t)sorted[p]) : -1;
+        }
+        if (a.tokens) {
+            int32_t *tok = a.tokens + i * W;
+            const long long tail0 = ((i + 1) / kQR) * kQR;
+            const int ntail = (int)(i + 1 - tail0);
+            for (int p = lane; p < W; p += kWave) {
+                const int u = p >> 2;
+                int32_t v;
+                if (u < nsel) {
+                    v = kQR * (all ? u : (int32_t)sorted[u]) + (p & 3);
+                } else {
+                    const int o = p - kQR * nsel;
+                    v = o < ntail ? (int32_t)(tail0 + o) : -1;
+                }
+                tok[p] = v;
+            }
         }
     }
 }
 
 }  // namespace
 
-static long long score_ld(long long nb) { return ((nb > 0 ? nb : 1) + 3) & ~3LL; }
-
 size_t qsa_workspace_bytes(long long n)
 {
     const long long nb = n / kQR;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return al((size_t)n * kQH * kQD * 2) + al((size_t)(nb > 0 ? nb : 1) * kQD * 2) +
-           al((size_t)n * score_ld(nb) * 4);
+    return al((size_t)n * kQH * kQD * 2) + al((size_t)(nb > 0 ? nb : 1) * kQD * 2);
 }
 
-long long qsa_max_tokens() { return (long long)kMaxRow * kQR; }
+long long qsa_max_tokens() { return 1LL << 20; }
+
+bool qsa_budget_supported(long long n, int block_budget)
+{
+    return block_budget <= kSelMaxBudget || n / kQR <= block_budget;
+}
 
 hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
 {
@@ -530,9 +698,6 @@ hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
     unsigned char *ws = (unsigned char *)workspace;
     a.qr = (uint16_t *)ws;
     a.kbk = (uint16_t *)(ws + al((size_t)p.n * kQH * kQD * 2));
-    a.scores = (float *)(ws + al((size_t)p.n * kQH * kQD * 2) +
-                         al((size_t)(nb > 0 ? nb : 1) * kQD * 2));
-    a.ld = score_ld(nb);
     a.blocks = p.blocks;
     a.tokens = p.tokens;
     const long long waves = p.n * kQH + nb;
@@ -541,16 +706,18 @@ hipError_t launch_qsa(const QsaProblem &p, void *workspace, hipStream_t stream)
         hipLaunchKernelGGL(qsa_prep_kernel<uint16_t>, dim3(prep_blocks), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(qsa_prep_kernel<float>, dim3(prep_blocks), dim3(256), 0, stream, a);
-    if (nb > 0) {
-        hipLaunchKernelGGL(qsa_score_kernel, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0,
-                           stream, a);
-    }
-    if (nb <= kMaxRowSmall)
-        hipLaunchKernelGGL(qsa_topk_kernel<kMaxRowSmall>, dim3((unsigned)p.n), dim3(kTK), 0,
-                           stream, a);
+    // lists of 2 x budget entries at least: 16 queries per workgroup up to a budget of 512,
+    // 8 up to 1,024, 4 up to 2,048 (a larger budget only where it covers every row)
+    const int kb = p.block_budget;
+    if (kb <= kSelEntries / 16 / 2 || nb <= kb)
+        hipLaunchKernelGGL(qsa_select_kernel<16>, dim3((unsigned)((p.n + 15) / 16)),
+                           dim3(64 * kSelWaves), 0, stream, a);
+    else if (kb <= kSelEntries / 8 / 2)
+        hipLaunchKernelGGL(qsa_select_kernel<8>, dim3((unsigned)((p.n + 7) / 8)),
+                           dim3(64 * kSelWaves), 0, stream, a);
     else
-        hipLaunchKernelGGL(qsa_topk_kernel<kMaxRow>, dim3((unsigned)p.n), dim3(kTK), 0, stream,
-                           a);
+        hipLaunchKernelGGL(qsa_select_kernel<4>, dim3((unsigned)((p.n + 3) / 4)),
+                           dim3(64 * kSelWaves), 0, stream, a);
     return hipGetLastError();
 }
 

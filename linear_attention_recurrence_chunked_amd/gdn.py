@@ -351,16 +351,18 @@ def gdn_qsa_workspace_bytes(n: int) -> int:
 
 
 def gdn_qsa_index(q, k, block_budget: int = 512, want_blocks: bool = True,
-                  want_tokens: bool = True, workspace=None, stream=None):
+                  want_tokens: bool = True, workspace=None, stream=None, blocks=None,
+                  tokens=None):
     """Sparse-attention block indexer for one sequence: q [n, 4, 128], k [n, 128]
     (bf16 or fp32).  Returns (blocks [n, budget] int32 or None, tokens [n, 4 budget + 3]
-    int32 or None), both ascending and -1 padded."""
+    int32 or None), both ascending and -1 padded; given output tensors are written in
+    place."""
     import torch
     n = q.shape[0]
-    blocks = torch.empty((n, block_budget), dtype=torch.int32, device=q.device) \
-        if want_blocks else None
-    tokens = torch.empty((n, 4 * block_budget + 3), dtype=torch.int32, device=q.device) \
-        if want_tokens else None
+    if blocks is None and want_blocks:
+        blocks = torch.empty((n, block_budget), dtype=torch.int32, device=q.device)
+    if tokens is None and want_tokens:
+        tokens = torch.empty((n, 4 * block_budget + 3), dtype=torch.int32, device=q.device)
     if workspace is None:
         workspace = torch.empty(max(gdn_qsa_workspace_bytes(n), 16), dtype=torch.uint8,
                                 device=q.device)

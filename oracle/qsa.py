@@ -76,6 +76,22 @@ def prepare(q, k, r=R):
     return qr, kb
 
 
+def prepare_rows(q_rows, rows, k, r=R):
+    """prepare() for a subset of the queries: q_rows [m, H, D] are the projected queries at
+    token positions rows [m]; returns (qr [m, H, D], kb [n // r, D]), the same values that
+    prepare(q, k) gives at those rows (used where the whole query tensor is too large to
+    normalise in fp64)."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    qr = rope(rmsnorm(q_rows), rows[:, None] * np.ones(q_rows.shape[1]))
+    nb = k.shape[0] // r
+    if nb == 0:
+        return qr, np.zeros((0, k.shape[1]))
+    pooled = k[:nb * r].reshape(nb, r, -1).mean(axis=1)
+    return qr, rope(rmsnorm(pooled), np.arange(nb) * r)
+
+
 def scores(qr, kb, r=R):
     """I [n, nb]: sum over heads of ReLU(<q^h_i, kb_b>); -inf where block b is not complete
     before query i (p_b + r - 1 > i)."""

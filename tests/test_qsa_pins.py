@@ -127,6 +127,18 @@ def test_indexer_end_to_end_small():
         assert tokens[i][tokens[i] >= 0][-1] == i or nvalid == 0 or (i + 1) % 4 == 0
 
 
+def test_prepare_rows_matches_prepare():
+    """The row-subset preparation gives prepare()'s values at those rows (positions taken from
+    the row indices, block keys over the whole sequence)."""
+    rng = np.random.default_rng(6)
+    q, k = _rand(rng, 203)
+    qr, kb = qsa.prepare(q, k)
+    rows = np.array([0, 3, 4, 77, 202])
+    qr_s, kb_s = qsa.prepare_rows(q[rows], rows, k)
+    assert np.array_equal(qr_s, qr[rows])
+    assert np.array_equal(kb_s, kb)
+
+
 # ---- mutants ------------------------------------------------------------------------------
 
 class _Mut:
