@@ -474,9 +474,11 @@ __global__ __launch_bounds__(64 * kSelWaves) void qsa_select_kernel(QsaArgs a)
                 fa[t][kk] = __builtin_bit_cast(bf16x8, x);
             }
         }
-        // blocks past the last visible one read that block's key (no lane takes them).  The
-        // keys of a step arrive in one of two register sets while the other feeds the MFMAs:
-        // a load never targets registers that an issued MFMA may still have to read.
+        // blocks past the last visible one read that block's key (no lane takes them), so the
+        // next step's keys are fetched unconditionally, also after the last step: no branch
+        // around the loads, whose wait counts then stay exact.  The keys of a step arrive in
+        // one of two register sets while the other feeds the MFMAs: a load never targets
+        // registers that an issued MFMA may still have to read.
         u32x4 fbA[kSelTiles][4], fbB[kSelTiles][4];
         auto load_b = [&](int step, u32x4 (&fb)[kSelTiles][4]) {
 #pragma unroll
@@ -492,7 +494,9 @@ __global__ __launch_bounds__(64 * kSelWaves) void qsa_select_kernel(QsaArgs a)
         // (heads in acc[st][t][0..3]), block blk.  v is exact up to the sign of a zero.
         auto scores = [&](int s, u32x4 (&fb)[kSelTiles][4], u32x4 (&fn)[kSelTiles][4],
                           auto &&visit) {
-            if (s + 1 < nsteps) load_b(s + 1, fn);
+            load_b(s + 1, fn);
+            // the loads stay ahead of this step's MFMAs (into the other register set)
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[kSelTiles][AT];
 #pragma unroll
             for (int st = 0; st < kSelTiles; ++st)
@@ -527,11 +531,13 @@ __global__ __launch_bounds__(64 * kSelWaves) void qsa_select_kernel(QsaArgs a)
         auto count = [&](int, int t, int blk, float v) {
             if (blk < nv[t]) atomicAdd(&hist[(4 * t + g) * kBins + score_bin(v)], 1);
         };
+        int s1 = 0;
 #pragma unroll 1
-        for (int s = 0; s < nsteps; s += 2) {
-            scores(s, fbA, fbB, count);
-            if (s + 1 < nsteps) scores(s + 1, fbB, fbA, count);
+        for (; s1 + 1 < nsteps; s1 += 2) {
+            scores(s1, fbA, fbB, count);
+            scores(s1 + 1, fbB, fbA, count);
         }
+        if (s1 < nsteps) scores(s1, fbA, fbB, count);
         load_b(0, fbA);
         __syncthreads();
         // b* per query (its owner wave): lane L holds bins kBins - 1 - 16 L - v, descending
@@ -617,14 +623,17 @@ __global__ __launch_bounds__(64 * kSelWaves) void qsa_select_kernel(QsaArgs a)
                 for (int t = 0; t < AT; ++t) thr[t] = thr_s[4 * t + g];
             }
         };
+        int s2 = 0;
 #pragma unroll 1
-        for (int s = 0; s < nsteps; s += 2) {
-            scores(s, fbA, fbB, collect);
+        for (; s2 + 1 < nsteps; s2 += 2) {
+            scores(s2, fbA, fbB, collect);
             if (crowded) sync_trim();
-            if (s + 1 < nsteps) {
-                scores(s + 1, fbB, fbA, collect);
-                if (crowded) sync_trim();
-            }
+            scores(s2 + 1, fbB, fbA, collect);
+            if (crowded) sync_trim();
+        }
+        if (s2 < nsteps) {
+            scores(s2, fbA, fbB, collect);
+            if (crowded) sync_trim();
         }
         __syncthreads();
     }
