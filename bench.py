@@ -597,7 +597,7 @@ def main():
         cflops = 7 * d * d * T * H          # decay, retrieval, write and read-out per token-head
         ctf = cflops / (cms * 1e-3) / 1e12
         del ca, cb, cw, cy, cs
-        ns = 64
+        ns = min(64, nsteps)         # decode steps of the channel-gated variant
         dg = wl.channel_gates({"q": np.empty((ns * B, 1, 1)), "H": Hd, "dk": dh, "dv": dh},
                               seed=3)
         dga, dgb, dgw = (torch.from_numpy(dg[n]).to(dev).view(ns, B, Hd, dh)

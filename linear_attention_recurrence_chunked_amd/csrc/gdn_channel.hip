@@ -102,6 +102,16 @@ struct Tok {
     float v, b, w;
 };
 
+// The job of this workgroup: (sequence, head) unit, then column tile.  Workgroups are dealt
+// to the eight XCDs in turn (block b to XCD b % 8); when the grid divides evenly, the column
+// tiles of a unit get block indices of one residue mod 8, so the k, q and decay rows that they
+// all read are fetched into one L2 instead of four.
+__device__ __forceinline__ int tile_job(int tiles)
+{
+    const int b = blockIdx.x, G = gridDim.x;
+    return G % (8 * tiles) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
+}
+
 template <int DK, typename T>
 __global__ __launch_bounds__(256) void channel_step_kernel(ChanArgs p)
 {
@@ -110,9 +120,10 @@ __global__ __launch_bounds__(256) void channel_step_kernel(ChanArgs p)
     const int g = lane >> 3, j = lane & 7;
     const int H = p.H, dv = p.dv;
     const int tiles = dv / kWgCols;
-    const int tile = blockIdx.x % tiles;
-    const int h = (blockIdx.x / tiles) % H;
-    const int n = blockIdx.x / (tiles * H);
+    const int job = tile_job(tiles);
+    const int tile = job % tiles;
+    const int h = (job / tiles) % H;
+    const int n = job / (tiles * H);
     const int col = tile * kWgCols + wave * kCols + j;
     long long t0;
     int len;
@@ -218,9 +229,10 @@ __global__ __launch_bounds__(512) void channel_gated_kernel(ChanArgs p)
     const int g = lane & 15, j = lane >> 4;
     const int H = p.H, dv = p.dv;
     const int tiles = dv / kWgCols;
-    const int tile = blockIdx.x % tiles;
-    const int h = (blockIdx.x / tiles) % H;
-    const int n = blockIdx.x / (tiles * H);
+    const int job = tile_job(tiles);
+    const int tile = job % tiles;
+    const int h = (job / tiles) % H;
+    const int n = job / (tiles * H);
     const int col0 = tile * kWgCols;
     const int cl = wave * 4 + j;                          // this lane's column in the tile
     long long t0;
