@@ -139,22 +139,34 @@ __device__ __forceinline__ void put_t2(uint16_t *Dh, uint16_t *Dl, int ld, int m
     *(bf16x4 *)(Dl + o) = __builtin_convertvector(v - __builtin_convertvector(h, f32x4), bf16x4);
 }
 
-// Sum over the 16 lanes that share lane / 16, and over the whole wave.
+// Sum over the 16 lanes that share lane / 16 (DPP moves within the row: neighbour and pair
+// swaps, then half-row and row mirrors, which meet lanes already holding equal sums), and
+// over the whole wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
 __device__ __forceinline__ float sum16(float x)
 {
-    x += __shfl_xor(x, 1, kWave);
-    x += __shfl_xor(x, 2, kWave);
-    x += __shfl_xor(x, 4, kWave);
-    x += __shfl_xor(x, 8, kWave);
+    x += dpp_f<0xb1>(x);                    // quad_perm [1, 0, 3, 2]: lane ^ 1
+    x += dpp_f<0x4e>(x);                    // quad_perm [2, 3, 0, 1]: lane ^ 2
+    x += dpp_f<0x141>(x);                   // row_half_mirror
+    x += dpp_f<0x140>(x);                   // row_mirror
     return x;
 }
-__device__ __forceinline__ float sum64(float x)
+// x summed over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48), in every lane: the
+// row swaps of gfx950 pair rows 0-1 and 2-3, then the two halves (VALU, no LDS round trip)
+__device__ __forceinline__ float sum_rows(float x)
 {
-    x = sum16(x);
-    x += __shfl_xor(x, 16, kWave);
-    x += __shfl_xor(x, 32, kWave);
-    return x;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+__device__ __forceinline__ float sum64(float x) { return sum_rows(sum16(x)); }
 
 struct BwdArgs {
     const uint16_t *q, *k, *v, *dy;
@@ -361,8 +373,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
             }
         }
         float s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        s += __shfl_xor(s, 16, kWave);
-        s += __shfl_xor(s, 32, kWave);
+        s = sum_rows(s);
         const float val = bet[t] * ((t == j ? 1.f : 0.f) - s);
         if (p == (t & 3)) {
             col[t >> 2] = val;
@@ -1015,8 +1026,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             cs += w;
         }
         put_t(sDPt, L64, m0, n0, dpg);
-        cs += __shfl_xor(cs, 16, kWave);
-        cs += __shfl_xor(cs, 32, kWave);
+        cs = sum_rows(cs);
         if (lane < 16) pC[(m0 / 16) * C + n0 + r] = cs;
     }
     __syncthreads();
