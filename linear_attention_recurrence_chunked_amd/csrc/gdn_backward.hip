@@ -155,18 +155,7 @@ __device__ __forceinline__ float sum16(float x)
     x += dpp_f<0x140>(x);                   // row_mirror
     return x;
 }
-// x summed over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48), in every lane: the
-// row swaps of gfx950 pair rows 0-1 and 2-3, then the two halves (VALU, no LDS round trip)
-__device__ __forceinline__ float sum_rows(float x)
-{
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
-                                                    false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float sum64(float x) { return sum_rows(sum16(x)); }
+__device__ __forceinline__ float sum64(float x) { return row_sum4(sum16(x)); }
 
 struct BwdArgs {
     const uint16_t *q, *k, *v, *dy;
@@ -373,7 +362,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
             }
         }
         float s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        s = sum_rows(s);
+        s = row_sum4(s);
         const float val = bet[t] * ((t == j ? 1.f : 0.f) - s);
         if (p == (t & 3)) {
             col[t >> 2] = val;
@@ -1026,7 +1015,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             cs += w;
         }
         put_t(sDPt, L64, m0, n0, dpg);
-        cs = sum_rows(cs);
+        cs = row_sum4(cs);
         if (lane < 16) pC[(m0 / 16) * C + n0 + r] = cs;
     }
     __syncthreads();

@@ -87,13 +87,13 @@ __device__ __forceinline__ void load_row(const uint16_t *p, float *o)
     }
 }
 
-// Sum over the eight row groups (lanes j, j + 8, ..., j + 56).
+// Sum over the eight row groups (lanes j, j + 8, ..., j + 56): the partner 8 lanes away
+// within a row by a DPP rotation of the row by 8 (lane i meets lane (i + 8) mod 16 = i ^ 8),
+// then across the four rows.
 __device__ __forceinline__ float sum_groups(float x)
 {
-    x += __shfl_xor(x, 8, kWave);
-    x += __shfl_xor(x, 16, kWave);
-    x += __shfl_xor(x, 32, kWave);
-    return x;
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, true));
+    return row_sum4(x);
 }
 
 template <int R>
@@ -429,14 +429,11 @@ __global__ __launch_bounds__(256) void channel_decode_kernel(ChanArgs p)
         ps += s[i] * qa[i];
     }
 #pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            pr[c] += __shfl_xor(pr[c], m, kWave);
-            ps[c] += __shfl_xor(ps[c], m, kWave);
-        }
-        pkq += __shfl_xor(pkq, m, kWave);
+    for (int c = 0; c < 4; ++c) {
+        pr[c] = row_sum4(pr[c]);
+        ps[c] = row_sum4(ps[c]);
     }
+    pkq = row_sum4(pkq);
     __shared__ f32x4 red_r[4][16], red_s[4][16];
     __shared__ float red_kq[4];
     if (lane < 16) {

@@ -58,4 +58,17 @@ __device__ __forceinline__ void store4(uint16_t *p, f32x4 x) {
 
 __device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
 
+// x summed over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows), in every lane: the
+// gfx950 row swaps pair rows 0-1 and 2-3, then the two halves (VALU, no LDS round trip).  The
+// same sum, bit for bit, as adding the xor-16 and then the xor-32 partner.
+__device__ __forceinline__ float row_sum4(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace gdn
