@@ -231,6 +231,24 @@ __device__ __forceinline__ u32x4 piece(const uint16_t *src, long long t0, int nv
     if (t >= nv) return u32x4{0u, 0u, 0u, 0u};
     return *(const u32x4 *)(src + ((t0 + t) * H + h) * (long long)W + col0 + 8 * p);
 }
+// The same piece loaded from a row clamped into the chunk (nv >= 1), without a branch: for
+// batches of loads that all go out before any is used; piece_keep() zeroes it past nv when
+// it is stored.
+template <int W, int NC>
+__device__ __forceinline__ u32x4 piece_clamped(const uint16_t *src, long long t0, int nv, int H,
+                                               int h, int col0, int i)
+{
+    constexpr int P = NC / 8;
+    const int t = i / P, p = i % P;
+    const int tc = t < nv ? t : nv - 1;
+    return *(const u32x4 *)(src + ((t0 + tc) * H + h) * (long long)W + col0 + 8 * p);
+}
+template <int NC>
+__device__ __forceinline__ u32x4 piece_keep(u32x4 x, int nv, int i)
+{
+    return i / (NC / 8) < nv ? x : u32x4{0u, 0u, 0u, 0u};
+}
+
 template <int NC>
 __device__ __forceinline__ void put_piece(uint16_t *dst, int ld, int i, u32x4 x)
 {
@@ -306,15 +324,31 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
 
-    for (int i = tid; i < C * DK / 8; i += 256) {
-        put_piece<DK>(sK, LK, i, piece<DK, DK>(a.k, t0, nv, H, h, 0, i));
-        put_piece<DK>(sQ, LK, i, piece<DK, DK>(a.q, t0, nv, H, h, 0, i));
+    // the gates, then every piece of K and Q, all in flight at once
+    float la = 0.f, bta = 0.f;
+    if (tid < C && tid < nv) {
+        la = a.alpha[(t0 + tid) * H + h];
+        bta = a.beta[(t0 + tid) * H + h];
+    }
+    {
+        constexpr int NP = C * DK / 8 / 256;
+        u32x4 kx[NP], qx[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            kx[u] = piece_clamped<DK, DK>(a.k, t0, nv, H, h, 0, tid + 256 * u);
+            qx[u] = piece_clamped<DK, DK>(a.q, t0, nv, H, h, 0, tid + 256 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            put_piece<DK>(sK, LK, tid + 256 * u, piece_keep<DK>(kx[u], nv, tid + 256 * u));
+            put_piece<DK>(sQ, LK, tid + 256 * u, piece_keep<DK>(qx[u], nv, tid + 256 * u));
+        }
     }
     if (tid < C) {
-        float la = 0.f, b = 0.f;
+        float b = 0.f;
         if (tid < nv) {
-            la = fmaxf(__logf(a.alpha[(t0 + tid) * H + h]), kLnAlphaFloor);
-            b = a.beta[(t0 + tid) * H + h];
+            la = fmaxf(__logf(la), kLnAlphaFloor);
+            b = bta;
         }
 #pragma unroll
         for (int s = 1; s < kWave; s <<= 1) {
@@ -798,10 +832,21 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
 
-    for (int i = tid; i < KP; i += 512)
-        put_piece<DK>(sK, LK, i, piece<DK, DK>(a.k, t0, nv, H, h, 0, i));
-    put_rec_piece(sT, tid, rec_piece(rec, kRT, tid));
-    put_rec_piece(sP, tid, rec_piece(rec, kRP, tid));
+    {
+        // the K pieces and the record's T' and P^T pieces in flight together
+        constexpr int NP = (KP + 511) / 512;
+        u32x4 kx[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            kx[u] = piece_clamped<DK, DK>(a.k, t0, nv, H, h, 0, (tid + 512 * u) % KP);
+        const u32x4 tx = rec_piece(rec, kRT, tid), px = rec_piece(rec, kRP, tid);
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            if (tid + 512 * u < KP)
+                put_piece<DK>(sK, LK, tid + 512 * u, piece_keep<DK>(kx[u], nv, tid + 512 * u));
+        put_rec_piece(sT, tid, tx);
+        put_rec_piece(sP, tid, px);
+    }
     if (tid < C) {
         const float gt = ((const float *)(rec + kRG))[tid];
         const float gl = ((const float *)(rec + kRG))[C - 1];
@@ -946,8 +991,17 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     }
     __syncthreads();   // the pass region now takes Q, (dP (.) Gamma)^T, dLG + dLG^T, partials
 
-    for (int i = tid; i < KP; i += 512)
-        put_piece<DK>(sQ, LK, i, piece<DK, DK>(a.q, t0, nv, H, h, 0, i));
+    {
+        constexpr int NP = (KP + 511) / 512;
+        u32x4 qx[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            qx[u] = piece_clamped<DK, DK>(a.q, t0, nv, H, h, 0, (tid + 512 * u) % KP);
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            if (tid + 512 * u < KP)
+                put_piece<DK>(sQ, LK, tid + 512 * u, piece_keep<DK>(qx[u], nv, tid + 512 * u));
+    }
     // Row sums are written per source tile and added in a fixed order afterwards, so every
     // output is bitwise repeatable.
     //   pG[kt][t]  row dot of the c x d_k accumulators, column tile kt
