@@ -380,8 +380,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 
     // forward substitution, T'[t] = beta_t (e_t - sum_{i<t} L[t][i] T'[i]): wave w owns
     // columns 16w .. 16w+15; lane (j = 16w + r, p = lane / 16) keeps rows 4m + p of its
-    // column in registers.
+    // column in registers.  Terms with i >= t vanish on their own (L[t][i] = 0 there and
+    // rows not yet solved are still 0), and the column reaches LDS only after the loop, so
+    // no store stands between one step's reads of L and the next.
+    // beta_t comes from lane t by a lane read and the new row enters its lane by a 0 / 1
+    // weight (the slot it lands in is still 0), so the steps are one straight run of code
+    // and the reads of L for later steps can be issued early.
     const int j = 16 * wave + r, p = lane >> 4;
+    const int bet_lane = __float_as_int(bet[lane]);
+    float own[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) own[u] = p == u ? 1.f : 0.f;
     float col[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) col[m] = 0.f;
@@ -389,20 +398,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     for (int t = 0; t < C; ++t) {
         float ps[4] = {0.f, 0.f, 0.f, 0.f};    // four partial sums: a short dependency chain
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            if (4 * m < t) {
-                const int i = 4 * m + p;
-                if (i < t) ps[m & 3] += sL[t * LF + i] * col[m];
-            }
-        }
+        for (int m = 0; m < 16; ++m)
+            if (4 * m < t) ps[m & 3] += sL[t * LF + 4 * m + p] * col[m];
         float s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         s = row_sum4(s);
-        const float val = bet[t] * ((t == j ? 1.f : 0.f) - s);
-        if (p == (t & 3)) {
-            col[t >> 2] = val;
-            sT[t * LF + j] = val;
-        }
+        const float bt = __int_as_float(__builtin_amdgcn_readlane(bet_lane, t));
+        const float val = bt * ((t == j ? 1.f : 0.f) - s);
+        col[t >> 2] += own[t & 3] * val;
     }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) sT[(4 * m + p) * LF + j] = col[m];
     __syncthreads();
     // T' and P^T to the record in 16-byte pieces
     for (int i = tid; i < C * C / 8; i += 256)
