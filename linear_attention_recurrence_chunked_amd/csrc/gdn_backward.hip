@@ -466,6 +466,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
     const long long r0 = row0_of(a, n);
+    const long long slot0 = slot_of(a, n, 0);   // chunk c has slot slot0 + c
     const int len = len_of(a, n);
     const int nch = (len + C - 1) / C;
 
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     };
     Pre ra, rb;
     auto fetch = [&](Pre &R, int c) {
-        const long long slot = slot_of(a, n, c);
+        const long long slot = slot0 + c;
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
         const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     const int mt = wave >> 1, nt = wave & 1;          // this wave's c x 32 tile
     // chunk c: LDS holds chunk c, cur holds chunk c + 1, nxt receives chunk c + 2
     auto step = [&](int c, Pre &cur, Pre &nxt) {
-        const long long slot = slot_of(a, n, c);
+        const long long slot = slot0 + c;
         if (c + 2 < nch) fetch(nxt, c + 2);
         float *hs = a.hs + ((slot * H + h) * DK) * (long long)DV + col0;
 #pragma unroll
@@ -624,6 +625,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
     const long long r0 = row0_of(a, n);
+    const long long slot0 = slot_of(a, n, 0);   // chunk c has slot slot0 + c
     const int len = len_of(a, n);
     const int nch = (len + C - 1) / C;
 
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
     };
     Pre ra, rb;
     auto fetch = [&](Pre &R, int c) {
-        const long long slot = slot_of(a, n, c);
+        const long long slot = slot0 + c;
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
         const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
     const int mt = wave >> 1, nt = wave & 1;
     // chunk c: LDS holds chunk c, cur holds chunk c - 1, nxt receives chunk c - 2
     auto step = [&](int c, Pre &cur, Pre &nxt) {
-        const long long slot = slot_of(a, n, c);
+        const long long slot = slot0 + c;
         if (c >= 2) fetch(nxt, c - 2);
         float *dh = a.dhs + ((slot * H + h) * DK) * (long long)DV + col0;
 #pragma unroll
@@ -898,8 +900,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             ps[j] = *(const f32x4 *)(hs + row * DV + col0 + c4);
             pd[j] = *(const f32x4 *)(dhs + row * DV + col0 + c4);
         }
-        if (tid < C * DVB / 8) pvy = piece<DV, DVB>(a.v, t0, nv, H, h, col0, tid);
-        else pvy = piece<DV, DVB>(a.dy, t0, nv, H, h, col0, tid - C * DVB / 8);
+        // V for the first 256 threads, dY for the rest: one load on either side
+        const uint16_t *src = tid < C * DVB / 8 ? a.v : a.dy;
+        pvy = piece_clamped<DV, DVB>(src, t0, nv, H, h, col0, tid % (C * DVB / 8));
     };
     auto commit = [&]() {
 #pragma unroll
@@ -917,8 +920,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             *(bf16x4 *)(sDl + row * LVT + c4) =
                 __builtin_convertvector(d4 - __builtin_convertvector(dh, f32x4), bf16x4);
         }
-        if (tid < C * DVB / 8) put_piece<DVB>(sV, LVT, tid, pvy);
-        else put_piece<DVB>(sY, LVT, tid - C * DVB / 8, pvy);
+        const int iv = tid % (C * DVB / 8);
+        put_piece<DVB>(tid < C * DVB / 8 ? sV : sY, LVT, iv, piece_keep<DVB>(pvy, nv, iv));
     };
     static_assert(2 * C * DVB / 8 == 512 && SP >= 1, "one V or dY piece per thread");
 
@@ -927,7 +930,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
         __syncthreads();   // the previous pass is done (and L^T written before the first)
         commit();
         __syncthreads();
-        if (col0 + DVB < DV) fetch(col0 + DVB);
+        fetch(col0 + DVB < DV ? col0 + DVB : col0);   // the last pass: its own columns again
         // phase 1: R = V - diag(gamma) K S;  diag(gamma_C / gamma) K D (kept in registers)
         f32x4 R = zero4(), kd = zero4();
         mm<false, false>(R, sK, LK, sS, LVT, 16 * mt, 16 * nt, DK);
