@@ -796,8 +796,8 @@ struct CkLds {
     // after the passes (the pass region is free)
     static constexpr int oQ = oBlk;                       // [64][LK]   Q
     static constexpr int oDPt = oQ + C * LK * 2;          // [64][L64]  (dP (.) Gamma)^T
-    static constexpr int oDLs = oDPt + C * L64 * 2;       // [64][L64]  dLG + dLG^T
-    static constexpr int oPart = oDLs + C * L64 * 2;      // row-sum partials (fp32)
+    static constexpr int oDLt = oDPt + C * L64 * 2;       // [64][L64]  (dL (.) Gamma)^T
+    static constexpr int oPart = oDLt + C * L64 * 2;      // row-sum partials (fp32)
     static constexpr int partFloats = 20 * C + 40;
     static_assert(oPart + partFloats * 4 <= blkEnd, "the after-pass data fits the pass region");
     static constexpr int total = blkEnd;
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     uint16_t *sDUt = (uint16_t *)(smem + L::oDUt), *sZt = (uint16_t *)(smem + L::oZt);
     uint16_t *sEt = (uint16_t *)(smem + L::oEt);
     uint16_t *sQ = (uint16_t *)(smem + L::oQ), *sDPt = (uint16_t *)(smem + L::oDPt);
-    uint16_t *sDLs = (uint16_t *)(smem + L::oDLs);
+    uint16_t *sDLt = (uint16_t *)(smem + L::oDLt);
 
     const int H = a.H;
     const long long slot = blockIdx.x / H;
@@ -839,30 +839,39 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
 
+    // Every input the kernel reads outside the passes goes out at once: K, the record's T',
+    // P^T and g, beta and alpha of the chunk's rows (clamped into the chunk), and Q, which is
+    // held in registers until the passes are done.
+    constexpr int NP = (KP + 511) / 512;
+    u32x4 qx[NP];
+    float al;
     {
-        // the K pieces and the record's T' and P^T pieces in flight together
-        constexpr int NP = (KP + 511) / 512;
         u32x4 kx[NP];
 #pragma unroll
-        for (int u = 0; u < NP; ++u)
+        for (int u = 0; u < NP; ++u) {
             kx[u] = piece_clamped<DK, DK>(a.k, t0, nv, H, h, 0, (tid + 512 * u) % KP);
+            qx[u] = piece_clamped<DK, DK>(a.q, t0, nv, H, h, 0, (tid + 512 * u) % KP);
+        }
         const u32x4 tx = rec_piece(rec, kRT, tid), px = rec_piece(rec, kRP, tid);
+        const int tc = tid % C < nv ? tid % C : nv - 1;
+        const float gt = ((const float *)(rec + kRG))[tid % C];
+        const float gl = ((const float *)(rec + kRG))[C - 1];
+        const float bt = a.beta[(t0 + tc) * H + h];
+        al = a.alpha[(t0 + tc) * H + h];
 #pragma unroll
         for (int u = 0; u < NP; ++u)
             if (tid + 512 * u < KP)
                 put_piece<DK>(sK, LK, tid + 512 * u, piece_keep<DK>(kx[u], nv, tid + 512 * u));
         put_rec_piece(sT, tid, tx);
         put_rec_piece(sP, tid, px);
-    }
-    if (tid < C) {
-        const float gt = ((const float *)(rec + kRG))[tid];
-        const float gl = ((const float *)(rec + kRG))[C - 1];
-        g[tid] = gt;
-        gam[tid] = __expf(gt);
-        rat[tid] = __expf(gl - gt);
-        bet[tid] = tid < nv ? a.beta[(t0 + tid) * H + h] : 0.f;
-        dbp[tid] = 0.f;
-        dbp[C + tid] = 0.f;
+        if (tid < C) {
+            g[tid] = gt;
+            gam[tid] = __expf(gt);
+            rat[tid] = __expf(gl - gt);
+            bet[tid] = tid < nv ? bt : 0.f;
+            dbp[tid] = 0.f;
+            dbp[C + tid] = 0.f;
+        }
     }
     __syncthreads();
     // L = strictlower(K K^T (.) Gamma), stored transposed: 16 tiles, two per wave
@@ -997,19 +1006,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             mm2<true, true>(accGb[i], sUt, L64, sD, sDl, LVT, m0, n0, DVB);
         }
     }
-    __syncthreads();   // the pass region now takes Q, (dP (.) Gamma)^T, dLG + dLG^T, partials
+    __syncthreads();   // the pass region now takes Q, (dP (.) Gamma)^T, (dL (.) Gamma)^T, partials
 
-    {
-        constexpr int NP = (KP + 511) / 512;
-        u32x4 qx[NP];
 #pragma unroll
-        for (int u = 0; u < NP; ++u)
-            qx[u] = piece_clamped<DK, DK>(a.q, t0, nv, H, h, 0, (tid + 512 * u) % KP);
-#pragma unroll
-        for (int u = 0; u < NP; ++u)
-            if (tid + 512 * u < KP)
-                put_piece<DK>(sQ, LK, tid + 512 * u, piece_keep<DK>(qx[u], nv, tid + 512 * u));
-    }
+    for (int u = 0; u < NP; ++u)
+        if (tid + 512 * u < KP)
+            put_piece<DK>(sQ, LK, tid + 512 * u, piece_keep<DK>(qx[u], nv, tid + 512 * u));
     // Row sums are written per source tile and added in a fixed order afterwards, so every
     // output is bitwise repeatable.
     //   pG[kt][t]  row dot of the c x d_k accumulators, column tile kt
@@ -1020,68 +1022,107 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     float *pG = (float *)(smem + L::oPart);
     float *pR = pG + 8 * C, *pC = pR + 4 * C, *pB = pC + 4 * C, *pX = pB + 4 * C;
     __syncthreads();
+    // Every LDS operand of the sums below is read before any sum is stored, so the reads go
+    // out together.
+    float qv[NQ][4], kv[NQ][4], gm[NQ][4], rt[NQ][4];
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const int tile = wave + 8 * i;
         const int m0 = 16 * (tile / KT), n0 = 16 * (tile % KT);
-        float xs = 0.f;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = m0 + q4 + ii, col = n0 + r;
-            accGq[i][ii] *= gam[t];
-            accGa[i][ii] *= -gam[t];
-            accGb[i][ii] *= rat[t];
-            const float qv = bf(sQ + t * LK + col), kv = bf(sK + t * LK + col);
-            const float xb = kv * accGb[i][ii];
-            const float d = sum16(qv * accGq[i][ii] + kv * accGa[i][ii] - xb);
-            if (r == 0) pG[(n0 / 16) * C + t] = d;
-            xs += xb;
+            qv[i][ii] = bf(sQ + t * LK + col);
+            kv[i][ii] = bf(sK + t * LK + col);
+            gm[i][ii] = gam[t];
+            rt[i][ii] = rat[t];
         }
-        xs = sum64(xs);
-        if (lane == 0) pX[tile] = xs;
     }
-    {
-        const float s = sum64(sd);
-        if (lane == 0) pX[32 + wave] = s;
-    }
-    // dP = lower_incl(M), dL = -diag(beta) strictlower(Eu); their decayed forms to LDS;
-    // dg from (dP (.) P + dL (.) L): + row sums, - column sums;  dbeta -= sum_i L (.) Eu
+    float gt2[2][4], gs2[2][4], lv2[2][4], pv2[2][4], bt2[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int tile = wave + 8 * i;
         const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
-        f32x4 dpg;
-        float cs = 0.f;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = m0 + q4 + ii, s = n0 + r;
-            const float G = decay(g, t, s);
-            const float dP = s <= t ? accM[i][ii] : 0.f;
-            const float lv = bf(sLt + s * L64 + t);
-            const float dL = s < t ? -bet[t] * accEu[i][ii] : 0.f;
-            dpg[ii] = dP * G;
-            const __bf16 dl = (__bf16)(dL * G);
-            if (s < t) {
-                *(__bf16 *)(sDLs + t * L64 + s) = dl;
-                *(__bf16 *)(sDLs + s * L64 + t) = dl;
-            } else if (s == t) {
-                sDLs[t * L64 + t] = 0;
-            }
-            const float w = dP * bf(sP + s * L64 + t) + dL * lv;
-            const float rs = sum16(w);
-            const float bsum = sum16(s < t ? lv * accEu[i][ii] : 0.f);
-            if (r == 0) {
-                pR[(n0 / 16) * C + t] = rs;
-                pB[(n0 / 16) * C + t] = bsum;
-            }
-            cs += w;
+            gt2[i][ii] = g[t];
+            gs2[i][ii] = g[s];
+            lv2[i][ii] = bf(sLt + s * L64 + t);
+            pv2[i][ii] = bf(sP + s * L64 + t);
+            bt2[i][ii] = bet[t];
         }
-        put_t(sDPt, L64, m0, n0, dpg);
-        cs = row_sum4(cs);
-        if (lane < 16) pC[(m0 / 16) * C + n0 + r] = cs;
+    }
+    // row dots of the c x d_k accumulators
+    float dG[NQ][4], xs[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        xs[i] = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            accGq[i][ii] *= gm[i][ii];
+            accGa[i][ii] *= -gm[i][ii];
+            accGb[i][ii] *= rt[i][ii];
+            const float xb = kv[i][ii] * accGb[i][ii];
+            dG[i][ii] = sum16(qv[i][ii] * accGq[i][ii] + kv[i][ii] * accGa[i][ii] - xb);
+            xs[i] += xb;
+        }
+        xs[i] = sum64(xs[i]);
+    }
+    const float sdw = sum64(sd);
+    // dP = lower_incl(M), dL = -diag(beta) strictlower(Eu) and their decayed forms;
+    // dg from (dP (.) P + dL (.) L): + row sums, - column sums;  dbeta -= sum_i L (.) Eu
+    f32x4 dpg[2], dlg[2];
+    float rs[2][4], bs[2][4], cs[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tile = wave + 8 * i;
+        const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
+        cs[i] = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = m0 + q4 + ii, s = n0 + r;
+            const float G = s <= t ? __expf(gt2[i][ii] - gs2[i][ii]) : 0.f;
+            const float dP = s <= t ? accM[i][ii] : 0.f;
+            const float dL = s < t ? -bt2[i][ii] * accEu[i][ii] : 0.f;
+            dpg[i][ii] = dP * G;
+            dlg[i][ii] = dL * G;
+            const float w = dP * pv2[i][ii] + dL * lv2[i][ii];
+            rs[i][ii] = sum16(w);
+            bs[i][ii] = sum16(s < t ? lv2[i][ii] * accEu[i][ii] : 0.f);
+            cs[i] += w;
+        }
+        cs[i] = row_sum4(cs[i]);
+    }
+    // the sums and the decayed tiles to LDS
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int tile = wave + 8 * i;
+        const int m0 = 16 * (tile / KT), n0 = 16 * (tile % KT);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            if (r == 0) pG[(n0 / 16) * C + m0 + q4 + ii] = dG[i][ii];
+        if (lane == 0) pX[tile] = xs[i];
+    }
+    if (lane == 0) pX[32 + wave] = sdw;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tile = wave + 8 * i;
+        const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            if (r == 0) {
+                pR[(n0 / 16) * C + m0 + q4 + ii] = rs[i][ii];
+                pB[(n0 / 16) * C + m0 + q4 + ii] = bs[i][ii];
+            }
+        }
+        put_t(sDPt, L64, m0, n0, dpg[i]);
+        put_t(sDLt, L64, m0, n0, dlg[i]);
+        if (lane < 16) pC[(m0 / 16) * C + n0 + r] = cs[i];
     }
     __syncthreads();
-    // dQ = Gq + (dP (.) Gamma) K;  dK = Ga + Gb + (dP (.) Gamma)^T Q + (dLG + dLG^T) K
+    // dQ = Gq + (dP (.) Gamma) K;  dK = Ga + Gb + (dP (.) Gamma)^T Q + (dL (.) Gamma) K
+    //                                   + (dL (.) Gamma)^T K
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const int tile = wave + 8 * i;
@@ -1090,7 +1131,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
         mm<true, false>(aq, sDPt, L64, sK, LK, m0, n0, C);
         f32x4 ak = accGa[i] + accGb[i];
         mm<false, false>(ak, sDPt, L64, sQ, LK, m0, n0, C);
-        mm<false, false>(ak, sDLs, L64, sK, LK, m0, n0, C);
+        mm<true, false>(ak, sDLt, L64, sK, LK, m0, n0, C);
+        mm<false, false>(ak, sDLt, L64, sK, LK, m0, n0, C);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = m0 + q4 + ii;
@@ -1126,7 +1168,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
         }
         if (t < nv) {
             const long long o = (t0 + t) * H + h;
-            const float al = a.alpha[o];
             a.dalpha[o] = __logf(al) > kLnAlphaFloor ? x / al : 0.f;
             a.dbeta[o] = bt;
         }
