@@ -839,19 +839,17 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q4 = (lane >> 4) * 4;
 
-    // Every input the kernel reads outside the passes goes out at once: K, the record's T',
-    // P^T and g, beta and alpha of the chunk's rows (clamped into the chunk), and Q, which is
-    // held in registers until the passes are done.
+    // K, the record's T', P^T and g, and beta and alpha of the chunk's rows (clamped into the
+    // chunk) go out at once; Q follows with the first pass's S and D and is held in
+    // registers until the passes are done.
     constexpr int NP = (KP + 511) / 512;
     u32x4 qx[NP];
     float al;
     {
         u32x4 kx[NP];
 #pragma unroll
-        for (int u = 0; u < NP; ++u) {
+        for (int u = 0; u < NP; ++u)
             kx[u] = piece_clamped<DK, DK>(a.k, t0, nv, H, h, 0, (tid + 512 * u) % KP);
-            qx[u] = piece_clamped<DK, DK>(a.q, t0, nv, H, h, 0, (tid + 512 * u) % KP);
-        }
         const u32x4 tx = rec_piece(rec, kRT, tid), px = rec_piece(rec, kRP, tid);
         const int tc = tid % C < nv ? tid % C : nv - 1;
         const float gt = ((const float *)(rec + kRG))[tid % C];
@@ -860,21 +858,23 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
         al = a.alpha[(t0 + tc) * H + h];
 #pragma unroll
         for (int u = 0; u < NP; ++u)
-            if (tid + 512 * u < KP)
+            if (KP % 512 == 0 || tid + 512 * u < KP)
                 put_piece<DK>(sK, LK, tid + 512 * u, piece_keep<DK>(kx[u], nv, tid + 512 * u));
         put_rec_piece(sT, tid, tx);
         put_rec_piece(sP, tid, px);
-        if (tid < C) {
-            g[tid] = gt;
-            gam[tid] = __expf(gt);
-            rat[tid] = __expf(gl - gt);
-            bet[tid] = tid < nv ? bt : 0.f;
-            dbp[tid] = 0.f;
-            dbp[C + tid] = 0.f;
-        }
+        // every thread stores its row's gate values (the eight threads of a row store the same
+        // values), so the gate loads are not held back behind a branch
+        const int tr = tid % C;
+        g[tr] = gt;
+        gam[tr] = __expf(gt);
+        rat[tr] = __expf(gl - gt);
+        bet[tr] = tr < nv ? bt : 0.f;
+        dbp[tr] = 0.f;
+        dbp[C + tr] = 0.f;
     }
     __syncthreads();
     // L = strictlower(K K^T (.) Gamma), stored transposed: 16 tiles, two per wave
+#pragma unroll
     for (int tile = wave; tile < 16; tile += 8) {
         const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
         f32x4 kk = zero4();
@@ -934,6 +934,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     };
     static_assert(2 * C * DVB / 8 == 512 && SP >= 1, "one V or dY piece per thread");
 
+#pragma unroll
+    for (int u = 0; u < NP; ++u)
+        qx[u] = piece_clamped<DK, DK>(a.q, t0, nv, H, h, 0, (tid + 512 * u) % KP);
     fetch(0);
     for (int col0 = 0; col0 < DV; col0 += DVB) {
         __syncthreads();   // the previous pass is done (and L^T written before the first)
@@ -1010,7 +1013,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
 
 #pragma unroll
     for (int u = 0; u < NP; ++u)
-        if (tid + 512 * u < KP)
+        if (KP % 512 == 0 || tid + 512 * u < KP)
             put_piece<DK>(sQ, LK, tid + 512 * u, piece_keep<DK>(qx[u], nv, tid + 512 * u));
     // Row sums are written per source tile and added in a fixed order afterwards, so every
     // output is bitwise repeatable.
