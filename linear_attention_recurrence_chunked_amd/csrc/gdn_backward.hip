@@ -270,10 +270,13 @@ __device__ __forceinline__ u32x4 scale_piece(u32x4 x, float s)
     return o;
 }
 
-// Gamma_ti = e^{g_t - g_i} for i <= t, else 0.
+// Gamma_ti = e^{g_t - g_i} for i <= t, else 0.  The exponent is capped at 0 (g falls with t,
+// so only the masked entries reach the cap) and the power is taken for every entry, so the
+// mask is a select rather than a branch around the reads of g.
 __device__ __forceinline__ float decay(const float *g, int t, int i)
 {
-    return i <= t ? __expf(g[t] - g[i]) : 0.f;
+    const float e = __expf(fminf(g[t] - g[i], 0.f));
+    return i <= t ? e : 0.f;
 }
 
 // Record pieces (16 bytes of a [64][64] bf16 matrix) and their place in an LDS tile
@@ -799,7 +802,12 @@ struct CkLds {
     static constexpr int oDLt = oDPt + C * L64 * 2;       // [64][L64]  (dL (.) Gamma)^T
     static constexpr int oPart = oDLt + C * L64 * 2;      // row-sum partials (fp32)
     static constexpr int partFloats = 20 * C + 40;
-    static_assert(oPart + partFloats * 4 <= blkEnd, "the after-pass data fits the pass region");
+    // each wave's dq and dk tiles (bf16, 16 x 16 each, rows of 32 bytes) before their store
+    static constexpr int SL = 16;
+    static constexpr int NQW = DK / 16 * 4 / 8;           // c x d_k tiles per wave
+    static constexpr int oStg = (oPart + partFloats * 4 + 15) / 16 * 16;
+    static constexpr int stgHalfs = NQW * 2 * 16 * SL;    // per wave
+    static_assert(oStg + 8 * stgHalfs * 2 <= blkEnd, "the after-pass data fits the pass region");
     static constexpr int total = blkEnd;
 };
 
@@ -1051,9 +1059,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             const int t = m0 + q4 + ii, s = n0 + r;
             gt2[i][ii] = g[t];
             gs2[i][ii] = g[s];
-            lv2[i][ii] = bf(sLt + s * L64 + t);
-            pv2[i][ii] = bf(sP + s * L64 + t);
             bt2[i][ii] = bet[t];
+        }
+        // L^T and P^T hold the four rows t of a lane next to each other
+        const bf16x4 l4 = *(const bf16x4 *)(sLt + (n0 + r) * L64 + m0 + q4);
+        const bf16x4 p4 = *(const bf16x4 *)(sP + (n0 + r) * L64 + m0 + q4);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            lv2[i][ii] = (float)l4[ii];
+            pv2[i][ii] = (float)p4[ii];
         }
     }
     // row dots of the c x d_k accumulators
@@ -1085,7 +1099,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = m0 + q4 + ii, s = n0 + r;
-            const float G = s <= t ? __expf(gt2[i][ii] - gs2[i][ii]) : 0.f;
+            const float e = __expf(fminf(gt2[i][ii] - gs2[i][ii], 0.f));
+            const float G = s <= t ? e : 0.f;
             const float dP = s <= t ? accM[i][ii] : 0.f;
             const float dL = s < t ? -bt2[i][ii] * accEu[i][ii] : 0.f;
             dpg[i][ii] = dP * G;
@@ -1126,6 +1141,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
     __syncthreads();
     // dQ = Gq + (dP (.) Gamma) K;  dK = Ga + Gb + (dP (.) Gamma)^T Q + (dL (.) Gamma) K
     //                                   + (dL (.) Gamma)^T K
+    // The wave's tiles go to its own LDS block and from there to HBM in 16-byte pieces (one
+    // wave's LDS accesses complete in order, so no barrier stands between the two).
+    constexpr int SL = L::SL;
+    static_assert(L::NQW == NQ, "tiles per wave");
+    __bf16 *stg = (__bf16 *)(smem + L::oStg) + wave * L::stgHalfs;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const int tile = wave + 8 * i;
@@ -1138,13 +1158,21 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
         mm<false, false>(ak, sDLt, L64, sK, LK, m0, n0, C);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int t = m0 + q4 + ii;
-            if (t < nv) {
-                const long long o = ((t0 + t) * H + h) * (long long)DK + n0 + r;
-                Elem<uint16_t>::store(a.dq + o, aq[ii]);
-                Elem<uint16_t>::store(a.dk + o, ak[ii]);
-            }
+            stg[((2 * i) * 16 + q4 + ii) * SL + r] = (__bf16)aq[ii];
+            stg[((2 * i + 1) * 16 + q4 + ii) * SL + r] = (__bf16)ak[ii];
         }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        // piece (tile i, dq or dk, row rr of the tile, half hf of its 16 columns)
+        const int pc = lane + 64 * j;
+        const int hf = pc & 1, rr = (pc >> 1) & 15, ten = (pc >> 5) & 1, i = pc >> 6;
+        const int tile = wave + 8 * i;
+        const int t = 16 * (tile / KT) + rr, n0 = 16 * (tile % KT);
+        const u32x4 x = *(const u32x4 *)(stg + ((2 * i + ten) * 16 + rr) * SL + 8 * hf);
+        if (t < nv)
+            *(u32x4 *)((ten ? a.dk : a.dq) + ((t0 + t) * H + h) * (long long)DK + n0 + 8 * hf) = x;
     }
     // dlog alpha = reverse prefix of dg (the chunk-end terms land on the last slot)
     if (tid < C) {
