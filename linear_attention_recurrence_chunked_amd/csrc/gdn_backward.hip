@@ -60,6 +60,31 @@ constexpr int LF = C + 4;                  // fp32 row stride of the prep kernel
 constexpr int kRT = 0, kRP = C * C, kRG = 2 * C * C;
 constexpr int kRecHalfs = 2 * C * C + 2 * C;
 constexpr int kThreadsScan = 512;
+constexpr int LSF = DVT + 4;               // fp32 row stride of a kept state block in LDS
+
+// An accumulator tile into a row-major fp32 [.][LSF] block, and the block's 16-byte pieces
+// (row i / (DVT / 4), columns 4 (i % (DVT / 4)) ..) to a [DK][DV] state in HBM: the state
+// leaves in whole pieces rather than one word per lane, and non-temporally, so the kept states
+// (read back by a later launch) do not push the chunk inputs that the other column tiles of
+// the same head still read out of L2.
+__device__ __forceinline__ void put_f(float *D, int m0, int n0, f32x4 v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) D[(m0 + 4 * (lane >> 4) + i) * LSF + n0 + (lane & 15)] = v[i];
+}
+template <int DK, int DV>
+__device__ __forceinline__ void store_state(float *dst, const float *Sf)
+{
+    constexpr int PR = DVT / 4, NPC = DK * PR / kThreadsScan;
+    static_assert(DK * PR % kThreadsScan == 0, "whole pieces per thread");
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+        const int i = threadIdx.x + kThreadsScan * j, row = i / PR, c4 = 4 * (i % PR);
+        __builtin_nontemporal_store(*(const f32x4 *)(Sf + row * LSF + c4),
+                                    (f32x4 *)(dst + row * DV + c4));
+    }
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ float bf(const uint16_t *p) { return bf16_to_f32(*p); }
@@ -443,7 +468,8 @@ struct StLds {
     static constexpr int oUt = oXt + DVT * L64 * 2;      // [DVT][L64] (diag(rho) U)^T
     static constexpr int oGam = oUt + DVT * L64 * 2;
     static constexpr int oRat = oGam + C * 4;
-    static constexpr int total = oRat + C * 4;
+    static constexpr int oSf = oRat + C * 4;             // [DK][LSF]  S (fp32), to HBM
+    static constexpr int total = oSf + DK * LSF * 4;
 };
 
 template <int DK, int DV>
@@ -460,6 +486,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     uint16_t *sV = (uint16_t *)(smem + L::oV), *sSt = (uint16_t *)(smem + L::oSt);
     uint16_t *sXt = (uint16_t *)(smem + L::oXt), *sUt = (uint16_t *)(smem + L::oUt);
     float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
+    float *sSf = (float *)(smem + L::oSf);
     const int H = a.H;
     int unit, tile;
     scan_job<NT>(unit, tile);
@@ -483,6 +510,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
                                   16 * nt + r]
                            : 0.f;
         put_t(sSt, LK, 16 * mi, 16 * nt, S[k]);
+        put_f(sSf, 16 * mi, 16 * nt, S[k]);
     }
 
     // inputs of a later chunk, fetched two chunks ahead into one of two register sets
@@ -533,13 +561,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     auto step = [&](int c, Pre &cur, Pre &nxt) {
         const long long slot = slot0 + c;
         if (c + 2 < nch) fetch(nxt, c + 2);
-        float *hs = a.hs + ((slot * H + h) * DK) * (long long)DV + col0;
-#pragma unroll
-        for (int k = 0; k < SPW; ++k) {
-            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hs[(16 * mi + q4 + i) * DV + 16 * nk + r] = S[k][i];
-        }
+        store_state<DK, DV>(a.hs + ((slot * H + h) * DK) * (long long)DV + col0, sSf);
         // X = V - diag(gamma) K S
         {
             f32x4 acc = zero4();
@@ -569,6 +591,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
             S[k] *= gC;
             mm<true, true>(S[k], sK, LK, sUt, L64, 16 * mi, 16 * nk, C);
             put_t(sSt, LK, 16 * mi, 16 * nk, S[k]);
+            put_f(sSf, 16 * mi, 16 * nk, S[k]);
         }
         __syncthreads();
         if (c + 1 < nch) commit(cur);
@@ -600,7 +623,8 @@ struct DsLds {
     static constexpr int oZt = oXt + DVT * L64 * 2;      // [DVT][L64] (-diag(gamma) Z)^T
     static constexpr int oGam = oZt + DVT * L64 * 2;
     static constexpr int oRat = oGam + C * 4;
-    static constexpr int total = oRat + C * 4;
+    static constexpr int oDf = oRat + C * 4;             // [DK][LSF]  D (fp32), to HBM
+    static constexpr int total = oDf + DK * LSF * 4;
 };
 
 template <int DK, int DV>
@@ -619,6 +643,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
     uint16_t *sDt = (uint16_t *)(smem + L::oDt), *sXt = (uint16_t *)(smem + L::oXt);
     uint16_t *sZt = (uint16_t *)(smem + L::oZt);
     float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
+    float *sDf = (float *)(smem + L::oDf);
     const int H = a.H;
     int unit, tile;
     scan_job<NT>(unit, tile);
@@ -642,6 +667,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
                                                   DV + col0 + 16 * nt + r]
                                  : 0.f;
         put_t(sDt, LK, 16 * mi, 16 * nt, D[k]);
+        put_f(sDf, 16 * mi, 16 * nt, D[k]);
     }
 
     struct Pre {
@@ -706,13 +732,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
     auto step = [&](int c, Pre &cur, Pre &nxt) {
         const long long slot = slot0 + c;
         if (c >= 2) fetch(nxt, c - 2);
-        float *dh = a.dhs + ((slot * H + h) * DK) * (long long)DV + col0;
-#pragma unroll
-        for (int k = 0; k < SPW; ++k) {
-            const int id = wave + 8 * k, mi = id >> 1, nk = id & 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dh[(16 * mi + q4 + i) * DV + 16 * nk + r] = D[k][i];
-        }
+        store_state<DK, DV>(a.dhs + ((slot * H + h) * DK) * (long long)DV + col0, sDf);
         // X = P^T dY + diag(gamma_C / gamma) K D
         {
             f32x4 a1 = zero4(), a2 = zero4();
@@ -741,6 +761,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
             mm<true, false>(D[k], sQ, LK, sYg, LVT, 16 * mi, 16 * nk, C);
             mm<true, true>(D[k], sK, LK, sZt, L64, 16 * mi, 16 * nk, C);
             put_t(sDt, LK, 16 * mi, 16 * nk, D[k]);
+            put_f(sDf, 16 * mi, 16 * nk, D[k]);
         }
         __syncthreads();
         if (c > 0) commit(cur);
