@@ -319,17 +319,19 @@ __device__ __forceinline__ void put_rec_piece(uint16_t *dst, int i, u32x4 x)
 // bwd_prep_kernel: per (chunk slot, head) T' = (I + diag(beta) L)^{-1} diag(beta) by forward
 // substitution (fp32), P = lower_incl(Q K^T (.) Gamma), g.  Four waves.
 // ======================================================================================
+// T' takes the place of K and Q once the products are done and P^T goes to the record from
+// the accumulators, so three workgroups fit in a CU's LDS.
 template <int DK>
 struct PrepLds {
     static constexpr int LK = DK + 8;
     static constexpr int oK = 0;
+    static constexpr int oT = 0;                    // [64][LF] fp32, over K and Q
     static constexpr int oQ = oK + C * LK * 2;
     static constexpr int oL = oQ + C * LK * 2;      // [64][LF] fp32
-    static constexpr int oT = oL + C * LF * 4;      // [64][LF] fp32
-    static constexpr int oPb = oT + C * LF * 4;     // [64][L64] bf16 P^T
-    static constexpr int oG = oPb + C * L64 * 2;
+    static constexpr int oG = oL + C * LF * 4;
     static constexpr int oBet = oG + C * 4;
     static constexpr int total = oBet + C * 4;
+    static_assert(C * LF * 4 <= 2 * C * LK * 2, "T' fits where K and Q were");
 };
 
 template <int DK>
@@ -341,7 +343,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     uint16_t *sK = (uint16_t *)(smem + L::oK), *sQ = (uint16_t *)(smem + L::oQ);
     float *sL = (float *)(smem + L::oL), *sT = (float *)(smem + L::oT);
     float *g = (float *)(smem + L::oG), *bet = (float *)(smem + L::oBet);
-    uint16_t *sPb = (uint16_t *)(smem + L::oPb);
     const int H = a.H;
     const long long slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -402,7 +403,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
             sL[t * LF + s] = s < t ? kk[i] * G : 0.f;
             qk[i] *= G;
         }
-        put_t(sPb, L64, m0, n0, qk);   // P^T
+        // P^T to the record: rows n0 + r, four adjacent columns m0 + q4 .. per lane
+        *(bf16x4 *)(rec + kRP + (n0 + r) * C + m0 + q4) = __builtin_convertvector(qk, bf16x4);
     }
     __syncthreads();
 
@@ -437,9 +439,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 #pragma unroll
     for (int m = 0; m < 16; ++m) sT[(4 * m + p) * LF + j] = col[m];
     __syncthreads();
-    // T' and P^T to the record in 16-byte pieces
-    for (int i = tid; i < C * C / 8; i += 256)
-        *(u32x4 *)(rec + kRP + 8 * i) = *(const u32x4 *)(sPb + (i >> 3) * L64 + 8 * (i & 7));
+    // T' to the record in 16-byte pieces
     for (int i = tid; i < C * C / 8; i += 256) {
         const int t = i >> 3, c8 = 8 * (i & 7);
         const f32x4 lo = *(const f32x4 *)(sT + t * LF + c8);
