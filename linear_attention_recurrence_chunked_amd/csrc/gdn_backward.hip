@@ -319,19 +319,20 @@ __device__ __forceinline__ void put_rec_piece(uint16_t *dst, int i, u32x4 x)
 // bwd_prep_kernel: per (chunk slot, head) T' = (I + diag(beta) L)^{-1} diag(beta) by forward
 // substitution (fp32), P = lower_incl(Q K^T (.) Gamma), g.  Four waves.
 // ======================================================================================
-// T' takes the place of K and Q once the products are done and P^T goes to the record from
-// the accumulators, so three workgroups fit in a CU's LDS.
+// L takes the place of Q once the products are done, T' that of K (and of L once the solve is
+// done), and P^T goes to the record from the accumulators, so four workgroups fit in a CU's LDS.
 template <int DK>
 struct PrepLds {
     static constexpr int LK = DK + 8;
     static constexpr int oK = 0;
-    static constexpr int oT = 0;                    // [64][LF] fp32, over K and Q
+    static constexpr int oT = 0;                    // [64][LF] fp32, after the solve
     static constexpr int oQ = oK + C * LK * 2;
-    static constexpr int oL = oQ + C * LK * 2;      // [64][LF] fp32
-    static constexpr int oG = oL + C * LF * 4;
+    static constexpr int oL = oQ;                   // [64][LF] fp32, after the products
+    static constexpr int szQL = C * LK * 2 > C * LF * 4 ? C * LK * 2 : C * LF * 4;
+    static constexpr int oG = oQ + szQL;
     static constexpr int oBet = oG + C * 4;
     static constexpr int total = oBet + C * 4;
-    static_assert(C * LF * 4 <= 2 * C * LK * 2, "T' fits where K and Q were");
+    static_assert(C * LF * 4 <= oG, "T' fits below the gates");
 };
 
 template <int DK>
@@ -390,8 +391,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     }
     __syncthreads();
 
-    // L (fp32, for the solve) and P (bf16, to the record): 16 tiles each, four per wave
-    for (int tile = wave; tile < 16; tile += 4) {
+    // L (fp32, for the solve) and P (bf16, to the record): 16 tiles each, four per wave; L is
+    // kept in registers until every wave is done with Q
+    f32x4 lt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int tile = wave + 4 * u;
         const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
         f32x4 kk = zero4(), qk = zero4();
         mm<false, true>(kk, sK, LK, sK, LK, m0, n0, DK);
@@ -400,11 +405,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i) {
             const int t = m0 + q4 + i, s = n0 + r;
             const float G = decay(g, t, s);
-            sL[t * LF + s] = s < t ? kk[i] * G : 0.f;
+            lt[u][i] = s < t ? kk[i] * G : 0.f;
             qk[i] *= G;
         }
         // P^T to the record: rows n0 + r, four adjacent columns m0 + q4 .. per lane
         *(bf16x4 *)(rec + kRP + (n0 + r) * C + m0 + q4) = __builtin_convertvector(qk, bf16x4);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int tile = wave + 4 * u;
+        const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sL[(m0 + q4 + i) * LF + n0 + r] = lt[u][i];
     }
     __syncthreads();
 
@@ -436,6 +449,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
         const float val = bt * ((t == j ? 1.f : 0.f) - s);
         col[t >> 2] += own[t & 3] * val;
     }
+    __syncthreads();   // every wave is done with L
 #pragma unroll
     for (int m = 0; m < 16; ++m) sT[(4 * m + p) * LF + j] = col[m];
     __syncthreads();
