@@ -256,6 +256,21 @@ __device__ __forceinline__ u32x4 piece(const uint16_t *src, long long t0, int nv
     if (t >= nv) return u32x4{0u, 0u, 0u, 0u};
     return *(const u32x4 *)(src + ((t0 + t) * H + h) * (long long)W + col0 + 8 * p);
 }
+// The same piece from the chunk's row base (first row, head h: one 64-bit address per chunk,
+// shared by the wave) and the thread's offset within the chunk (fixed for a thread), so a
+// scan's per-chunk fetch adds one offset per piece instead of forming each address anew.
+template <int W, int NC>
+__device__ __forceinline__ int piece_off(int H, int col0, int i)
+{
+    constexpr int P = NC / 8;
+    return (i / P) * H * W + col0 + 8 * (i % P);
+}
+template <int NC>
+__device__ __forceinline__ u32x4 piece_at(const uint16_t *base, int off, int nv, int i)
+{
+    if (i / (NC / 8) >= nv) return u32x4{0u, 0u, 0u, 0u};
+    return *(const u32x4 *)(base + off);
+}
 // The same piece loaded from a row clamped into the chunk (nv >= 1), without a branch: for
 // batches of loads that all go out before any is used; piece_keep() zeroes it past nv when
 // it is stored.
@@ -538,13 +553,15 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
         const long long t0 = r0 + (long long)c * C;
         const int nv = len - c * C < C ? len - c * C : C;
         const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
+        const uint16_t *kb = a.k + (t0 * H + h) * (long long)DK;
+        const uint16_t *vb = a.v + (t0 * H + h) * (long long)DV;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
-            if (i < KP) R.pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
+            if (i < KP) R.pk[j] = piece_at<DK>(kb, piece_off<DK, DK>(H, 0, i), nv, i);
         }
         R.pt = rec_piece(rec, kRT, tid);
-        if (tid < VP) R.pv = piece<DV, DVT>(a.v, t0, nv, H, h, col0, tid);
+        if (tid < VP) R.pv = piece_at<DVT>(vb, piece_off<DV, DVT>(H, col0, tid), nv, tid);
         if (tid < C) {
             R.pg = ((const float *)(rec + kRG))[tid];
             R.pgl = ((const float *)(rec + kRG))[C - 1];
@@ -695,18 +712,21 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_dstates_kernel(BwdArgs a)
         const int nv = len - c * C < C ? len - c * C : C;
         const uint16_t *rec = a.rec + (slot * H + h) * (long long)kRecHalfs;
         const float *rg = (const float *)(rec + kRG);
+        const long long rb = (t0 * H + h) * (long long)DK;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
             if (i < KP) {
-                R.pk[j] = piece<DK, DK>(a.k, t0, nv, H, h, 0, i);
-                R.pq[j] = piece<DK, DK>(a.q, t0, nv, H, h, 0, i);
+                const int o = piece_off<DK, DK>(H, 0, i);
+                R.pk[j] = piece_at<DK>(a.k + rb, o, nv, i);
+                R.pq[j] = piece_at<DK>(a.q + rb, o, nv, i);
             }
         }
         R.pp = rec_piece(rec, kRP, tid);
         R.pt = rec_piece(rec, kRT, tid);
         if (tid < VP) {
-            R.py = piece<DV, DVT>(a.dy, t0, nv, H, h, col0, tid);
+            R.py = piece_at<DVT>(a.dy + (t0 * H + h) * (long long)DV,
+                                 piece_off<DV, DVT>(H, col0, tid), nv, tid);
             R.pgy = rg[tid / (DVT / 8)];
         }
         if (tid < C) {
