@@ -181,6 +181,22 @@ __device__ __forceinline__ float sum16(float x)
     return x;
 }
 __device__ __forceinline__ float sum64(float x) { return row_sum4(sum16(x)); }
+// Sum over lanes l .. 63 (a reverse prefix): within each 16-lane row by DPP row shifts (lane
+// l adds lane l + n of its row, 0 past the row's end), then the totals of the later rows,
+// read from their first lanes.
+__device__ __forceinline__ float suffix_sum64(float x)
+{
+    x += dpp_f<0x101>(x);                   // row_shl:1
+    x += dpp_f<0x102>(x);                   // row_shl:2
+    x += dpp_f<0x104>(x);                   // row_shl:4
+    x += dpp_f<0x108>(x);                   // row_shl:8
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    const int row = (threadIdx.x & 63) >> 4;
+    const float later = row == 0 ? r1 + (r2 + r3) : row == 1 ? r2 + r3 : row == 2 ? r3 : 0.f;
+    return x + later;
+}
 
 struct BwdArgs {
     const uint16_t *q, *k, *v, *dy;
@@ -1247,11 +1263,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a)
             for (int w = 0; w < 8; ++w) sdt += pX[32 + w];
             x += xb + gam[C - 1] * sdt;
         }
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const float o = __shfl_down(x, s, kWave);
-            if (t + s < kWave) x += o;
-        }
+        x = suffix_sum64(x);
         if (t < nv) {
             const long long o = (t0 + t) * H + h;
             a.dalpha[o] = __logf(al) > kLnAlphaFloor ? x / al : 0.f;
