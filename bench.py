@@ -456,6 +456,24 @@ def main():
     dbytes = decode_bytes_per_head_step(dh) * B * Hd
     gbs = dbytes / (dec_us * 1e-6) / 1e9
     gbs4 = dbytes / (dec4_us * 1e-6) / 1e9
+    # what a plain device copy reaches on the same traffic: torch's copy of one state set's
+    # bytes (read once, written once), four source / destination pairs in rotation as above
+    csrc = [torch.empty_like(s0).uniform_() for _ in range(4)]
+    cdst = [torch.empty_like(s0) for _ in range(4)]
+    for i in range(4):
+        cdst[i].copy_(csrc[i])
+    torch.cuda.synchronize()
+    ncopy = 64
+    e4, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e4.record(stream)
+    with torch.cuda.stream(stream):
+        for i in range(ncopy):
+            cdst[i % 4].copy_(csrc[i % 4])
+    e5.record(stream)
+    torch.cuda.synchronize()
+    copy_us = e4.elapsed_time(e5) * 1e3 / ncopy
+    copy_gbs = 2 * s0.numel() * 4 / (copy_us * 1e-6) / 1e9
+    del csrc, cdst
     dtr = load_traffic("decode_bf16_B128_H16_d128", DECODE_SOURCES)
     # the roofline takes the rotating measurement: four state sets (512 MiB) exceed the
     # 256 MB MALL, so each step streams its state from and to HBM, as in a many-layer model
@@ -471,6 +489,12 @@ def main():
                           "steps_per_s": round(1e6 / dec_us, 1),
                           "achieved_GBs": round(gbs, 1),
                           "frac": round(gbs / PEAK_HBM_GBS, 4)},
+        "copy_reference": {"what": "torch copy_ of one state set's bytes (%d MB read, %d MB "
+                                   "written), four pairs in rotation" % (
+                                       s0.numel() * 4 // 10**6, s0.numel() * 4 // 10**6),
+                           "us": round(copy_us, 2), "achieved_GBs": round(copy_gbs, 1),
+                           "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+                           "decode_frac_of_copy": round(gbs4 / copy_gbs, 4)},
     }
 
     # ------------------------------------------------------------------ layer steps
