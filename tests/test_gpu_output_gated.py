@@ -71,11 +71,31 @@ def test_fused_gate_one_launch_scan(dev, oracle_lib, seg):
     _check(inp, dev, oracle_lib, 128, seg, "fused")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_composed_gate_other_plans(dev, oracle_lib, dtype):
-    """The column-split plans: prefill, then the output-gate kernel over the output in place."""
+@pytest.mark.parametrize("d,seg", [(128, -1), (128, 2), (64, -1), (64, 3)])
+def test_composed_gate_pipelined_scan(dev, oracle_lib, d, seg):
+    """bf16 with 32-column tiles (the default plan of short work), whose rows are gated after
+    the prefill: four tiles per head at d = 128, two at d = 64; ragged, single-token and empty
+    sequences, and segments whose final pass starts from combined segment states."""
+    inp = _inputs([300, 64, 1, 129, 0, 700, 65], 3, "bf16", seed=81 + d + seg, d=d)
+    _check(inp, dev, oracle_lib, 32, seg, "composed, pipelined scan")
+
+
+def test_gate_prefill_workload_full_size(dev, oracle_lib):
+    """The prefill workload (B = 4, H = 16, T = 4096, d = 128, bf16, S0 = 0) on the library's
+    own plan (32-column tiles, 256 workgroups), gated: every token of every head."""
+    from linear_attention_recurrence_chunked_amd import gdn
+    assert gdn.gdn_prefill_plan(4, 4 * 4096, 16, 128, 128, gdn.GDN_DTYPE_BF16)[0] == 32
+    inp = _inputs([4096] * 4, 16, "bf16", seed=85)
+    inp["s0"] = None
+    _check(inp, dev, oracle_lib, 0, 0, "prefill workload")
+
+
+@pytest.mark.parametrize("dtype,tile", [("bf16", 16), ("bf16", 64), ("f32", 0)])
+def test_composed_gate_other_plans(dev, oracle_lib, dtype, tile):
+    """The other column-split plans: prefill, then the output-gate kernel over the output in
+    place."""
     inp = _inputs([300, 64, 1, 129, 0, 200], 2, dtype, seed=75)
-    _check(inp, dev, oracle_lib, 0, 0, "composed")
+    _check(inp, dev, oracle_lib, tile, 0, "composed")
 
 
 def test_fused_equals_gate_of_prefill(dev):
