@@ -32,20 +32,22 @@ namespace gdn {
 constexpr int kRecT = 0;
 constexpr int kRecG = kChunk * kChunk * 2;
 static_assert(kRecG + kChunk * 4 == kPrepRecordBytes, "record layout");
-constexpr int kRecGranules = kPrepRecordBytes / 16;
 
 
 // =========================================================================================
 // Launch 1: per (chunk slot, head) record T', P, g.  Four waves; wave w owns block row /
 // column w of the 4 x 4 grid of 16 x 16 blocks.
 // =========================================================================================
+// T' goes from registers straight to the record in HBM (it is never read back here), so the
+// LDS holds only g, beta, the decay factors and the K rows, later A and the X blocks: 17 KiB,
+// eight workgroups per CU.
 template <int DK>
 struct LdsPrep {
     static constexpr int szRow = kChunk * DK * 2;
     static constexpr int LDB = 20;                  // padded fp32 rows of an A block
     static constexpr int LDX = 20;                  // padded rows of a diagonal X block
-    static constexpr int oT = kRecT, oG = kRecG;
-    static constexpr int oBeta = kPrepRecordBytes;
+    static constexpr int oG = 0;
+    static constexpr int oBeta = oG + kChunk * 4;
     static constexpr int oE = oBeta + 256;          // 2^g and 2^-g of the tokens
     static constexpr int oK = oE + 512;             // K rows (phases 1-2) ...
     static constexpr int oA = oK;                   // ... then A and the X blocks (phase 3)
@@ -57,7 +59,7 @@ struct LdsPrep {
 };
 
 template <int DK>
-__global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long long nslots)
+__global__ __launch_bounds__(256, 8) void chunk_prep_kernel(PrefillArgs a, long long nslots)
 {
     using L = LdsPrep<DK>;
     using OP = uint16_t;
@@ -73,7 +75,6 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     float *const sA = (float *)(smem + L::oA);
     float *const sX = (float *)(smem + L::oX);
     unsigned char *const bK = smem + L::oK;
-    unsigned char *const bT = smem + L::oT;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,6 +117,8 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
     if (c < 0 || c * kChunk >= slen) return;          // unused slot
     const long long t0 = st0 + c * kChunk;
     const int nv = (int)((slen - c * kChunk) < kChunk ? (slen - c * kChunk) : kChunk);
+    // the record: T' (written block by block as it is formed), then g
+    unsigned char *const bT = gprep + (slot * H + h) * (long long)kPrepRecordBytes;
 
     // ---- phase 1: K rows (zero beyond the chunk's last row), g, beta ----
     {
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
             x += dpp_f32<0x142, 0xa>(x);
             x += dpp_f32<0x143, 0xc>(x);
             sG[lane] = x;
+            ((float *)(bT + kRecG))[lane] = x;
             sE[lane] = __builtin_amdgcn_exp2f(x);
             sIE[lane] = __builtin_amdgcn_exp2f(-x);
         } else if (wave == 1) {
@@ -323,11 +327,6 @@ __global__ __launch_bounds__(256, 6) void chunk_prep_kernel(PrefillArgs a, long 
             }
         }
     }
-    __syncthreads();
-
-    // ---- phase 5: the record, granule for granule ----
-    u32x4 *dst = (u32x4 *)(gprep + (slot * H + h) * (long long)kPrepRecordBytes);
-    for (int i = tid; i < kRecGranules; i += 256) dst[i] = *(const u32x4 *)(smem + 16 * i);
 }
 
 // =========================================================================================
