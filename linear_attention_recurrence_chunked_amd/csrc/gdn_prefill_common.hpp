@@ -13,9 +13,13 @@ constexpr int kThreads = 256;
 constexpr float kLog2AlphaFloor = -126.0f;   // log2 alpha clamp: keeps alpha = 0 finite
 
 // Drain after a chain of v_mfma_f32_16x16x4_f32 whose result is read by anything but the
-// next MFMA's accumulator input.  On gfx950 the wait states the compiler inserts before such
-// a read were measured too few for this instruction (stale accumulator values; results
-// correct once 32 wait states separate the chain from the read).
+// next MFMA's accumulator input.  The compiler separates the chain's last MFMA from a VALU
+// read of its result by 11 wait states (an s_nop 9 in the AMD assembly it emits for gfx950),
+// the CDNA3 ISA's required count for reading the result of an 8-pass XDL instruction.  On
+// gfx950 reads at that distance returned stale accumulator values for this instruction (the
+// fp32-input prefill then failed its parity tests) and correct ones once 32 wait states
+// separated them, so the drain issues four s_nop 7 (32 wait states, more than the 19 that
+// table requires even for a 16-pass instruction).
 __device__ __forceinline__ void mfma_f32_drain()
 {
     __builtin_amdgcn_sched_barrier(0);
