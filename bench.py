@@ -64,12 +64,13 @@ def decode_bytes_per_head_step(d: int) -> int:
 
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunked_amd", "csrc")
 PREFILL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_prefill_common.hpp",
-                   "gdn_prefill_ops.hpp", "gdn_prefill.hip", "gdn_prefill_split.hip",
-                   "gdn_prefill_wide.hip"]
+                   "gdn_split_bf16.hpp", "gdn_prefill_ops.hpp", "gdn_prefill.hip",
+                   "gdn_prefill_split.hip", "gdn_prefill_wide.hip"]
 DECODE_SOURCES = ["gdn_device.hpp", "gdn_decode.hip"]
 CHANNEL_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_channel.hip"]
 QSA_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_qsa.hip"]
-BACKWARD_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_backward.hip"]
+BACKWARD_SOURCES = ["gdn_device.hpp", "gdn_internal.hpp", "gdn_split_bf16.hpp",
+                    "gdn_backward.hip"]
 
 
 def sha_of(names) -> str:

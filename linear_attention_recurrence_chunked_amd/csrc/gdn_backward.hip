@@ -25,7 +25,7 @@
 //   dlog alpha_s = sum_{t >= s in the chunk} dg_t,  dalpha = dlog alpha / alpha.
 //
 // Four launches:
-//   bwd_prep_kernel     (chunk slot, head): T' (forward substitution in fp32) and P^T,
+//   bwd_prep_kernel     (chunk slot, head): T' (blocked inversion, split-bf16 MFMAs) and P^T,
 //                       bf16, and g into a record.
 //   bwd_states_kernel   (sequence, head, 32 state columns): the forward scan, keeping S at
 //                       the start of every chunk.
@@ -44,6 +44,7 @@
 // floor(t0_n / 64) + n + c, below floor(total_T / 64) + num_seqs.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
+#include "gdn_split_bf16.hpp"
 
 namespace gdn {
 namespace {
@@ -54,7 +55,8 @@ constexpr int L64 = C + 8;                 // bf16 row stride of a [.][64] LDS t
 constexpr int DVT = 32;                    // state columns per workgroup of the two scans
 constexpr int LVT = DVT + 8;               // bf16 row stride of a [.][32] LDS tile
 constexpr int DVB = 32;                    // value columns per pass of the chunk kernel
-constexpr int LF = C + 4;                  // fp32 row stride of the prep kernel's solve
+constexpr int LF = C + 4;                  // fp32 row stride of the prep kernel's T'
+constexpr int LNB = 20;                    // fp32 row stride of its 16 x 16 blocks
 // Record of one (chunk slot, head), in bf16 units: T' [64][64], P^T [64][64], then the 64
 // within-chunk log-decay prefixes g as fp32.
 constexpr int kRT = 0, kRP = C * C, kRG = 2 * C * C;
@@ -347,23 +349,27 @@ __device__ __forceinline__ void put_rec_piece(uint16_t *dst, int i, u32x4 x)
 }
 
 // ======================================================================================
-// bwd_prep_kernel: per (chunk slot, head) T' = (I + diag(beta) L)^{-1} diag(beta) by forward
-// substitution (fp32), P = lower_incl(Q K^T (.) Gamma), g.  Four waves.
+// bwd_prep_kernel: per (chunk slot, head) T' = (I + N)^{-1} diag(beta) with N = diag(beta) L,
+// P = lower_incl(Q K^T (.) Gamma), g.  Four waves; wave w owns block column w of the 4 x 4 grid
+// of 16 x 16 blocks.  The diagonal blocks of (I + N)^{-1} come by doubling (exact, since a
+// strictly lower 16 x 16 block has N^16 = 0), the blocks below them by block substitution;
+// every product of the solve runs on bf16 MFMAs with its operands split into high parts and
+// remainders (about 2^-16 relative).
 // ======================================================================================
-// L takes the place of Q once the products are done, T' that of K (and of L once the solve is
-// done), and P^T goes to the record from the accumulators, so four workgroups fit in a CU's LDS.
+// N and the diagonal inverses take the place of Q once the products are done, T' that of K,
+// and P^T goes to the record from the accumulators, so four workgroups fit in a CU's LDS.
 template <int DK>
 struct PrepLds {
+    static constexpr int mx(int a, int b) { return a > b ? a : b; }
     static constexpr int LK = DK + 8;
     static constexpr int oK = 0;
-    static constexpr int oT = 0;                    // [64][LF] fp32, after the solve
+    static constexpr int oT = 0;                    // [64][LF] fp32 T', after the products
     static constexpr int oQ = oK + C * LK * 2;
-    static constexpr int oL = oQ;                   // [64][LF] fp32, after the products
-    static constexpr int szQL = C * LK * 2 > C * LF * 4 ? C * LK * 2 : C * LF * 4;
-    static constexpr int oG = oQ + szQL;
+    static constexpr int oN = mx(oQ, C * LF * 4);   // six [16][LNB] fp32 blocks of N, and
+    static constexpr int oX = oN + 6 * 16 * LNB * 4;    // four of X_ii, after the products
+    static constexpr int oG = mx(oQ + C * LK * 2, oX + 4 * 16 * LNB * 4);
     static constexpr int oBet = oG + C * 4;
     static constexpr int total = oBet + C * 4;
-    static_assert(C * LF * 4 <= oG, "T' fits below the gates");
 };
 
 template <int DK>
@@ -373,7 +379,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     constexpr int LK = L::LK;
     __shared__ __align__(16) unsigned char smem[L::total];
     uint16_t *sK = (uint16_t *)(smem + L::oK), *sQ = (uint16_t *)(smem + L::oQ);
-    float *sL = (float *)(smem + L::oL), *sT = (float *)(smem + L::oT);
+    float *sN = (float *)(smem + L::oN), *sX = (float *)(smem + L::oX);
+    float *sT = (float *)(smem + L::oT);
     float *g = (float *)(smem + L::oG), *bet = (float *)(smem + L::oBet);
     const int H = a.H;
     const long long slot = blockIdx.x / H;
@@ -422,67 +429,117 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     }
     __syncthreads();
 
-    // L (fp32, for the solve) and P (bf16, to the record): 16 tiles each, four per wave; L is
-    // kept in registers until every wave is done with Q
-    f32x4 lt[4];
+    // N = diag(beta) L (fp32) and P (bf16, to the record): 16 tiles each, four per wave.  Wave w
+    // takes block column w: tile (u, w) of N in the accumulator layout (lane (r, p) holds rows
+    // 16u + 4p .. + 3 of column 16w + r).  The diagonal block also in the layout of its
+    // transpose, from the same entries of the symmetric K K^T block.
+    f32x4 nb[4], nT;
+    const int w16 = 16 * wave;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int tile = wave + 4 * u;
-        const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
+        const int m0 = 16 * u;
         f32x4 kk = zero4(), qk = zero4();
-        mm<false, true>(kk, sK, LK, sK, LK, m0, n0, DK);
-        mm<false, true>(qk, sQ, LK, sK, LK, m0, n0, DK);
+        mm<false, true>(kk, sK, LK, sK, LK, m0, w16, DK);
+        mm<false, true>(qk, sQ, LK, sK, LK, m0, w16, DK);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = m0 + q4 + i, s = n0 + r;
+            const int t = m0 + q4 + i, s = w16 + r;
             const float G = decay(g, t, s);
-            lt[u][i] = s < t ? kk[i] * G : 0.f;
+            nb[u][i] = s < t ? bet[t] * kk[i] * G : 0.f;
             qk[i] *= G;
         }
-        // P^T to the record: rows n0 + r, four adjacent columns m0 + q4 .. per lane
-        *(bf16x4 *)(rec + kRP + (n0 + r) * C + m0 + q4) = __builtin_convertvector(qk, bf16x4);
-    }
-    __syncthreads();
+        if (u == wave) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int tile = wave + 4 * u;
-        const int m0 = 16 * (tile >> 2), n0 = 16 * (tile & 3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sL[(m0 + q4 + i) * LF + n0 + r] = lt[u][i];
+            for (int i = 0; i < 4; ++i) {
+                const int t = w16 + r, s = w16 + q4 + i;
+                nT[i] = s < t ? bet[t] * kk[i] * decay(g, t, s) : 0.f;
+            }
+        }
+        // P^T to the record: rows w16 + r, four adjacent columns m0 + q4 .. per lane
+        *(bf16x4 *)(rec + kRP + (w16 + r) * C + m0 + q4) = __builtin_convertvector(qk, bf16x4);
     }
+    // (I + N)^{-1} of the diagonal block by doubling, (I - N)(I + N^2)(I + N^4)(I + N^8)
+    // (exact: N^16 = 0), with split-bf16 products; C = the accumulator layout of a block, T =
+    // that of its transpose
+    f32x4 nC = nb[0];
+#pragma unroll
+    for (int u = 1; u < 4; ++u)
+        if (u == wave) nC = nb[u];
+    f32x4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = q4 + i == r ? 1.f : 0.f;
+    const Sp snT = split4(nT), snC = split4(nC);
+    const f32x4 n2C = mm3r(snT, snC), n2T = mm3r(snC, snT);
+    const Sp sn2C = split4(n2C), sn2T = split4(n2T);
+    const f32x4 m1C = mm3r(snT, sn2C), m1T = mm3r(sn2C, snT);
+    const f32x4 n4C = mm3r(sn2T, sn2C), n4T = mm3r(sn2C, sn2T);
+    const f32x4 p1C = eye - nC + n2C - m1C, p1T = eye - nT + n2T - m1T;
+    const Sp sn4C = split4(n4C), sp1T = split4(p1T);
+    const f32x4 n8C = mm3r(split4(n4T), sn4C);
+    f32x4 p2C = p1C, p2T = p1T;
+    mm3(p2C, sp1T, sn4C);
+    mm3(p2T, sn4C, sp1T);
+    const Sp sn8C = split4(n8C), sp2T = split4(p2T);
+    f32x4 xC = p2C, xT = p2T;
+    mm3(xC, sp2T, sn8C);
+    mm3(xT, sn8C, sp2T);
+    __syncthreads();   // every wave is done with K and Q: T' goes over K, N and X over Q
+
+    // the strictly lower blocks of N row-major (block (i, m) at index i (i - 1) / 2 + m), the
+    // diagonal inverses X_ii row-major, T'_ww = X_ww diag(beta) and zeros above the diagonal
+    auto nblk = [&](int i, int m) { return sN + (i * (i - 1) / 2 + m) * 16 * LNB; };
+#pragma unroll
+    for (int u = 1; u < 4; ++u)
+        if (u > wave) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nblk(u, wave)[(q4 + i) * LNB + r] = nb[u][i];
+        }
+    *(f32x4 *)(sX + (w16 + r) * LNB + q4) = xT;
+    const float bcol = bet[w16 + r];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sT[(w16 + q4 + i) * LF + w16 + r] = xC[i] * bcol;
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+        if (j > wave) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[(w16 + q4 + i) * LF + 16 * j + r] = 0.f;
+        }
     __syncthreads();
 
-    // forward substitution, T'[t] = beta_t (e_t - sum_{i<t} L[t][i] T'[i]): wave w owns
-    // columns 16w .. 16w+15; lane (j = 16w + r, p = lane / 16) keeps rows 4m + p of its
-    // column in registers.  Terms with i >= t vanish on their own (L[t][i] = 0 there and
-    // rows not yet solved are still 0), and the column reaches LDS only after the loop, so
-    // no store stands between one step's reads of L and the next.
-    // beta_t comes from lane t by a lane read and the new row enters its lane by a 0 / 1
-    // weight (the slot it lands in is still 0), so the steps are one straight run of code
-    // and the reads of L for later steps can be issued early.
-    const int j = 16 * wave + r, p = lane >> 4;
-    const int bet_lane = __float_as_int(bet[lane]);
-    float own[4];
+    // the blocks below the diagonal of block column j = w:
+    // X_ij = -X_ii sum_{m=j}^{i-1} N_im X_mj,  T'_ij = X_ij diag(beta_j)
+    {
+        const int j = wave;
+        auto arow = [&](int i, int m) {
+            return split4(*(const f32x4 *)(nblk(i, m) + r * LNB + q4));
+        };
+        auto xrow = [&](int i) { return split4(*(const f32x4 *)(sX + (16 * i + r) * LNB + q4)); };
+        auto put_tb = [&](int i, f32x4 x) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) own[u] = p == u ? 1.f : 0.f;
-    float col[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) col[m] = 0.f;
-#pragma unroll
-    for (int t = 0; t < C; ++t) {
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};    // four partial sums: a short dependency chain
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-            if (4 * m < t) ps[m & 3] += sL[t * LF + 4 * m + p] * col[m];
-        float s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        s = row_sum4(s);
-        const float bt = __int_as_float(__builtin_amdgcn_readlane(bet_lane, t));
-        const float val = bt * ((t == j ? 1.f : 0.f) - s);
-        col[t >> 2] += own[t & 3] * val;
+            for (int e = 0; e < 4; ++e) sT[(16 * i + q4 + e) * LF + w16 + r] = x[e] * bcol;
+        };
+        if (j <= 2) {
+            const Sp xjj = split4(xC);
+            f32x4 acc1 = mm3r(arow(j + 1, j), xjj);
+            f32x4 acc2 = zero4(), acc3 = zero4();
+            if (j + 2 <= 3) acc2 = mm3r(arow(j + 2, j), xjj);
+            if (j + 3 <= 3) acc3 = mm3r(arow(j + 3, j), xjj);
+            const f32x4 x1 = -mm3r(xrow(j + 1), split4(acc1));
+            put_tb(j + 1, x1);
+            if (j + 2 <= 3) {
+                const Sp sx1 = split4(x1);
+                mm3(acc2, arow(j + 2, j + 1), sx1);
+                if (j + 3 <= 3) mm3(acc3, arow(j + 3, j + 1), sx1);
+                const f32x4 x2 = -mm3r(xrow(j + 2), split4(acc2));
+                put_tb(j + 2, x2);
+                if (j + 3 <= 3) {
+                    mm3(acc3, arow(j + 3, j + 2), split4(x2));
+                    const f32x4 x3 = -mm3r(xrow(j + 3), split4(acc3));
+                    put_tb(j + 3, x3);
+                }
+            }
+        }
     }
-    __syncthreads();   // every wave is done with L
-#pragma unroll
-    for (int m = 0; m < 16; ++m) sT[(4 * m + p) * LF + j] = col[m];
     __syncthreads();
     // T' to the record in 16-byte pieces
     for (int i = tid; i < C * C / 8; i += 256) {
