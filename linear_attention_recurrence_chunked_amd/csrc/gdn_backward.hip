@@ -562,15 +562,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 template <int DK>
 struct StLds {
     static constexpr int LK = DK + 8;
+    // a chunk's inputs, in one of two sets by chunk parity (set stride SET)
     static constexpr int oK = 0;                         // [64][LK]   K
     static constexpr int oT = oK + C * LK * 2;           // [64][L64]  T'
     static constexpr int oV = oT + C * L64 * 2;          // [64][LVT]  V columns
-    static constexpr int oSt = oV + C * LVT * 2;         // [DVT][LK]  S^T (bf16)
+    static constexpr int oGam = oV + C * LVT * 2;
+    static constexpr int oRat = oGam + C * 4;
+    static constexpr int SET = oRat + C * 4;
+    static constexpr int oSt = 2 * SET;                  // [DVT][LK]  S^T (bf16)
     static constexpr int oXt = oSt + DVT * LK * 2;       // [DVT][L64] X^T
     static constexpr int oUt = oXt + DVT * L64 * 2;      // [DVT][L64] (diag(rho) U)^T
-    static constexpr int oGam = oUt + DVT * L64 * 2;
-    static constexpr int oRat = oGam + C * 4;
-    static constexpr int oSf = oRat + C * 4;             // [DK][LSF]  S (fp32), to HBM
+    static constexpr int oSf = oUt + DVT * L64 * 2;      // [DK][LSF]  S (fp32), to HBM
     static constexpr int total = oSf + DK * LSF * 4;
 };
 
@@ -584,10 +586,8 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
     constexpr int VP = C * DVT / 8;                    // pieces of the V columns
     constexpr int SPW = DK / 64;                       // state tiles per wave
     __shared__ __align__(16) unsigned char smem[L::total];
-    uint16_t *sK = (uint16_t *)(smem + L::oK), *sT = (uint16_t *)(smem + L::oT);
-    uint16_t *sV = (uint16_t *)(smem + L::oV), *sSt = (uint16_t *)(smem + L::oSt);
+    uint16_t *sSt = (uint16_t *)(smem + L::oSt);
     uint16_t *sXt = (uint16_t *)(smem + L::oXt), *sUt = (uint16_t *)(smem + L::oUt);
-    float *gam = (float *)(smem + L::oGam), *rat = (float *)(smem + L::oRat);
     float *sSf = (float *)(smem + L::oSf);
     const int H = a.H;
     int unit, tile;
@@ -640,7 +640,13 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
             R.pgl = ((const float *)(rec + kRG))[C - 1];
         }
     };
-    auto commit = [&](const Pre &R) {
+    // the input set of chunk c
+    auto set_of = [&](int c) { return smem + (c & 1) * L::SET; };
+    auto commit = [&](const Pre &R, int c) {
+        unsigned char *st = set_of(c);
+        uint16_t *sK = (uint16_t *)(st + L::oK), *sT = (uint16_t *)(st + L::oT);
+        uint16_t *sV = (uint16_t *)(st + L::oV);
+        float *gam = (float *)(st + L::oGam), *rat = (float *)(st + L::oRat);
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int i = tid + kThreadsScan * j;
@@ -656,14 +662,19 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
 
     if (nch > 0) {
         fetch(ra, 0);
-        commit(ra);
+        commit(ra, 0);
     }
     if (nch > 1) fetch(ra, 1);
     __syncthreads();
     const int mt = wave >> 1, nt = wave & 1;          // this wave's c x 32 tile
-    // chunk c: LDS holds chunk c, cur holds chunk c + 1, nxt receives chunk c + 2
+    // chunk c: LDS set c % 2 holds chunk c, cur holds chunk c + 1 (written into the other set
+    // during the state update, that set's last reader being chunk c - 1), nxt receives c + 2
     auto step = [&](int c, Pre &cur, Pre &nxt) {
         const long long slot = slot0 + c;
+        unsigned char *st = set_of(c);
+        const uint16_t *sK = (const uint16_t *)(st + L::oK), *sT = (const uint16_t *)(st + L::oT);
+        const uint16_t *sV = (const uint16_t *)(st + L::oV);
+        const float *gam = (const float *)(st + L::oGam), *rat = (const float *)(st + L::oRat);
         if (c + 2 < nch) fetch(nxt, c + 2);
         store_state<DK, DV>(a.hs + ((slot * H + h) * DK) * (long long)DV + col0, sSf);
         // X = V - diag(gamma) K S
@@ -697,8 +708,7 @@ __global__ __launch_bounds__(kThreadsScan) void bwd_states_kernel(BwdArgs a)
             put_t(sSt, LK, 16 * mi, 16 * nk, S[k]);
             put_f(sSf, 16 * mi, 16 * nk, S[k]);
         }
-        __syncthreads();
-        if (c + 1 < nch) commit(cur);
+        if (c + 1 < nch) commit(cur, c + 1);
         __syncthreads();
     };
     for (int c = 0; c < nch; c += 2) {
