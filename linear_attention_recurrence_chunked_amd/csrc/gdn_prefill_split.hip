@@ -27,15 +27,15 @@
 namespace gdn {
 
 // Record of one (slot, head): T' [64][64] bf16 (rows in the internal token order of
-// gdn_prefill_ops.hpp) in the XOR-swizzled byte layout of a 64-wide LDS tile (so both launches copy it
-// granule for granule), then g [64] fp32.
+// gdn_prefill_ops.hpp) in the XOR-swizzled byte layout of a 64-wide LDS tile (so the scan
+// copies it into LDS granule for granule), then g [64] fp32.
 constexpr int kRecT = 0;
 constexpr int kRecG = kChunk * kChunk * 2;
 static_assert(kRecG + kChunk * 4 == kPrepRecordBytes, "record layout");
 
 
 // =========================================================================================
-// Launch 1: per (chunk slot, head) record T', P, g.  Four waves; wave w owns block row /
+// Launch 1: per (chunk slot, head) record T', g.  Four waves; wave w owns block row /
 // column w of the 4 x 4 grid of 16 x 16 blocks.
 // =========================================================================================
 // T' goes from registers straight to the record in HBM (it is never read back here), so the
