@@ -2,8 +2,8 @@
 
 Every gradient (dq, dk, dv, dalpha, dbeta, dS0) is compared element by element; the error is
 the per-(sequence, head) max relative error, bound 2e-2 for bf16 activations (the forward's
-bound).  The full-size prefill workload is checked on sampled heads against the oracle and,
-over all heads, through the adjoint identity <dq, q> = <dy, y>.
+bound).  The full-size prefill workload is checked on every head against the oracle and
+through the adjoint identity <dq, q> = <dy, y>.
 """
 import numpy as np
 import pytest
@@ -161,20 +161,21 @@ def test_backward_matches_forward_adjoint_identities(dev):
     assert abs(lhs_v - rhs_v) <= 5e-3 * scale
 
 
-def test_backward_full_prefill_workload_sampled_heads(dev, oracle_lib):
-    """The 4 x 4096-token, 16-head, d = 128 bf16 prefill at full size: two heads against the
-    oracle over all four sequences, every output finite."""
+def test_backward_full_prefill_workload(dev, oracle_lib):
+    """The 4 x 4096-token, 16-head, d = 128 bf16 prefill at full size, in the launch
+    configuration the benchmark times: every gradient of every head and sequence against the
+    oracle, every output finite."""
     from linear_attention_recurrence_chunked_amd import workloads as wl
     inp = wl.workload_inputs(wl.PREFILL)
     adj = wl.backward_inputs(inp, 0.02, seed=27)
     say("[gpu] backward full prefill workload")
     got = gpu_backward(inp, adj, dev)
-    cu = np.concatenate([[0], np.cumsum(inp["lengths"])]).astype(np.int64)
-    for h in (0, 11):
-        ref = oracle_backward(inp, adj, oracle_lib, heads=(h, h + 1))
-        compare(got, ref, cu, "full-size head %d" % h, heads=(h, h + 1))
     for i, x in enumerate(got):
         assert np.all(np.isfinite(x)), "output %d has non-finite values" % i
+    cu = np.concatenate([[0], np.cumsum(inp["lengths"])]).astype(np.int64)
+    say("[gpu] backward full prefill workload: oracle over all %d heads" % inp["H"])
+    ref = oracle_backward(inp, adj, oracle_lib)
+    compare(got, ref, cu, "full-size, all heads")
 
 
 def test_backward_deterministic(dev):

@@ -130,13 +130,12 @@ def test_decode_steps_in_place(dev, oracle_lib):
         assert ey <= TOL[dtype] and es <= TOL[dtype]
 
 
-def test_channel_full_prefill_shape_sampled_heads(dev, oracle_lib):
-    """4 x 4096 tokens, 16 heads of 128, bf16: two heads against the oracle."""
+def test_channel_full_prefill_shape(dev, oracle_lib):
+    """4 x 4096 tokens, 16 heads of 128, bf16: every head against the oracle."""
     from linear_attention_recurrence_chunked_amd import workloads as wl
     inp = wl.workload_inputs(wl.PREFILL)
     g = wl.channel_gates(inp, seed=36)
-    for h in (0, 13):
-        check(inp, g, dev, oracle_lib, "full-size head %d" % h, heads=(h, h + 1))
+    check(inp, g, dev, oracle_lib, "full-size, all heads")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

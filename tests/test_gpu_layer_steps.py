@@ -134,10 +134,10 @@ def test_output_gate_parity(dev, T, H, d, dt, in_place):
     assert err <= TOL[dt]
 
 
-def test_layer_steps_full_size_sampled(dev):
-    """The config-2 shape (T = 16384 packed tokens, H = 16, d = 128, bf16): the three steps at
-    full size, checked on sampled tokens against the oracle (each output token depends only
-    on its own window / row)."""
+def test_layer_steps_full_size(dev):
+    """The config-2 shape (T = 16384 packed tokens, H = 16, d = 128, bf16): the convolution
+    with its carried states and the output gate at full size, every token and every (token,
+    head) row against the oracle (each compared on its own scale)."""
     from linear_attention_recurrence_chunked_amd import gdn
     from linear_attention_recurrence_chunked_amd import workloads as wl
     from oracle import layer_steps as ls
@@ -150,22 +150,20 @@ def test_layer_steps_full_size_sampled(dev):
     y = _t(inp["y"], dev, "bf16")
     og = gdn.gdn_output_gate(y, _t(inp["z"], dev, "bf16"), torch.from_numpy(inp["norm_w"]).to(dev))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    xs = wl.as_f64(inp["x_q"], "bf16")
     got = _host(out)
-    for n in range(4):
-        s = inp["cu_seqlens"][n]
-        for t in sorted(set([0, 1, 2, 3, 4095] + [int(v) for v in rng.integers(0, 4096, 20)])):
-            # token t depends on tokens t-3 .. t only; the carried state enters for t < 3
-            if t >= 3:
-                ref, _ = ls.short_conv_silu(xs[s + t - 3:s + t + 1], inp["w_q"], [0, 4], 128)
-            else:
-                ref, _ = ls.short_conv_silu(xs[s:s + t + 1], inp["w_q"], [0, t + 1], 128,
-                                            inp["s_q"][n:n + 1])
-            assert _rel(got[s + t], ref[-1]) <= TOL["bf16"], (n, t)
-    rows = rng.integers(0, 16384, 64)
-    ref = ls.output_gate(wl.as_f64(inp["y"], "bf16")[rows], wl.as_f64(inp["z"], "bf16")[rows],
+    assert np.all(np.isfinite(got))
+    ref, _ = ls.short_conv_silu(wl.as_f64(inp["x_q"], "bf16"), inp["w_q"], inp["cu_seqlens"],
+                                128, inp["s_q"])
+    err = np.max(np.abs(got - ref).max(axis=-1) /
+                 np.maximum(np.abs(ref).max(axis=-1), 1e-30))
+    say("layer steps full size: convolution rel err %.3e over %d tokens" % (err, got.shape[0]))
+    assert err <= TOL["bf16"]
+    ref = ls.output_gate(wl.as_f64(inp["y"], "bf16"), wl.as_f64(inp["z"], "bf16"),
                          inp["norm_w"])
-    got = _host(og)[rows]
-    err = np.max(np.abs(got - ref) / np.abs(ref).max(axis=-1, keepdims=True))
+    got = _host(og)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref).max(axis=-1) /
+                 np.maximum(np.abs(ref).max(axis=-1), 1e-30))
+    say("layer steps full size: output gate rel err %.3e over %d rows" % (
+        err, got.shape[0] * got.shape[1]))
     assert err <= TOL["bf16"]
