@@ -217,8 +217,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     const int nchunks = (job.len + kChunk - 1) / kChunk;
     if (nchunks > 0) prefetch(job.tok0, job.len < kChunk ? job.len : kChunk);
 
-    constexpr int kPairs = 10;           // Gram tile pairs (t-block, i-block), i-block <= t-block
-    constexpr int kPairsPerWave = 3;
     const int trow = wave * 16 + 4 * lg;   // first token row of this lane in the acc layout
 
     for (int c = 0; c < nchunks; ++c) {

@@ -119,7 +119,10 @@ __device__ __forceinline__ int vswz(int row, int col)
 // that the compiler does not treat the wave's later LDS reads as waiting on them: the prep
 // waves read other stages while these copies fly, and wait for them (s_waitcnt vmcnt(0))
 // only before the step barrier that hands them to their readers.  The instruction has no
-// register output; M0 carries the LDS address.
+// register output; M0 carries the LDS address.  The compiler does not honour a clobber of M0
+// (it warns so), which is safe here only because nothing else in this kernel uses M0: its
+// AMD assembly holds no M0 access besides these copies' own "s_mov_b32 m0" (no indexed
+// register moves, no messages, no compiler-emitted direct-to-LDS loads).
 __device__ __forceinline__ unsigned lds_addr(const void *p)
 {
     return (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p;
