@@ -96,13 +96,6 @@ __global__ __launch_bounds__(256) void qsa_prep_kernel(QsaArgs a)
     }
 }
 
-// number of lanes below this one whose bit is set in m
-__device__ __forceinline__ int lanes_below(uint64_t m)
-{
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // The 16-lane group g's bits of a ballot (lanes 16 g .. 16 g + 15).
 __device__ __forceinline__ uint32_t group_bits(uint64_t m, int g)
 {
